@@ -1,0 +1,165 @@
+"""ctypes front end of the fp64 reference checker in ``mom_oracle.c``.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg
+of the benchmark may call this module; the GPU library never does.  Inputs are
+converted exactly to float64 (fp32 and bfloat16 values are exact in fp64).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mom_oracle.c")
+_LIB = os.path.join(_HERE, "_build", "libmom_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the checker with gcc (plain C99, OpenMP, IEEE double)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    os.makedirs(os.path.dirname(_LIB), exist_ok=True)
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        _lib = ctypes.CDLL(_LIB)
+    return _lib
+
+
+def _d(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _i(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def threads() -> int:
+    """Number of OpenMP threads the checker uses."""
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def route(x, w_r, bias, K, want_logits=False):
+    x, w_r, bias = _d(x), _d(w_r), _d(bias)
+    n, D = x.shape
+    M = w_r.shape[0]
+    idx = np.empty((n, K), np.int32)
+    w = np.empty((n, K), np.float64)
+    lg = np.empty((n, M), np.float64) if want_logits else None
+    lib().oracle_route(ctypes.c_int64(n), D, M, K, _p(x), _p(w_r), _p(bias), _p(idx), _p(w), _p(lg))
+    return (idx, w, lg) if want_logits else (idx, w)
+
+
+def dispatch(idx, B, T, M):
+    idx = _i(idx)
+    K = idx.shape[1]
+    N = B * T * (K + 1)
+    seg_off = np.empty((M + 1) * B + 1, np.int32)
+    perm = np.empty(N, np.int32)
+    inv = np.empty((B * T, K), np.int32)
+    lib().oracle_dispatch(B, T, M, K, _p(idx), _p(seg_off), _p(perm), _p(inv))
+    return seg_off, perm, inv
+
+
+def gdn_step(q, k, v, a, c, S):
+    """One recurrence step; S [dk][dv] is updated in place (float64)."""
+    q, k, v = _d(q), _d(k), _d(v)
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    dk, dv = S.shape
+    o = np.empty(dv, np.float64)
+    lib().oracle_gdn_step(dk, dv, ctypes.c_double(a), ctypes.c_double(c), _p(q), _p(k), _p(v),
+                          _p(S), _p(o))
+    return o
+
+
+def gdn_chain(q, k, v, a, c, S0=None):
+    """Recurrence over one memory's own rows: returns (o [L][dv], S_final)."""
+    q, k, v, a, c = _d(q), _d(k), _d(v), _d(a), _d(c)
+    L, dk = k.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else _d(S0).copy()
+    o = np.empty((L, dv), np.float64)
+    lib().oracle_gdn_chain(ctypes.c_int64(L), dk, dv, _p(q), _p(k), _p(v), _p(a), _p(c), _p(S), _p(o))
+    return o, S
+
+
+def layer(dims, x, w_r, bias, w_q, w_k, w_v, alpha, beta, state0=None, mixed=False,
+          want_qkv=False):
+    """Whole layer forward.  dims = (B, T, D, H, dk, dv, M, K)."""
+    B, T, D, H, dk, dv, M, K = [int(v) for v in dims]
+    NT = B * T
+    args = [_d(a) for a in (x, w_r, bias, w_q, w_k, w_v, alpha, beta, state0)]
+    res = dict(
+        idx=np.empty((NT, K), np.int32), w=np.empty((NT, K)),
+        o_routed=np.empty((NT, K, H, dv)), o_shared=np.empty((NT, H, dv)),
+        out=np.empty((NT, H, dv)), out_mixed=np.empty((NT, H, dv)) if mixed else None,
+        state=np.empty((B, M + 1, H, dk, dv)),
+        q=np.empty((NT, H, dk)) if want_qkv else None,
+        k=np.empty((NT, K + 1, H, dk)) if want_qkv else None,
+        v=np.empty((NT, K + 1, H, dv)) if want_qkv else None)
+    dims_a = np.array([B, T, D, H, dk, dv, M, K], np.int32)
+    lib().oracle_layer(_p(dims_a), *[_p(a) for a in args], _p(res["idx"]), _p(res["w"]),
+                       _p(res["o_routed"]), _p(res["o_shared"]), _p(res["out"]),
+                       _p(res["out_mixed"]), _p(res["state"]), _p(res["q"]), _p(res["k"]),
+                       _p(res["v"]))
+    return res
+
+
+def combine(inv, w, o_routed, o_shared):
+    w, o_routed, o_shared = _d(w), _d(o_routed), _d(o_shared)
+    inv = _i(inv)
+    n, K = w.shape
+    H, dv = o_shared.shape[1], o_shared.shape[2]
+    out = np.empty((n, H, dv))
+    lib().oracle_combine(ctypes.c_int64(n), K, H, dv, _p(inv), _p(w), _p(o_routed), _p(o_shared),
+                         _p(out))
+    return out
+
+
+def segments(seg_off, seg_state, row_token, q, k, v, a, c, state, which=None):
+    """Run the recurrence over packed segments.  `state` (float64 [n_state][H][dk][dv])
+    is updated in place; returns o [N][H][dv] (rows of segments not run are NaN)."""
+    seg_off, seg_state, row_token, which = _i(seg_off), _i(seg_state), _i(row_token), _i(which)
+    q, k, v, a, c = _d(q), _d(k), _d(v), _d(a), _d(c)
+    assert state.dtype == np.float64 and state.flags.c_contiguous
+    N, H, dk = k.shape
+    dv = v.shape[2]
+    o = np.full((N, H, dv), np.nan)
+    n_seg = seg_off.shape[0] - 1
+    lib().oracle_segments(n_seg, _p(seg_off), _p(seg_state), _p(row_token), H, dk, dv, _p(q), _p(k),
+                          _p(v), _p(a), _p(c), _p(state), _p(o), 0 if which is None else len(which),
+                          _p(which))
+    return o
+
+
+def project_head(rows_tok, x, wq_h, wk_h, wv_h):
+    """Projections of one head for the tokens rows_tok: (q, k normalised, v)."""
+    rows_tok, x = _i(rows_tok), _d(x)
+    wq_h, wk_h, wv_h = _d(wq_h), _d(wk_h), _d(wv_h)
+    n = rows_tok.shape[0]
+    D = x.shape[1]
+    dk = (wk_h if wk_h is not None else wq_h).shape[0]
+    dv = wv_h.shape[0] if wv_h is not None else 1
+    q = np.empty((n, dk)) if wq_h is not None else None
+    k = np.empty((n, dk)) if wk_h is not None else None
+    v = np.empty((n, dv)) if wv_h is not None else None
+    lib().oracle_project_head(ctypes.c_int64(n), _p(rows_tok), D, dk, dv, _p(x), _p(wq_h), _p(wk_h),
+                              _p(wv_h), _p(q), _p(k), _p(v))
+    return q, k, v
