@@ -1,0 +1,187 @@
+/*
+ * mom.h -- C ABI of the MI355X Mixture-of-Memories (MoM) layer forward library
+ * (libmom.so, HIP kernels for gfx950).
+ *
+ * The layer (arXiv 2502.13685, "MoM: Linear Sequence Modeling with
+ * Mixture-of-Memories") is split into the parts the pages describe:
+ *   mom_route        linear router: matmul, softmax, top-k, renormalisation
+ *                    (podcast.do-not-panic.com page, "Router mechanics, step by
+ *                    step"; research.elamur.ai summary, "Summary").
+ *   mom_dispatch     tokens reordered into contiguous per-memory segments
+ *                    (podcast.do-not-panic.com page, "Solving scatter-gather
+ *                    without new kernels").
+ *   mom_project      shared query projection, per-memory key/value projections
+ *                    (research.elamur.ai summary: each memory has its own
+ *                    key/value projections), keys L2-normalised per head.
+ *   gdn_chunk_fwd    the single-memory Gated DeltaNet operator run over each
+ *                    segment (jxzklqfsx.com write-up, hardware-efficient
+ *                    implementation section: each memory reuses the
+ *                    single-memory operator; the gist.science page, "Core
+ *                    mechanism", restates the forget/delta update).
+ *   gdn_decode_step  one recurrent step per sequence (constant-cost inference,
+ *                    jxzklqfsx.com write-up, introduction and inference section).
+ *   mom_combine      router-weighted sum of the per-memory reads plus the
+ *                    always-on shared memory (jxzklqfsx.com write-up,
+ *                    Mixture-of-Memories section and hardware-efficient
+ *                    implementation section).
+ *
+ * Recurrence of one memory, per head, on a state S [dk][dv] (float32):
+ *   S <- a S;  S <- S + c k (v - S^T k)^T;  o = S^T q      (a = alpha, c = beta)
+ * A memory that a token is not routed to is not touched at that token.
+ *
+ * Conventions for every entry point
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates or frees device memory and never synchronises; each call
+ *     validates its arguments on the host, enqueues its kernels on `stream`
+ *     (a hipStream_t; NULL = the null stream) and returns.
+ *   - Arguments are checked before any launch.  A failed check returns a
+ *     negative mom_status and enqueues nothing.  A launch error returns
+ *     MOM_ERR_LAUNCH.  Kernel faults surface on the stream, as with any HIP call.
+ *   - Every pointer must be 16-byte aligned.  Inputs must be finite.
+ *   - Identical inputs give bit-identical outputs (no floating-point atomics).
+ *   - Layouts are row-major with the shapes given below.
+ *
+ * Sizes derived from mom_dims: NT = B*T tokens (token id = b*T + t),
+ * NR = NT*topk routed rows, N = NR + NT packed rows, n_seg = (M+1)*B segments,
+ * n_state = B*(M+1) state slots, slot of (b, m) = b*(M+1) + m.
+ *
+ * Packed row order: segment s = m*B + b holds the tokens of sequence b routed
+ * to memory m in increasing position; segments follow each other in s order.
+ * Memory m = M is the shared memory: its segments hold every token, so rows
+ * NR + (b*T + t) belong to it, in token order.
+ *
+ * Storage types: when dims->dtype == MOM_DTYPE_F32, x and the weights are
+ * float32 and q/k/v are float32.  When dims->dtype == MOM_DTYPE_BF16, x and the
+ * weights are bfloat16 and q/k/v are IEEE binary16 (half): keys have unit norm
+ * and the queries/values of the layer stay far inside the half range, and half
+ * carries 8x the precision of bfloat16 into the recurrence's matrix-core
+ * products.  Gates, router weights, outputs and states are always float32.
+ *
+ * Supported shapes: dk in {64,128}; dv in {64,128,256}; chunk == 64;
+ * D % 64 == 0, 64 <= D <= 8192; 1 <= topk <= M <= 64, topk <= 8; B,T >= 1;
+ * N < 2^31.
+ */
+#ifndef MOM_H_
+#define MOM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mom_status {
+  MOM_OK = 0,
+  MOM_ERR_NULL = -1,        /* a required pointer is NULL */
+  MOM_ERR_DIMS = -2,        /* a size is out of range or inconsistent */
+  MOM_ERR_UNSUPPORTED = -3, /* a shape or dtype outside the supported set */
+  MOM_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+  MOM_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
+  MOM_ERR_LAUNCH = -6       /* the HIP runtime refused a kernel launch */
+} mom_status;
+
+enum { MOM_DTYPE_F32 = 0, MOM_DTYPE_BF16 = 1 };
+
+typedef struct mom_dims {
+  int32_t B;      /* sequences */
+  int32_t T;      /* tokens per sequence */
+  int32_t D;      /* model width */
+  int32_t H;      /* heads */
+  int32_t dk;     /* key dimension per head */
+  int32_t dv;     /* value dimension per head */
+  int32_t M;      /* routed memories (the shared memory is index M) */
+  int32_t topk;   /* memories selected per token */
+  int32_t chunk;  /* chunk length of the chunkwise recurrence (64) */
+  int32_t dtype;  /* MOM_DTYPE_F32 or MOM_DTYPE_BF16 */
+} mom_dims;
+
+/* Router.  For each token: logit_m = x . w_r[m] + bias[m] (accumulated in
+ * float64; products of the stored inputs are exact), top-k memories by
+ * decreasing logit with ties to the lower index, weights = softmax over all M
+ * renormalised over the selected k (= softmax of the selected logits).
+ *   x     [NT][D]   (dtype)          w_r  [M][D] (dtype)
+ *   bias  [M] float32 or NULL (= 0)
+ *   idx   [NT][topk] int32 out       w    [NT][topk] float32 out            */
+mom_status mom_route(const mom_dims* dims, const void* x, const void* w_r, const float* bias,
+                     int32_t* idx, float* w, void* stream);
+
+/* Dispatch: stable counting sort of the (token, memory) pairs by (memory,
+ * sequence), tokens in increasing position, plus the gates in packed order.
+ *   idx      [NT][topk] int32 in (every entry in [0, M), distinct per token)
+ *   x        [NT][D] (dtype) in, only read when x_packed != NULL
+ *   alpha    [NT][H][M+1] float32 in,  beta same
+ *   seg_off  [n_seg+1] int32 out: segment s = m*B+b covers [seg_off[s], seg_off[s+1])
+ *   perm     [N] int32 out: token of each packed row (rows >= NR: identity)
+ *   inv      [NT][topk] int32 out: packed row of (token, j)
+ *   x_packed [NR][D] (dtype) out or NULL: x gathered in packed order
+ *   alpha_p  [N][H] float32 out: alpha[perm[r]][h][memory of r]; beta_p same
+ *   ws       workspace of at least mom_workspace_bytes(dims, MOM_WS_DISPATCH)  */
+mom_status mom_dispatch(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
+                        const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv,
+                        void* x_packed, float* alpha_p, float* beta_p, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* Projections.  q[t] = w_q x[t] for every token; for packed row r of memory m
+ * (from seg_off): k[r] = w_k[m] x[perm[r]] normalised to unit L2 norm per head
+ * (no epsilon), v[r] = w_v[m] x[perm[r]].  Accumulation in float32.
+ *   x [NT][D], w_q [H*dk][D], w_k [M+1][H*dk][D], w_v [M+1][H*dv][D] (dtype)
+ *   seg_off, perm: as written by mom_dispatch
+ *   q [NT][H][dk], k [N][H][dk], v [N][H][dv] out (float32 or half, see above) */
+mom_status mom_project(const mom_dims* dims, const void* x, const int32_t* perm,
+                       const int32_t* seg_off, const void* w_q, const void* w_k, const void* w_v,
+                       void* q, void* k, void* v, void* stream);
+
+/* Chunkwise Gated DeltaNet over packed segments.  Segment s (rows
+ * [seg_off[s], seg_off[s+1]) of the row arrays) runs the recurrence above in
+ * row order from state slot seg_state[s] (NULL: slot s); different segments
+ * must use different slots.  Chunks of dims->chunk rows are processed in the
+ * WY/UT form, which equals the token recurrence up to rounding.
+ *   q         [n_tok][H][dk] read at row row_token[r] (NULL: row r itself)
+ *   k [N][H][dk], v [N][H][dv] (float32 or half per dims->dtype)
+ *   alpha_p, beta_p [N][H] float32
+ *   state_in  [n_state][H][dk][dv] float32 or NULL (zeros); may equal state_out
+ *   state_out [n_state][H][dk][dv] float32; slots of segments run are written
+ *             (an empty segment copies its state unchanged)
+ *   o         [N][H][dv] float32: the read after each row's write
+ * Preconditions: seg_off non-decreasing with seg_off[n_seg] <= n_rows,
+ * row_token entries in [0, n_tok).  ws may be NULL when
+ * mom_workspace_bytes(dims, MOM_WS_CHUNK) is 0.                              */
+mom_status gdn_chunk_fwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
+                         int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
+                         const int32_t* row_token, const void* q, const void* k, const void* v,
+                         const float* alpha_p, const float* beta_p, const float* state_in,
+                         float* state_out, float* o, void* ws, size_t ws_bytes, void* stream);
+
+/* One recurrent step for n_seq sequences with one new token each (T = 1 view:
+ * rows as written by mom_dispatch/mom_project for dims with B = n_seq, T = 1).
+ * For sequence b and slot j < topk the memory is idx[b][j] and the packed row
+ * inv[b][j]; slot topk is the shared memory M at row NR + b.  The state of
+ * (b, memory) is updated in place; memories not selected are not touched.
+ *   idx, inv  [n_seq][topk] int32
+ *   q [n_seq][H][dk], k [N][H][dk], v [N][H][dv] (float32 or half)
+ *   alpha, beta [n_seq][H][M+1] float32
+ *   states [n_seq][M+1][H][dk][dv] float32, updated in place
+ *   o [N][H][dv] float32 out (packed rows, as gdn_chunk_fwd)                   */
+mom_status gdn_decode_step(const mom_dims* dims, int32_t n_seq, const int32_t* idx,
+                           const int32_t* inv, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, float* states, float* o,
+                           void* stream);
+
+/* Combine: out[t] = o_shared[t] + sum_j w[t][j] * o_routed[row(t, j)], shared
+ * first then j ascending, float32, row(t, j) = inv[t][j] (NULL: t*topk + j).
+ *   o_routed [*][H][dv], o_shared [n_tok][H][dv], out [n_tok][H][dv] float32  */
+mom_status mom_combine(const mom_dims* dims, int32_t n_tok, const int32_t* inv, const float* w,
+                       const float* o_routed, const float* o_shared, float* out, void* stream);
+
+enum { MOM_WS_DISPATCH = 0, MOM_WS_CHUNK = 1 };
+/* Workspace bytes an entry point needs (0 = none); 0 for invalid dims. */
+size_t mom_workspace_bytes(const mom_dims* dims, int32_t which);
+
+/* Static text for a status code. */
+const char* mom_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOM_H_ */

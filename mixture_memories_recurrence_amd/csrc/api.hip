@@ -1,0 +1,71 @@
+// Entry points without kernels of their own: gdn_chunk_fwd's validation and
+// dispatch to the kernel variant for the storage type, workspace sizes, and
+// status strings.
+#include "common.h"
+
+namespace mom {
+template <typename IT>
+mom_status launch_gdn_chunk_valu(const mom_dims& d, int n_seg, const int32_t* seg_off, const int32_t* seg_state,
+                                 const int32_t* row_token, const void* q, const void* k, const void* v,
+                                 const float* alpha_p, const float* beta_p, const float* state_in, float* state_out,
+                                 float* o, hipStream_t st);
+}  // namespace mom
+
+extern "C" mom_status gdn_chunk_fwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
+                                    int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
+                                    const int32_t* row_token, const void* q, const void* k, const void* v,
+                                    const float* alpha_p, const float* beta_p, const float* state_in,
+                                    float* state_out, float* o, void* ws, size_t ws_bytes, void* stream) {
+  using namespace mom;
+  mom_status s = check_dims(dims);
+  if (s != MOM_OK) return s;
+  if (n_seg < 0 || n_rows < 0 || n_tok < 0 || n_state < 0) return MOM_ERR_DIMS;
+  if (!seg_state && n_state < n_seg) return MOM_ERR_DIMS;
+  MOM_CHECK_PTR(seg_off);
+  MOM_CHECK_OPT_PTR(seg_state);
+  MOM_CHECK_OPT_PTR(row_token);
+  MOM_CHECK_OPT_PTR(state_in);
+  MOM_CHECK_PTR(state_out);
+  if (n_rows > 0) {
+    MOM_CHECK_PTR(q);
+    MOM_CHECK_PTR(k);
+    MOM_CHECK_PTR(v);
+    MOM_CHECK_PTR(alpha_p);
+    MOM_CHECK_PTR(beta_p);
+    MOM_CHECK_PTR(o);
+  }
+  const size_t need = mom_workspace_bytes(dims, MOM_WS_CHUNK);
+  if (need && (!ws || ws_bytes < need)) return MOM_ERR_WORKSPACE;
+  if (n_seg == 0) return MOM_OK;
+  hipStream_t st = (hipStream_t)stream;
+  if (dims->dtype == MOM_DTYPE_BF16)
+    return launch_gdn_chunk_valu<f16_t>(*dims, n_seg, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
+                                        state_in, state_out, o, st);
+  return launch_gdn_chunk_valu<float>(*dims, n_seg, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
+                                      state_in, state_out, o, st);
+}
+
+extern "C" size_t mom_workspace_bytes(const mom_dims* dims, int32_t which) {
+  using namespace mom;
+  if (check_dims(dims) != MOM_OK) return 0;
+  const mom_dims& d = *dims;
+  if (which == MOM_WS_DISPATCH) {
+    const int64_t ntile = (d.T + kDispatchTile - 1) / kDispatchTile;
+    const int64_t bytes = (int64_t)d.M * d.B * ntile * 4;
+    return (size_t)((bytes + 255) / 256 * 256);
+  }
+  return 0;
+}
+
+extern "C" const char* mom_status_string(int32_t status) {
+  switch (status) {
+    case MOM_OK: return "ok";
+    case MOM_ERR_NULL: return "a required pointer is NULL";
+    case MOM_ERR_DIMS: return "a size is out of range or inconsistent";
+    case MOM_ERR_UNSUPPORTED: return "shape or dtype outside the supported set";
+    case MOM_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MOM_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOM_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}

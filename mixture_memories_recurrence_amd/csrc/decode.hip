@@ -1,0 +1,153 @@
+// One recurrent step per sequence (constant cost per token, jxzklqfsx.com
+// write-up, introduction and inference-efficiency section).  For each
+// (sequence, activated memory incl. the shared one, head):
+//   a = S^T k, b = S^T q                 one pass over S
+//   u = c (v - a_g a)                    a_g = forget gate, c = write strength
+//   o = a_g b + (k.q) u                  = (a_g S + k u^T)^T q
+//   S <- a_g S + k u^T                   written back in place
+// (gist.science page, "Core mechanism": forget then delta update; read after
+// the write.)  The kernel streams the resident float32 states: one block per
+// (sequence, slot, head) holds its whole [dk][dv] state in registers between
+// the read and the write, so each state is read once and written once.
+#include "common.h"
+
+namespace mom {
+
+template <typename IT, int DK, int DV>
+__global__ __launch_bounds__(256) void k_gdn_decode(int n_seq, int H, int M, int K, const int32_t* __restrict__ idx,
+                                                    const int32_t* __restrict__ inv, const IT* __restrict__ q,
+                                                    const IT* __restrict__ k, const IT* __restrict__ v,
+                                                    const float* __restrict__ alpha, const float* __restrict__ beta,
+                                                    float* __restrict__ states, float* __restrict__ o) {
+  constexpr int CPR = DV / 4;     // threads per state row (float4 each)
+  constexpr int RG = 256 / CPR;   // row groups
+  constexpr int RPT = DK / RG;    // rows per thread
+  __shared__ float qs[DK], ks[DK], vs[DV];
+  __shared__ float4 red_a[RG][CPR], red_b[RG][CPR];
+  __shared__ float kq_s;
+
+  const int h = blockIdx.x % H;
+  const int j = (blockIdx.x / H) % (K + 1);
+  const int b = blockIdx.x / (H * (K + 1));
+  const int tid = threadIdx.x;
+  int m;
+  int64_t row;
+  if (j < K) {
+    m = idx[(int64_t)b * K + j];
+    row = inv[(int64_t)b * K + j];
+  } else {
+    m = M;
+    row = (int64_t)n_seq * K + b;
+  }
+  if ((unsigned)m > (unsigned)M) return;
+  const float ag = alpha[((int64_t)b * H + h) * (M + 1) + m];
+  const float cg = beta[((int64_t)b * H + h) * (M + 1) + m];
+  for (int e = tid; e < DK; e += 256) {
+    qs[e] = load_as_f32(q + ((int64_t)b * H + h) * DK + e);
+    ks[e] = load_as_f32(k + (row * H + h) * DK + e);
+  }
+  for (int e = tid; e < DV; e += 256) vs[e] = load_as_f32(v + (row * H + h) * DV + e);
+  float4* S = reinterpret_cast<float4*>(states + ((((int64_t)b * (M + 1) + m) * H + h) * DK) * DV);
+  const int c4 = tid % CPR, rg = tid / CPR;
+  float4 reg[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) reg[r] = S[(int64_t)(rg + RG * r) * CPR + c4];
+  __syncthreads();
+  if (tid < 64) {
+    float p = 0.f;
+    for (int e = tid; e < DK; e += 64) p = fmaf(ks[e], qs[e], p);
+    p = wave_sum_xor(p);
+    if (tid == 0) kq_s = p;
+  }
+  float4 pa = {0.f, 0.f, 0.f, 0.f}, pb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const float kd = ks[rg + RG * r], qd = qs[rg + RG * r];
+    pa.x = fmaf(reg[r].x, kd, pa.x); pa.y = fmaf(reg[r].y, kd, pa.y);
+    pa.z = fmaf(reg[r].z, kd, pa.z); pa.w = fmaf(reg[r].w, kd, pa.w);
+    pb.x = fmaf(reg[r].x, qd, pb.x); pb.y = fmaf(reg[r].y, qd, pb.y);
+    pb.z = fmaf(reg[r].z, qd, pb.z); pb.w = fmaf(reg[r].w, qd, pb.w);
+  }
+  red_a[rg][c4] = pa;
+  red_b[rg][c4] = pb;
+  __syncthreads();
+  float4 sa = red_a[0][c4], sb = red_b[0][c4];
+#pragma unroll
+  for (int g = 1; g < RG; ++g) {
+    const float4 ta = red_a[g][c4], tb = red_b[g][c4];
+    sa.x += ta.x; sa.y += ta.y; sa.z += ta.z; sa.w += ta.w;
+    sb.x += tb.x; sb.y += tb.y; sb.z += tb.z; sb.w += tb.w;
+  }
+  const float kq = kq_s;
+  const float4 vv = reinterpret_cast<const float4*>(vs)[c4];
+  float4 u;
+  u.x = cg * (vv.x - ag * sa.x);
+  u.y = cg * (vv.y - ag * sa.y);
+  u.z = cg * (vv.z - ag * sa.z);
+  u.w = cg * (vv.w - ag * sa.w);
+  if (rg == 0) {
+    float4 ov;
+    ov.x = fmaf(kq, u.x, ag * sb.x);
+    ov.y = fmaf(kq, u.y, ag * sb.y);
+    ov.z = fmaf(kq, u.z, ag * sb.z);
+    ov.w = fmaf(kq, u.w, ag * sb.w);
+    reinterpret_cast<float4*>(o + (row * H + h) * DV)[c4] = ov;
+  }
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const float kd = ks[rg + RG * r];
+    float4 s2;
+    s2.x = fmaf(kd, u.x, ag * reg[r].x);
+    s2.y = fmaf(kd, u.y, ag * reg[r].y);
+    s2.z = fmaf(kd, u.z, ag * reg[r].z);
+    s2.w = fmaf(kd, u.w, ag * reg[r].w);
+    S[(int64_t)(rg + RG * r) * CPR + c4] = s2;
+  }
+}
+
+template <typename IT>
+static void launch_decode(const mom_dims& d, int n_seq, const int32_t* idx, const int32_t* inv, const void* q,
+                          const void* k, const void* v, const float* alpha, const float* beta, float* states,
+                          float* o, hipStream_t st) {
+  const unsigned blocks = (unsigned)((int64_t)n_seq * (d.topk + 1) * d.H);
+#define MOM_DEC(DK, DV)                                                                                         \
+  hipLaunchKernelGGL((k_gdn_decode<IT, DK, DV>), dim3(blocks), dim3(256), 0, st, n_seq, d.H, d.M, d.topk, idx, \
+                     inv, (const IT*)q, (const IT*)k, (const IT*)v, alpha, beta, states, o)
+  if (d.dk == 64) {
+    if (d.dv == 64) MOM_DEC(64, 64);
+    else if (d.dv == 128) MOM_DEC(64, 128);
+    else MOM_DEC(64, 256);
+  } else {
+    if (d.dv == 64) MOM_DEC(128, 64);
+    else if (d.dv == 128) MOM_DEC(128, 128);
+    else MOM_DEC(128, 256);
+  }
+#undef MOM_DEC
+}
+
+}  // namespace mom
+
+extern "C" mom_status gdn_decode_step(const mom_dims* dims, int32_t n_seq, const int32_t* idx, const int32_t* inv,
+                                      const void* q, const void* k, const void* v, const float* alpha,
+                                      const float* beta, float* states, float* o, void* stream) {
+  using namespace mom;
+  mom_status s = check_dims(dims);
+  if (s != MOM_OK) return s;
+  if (n_seq < 0) return MOM_ERR_DIMS;
+  MOM_CHECK_PTR(idx);
+  MOM_CHECK_PTR(inv);
+  MOM_CHECK_PTR(q);
+  MOM_CHECK_PTR(k);
+  MOM_CHECK_PTR(v);
+  MOM_CHECK_PTR(alpha);
+  MOM_CHECK_PTR(beta);
+  MOM_CHECK_PTR(states);
+  MOM_CHECK_PTR(o);
+  if (n_seq == 0) return MOM_OK;
+  hipStream_t st = (hipStream_t)stream;
+  if (dims->dtype == MOM_DTYPE_BF16)
+    launch_decode<f16_t>(*dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, st);
+  else
+    launch_decode<float>(*dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, st);
+  return launch_status();
+}

@@ -1,0 +1,193 @@
+// Dispatch of the MoM layer: the scatter/gather of routed tokens becomes a
+// reordering of each memory's tokens into one contiguous segment per
+// (memory, sequence) (podcast.do-not-panic.com page, "Solving scatter-gather
+// without new kernels").
+//
+// A stable counting sort in three launches, all integer work:
+//   k_count   one block per (tile of 256 positions, sequence): per-memory counts
+//             of the tile, written to cnt[m][b][tile];
+//   k_scan    one block: exclusive scan of cnt in (m, b, tile) order, which is
+//             exactly the packed row order; writes seg_off;
+//   k_scatter one block per tile again: a token's rank among the tile's tokens
+//             routed to the same memory comes from wavefront ballots (popcount
+//             of the lower lanes) plus the totals of the waves before it, so
+//             the order inside a segment is increasing position.  The block
+//             then writes perm/inv, gathers the gates of the routed memory and,
+//             if asked, the x rows.
+#include "common.h"
+
+namespace mom {
+
+constexpr int kTile = kDispatchTile;
+
+__global__ __launch_bounds__(kTile) void k_count(int B, int T, int M, int K, int ntile,
+                                                 const int32_t* __restrict__ idx, int32_t* __restrict__ cnt) {
+  __shared__ int32_t c[64];
+  const int tile = blockIdx.x, b = blockIdx.y;
+  if (threadIdx.x < 64) c[threadIdx.x] = 0;
+  __syncthreads();
+  const int t = tile * kTile + threadIdx.x;
+  if (t < T) {
+    const int64_t tok = (int64_t)b * T + t;
+    for (int j = 0; j < K; ++j) {
+      const int m = idx[tok * K + j];
+      if ((unsigned)m < (unsigned)M) atomicAdd(&c[m], 1);  // out-of-range entries are ignored
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < M) cnt[((int64_t)threadIdx.x * B + b) * ntile + tile] = c[threadIdx.x];
+}
+
+// Exclusive scan of n counts in place (single block of 1024 threads).
+__global__ __launch_bounds__(1024) void k_scan(int B, int T, int M, int K, int ntile, int32_t* __restrict__ cnt,
+                                               int32_t* __restrict__ seg_off) {
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t carry_s;
+  const int n = M * B * ntile;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (threadIdx.x == 0) carry_s = 0;
+  __syncthreads();
+  for (int base = 0; base < n; base += 1024) {
+    const int i = base + threadIdx.x;
+    const int32_t v = i < n ? cnt[i] : 0;
+    // inclusive scan inside the wave
+    int32_t s = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t u = __shfl_up(s, o, 64);
+      if (lane >= o) s += u;
+    }
+    if (lane == 63) wsum[wv] = s;
+    __syncthreads();
+    int32_t pre = carry_s;
+    for (int w2 = 0; w2 < wv; ++w2) pre += wsum[w2];
+    if (i < n) cnt[i] = pre + s - v;
+    __syncthreads();
+    if (threadIdx.x == 1023) carry_s = pre + s;
+    __syncthreads();
+  }
+  const int64_t NR = (int64_t)B * T * K;
+  for (int s = threadIdx.x; s <= (M + 1) * B; s += 1024) {
+    int64_t off;
+    if (s < M * B) off = cnt[(int64_t)s * ntile];
+    else if (s < (M + 1) * B) off = NR + (int64_t)(s - M * B) * T;
+    else off = NR + (int64_t)B * T;
+    seg_off[s] = (int32_t)off;
+  }
+}
+
+template <typename XT>
+__global__ __launch_bounds__(kTile) void k_scatter(int B, int T, int D, int H, int M, int K, int ntile,
+                                                   const int32_t* __restrict__ idx, const int32_t* __restrict__ base,
+                                                   const float* __restrict__ alpha, const float* __restrict__ beta,
+                                                   int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                                   float* __restrict__ alpha_p, float* __restrict__ beta_p,
+                                                   const XT* __restrict__ x, XT* __restrict__ x_packed) {
+  __shared__ int32_t wave_tot[64][kTile / kWave];
+  __shared__ int32_t rows_s[kTile * 8];
+  const int tile = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = tile * kTile + threadIdx.x;
+  const bool valid = t < T;
+  const int64_t tok = (int64_t)b * T + (valid ? t : 0);
+  int mem[8], rank[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    mem[j] = (valid && j < K) ? idx[tok * K + j] : -1;
+    if ((unsigned)mem[j] >= (unsigned)M) mem[j] = -1;
+    rank[j] = 0;
+  }
+  const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int m = 0; m < M; ++m) {
+    bool f = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f |= (mem[j] == m);
+    const uint64_t bal = __ballot(f);
+    const int pre = __popcll(bal & lower);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (mem[j] == m) rank[j] = pre;
+    if (lane == 0) wave_tot[m][wv] = __popcll(bal);
+  }
+  __syncthreads();
+  const int64_t NR = (int64_t)B * T * K;
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < K && mem[j] >= 0) {
+        const int m = mem[j];
+        int r = rank[j];
+        for (int w2 = 0; w2 < wv; ++w2) r += wave_tot[m][w2];
+        const int32_t row = base[((int64_t)m * B + b) * ntile + tile] + r;
+        perm[row] = (int32_t)tok;
+        inv[tok * K + j] = row;
+        rows_s[threadIdx.x * 8 + j] = row;
+        for (int h = 0; h < H; ++h) {
+          const int64_t src = (tok * H + h) * (M + 1) + m;
+          alpha_p[(int64_t)row * H + h] = alpha[src];
+          beta_p[(int64_t)row * H + h] = beta[src];
+        }
+      }
+    }
+    const int64_t srow = NR + tok;
+    perm[srow] = (int32_t)tok;
+    for (int h = 0; h < H; ++h) {
+      const int64_t src = (tok * H + h) * (M + 1) + M;
+      alpha_p[srow * H + h] = alpha[src];
+      beta_p[srow * H + h] = beta[src];
+    }
+  }
+  if (x_packed == nullptr) return;
+  __syncthreads();
+  // gather x rows: one wave per (token, j), 16-byte lanes
+  const int n_valid = min(kTile, T - tile * kTile);
+  constexpr int kEl = 16 / (int)sizeof(XT);
+  for (int e = wv; e < n_valid * K; e += kTile / kWave) {
+    const int tt = e / K, j = e % K;
+    const int64_t src_tok = (int64_t)b * T + tile * kTile + tt;
+    const int32_t row = rows_s[tt * 8 + j];
+    const uint4* s = reinterpret_cast<const uint4*>(x + src_tok * D);
+    uint4* d = reinterpret_cast<uint4*>(x_packed + (int64_t)row * D);
+    for (int c = lane; c < D / kEl; c += kWave) d[c] = s[c];
+  }
+}
+
+}  // namespace mom
+
+extern "C" mom_status mom_dispatch(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
+                                   const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv,
+                                   void* x_packed, float* alpha_p, float* beta_p, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  using namespace mom;
+  mom_status s = check_dims(dims);
+  if (s != MOM_OK) return s;
+  MOM_CHECK_PTR(idx);
+  MOM_CHECK_PTR(alpha);
+  MOM_CHECK_PTR(beta);
+  MOM_CHECK_PTR(seg_off);
+  MOM_CHECK_PTR(perm);
+  MOM_CHECK_PTR(inv);
+  MOM_CHECK_PTR(alpha_p);
+  MOM_CHECK_PTR(beta_p);
+  MOM_CHECK_OPT_PTR(x_packed);
+  if (x_packed) MOM_CHECK_PTR(x);
+  const size_t need = mom_workspace_bytes(dims, MOM_WS_DISPATCH);
+  if (!ws || ws_bytes < need) return MOM_ERR_WORKSPACE;
+  MOM_CHECK_PTR(ws);
+  const mom_dims& d = *dims;
+  const int ntile = ceil_div(d.T, kTile);
+  if ((int64_t)ntile * d.B > 0x7fffffff / 2) return MOM_ERR_DIMS;
+  hipStream_t st = (hipStream_t)stream;
+  int32_t* cnt = (int32_t*)ws;
+  hipLaunchKernelGGL(k_count, dim3(ntile, d.B), dim3(kTile), 0, st, d.B, d.T, d.M, d.topk, ntile, idx, cnt);
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, d.B, d.T, d.M, d.topk, ntile, cnt, seg_off);
+  if (d.dtype == MOM_DTYPE_BF16)
+    hipLaunchKernelGGL(k_scatter<bf16_t>, dim3(ntile, d.B), dim3(kTile), 0, st, d.B, d.T, d.D, d.H, d.M, d.topk,
+                       ntile, idx, cnt, alpha, beta, perm, inv, alpha_p, beta_p, (const bf16_t*)x,
+                       (bf16_t*)x_packed);
+  else
+    hipLaunchKernelGGL(k_scatter<float>, dim3(ntile, d.B), dim3(kTile), 0, st, d.B, d.T, d.D, d.H, d.M, d.topk,
+                       ntile, idx, cnt, alpha, beta, perm, inv, alpha_p, beta_p, (const float*)x,
+                       (float*)x_packed);
+  return launch_status();
+}

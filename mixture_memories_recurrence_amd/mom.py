@@ -1,0 +1,218 @@
+"""Thin ctypes binding of libmom.so (argument marshalling only).
+
+Every function named like a C entry point takes torch tensors that already
+live on the GPU, passes their data pointers and the current HIP stream, and
+raises MomError on a non-zero status.  No arithmetic of the layer happens in
+Python: there is no CPU fallback, and a missing library raises at load time.
+
+``MomLayer`` strings the entry points together for one layer forward or one
+decode step, allocating its intermediates with torch (device memory only).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .synth import LayerConfig
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmom.so")
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+WS_DISPATCH, WS_CHUNK = 0, 1
+
+
+class MomError(RuntimeError):
+    pass
+
+
+class MomDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "T", "D", "H", "dk", "dv", "M", "topk", "chunk", "dtype")]
+
+
+_lib = None
+_VP = ctypes.c_void_p
+_I32 = ctypes.c_int32
+
+
+def lib():
+    """Load libmom.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise MomError("libmom.so is not built (%s); run mixture_memories_recurrence_amd.build" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    D = ctypes.POINTER(MomDims)
+    sigs = {
+        "mom_route": [D, _VP, _VP, _VP, _VP, _VP, _VP],
+        "mom_dispatch": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+        "mom_project": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+        "gdn_chunk_fwd": [D, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                          _VP, ctypes.c_size_t, _VP],
+        "gdn_decode_step": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+        "mom_combine": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP],
+        "mom_workspace_bytes": [D, _I32],
+        "mom_status_string": [_I32],
+    }
+    for name, args in sigs.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = _I32
+    L.mom_workspace_bytes.restype = ctypes.c_size_t
+    L.mom_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+EXPORTS = ("mom_route", "mom_dispatch", "mom_project", "gdn_chunk_fwd", "gdn_decode_step", "mom_combine",
+           "mom_workspace_bytes", "mom_status_string")
+
+
+def dims_of(cfg: LayerConfig, B: int | None = None, T: int | None = None) -> MomDims:
+    return MomDims(cfg.B if B is None else B, cfg.T if T is None else T, cfg.D, cfg.H, cfg.dk, cfg.dv, cfg.M,
+                   cfg.K, cfg.chunk, DTYPE_BF16 if cfg.dtype == "bf16" else DTYPE_F32)
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise MomError("tensor is not on the GPU")
+    if not t.is_contiguous():
+        raise MomError("tensor is not contiguous")
+    return _VP(t.data_ptr())
+
+
+def _s(stream):
+    return _VP(torch.cuda.current_stream().cuda_stream if stream is None else stream)
+
+
+def _check(status, name):
+    if status != 0:
+        msg = lib().mom_status_string(status).decode()
+        raise MomError("%s: %s (status %d)" % (name, msg, status))
+
+
+def mom_route(dims, x, w_r, bias, idx, w, stream=None):
+    _check(lib().mom_route(ctypes.byref(dims), _p(x), _p(w_r), _p(bias), _p(idx), _p(w), _s(stream)), "mom_route")
+
+
+def mom_dispatch(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_p, beta_p, ws, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().mom_dispatch(ctypes.byref(dims), _p(idx), _p(x), _p(alpha), _p(beta), _p(seg_off), _p(perm),
+                              _p(inv), _p(x_packed), _p(alpha_p), _p(beta_p), _p(ws), nbytes, _s(stream)),
+           "mom_dispatch")
+
+
+def mom_project(dims, x, perm, seg_off, w_q, w_k, w_v, q, k, v, stream=None):
+    _check(lib().mom_project(ctypes.byref(dims), _p(x), _p(perm), _p(seg_off), _p(w_q), _p(w_k), _p(w_v), _p(q),
+                             _p(k), _p(v), _s(stream)), "mom_project")
+
+
+def gdn_chunk_fwd(dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
+                  state_in, state_out, o, ws=None, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().gdn_chunk_fwd(ctypes.byref(dims), n_seg, n_rows, n_tok, n_state, _p(seg_off), _p(seg_state),
+                               _p(row_token), _p(q), _p(k), _p(v), _p(alpha_p), _p(beta_p), _p(state_in),
+                               _p(state_out), _p(o), _p(ws), nbytes, _s(stream)), "gdn_chunk_fwd")
+
+
+def gdn_decode_step(dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, stream=None):
+    _check(lib().gdn_decode_step(ctypes.byref(dims), n_seq, _p(idx), _p(inv), _p(q), _p(k), _p(v), _p(alpha),
+                                 _p(beta), _p(states), _p(o), _s(stream)), "gdn_decode_step")
+
+
+def mom_combine(dims, n_tok, inv, w, o_routed, o_shared, out, stream=None):
+    _check(lib().mom_combine(ctypes.byref(dims), n_tok, _p(inv), _p(w), _p(o_routed), _p(o_shared), _p(out),
+                             _s(stream)), "mom_combine")
+
+
+def mom_workspace_bytes(dims, which):
+    return int(lib().mom_workspace_bytes(ctypes.byref(dims), which))
+
+
+# ---------------------------------------------------------------- layer driver
+def storage_dtype(cfg):
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+def act_dtype(cfg):
+    """Storage of q/k/v between the projection and the recurrence."""
+    return torch.float16 if cfg.dtype == "bf16" else torch.float32
+
+
+class MomLayer:
+    """One MoM layer on the GPU: weights resident, intermediates allocated once
+    per (B, T).  forward() and decode_step() only enqueue library calls."""
+
+    def __init__(self, cfg: LayerConfig, w_r, bias, w_q, w_k, w_v, device="cuda"):
+        self.cfg = cfg
+        sd = storage_dtype(cfg)
+        t = lambda a, dt: None if a is None else torch.as_tensor(a).to(device=device, dtype=dt).contiguous()
+        self.w_r, self.w_q, self.w_k, self.w_v = t(w_r, sd), t(w_q, sd), t(w_k, sd), t(w_v, sd)
+        self.bias = t(bias, torch.float32)
+        self.device = device
+        self._bufs = {}
+
+    def buffers(self, B, T):
+        key = (B, T)
+        if key in self._bufs:
+            return self._bufs[key]
+        c, dev = self.cfg, self.device
+        NT = B * T
+        NR = NT * c.K
+        N = NR + NT
+        dims = dims_of(c, B, T)
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        ad = dict(dtype=act_dtype(c), device=dev)
+        ws = max(mom_workspace_bytes(dims, WS_DISPATCH), 256)
+        n_seg = (c.M + 1) * B
+        seg_state = torch.tensor([(s % B) * (c.M + 1) + s // B for s in range(n_seg)], **i32)
+        b = dict(
+            dims=dims, NT=NT, NR=NR, N=N, n_seg=n_seg, seg_state=seg_state,
+            idx=torch.empty(NT, c.K, **i32), w=torch.empty(NT, c.K, **f32),
+            seg_off=torch.empty(n_seg + 1, **i32), perm=torch.empty(N, **i32), inv=torch.empty(NT, c.K, **i32),
+            alpha_p=torch.empty(N, c.H, **f32), beta_p=torch.empty(N, c.H, **f32),
+            ws=torch.empty(ws, dtype=torch.uint8, device=dev),
+            q=torch.empty(NT, c.H, c.dk, **ad), k=torch.empty(N, c.H, c.dk, **ad), v=torch.empty(N, c.H, c.dv, **ad),
+            o=torch.empty(N, c.H, c.dv, **f32), out=torch.empty(NT, c.H, c.dv, **f32),
+        )
+        self._bufs[key] = b
+        return b
+
+    def route_dispatch_project(self, x, alpha, beta, b, stream=None):
+        c, d = self.cfg, b["dims"]
+        mom_route(d, x, self.w_r, self.bias, b["idx"], b["w"], stream)
+        mom_dispatch(d, b["idx"], x, alpha, beta, b["seg_off"], b["perm"], b["inv"], None, b["alpha_p"],
+                     b["beta_p"], b["ws"], stream)
+        mom_project(d, x, b["perm"], b["seg_off"], self.w_q, self.w_k, self.w_v, b["q"], b["k"], b["v"], stream)
+
+    def forward(self, x, alpha, beta, state_in=None, state_out=None, B=None, T=None, stream=None):
+        """x [B*T, D], alpha/beta [B*T, H, M+1]; state_in/out [B, M+1, H, dk, dv] fp32.
+        Returns (out [B*T, H, dv] fp32, state_out, buffers)."""
+        c = self.cfg
+        B = c.B if B is None else B
+        T = c.T if T is None else T
+        b = self.buffers(B, T)
+        if state_out is None:
+            state_out = torch.empty(B, c.M + 1, c.H, c.dk, c.dv, dtype=torch.float32, device=self.device)
+        self.route_dispatch_project(x, alpha, beta, b, stream)
+        gdn_chunk_fwd(b["dims"], b["n_seg"], b["N"], b["NT"], B * (c.M + 1), b["seg_off"], b["seg_state"], b["perm"],
+                      b["q"], b["k"], b["v"], b["alpha_p"], b["beta_p"], state_in, state_out, b["o"], None, stream)
+        mom_combine(b["dims"], b["NT"], b["inv"], b["w"], b["o"], b["o"][b["NR"]:], b["out"], stream)
+        return b["out"], state_out, b
+
+    def decode_step(self, x_t, alpha, beta, states, stream=None):
+        """One token for each of n_seq sequences: x_t [n_seq, D], alpha/beta
+        [n_seq, H, M+1], states [n_seq, M+1, H, dk, dv] updated in place."""
+        n_seq = x_t.shape[0]
+        b = self.buffers(n_seq, 1)
+        self.route_dispatch_project(x_t, alpha, beta, b, stream)
+        gdn_decode_step(b["dims"], n_seq, b["idx"], b["inv"], b["q"], b["k"], b["v"], alpha, beta, states, b["o"],
+                        stream)
+        mom_combine(b["dims"], n_seq, b["inv"], b["w"], b["o"], b["o"][b["NR"]:], b["out"], stream)
+        return b["out"], b

@@ -1,0 +1,99 @@
+"""The C ABI without a GPU: the library loads, exports every function the header
+declares, sizes its workspace, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+torch = pytest.importorskip("torch")
+from mixture_memories_recurrence_amd import mom  # noqa: E402
+from mixture_memories_recurrence_amd.synth import CONFIGS  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mom.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(mom.LIB_PATH), reason="libmom.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:mom_status|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(mom.EXPORTS)
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", mom.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for f in declared_functions():
+        assert f in exported, f
+    L = mom.lib()
+    for f in declared_functions():
+        assert getattr(L, f) is not None
+
+
+def _dims(**kw):
+    d = mom.dims_of(CONFIGS["l380m"])
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: every call below fails validation
+ODD = ctypes.c_void_p(0x10004)
+
+
+@needs_lib
+@pytest.mark.parametrize("field,value,status", [
+    ("dk", 96, -3), ("dv", 32, -3), ("chunk", 32, -3), ("D", 1000, -3), ("M", 65, -3), ("topk", 9, -3),
+    ("topk", 0, -2), ("B", 0, -2), ("T", -1, -2), ("dtype", 7, -3), ("topk", 5, -2)])
+def test_bad_dims_are_rejected(field, value, status):
+    d = _dims(**{field: value})
+    if field == "topk" and value == 9:
+        d.M = 16          # topk <= M, but above the supported 8
+    L = mom.lib()
+    assert L.mom_route(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, None) == status
+    assert L.mom_workspace_bytes(ctypes.byref(d), 0) == 0
+
+
+@needs_lib
+def test_null_and_alignment_are_rejected():
+    L = mom.lib()
+    d = _dims()
+    assert L.mom_route(None, FAKE, FAKE, None, FAKE, FAKE, None) == -1
+    assert L.mom_route(ctypes.byref(d), None, FAKE, None, FAKE, FAKE, None) == -1
+    assert L.mom_route(ctypes.byref(d), ODD, FAKE, None, FAKE, FAKE, None) == -4
+    assert L.mom_combine(ctypes.byref(d), 4, None, FAKE, FAKE, FAKE, None, None) == -1
+    assert L.mom_combine(ctypes.byref(d), -1, None, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert L.mom_project(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ODD, None) == -4
+    assert L.gdn_decode_step(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == -1
+    # chunk: n_state smaller than the segments with identity slots
+    assert L.gdn_chunk_fwd(ctypes.byref(d), 10, 10, 10, 3, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                           FAKE, FAKE, None, 0, None) == -2
+
+
+@needs_lib
+def test_dispatch_workspace_is_checked():
+    L = mom.lib()
+    d = _dims()
+    need = L.mom_workspace_bytes(ctypes.byref(d), 0)
+    ntile = -(-d.T // 256)
+    assert need >= d.M * d.B * ntile * 4 and need % 256 == 0
+    args = [FAKE] * 10
+    assert L.mom_dispatch(ctypes.byref(d), *args, None, need, None) == -5
+    assert L.mom_dispatch(ctypes.byref(d), *args, FAKE, need - 1, None) == -5
+    assert L.mom_workspace_bytes(ctypes.byref(d), 1) == 0
+
+
+@needs_lib
+def test_status_strings():
+    L = mom.lib()
+    for s in range(-6, 1):
+        assert L.mom_status_string(s).decode()
+    assert L.mom_status_string(-99).decode() == "unknown status"
