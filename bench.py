@@ -1,0 +1,226 @@
+"""Throughput of the MoM layer forward (and decode) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload l380m]
+
+A step is one whole layer forward on one batch of synthetic input: route,
+dispatch, projections, chunkwise recurrence, combine.  Inputs are resident in
+HBM before the timed region.  The JSON line also carries, for the slowest
+stage, its roofline position (HIP events around that stage's launches on the
+stream it runs on), the decode-step throughput of the long-context workload
+(256 sequences, one token each, float32 states resident), and the fp64 CPU
+checker timed on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0      # dense bf16 / fp16 matrix cores
+FP32_VALU_PEAK_TFLOPS = 157.3  # vector fp32 (packed); 78.6 without packed ops
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="l380m")
+    p.add_argument("--decode-steps", type=int, default=20)
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per launch of the slowest stage")
+    return p.parse_args()
+
+
+def stage_costs(cfg):
+    """Algorithmic bytes and flops of one launch of each stage for one layer
+    forward: every tensor read or written once at its stored width."""
+    NT = cfg.B * cfg.T
+    K, H, dk, dv, D, M, C = cfg.K, cfg.H, cfg.dk, cfg.dv, cfg.D, cfg.M, cfg.chunk
+    N = NT * (K + 1)
+    xb = 2 if cfg.dtype == "bf16" else 4
+    ab = 2 if cfg.dtype == "bf16" else 4  # q/k/v storage (half or float32)
+    n_state = cfg.B * (M + 1)
+    c = {}
+    c["route"] = dict(bytes=NT * (D * xb + 8 * K) + M * D * xb, flops=2 * NT * D * M)
+    c["dispatch"] = dict(bytes=NT * K * 4 * 3 + 2 * NT * H * (M + 1) * 4 + 2 * N * H * 4 + N * 4, flops=0)
+    proj_w = (H * dk + (M + 1) * H * (dk + dv)) * D * xb
+    c["project"] = dict(bytes=NT * D * xb * (K + 2) + proj_w + (NT * H * dk + N * H * (dk + dv)) * ab,
+                        flops=2 * D * (NT * H * dk + N * H * (dk + dv)))
+    chunk_flops_row = 6 * C * dk + 4 * C * dv + 6 * dk * dv + (2 * C * C) // 3
+    c["chunk"] = dict(bytes=N * H * (2 * dk * ab + dv * ab + 8 + dv * 4) + 2 * n_state * H * dk * dv * 4,
+                      flops=N * H * chunk_flops_row)
+    c["combine"] = dict(bytes=NT * H * dv * 4 * (K + 2) + NT * K * 8, flops=2 * NT * K * H * dv)
+    return c
+
+
+def decode_costs(cfg, n_seq):
+    K, H, dk, dv, D, M = cfg.K, cfg.H, cfg.dk, cfg.dv, cfg.D, cfg.M
+    state = 2 * n_seq * (K + 1) * H * dk * dv * 4
+    io = n_seq * (H * dk * 2 + (K + 1) * H * (dk + dv) * 2 + 2 * H * (M + 1) * 4 + (K + 1) * H * dv * 4)
+    return dict(bytes=state + io, flops=n_seq * (K + 1) * H * 6 * dk * dv)
+
+
+def time_cpu_baseline(cfg, inp):
+    """fp64 checker on a bounded sample: the first 2 sequences x 1024 tokens."""
+    from oracle import oracle
+    B, T = min(cfg.B, 2), min(cfg.T, 1024)
+    NT = B * T
+    sl = lambda a: a.reshape(cfg.B, cfg.T, *a.shape[1:])[:B, :T].reshape(NT, *a.shape[1:])
+    x, al, be = sl(inp["x"]), sl(inp["alpha"]), sl(inp["beta"])
+    oracle.lib()
+    t0 = time.perf_counter()
+    oracle.layer((B, T, cfg.D, cfg.H, cfg.dk, cfg.dv, cfg.M, cfg.K), x, inp["w_r"], inp["bias"], inp["w_q"],
+                 inp["w_k"], inp["w_v"], al, be)
+    dt = time.perf_counter() - t0
+    return {"value": NT / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": "fp64 checker, layer forward on the first %d sequences x %d tokens of the workload (%.1f s)"
+                      % (B, T, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mixture_memories_recurrence_amd import mom, synth
+
+    cfg = synth.CONFIGS[args.workload]
+    inp = synth.make_layer_inputs(cfg, seed=0)
+    layer = mom.MomLayer(cfg, inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"])
+    sd = mom.storage_dtype(cfg)
+    x = torch.from_numpy(inp["x"]).to(sd).cuda()
+    alpha = torch.from_numpy(inp["alpha"]).cuda()
+    beta = torch.from_numpy(inp["beta"]).cuda()
+    state = torch.empty(cfg.B, cfg.M + 1, cfg.H, cfg.dk, cfg.dv, dtype=torch.float32, device="cuda")
+    b = layer.buffers(cfg.B, cfg.T)
+    NT, N = b["NT"], b["N"]
+    stages = ["route", "dispatch", "project", "chunk", "combine"]
+
+    def step(ev=None):
+        d = b["dims"]
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        mom.mom_route(d, x, layer.w_r, layer.bias, b["idx"], b["w"])
+        rec(1)
+        mom.mom_dispatch(d, b["idx"], x, alpha, beta, b["seg_off"], b["perm"], b["inv"], None, b["alpha_p"],
+                         b["beta_p"], b["ws"])
+        rec(2)
+        mom.mom_project(d, x, b["perm"], b["seg_off"], layer.w_q, layer.w_k, layer.w_v, b["q"], b["k"], b["v"])
+        rec(3)
+        mom.gdn_chunk_fwd(d, b["n_seg"], N, NT, cfg.B * (cfg.M + 1), b["seg_off"], b["seg_state"], b["perm"],
+                          b["q"], b["k"], b["v"], b["alpha_p"], b["beta_p"], None, state, b["o"])
+        rec(4)
+        mom.mom_combine(d, NT, b["inv"], b["w"], b["o"], b["o"][b["NR"]:], b["out"])
+        rec(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st_ms = {s: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]))
+             for j, s in enumerate(stages)}
+    ms_per_step = wall * 1e3 / args.steps
+    value = NT / (wall / args.steps)
+
+    costs = stage_costs(cfg)
+    kern = {}
+    for s in stages:
+        t = st_ms[s] * 1e-3
+        kern[s] = {"ms": round(st_ms[s], 4), "GB/s": round(costs[s]["bytes"] / t / 1e9, 1),
+                   "TFLOP/s": round(costs[s]["flops"] / t / 1e12, 2),
+                   "hbm_frac": round(costs[s]["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
+                   "mfma_frac": round(costs[s]["flops"] / t / 1e12 / MFMA_PEAK_TFLOPS, 4)}
+    dom = max(stages, key=lambda s: st_ms[s])
+    t = st_ms[dom] * 1e-3
+    ai = costs[dom]["flops"] / max(costs[dom]["bytes"], 1)
+    if ai > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        ach, peak, unit, bound = costs[dom]["flops"] / t / 1e12, MFMA_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        ach, peak, unit, bound = costs[dom]["bytes"] / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        tr = json.load(open(args.traffic))
+        if tr.get("stage") == dom and tr.get("workload") == cfg.name:
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
+                "traffic": traffic, "kernel": dom, "algorithmic_bytes": costs[dom]["bytes"],
+                "algorithmic_flops": costs[dom]["flops"]}
+
+    res = {
+        "metric": "MoM layer fwd tokens/s (T=2048, M=4 top-2+shared) + decode tokens/s; % roofline",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": "%s: B=%d T=%d D=%d H=%d dk=%d dv=%d M=%d top-%d + shared, %s inputs, fp32 state"
+                               % (cfg.name, cfg.B, cfg.T, cfg.D, cfg.H, cfg.dk, cfg.dv, cfg.M, cfg.K, cfg.dtype),
+                   "tokens_per_step": NT, "chunk": cfg.chunk},
+        "roofline": roofline,
+        "stages": kern,
+    }
+
+    if not args.no_decode:
+        dcfg = synth.CONFIGS["long32k"]
+        n_seq = synth.DECODE_SEQS
+        dinp = synth.make_layer_inputs(dataclasses_replace(dcfg, B=1, T=1), seed=0)
+        dlayer = mom.MomLayer(dcfg, dinp["w_r"], dinp["bias"], dinp["w_q"], dinp["w_k"], dinp["w_v"])
+        states = torch.from_numpy(synth.make_state(dcfg, n_seq, seed=8)).cuda()
+        steps_in = []
+        for s in range(4):
+            d = synth.make_decode_step_inputs(dcfg, n_seq, seed=100 + s)
+            steps_in.append((torch.from_numpy(d["x"]).to(torch.bfloat16).cuda(), torch.from_numpy(d["alpha"]).cuda(),
+                             torch.from_numpy(d["beta"]).cuda()))
+        db = dlayer.buffers(n_seq, 1)
+        for i in range(3):
+            dlayer.decode_step(*steps_in[i % 4], states)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.decode_steps)]
+        t0 = time.perf_counter()
+        for i in range(args.decode_steps):
+            xx, aa, bb = steps_in[i % 4]
+            dlayer.route_dispatch_project(xx, aa, bb, db)
+            ev[i][0].record()
+            mom.gdn_decode_step(db["dims"], n_seq, db["idx"], db["inv"], db["q"], db["k"], db["v"], aa, bb, states,
+                                db["o"])
+            ev[i][1].record()
+            mom.mom_combine(db["dims"], n_seq, db["inv"], db["w"], db["o"], db["o"][db["NR"]:], db["out"])
+        torch.cuda.synchronize()
+        dwall = time.perf_counter() - t0
+        dk_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        dc = decode_costs(dcfg, n_seq)
+        res["decode"] = {"workload": "long32k decode: %d sequences x 1 token, D=%d H=%d dk=%d dv=%d M=%d top-%d, "
+                                     "fp32 states [%d,%d,%d,%d,%d] resident" % (n_seq, dcfg.D, dcfg.H, dcfg.dk, dcfg.dv,
+                                                                               dcfg.M, dcfg.K, n_seq, dcfg.M + 1,
+                                                                               dcfg.H, dcfg.dk, dcfg.dv),
+                         "tokens_per_s": round(n_seq * args.decode_steps / dwall, 1),
+                         "ms_per_step": round(dwall * 1e3 / args.decode_steps, 4),
+                         "decode_kernel_ms": round(dk_ms, 4),
+                         "decode_kernel_GB/s": round(dc["bytes"] / (dk_ms * 1e-3) / 1e9, 1),
+                         "decode_kernel_hbm_frac": round(dc["bytes"] / (dk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = time_cpu_baseline(cfg, inp)
+    print(json.dumps(res), flush=True)
+
+
+def dataclasses_replace(c, **kw):
+    import dataclasses
+    return dataclasses.replace(c, **kw)
+
+
+if __name__ == "__main__":
+    main()
