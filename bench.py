@@ -117,7 +117,7 @@ def main():
         mom.mom_project(d, x, b["perm"], b["seg_off"], layer.w_q, layer.w_k, layer.w_v, b["q"], b["k"], b["v"])
         rec(3)
         mom.gdn_chunk_fwd(d, b["n_seg"], N, NT, cfg.B * (cfg.M + 1), b["seg_off"], b["seg_state"], b["perm"],
-                          b["q"], b["k"], b["v"], b["alpha_p"], b["beta_p"], None, state, b["o"])
+                          b["q"], b["k"], b["v"], b["alpha_p"], b["beta_p"], None, state, b["o"], b["ws_chunk"])
         rec(4)
         mom.mom_combine(d, NT, b["inv"], b["w"], b["o"], b["o"][b["NR"]:], b["out"])
         rec(5)

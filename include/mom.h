@@ -145,8 +145,9 @@ mom_status mom_project(const mom_dims* dims, const void* x, const int32_t* perm,
  *             (an empty segment copies its state unchanged)
  *   o         [N][H][dv] float32: the read after each row's write
  * Preconditions: seg_off non-decreasing with seg_off[n_seg] <= n_rows,
- * row_token entries in [0, n_tok).  ws may be NULL when
- * mom_workspace_bytes(dims, MOM_WS_CHUNK) is 0.                              */
+ * row_token entries in [0, n_tok).  ws holds at least
+ * gdn_chunk_workspace_bytes(dims, n_seg, n_rows) bytes (may be NULL when that
+ * is 0); its contents on entry do not matter.                                */
 mom_status gdn_chunk_fwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
                          int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
                          const int32_t* row_token, const void* q, const void* k, const void* v,
@@ -175,8 +176,17 @@ mom_status mom_combine(const mom_dims* dims, int32_t n_tok, const int32_t* inv, 
                        const float* o_routed, const float* o_shared, float* out, void* stream);
 
 enum { MOM_WS_DISPATCH = 0, MOM_WS_CHUNK = 1 };
-/* Workspace bytes an entry point needs (0 = none); 0 for invalid dims. */
+/* Workspace bytes an entry point needs for the layer's own sizes (0 = none):
+ * MOM_WS_DISPATCH for mom_dispatch, MOM_WS_CHUNK for gdn_chunk_fwd over the
+ * layer's n_seg = (M+1)*B segments and N rows.  0 for invalid dims. */
 size_t mom_workspace_bytes(const mom_dims* dims, int32_t which);
+
+/* Workspace bytes gdn_chunk_fwd needs for n_seg segments over n_rows packed
+ * rows (0 = none: the float32 path keeps everything on chip).  The bfloat16
+ * path stores, per (chunk, head), the chunk's solved triangular factor and its
+ * masked, decayed query-key products (half) and the log-decay prefix sums
+ * (float32).  0 for invalid arguments. */
+size_t gdn_chunk_workspace_bytes(const mom_dims* dims, int32_t n_seg, int32_t n_rows);
 
 /* Static text for a status code. */
 const char* mom_status_string(int32_t status);

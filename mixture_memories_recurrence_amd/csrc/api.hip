@@ -9,7 +9,19 @@ mom_status launch_gdn_chunk_valu(const mom_dims& d, int n_seg, const int32_t* se
                                  const int32_t* row_token, const void* q, const void* k, const void* v,
                                  const float* alpha_p, const float* beta_p, const float* state_in, float* state_out,
                                  float* o, hipStream_t st);
+mom_status launch_gdn_chunk_mfma(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
+                                 const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
+                                 const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
+                                 float* state_out, float* o, void* ws, hipStream_t st);
+size_t gdn_chunk_ws_bytes(int64_t n_seg, int64_t n_rows, int H);
 }  // namespace mom
+
+extern "C" size_t gdn_chunk_workspace_bytes(const mom_dims* dims, int32_t n_seg, int32_t n_rows) {
+  using namespace mom;
+  if (check_dims(dims) != MOM_OK || n_seg < 0 || n_rows < 0) return 0;
+  if (dims->dtype != MOM_DTYPE_BF16) return 0;
+  return gdn_chunk_ws_bytes(n_seg, n_rows, dims->H);
+}
 
 extern "C" mom_status gdn_chunk_fwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
                                     int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
@@ -34,13 +46,14 @@ extern "C" mom_status gdn_chunk_fwd(const mom_dims* dims, int32_t n_seg, int32_t
     MOM_CHECK_PTR(beta_p);
     MOM_CHECK_PTR(o);
   }
-  const size_t need = mom_workspace_bytes(dims, MOM_WS_CHUNK);
+  const size_t need = gdn_chunk_workspace_bytes(dims, n_seg, n_rows);
   if (need && (!ws || ws_bytes < need)) return MOM_ERR_WORKSPACE;
+  MOM_CHECK_OPT_PTR(ws);
   if (n_seg == 0) return MOM_OK;
   hipStream_t st = (hipStream_t)stream;
   if (dims->dtype == MOM_DTYPE_BF16)
-    return launch_gdn_chunk_valu<f16_t>(*dims, n_seg, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
-                                        state_in, state_out, o, st);
+    return launch_gdn_chunk_mfma(*dims, n_seg, n_rows, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
+                                 state_in, state_out, o, ws, st);
   return launch_gdn_chunk_valu<float>(*dims, n_seg, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
                                       state_in, state_out, o, st);
 }
@@ -53,6 +66,10 @@ extern "C" size_t mom_workspace_bytes(const mom_dims* dims, int32_t which) {
     const int64_t ntile = (d.T + kDispatchTile - 1) / kDispatchTile;
     const int64_t bytes = (int64_t)d.M * d.B * ntile * 4;
     return (size_t)((bytes + 255) / 256 * 256);
+  }
+  if (which == MOM_WS_CHUNK) {
+    const Sizes z = sizes_of(d);
+    return gdn_chunk_workspace_bytes(dims, (int32_t)z.n_seg, (int32_t)z.N);
   }
   return 0;
 }

@@ -90,4 +90,14 @@ __device__ __forceinline__ T wave_sum_xor(T v) {
   return v;
 }
 
+// Workgroups are handed to the 8 XCDs round-robin (block p runs on XCD p % 8).
+// Map physical block p to a logical index so that each XCD receives one
+// contiguous range of logical work items: neighbours in logical order then
+// share that XCD's L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t p, int64_t G) {
+  const int64_t x = p & 7, i = p >> 3;
+  const int64_t per = G >> 3, rem = G & 7;
+  return x * per + (x < rem ? x : rem) + i;
+}
+
 }  // namespace mom

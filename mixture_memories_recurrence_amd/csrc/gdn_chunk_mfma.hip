@@ -1,0 +1,587 @@
+// Chunkwise Gated DeltaNet on the gfx950 matrix cores (half operands, float32
+// accumulation, float32 state).  This is the bfloat16-input path of
+// gdn_chunk_fwd.
+//
+// The recurrence of one memory (gist.science page, "Core mechanism": forget
+// then delta update, read after the write) is, per head,
+//   S_i = a_i S_{i-1} + k_i u_i^T,  u_i = c_i (v_i - a_i S_{i-1}^T k_i),  o_i = S_i^T q_i.
+// For a chunk of rows entering with state S, g_i = sum_{j<=i} log a_j and
+// gamma_i = e^{g_i}, unrolling gives the WY / UT form
+//   A_ij = c_i e^{g_i-g_j} k_i.k_j (j<i),   T = (I + A)^{-1} diag(c)
+//   W = T diag(gamma) K,   U~ = T V,   U = U~ - W S
+//   O = diag(gamma) Q S + P U,          P_ij = e^{g_i-g_j} q_i.k_j (j<=i)
+//   S <- gamma_L S + (diag(gamma_L / gamma) K)^T U
+// Only U, O and the new S depend on the entering state, so the work splits in
+// two launches:
+//   k_gdn_prep   fully parallel over (chunk, head): g, A and P from two MFMA
+//                products, then T by a blocked solve (16x16 diagonal blocks by
+//                forward substitution, off-diagonal blocks by block products),
+//                all in float32; T and P are stored as half, g as float32.
+//   k_gdn_chain  one block per (segment, head, 64 value columns); value
+//                columns of the state evolve independently.  It walks the
+//                segment's chunks in order with the state in MFMA accumulators
+//                (float32) and a half copy of S^T in LDS as the operand.
+// Every product is v_mfma_f32_16x16x32_f16 with both operands staged in LDS
+// with the contraction index contiguous.
+#include "common.h"
+
+namespace mom {
+
+constexpr int GC = 64;     // chunk rows
+constexpr int GDVB = 64;   // value columns per chain block
+constexpr int GLD = 72;    // LDS row stride (halfs) of 64-wide tiles
+
+__device__ __forceinline__ f32x4 mfma16(const half8& a, const half8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ half8 lds8(const f16_t* p) { return *reinterpret_cast<const half8*>(p); }
+
+// ------------------------------------------------------------------ chunk numbering
+// chunk_base[s] = number of chunks in segments before s; chunk_base[n_seg] = total.
+__global__ __launch_bounds__(1024) void k_chunk_base(int n_seg, const int32_t* __restrict__ seg_off,
+                                                     int32_t* __restrict__ chunk_base) {
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t carry_s;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (threadIdx.x == 0) carry_s = 0;
+  __syncthreads();
+  for (int base = 0; base < n_seg; base += 1024) {
+    const int i = base + threadIdx.x;
+    const int32_t v = i < n_seg ? (seg_off[i + 1] - seg_off[i] + GC - 1) / GC : 0;
+    int32_t s = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t u = __shfl_up(s, o, 64);
+      if (lane >= o) s += u;
+    }
+    if (lane == 63) wsum[wv] = s;
+    __syncthreads();
+    int32_t pre = carry_s;
+    for (int w2 = 0; w2 < wv; ++w2) pre += wsum[w2];
+    if (i < n_seg) chunk_base[i] = pre + s - v;
+    __syncthreads();
+    if (threadIdx.x == 1023) carry_s = pre + s;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) chunk_base[n_seg] = carry_s;
+}
+
+// ------------------------------------------------------------------ prep
+template <int DK>
+__global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_t* __restrict__ seg_off,
+                                                  const int32_t* __restrict__ chunk_base,
+                                                  const int32_t* __restrict__ row_token, const f16_t* __restrict__ q,
+                                                  const f16_t* __restrict__ k, const float* __restrict__ alpha_p,
+                                                  const float* __restrict__ beta_p, f16_t* __restrict__ Tws,
+                                                  f16_t* __restrict__ Tgws, f16_t* __restrict__ Pws,
+                                                  float* __restrict__ Gws) {
+  constexpr int KLD = DK + 8;
+  __shared__ __attribute__((aligned(16))) f16_t Ks[GC * KLD];
+  __shared__ __attribute__((aligned(16))) f16_t Qs[GC * KLD];
+  __shared__ float As[GC][GC + 1];
+  __shared__ float Xs[GC][GC + 1];
+  __shared__ float Ys[3][16][17];
+  __shared__ float gs[GC], bs[GC];
+
+  const int h = blockIdx.x % H;
+  const int c = blockIdx.x / H;
+  const int total = chunk_base[n_seg];
+  if (c >= total) return;
+  // segment of chunk c: the last s with chunk_base[s] <= c
+  int lo = 0, hi = n_seg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (chunk_base[mid] <= c) lo = mid;
+    else hi = mid - 1;
+  }
+  const int s = lo;
+  const int64_t r0 = seg_off[s] + (int64_t)(c - chunk_base[s]) * GC;
+  const int L = (int)min((int64_t)GC, (int64_t)seg_off[s + 1] - r0);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+
+  // K and Q rows of the chunk (zero past L)
+  constexpr int CPR = DK / 8;  // 16-byte pieces per row
+  for (int e = tid; e < GC * CPR; e += 256) {
+    const int i = e / CPR, p = (e % CPR) * 8;
+    uint4 kv = {0, 0, 0, 0}, qv = {0, 0, 0, 0};
+    if (i < L) {
+      const int64_t row = r0 + i;
+      const int64_t tk = row_token ? (int64_t)row_token[row] : row;
+      kv = *reinterpret_cast<const uint4*>(k + (row * H + h) * DK + p);
+      qv = *reinterpret_cast<const uint4*>(q + (tk * H + h) * DK + p);
+    }
+    *reinterpret_cast<uint4*>(Ks + i * KLD + p) = kv;
+    *reinterpret_cast<uint4*>(Qs + i * KLD + p) = qv;
+  }
+  if (w == 0) {
+    float la = 0.f, bb = 0.f;
+    if (lane < L) {
+      la = logf(alpha_p[(r0 + lane) * H + h]);
+      bb = beta_p[(r0 + lane) * H + h];
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float u = __shfl_up(la, o, 64);
+      if (lane >= o) la += u;
+    }
+    gs[lane] = la;
+    bs[lane] = bb;
+  }
+  __syncthreads();
+
+  // wave w: row block w of K K^T and Q K^T (column blocks jb <= w)
+  const int64_t ch = (int64_t)c * H + h;
+  f16_t* Pout = Pws + ch * GC * GC;
+  for (int jb = 0; jb < 4; ++jb) {
+    f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+    if (jb <= w) {
+#pragma unroll
+      for (int d0 = 0; d0 < DK; d0 += 32) {
+        const int off = d0 + 8 * (lane >> 4);
+        const half8 ka = lds8(Ks + (16 * w + (lane & 15)) * KLD + off);
+        const half8 qa = lds8(Qs + (16 * w + (lane & 15)) * KLD + off);
+        const half8 kb = lds8(Ks + (16 * jb + (lane & 15)) * KLD + off);
+        kk = mfma16(ka, kb, kk);
+        qk = mfma16(qa, kb, qk);
+      }
+    }
+    const int j = 16 * jb + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * w + 4 * (lane >> 4) + r;
+      float a = 0.f, p = 0.f;
+      if (j <= i) {
+        const float dec = expf(gs[i] - gs[j]);
+        if (j < i) a = bs[i] * dec * kk[r];
+        p = dec * qk[r];
+      }
+      As[i][j] = a;
+      Pout[i * GC + j] = (f16_t)p;
+    }
+  }
+  __syncthreads();
+
+  // X = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution, one lane
+  // per (block, column)
+  if (tid < 64) {
+    const int bb = tid >> 4, cc = tid & 15;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+      for (int t = 0; t < r; ++t) v = fmaf(-As[16 * bb + r][16 * bb + t], x[t], v);
+      x[r] = v;
+      Xs[16 * bb + r][16 * bb + cc] = v;
+    }
+  }
+  __syncthreads();
+  // off-diagonal blocks, one block-diagonal at a time:
+  //   X_ij = -X_ii * sum_{t=j}^{i-1} A_it X_tj
+  for (int dist = 1; dist < 4; ++dist) {
+    const int nblk = 4 - dist;
+    const int r = tid >> 4, cc = tid & 15;
+    for (int bI = 0; bI < nblk; ++bI) {
+      const int ib = bI + dist, jb = bI;
+      float acc = 0.f;
+      for (int t = 16 * jb; t < 16 * ib; ++t) acc = fmaf(As[16 * ib + r][t], Xs[t][16 * jb + cc], acc);
+      Ys[bI][r][cc] = acc;
+    }
+    __syncthreads();
+    for (int bI = 0; bI < nblk; ++bI) {
+      const int ib = bI + dist, jb = bI;
+      float acc = 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc = fmaf(Xs[16 * ib + r][16 * ib + u], Ys[bI][u][cc], acc);
+      Xs[16 * ib + r][16 * jb + cc] = -acc;
+    }
+    __syncthreads();
+  }
+  // T = X diag(beta) and T diag(gamma), lower block triangle; zero above
+  f16_t* Tout = Tws + ch * GC * GC;
+  f16_t* Tgout = Tgws + ch * GC * GC;
+  for (int e = tid; e < GC * GC; e += 256) {
+    const int i = e / GC, j = e % GC;
+    const bool lower = (j >> 4) < (i >> 4) || ((j >> 4) == (i >> 4) && j <= i);
+    const float t = lower ? Xs[i][j] * bs[j] : 0.f;
+    Tout[e] = (f16_t)t;
+    Tgout[e] = (f16_t)(t * expf(gs[j]));
+  }
+  if (tid < GC) Gws[ch * GC + tid] = gs[tid];
+}
+
+// ------------------------------------------------------------------ chain
+// Barrier for LDS hand-offs only: waits for this wave's LDS operations, not for
+// its global loads, so prefetches stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Wave-local LDS hand-off: rows written by this wave are read back by this wave.
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint4 zero_if(bool z, uint4 v) {
+  return z ? uint4{0u, 0u, 0u, 0u} : v;
+}
+
+template <int DK, bool GATHER>
+__global__ __launch_bounds__(256) void k_gdn_chain(int H, int dv, int n_seg, const int32_t* __restrict__ seg_off,
+                                                   const int32_t* __restrict__ seg_state,
+                                                   const int32_t* __restrict__ chunk_base,
+                                                   const int32_t* __restrict__ row_token, const f16_t* __restrict__ q,
+                                                   const f16_t* __restrict__ k, const f16_t* __restrict__ v,
+                                                   const f16_t* __restrict__ Tws, const f16_t* __restrict__ Tgws,
+                                                   const f16_t* __restrict__ Pws, const float* __restrict__ Gws,
+                                                   const float* __restrict__ state_in, float* __restrict__ state_out,
+                                                   float* __restrict__ o) {
+  constexpr int KLD = DK + 8;
+  constexpr int NDB = DK / 16;          // 16-row blocks of the state
+  constexpr int SDB = NDB / 4;          // state row blocks per wave
+  constexpr int KIT = DK / 64;          // pair-transposed K pieces per thread
+  constexpr int QPR = DK / 8;           // 16-byte pieces per Q row
+  constexpr int QIT = GC * QPR / 256;   // Q pieces per thread
+  constexpr int ND = DK / 32;           // contraction steps over d
+  __shared__ __attribute__((aligned(16))) f16_t KT[DK * GLD];     // K^T  [d][j]
+  __shared__ __attribute__((aligned(16))) f16_t Qh[GC * KLD];     // Q    [i][d]
+  __shared__ __attribute__((aligned(16))) f16_t VT[GDVB * GLD];   // V^T  [n][j]
+  __shared__ __attribute__((aligned(16))) f16_t Th[GC * GLD];     // T    [i][j]
+  __shared__ __attribute__((aligned(16))) f16_t Tg[GC * GLD];     // T diag(gamma)
+  __shared__ __attribute__((aligned(16))) f16_t Ph[GC * GLD];     // P    [i][j]
+  __shared__ __attribute__((aligned(16))) f16_t ST[GDVB * KLD];   // S^T  [n][d]
+  __shared__ __attribute__((aligned(16))) f16_t Wh[GC * KLD];     // W    [i][d]
+  __shared__ __attribute__((aligned(16))) f16_t UT[GDVB * GLD];   // U^T  [n][j]
+  __shared__ __attribute__((aligned(16))) f16_t UT2[GDVB * GLD];  // (diag(gamma_L/gamma) U)^T
+  __shared__ float eg[GC], egl[GC];                               // gamma_i, gamma_L / gamma_i
+
+  const int nb = dv / GDVB;
+  const int64_t Lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int cb = (int)(Lid % nb);
+  const int h = (int)((Lid / nb) % H);
+  const int s = n_seg - 1 - (int)(Lid / ((int64_t)nb * H));  // last segments (shared memory, longest) first
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int ip = tid & 31, pg = tid >> 5;  // row pair and 8-column group of the transposed loads
+  const int slot = seg_state ? seg_state[s] : s;
+  const int64_t sbase = ((int64_t)slot * H + h) * DK * dv + cb * GDVB;
+  const int64_t rbeg = seg_off[s], rend = seg_off[s + 1];
+  const int cbase = chunk_base[s];
+  const int qi0 = tid / QPR, qp = (tid % QPR) * 8;  // Q piece it covers row qi0 + (256/QPR)*it
+
+  // ---- registers of the next chunk's inputs (loaded during the current chunk)
+  uint4 rk0[KIT], rk1[KIT], rq[QIT], rv0, rv1, rt[2], rtg[2], rp[2];
+  int32_t rtok[QIT];
+  float rg = 0.f;
+  auto prefetch_a = [&](int64_t r0) {  // everything but the gathered queries
+    const int L = (int)min((int64_t)GC, rend - r0);
+    const int64_t ch = (int64_t)(cbase + (r0 - rbeg) / GC) * H + h;
+    const int64_t ra = r0 + min(2 * ip, L - 1), rb = r0 + min(2 * ip + 1, L - 1);
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int p = 8 * pg + 64 * it;
+      rk0[it] = *reinterpret_cast<const uint4*>(k + (ra * H + h) * DK + p);
+      rk1[it] = *reinterpret_cast<const uint4*>(k + (rb * H + h) * DK + p);
+    }
+    rv0 = *reinterpret_cast<const uint4*>(v + (ra * H + h) * dv + cb * GDVB + 8 * pg);
+    rv1 = *reinterpret_cast<const uint4*>(v + (rb * H + h) * dv + cb * GDVB + 8 * pg);
+#pragma unroll
+    for (int it = 0; it < QIT; ++it) {
+      const int64_t row = r0 + min(qi0 + (256 / QPR) * it, L - 1);
+      rtok[it] = GATHER ? row_token[row] : (int32_t)row;
+    }
+    const uint4* tsrc = reinterpret_cast<const uint4*>(Tws + ch * GC * GC);
+    const uint4* tgsrc = reinterpret_cast<const uint4*>(Tgws + ch * GC * GC);
+    const uint4* psrc = reinterpret_cast<const uint4*>(Pws + ch * GC * GC);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      rt[it] = tsrc[tid + 256 * it];
+      rtg[it] = tgsrc[tid + 256 * it];
+      rp[it] = psrc[tid + 256 * it];
+    }
+    rg = Gws[ch * GC + (tid & (GC - 1))];
+  };
+  auto prefetch_b = [&]() {  // gathered queries, once the row tokens are in
+#pragma unroll
+    for (int it = 0; it < QIT; ++it)
+      rq[it] = *reinterpret_cast<const uint4*>(q + ((int64_t)rtok[it] * H + h) * DK + qp);
+  };
+  auto stage = [&](int L) {
+    const bool z0 = 2 * ip >= L, z1 = 2 * ip + 1 >= L;
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int p = 8 * pg + 64 * it;
+      const uint4 a4 = zero_if(z0, rk0[it]), b4 = zero_if(z1, rk1[it]);
+      const f16_t* a = reinterpret_cast<const f16_t*>(&a4);
+      const f16_t* b = reinterpret_cast<const f16_t*>(&b4);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        __attribute__((ext_vector_type(2))) _Float16 pr = {a[t], b[t]};
+        *reinterpret_cast<decltype(pr)*>(KT + (p + t) * GLD + 2 * ip) = pr;
+      }
+    }
+    {
+      const uint4 a4 = zero_if(z0, rv0), b4 = zero_if(z1, rv1);
+      const f16_t* a = reinterpret_cast<const f16_t*>(&a4);
+      const f16_t* b = reinterpret_cast<const f16_t*>(&b4);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        __attribute__((ext_vector_type(2))) _Float16 pr = {a[t], b[t]};
+        *reinterpret_cast<decltype(pr)*>(VT + (8 * pg + t) * GLD + 2 * ip) = pr;
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < QIT; ++it) {
+      const int i = qi0 + (256 / QPR) * it;
+      *reinterpret_cast<uint4*>(Qh + i * KLD + qp) = zero_if(i >= L, rq[it]);
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int e = tid + 256 * it;
+      const int i = e >> 3, p = (e & 7) * 8;
+      *reinterpret_cast<uint4*>(Th + i * GLD + p) = rt[it];
+      *reinterpret_cast<uint4*>(Tg + i * GLD + p) = rtg[it];
+      *reinterpret_cast<uint4*>(Ph + i * GLD + p) = rp[it];
+    }
+    if (tid < GC) {
+      const float gl = __shfl(rg, GC - 1, 64);
+      eg[tid] = expf(rg);
+      egl[tid] = expf(gl - rg);
+    }
+  };
+
+  // state accumulators: wave w owns state rows [16*SDB*w, 16*SDB*(w+1)), all 64 columns
+  f32x4 S[SDB][4];
+  if (state_in) {
+#pragma unroll
+    for (int a = 0; a < SDB; ++a)
+#pragma unroll
+      for (int nbk = 0; nbk < 4; ++nbk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = 16 * (SDB * w + a) + 4 * lg + r;
+          S[a][nbk][r] = state_in[sbase + (int64_t)d * dv + 16 * nbk + l16];
+        }
+  } else {
+#pragma unroll
+    for (int a = 0; a < SDB; ++a)
+#pragma unroll
+      for (int nbk = 0; nbk < 4; ++nbk) S[a][nbk] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+  auto write_st = [&]() {
+#pragma unroll
+    for (int a = 0; a < SDB; ++a)
+#pragma unroll
+      for (int nbk = 0; nbk < 4; ++nbk) {
+        const int d = 16 * (SDB * w + a) + 4 * lg;
+        half4 hv = {(f16_t)S[a][nbk][0], (f16_t)S[a][nbk][1], (f16_t)S[a][nbk][2], (f16_t)S[a][nbk][3]};
+        *reinterpret_cast<half4*>(ST + (16 * nbk + l16) * KLD + d) = hv;
+      }
+  };
+  write_st();
+  if (rbeg < rend) {
+    prefetch_a(rbeg);
+    prefetch_b();
+  }
+  // The loads for the next chunk are issued unconditionally (the last chunk
+  // reloads itself), so they land straight in the registers staged next.
+
+  const int arow = 16 * w + l16;
+  for (int64_t r0 = rbeg; r0 < rend; r0 += GC) {
+    const int L = (int)min((int64_t)GC, rend - r0);
+    const bool more = r0 + GC < rend;
+    lds_barrier();  // previous chunk done with every LDS tile; ST written
+    stage(L);
+    lds_barrier();
+    prefetch_a(more ? r0 + GC : r0);  // in flight during this chunk's products
+
+    // ---- W = T diag(gamma) K for row block w (only this wave reads these rows back)
+    {
+      const half8 ta0 = lds8(Tg + arow * GLD + 8 * lg), ta1 = lds8(Tg + arow * GLD + 32 + 8 * lg);
+#pragma unroll
+      for (int db0 = 0; db0 < NDB; db0 += 4) {
+        half8 kb[4][2];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          kb[x][0] = lds8(KT + (16 * (db0 + x) + l16) * GLD + 8 * lg);
+          kb[x][1] = lds8(KT + (16 * (db0 + x) + l16) * GLD + 32 + 8 * lg);
+        }
+        f32x4 acc[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) acc[x] = mfma16(ta0, kb[x][0], (f32x4){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int x = 0; x < 4; ++x) acc[x] = mfma16(ta1, kb[x][1], acc[x]);
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Wh[(16 * w + 4 * lg + r) * KLD + 16 * (db0 + x) + l16] = (f16_t)acc[x][r];
+      }
+    }
+    prefetch_b();
+    wave_lds_fence();
+    // ---- U~ = T V, Q S and W S (sharing the S^T operand), then U and U^T
+    f32x4 U[4], O[4];
+    {
+      half8 qa[ND], wa[ND];
+#pragma unroll
+      for (int d0 = 0; d0 < ND; ++d0) {
+        qa[d0] = lds8(Qh + arow * KLD + 32 * d0 + 8 * lg);
+        wa[d0] = lds8(Wh + arow * KLD + 32 * d0 + 8 * lg);
+      }
+      const half8 t0 = lds8(Th + arow * GLD + 8 * lg), t1 = lds8(Th + arow * GLD + 32 + 8 * lg);
+      float gi[4], gli[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        gi[r] = eg[16 * w + 4 * lg + r];
+        gli[r] = egl[16 * w + 4 * lg + r];
+      }
+#pragma unroll
+      for (int nbk = 0; nbk < 4; ++nbk) {
+        half8 sb[ND];
+#pragma unroll
+        for (int d0 = 0; d0 < ND; ++d0) sb[d0] = lds8(ST + (16 * nbk + l16) * KLD + 32 * d0 + 8 * lg);
+        const half8 vb0 = lds8(VT + (16 * nbk + l16) * GLD + 8 * lg);
+        const half8 vb1 = lds8(VT + (16 * nbk + l16) * GLD + 32 + 8 * lg);
+        f32x4 ut = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f}, ws = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int d0 = 0; d0 < ND; ++d0) {
+          qs = mfma16(qa[d0], sb[d0], qs);
+          ws = mfma16(wa[d0], sb[d0], ws);
+        }
+        ut = mfma16(t0, vb0, ut);
+        ut = mfma16(t1, vb1, ut);
+        half4 u1, u2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float u = ut[r] - ws[r];
+          U[nbk][r] = u;
+          O[nbk][r] = qs[r] * gi[r];
+          u1[r] = (f16_t)u;
+          u2[r] = (f16_t)(u * gli[r]);
+        }
+        *reinterpret_cast<half4*>(UT + (16 * nbk + l16) * GLD + 16 * w + 4 * lg) = u1;
+        *reinterpret_cast<half4*>(UT2 + (16 * nbk + l16) * GLD + 16 * w + 4 * lg) = u2;
+      }
+    }
+    lds_barrier();
+    // ---- O += P U (store), S <- gamma_L S + K^T U'
+    {
+      const half8 p0 = lds8(Ph + arow * GLD + 8 * lg), p1 = lds8(Ph + arow * GLD + 32 + 8 * lg);
+      half8 ub[4][2];
+#pragma unroll
+      for (int nbk = 0; nbk < 4; ++nbk) {
+        ub[nbk][0] = lds8(UT + (16 * nbk + l16) * GLD + 8 * lg);
+        ub[nbk][1] = lds8(UT + (16 * nbk + l16) * GLD + 32 + 8 * lg);
+      }
+#pragma unroll
+      for (int nbk = 0; nbk < 4; ++nbk) O[nbk] = mfma16(p0, ub[nbk][0], O[nbk]);
+#pragma unroll
+      for (int nbk = 0; nbk < 4; ++nbk) O[nbk] = mfma16(p1, ub[nbk][1], O[nbk]);
+#pragma unroll
+      for (int nbk = 0; nbk < 4; ++nbk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * w + 4 * lg + r;
+          if (i < L) o[((r0 + i) * H + h) * dv + cb * GDVB + 16 * nbk + l16] = O[nbk][r];
+        }
+    }
+    {
+      const float eL = eg[GC - 1];
+      half8 u2b[4][2];
+#pragma unroll
+      for (int nbk = 0; nbk < 4; ++nbk) {
+        u2b[nbk][0] = lds8(UT2 + (16 * nbk + l16) * GLD + 8 * lg);
+        u2b[nbk][1] = lds8(UT2 + (16 * nbk + l16) * GLD + 32 + 8 * lg);
+      }
+#pragma unroll
+      for (int a = 0; a < SDB; ++a) {
+        const int drow = 16 * (SDB * w + a) + l16;
+        const half8 k0 = lds8(KT + drow * GLD + 8 * lg), k1 = lds8(KT + drow * GLD + 32 + 8 * lg);
+#pragma unroll
+        for (int nbk = 0; nbk < 4; ++nbk) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S[a][nbk][r] *= eL;
+          S[a][nbk] = mfma16(k0, u2b[nbk][0], S[a][nbk]);
+        }
+#pragma unroll
+        for (int nbk = 0; nbk < 4; ++nbk) S[a][nbk] = mfma16(k1, u2b[nbk][1], S[a][nbk]);
+      }
+    }
+    write_st();  // ST is no longer read in this chunk
+  }
+#pragma unroll
+  for (int a = 0; a < SDB; ++a)
+#pragma unroll
+    for (int nbk = 0; nbk < 4; ++nbk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = 16 * (SDB * w + a) + 4 * lg + r;
+        state_out[sbase + (int64_t)d * dv + 16 * nbk + l16] = S[a][nbk][r];
+      }
+}
+
+// ------------------------------------------------------------------ workspace + launch
+struct ChunkWs {
+  int32_t* chunk_base;
+  f16_t* T;
+  f16_t* Tg;
+  f16_t* P;
+  float* G;
+  size_t bytes;
+};
+
+inline ChunkWs chunk_ws_layout(void* base, int64_t n_seg, int64_t n_rows, int H) {
+  const int64_t nch = n_rows / GC + n_seg;  // bound on the number of chunks
+  ChunkWs w;
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    const size_t o = off;
+    off += (b + 255) / 256 * 256;
+    return o;
+  };
+  const size_t o_cb = take((size_t)(n_seg + 1) * 4);
+  const size_t o_t = take((size_t)nch * H * GC * GC * 2);
+  const size_t o_tg = take((size_t)nch * H * GC * GC * 2);
+  const size_t o_p = take((size_t)nch * H * GC * GC * 2);
+  const size_t o_g = take((size_t)nch * H * GC * 4);
+  char* b = (char*)base;
+  w.chunk_base = (int32_t*)(b + o_cb);
+  w.T = (f16_t*)(b + o_t);
+  w.Tg = (f16_t*)(b + o_tg);
+  w.P = (f16_t*)(b + o_p);
+  w.G = (float*)(b + o_g);
+  w.bytes = off;
+  return w;
+}
+
+size_t gdn_chunk_ws_bytes(int64_t n_seg, int64_t n_rows, int H) {
+  return chunk_ws_layout(nullptr, n_seg, n_rows, H).bytes;
+}
+
+mom_status launch_gdn_chunk_mfma(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
+                                 const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
+                                 const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
+                                 float* state_out, float* o, void* ws, hipStream_t st) {
+  const ChunkWs W = chunk_ws_layout(ws, n_seg, n_rows, d.H);
+  const int64_t nch = (int64_t)n_rows / GC + n_seg;
+  hipLaunchKernelGGL(k_chunk_base, dim3(1), dim3(1024), 0, st, n_seg, seg_off, W.chunk_base);
+  const int64_t prep_blocks = nch * d.H;
+  const int64_t chain_blocks = (int64_t)n_seg * d.H * (d.dv / GDVB);
+#define MOM_MFMA_CASE(DK)                                                                                          \
+  do {                                                                                                             \
+    if (prep_blocks > 0)                                                                                           \
+      hipLaunchKernelGGL((k_gdn_prep<DK>), dim3((unsigned)prep_blocks), dim3(256), 0, st, d.H, n_seg, seg_off,     \
+                         W.chunk_base, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.Tg, W.P,  \
+                         W.G);                                                                                     \
+    if (row_token)                                                                                                 \
+      hipLaunchKernelGGL((k_gdn_chain<DK, true>), dim3((unsigned)chain_blocks), dim3(256), 0, st, d.H, d.dv, n_seg, \
+                         seg_off, seg_state, W.chunk_base, row_token, (const f16_t*)q, (const f16_t*)k,             \
+                         (const f16_t*)v, W.T, W.Tg, W.P, W.G, state_in, state_out, o);                             \
+    else                                                                                                           \
+      hipLaunchKernelGGL((k_gdn_chain<DK, false>), dim3((unsigned)chain_blocks), dim3(256), 0, st, d.H, d.dv,      \
+                         n_seg, seg_off, seg_state, W.chunk_base, row_token, (const f16_t*)q, (const f16_t*)k,      \
+                         (const f16_t*)v, W.T, W.Tg, W.P, W.G, state_in, state_out, o);                             \
+  } while (0)
+  if (d.dk == 64) MOM_MFMA_CASE(64);
+  else MOM_MFMA_CASE(128);
+#undef MOM_MFMA_CASE
+  return launch_status();
+}
+
+}  // namespace mom

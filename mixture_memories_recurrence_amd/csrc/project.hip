@@ -74,12 +74,6 @@ __device__ TileJob decode_tile(int64_t L, int64_t NT, int M, int B, int HK, int 
   return j;
 }
 
-// Physical block -> logical tile: XCD x = p % 8 gets the x-th contiguous slice.
-__device__ __forceinline__ int64_t xcd_remap(int64_t p, int64_t G) {
-  const int64_t x = p & 7, i = p >> 3;
-  const int64_t per = G >> 3, rem = G & 7;
-  return x * per + (x < rem ? x : rem) + i;
-}
 
 inline int64_t n_tiles_bound(const mom_dims& d, int BM, int BN) {
   const Sizes s = sizes_of(d);

@@ -55,6 +55,7 @@ def lib():
         "gdn_decode_step": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
         "mom_combine": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP],
         "mom_workspace_bytes": [D, _I32],
+        "gdn_chunk_workspace_bytes": [D, _I32, _I32],
         "mom_status_string": [_I32],
     }
     for name, args in sigs.items():
@@ -62,13 +63,14 @@ def lib():
         f.argtypes = args
         f.restype = _I32
     L.mom_workspace_bytes.restype = ctypes.c_size_t
+    L.gdn_chunk_workspace_bytes.restype = ctypes.c_size_t
     L.mom_status_string.restype = ctypes.c_char_p
     _lib = L
     return L
 
 
 EXPORTS = ("mom_route", "mom_dispatch", "mom_project", "gdn_chunk_fwd", "gdn_decode_step", "mom_combine",
-           "mom_workspace_bytes", "mom_status_string")
+           "mom_workspace_bytes", "gdn_chunk_workspace_bytes", "mom_status_string")
 
 
 def dims_of(cfg: LayerConfig, B: int | None = None, T: int | None = None) -> MomDims:
@@ -134,6 +136,16 @@ def mom_workspace_bytes(dims, which):
     return int(lib().mom_workspace_bytes(ctypes.byref(dims), which))
 
 
+def gdn_chunk_workspace_bytes(dims, n_seg, n_rows):
+    return int(lib().gdn_chunk_workspace_bytes(ctypes.byref(dims), n_seg, n_rows))
+
+
+def chunk_workspace(dims, n_seg, n_rows, device="cuda"):
+    """A device buffer large enough for gdn_chunk_fwd (None when none is needed)."""
+    n = gdn_chunk_workspace_bytes(dims, n_seg, n_rows)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 # ---------------------------------------------------------------- layer driver
 def storage_dtype(cfg):
     return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -178,6 +190,7 @@ class MomLayer:
             seg_off=torch.empty(n_seg + 1, **i32), perm=torch.empty(N, **i32), inv=torch.empty(NT, c.K, **i32),
             alpha_p=torch.empty(N, c.H, **f32), beta_p=torch.empty(N, c.H, **f32),
             ws=torch.empty(ws, dtype=torch.uint8, device=dev),
+            ws_chunk=chunk_workspace(dims, n_seg, N, dev),
             q=torch.empty(NT, c.H, c.dk, **ad), k=torch.empty(N, c.H, c.dk, **ad), v=torch.empty(N, c.H, c.dv, **ad),
             o=torch.empty(N, c.H, c.dv, **f32), out=torch.empty(NT, c.H, c.dv, **f32),
         )
@@ -202,7 +215,8 @@ class MomLayer:
             state_out = torch.empty(B, c.M + 1, c.H, c.dk, c.dv, dtype=torch.float32, device=self.device)
         self.route_dispatch_project(x, alpha, beta, b, stream)
         gdn_chunk_fwd(b["dims"], b["n_seg"], b["N"], b["NT"], B * (c.M + 1), b["seg_off"], b["seg_state"], b["perm"],
-                      b["q"], b["k"], b["v"], b["alpha_p"], b["beta_p"], state_in, state_out, b["o"], None, stream)
+                      b["q"], b["k"], b["v"], b["alpha_p"], b["beta_p"], state_in, state_out, b["o"], b["ws_chunk"],
+                      stream)
         mom_combine(b["dims"], b["NT"], b["inv"], b["w"], b["o"], b["o"][b["NR"]:], b["out"], stream)
         return b["out"], state_out, b
 

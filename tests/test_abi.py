@@ -88,7 +88,6 @@ def test_dispatch_workspace_is_checked():
     args = [FAKE] * 10
     assert L.mom_dispatch(ctypes.byref(d), *args, None, need, None) == -5
     assert L.mom_dispatch(ctypes.byref(d), *args, FAKE, need - 1, None) == -5
-    assert L.mom_workspace_bytes(ctypes.byref(d), 1) == 0
 
 
 @needs_lib
@@ -97,3 +96,20 @@ def test_status_strings():
     for s in range(-6, 1):
         assert L.mom_status_string(s).decode()
     assert L.mom_status_string(-99).decode() == "unknown status"
+
+
+@needs_lib
+def test_chunk_workspace_sizes():
+    L = mom.lib()
+    d = _dims()
+    n_seg, n_rows = (d.M + 1) * d.B, d.B * d.T * (d.topk + 1)
+    need = L.gdn_chunk_workspace_bytes(ctypes.byref(d), n_seg, n_rows)
+    n_chunks = n_rows // 64 + n_seg
+    assert need >= n_chunks * d.H * (64 * 64 * 2 * 2 + 64 * 4) and need % 256 == 0
+    assert L.mom_workspace_bytes(ctypes.byref(d), 1) == need
+    assert L.gdn_chunk_workspace_bytes(ctypes.byref(d), -1, n_rows) == 0
+    # missing workspace is refused before any launch
+    assert L.gdn_chunk_fwd(ctypes.byref(d), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, FAKE, FAKE, FAKE,
+                           FAKE, FAKE, None, FAKE, FAKE, None, 0, None) == -5
+    d32 = _dims(dtype=0)
+    assert L.gdn_chunk_workspace_bytes(ctypes.byref(d32), n_seg, n_rows) == 0

@@ -198,9 +198,11 @@ def test_chunk_segments(store, dk, dv):
     so = torch.full((n_state, H, dk, dv), float("nan"), device="cuda")
     o = torch.full((N, H, dv), float("nan"), device="cuda")
     log("chunk", store, dk, dv)
-    mom.gdn_chunk_fwd(mom.dims_of(cfg), n_seg, N, n_tok, n_state, to_gpu(seg_off), to_gpu(seg_state),
+    dims = mom.dims_of(cfg)
+    mom.gdn_chunk_fwd(dims, n_seg, N, n_tok, n_state, to_gpu(seg_off), to_gpu(seg_state),
                       to_gpu(row_token), to_gpu(qtok, ad), to_gpu(ch["k"], ad), to_gpu(ch["v"], ad),
-                      to_gpu(ch["alpha"]), to_gpu(ch["beta"]), to_gpu(S0), so, o)
+                      to_gpu(ch["alpha"]), to_gpu(ch["beta"]), to_gpu(S0), so, o,
+                      mom.chunk_workspace(dims, n_seg, N))
     torch.cuda.synchronize()
     st = S0.astype(np.float64).copy()
     o_ref = oracle.segments(seg_off, seg_state, row_token, qtok, ch["k"], ch["v"], ch["alpha"], ch["beta"], st)
@@ -228,10 +230,12 @@ def test_chunk_in_place_and_zero_state():
     st0 = torch.zeros(2, H, dk, dv, device="cuda")
     o1 = torch.empty(N, H, dv, device="cuda")
     s1 = torch.empty(2, H, dk, dv, device="cuda")
-    mom.gdn_chunk_fwd(mom.dims_of(cfg), 2, N, N, 2, to_gpu(seg_off), None, None, *args, None, s1, o1)
+    dims = mom.dims_of(cfg)
+    ws = mom.chunk_workspace(dims, 2, N)
+    mom.gdn_chunk_fwd(dims, 2, N, N, 2, to_gpu(seg_off), None, None, *args, None, s1, o1, ws)
     # in place from an explicit zero state
     o2 = torch.empty(N, H, dv, device="cuda")
-    mom.gdn_chunk_fwd(mom.dims_of(cfg), 2, N, N, 2, to_gpu(seg_off), None, None, *args, st0, st0, o2)
+    mom.gdn_chunk_fwd(dims, 2, N, N, 2, to_gpu(seg_off), None, None, *args, st0, st0, o2, ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, st0)
 
