@@ -73,8 +73,7 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
                                                   const int32_t* __restrict__ row_token, const f16_t* __restrict__ q,
                                                   const f16_t* __restrict__ k, const float* __restrict__ alpha_p,
                                                   const float* __restrict__ beta_p, f16_t* __restrict__ Tws,
-                                                  f16_t* __restrict__ Tgws, f16_t* __restrict__ Pws,
-                                                  float* __restrict__ Gws) {
+                                                  f16_t* __restrict__ Pws, float* __restrict__ Gws) {
   constexpr int KLD = DK + 8;
   __shared__ __attribute__((aligned(16))) f16_t Ks[GC * KLD];
   __shared__ __attribute__((aligned(16))) f16_t Qs[GC * KLD];
@@ -197,15 +196,12 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
     }
     __syncthreads();
   }
-  // T = X diag(beta) and T diag(gamma), lower block triangle; zero above
+  // T = X diag(beta), lower block triangle; zero above
   f16_t* Tout = Tws + ch * GC * GC;
-  f16_t* Tgout = Tgws + ch * GC * GC;
   for (int e = tid; e < GC * GC; e += 256) {
     const int i = e / GC, j = e % GC;
     const bool lower = (j >> 4) < (i >> 4) || ((j >> 4) == (i >> 4) && j <= i);
-    const float t = lower ? Xs[i][j] * bs[j] : 0.f;
-    Tout[e] = (f16_t)t;
-    Tgout[e] = (f16_t)(t * expf(gs[j]));
+    Tout[e] = (f16_t)(lower ? Xs[i][j] * bs[j] : 0.f);
   }
   if (tid < GC) Gws[ch * GC + tid] = gs[tid];
 }
@@ -222,80 +218,97 @@ __device__ __forceinline__ uint4 zero_if(bool z, uint4 v) {
   return z ? uint4{0u, 0u, 0u, 0u} : v;
 }
 
+constexpr int CHAIN_THREADS = 512;  // 8 waves: wave w owns row block w & 3 and column half w >> 2
+
 template <int DK, bool GATHER>
-__global__ __launch_bounds__(256) void k_gdn_chain(int H, int dv, int n_seg, const int32_t* __restrict__ seg_off,
-                                                   const int32_t* __restrict__ seg_state,
-                                                   const int32_t* __restrict__ chunk_base,
-                                                   const int32_t* __restrict__ row_token, const f16_t* __restrict__ q,
-                                                   const f16_t* __restrict__ k, const f16_t* __restrict__ v,
-                                                   const f16_t* __restrict__ Tws, const f16_t* __restrict__ Tgws,
-                                                   const f16_t* __restrict__ Pws, const float* __restrict__ Gws,
-                                                   const float* __restrict__ state_in, float* __restrict__ state_out,
-                                                   float* __restrict__ o) {
+__global__ __launch_bounds__(CHAIN_THREADS) void k_gdn_chain(
+    int H, int dv, int n_seg, const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_state,
+    const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ row_token, const f16_t* __restrict__ q,
+    const f16_t* __restrict__ k, const f16_t* __restrict__ v, const f16_t* __restrict__ Tws,
+    const f16_t* __restrict__ Pws, const float* __restrict__ Gws, const float* __restrict__ state_in,
+    float* __restrict__ state_out, float* __restrict__ o) {
+  constexpr int NT = CHAIN_THREADS;
   constexpr int KLD = DK + 8;
-  constexpr int NDB = DK / 16;          // 16-row blocks of the state
+  constexpr int NDB = DK / 16;          // 16-row blocks of the state / 16-column blocks of W
   constexpr int SDB = NDB / 4;          // state row blocks per wave
-  constexpr int KIT = DK / 64;          // pair-transposed K pieces per thread
+  constexpr int WDB = NDB / 2;          // W column blocks per wave
   constexpr int QPR = DK / 8;           // 16-byte pieces per Q row
-  constexpr int QIT = GC * QPR / 256;   // Q pieces per thread
+  constexpr int QIT = GC * QPR / NT;    // Q pieces per thread
   constexpr int ND = DK / 32;           // contraction steps over d
   __shared__ __attribute__((aligned(16))) f16_t KT[DK * GLD];     // K^T  [d][j]
   __shared__ __attribute__((aligned(16))) f16_t Qh[GC * KLD];     // Q    [i][d]
   __shared__ __attribute__((aligned(16))) f16_t VT[GDVB * GLD];   // V^T  [n][j]
   __shared__ __attribute__((aligned(16))) f16_t Th[GC * GLD];     // T    [i][j]
-  __shared__ __attribute__((aligned(16))) f16_t Tg[GC * GLD];     // T diag(gamma)
   __shared__ __attribute__((aligned(16))) f16_t Ph[GC * GLD];     // P    [i][j]
   __shared__ __attribute__((aligned(16))) f16_t ST[GDVB * KLD];   // S^T  [n][d]
   __shared__ __attribute__((aligned(16))) f16_t Wh[GC * KLD];     // W    [i][d]
   __shared__ __attribute__((aligned(16))) f16_t UT[GDVB * GLD];   // U^T  [n][j]
   __shared__ __attribute__((aligned(16))) f16_t UT2[GDVB * GLD];  // (diag(gamma_L/gamma) U)^T
-  __shared__ float eg[GC], egl[GC];                               // gamma_i, gamma_L / gamma_i
+  __shared__ __attribute__((aligned(16))) float eg[GC];           // gamma_i
+  __shared__ float egl[GC];                                       // gamma_L / gamma_i
 
+  // Work items are (segment, head) groups of nb column blocks.  Block p runs on
+  // XCD p % 8.  The first 8*floor(groups/8) groups are dealt round-robin over
+  // the XCDs, each group's nb blocks on one XCD one after another (they read
+  // the same K, Q, T, P through that XCD's L2); the remaining groups follow in
+  // plain order.  Groups are numbered from the last segment (the shared
+  // memory's, the longest) backwards, so long chains start first everywhere.
   const int nb = dv / GDVB;
-  const int64_t Lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int cb = (int)(Lid % nb);
-  const int h = (int)((Lid / nb) % H);
-  const int s = n_seg - 1 - (int)(Lid / ((int64_t)nb * H));  // last segments (shared memory, longest) first
+  const int64_t p = blockIdx.x;
+  const int64_t n_grp = (int64_t)n_seg * H;
+  const int64_t full = (n_grp / 8) * 8;
+  int64_t grp;
+  int cb;
+  if (p < full * nb) {
+    const int64_t xi = p & 7, ii = p >> 3;
+    grp = (ii / nb) * 8 + xi;
+    cb = (int)(ii % nb);
+  } else {
+    const int64_t r = p - full * nb;
+    grp = full + r / nb;
+    cb = (int)(r % nb);
+  }
+  const int h = (int)(grp % H);
+  const int s = n_seg - 1 - (int)(grp / H);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rb = w & 3, chh = w >> 2;   // row block, column half
   const int l16 = lane & 15, lg = lane >> 4;
-  const int ip = tid & 31, pg = tid >> 5;  // row pair and 8-column group of the transposed loads
+  const int ip = tid & 31, pg = tid >> 5;  // row pair and 8-column group of the transposed loads (pg < 16)
   const int slot = seg_state ? seg_state[s] : s;
   const int64_t sbase = ((int64_t)slot * H + h) * DK * dv + cb * GDVB;
   const int64_t rbeg = seg_off[s], rend = seg_off[s + 1];
   const int cbase = chunk_base[s];
-  const int qi0 = tid / QPR, qp = (tid % QPR) * 8;  // Q piece it covers row qi0 + (256/QPR)*it
+  const int qi0 = tid / QPR, qp = (tid % QPR) * 8;  // Q piece: row qi0 + (NT/QPR)*it
 
   // ---- registers of the next chunk's inputs (loaded during the current chunk)
-  uint4 rk0[KIT], rk1[KIT], rq[QIT], rv0, rv1, rt[2], rtg[2], rp[2];
+  constexpr int KPI = (DK / 8 + 15) / 16;  // K column groups per thread
+  uint4 rk0[KPI], rk1[KPI], rq[QIT], rv0, rv1, rt, rp;
   int32_t rtok[QIT];
   float rg = 0.f;
   auto prefetch_a = [&](int64_t r0) {  // everything but the gathered queries
     const int L = (int)min((int64_t)GC, rend - r0);
-    const int64_t ch = (int64_t)(cbase + (r0 - rbeg) / GC) * H + h;
-    const int64_t ra = r0 + min(2 * ip, L - 1), rb = r0 + min(2 * ip + 1, L - 1);
+    const int64_t chk = (int64_t)(cbase + (r0 - rbeg) / GC) * H + h;
+    const int64_t ra = r0 + min(2 * ip, L - 1), rbr = r0 + min(2 * ip + 1, L - 1);
 #pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-      const int p = 8 * pg + 64 * it;
-      rk0[it] = *reinterpret_cast<const uint4*>(k + (ra * H + h) * DK + p);
-      rk1[it] = *reinterpret_cast<const uint4*>(k + (rb * H + h) * DK + p);
+    for (int it = 0; it < KPI; ++it) {
+      const int p = 8 * (pg + 16 * it);
+      if (p < DK) {
+        rk0[it] = *reinterpret_cast<const uint4*>(k + (ra * H + h) * DK + p);
+        rk1[it] = *reinterpret_cast<const uint4*>(k + (rbr * H + h) * DK + p);
+      }
     }
-    rv0 = *reinterpret_cast<const uint4*>(v + (ra * H + h) * dv + cb * GDVB + 8 * pg);
-    rv1 = *reinterpret_cast<const uint4*>(v + (rb * H + h) * dv + cb * GDVB + 8 * pg);
+    if (pg < GDVB / 8) {
+      rv0 = *reinterpret_cast<const uint4*>(v + (ra * H + h) * dv + cb * GDVB + 8 * pg);
+      rv1 = *reinterpret_cast<const uint4*>(v + (rbr * H + h) * dv + cb * GDVB + 8 * pg);
+    }
 #pragma unroll
     for (int it = 0; it < QIT; ++it) {
-      const int64_t row = r0 + min(qi0 + (256 / QPR) * it, L - 1);
+      const int64_t row = r0 + min(qi0 + (NT / QPR) * it, L - 1);
       rtok[it] = GATHER ? row_token[row] : (int32_t)row;
     }
-    const uint4* tsrc = reinterpret_cast<const uint4*>(Tws + ch * GC * GC);
-    const uint4* tgsrc = reinterpret_cast<const uint4*>(Tgws + ch * GC * GC);
-    const uint4* psrc = reinterpret_cast<const uint4*>(Pws + ch * GC * GC);
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      rt[it] = tsrc[tid + 256 * it];
-      rtg[it] = tgsrc[tid + 256 * it];
-      rp[it] = psrc[tid + 256 * it];
-    }
-    rg = Gws[ch * GC + (tid & (GC - 1))];
+    rt = reinterpret_cast<const uint4*>(Tws + chk * GC * GC)[tid];
+    rp = reinterpret_cast<const uint4*>(Pws + chk * GC * GC)[tid];
+    rg = Gws[chk * GC + (tid & (GC - 1))];
   };
   auto prefetch_b = [&]() {  // gathered queries, once the row tokens are in
 #pragma unroll
@@ -305,18 +318,20 @@ __global__ __launch_bounds__(256) void k_gdn_chain(int H, int dv, int n_seg, con
   auto stage = [&](int L) {
     const bool z0 = 2 * ip >= L, z1 = 2 * ip + 1 >= L;
 #pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-      const int p = 8 * pg + 64 * it;
-      const uint4 a4 = zero_if(z0, rk0[it]), b4 = zero_if(z1, rk1[it]);
-      const f16_t* a = reinterpret_cast<const f16_t*>(&a4);
-      const f16_t* b = reinterpret_cast<const f16_t*>(&b4);
+    for (int it = 0; it < KPI; ++it) {
+      const int p = 8 * (pg + 16 * it);
+      if (p < DK) {
+        const uint4 a4 = zero_if(z0, rk0[it]), b4 = zero_if(z1, rk1[it]);
+        const f16_t* a = reinterpret_cast<const f16_t*>(&a4);
+        const f16_t* b = reinterpret_cast<const f16_t*>(&b4);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        __attribute__((ext_vector_type(2))) _Float16 pr = {a[t], b[t]};
-        *reinterpret_cast<decltype(pr)*>(KT + (p + t) * GLD + 2 * ip) = pr;
+        for (int t = 0; t < 8; ++t) {
+          __attribute__((ext_vector_type(2))) _Float16 pr = {a[t], b[t]};
+          *reinterpret_cast<decltype(pr)*>(KT + (p + t) * GLD + 2 * ip) = pr;
+        }
       }
     }
-    {
+    if (pg < GDVB / 8) {
       const uint4 a4 = zero_if(z0, rv0), b4 = zero_if(z1, rv1);
       const f16_t* a = reinterpret_cast<const f16_t*>(&a4);
       const f16_t* b = reinterpret_cast<const f16_t*>(&b4);
@@ -328,16 +343,13 @@ __global__ __launch_bounds__(256) void k_gdn_chain(int H, int dv, int n_seg, con
     }
 #pragma unroll
     for (int it = 0; it < QIT; ++it) {
-      const int i = qi0 + (256 / QPR) * it;
+      const int i = qi0 + (NT / QPR) * it;
       *reinterpret_cast<uint4*>(Qh + i * KLD + qp) = zero_if(i >= L, rq[it]);
     }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int e = tid + 256 * it;
-      const int i = e >> 3, p = (e & 7) * 8;
-      *reinterpret_cast<uint4*>(Th + i * GLD + p) = rt[it];
-      *reinterpret_cast<uint4*>(Tg + i * GLD + p) = rtg[it];
-      *reinterpret_cast<uint4*>(Ph + i * GLD + p) = rp[it];
+    {
+      const int i = tid >> 3, p = (tid & 7) * 8;
+      *reinterpret_cast<uint4*>(Th + i * GLD + p) = rt;
+      *reinterpret_cast<uint4*>(Ph + i * GLD + p) = rp;
     }
     if (tid < GC) {
       const float gl = __shfl(rg, GC - 1, 64);
@@ -346,32 +358,32 @@ __global__ __launch_bounds__(256) void k_gdn_chain(int H, int dv, int n_seg, con
     }
   };
 
-  // state accumulators: wave w owns state rows [16*SDB*w, 16*SDB*(w+1)), all 64 columns
-  f32x4 S[SDB][4];
+  // state accumulators: wave owns state rows [16*SDB*rb, +16*SDB) and column blocks 2*chh, 2*chh+1
+  f32x4 S[SDB][2];
   if (state_in) {
 #pragma unroll
     for (int a = 0; a < SDB; ++a)
 #pragma unroll
-      for (int nbk = 0; nbk < 4; ++nbk)
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int d = 16 * (SDB * w + a) + 4 * lg + r;
-          S[a][nbk][r] = state_in[sbase + (int64_t)d * dv + 16 * nbk + l16];
+          const int d = 16 * (SDB * rb + a) + 4 * lg + r;
+          S[a][c][r] = state_in[sbase + (int64_t)d * dv + 16 * (2 * chh + c) + l16];
         }
   } else {
 #pragma unroll
     for (int a = 0; a < SDB; ++a)
 #pragma unroll
-      for (int nbk = 0; nbk < 4; ++nbk) S[a][nbk] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < 2; ++c) S[a][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   auto write_st = [&]() {
 #pragma unroll
     for (int a = 0; a < SDB; ++a)
 #pragma unroll
-      for (int nbk = 0; nbk < 4; ++nbk) {
-        const int d = 16 * (SDB * w + a) + 4 * lg;
-        half4 hv = {(f16_t)S[a][nbk][0], (f16_t)S[a][nbk][1], (f16_t)S[a][nbk][2], (f16_t)S[a][nbk][3]};
-        *reinterpret_cast<half4*>(ST + (16 * nbk + l16) * KLD + d) = hv;
+      for (int c = 0; c < 2; ++c) {
+        const int d = 16 * (SDB * rb + a) + 4 * lg;
+        half4 hv = {(f16_t)S[a][c][0], (f16_t)S[a][c][1], (f16_t)S[a][c][2], (f16_t)S[a][c][3]};
+        *reinterpret_cast<half4*>(ST + (16 * (2 * chh + c) + l16) * KLD + d) = hv;
       }
   };
   write_st();
@@ -382,7 +394,7 @@ __global__ __launch_bounds__(256) void k_gdn_chain(int H, int dv, int n_seg, con
   // The loads for the next chunk are issued unconditionally (the last chunk
   // reloads itself), so they land straight in the registers staged next.
 
-  const int arow = 16 * w + l16;
+  const int arow = 16 * rb + l16;
   for (int64_t r0 = rbeg; r0 < rend; r0 += GC) {
     const int L = (int)min((int64_t)GC, rend - r0);
     const bool more = r0 + GC < rend;
@@ -391,32 +403,39 @@ __global__ __launch_bounds__(256) void k_gdn_chain(int H, int dv, int n_seg, con
     lds_barrier();
     prefetch_a(more ? r0 + GC : r0);  // in flight during this chunk's products
 
-    // ---- W = T diag(gamma) K for row block w (only this wave reads these rows back)
+    // ---- W = T diag(gamma) K: row block rb, column blocks [WDB*chh, WDB*(chh+1))
     {
-      const half8 ta0 = lds8(Tg + arow * GLD + 8 * lg), ta1 = lds8(Tg + arow * GLD + 32 + 8 * lg);
+      half8 ta[2];
 #pragma unroll
-      for (int db0 = 0; db0 < NDB; db0 += 4) {
-        half8 kb[4][2];
+      for (int x = 0; x < 2; ++x) {
+        const half8 t8 = lds8(Th + arow * GLD + 32 * x + 8 * lg);
+        const float4 g0 = *reinterpret_cast<const float4*>(eg + 32 * x + 8 * lg);
+        const float4 g1 = *reinterpret_cast<const float4*>(eg + 32 * x + 8 * lg + 4);
+        const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          kb[x][0] = lds8(KT + (16 * (db0 + x) + l16) * GLD + 8 * lg);
-          kb[x][1] = lds8(KT + (16 * (db0 + x) + l16) * GLD + 32 + 8 * lg);
-        }
-        f32x4 acc[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) acc[x] = mfma16(ta0, kb[x][0], (f32x4){0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int x = 0; x < 4; ++x) acc[x] = mfma16(ta1, kb[x][1], acc[x]);
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) Wh[(16 * w + 4 * lg + r) * KLD + 16 * (db0 + x) + l16] = (f16_t)acc[x][r];
+        for (int t = 0; t < 8; ++t) ta[x][t] = (f16_t)((float)t8[t] * gg[t]);
       }
+      half8 kb[WDB][2];
+#pragma unroll
+      for (int y = 0; y < WDB; ++y) {
+        const int db = WDB * chh + y;
+        kb[y][0] = lds8(KT + (16 * db + l16) * GLD + 8 * lg);
+        kb[y][1] = lds8(KT + (16 * db + l16) * GLD + 32 + 8 * lg);
+      }
+      f32x4 acc[WDB];
+#pragma unroll
+      for (int y = 0; y < WDB; ++y) acc[y] = mfma16(ta[0], kb[y][0], (f32x4){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int y = 0; y < WDB; ++y) acc[y] = mfma16(ta[1], kb[y][1], acc[y]);
+#pragma unroll
+      for (int y = 0; y < WDB; ++y)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Wh[(16 * rb + 4 * lg + r) * KLD + 16 * (WDB * chh + y) + l16] = (f16_t)acc[y][r];
     }
     prefetch_b();
-    wave_lds_fence();
+    lds_barrier();  // W rows come from two waves
     // ---- U~ = T V, Q S and W S (sharing the S^T operand), then U and U^T
-    f32x4 U[4], O[4];
+    f32x4 O[2];
     {
       half8 qa[ND], wa[ND];
 #pragma unroll
@@ -425,94 +444,107 @@ __global__ __launch_bounds__(256) void k_gdn_chain(int H, int dv, int n_seg, con
         wa[d0] = lds8(Wh + arow * KLD + 32 * d0 + 8 * lg);
       }
       const half8 t0 = lds8(Th + arow * GLD + 8 * lg), t1 = lds8(Th + arow * GLD + 32 + 8 * lg);
+      half8 sb[2][ND], vb[2][2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int nbk = 2 * chh + c;
+#pragma unroll
+        for (int d0 = 0; d0 < ND; ++d0) sb[c][d0] = lds8(ST + (16 * nbk + l16) * KLD + 32 * d0 + 8 * lg);
+        vb[c][0] = lds8(VT + (16 * nbk + l16) * GLD + 8 * lg);
+        vb[c][1] = lds8(VT + (16 * nbk + l16) * GLD + 32 + 8 * lg);
+      }
       float gi[4], gli[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        gi[r] = eg[16 * w + 4 * lg + r];
-        gli[r] = egl[16 * w + 4 * lg + r];
+        gi[r] = eg[16 * rb + 4 * lg + r];
+        gli[r] = egl[16 * rb + 4 * lg + r];
+      }
+      f32x4 ut[2], qs[2], ws[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        ut[c] = mfma16(t0, vb[c][0], (f32x4){0.f, 0.f, 0.f, 0.f});
+        qs[c] = mfma16(qa[0], sb[c][0], (f32x4){0.f, 0.f, 0.f, 0.f});
+        ws[c] = mfma16(wa[0], sb[c][0], (f32x4){0.f, 0.f, 0.f, 0.f});
       }
 #pragma unroll
-      for (int nbk = 0; nbk < 4; ++nbk) {
-        half8 sb[ND];
+      for (int d0 = 1; d0 < ND; ++d0)
 #pragma unroll
-        for (int d0 = 0; d0 < ND; ++d0) sb[d0] = lds8(ST + (16 * nbk + l16) * KLD + 32 * d0 + 8 * lg);
-        const half8 vb0 = lds8(VT + (16 * nbk + l16) * GLD + 8 * lg);
-        const half8 vb1 = lds8(VT + (16 * nbk + l16) * GLD + 32 + 8 * lg);
-        f32x4 ut = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f}, ws = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int d0 = 0; d0 < ND; ++d0) {
-          qs = mfma16(qa[d0], sb[d0], qs);
-          ws = mfma16(wa[d0], sb[d0], ws);
+        for (int c = 0; c < 2; ++c) {
+          qs[c] = mfma16(qa[d0], sb[c][d0], qs[c]);
+          ws[c] = mfma16(wa[d0], sb[c][d0], ws[c]);
         }
-        ut = mfma16(t0, vb0, ut);
-        ut = mfma16(t1, vb1, ut);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) ut[c] = mfma16(t1, vb[c][1], ut[c]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int nbk = 2 * chh + c;
         half4 u1, u2;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float u = ut[r] - ws[r];
-          U[nbk][r] = u;
-          O[nbk][r] = qs[r] * gi[r];
+          const float u = ut[c][r] - ws[c][r];
+          O[c][r] = qs[c][r] * gi[r];
           u1[r] = (f16_t)u;
           u2[r] = (f16_t)(u * gli[r]);
         }
-        *reinterpret_cast<half4*>(UT + (16 * nbk + l16) * GLD + 16 * w + 4 * lg) = u1;
-        *reinterpret_cast<half4*>(UT2 + (16 * nbk + l16) * GLD + 16 * w + 4 * lg) = u2;
+        *reinterpret_cast<half4*>(UT + (16 * nbk + l16) * GLD + 16 * rb + 4 * lg) = u1;
+        *reinterpret_cast<half4*>(UT2 + (16 * nbk + l16) * GLD + 16 * rb + 4 * lg) = u2;
       }
     }
     lds_barrier();
     // ---- O += P U (store), S <- gamma_L S + K^T U'
     {
       const half8 p0 = lds8(Ph + arow * GLD + 8 * lg), p1 = lds8(Ph + arow * GLD + 32 + 8 * lg);
-      half8 ub[4][2];
+      half8 ub[2][2], u2b[2][2];
 #pragma unroll
-      for (int nbk = 0; nbk < 4; ++nbk) {
-        ub[nbk][0] = lds8(UT + (16 * nbk + l16) * GLD + 8 * lg);
-        ub[nbk][1] = lds8(UT + (16 * nbk + l16) * GLD + 32 + 8 * lg);
+      for (int c = 0; c < 2; ++c) {
+        const int nbk = 2 * chh + c;
+        ub[c][0] = lds8(UT + (16 * nbk + l16) * GLD + 8 * lg);
+        ub[c][1] = lds8(UT + (16 * nbk + l16) * GLD + 32 + 8 * lg);
+        u2b[c][0] = lds8(UT2 + (16 * nbk + l16) * GLD + 8 * lg);
+        u2b[c][1] = lds8(UT2 + (16 * nbk + l16) * GLD + 32 + 8 * lg);
       }
-#pragma unroll
-      for (int nbk = 0; nbk < 4; ++nbk) O[nbk] = mfma16(p0, ub[nbk][0], O[nbk]);
-#pragma unroll
-      for (int nbk = 0; nbk < 4; ++nbk) O[nbk] = mfma16(p1, ub[nbk][1], O[nbk]);
-#pragma unroll
-      for (int nbk = 0; nbk < 4; ++nbk)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * w + 4 * lg + r;
-          if (i < L) o[((r0 + i) * H + h) * dv + cb * GDVB + 16 * nbk + l16] = O[nbk][r];
-        }
-    }
-    {
-      const float eL = eg[GC - 1];
-      half8 u2b[4][2];
-#pragma unroll
-      for (int nbk = 0; nbk < 4; ++nbk) {
-        u2b[nbk][0] = lds8(UT2 + (16 * nbk + l16) * GLD + 8 * lg);
-        u2b[nbk][1] = lds8(UT2 + (16 * nbk + l16) * GLD + 32 + 8 * lg);
-      }
+      half8 ka[SDB][2];
 #pragma unroll
       for (int a = 0; a < SDB; ++a) {
-        const int drow = 16 * (SDB * w + a) + l16;
-        const half8 k0 = lds8(KT + drow * GLD + 8 * lg), k1 = lds8(KT + drow * GLD + 32 + 8 * lg);
+        const int drow = 16 * (SDB * rb + a) + l16;
+        ka[a][0] = lds8(KT + drow * GLD + 8 * lg);
+        ka[a][1] = lds8(KT + drow * GLD + 32 + 8 * lg);
+      }
+      const float eL = eg[GC - 1];
 #pragma unroll
-        for (int nbk = 0; nbk < 4; ++nbk) {
+      for (int c = 0; c < 2; ++c) O[c] = mfma16(p0, ub[c][0], O[c]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) S[a][nbk][r] *= eL;
-          S[a][nbk] = mfma16(k0, u2b[nbk][0], S[a][nbk]);
+      for (int a = 0; a < SDB; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S[a][c][r] *= eL;
+          S[a][c] = mfma16(ka[a][0], u2b[c][0], S[a][c]);
         }
 #pragma unroll
-        for (int nbk = 0; nbk < 4; ++nbk) S[a][nbk] = mfma16(k1, u2b[nbk][1], S[a][nbk]);
-      }
+      for (int c = 0; c < 2; ++c) O[c] = mfma16(p1, ub[c][1], O[c]);
+#pragma unroll
+      for (int a = 0; a < SDB; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) S[a][c] = mfma16(ka[a][1], u2b[c][1], S[a][c]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * rb + 4 * lg + r;
+          if (i < L) o[((r0 + i) * H + h) * dv + cb * GDVB + 16 * (2 * chh + c) + l16] = O[c][r];
+        }
     }
     write_st();  // ST is no longer read in this chunk
   }
 #pragma unroll
   for (int a = 0; a < SDB; ++a)
 #pragma unroll
-    for (int nbk = 0; nbk < 4; ++nbk)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int d = 16 * (SDB * w + a) + 4 * lg + r;
-        state_out[sbase + (int64_t)d * dv + 16 * nbk + l16] = S[a][nbk][r];
+        const int d = 16 * (SDB * rb + a) + 4 * lg + r;
+        state_out[sbase + (int64_t)d * dv + 16 * (2 * chh + c) + l16] = S[a][c][r];
       }
 }
 
@@ -520,7 +552,6 @@ __global__ __launch_bounds__(256) void k_gdn_chain(int H, int dv, int n_seg, con
 struct ChunkWs {
   int32_t* chunk_base;
   f16_t* T;
-  f16_t* Tg;
   f16_t* P;
   float* G;
   size_t bytes;
@@ -537,13 +568,11 @@ inline ChunkWs chunk_ws_layout(void* base, int64_t n_seg, int64_t n_rows, int H)
   };
   const size_t o_cb = take((size_t)(n_seg + 1) * 4);
   const size_t o_t = take((size_t)nch * H * GC * GC * 2);
-  const size_t o_tg = take((size_t)nch * H * GC * GC * 2);
   const size_t o_p = take((size_t)nch * H * GC * GC * 2);
   const size_t o_g = take((size_t)nch * H * GC * 4);
   char* b = (char*)base;
   w.chunk_base = (int32_t*)(b + o_cb);
   w.T = (f16_t*)(b + o_t);
-  w.Tg = (f16_t*)(b + o_tg);
   w.P = (f16_t*)(b + o_p);
   w.G = (float*)(b + o_g);
   w.bytes = off;
@@ -567,16 +596,15 @@ mom_status launch_gdn_chunk_mfma(const mom_dims& d, int n_seg, int n_rows, const
   do {                                                                                                             \
     if (prep_blocks > 0)                                                                                           \
       hipLaunchKernelGGL((k_gdn_prep<DK>), dim3((unsigned)prep_blocks), dim3(256), 0, st, d.H, n_seg, seg_off,     \
-                         W.chunk_base, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.Tg, W.P,  \
-                         W.G);                                                                                     \
+                         W.chunk_base, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.G); \
     if (row_token)                                                                                                 \
-      hipLaunchKernelGGL((k_gdn_chain<DK, true>), dim3((unsigned)chain_blocks), dim3(256), 0, st, d.H, d.dv, n_seg, \
-                         seg_off, seg_state, W.chunk_base, row_token, (const f16_t*)q, (const f16_t*)k,             \
-                         (const f16_t*)v, W.T, W.Tg, W.P, W.G, state_in, state_out, o);                             \
+      hipLaunchKernelGGL((k_gdn_chain<DK, true>), dim3((unsigned)chain_blocks), dim3(CHAIN_THREADS), 0, st, d.H,    \
+                         d.dv, n_seg, seg_off, seg_state, W.chunk_base, row_token, (const f16_t*)q,                 \
+                         (const f16_t*)k, (const f16_t*)v, W.T, W.P, W.G, state_in, state_out, o);                  \
     else                                                                                                           \
-      hipLaunchKernelGGL((k_gdn_chain<DK, false>), dim3((unsigned)chain_blocks), dim3(256), 0, st, d.H, d.dv,      \
-                         n_seg, seg_off, seg_state, W.chunk_base, row_token, (const f16_t*)q, (const f16_t*)k,      \
-                         (const f16_t*)v, W.T, W.Tg, W.P, W.G, state_in, state_out, o);                             \
+      hipLaunchKernelGGL((k_gdn_chain<DK, false>), dim3((unsigned)chain_blocks), dim3(CHAIN_THREADS), 0, st, d.H,   \
+                         d.dv, n_seg, seg_off, seg_state, W.chunk_base, row_token, (const f16_t*)q,                 \
+                         (const f16_t*)k, (const f16_t*)v, W.T, W.P, W.G, state_in, state_out, o);                  \
   } while (0)
   if (d.dk == 64) MOM_MFMA_CASE(64);
   else MOM_MFMA_CASE(128);
