@@ -251,6 +251,187 @@ __global__ __launch_bounds__(256, 2) void k_project_bf16(int64_t NT, int D, int 
   }
 }
 
+// ------------------------------------------------------------------ bf16 MFMA GEMM, large tiles
+// 256 x 256 tiles, 8 waves (wave tile 128 x 64 = 8 x 4 MFMA tiles), K-steps of
+// 32 through a 4-stage LDS ring filled by direct global->LDS loads
+// (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16 l), so the
+// gathered rows never pass through registers.  Each 64-byte row of a stage
+// holds 4 16-byte chunks; chunk c of row r sits at position c ^ ((r >> 2) & 3),
+// which keeps the 16-row fragment reads of one MFMA operand conflict-free.
+constexpr int PL_M = 256, PL_N = 256, PL_K = 32, PL_NS = 4;
+constexpr int PL_STAGE = (PL_M + PL_N) * PL_K;  // bf16 elements per stage
+constexpr int PL_THREADS = 512;
+
+__device__ __forceinline__ void lds_dma16(const void* g, bf16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__global__ __launch_bounds__(PL_THREADS) void k_project_bf16_l(int64_t NT, int D, int H, int dk, int dv, int M,
+                                                              int B, const bf16_t* __restrict__ x,
+                                                              const int32_t* __restrict__ perm,
+                                                              const int32_t* __restrict__ seg_off,
+                                                              const bf16_t* __restrict__ wq,
+                                                              const bf16_t* __restrict__ wk,
+                                                              const bf16_t* __restrict__ wv, f16_t* __restrict__ q,
+                                                              f16_t* __restrict__ k, f16_t* __restrict__ v) {
+  extern __shared__ __attribute__((aligned(16))) bf16_t smem_l[];
+  const int HK = H * dk, HV = H * dv;
+  const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
+  const TileJob job = decode_tile<PL_M, PL_N>(L, NT, M, B, HK, HV, seg_off);
+  if (job.kind < 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 2, wn = w & 3;
+  const int l16 = lane & 15, lg = lane >> 4;
+
+  const bf16_t* W;
+  if (job.kind == 0) W = wq + (int64_t)job.col0 * D;
+  else if (job.kind == 1) W = wk + ((int64_t)job.m * HK + job.col0) * D;
+  else W = wv + ((int64_t)job.m * HV + job.col0) * D;
+
+  // loads: wave w, instruction j in {0,1} covers stage rows 32w + 16j + lane/4,
+  // LDS position lane%4 holding global chunk (lane%4) ^ ((row >> 2) & 3)
+  const bf16_t* a_src[2];
+  const bf16_t* b_src[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 32 * w + 16 * j + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    int64_t gr = job.trow + r;
+    if (gr >= job.rows) gr = job.rows - 1;  // rows past the end reuse the last row; never stored
+    const int64_t tok = (job.kind == 0) ? gr : (int64_t)perm[job.row0 + gr];
+    a_src[j] = x + tok * D + 8 * c;
+    b_src[j] = W + (int64_t)r * D + 8 * c;
+  }
+  auto issue = [&](int kt) {
+    bf16_t* st = smem_l + (kt % PL_NS) * PL_STAGE;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      lds_dma16(a_src[j] + kt * PL_K, st + (32 * w + 16 * j) * PL_K);
+      lds_dma16(b_src[j] + kt * PL_K, st + PL_M * PL_K + (32 * w + 16 * j) * PL_K);
+    }
+  };
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int nk = D / PL_K;
+#pragma unroll
+  for (int s = 0; s < PL_NS - 1; ++s)
+    if (s < nk) issue(s);
+  for (int kt = 0; kt < nk; ++kt) {
+    // tile kt has landed once at most the loads of the later issued tiles are outstanding
+    const int later = min(PL_NS - 2, nk - 1 - kt);
+    if (later >= 2) wait_vm<8>();
+    else if (later == 1) wait_vm<4>();
+    else wait_vm<0>();
+    lds_sync();
+    if (kt + PL_NS - 1 < nk) issue(kt + PL_NS - 1);
+    const bf16_t* As = smem_l + (kt % PL_NS) * PL_STAGE;
+    const bf16_t* Bs = As + PL_M * PL_K;
+    bfv8 af[8], bfr[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 128 * wm + 16 * i + l16;
+      af[i] = *reinterpret_cast<const bfv8*>(As + r * PL_K + 8 * (lg ^ ((r >> 2) & 3)));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 64 * wn + 16 * j + l16;
+      bfr[j] = *reinterpret_cast<const bfv8*>(Bs + r * PL_K + 8 * (lg ^ ((r >> 2) & 3)));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  }
+  lds_sync();  // every wave done with the ring: LDS is free for the epilogue
+
+  // ---- key rows normalised per head (head = dk columns)
+  if (job.kind == 1) {
+    float* red = reinterpret_cast<float*>(smem_l);  // [4][256]
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s = fmaf(acc[i][j][r], acc[i][j][r], s);
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        s += __shfl_xor(s, 4, 64);
+        s += __shfl_xor(s, 8, 64);
+        if (l16 == 0) red[wn * 256 + 128 * wm + 16 * i + 4 * lg + r] = s;  // sum over this wave's 64 columns
+      }
+    lds_sync();
+    const int per_head = dk / 64;  // waves per head
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rr = 128 * wm + 16 * i + 4 * lg + r;
+        float s = 0.f;
+        const int w0 = (wn / per_head) * per_head;
+        for (int u = 0; u < per_head; ++u) s += red[(w0 + u) * 256 + rr];
+        const float inv_n = 1.0f / sqrtf(s);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j][r] *= inv_n;
+      }
+    lds_sync();
+  }
+  // ---- output through LDS, 128 rows (one wm half) at a time, 16-byte stores
+  f16_t* out;
+  int ld;
+  int64_t orow0;
+  if (job.kind == 0) {
+    out = q;
+    ld = HK;
+    orow0 = job.trow;
+  } else if (job.kind == 1) {
+    out = k;
+    ld = HK;
+    orow0 = job.row0 + job.trow;
+  } else {
+    out = v;
+    ld = HV;
+    orow0 = job.row0 + job.trow;
+  }
+  const int64_t nrows = job.rows - job.trow < PL_M ? job.rows - job.trow : PL_M;
+  constexpr int CLD = PL_N + 8;
+  f16_t* Cs = reinterpret_cast<f16_t*>(smem_l);  // [128][264]
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            Cs[(16 * i + 4 * lg + r) * CLD + 64 * wn + 16 * j + l16] = (f16_t)acc[i][j][r];
+    }
+    lds_sync();
+#pragma unroll
+    for (int p = 0; p < (128 * PL_N / 8) / PL_THREADS; ++p) {
+      const int c = tid + PL_THREADS * p;
+      const int r = c >> 5, c8 = (c & 31) * 8;
+      const int64_t row = 128 * half + r;
+      if (row < nrows)
+        *reinterpret_cast<uint4*>(out + (orow0 + row) * ld + job.col0 + c8) =
+            *reinterpret_cast<const uint4*>(Cs + r * CLD + c8);
+    }
+    lds_sync();
+  }
+}
+
 // ------------------------------------------------------------------ fp32 VALU GEMM
 constexpr int PF_M = 64, PF_N = 64, PF_K = 16;
 
@@ -360,6 +541,21 @@ extern "C" mom_status mom_project(const mom_dims* dims, const void* x, const int
   hipStream_t st = (hipStream_t)stream;
   if (d.dtype == MOM_DTYPE_BF16) {
     if ((d.H * d.dk) % PB_N || (d.H * d.dv) % PB_N) return MOM_ERR_UNSUPPORTED;
+    if ((d.H * d.dk) % PL_N == 0 && (d.H * d.dv) % PL_N == 0 && z.NT >= 4096) {
+      const int64_t G = n_tiles_bound(d, PL_M, PL_N);
+      const size_t lds = (size_t)PL_NS * PL_STAGE * sizeof(bf16_t);
+      static bool attr_set = false;  // idempotent; benign if two threads race
+      if (!attr_set) {
+        if (hipFuncSetAttribute((const void*)k_project_bf16_l, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds) != hipSuccess)
+          return MOM_ERR_LAUNCH;
+        attr_set = true;
+      }
+      hipLaunchKernelGGL(k_project_bf16_l, dim3((unsigned)G), dim3(PL_THREADS), lds, st, z.NT, d.D, d.H, d.dk, d.dv,
+                         d.M, d.B, (const bf16_t*)x, perm, seg_off, (const bf16_t*)w_q, (const bf16_t*)w_k,
+                         (const bf16_t*)w_v, (f16_t*)q, (f16_t*)k, (f16_t*)v);
+      return launch_status();
+    }
     const int64_t G = n_tiles_bound(d, PB_M, PB_N);
     hipLaunchKernelGGL(k_project_bf16, dim3((unsigned)G), dim3(256), 0, st, z.NT, d.D, d.H, d.dk, d.dv, d.M, d.B,
                        (const bf16_t*)x, perm, seg_off, (const bf16_t*)w_q, (const bf16_t*)w_k, (const bf16_t*)w_v,
