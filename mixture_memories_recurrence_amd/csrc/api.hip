@@ -13,14 +13,14 @@ mom_status launch_gdn_chunk_mfma(const mom_dims& d, int n_seg, int n_rows, const
                                  const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
                                  const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
                                  float* state_out, float* o, void* ws, hipStream_t st);
-size_t gdn_chunk_ws_bytes(int64_t n_seg, int64_t n_rows, int H);
+size_t gdn_chunk_ws_bytes(int64_t n_seg, int64_t n_rows, int H, int dk);
 }  // namespace mom
 
 extern "C" size_t gdn_chunk_workspace_bytes(const mom_dims* dims, int32_t n_seg, int32_t n_rows) {
   using namespace mom;
   if (check_dims(dims) != MOM_OK || n_seg < 0 || n_rows < 0) return 0;
   if (dims->dtype != MOM_DTYPE_BF16) return 0;
-  return gdn_chunk_ws_bytes(n_seg, n_rows, dims->H);
+  return gdn_chunk_ws_bytes(n_seg, n_rows, dims->H, dims->dk);
 }
 
 extern "C" mom_status gdn_chunk_fwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,

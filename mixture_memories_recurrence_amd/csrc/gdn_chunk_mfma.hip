@@ -73,7 +73,8 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
                                                   const int32_t* __restrict__ row_token, const f16_t* __restrict__ q,
                                                   const f16_t* __restrict__ k, const float* __restrict__ alpha_p,
                                                   const float* __restrict__ beta_p, f16_t* __restrict__ Tws,
-                                                  f16_t* __restrict__ Pws, float* __restrict__ Gws) {
+                                                  f16_t* __restrict__ Pws, float* __restrict__ Gws,
+                                                  f16_t* __restrict__ Qws) {
   constexpr int KLD = DK + 8;
   __shared__ __attribute__((aligned(16))) f16_t Ks[GC * KLD];
   __shared__ __attribute__((aligned(16))) f16_t Qs[GC * KLD];
@@ -204,6 +205,11 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
     Tout[e] = (f16_t)(lower ? Xs[i][j] * bs[j] : 0.f);
   }
   if (tid < GC) Gws[ch * GC + tid] = gs[tid];
+  // the chunk's (gathered, zero-padded) queries, contiguous for the chain kernel
+  for (int e = tid; e < GC * CPR; e += 256) {
+    const int i = e / CPR, p = (e % CPR) * 8;
+    *reinterpret_cast<uint4*>(Qws + ch * GC * DK + i * DK + p) = *reinterpret_cast<const uint4*>(Qs + i * KLD + p);
+  }
 }
 
 // ------------------------------------------------------------------ chain
@@ -301,16 +307,21 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_gdn_chain(
       rv0 = *reinterpret_cast<const uint4*>(v + (ra * H + h) * dv + cb * GDVB + 8 * pg);
       rv1 = *reinterpret_cast<const uint4*>(v + (rbr * H + h) * dv + cb * GDVB + 8 * pg);
     }
+    rt = reinterpret_cast<const uint4*>(Tws + chk * GC * GC)[tid];
+    rp = reinterpret_cast<const uint4*>(Pws + chk * GC * GC)[tid];
+    rg = Gws[chk * GC + (tid & (GC - 1))];
+  };
+  // Row tokens run two chunks ahead of the gathered query loads, so a query
+  // load never waits on the token load it depends on.
+  auto load_tokens = [&](int64_t r0) {
+    const int L = (int)min((int64_t)GC, rend - r0);
 #pragma unroll
     for (int it = 0; it < QIT; ++it) {
       const int64_t row = r0 + min(qi0 + (NT / QPR) * it, L - 1);
       rtok[it] = GATHER ? row_token[row] : (int32_t)row;
     }
-    rt = reinterpret_cast<const uint4*>(Tws + chk * GC * GC)[tid];
-    rp = reinterpret_cast<const uint4*>(Pws + chk * GC * GC)[tid];
-    rg = Gws[chk * GC + (tid & (GC - 1))];
   };
-  auto prefetch_b = [&]() {  // gathered queries, once the row tokens are in
+  auto prefetch_b = [&]() {  // gathered queries of the chunk whose tokens are in rtok
 #pragma unroll
     for (int it = 0; it < QIT; ++it)
       rq[it] = *reinterpret_cast<const uint4*>(q + ((int64_t)rtok[it] * H + h) * DK + qp);
@@ -389,7 +400,9 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_gdn_chain(
   write_st();
   if (rbeg < rend) {
     prefetch_a(rbeg);
+    load_tokens(rbeg);
     prefetch_b();
+    load_tokens(min(rbeg + GC, rend - 1));
   }
   // The loads for the next chunk are issued unconditionally (the last chunk
   // reloads itself), so they land straight in the registers staged next.
@@ -402,6 +415,8 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_gdn_chain(
     stage(L);
     lds_barrier();
     prefetch_a(more ? r0 + GC : r0);  // in flight during this chunk's products
+    prefetch_b();                      // queries of chunk r0 + GC (tokens loaded a chunk ago)
+    load_tokens(r0 + 2 * GC < rend ? r0 + 2 * GC : r0);
 
     // ---- W = T diag(gamma) K: row block rb, column blocks [WDB*chh, WDB*(chh+1))
     {
@@ -432,7 +447,6 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_gdn_chain(
 #pragma unroll
         for (int r = 0; r < 4; ++r) Wh[(16 * rb + 4 * lg + r) * KLD + 16 * (WDB * chh + y) + l16] = (f16_t)acc[y][r];
     }
-    prefetch_b();
     lds_barrier();  // W rows come from two waves
     // ---- U~ = T V, Q S and W S (sharing the S^T operand), then U and U^T
     f32x4 O[2];
@@ -548,16 +562,595 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_gdn_chain(
       }
 }
 
+// ------------------------------------------------------------------ chain, column-owner form
+// One block per (segment, head, DVB value columns), DVB/32 waves; wave w owns
+// value columns [32w, 32w+32) of the block for every key row, so its part of
+// the state lives in float32 accumulators of v_mfma_f32_32x32x16_f16 and never
+// leaves the wave.  Accumulator rows of a 32x32 tile (8q + 4g + t for lane
+// group g = lane / 32) become the 16-deep B operand of the next product after a
+// v_permlane32_swap between lanes l and l+32, so S and U feed W S, Q S, P U and
+// K~^T U' straight from registers.  Per chunk, the inputs are staged in LDS
+// (K and V transposed) and W = T diag(gamma) K is formed once per block; the
+// rest runs per wave without block barriers.
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef float f16x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f16x16 mfma32(const h8v& a, const h8v& b, const f16x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ unsigned pack_h2(float a, float b) {
+  const _Float16 x = (_Float16)a, y = (_Float16)b;
+  return (unsigned)__builtin_bit_cast(unsigned short, x) | ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
+}
+// Rows [16p, 16p+16) of a 32x32 accumulator tile as the B operand (k = row) of
+// a 32x32x16 product; rows are scaled by sc[0..7] = the scales of rows 8q+4g+t
+// for q = 2p, 2p+1 (t = 0..3), or by 1.
+__device__ __forceinline__ h8v acc_to_b(const f16x16& d, int p, const float* sc) {
+  const unsigned X0 = pack_h2(d[8 * p + 0] * sc[0], d[8 * p + 1] * sc[1]);
+  const unsigned X1 = pack_h2(d[8 * p + 2] * sc[2], d[8 * p + 3] * sc[3]);
+  const unsigned Y0 = pack_h2(d[8 * p + 4] * sc[4], d[8 * p + 5] * sc[5]);
+  const unsigned Y1 = pack_h2(d[8 * p + 6] * sc[6], d[8 * p + 7] * sc[7]);
+  const u2v s0 = __builtin_amdgcn_permlane32_swap(X0, Y0, false, false);
+  const u2v s1 = __builtin_amdgcn_permlane32_swap(X1, Y1, false, false);
+  const unsigned w4[4] = {s0.x, s1.x, s0.y, s1.y};
+  return __builtin_bit_cast(h8v, *reinterpret_cast<const __attribute__((ext_vector_type(4))) unsigned*>(w4));
+}
+
+__device__ __forceinline__ void chunk_dma16(const void* g, f16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void chunk_wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Transposing LDS read (ds_read_b64_tr_b16): inside each 16-lane group, lane i
+// receives element i % 4 of the 8-byte values addressed by lanes i / 4,
+// 4 + i / 4, 8 + i / 4 and 12 + i / 4 of the group.  Pointing lane j of a group
+// at X[k0 + j / 4][n0 + 4 (j % 4)] hands lane i the column n0 + i of rows
+// k0 .. k0 + 3, so a k-major MFMA operand comes straight from a row-major tile.
+typedef short s4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s4v lds_tr4(const f16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)p);
+}
+// 32x32x16 operand fragment (k = 16 kb .. 16 kb + 15, 32 rows/columns from c0)
+// out of a row-major LDS tile X[k][c] with row stride RS halfs.
+template <int RS>
+__device__ __forceinline__ h8v kmajor_frag(const f16_t* X, int kb, int c0, int lane) {
+  const int row = 16 * kb + 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const s4v a = lds_tr4(X + row * RS + col);
+  const s4v b = lds_tr4(X + (row + 4) * RS + col);
+  const s4v v8[2] = {a, b};
+  return __builtin_bit_cast(h8v, v8);
+}
+
+template <int DK, int DVB>
+__global__ __launch_bounds__(DVB * 2) void k_gdn_chain3(
+    int H, int dv, int n_seg, const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_state,
+    const int32_t* __restrict__ chunk_base, const f16_t* __restrict__ k, const f16_t* __restrict__ v,
+    const f16_t* __restrict__ Tws, const f16_t* __restrict__ Pws, const float* __restrict__ Gws,
+    const f16_t* __restrict__ Qws, const float* __restrict__ state_in, float* __restrict__ state_out,
+    float* __restrict__ o) {
+  constexpr int NW = DVB / 32;          // waves
+  constexpr int NT = 64 * NW;           // threads
+  constexpr int RS = DK + 32;           // K row stride: 4 consecutive rows land on distinct banks
+  constexpr int VRS = DVB + 32;         // V row stride
+  constexpr int KLD = DK + 8;
+  constexpr int ND = DK / 32;           // 32-row tiles of the state
+  constexpr int NKD = DK / 16;          // 16-deep k blocks over d
+  constexpr int WT = 2 * ND / NW;       // W^T tiles per wave
+  constexpr int KC = GC * (DK / 8) / NT;
+  constexpr int VC = GC * (DVB / 8) / NT;
+  constexpr int TC = GC * (GC / 8) / NT;
+  __shared__ __attribute__((aligned(16))) f16_t Ks[GC * RS];      // K    [j][d]
+  __shared__ __attribute__((aligned(16))) f16_t Vs[GC * VRS];     // V    [j][n]
+  __shared__ __attribute__((aligned(16))) f16_t Th[GC * GLD];     // T    [i][j]
+  __shared__ __attribute__((aligned(16))) f16_t Ph[GC * GLD];     // P    [i][j]
+  __shared__ __attribute__((aligned(16))) f16_t Qh[GC * KLD];     // Q    [i][d]
+  __shared__ __attribute__((aligned(16))) f16_t Wh[GC * KLD];     // W    [i][d]
+  __shared__ __attribute__((aligned(16))) float eg[GC];           // gamma_i
+  __shared__ __attribute__((aligned(16))) float egl[GC];          // gamma_L / gamma_i
+
+  // (segment, head) groups dealt round-robin over the 8 XCDs, longest first
+  const int nb = dv / DVB;
+  const int64_t pblk = blockIdx.x;
+  const int64_t n_grp = (int64_t)n_seg * H;
+  const int64_t full = (n_grp / 8) * 8;
+  int64_t grp;
+  int cb;
+  if (pblk < full * nb) {
+    const int64_t xi = pblk & 7, ii = pblk >> 3;
+    grp = (ii / nb) * 8 + xi;
+    cb = (int)(ii % nb);
+  } else {
+    const int64_t r = pblk - full * nb;
+    grp = full + r / nb;
+    cb = (int)(r % nb);
+  }
+  const int h = (int)(grp % H);
+  const int s = n_seg - 1 - (int)(grp / H);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c32 = lane & 31, g2 = lane >> 5;
+  const int slot = seg_state ? seg_state[s] : s;
+  const int ncol0 = cb * DVB + 32 * w;      // first value column of this wave
+  const int64_t sbase = ((int64_t)slot * H + h) * DK * dv + ncol0;
+  const int64_t rbeg = seg_off[s], rend = seg_off[s + 1];
+  const int cbase = chunk_base[s];
+
+  // ---- next-chunk registers: coalesced 16-byte pieces (row = e / (width / 8))
+  uint4 rk[KC], rv[VC], rq[KC], rt[TC], rp[TC];
+  float rg = 0.f;
+  auto prefetch = [&](int64_t r0) {
+    const int L = (int)min((int64_t)GC, rend - r0);
+    const int64_t chk = (int64_t)(cbase + (r0 - rbeg) / GC) * H + h;
+#pragma unroll
+    for (int it = 0; it < KC; ++it) {
+      const int e = tid + NT * it, i = e / (DK / 8), p = (e % (DK / 8)) * 8;
+      const int64_t row = r0 + min(i, L - 1);
+      rk[it] = *reinterpret_cast<const uint4*>(k + (row * H + h) * DK + p);
+      rq[it] = *reinterpret_cast<const uint4*>(Qws + chk * GC * DK + i * DK + p);
+    }
+#pragma unroll
+    for (int it = 0; it < VC; ++it) {
+      const int e = tid + NT * it, i = e / (DVB / 8), p = (e % (DVB / 8)) * 8;
+      const int64_t row = r0 + min(i, L - 1);
+      rv[it] = *reinterpret_cast<const uint4*>(v + (row * H + h) * dv + cb * DVB + p);
+    }
+#pragma unroll
+    for (int it = 0; it < TC; ++it) {
+      rt[it] = reinterpret_cast<const uint4*>(Tws + chk * GC * GC)[tid + NT * it];
+      rp[it] = reinterpret_cast<const uint4*>(Pws + chk * GC * GC)[tid + NT * it];
+    }
+    rg = Gws[chk * GC + (tid & (GC - 1))];
+  };
+  auto stage = [&](int L) {
+#pragma unroll
+    for (int it = 0; it < KC; ++it) {
+      const int e = tid + NT * it, i = e / (DK / 8), p = (e % (DK / 8)) * 8;
+      *reinterpret_cast<uint4*>(Ks + i * RS + p) = zero_if(i >= L, rk[it]);
+      *reinterpret_cast<uint4*>(Qh + i * KLD + p) = rq[it];
+    }
+#pragma unroll
+    for (int it = 0; it < VC; ++it) {
+      const int e = tid + NT * it, i = e / (DVB / 8), p = (e % (DVB / 8)) * 8;
+      *reinterpret_cast<uint4*>(Vs + i * VRS + p) = zero_if(i >= L, rv[it]);
+    }
+#pragma unroll
+    for (int it = 0; it < TC; ++it) {
+      const int e = tid + NT * it, i = e >> 3, p = (e & 7) * 8;
+      *reinterpret_cast<uint4*>(Th + i * GLD + p) = rt[it];
+      *reinterpret_cast<uint4*>(Ph + i * GLD + p) = rp[it];
+    }
+    if (tid < GC) {
+      const float gl = __shfl(rg, GC - 1, 64);
+      eg[tid] = expf(rg);
+      egl[tid] = expf(gl - rg);
+    }
+  };
+
+  // ---- state: ND tiles of 32 key rows x the wave's 32 value columns
+  f16x16 S[ND];
+  if (state_in) {
+#pragma unroll
+    for (int a = 0; a < ND; ++a)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int d = 32 * a + 8 * (i / 4) + 4 * g2 + (i % 4);
+        S[a][i] = state_in[sbase + (int64_t)d * dv + c32];
+      }
+  } else {
+#pragma unroll
+    for (int a = 0; a < ND; ++a)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) S[a][i] = 0.f;
+  }
+  if (rbeg < rend) prefetch(rbeg);
+  const float ones[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+
+  for (int64_t r0 = rbeg; r0 < rend; r0 += GC) {
+    const int L = (int)min((int64_t)GC, rend - r0);
+    lds_barrier();  // the previous chunk is done with every LDS tile
+    stage(L);
+    lds_barrier();
+    prefetch(r0 + GC < rend ? r0 + GC : r0);  // lands during this chunk's products
+
+    // ---- W^T tiles of this wave: D[d][i] = sum_j K^T[d][j] (T diag(gamma))^T[j][i] -> Wh[i][d]
+#pragma unroll
+    for (int x = 0; x < WT; ++x) {
+      const int tix = w * WT + x;
+      const int a = tix % ND, bt = tix / ND;  // d tile, i tile
+      f16x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < GC / 16; ++kb) {
+        const h8v ka = kmajor_frag<RS>(Ks, kb, 32 * a, lane);
+        h8v tb = *reinterpret_cast<const h8v*>(Th + (32 * bt + c32) * GLD + 16 * kb + 8 * g2);
+        const float4 e0 = *reinterpret_cast<const float4*>(eg + 16 * kb + 8 * g2);
+        const float4 e1 = *reinterpret_cast<const float4*>(eg + 16 * kb + 8 * g2 + 4);
+        const float es[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) tb[t] = (f16_t)((float)tb[t] * es[t]);
+        acc = mfma32(ka, tb, acc);
+      }
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const half4 hv = {(f16_t)acc[4 * qq], (f16_t)acc[4 * qq + 1], (f16_t)acc[4 * qq + 2], (f16_t)acc[4 * qq + 3]};
+        *reinterpret_cast<half4*>(Wh + (32 * bt + c32) * KLD + 32 * a + 8 * qq + 4 * g2) = hv;
+      }
+    }
+    lds_barrier();  // W complete
+
+    // ---- state as an operand (k = key rows): B of W S, A of S^T Q^T
+    h8v sb[NKD];
+#pragma unroll
+    for (int a = 0; a < ND; ++a) {
+      sb[2 * a] = acc_to_b(S[a], 0, ones);
+      sb[2 * a + 1] = acc_to_b(S[a], 1, ones);
+    }
+    // ---- U = T V - W S for the two 32-row tiles
+    f16x16 U[2];
+    {
+      h8v vb[GC / 16];
+#pragma unroll
+      for (int kb = 0; kb < GC / 16; ++kb) vb[kb] = kmajor_frag<VRS>(Vs, kb, 32 * w, lane);
+#pragma unroll
+      for (int bt = 0; bt < 2; ++bt) {
+        f16x16 ut, ws;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          ut[i] = 0.f;
+          ws[i] = 0.f;
+        }
+#pragma unroll
+        for (int kb = 0; kb < GC / 16; ++kb)
+          ut = mfma32(*reinterpret_cast<const h8v*>(Th + (32 * bt + c32) * GLD + 16 * kb + 8 * g2), vb[kb], ut);
+#pragma unroll
+        for (int kb = 0; kb < NKD; ++kb)
+          ws = mfma32(*reinterpret_cast<const h8v*>(Wh + (32 * bt + c32) * KLD + 16 * kb + 8 * g2), sb[kb], ws);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) U[bt][i] = ut[i] - ws[i];
+      }
+    }
+    // ---- U and diag(gamma_L / gamma) U as operands (k = chunk rows)
+    h8v ub[GC / 16], u2b[GC / 16];
+#pragma unroll
+    for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        float sc[8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          sc[t] = egl[32 * bt + 16 * p + 4 * g2 + t];
+          sc[4 + t] = egl[32 * bt + 16 * p + 8 + 4 * g2 + t];
+        }
+        ub[2 * bt + p] = acc_to_b(U[bt], p, ones);
+        u2b[2 * bt + p] = acc_to_b(U[bt], p, sc);
+      }
+    // ---- O^T = diag... : O^T[n][i] = gamma_i (S^T Q^T)[n][i] + (U^T P^T)[n][i]; float4 stores
+#pragma unroll
+    for (int bt = 0; bt < 2; ++bt) {
+      f16x16 ot;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ot[i] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKD; ++kb)
+        ot = mfma32(sb[kb], *reinterpret_cast<const h8v*>(Qh + (32 * bt + c32) * KLD + 16 * kb + 8 * g2), ot);
+      const float gi = eg[32 * bt + c32];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ot[i] *= gi;
+#pragma unroll
+      for (int kb = 0; kb < GC / 16; ++kb)
+        ot = mfma32(ub[kb], *reinterpret_cast<const h8v*>(Ph + (32 * bt + c32) * GLD + 16 * kb + 8 * g2), ot);
+      const int ri = 32 * bt + c32;
+      if (ri < L) {
+        float* orow = o + ((r0 + ri) * H + h) * dv + ncol0 + 4 * g2;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          *reinterpret_cast<float4*>(orow + 8 * qq) = make_float4(ot[4 * qq], ot[4 * qq + 1], ot[4 * qq + 2], ot[4 * qq + 3]);
+      }
+    }
+    // ---- S <- gamma_L S + K^T U'
+    const float eL = eg[GC - 1];
+#pragma unroll
+    for (int a = 0; a < ND; ++a) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) S[a][i] *= eL;
+#pragma unroll
+      for (int kb = 0; kb < GC / 16; ++kb) S[a] = mfma32(kmajor_frag<RS>(Ks, kb, 32 * a, lane), u2b[kb], S[a]);
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < ND; ++a)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int d = 32 * a + 8 * (i / 4) + 4 * g2 + (i % 4);
+      state_out[sbase + (int64_t)d * dv + c32] = S[a][i];
+    }
+}
+
+// ------------------------------------------------------------------ chain, double-buffered (dk = 128, 128 columns)
+// Same products as k_gdn_chain3, but every chunk input (K, V, Q, T, P) is
+// prefetched straight from global memory into the idle half of a double
+// buffer with global_load_lds_dwordx4 (lane l's 16 bytes land at base + 16 l),
+// so no registers hold in-flight data.  Rows are unpadded; the 16-byte chunk
+// c of row r is stored at position c ^ sw(r):
+//   K, V (256-byte rows, read transposed 4 rows x 64 bytes): sw = 4 (r & 3)
+//   Q    (256-byte rows, read 16 rows x 16 bytes):            sw = r & 15
+//   T, P (128-byte rows, read 16 rows x 16 bytes):            sw = (r >> 1) & 7
+// Rows past the segment end are loaded from its last row; T has zero rows and
+// columns there and the prepared queries are zero, so they contribute nothing.
+__device__ __forceinline__ int swz_kv(int r, int c) { return c ^ (4 * (r & 3)); }
+__device__ __forceinline__ int swz_q(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int swz_tp(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// 32x32x16 operand (k = 16 kb ..) from a swizzled 256-byte-row tile read transposed.
+__device__ __forceinline__ h8v kmajor_frag_sw(const f16_t* X, int kb, int c0, int lane) {
+  const int row = 16 * kb + 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // halfs
+  const int ch = col >> 3, sub = col & 7;
+  const s4v a = lds_tr4(X + row * 128 + 8 * swz_kv(row, ch) + sub);
+  const s4v b = lds_tr4(X + (row + 4) * 128 + 8 * swz_kv(row + 4, ch) + sub);
+  const s4v v8[2] = {a, b};
+  return __builtin_bit_cast(h8v, v8);
+}
+
+__global__ __launch_bounds__(256) void k_gdn_chain4(
+    int H, int dv, int n_seg, const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_state,
+    const int32_t* __restrict__ chunk_base, const f16_t* __restrict__ k, const f16_t* __restrict__ v,
+    const f16_t* __restrict__ Tws, const f16_t* __restrict__ Pws, const float* __restrict__ Gws,
+    const f16_t* __restrict__ Qws, const float* __restrict__ state_in, float* __restrict__ state_out,
+    float* __restrict__ o) {
+  constexpr int DK = 128, DVB = 128;
+  constexpr int KLD = DK + 8;
+  constexpr int ND = DK / 32, NKD = DK / 16, WT = 2;
+  constexpr int BUF = GC * 128 * 3 + GC * 64 * 2;  // halfs per buffer: K, V, Q + T, P
+  extern __shared__ __attribute__((aligned(16))) f16_t smem4[];
+  f16_t* Wh = smem4 + 2 * BUF;                                        // W [i][d], padded
+  float* egb = reinterpret_cast<float*>(Wh + GC * KLD);                // [2][2][64]: gamma, gamma_L/gamma
+
+  const int nb = dv / DVB;
+  const int64_t pblk = blockIdx.x;
+  const int64_t n_grp = (int64_t)n_seg * H;
+  const int64_t full = (n_grp / 8) * 8;
+  int64_t grp;
+  int cb;
+  if (pblk < full * nb) {
+    const int64_t xi = pblk & 7, ii = pblk >> 3;
+    grp = (ii / nb) * 8 + xi;
+    cb = (int)(ii % nb);
+  } else {
+    const int64_t r = pblk - full * nb;
+    grp = full + r / nb;
+    cb = (int)(r % nb);
+  }
+  const int h = (int)(grp % H);
+  const int s = n_seg - 1 - (int)(grp / H);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c32 = lane & 31, g2 = lane >> 5;
+  const int slot = seg_state ? seg_state[s] : s;
+  const int ncol0 = cb * DVB + 32 * w;
+  const int64_t sbase = ((int64_t)slot * H + h) * DK * dv + ncol0;
+  const int64_t rbeg = seg_off[s], rend = seg_off[s + 1];
+  const int cbase = chunk_base[s];
+
+  float rg = 0.f;  // log-decay prefix of the next chunk (thread tid < 64)
+  auto prefetch = [&](int64_t r0, int buf) {
+    const int L = (int)min((int64_t)GC, rend - r0);
+    const int64_t chk = (int64_t)(cbase + (r0 - rbeg) / GC) * H + h;
+    f16_t* B = smem4 + buf * BUF;
+    // K, V, Q: 64 rows x 16 chunks; wave w, instruction it covers rows 4 (w + 4 it) .. +3
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int rbase = 4 * (w + 4 * it);
+      const int r = rbase + (lane >> 4), pos = lane & 15;
+      const int64_t row = r0 + min(r, L - 1);
+      chunk_dma16(k + (row * H + h) * DK + 8 * swz_kv(r, pos), B + rbase * 128);
+      chunk_dma16(v + (row * H + h) * dv + cb * DVB + 8 * swz_kv(r, pos), B + GC * 128 + rbase * 128);
+      chunk_dma16(Qws + chk * GC * DK + r * DK + 8 * swz_q(r, pos), B + 2 * GC * 128 + rbase * 128);
+    }
+    // T, P: 64 rows x 8 chunks; instruction it covers rows 8 (w + 4 it) .. +7
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int rbase = 8 * (w + 4 * it);
+      const int r = rbase + (lane >> 3), pos = lane & 7;
+      chunk_dma16(Tws + chk * GC * GC + r * GC + 8 * swz_tp(r, pos), B + 3 * GC * 128 + rbase * 64);
+      chunk_dma16(Pws + chk * GC * GC + r * GC + 8 * swz_tp(r, pos), B + 3 * GC * 128 + GC * 64 + rbase * 64);
+    }
+    rg = Gws[chk * GC + (tid & (GC - 1))];
+  };
+
+  f16x16 S[ND];
+  if (state_in) {
+#pragma unroll
+    for (int a = 0; a < ND; ++a)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int d = 32 * a + 8 * (i / 4) + 4 * g2 + (i % 4);
+        S[a][i] = state_in[sbase + (int64_t)d * dv + c32];
+      }
+  } else {
+#pragma unroll
+    for (int a = 0; a < ND; ++a)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) S[a][i] = 0.f;
+  }
+  const float ones[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+  if (rbeg < rend) prefetch(rbeg, 0);
+
+  int buf = 0;
+  for (int64_t r0 = rbeg; r0 < rend; r0 += GC, buf ^= 1) {
+    const int L = (int)min((int64_t)GC, rend - r0);
+    chunk_wait_vm0();                   // this chunk's inputs (and the last chunk's stores) are done
+    float* eg = egb + buf * 128;    // gamma_i
+    float* egl = eg + 64;           // gamma_L / gamma_i
+    if (tid < GC) {
+      const float gl = __shfl(rg, GC - 1, 64);
+      eg[tid] = expf(rg);
+      egl[tid] = expf(gl - rg);
+    }
+    lds_barrier();                     // inputs visible; every wave is done with the other buffer
+    prefetch(r0 + GC < rend ? r0 + GC : r0, buf ^ 1);
+    const f16_t* Ks = smem4 + buf * BUF;
+    const f16_t* Vs = Ks + GC * 128;
+    const f16_t* Qs = Ks + 2 * GC * 128;
+    const f16_t* Ts = Ks + 3 * GC * 128;
+    const f16_t* Ps = Ts + GC * 64;
+    auto tfrag = [&](const f16_t* X, int row, int kb) {  // 16-byte operand piece of a T/P row
+      return *reinterpret_cast<const h8v*>(X + row * 64 + 8 * swz_tp(row, 2 * kb + g2));
+    };
+    auto qfrag = [&](int row, int kb) {
+      return *reinterpret_cast<const h8v*>(Qs + row * 128 + 8 * swz_q(row, 2 * kb + g2));
+    };
+
+    // ---- W^T tiles: wave w computes (d tile w, i tiles 0 and 1) -> Wh[i][d]
+    {
+      f16x16 acc[WT];
+#pragma unroll
+      for (int x = 0; x < WT; ++x)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[x][i] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < GC / 16; ++kb) {
+        const h8v ka = kmajor_frag_sw(Ks, kb, 32 * w, lane);
+        const float4 e0 = *reinterpret_cast<const float4*>(eg + 16 * kb + 8 * g2);
+        const float4 e1 = *reinterpret_cast<const float4*>(eg + 16 * kb + 8 * g2 + 4);
+        const float es[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+        for (int x = 0; x < WT; ++x) {
+          h8v tb = tfrag(Ts, 32 * x + c32, kb);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) tb[t] = (f16_t)((float)tb[t] * es[t]);
+          acc[x] = mfma32(ka, tb, acc[x]);
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < WT; ++x)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const half4 hv = {(f16_t)acc[x][4 * qq], (f16_t)acc[x][4 * qq + 1], (f16_t)acc[x][4 * qq + 2],
+                            (f16_t)acc[x][4 * qq + 3]};
+          *reinterpret_cast<half4*>(Wh + (32 * x + c32) * KLD + 32 * w + 8 * qq + 4 * g2) = hv;
+        }
+    }
+    lds_barrier();  // W complete
+
+    // ---- state as an operand (k = key rows)
+    h8v sb[NKD];
+#pragma unroll
+    for (int a = 0; a < ND; ++a) {
+      sb[2 * a] = acc_to_b(S[a], 0, ones);
+      sb[2 * a + 1] = acc_to_b(S[a], 1, ones);
+    }
+    // ---- U = T V - W S, both 32-row tiles interleaved
+    f16x16 U[2];
+    {
+      f16x16 ut[2], ws[2];
+#pragma unroll
+      for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          ut[bt][i] = 0.f;
+          ws[bt][i] = 0.f;
+        }
+#pragma unroll
+      for (int kb = 0; kb < GC / 16; ++kb) {
+        const h8v vb = kmajor_frag_sw(Vs, kb, 32 * w, lane);
+#pragma unroll
+        for (int bt = 0; bt < 2; ++bt) ut[bt] = mfma32(tfrag(Ts, 32 * bt + c32, kb), vb, ut[bt]);
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKD; ++kb)
+#pragma unroll
+        for (int bt = 0; bt < 2; ++bt)
+          ws[bt] = mfma32(*reinterpret_cast<const h8v*>(Wh + (32 * bt + c32) * KLD + 16 * kb + 8 * g2), sb[kb], ws[bt]);
+#pragma unroll
+      for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) U[bt][i] = ut[bt][i] - ws[bt][i];
+    }
+    // ---- U and diag(gamma_L / gamma) U as operands (k = chunk rows)
+    h8v ub[GC / 16], u2b[GC / 16];
+#pragma unroll
+    for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        float sc[8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          sc[t] = egl[32 * bt + 16 * p + 4 * g2 + t];
+          sc[4 + t] = egl[32 * bt + 16 * p + 8 + 4 * g2 + t];
+        }
+        ub[2 * bt + p] = acc_to_b(U[bt], p, ones);
+        u2b[2 * bt + p] = acc_to_b(U[bt], p, sc);
+      }
+    // ---- O^T[n][i] = gamma_i (S^T Q^T)[n][i] + (U^T P^T)[n][i], both i tiles interleaved
+    {
+      f16x16 ot[2];
+#pragma unroll
+      for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ot[bt][i] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKD; ++kb)
+#pragma unroll
+        for (int bt = 0; bt < 2; ++bt) ot[bt] = mfma32(sb[kb], qfrag(32 * bt + c32, kb), ot[bt]);
+#pragma unroll
+      for (int bt = 0; bt < 2; ++bt) {
+        const float gi = eg[32 * bt + c32];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ot[bt][i] *= gi;
+      }
+#pragma unroll
+      for (int kb = 0; kb < GC / 16; ++kb)
+#pragma unroll
+        for (int bt = 0; bt < 2; ++bt) ot[bt] = mfma32(ub[kb], tfrag(Ps, 32 * bt + c32, kb), ot[bt]);
+#pragma unroll
+      for (int bt = 0; bt < 2; ++bt) {
+        const int ri = 32 * bt + c32;
+        if (ri < L) {
+          float* orow = o + ((r0 + ri) * H + h) * dv + ncol0 + 4 * g2;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq)
+            *reinterpret_cast<float4*>(orow + 8 * qq) =
+                make_float4(ot[bt][4 * qq], ot[bt][4 * qq + 1], ot[bt][4 * qq + 2], ot[bt][4 * qq + 3]);
+        }
+      }
+    }
+    // ---- S <- gamma_L S + K^T U', the four state tiles interleaved
+    {
+      const float eL = eg[GC - 1];
+#pragma unroll
+      for (int a = 0; a < ND; ++a)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[a][i] *= eL;
+#pragma unroll
+      for (int kb = 0; kb < GC / 16; ++kb)
+#pragma unroll
+        for (int a = 0; a < ND; ++a) S[a] = mfma32(kmajor_frag_sw(Ks, kb, 32 * a, lane), u2b[kb], S[a]);
+    }
+  }
+  chunk_wait_vm0();  // the dummy prefetch of the last chunk has landed before the block ends
+#pragma unroll
+  for (int a = 0; a < ND; ++a)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int d = 32 * a + 8 * (i / 4) + 4 * g2 + (i % 4);
+      state_out[sbase + (int64_t)d * dv + c32] = S[a][i];
+    }
+}
+constexpr size_t CHAIN4_LDS = (size_t)(2 * (GC * 128 * 3 + GC * 64 * 2) + GC * (128 + 8)) * 2 + 2 * 2 * 64 * 4;
+
 // ------------------------------------------------------------------ workspace + launch
 struct ChunkWs {
   int32_t* chunk_base;
   f16_t* T;
   f16_t* P;
+  f16_t* Q;
   float* G;
   size_t bytes;
 };
 
-inline ChunkWs chunk_ws_layout(void* base, int64_t n_seg, int64_t n_rows, int H) {
+inline ChunkWs chunk_ws_layout(void* base, int64_t n_seg, int64_t n_rows, int H, int dk) {
   const int64_t nch = n_rows / GC + n_seg;  // bound on the number of chunks
   ChunkWs w;
   size_t off = 0;
@@ -570,24 +1163,26 @@ inline ChunkWs chunk_ws_layout(void* base, int64_t n_seg, int64_t n_rows, int H)
   const size_t o_t = take((size_t)nch * H * GC * GC * 2);
   const size_t o_p = take((size_t)nch * H * GC * GC * 2);
   const size_t o_g = take((size_t)nch * H * GC * 4);
+  const size_t o_q = take((size_t)nch * H * GC * dk * 2);
   char* b = (char*)base;
   w.chunk_base = (int32_t*)(b + o_cb);
   w.T = (f16_t*)(b + o_t);
   w.P = (f16_t*)(b + o_p);
   w.G = (float*)(b + o_g);
+  w.Q = (f16_t*)(b + o_q);
   w.bytes = off;
   return w;
 }
 
-size_t gdn_chunk_ws_bytes(int64_t n_seg, int64_t n_rows, int H) {
-  return chunk_ws_layout(nullptr, n_seg, n_rows, H).bytes;
+size_t gdn_chunk_ws_bytes(int64_t n_seg, int64_t n_rows, int H, int dk) {
+  return chunk_ws_layout(nullptr, n_seg, n_rows, H, dk).bytes;
 }
 
 mom_status launch_gdn_chunk_mfma(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
                                  const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
                                  const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
                                  float* state_out, float* o, void* ws, hipStream_t st) {
-  const ChunkWs W = chunk_ws_layout(ws, n_seg, n_rows, d.H);
+  const ChunkWs W = chunk_ws_layout(ws, n_seg, n_rows, d.H, d.dk);
   const int64_t nch = (int64_t)n_rows / GC + n_seg;
   hipLaunchKernelGGL(k_chunk_base, dim3(1), dim3(1024), 0, st, n_seg, seg_off, W.chunk_base);
   const int64_t prep_blocks = nch * d.H;
@@ -596,15 +1191,27 @@ mom_status launch_gdn_chunk_mfma(const mom_dims& d, int n_seg, int n_rows, const
   do {                                                                                                             \
     if (prep_blocks > 0)                                                                                           \
       hipLaunchKernelGGL((k_gdn_prep<DK>), dim3((unsigned)prep_blocks), dim3(256), 0, st, d.H, n_seg, seg_off,     \
-                         W.chunk_base, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.G); \
-    if (row_token)                                                                                                 \
-      hipLaunchKernelGGL((k_gdn_chain<DK, true>), dim3((unsigned)chain_blocks), dim3(CHAIN_THREADS), 0, st, d.H,    \
-                         d.dv, n_seg, seg_off, seg_state, W.chunk_base, row_token, (const f16_t*)q,                 \
-                         (const f16_t*)k, (const f16_t*)v, W.T, W.P, W.G, state_in, state_out, o);                  \
+                         W.chunk_base, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.G,  \
+                         W.Q);                                                                                     \
+    if (DK == 128 && d.dv % 128 == 0) {                                                                           \
+      static bool attr4 = false;                                                                                   \
+      if (!attr4) {                                                                                                \
+        if (hipFuncSetAttribute((const void*)k_gdn_chain4, hipFuncAttributeMaxDynamicSharedMemorySize,             \
+                                (int)CHAIN4_LDS) != hipSuccess)                                                    \
+          return MOM_ERR_LAUNCH;                                                                                   \
+        attr4 = true;                                                                                              \
+      }                                                                                                            \
+      hipLaunchKernelGGL(k_gdn_chain4, dim3((unsigned)((int64_t)n_seg * d.H * (d.dv / 128))), dim3(256),          \
+                         CHAIN4_LDS, st, d.H, d.dv, n_seg, seg_off, seg_state, W.chunk_base, (const f16_t*)k,      \
+                         (const f16_t*)v, W.T, W.P, W.G, W.Q, state_in, state_out, o);                              \
+    } else if (d.dv % 128 == 0)                                                                                    \
+      hipLaunchKernelGGL((k_gdn_chain3<DK, 128>), dim3((unsigned)((int64_t)n_seg * d.H * (d.dv / 128))), dim3(256), \
+                         0, st, d.H, d.dv, n_seg, seg_off, seg_state, W.chunk_base, (const f16_t*)k,               \
+                         (const f16_t*)v, W.T, W.P, W.G, W.Q, state_in, state_out, o);                              \
     else                                                                                                           \
-      hipLaunchKernelGGL((k_gdn_chain<DK, false>), dim3((unsigned)chain_blocks), dim3(CHAIN_THREADS), 0, st, d.H,   \
-                         d.dv, n_seg, seg_off, seg_state, W.chunk_base, row_token, (const f16_t*)q,                 \
-                         (const f16_t*)k, (const f16_t*)v, W.T, W.P, W.G, state_in, state_out, o);                  \
+      hipLaunchKernelGGL((k_gdn_chain3<DK, 64>), dim3((unsigned)chain_blocks), dim3(128), 0, st, d.H, d.dv, n_seg,  \
+                         seg_off, seg_state, W.chunk_base, (const f16_t*)k, (const f16_t*)v, W.T, W.P, W.G, W.Q,   \
+                         state_in, state_out, o);                                                                  \
   } while (0)
   if (d.dk == 64) MOM_MFMA_CASE(64);
   else MOM_MFMA_CASE(128);

@@ -317,11 +317,12 @@ __global__ __launch_bounds__(PL_THREADS) void k_project_bf16_l(int64_t NT, int D
     }
   };
 
-  f32x4 acc[8][4];
+  // acc[j][i]: features 64 wn + 16 j + 4 lg + r (4 consecutive per lane), tokens 128 wm + 16 i + l16
+  f32x4 acc[4][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 8; ++i) acc[j][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   const int nk = D / PL_K;
 #pragma unroll
@@ -349,45 +350,43 @@ __global__ __launch_bounds__(PL_THREADS) void k_project_bf16_l(int64_t NT, int D
       bfr[j] = *reinterpret_cast<const bfv8*>(Bs + r * PL_K + 8 * (lg ^ ((r >> 2) & 3)));
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < 8; ++i) acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[j][i], 0, 0, 0);
   }
   lds_sync();  // every wave done with the ring: LDS is free for the epilogue
 
-  // ---- key rows normalised per head (head = dk columns)
+  // ---- key rows normalised per head (head = dk features)
   if (job.kind == 1) {
-    float* red = reinterpret_cast<float*>(smem_l);  // [4][256]
+    float* red = reinterpret_cast<float*>(smem_l);  // [4 wn][256 tokens]
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+      float s = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float s = 0.f;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s = fmaf(acc[i][j][r], acc[i][j][r], s);
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
-        s += __shfl_xor(s, 4, 64);
-        s += __shfl_xor(s, 8, 64);
-        if (l16 == 0) red[wn * 256 + 128 * wm + 16 * i + 4 * lg + r] = s;  // sum over this wave's 64 columns
-      }
+        for (int r = 0; r < 4; ++r) s = fmaf(acc[j][i][r], acc[j][i][r], s);
+      s += __shfl_xor(s, 16, 64);
+      s += __shfl_xor(s, 32, 64);  // sum over this wave's 64 features
+      if (lg == 0) red[wn * 256 + 128 * wm + 16 * i + l16] = s;
+    }
     lds_sync();
     const int per_head = dk / 64;  // waves per head
+    const int w0 = (wn / per_head) * per_head;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+      const int tt = 128 * wm + 16 * i + l16;
+      float s = 0.f;
+      for (int u = 0; u < per_head; ++u) s += red[(w0 + u) * 256 + tt];
+      const float inv_n = 1.0f / sqrtf(s);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rr = 128 * wm + 16 * i + 4 * lg + r;
-        float s = 0.f;
-        const int w0 = (wn / per_head) * per_head;
-        for (int u = 0; u < per_head; ++u) s += red[(w0 + u) * 256 + rr];
-        const float inv_n = 1.0f / sqrtf(s);
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j][r] *= inv_n;
-      }
+        for (int r = 0; r < 4; ++r) acc[j][i][r] *= inv_n;
+    }
     lds_sync();
   }
-  // ---- output through LDS, 128 rows (one wm half) at a time, 16-byte stores
+  // ---- output through LDS, 128 tokens (one wm half) at a time, 16-byte stores
   f16_t* out;
   int ld;
   int64_t orow0;
@@ -406,17 +405,17 @@ __global__ __launch_bounds__(PL_THREADS) void k_project_bf16_l(int64_t NT, int D
   }
   const int64_t nrows = job.rows - job.trow < PL_M ? job.rows - job.trow : PL_M;
   constexpr int CLD = PL_N + 8;
-  f16_t* Cs = reinterpret_cast<f16_t*>(smem_l);  // [128][264]
+  f16_t* Cs = reinterpret_cast<f16_t*>(smem_l);  // [128 tokens][264]
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     if (wm == half) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            Cs[(16 * i + 4 * lg + r) * CLD + 64 * wn + 16 * j + l16] = (f16_t)acc[i][j][r];
+        for (int i = 0; i < 8; ++i) {
+          const half4 hv = {(f16_t)acc[j][i][0], (f16_t)acc[j][i][1], (f16_t)acc[j][i][2], (f16_t)acc[j][i][3]};
+          *reinterpret_cast<half4*>(Cs + (16 * i + l16) * CLD + 64 * wn + 16 * j + 4 * lg) = hv;
+        }
     }
     lds_sync();
 #pragma unroll
