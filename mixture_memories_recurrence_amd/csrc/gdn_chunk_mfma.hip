@@ -27,10 +27,6 @@ namespace mom {
 
 constexpr int GC = 64;     // chunk rows
 
-__device__ __forceinline__ f32x4 mfma16(const half8& a, const half8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ half8 lds8(const f16_t* p) { return *reinterpret_cast<const half8*>(p); }
 
 // ------------------------------------------------------------------ chunk numbering
 // chunk_base[s] = number of chunks in segments before s; chunk_base[n_seg] = total.
@@ -62,158 +58,6 @@ __global__ __launch_bounds__(1024) void k_chunk_base(int n_seg, const int32_t* _
   if (threadIdx.x == 0) chunk_base[n_seg] = carry_s;
 }
 
-// ------------------------------------------------------------------ prep
-template <int DK>
-__global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_t* __restrict__ seg_off,
-                                                  const int32_t* __restrict__ chunk_base,
-                                                  const int32_t* __restrict__ row_token, const f16_t* __restrict__ q,
-                                                  const f16_t* __restrict__ k, const float* __restrict__ alpha_p,
-                                                  const float* __restrict__ beta_p, f16_t* __restrict__ Tws,
-                                                  f16_t* __restrict__ Pws, float* __restrict__ Ews,
-                                                  f16_t* __restrict__ Qws) {
-  constexpr int KLD = DK + 8;
-  __shared__ __attribute__((aligned(16))) f16_t Ks[GC * KLD];
-  __shared__ __attribute__((aligned(16))) f16_t Qs[GC * KLD];
-  __shared__ float As[GC][GC + 1];
-  __shared__ float Xs[GC][GC + 1];
-  __shared__ float Ys[3][16][17];
-  __shared__ float gs[GC], bs[GC], es[GC];
-
-  const int h = blockIdx.x % H;
-  const int c = blockIdx.x / H;
-  const int total = chunk_base[n_seg];
-  if (c >= total) return;
-  // segment of chunk c: the last s with chunk_base[s] <= c
-  int lo = 0, hi = n_seg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (chunk_base[mid] <= c) lo = mid;
-    else hi = mid - 1;
-  }
-  const int s = lo;
-  const int64_t r0 = seg_off[s] + (int64_t)(c - chunk_base[s]) * GC;
-  const int L = (int)min((int64_t)GC, (int64_t)seg_off[s + 1] - r0);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-
-  // K and Q rows of the chunk (zero past L)
-  constexpr int CPR = DK / 8;  // 16-byte pieces per row
-  for (int e = tid; e < GC * CPR; e += 256) {
-    const int i = e / CPR, p = (e % CPR) * 8;
-    uint4 kv = {0, 0, 0, 0}, qv = {0, 0, 0, 0};
-    if (i < L) {
-      const int64_t row = r0 + i;
-      const int64_t tk = row_token ? (int64_t)row_token[row] : row;
-      kv = *reinterpret_cast<const uint4*>(k + (row * H + h) * DK + p);
-      qv = *reinterpret_cast<const uint4*>(q + (tk * H + h) * DK + p);
-    }
-    *reinterpret_cast<uint4*>(Ks + i * KLD + p) = kv;
-    *reinterpret_cast<uint4*>(Qs + i * KLD + p) = qv;
-  }
-  if (w == 0) {
-    float la = 0.f, bb = 0.f;
-    if (lane < L) {
-      la = logf(alpha_p[(r0 + lane) * H + h]);
-      bb = beta_p[(r0 + lane) * H + h];
-    }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float u = __shfl_up(la, o, 64);
-      if (lane >= o) la += u;
-    }
-    gs[lane] = la;
-    bs[lane] = bb;
-    es[lane] = expf(la);
-    const float gl = __shfl(la, GC - 1, 64);
-    Ews[((int64_t)c * H + h) * 2 * GC + lane] = expf(la);
-    Ews[((int64_t)c * H + h) * 2 * GC + GC + lane] = expf(gl - la);
-  }
-  __syncthreads();
-
-  // wave w: row block w of K K^T and Q K^T (column blocks jb <= w)
-  const int64_t ch = (int64_t)c * H + h;
-  f16_t* Pout = Pws + ch * GC * GC;
-  for (int jb = 0; jb < 4; ++jb) {
-    f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
-    if (jb <= w) {
-#pragma unroll
-      for (int d0 = 0; d0 < DK; d0 += 32) {
-        const int off = d0 + 8 * (lane >> 4);
-        const half8 ka = lds8(Ks + (16 * w + (lane & 15)) * KLD + off);
-        const half8 qa = lds8(Qs + (16 * w + (lane & 15)) * KLD + off);
-        const half8 kb = lds8(Ks + (16 * jb + (lane & 15)) * KLD + off);
-        kk = mfma16(ka, kb, kk);
-        qk = mfma16(qa, kb, qk);
-      }
-    }
-    const int j = 16 * jb + (lane & 15);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * w + 4 * (lane >> 4) + r;
-      float a = 0.f, p = 0.f;
-      if (j <= i) {
-        const float dec = expf(gs[i] - gs[j]);
-        if (j < i) a = bs[i] * dec * kk[r];
-        p = dec * qk[r];
-      }
-      As[i][j] = a;
-      Pout[i * GC + j] = (f16_t)p;
-    }
-  }
-  __syncthreads();
-
-  // X = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution, one lane
-  // per (block, column)
-  if (tid < 64) {
-    const int bb = tid >> 4, cc = tid & 15;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float v = (r == cc) ? 1.f : 0.f;
-#pragma unroll
-      for (int t = 0; t < r; ++t) v = fmaf(-As[16 * bb + r][16 * bb + t], x[t], v);
-      x[r] = v;
-      Xs[16 * bb + r][16 * bb + cc] = v;
-    }
-  }
-  __syncthreads();
-  // off-diagonal blocks, one block-diagonal at a time:
-  //   X_ij = -X_ii * sum_{t=j}^{i-1} A_it X_tj
-  for (int dist = 1; dist < 4; ++dist) {
-    const int nblk = 4 - dist;
-    const int r = tid >> 4, cc = tid & 15;
-    for (int bI = 0; bI < nblk; ++bI) {
-      const int ib = bI + dist, jb = bI;
-      float acc = 0.f;
-      for (int t = 16 * jb; t < 16 * ib; ++t) acc = fmaf(As[16 * ib + r][t], Xs[t][16 * jb + cc], acc);
-      Ys[bI][r][cc] = acc;
-    }
-    __syncthreads();
-    for (int bI = 0; bI < nblk; ++bI) {
-      const int ib = bI + dist, jb = bI;
-      float acc = 0.f;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) acc = fmaf(Xs[16 * ib + r][16 * ib + u], Ys[bI][u][cc], acc);
-      Xs[16 * ib + r][16 * jb + cc] = -acc;
-    }
-    __syncthreads();
-  }
-  // T = X diag(beta), lower block triangle; zero above
-  f16_t* Tout = Tws + ch * GC * GC;
-  for (int e = tid; e < GC * GC; e += 256) {
-    const int i = e / GC, j = e % GC;
-    const bool lower = (j >> 4) < (i >> 4) || ((j >> 4) == (i >> 4) && j <= i);
-    Tout[e] = (f16_t)(lower ? Xs[i][j] * bs[j] : 0.f);
-  }
-  // the chunk's gathered queries scaled by gamma_i (zero past L), contiguous for the chain kernel
-  for (int e = tid; e < GC * CPR; e += 256) {
-    const int i = e / CPR, p = (e % CPR) * 8;
-    half8 qv = *reinterpret_cast<const half8*>(Qs + i * KLD + p);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) qv[t] = (f16_t)((float)qv[t] * es[i]);
-    *reinterpret_cast<half8*>(Qws + ch * GC * DK + i * DK + p) = qv;
-  }
-}
-
 // ------------------------------------------------------------------ chain
 // One block per (segment, head, DVB = 32 NW value columns), NW waves.  Value
 // columns of the state evolve independently, so wave w owns columns
@@ -231,6 +75,7 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
 // next chunk's inputs, which every wave prefetches into the idle half of a
 // double buffer with asynchronous global -> LDS copies.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void vm_wait_8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
 
@@ -547,6 +392,173 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     }
 }
 
+// ------------------------------------------------------------------ prep
+// One wave per (chunk, head), four per block; waves share nothing.
+//   g, gamma = e^g and gamma_L / gamma from a wave prefix sum of log alpha;
+//   K K^T and Q K^T (lower 32x32 tiles) on v_mfma_f32_32x32x16_f16, with both
+//   operands loaded straight from global memory as row pieces (lane l holds
+//   row 32 t + l % 32, halfs 16 kb + 8 (l / 32) .. + 7, for either side);
+//   A_ij = c_i e^{g_i - g_j} k_i.k_j (j < i) to LDS as float32, P_ij =
+//   e^{g_i - g_j} q_i.k_j (j <= i) to global as half;
+//   X = (I + A)^{-1} by forward substitution in float32 with lane j owning
+//   column j (A's rows are read as LDS broadcasts), T = X diag(c) as half;
+//   Q' = diag(gamma) Q as half.
+// Rows at or past the chunk length L are zero in K, Q, A and P; T is then zero
+// in those rows and columns (c = 0 there).
+constexpr int PREP_ALD = GC + 4;  // float row stride of A in LDS
+// Keeps the scheduler from hoisting the next phase's loads, which would hold
+// every operand of the kernel in registers at once.
+#define PREP_PHASE() __builtin_amdgcn_sched_barrier(0)
+
+template <int DK>
+__global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_t* __restrict__ seg_off,
+                                                  const int32_t* __restrict__ chunk_base,
+                                                  const int32_t* __restrict__ row_token, const f16_t* __restrict__ q,
+                                                  const f16_t* __restrict__ k, const float* __restrict__ alpha_p,
+                                                  const float* __restrict__ beta_p, f16_t* __restrict__ Tws,
+                                                  f16_t* __restrict__ Pws, float* __restrict__ Ews,
+                                                  f16_t* __restrict__ Qws) {
+  constexpr int NKD = DK / 16;
+  __shared__ __attribute__((aligned(16))) float As_all[4][GC * PREP_ALD];
+  __shared__ float gs_all[4][GC];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c32 = lane & 31, g2 = lane >> 5;
+  const int64_t ch = (int64_t)blockIdx.x * 4 + w;  // chunk * H + head
+  const int total = chunk_base[n_seg];
+  if (ch >= (int64_t)total * H) return;  // whole wave; no block barrier below
+  const int c = (int)(ch / H), h = (int)(ch % H);
+  // segment of chunk c: the last s with chunk_base[s] <= c
+  int lo = 0, hi = n_seg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (chunk_base[mid] <= c) lo = mid;
+    else hi = mid - 1;
+  }
+  const int64_t r0 = seg_off[lo] + (int64_t)(c - chunk_base[lo]) * GC;
+  const int L = (int)min((int64_t)GC, (int64_t)seg_off[lo + 1] - r0);
+  float* As = As_all[w];
+  float* gs = gs_all[w];
+
+  // gates: lane i holds g_i (inclusive prefix of log alpha; 0 past L) and c_i
+  float g = 0.f, bb = 0.f;
+  if (lane < L) {
+    g = logf(alpha_p[(r0 + lane) * H + h]);
+    bb = beta_p[(r0 + lane) * H + h];
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float u = __shfl_up(g, off, 64);
+    if (lane >= off) g += u;
+  }
+  const float gL = __shfl(g, GC - 1, 64);
+  Ews[ch * 2 * GC + lane] = expf(g);
+  Ews[ch * 2 * GC + GC + lane] = expf(gL - g);
+  gs[lane] = g;
+  wave_lds_fence();  // gs visible to the whole wave
+  // K row pieces (zero past L)
+  h8v kf[2][NKD];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int row = 32 * t + c32;
+    const bool ok = row < L;
+    const f16_t* kp = k + ((r0 + (ok ? row : 0)) * H + h) * DK + 8 * g2;
+#pragma unroll
+    for (int kb = 0; kb < NKD; ++kb) {
+      const h8v z = {}, kv = *reinterpret_cast<const h8v*>(kp + 16 * kb);
+      kf[t][kb] = ok ? kv : z;
+    }
+  }
+  // A' = e^{g_i - g_j} k_i.k_j (j < i), lower tiles (ti, tj) = (0,0), (1,0), (1,1)
+#pragma unroll
+  for (int x = 0; x < 3; ++x) {
+    const int ti = x == 0 ? 0 : 1, tj = x == 2 ? 1 : 0;
+    f16x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKD; ++kb) acc = mfma32(kf[ti][kb], kf[tj][kb], acc);
+    const int j = 32 * tj + c32;
+    const float gj = gs[j];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int i = 32 * ti + 8 * (e / 4) + 4 * g2 + (e % 4);
+      As[i * PREP_ALD + j] = j < i ? expf(gs[i] - gj) * acc[e] : 0.f;
+    }
+  }
+  PREP_PHASE();
+  // Q row pieces: Q' = diag(gamma) Q, and P = (e^{g_i - g_j} q_i.k_j) for j <= i
+  f16_t* Pout = Pws + ch * GC * GC;
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti) {
+    const int row = 32 * ti + c32;
+    const bool ok = row < L;
+    const int64_t rr = r0 + (ok ? row : 0);
+    const int64_t tk = row_token ? (int64_t)row_token[rr] : rr;
+    const f16_t* qp = q + (tk * H + h) * DK + 8 * g2;
+    h8v qf[NKD];
+#pragma unroll
+    for (int kb = 0; kb < NKD; ++kb) {
+      const h8v z = {}, qv = *reinterpret_cast<const h8v*>(qp + 16 * kb);
+      qf[kb] = ok ? qv : z;
+    }
+    const float gam = expf(gs[row]);
+    f16_t* dst = Qws + (ch * GC + row) * DK + 8 * g2;
+#pragma unroll
+    for (int kb = 0; kb < NKD; ++kb) {
+      h8v x = qf[kb];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (f16_t)((float)x[e] * gam);
+      *reinterpret_cast<h8v*>(dst + 16 * kb) = x;
+    }
+#pragma unroll
+    for (int tj = 0; tj < 2; ++tj) {
+      const int j = 32 * tj + c32;
+      if (tj > ti) {  // upper tile: zero
+#pragma unroll
+        for (int e = 0; e < 16; ++e) Pout[(32 * ti + 8 * (e / 4) + 4 * g2 + (e % 4)) * GC + j] = (f16_t)0.f;
+        continue;
+      }
+      f16x16 acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKD; ++kb) acc = mfma32(qf[kb], kf[tj][kb], acc);
+      const float gj = gs[j];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int i = 32 * ti + 8 * (e / 4) + 4 * g2 + (e % 4);
+        Pout[i * GC + j] = (f16_t)(j <= i ? expf(gs[i] - gj) * acc[e] : 0.f);
+      }
+    }
+    PREP_PHASE();
+  }
+  wave_lds_fence();
+  // A_ij above carries k_i.k_j e^{g_i - g_j}; the row factor c_i is applied here.
+  // x = column `lane` of (I + A)^{-1}: x_i = [i == lane] - sum_{t<i} A_it x_t
+  float xc[GC];
+#pragma unroll
+  for (int i = 0; i < GC; ++i) {
+    const float ci = __shfl(bb, i, 64);
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < (i & ~3); t += 4) {
+      const float4 a4 = *reinterpret_cast<const float4*>(As + i * PREP_ALD + t);
+      acc = fmaf(a4.x, xc[t], acc);
+      acc = fmaf(a4.y, xc[t + 1], acc);
+      acc = fmaf(a4.z, xc[t + 2], acc);
+      acc = fmaf(a4.w, xc[t + 3], acc);
+    }
+#pragma unroll
+    for (int t = i & ~3; t < i; ++t) acc = fmaf(As[i * PREP_ALD + t], xc[t], acc);
+    xc[i] = (i == lane ? 1.f : 0.f) - ci * acc;
+  }
+  // T = X diag(c): lane j scales its column by c_j
+  f16_t* Tout = Tws + ch * GC * GC;
+#pragma unroll
+  for (int i = 0; i < GC; ++i) Tout[i * GC + lane] = (f16_t)(xc[i] * bb);
+}
+
 // ------------------------------------------------------------------ workspace + launch
 struct ChunkWs {
   int32_t* chunk_base;
@@ -611,7 +623,7 @@ mom_status launch_gdn_chunk_mfma(const mom_dims& d, int n_seg, int n_rows, const
                                  float* state_out, float* o, void* ws, hipStream_t st) {
   const ChunkWs W = chunk_ws_layout(ws, n_seg, n_rows, d.H, d.dk);
   const int64_t nch = (int64_t)n_rows / GC + n_seg;
-  const int64_t prep_blocks = nch * d.H;
+  const int64_t prep_blocks = (nch * d.H + 3) / 4;  // one wave per (chunk, head)
   hipLaunchKernelGGL(k_chunk_base, dim3(1), dim3(1024), 0, st, n_seg, seg_off, W.chunk_base);
   mom_status r;
   if (d.dk == 64) {
