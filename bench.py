@@ -34,7 +34,8 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=20)
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per launch of the slowest stage")
+    p.add_argument("--traffic", default=None,
+                   help="summary of measured HBM bytes per call (default: profiles/traffic_<workload>.json)")
     return p.parse_args()
 
 
@@ -68,9 +69,10 @@ def decode_costs(cfg, n_seq):
 
 
 def time_cpu_baseline(cfg, inp):
-    """fp64 checker on a bounded sample: the first 2 sequences x 1024 tokens."""
+    """The fp64 oracle on the same batch the GPU step processes (about 10-20 s
+    on 8-16 host cores for the 380M-shape workload)."""
     from oracle import oracle
-    B, T = min(cfg.B, 2), min(cfg.T, 1024)
+    B, T = cfg.B, cfg.T
     NT = B * T
     sl = lambda a: a.reshape(cfg.B, cfg.T, *a.shape[1:])[:B, :T].reshape(NT, *a.shape[1:])
     x, al, be = sl(inp["x"]), sl(inp["alpha"]), sl(inp["beta"])
@@ -80,7 +82,7 @@ def time_cpu_baseline(cfg, inp):
                  inp["w_k"], inp["w_v"], al, be)
     dt = time.perf_counter() - t0
     return {"value": NT / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": "fp64 checker, layer forward on the first %d sequences x %d tokens of the workload (%.1f s)"
+            "sample": "fp64 oracle, one layer forward over the whole step batch (%d sequences x %d tokens, %.1f s)"
                       % (B, T, dt)}
 
 
@@ -152,14 +154,13 @@ def main():
         ach, peak, unit, bound = costs[dom]["flops"] / t / 1e12, MFMA_PEAK_TFLOPS, "TFLOP/s", "mfma"
     else:
         ach, peak, unit, bound = costs[dom]["bytes"] / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        tr = json.load(open(args.traffic))
-        if tr.get("stage") == dom and tr.get("workload") == cfg.name:
-            traffic = tr.get("bytes_per_launch")
+    from mixture_memories_recurrence_amd import pmc_traffic
+    tpath = args.traffic or os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                         "traffic_%s.json" % cfg.name)
+    traffic = pmc_traffic.load_traffic(tpath, dom, cfg.name)
     roofline = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
-                "traffic": traffic, "kernel": dom, "algorithmic_bytes": costs[dom]["bytes"],
-                "algorithmic_flops": costs[dom]["flops"]}
+                "traffic": traffic, "kernel": "%s (%s)" % (dom, ", ".join(pmc_traffic.STAGES[dom][0])),
+                "algorithmic_bytes": costs[dom]["bytes"], "algorithmic_flops": costs[dom]["flops"]}
 
     res = {
         "metric": "MoM layer fwd tokens/s (T=2048, M=4 top-2+shared) + decode tokens/s; % roofline",
