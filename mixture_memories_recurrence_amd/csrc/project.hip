@@ -252,7 +252,8 @@ __global__ __launch_bounds__(256, 2) void k_project_bf16(int64_t NT, int D, int 
 }
 
 // ------------------------------------------------------------------ bf16 MFMA GEMM, large tiles
-// 256 x 256 tiles, 8 waves (wave tile 128 x 64 = 8 x 4 MFMA tiles), K-steps of
+// 256 x 256 tiles, 8 waves (wave tile 128 x 64 = 4 x 2 tiles of
+// v_mfma_f32_32x32x16_bf16), K-steps of
 // 32 through a 4-stage LDS ring filled by direct global->LDS loads
 // (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16 l), so the
 // gathered rows never pass through registers.  Each 64-byte row of a stage
@@ -287,7 +288,6 @@ __global__ __launch_bounds__(PL_THREADS) void k_project_bf16_l(int64_t NT, int D
   if (job.kind < 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 2, wn = w & 3;
-  const int l16 = lane & 15, lg = lane >> 4;
 
   const bf16_t* W;
   if (job.kind == 0) W = wq + (int64_t)job.col0 * D;
@@ -317,12 +317,17 @@ __global__ __launch_bounds__(PL_THREADS) void k_project_bf16_l(int64_t NT, int D
     }
   };
 
-  // acc[j][i]: features 64 wn + 16 j + 4 lg + r (4 consecutive per lane), tokens 128 wm + 16 i + l16
-  f32x4 acc[4][8];
+  // acc[jf][it]: v_mfma_f32_32x32x16_bf16 tiles, weights as the A operand:
+  // element e holds feature 64 wn + 32 jf + 8 (e / 4) + 4 g + (e % 4) of token
+  // 128 wm + 32 it + l32 (g = lane / 32, l32 = lane % 32)
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int jf = 0; jf < 2; ++jf)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[j][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[jf][it][e] = 0.f;
+  const int l32 = lane & 31, g = lane >> 5;
 
   const int nk = D / PL_K;
 #pragma unroll
@@ -338,21 +343,26 @@ __global__ __launch_bounds__(PL_THREADS) void k_project_bf16_l(int64_t NT, int D
     if (kt + PL_NS - 1 < nk) issue(kt + PL_NS - 1);
     const bf16_t* As = smem_l + (kt % PL_NS) * PL_STAGE;
     const bf16_t* Bs = As + PL_M * PL_K;
-    bfv8 af[8], bfr[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 128 * wm + 16 * i + l16;
-      af[i] = *reinterpret_cast<const bfv8*>(As + r * PL_K + 8 * (lg ^ ((r >> 2) & 3)));
+    for (int kb = 0; kb < PL_K / 16; ++kb) {
+      const int ch = 2 * kb + g;  // 16-byte piece of the 64-byte row
+      bfv8 wf[2], xf[4];
+#pragma unroll
+      for (int jf = 0; jf < 2; ++jf) {
+        const int r = 64 * wn + 32 * jf + l32;
+        wf[jf] = *reinterpret_cast<const bfv8*>(Bs + r * PL_K + 8 * (ch ^ ((r >> 2) & 3)));
+      }
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = 128 * wm + 32 * it + l32;
+        xf[it] = *reinterpret_cast<const bfv8*>(As + r * PL_K + 8 * (ch ^ ((r >> 2) & 3)));
+      }
+#pragma unroll
+      for (int jf = 0; jf < 2; ++jf)
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+          acc[jf][it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[jf], xf[it], acc[jf][it], 0, 0, 0);
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 64 * wn + 16 * j + l16;
-      bfr[j] = *reinterpret_cast<const bfv8*>(Bs + r * PL_K + 8 * (lg ^ ((r >> 2) & 3)));
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[j][i], 0, 0, 0);
   }
   lds_sync();  // every wave done with the ring: LDS is free for the epilogue
 
@@ -360,29 +370,28 @@ __global__ __launch_bounds__(PL_THREADS) void k_project_bf16_l(int64_t NT, int D
   if (job.kind == 1) {
     float* red = reinterpret_cast<float*>(smem_l);  // [4 wn][256 tokens]
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int it = 0; it < 4; ++it) {
       float s = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int jf = 0; jf < 2; ++jf)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s = fmaf(acc[j][i][r], acc[j][i][r], s);
-      s += __shfl_xor(s, 16, 64);
+        for (int e = 0; e < 16; ++e) s = fmaf(acc[jf][it][e], acc[jf][it][e], s);
       s += __shfl_xor(s, 32, 64);  // sum over this wave's 64 features
-      if (lg == 0) red[wn * 256 + 128 * wm + 16 * i + l16] = s;
+      if (g == 0) red[wn * 256 + 128 * wm + 32 * it + l32] = s;
     }
     lds_sync();
     const int per_head = dk / 64;  // waves per head
     const int w0 = (wn / per_head) * per_head;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int tt = 128 * wm + 16 * i + l16;
+    for (int it = 0; it < 4; ++it) {
+      const int tt = 128 * wm + 32 * it + l32;
       float s = 0.f;
       for (int u = 0; u < per_head; ++u) s += red[(w0 + u) * 256 + tt];
       const float inv_n = 1.0f / sqrtf(s);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int jf = 0; jf < 2; ++jf)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[j][i][r] *= inv_n;
+        for (int e = 0; e < 16; ++e) acc[jf][it][e] *= inv_n;
     }
     lds_sync();
   }
@@ -410,12 +419,15 @@ __global__ __launch_bounds__(PL_THREADS) void k_project_bf16_l(int64_t NT, int D
   for (int half = 0; half < 2; ++half) {
     if (wm == half) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int jf = 0; jf < 2; ++jf)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const half4 hv = {(f16_t)acc[j][i][0], (f16_t)acc[j][i][1], (f16_t)acc[j][i][2], (f16_t)acc[j][i][3]};
-          *reinterpret_cast<half4*>(Cs + (16 * i + l16) * CLD + 64 * wn + 16 * j + 4 * lg) = hv;
-        }
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const half4 hv = {(f16_t)acc[jf][it][4 * qq], (f16_t)acc[jf][it][4 * qq + 1],
+                              (f16_t)acc[jf][it][4 * qq + 2], (f16_t)acc[jf][it][4 * qq + 3]};
+            *reinterpret_cast<half4*>(Cs + (32 * it + l32) * CLD + 64 * wn + 32 * jf + 8 * qq + 4 * g) = hv;
+          }
     }
     lds_sync();
 #pragma unroll
