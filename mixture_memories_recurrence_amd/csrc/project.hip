@@ -4,12 +4,11 @@
 // projections).  Keys are L2-normalised per head.
 //
 // bfloat16 path: one grouped "TN" GEMM on the matrix cores
-// (v_mfma_f32_16x16x32_bf16), both operands K-contiguous:
+// (v_mfma_f32_32x32x16_bf16), both operands K-contiguous:
 //   C[r][c] = sum_d A[r][d] * W[c][d],  A rows gathered through perm.
 // Logical tiles: first the query tiles (rows = tokens), then for every memory
-// m = 0..M the tiles of its packed rows, whose columns run over [W_k[m]; W_v[m]].
-// A tile is 128 x 128 with K-steps of 64, staged through LDS with a register
-// double buffer; four waves each own a 64 x 64 quadrant (4 x 4 MFMA tiles).
+// m = 0..M the tiles of its packed rows, whose columns run over [W_k[m]; W_v[m]]
+// (see k_project_bf16 for the tile shapes).
 // The blockIdx -> tile map is XCD-aware: every XCD receives one contiguous
 // range of logical tiles, so the column tiles that share a row tile run on the
 // same XCD and reuse its L2 copy of the gathered rows.
@@ -83,185 +82,18 @@ inline int64_t n_tiles_bound(const mom_dims& d, int BM, int BN) {
 }
 
 // ------------------------------------------------------------------ bf16 MFMA GEMM
-constexpr int PB_M = 128, PB_N = 128, PB_K = 64, PB_LD = PB_K + 8;  // LDS row stride (bf16)
-constexpr int PB_CLD = PB_N + 8;                                    // LDS stride of the C tile (half)
-
-__global__ __launch_bounds__(256, 2) void k_project_bf16(int64_t NT, int D, int H, int dk, int dv, int M, int B,
-                                                         const bf16_t* __restrict__ x, const int32_t* __restrict__ perm,
-                                                         const int32_t* __restrict__ seg_off,
-                                                         const bf16_t* __restrict__ wq, const bf16_t* __restrict__ wk,
-                                                         const bf16_t* __restrict__ wv, f16_t* __restrict__ q,
-                                                         f16_t* __restrict__ k, f16_t* __restrict__ v) {
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * 2 * PB_M * PB_LD];
-  bf16_t* As = smem;                      // [2][128][72]
-  bf16_t* Bs = smem + 2 * PB_M * PB_LD;   // [2][128][72]
-  __shared__ float red[2][PB_M];
-
-  const int HK = H * dk, HV = H * dv;
-  const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
-  const TileJob job = decode_tile<PB_M, PB_N>(L, NT, M, B, HK, HV, seg_off);
-  if (job.kind < 0) return;
-
-  const int tid = threadIdx.x, lane = tid & 63, wv_id = tid >> 6;
-  const int wm = wv_id >> 1, wn = wv_id & 1;
-
-  // weight rows of this tile: W[col][d]
-  const bf16_t* W;
-  if (job.kind == 0) W = wq + (int64_t)job.col0 * D;
-  else if (job.kind == 1) W = wk + ((int64_t)job.m * HK + job.col0) * D;
-  else W = wv + ((int64_t)job.m * HV + job.col0) * D;
-
-  // per-thread source rows for the 4 A chunks and 4 B chunks it loads
-  const int lrow = tid >> 3, lcol = (tid & 7) * 8;
-  const bf16_t* a_src[4];
-  const bf16_t* b_src[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int r = lrow + 32 * p;
-    int64_t gr = job.trow + r;
-    if (gr >= job.rows) gr = job.rows - 1;  // rows past the end reuse the last row; never stored
-    const int64_t tok = (job.kind == 0) ? gr : (int64_t)perm[job.row0 + gr];
-    a_src[p] = x + tok * D + lcol;
-    b_src[p] = W + (int64_t)r * D + lcol;
-  }
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-  uint4 ra[4], rb[4];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      ra[p] = *reinterpret_cast<const uint4*>(a_src[p] + k0);
-      rb[p] = *reinterpret_cast<const uint4*>(b_src[p] + k0);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      *reinterpret_cast<uint4*>(As + (buf * PB_M + lrow + 32 * p) * PB_LD + lcol) = ra[p];
-      *reinterpret_cast<uint4*>(Bs + (buf * PB_M + lrow + 32 * p) * PB_LD + lcol) = rb[p];
-    }
-  };
-
-  const int nk = D / PB_K;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * PB_K);
-#pragma unroll
-    for (int ks = 0; ks < PB_K / 32; ++ks) {
-      bfv8 af[4], bfr[4];
-      const int kof = ks * 32 + 8 * (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bfv8*>(As + (cur * PB_M + wm * 64 + 16 * i + (lane & 15)) * PB_LD + kof);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const bfv8*>(Bs + (cur * PB_M + wn * 64 + 16 * j + (lane & 15)) * PB_LD + kof);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: key rows normalised per head
-  if (job.kind == 1) {
-    float ss[4][4];  // [i][r] partial sum of squares over this lane's 4 columns
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float s = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s = fmaf(acc[i][j][r], acc[i][j][r], s);
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
-        s += __shfl_xor(s, 4, 64);
-        s += __shfl_xor(s, 8, 64);
-        ss[i][r] = s;  // sum over this wave's 64 columns
-      }
-    if (dk == 128) {
-      if ((lane & 15) == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) red[wn][wm * 64 + 16 * i + 4 * (lane >> 4) + r] = ss[i][r];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rr = wm * 64 + 16 * i + 4 * (lane >> 4) + r;
-          ss[i][r] = red[0][rr] + red[1][rr];
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float inv_n = 1.0f / sqrtf(ss[i][r]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j][r] *= inv_n;
-      }
-  }
-  // ---- stage the half tile in LDS (the operand buffers are free now)
-  f16_t* Cs = reinterpret_cast<f16_t*>(smem);  // [128][136]
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        Cs[(wm * 64 + 16 * i + 4 * (lane >> 4) + r) * PB_CLD + wn * 64 + 16 * j + (lane & 15)] = (f16_t)acc[i][j][r];
-  __syncthreads();
-  f16_t* out;
-  int ld;
-  int64_t orow0;
-  if (job.kind == 0) {
-    out = q;
-    ld = HK;
-    orow0 = job.trow;
-  } else if (job.kind == 1) {
-    out = k;
-    ld = HK;
-    orow0 = job.row0 + job.trow;
-  } else {
-    out = v;
-    ld = HV;
-    orow0 = job.row0 + job.trow;
-  }
-  const int64_t nrows = job.rows - job.trow < PB_M ? job.rows - job.trow : PB_M;
-#pragma unroll
-  for (int p = 0; p < (PB_M * PB_N / 8) / 256; ++p) {
-    const int c = tid + 256 * p;
-    const int r = c >> 4, c8 = (c & 15) * 8;
-    if (r < nrows)
-      *reinterpret_cast<uint4*>(out + (orow0 + r) * ld + job.col0 + c8) =
-          *reinterpret_cast<const uint4*>(Cs + r * PB_CLD + c8);
-  }
-}
-
-// ------------------------------------------------------------------ bf16 MFMA GEMM, large tiles
-// 256 x 256 tiles, 8 waves (wave tile 128 x 64 = 4 x 2 tiles of
-// v_mfma_f32_32x32x16_bf16), K-steps of
-// 32 through a 4-stage LDS ring filled by direct global->LDS loads
-// (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16 l), so the
-// gathered rows never pass through registers.  Each 64-byte row of a stage
-// holds 4 16-byte chunks; chunk c of row r sits at position c ^ ((r >> 2) & 3),
-// which keeps the 16-row fragment reads of one MFMA operand conflict-free.
-constexpr int PL_M = 256, PL_N = 256, PL_K = 32, PL_NS = 4;
-constexpr int PL_STAGE = (PL_M + PL_N) * PL_K;  // bf16 elements per stage
-constexpr int PL_THREADS = 512;
+// Tiles of BM = BN = 64 NWN rows x features, 2 NWN waves in a 2 x NWN grid;
+// wave tile (32 NWN) x 64 = NWN x 2 tiles of v_mfma_f32_32x32x16_bf16 with the
+// weights as the A operand, so each lane's accumulators hold four consecutive
+// output features.  K-steps of 32 through a 4-stage LDS ring filled by direct
+// global->LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land at
+// base + 16 l), so the gathered rows never pass through registers; every wave
+// copies 32 rows of each operand per stage (4 loads).  Each 64-byte row of a
+// stage holds 4 16-byte pieces; piece c of row r sits at position
+// c ^ ((r >> 2) & 3), which keeps the 32-row operand reads conflict-free.
+// NWN = 4 (256 x 256, 512 threads) for large batches, NWN = 2 (128 x 128, 256
+// threads) for small ones such as decode steps.
+constexpr int PL_K = 32, PL_NS = 4;
 
 __device__ __forceinline__ void lds_dma16(const void* g, bf16_t* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
@@ -273,21 +105,28 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__global__ __launch_bounds__(PL_THREADS) void k_project_bf16_l(int64_t NT, int D, int H, int dk, int dv, int M,
-                                                              int B, const bf16_t* __restrict__ x,
-                                                              const int32_t* __restrict__ perm,
-                                                              const int32_t* __restrict__ seg_off,
-                                                              const bf16_t* __restrict__ wq,
-                                                              const bf16_t* __restrict__ wk,
-                                                              const bf16_t* __restrict__ wv, f16_t* __restrict__ q,
-                                                              f16_t* __restrict__ k, f16_t* __restrict__ v) {
+template <int NWN>
+struct ProjTile {
+  static constexpr int NW = 2 * NWN, THREADS = 64 * NW, BM = 64 * NWN, BN = 64 * NWN;
+  static constexpr int STAGE = (BM + BN) * PL_K;  // bf16 elements per ring stage
+  static constexpr size_t LDS = (size_t)PL_NS * STAGE * sizeof(bf16_t);
+};
+
+template <int NWN>
+__global__ __launch_bounds__(ProjTile<NWN>::THREADS) void k_project_bf16(
+    int64_t NT, int D, int H, int dk, int dv, int M, int B, const bf16_t* __restrict__ x,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ seg_off, const bf16_t* __restrict__ wq,
+    const bf16_t* __restrict__ wk, const bf16_t* __restrict__ wv, f16_t* __restrict__ q, f16_t* __restrict__ k,
+    f16_t* __restrict__ v) {
+  using TL = ProjTile<NWN>;
+  constexpr int BM = TL::BM, BN = TL::BN, IT = NWN;
   extern __shared__ __attribute__((aligned(16))) bf16_t smem_l[];
   const int HK = H * dk, HV = H * dv;
   const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
-  const TileJob job = decode_tile<PL_M, PL_N>(L, NT, M, B, HK, HV, seg_off);
+  const TileJob job = decode_tile<BM, BN>(L, NT, M, B, HK, HV, seg_off);
   if (job.kind < 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 2, wn = w & 3;
+  const int wm = w / NWN, wn = w % NWN;
 
   const bf16_t* W;
   if (job.kind == 0) W = wq + (int64_t)job.col0 * D;
@@ -295,7 +134,7 @@ __global__ __launch_bounds__(PL_THREADS) void k_project_bf16_l(int64_t NT, int D
   else W = wv + ((int64_t)job.m * HV + job.col0) * D;
 
   // loads: wave w, instruction j in {0,1} covers stage rows 32w + 16j + lane/4,
-  // LDS position lane%4 holding global chunk (lane%4) ^ ((row >> 2) & 3)
+  // LDS position lane%4 holding global piece (lane%4) ^ ((row >> 2) & 3)
   const bf16_t* a_src[2];
   const bf16_t* b_src[2];
 #pragma unroll
@@ -309,84 +148,103 @@ __global__ __launch_bounds__(PL_THREADS) void k_project_bf16_l(int64_t NT, int D
     b_src[j] = W + (int64_t)r * D + 8 * c;
   }
   auto issue = [&](int kt) {
-    bf16_t* st = smem_l + (kt % PL_NS) * PL_STAGE;
+    bf16_t* st = smem_l + (kt % PL_NS) * TL::STAGE;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       lds_dma16(a_src[j] + kt * PL_K, st + (32 * w + 16 * j) * PL_K);
-      lds_dma16(b_src[j] + kt * PL_K, st + PL_M * PL_K + (32 * w + 16 * j) * PL_K);
+      lds_dma16(b_src[j] + kt * PL_K, st + BM * PL_K + (32 * w + 16 * j) * PL_K);
     }
   };
 
-  // acc[jf][it]: v_mfma_f32_32x32x16_bf16 tiles, weights as the A operand:
-  // element e holds feature 64 wn + 32 jf + 8 (e / 4) + 4 g + (e % 4) of token
-  // 128 wm + 32 it + l32 (g = lane / 32, l32 = lane % 32)
-  f32x16 acc[2][4];
+  // acc[jf][it]: element e holds feature 64 wn + 32 jf + 8 (e / 4) + 4 g + (e % 4)
+  // of token (BM / 2) wm + 32 it + l32 (g = lane / 32, l32 = lane % 32)
+  f32x16 acc[2][IT];
 #pragma unroll
   for (int jf = 0; jf < 2; ++jf)
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
+    for (int it = 0; it < IT; ++it)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[jf][it][e] = 0.f;
   const int l32 = lane & 31, g = lane >> 5;
 
+  // Operand pieces of one 16-deep k block of stage kt (ring slot kt % PL_NS).
+  auto read_frags = [&](int kt, int kb, bfv8* wf, bfv8* xf) {
+    const bf16_t* As = smem_l + (kt % PL_NS) * TL::STAGE;
+    const bf16_t* Bs = As + BM * PL_K;
+    const int ch = 2 * kb + g;  // 16-byte piece of the 64-byte row
+#pragma unroll
+    for (int jf = 0; jf < 2; ++jf) {
+      const int r = 64 * wn + 32 * jf + l32;
+      wf[jf] = *reinterpret_cast<const bfv8*>(Bs + r * PL_K + 8 * (ch ^ ((r >> 2) & 3)));
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int r = (BM / 2) * wm + 32 * it + l32;
+      xf[it] = *reinterpret_cast<const bfv8*>(As + r * PL_K + 8 * (ch ^ ((r >> 2) & 3)));
+    }
+  };
+  auto mfmas = [&](const bfv8* wf, const bfv8* xf) {
+#pragma unroll
+    for (int jf = 0; jf < 2; ++jf)
+#pragma unroll
+      for (int it = 0; it < IT; ++it)
+        acc[jf][it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[jf], xf[it], acc[jf][it], 0, 0, 0);
+  };
+  // Stage kt has landed once at most the loads of the stages issued after it
+  // (4 per stage per wave) are outstanding.
+  auto wait_stage = [&](int later) {
+    if (later >= 2) wait_vm<8>();
+    else if (later == 1) wait_vm<4>();
+    else wait_vm<0>();
+  };
+
+  // Software pipeline over the two 16-deep halves of each stage: the MFMAs of
+  // one half run while the operand reads of the next half are in flight; the
+  // barrier that publishes stage kt + 1 sits between the two halves of kt.
   const int nk = D / PL_K;
 #pragma unroll
   for (int s = 0; s < PL_NS - 1; ++s)
     if (s < nk) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
-    // tile kt has landed once at most the loads of the later issued tiles are outstanding
-    const int later = min(PL_NS - 2, nk - 1 - kt);
-    if (later >= 2) wait_vm<8>();
-    else if (later == 1) wait_vm<4>();
-    else wait_vm<0>();
-    lds_sync();
-    if (kt + PL_NS - 1 < nk) issue(kt + PL_NS - 1);
-    const bf16_t* As = smem_l + (kt % PL_NS) * PL_STAGE;
-    const bf16_t* Bs = As + PL_M * PL_K;
-#pragma unroll
-    for (int kb = 0; kb < PL_K / 16; ++kb) {
-      const int ch = 2 * kb + g;  // 16-byte piece of the 64-byte row
-      bfv8 wf[2], xf[4];
-#pragma unroll
-      for (int jf = 0; jf < 2; ++jf) {
-        const int r = 64 * wn + 32 * jf + l32;
-        wf[jf] = *reinterpret_cast<const bfv8*>(Bs + r * PL_K + 8 * (ch ^ ((r >> 2) & 3)));
-      }
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int r = 128 * wm + 32 * it + l32;
-        xf[it] = *reinterpret_cast<const bfv8*>(As + r * PL_K + 8 * (ch ^ ((r >> 2) & 3)));
-      }
-#pragma unroll
-      for (int jf = 0; jf < 2; ++jf)
-#pragma unroll
-        for (int it = 0; it < 4; ++it)
-          acc[jf][it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[jf], xf[it], acc[jf][it], 0, 0, 0);
-    }
+  wait_stage(min(PL_NS - 2, nk - 1));
+  lds_sync();
+  if (PL_NS - 1 < nk) issue(PL_NS - 1);
+  bfv8 w0[2], x0[IT], w1[2], x1[IT];
+  read_frags(0, 0, w0, x0);
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    read_frags(kt, 1, w1, x1);
+    mfmas(w0, x0);
+    wait_stage(min(PL_NS - 2, nk - 2 - kt));
+    lds_sync();  // stage kt + 1 visible; every wave is done reading stage kt
+    if (kt + PL_NS < nk) issue(kt + PL_NS);
+    read_frags(kt + 1, 0, w0, x0);
+    mfmas(w1, x1);
   }
+  read_frags(nk - 1, 1, w1, x1);
+  mfmas(w0, x0);
+  mfmas(w1, x1);
   lds_sync();  // every wave done with the ring: LDS is free for the epilogue
 
-  // ---- key rows normalised per head (head = dk features)
+  // ---- key rows normalised per head (head = dk features = dk / 64 waves)
   if (job.kind == 1) {
-    float* red = reinterpret_cast<float*>(smem_l);  // [4 wn][256 tokens]
+    float* red = reinterpret_cast<float*>(smem_l);  // [NWN][BM tokens]
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < IT; ++it) {
       float s = 0.f;
 #pragma unroll
       for (int jf = 0; jf < 2; ++jf)
 #pragma unroll
         for (int e = 0; e < 16; ++e) s = fmaf(acc[jf][it][e], acc[jf][it][e], s);
       s += __shfl_xor(s, 32, 64);  // sum over this wave's 64 features
-      if (g == 0) red[wn * 256 + 128 * wm + 32 * it + l32] = s;
+      if (g == 0) red[wn * BM + (BM / 2) * wm + 32 * it + l32] = s;
     }
     lds_sync();
-    const int per_head = dk / 64;  // waves per head
-    const int w0 = (wn / per_head) * per_head;
+    const int per_head = dk / 64;
+    const int w0h = (wn / per_head) * per_head;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int tt = 128 * wm + 32 * it + l32;
+    for (int it = 0; it < IT; ++it) {
+      const int tt = (BM / 2) * wm + 32 * it + l32;
       float s = 0.f;
-      for (int u = 0; u < per_head; ++u) s += red[(w0 + u) * 256 + tt];
+      for (int u = 0; u < per_head; ++u) s += red[(w0h + u) * BM + tt];
       const float inv_n = 1.0f / sqrtf(s);
 #pragma unroll
       for (int jf = 0; jf < 2; ++jf)
@@ -395,7 +253,7 @@ __global__ __launch_bounds__(PL_THREADS) void k_project_bf16_l(int64_t NT, int D
     }
     lds_sync();
   }
-  // ---- output through LDS, 128 tokens (one wm half) at a time, 16-byte stores
+  // ---- output through LDS, BM / 2 tokens (one wm half) at a time, 16-byte stores
   f16_t* out;
   int ld;
   int64_t orow0;
@@ -412,16 +270,17 @@ __global__ __launch_bounds__(PL_THREADS) void k_project_bf16_l(int64_t NT, int D
     ld = HV;
     orow0 = job.row0 + job.trow;
   }
-  const int64_t nrows = job.rows - job.trow < PL_M ? job.rows - job.trow : PL_M;
-  constexpr int CLD = PL_N + 8;
-  f16_t* Cs = reinterpret_cast<f16_t*>(smem_l);  // [128 tokens][264]
+  const int64_t nrows = job.rows - job.trow < BM ? job.rows - job.trow : BM;
+  constexpr int CLD = BN + 8;
+  constexpr int HR = BM / 2;  // tokens per half
+  f16_t* Cs = reinterpret_cast<f16_t*>(smem_l);  // [HR tokens][CLD]
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     if (wm == half) {
 #pragma unroll
       for (int jf = 0; jf < 2; ++jf)
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
+        for (int it = 0; it < IT; ++it)
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
             const half4 hv = {(f16_t)acc[jf][it][4 * qq], (f16_t)acc[jf][it][4 * qq + 1],
@@ -431,16 +290,35 @@ __global__ __launch_bounds__(PL_THREADS) void k_project_bf16_l(int64_t NT, int D
     }
     lds_sync();
 #pragma unroll
-    for (int p = 0; p < (128 * PL_N / 8) / PL_THREADS; ++p) {
-      const int c = tid + PL_THREADS * p;
-      const int r = c >> 5, c8 = (c & 31) * 8;
-      const int64_t row = 128 * half + r;
+    for (int p = 0; p < (HR * BN / 8) / TL::THREADS; ++p) {
+      const int c = tid + TL::THREADS * p;
+      const int r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
+      const int64_t row = HR * half + r;
       if (row < nrows)
         *reinterpret_cast<uint4*>(out + (orow0 + row) * ld + job.col0 + c8) =
             *reinterpret_cast<const uint4*>(Cs + r * CLD + c8);
     }
     lds_sync();
   }
+}
+
+template <int NWN>
+static mom_status launch_project_bf16(const mom_dims& d, const Sizes& z, const void* x, const int32_t* perm,
+                                      const int32_t* seg_off, const void* w_q, const void* w_k, const void* w_v,
+                                      void* q, void* k, void* v, hipStream_t st) {
+  using TL = ProjTile<NWN>;
+  static bool attr_set = false;  // idempotent; benign if two threads race
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)k_project_bf16<NWN>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)TL::LDS) != hipSuccess)
+      return MOM_ERR_LAUNCH;
+    attr_set = true;
+  }
+  const int64_t G = n_tiles_bound(d, TL::BM, TL::BN);
+  hipLaunchKernelGGL((k_project_bf16<NWN>), dim3((unsigned)G), dim3(TL::THREADS), TL::LDS, st, z.NT, d.D, d.H, d.dk,
+                     d.dv, d.M, d.B, (const bf16_t*)x, perm, seg_off, (const bf16_t*)w_q, (const bf16_t*)w_k,
+                     (const bf16_t*)w_v, (f16_t*)q, (f16_t*)k, (f16_t*)v);
+  return MOM_OK;
 }
 
 // ------------------------------------------------------------------ fp32 VALU GEMM
@@ -551,26 +429,13 @@ extern "C" mom_status mom_project(const mom_dims* dims, const void* x, const int
   const Sizes z = sizes_of(d);
   hipStream_t st = (hipStream_t)stream;
   if (d.dtype == MOM_DTYPE_BF16) {
-    if ((d.H * d.dk) % PB_N || (d.H * d.dv) % PB_N) return MOM_ERR_UNSUPPORTED;
-    if ((d.H * d.dk) % PL_N == 0 && (d.H * d.dv) % PL_N == 0 && z.NT >= 4096) {
-      const int64_t G = n_tiles_bound(d, PL_M, PL_N);
-      const size_t lds = (size_t)PL_NS * PL_STAGE * sizeof(bf16_t);
-      static bool attr_set = false;  // idempotent; benign if two threads race
-      if (!attr_set) {
-        if (hipFuncSetAttribute((const void*)k_project_bf16_l, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)lds) != hipSuccess)
-          return MOM_ERR_LAUNCH;
-        attr_set = true;
-      }
-      hipLaunchKernelGGL(k_project_bf16_l, dim3((unsigned)G), dim3(PL_THREADS), lds, st, z.NT, d.D, d.H, d.dk, d.dv,
-                         d.M, d.B, (const bf16_t*)x, perm, seg_off, (const bf16_t*)w_q, (const bf16_t*)w_k,
-                         (const bf16_t*)w_v, (f16_t*)q, (f16_t*)k, (f16_t*)v);
-      return launch_status();
-    }
-    const int64_t G = n_tiles_bound(d, PB_M, PB_N);
-    hipLaunchKernelGGL(k_project_bf16, dim3((unsigned)G), dim3(256), 0, st, z.NT, d.D, d.H, d.dk, d.dv, d.M, d.B,
-                       (const bf16_t*)x, perm, seg_off, (const bf16_t*)w_q, (const bf16_t*)w_k, (const bf16_t*)w_v,
-                       (f16_t*)q, (f16_t*)k, (f16_t*)v);
+    if ((d.H * d.dk) % 128 || (d.H * d.dv) % 128) return MOM_ERR_UNSUPPORTED;
+    mom_status r;
+    if ((d.H * d.dk) % 256 == 0 && (d.H * d.dv) % 256 == 0 && z.NT >= 4096)
+      r = launch_project_bf16<4>(d, z, x, perm, seg_off, w_q, w_k, w_v, q, k, v, st);
+    else
+      r = launch_project_bf16<2>(d, z, x, perm, seg_off, w_q, w_k, w_v, q, k, v, st);
+    if (r != MOM_OK) return r;
   } else {
     const int64_t G = n_tiles_bound(d, PF_M, PF_N);
     hipLaunchKernelGGL(k_project_f32, dim3((unsigned)G), dim3(256), 0, st, z.NT, d.D, d.H, d.dk, d.dv, d.M, d.B,
