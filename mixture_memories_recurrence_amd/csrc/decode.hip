@@ -6,29 +6,35 @@
 //   o = a_g b + (k.q) u                  = (a_g S + k u^T)^T q
 //   S <- a_g S + k u^T                   written back in place
 // (gist.science page, "Core mechanism": forget then delta update; read after
-// the write.)  The kernel streams the resident float32 states: one block per
-// (sequence, slot, head) holds its whole [dk][dv] state in registers between
-// the read and the write, so each state is read once and written once.
+// the write.)  Every value column of the state is updated independently, so
+// the kernel streams the resident float32 states in column slices: one block
+// per (sequence, slot, head, DVB columns) holds its [dk][DVB] slice in
+// registers between the read and the write (64 registers per thread for
+// DVB = 128), so each state is read once and written once and many slices are
+// in flight per compute unit.
 #include "common.h"
 
 namespace mom {
 
-template <typename IT, int DK, int DV>
+template <typename IT, int DK, int DV, int DVB>
 __global__ __launch_bounds__(256) void k_gdn_decode(int n_seq, int H, int M, int K, const int32_t* __restrict__ idx,
                                                     const int32_t* __restrict__ inv, const IT* __restrict__ q,
                                                     const IT* __restrict__ k, const IT* __restrict__ v,
                                                     const float* __restrict__ alpha, const float* __restrict__ beta,
                                                     float* __restrict__ states, float* __restrict__ o) {
-  constexpr int CPR = DV / 4;     // threads per state row (float4 each)
+  constexpr int CPR = DVB / 4;    // threads per state row slice (float4 each)
   constexpr int RG = 256 / CPR;   // row groups
   constexpr int RPT = DK / RG;    // rows per thread
-  __shared__ float qs[DK], ks[DK], vs[DV];
+  constexpr int NCB = DV / DVB;   // column slices per state
+  __shared__ float qs[DK], ks[DK], vs[DVB];
   __shared__ float4 red_a[RG][CPR], red_b[RG][CPR];
   __shared__ float kq_s;
 
-  const int h = blockIdx.x % H;
-  const int j = (blockIdx.x / H) % (K + 1);
-  const int b = blockIdx.x / (H * (K + 1));
+  const int cb = blockIdx.x % NCB;
+  const int bid = blockIdx.x / NCB;
+  const int h = bid % H;
+  const int j = (bid / H) % (K + 1);
+  const int b = bid / (H * (K + 1));
   const int tid = threadIdx.x;
   int m;
   int64_t row;
@@ -46,12 +52,13 @@ __global__ __launch_bounds__(256) void k_gdn_decode(int n_seq, int H, int M, int
     qs[e] = load_as_f32(q + ((int64_t)b * H + h) * DK + e);
     ks[e] = load_as_f32(k + (row * H + h) * DK + e);
   }
-  for (int e = tid; e < DV; e += 256) vs[e] = load_as_f32(v + (row * H + h) * DV + e);
-  float4* S = reinterpret_cast<float4*>(states + ((((int64_t)b * (M + 1) + m) * H + h) * DK) * DV);
+  for (int e = tid; e < DVB; e += 256) vs[e] = load_as_f32(v + (row * H + h) * DV + cb * DVB + e);
+  float4* S = reinterpret_cast<float4*>(states + ((((int64_t)b * (M + 1) + m) * H + h) * DK) * DV + cb * DVB);
+  constexpr int RS4 = DV / 4;  // float4 per full state row
   const int c4 = tid % CPR, rg = tid / CPR;
   float4 reg[RPT];
 #pragma unroll
-  for (int r = 0; r < RPT; ++r) reg[r] = S[(int64_t)(rg + RG * r) * CPR + c4];
+  for (int r = 0; r < RPT; ++r) reg[r] = S[(int64_t)(rg + RG * r) * RS4 + c4];
   __syncthreads();
   if (tid < 64) {
     float p = 0.f;
@@ -91,7 +98,7 @@ __global__ __launch_bounds__(256) void k_gdn_decode(int n_seq, int H, int M, int
     ov.y = fmaf(kq, u.y, ag * sb.y);
     ov.z = fmaf(kq, u.z, ag * sb.z);
     ov.w = fmaf(kq, u.w, ag * sb.w);
-    reinterpret_cast<float4*>(o + (row * H + h) * DV)[c4] = ov;
+    reinterpret_cast<float4*>(o + (row * H + h) * DV + cb * DVB)[c4] = ov;
   }
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
@@ -101,7 +108,7 @@ __global__ __launch_bounds__(256) void k_gdn_decode(int n_seq, int H, int M, int
     s2.y = fmaf(kd, u.y, ag * reg[r].y);
     s2.z = fmaf(kd, u.z, ag * reg[r].z);
     s2.w = fmaf(kd, u.w, ag * reg[r].w);
-    S[(int64_t)(rg + RG * r) * CPR + c4] = s2;
+    S[(int64_t)(rg + RG * r) * RS4 + c4] = s2;
   }
 }
 
@@ -109,10 +116,14 @@ template <typename IT>
 static void launch_decode(const mom_dims& d, int n_seq, const int32_t* idx, const int32_t* inv, const void* q,
                           const void* k, const void* v, const float* alpha, const float* beta, float* states,
                           float* o, hipStream_t st) {
-  const unsigned blocks = (unsigned)((int64_t)n_seq * (d.topk + 1) * d.H);
-#define MOM_DEC(DK, DV)                                                                                         \
-  hipLaunchKernelGGL((k_gdn_decode<IT, DK, DV>), dim3(blocks), dim3(256), 0, st, n_seq, d.H, d.M, d.topk, idx, \
-                     inv, (const IT*)q, (const IT*)k, (const IT*)v, alpha, beta, states, o)
+  const int64_t slots = (int64_t)n_seq * (d.topk + 1) * d.H;
+#define MOM_DEC(DK, DV)                                                                                          \
+  do {                                                                                                           \
+    constexpr int DVB = DV < 128 ? DV : 128;                                                                     \
+    hipLaunchKernelGGL((k_gdn_decode<IT, DK, DV, DVB>), dim3((unsigned)(slots * (DV / DVB))), dim3(256), 0, st,  \
+                       n_seq, d.H, d.M, d.topk, idx, inv, (const IT*)q, (const IT*)k, (const IT*)v, alpha, beta, \
+                       states, o);                                                                               \
+  } while (0)
   if (d.dk == 64) {
     if (d.dv == 64) MOM_DEC(64, 64);
     else if (d.dv == 128) MOM_DEC(64, 128);

@@ -18,9 +18,9 @@ template <typename XT>
 struct ExactProd;
 template <>
 struct ExactProd<bf16_t> {
-  typedef float V;
-  __device__ static void load(const bf16_t* p, float* out) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
+  typedef uint4 Raw;  // eight bf16
+  __device__ static Raw raw(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void unpack(const Raw& u, float* out) {
     const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -32,12 +32,15 @@ struct ExactProd<bf16_t> {
 };
 template <>
 struct ExactProd<float> {
-  typedef float V;
-  __device__ static void load(const float* p, float* out) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  struct Raw {
+    float4 a, b;
+  };
+  __device__ static Raw raw(const float* p) {
+    return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
+  }
+  __device__ static void unpack(const Raw& r, float* out) {
+    out[0] = r.a.x; out[1] = r.a.y; out[2] = r.a.z; out[3] = r.a.w;
+    out[4] = r.b.x; out[5] = r.b.y; out[6] = r.b.z; out[7] = r.b.w;
   }
   __device__ static double fma(float a, float b, double c) { return ::fma((double)a, (double)b, c); }
 };
@@ -58,15 +61,28 @@ __global__ __launch_bounds__(256) void k_route(int64_t NT, int D, int M, int K, 
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.0;
     const XT* xt = x + t * D;
-#pragma unroll 4
-    for (int d0 = sub * 8; d0 < D; d0 += G * 8) {
-      float xv[8];
-      P::load(xt + d0, xv);
+    // Memories m >= M (when M < MT) read row M - 1 and are never selected.  The
+    // row is read in batches of NB steps whose loads are all issued before the
+    // first product; steps past D read the last piece and are masked to zero.
+    constexpr int NB = MT <= 8 ? 4 : 2;
+    for (int d0 = sub * 8; d0 < D; d0 += NB * G * 8) {
+      typename P::Raw xr[NB], wr_[NB][MT];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m < M) {
+      for (int b = 0; b < NB; ++b) {
+        const int d = min(d0 + b * G * 8, D - 8);
+        xr[b] = P::raw(xt + d);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) wr_[b][m] = P::raw(wr + (int64_t)(m < M ? m : M - 1) * D + d);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (d0 + b * G * 8 >= D) break;
+        float xv[8];
+        P::unpack(xr[b], xv);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
           float wv[8];
-          P::load(wr + (int64_t)m * D + d0, wv);
+          P::unpack(wr_[b][m], wv);
 #pragma unroll
           for (int i = 0; i < 8; ++i) acc[m] = P::fma(xv[i], wv[i], acc[m]);
         }
