@@ -3,11 +3,13 @@
 // (memory, sequence) (podcast.do-not-panic.com page, "Solving scatter-gather
 // without new kernels").
 //
-// A stable counting sort in three launches, all integer work:
+// A stable counting sort, all integer work:
 //   k_count   one block per (tile of 256 positions, sequence): per-memory counts
 //             of the tile, written to cnt[m][b][tile];
 //   k_scan    one block: exclusive scan of cnt in (m, b, tile) order, which is
-//             exactly the packed row order; writes seg_off;
+//             exactly the packed row order; writes seg_off.  When cnt is small
+//             (at most kFuseScan entries) every k_scatter block scans it in
+//             LDS itself instead, which saves this launch;
 //   k_scatter one block per tile again: a token's rank among the tile's tokens
 //             routed to the same memory comes from wavefront ballots (popcount
 //             of the lower lanes) plus the totals of the waves before it, so
@@ -19,6 +21,7 @@
 namespace mom {
 
 constexpr int kTile = kDispatchTile;
+constexpr int kFuseScan = 8192;  // largest cnt scanned inside k_scatter
 
 __global__ __launch_bounds__(kTile) void k_count(int B, int T, int M, int K, int ntile,
                                                  const int32_t* __restrict__ idx, int32_t* __restrict__ cnt) {
@@ -76,16 +79,59 @@ __global__ __launch_bounds__(1024) void k_scan(int B, int T, int M, int K, int n
   }
 }
 
-template <typename XT>
+// Exclusive scan of cnt[0, n) into cs (LDS), n <= kFuseScan, by one block of
+// kTile threads: contiguous runs per thread, then a scan of the run totals.
+__device__ void block_exclusive_scan(const int32_t* __restrict__ cnt, int n, int32_t* cs, int32_t* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int per = (n + kTile - 1) / kTile;
+  for (int i = tid; i < n; i += kTile) cs[i] = cnt[i];
+  __syncthreads();
+  const int i0 = tid * per, i1 = min(n, i0 + per);
+  int32_t run = 0;
+  for (int i = i0; i < i1; ++i) run += cs[i];
+  int32_t sc = run;  // inclusive scan of the run totals inside the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t u = __shfl_up(sc, o, 64);
+    if (lane >= o) sc += u;
+  }
+  if (lane == 63) wsum[wv] = sc;
+  __syncthreads();
+  int32_t pre = sc - run;
+  for (int w2 = 0; w2 < wv; ++w2) pre += wsum[w2];
+  for (int i = i0; i < i1; ++i) {
+    const int32_t c = cs[i];
+    cs[i] = pre;
+    pre += c;
+  }
+  __syncthreads();
+}
+
+template <typename XT, bool FUSED>
 __global__ __launch_bounds__(kTile) void k_scatter(int B, int T, int D, int H, int M, int K, int ntile,
                                                    const int32_t* __restrict__ idx, const int32_t* __restrict__ base,
+                                                   int32_t* __restrict__ seg_off,
                                                    const float* __restrict__ alpha, const float* __restrict__ beta,
                                                    int32_t* __restrict__ perm, int32_t* __restrict__ inv,
                                                    float* __restrict__ alpha_p, float* __restrict__ beta_p,
                                                    const XT* __restrict__ x, XT* __restrict__ x_packed) {
   __shared__ int32_t wave_tot[64][kTile / kWave];
   __shared__ int32_t rows_s[kTile * 8];
+  __shared__ int32_t cs[FUSED ? kFuseScan : 1];
+  __shared__ int32_t wsum[kTile / kWave];
   const int tile = blockIdx.x, b = blockIdx.y;
+  const int64_t NR = (int64_t)B * T * K;
+  if (FUSED) {
+    block_exclusive_scan(base, M * B * ntile, cs, wsum);
+    if (tile == 0 && b == 0)
+      for (int sg = threadIdx.x; sg <= (M + 1) * B; sg += kTile) {
+        int64_t off;
+        if (sg < M * B) off = cs[(int64_t)sg * ntile];
+        else if (sg < (M + 1) * B) off = NR + (int64_t)(sg - M * B) * T;
+        else off = NR + (int64_t)B * T;
+        seg_off[sg] = (int32_t)off;
+      }
+  }
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = tile * kTile + threadIdx.x;
   const bool valid = t < T;
@@ -110,7 +156,6 @@ __global__ __launch_bounds__(kTile) void k_scatter(int B, int T, int D, int H, i
     if (lane == 0) wave_tot[m][wv] = __popcll(bal);
   }
   __syncthreads();
-  const int64_t NR = (int64_t)B * T * K;
   if (valid) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -118,7 +163,8 @@ __global__ __launch_bounds__(kTile) void k_scatter(int B, int T, int D, int H, i
         const int m = mem[j];
         int r = rank[j];
         for (int w2 = 0; w2 < wv; ++w2) r += wave_tot[m][w2];
-        const int32_t row = base[((int64_t)m * B + b) * ntile + tile] + r;
+        const int64_t bi = ((int64_t)m * B + b) * ntile + tile;
+        const int32_t row = (FUSED ? cs[bi] : base[bi]) + r;
         perm[row] = (int32_t)tok;
         inv[tok * K + j] = row;
         rows_s[threadIdx.x * 8 + j] = row;
@@ -180,14 +226,19 @@ extern "C" mom_status mom_dispatch(const mom_dims* dims, const int32_t* idx, con
   hipStream_t st = (hipStream_t)stream;
   int32_t* cnt = (int32_t*)ws;
   hipLaunchKernelGGL(k_count, dim3(ntile, d.B), dim3(kTile), 0, st, d.B, d.T, d.M, d.topk, ntile, idx, cnt);
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, d.B, d.T, d.M, d.topk, ntile, cnt, seg_off);
-  if (d.dtype == MOM_DTYPE_BF16)
-    hipLaunchKernelGGL(k_scatter<bf16_t>, dim3(ntile, d.B), dim3(kTile), 0, st, d.B, d.T, d.D, d.H, d.M, d.topk,
-                       ntile, idx, cnt, alpha, beta, perm, inv, alpha_p, beta_p, (const bf16_t*)x,
-                       (bf16_t*)x_packed);
-  else
-    hipLaunchKernelGGL(k_scatter<float>, dim3(ntile, d.B), dim3(kTile), 0, st, d.B, d.T, d.D, d.H, d.M, d.topk,
-                       ntile, idx, cnt, alpha, beta, perm, inv, alpha_p, beta_p, (const float*)x,
-                       (float*)x_packed);
+  const bool fused = (int64_t)d.M * d.B * ntile <= kFuseScan;
+  if (!fused)
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, d.B, d.T, d.M, d.topk, ntile, cnt, seg_off);
+#define MOM_SCATTER(XT, F)                                                                                         \
+  hipLaunchKernelGGL((k_scatter<XT, F>), dim3(ntile, d.B), dim3(kTile), 0, st, d.B, d.T, d.D, d.H, d.M, d.topk,    \
+                     ntile, idx, cnt, seg_off, alpha, beta, perm, inv, alpha_p, beta_p, (const XT*)x, (XT*)x_packed)
+  if (d.dtype == MOM_DTYPE_BF16) {
+    if (fused) MOM_SCATTER(bf16_t, true);
+    else MOM_SCATTER(bf16_t, false);
+  } else {
+    if (fused) MOM_SCATTER(float, true);
+    else MOM_SCATTER(float, false);
+  }
+#undef MOM_SCATTER
   return launch_status();
 }

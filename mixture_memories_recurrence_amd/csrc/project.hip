@@ -82,17 +82,21 @@ inline int64_t n_tiles_bound(const mom_dims& d, int BM, int BN) {
 }
 
 // ------------------------------------------------------------------ bf16 MFMA GEMM
-// Tiles of BM = BN = 64 NWN rows x features, 2 NWN waves in a 2 x NWN grid;
-// wave tile (32 NWN) x 64 = NWN x 2 tiles of v_mfma_f32_32x32x16_bf16 with the
+// Tiles of BM tokens x BN output features, 2 x NWN waves; wave tile (32 IT)
+// tokens x (32 JF) features = IT x JF tiles of v_mfma_f32_32x32x16_bf16 with the
 // weights as the A operand, so each lane's accumulators hold four consecutive
 // output features.  K-steps of 32 through a 4-stage LDS ring filled by direct
 // global->LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land at
-// base + 16 l), so the gathered rows never pass through registers; every wave
-// copies 32 rows of each operand per stage (4 loads).  Each 64-byte row of a
-// stage holds 4 16-byte pieces; piece c of row r sits at position
-// c ^ ((r >> 2) & 3), which keeps the 32-row operand reads conflict-free.
-// NWN = 4 (256 x 256, 512 threads) for large batches, NWN = 2 (128 x 128, 256
-// threads) for small ones such as decode steps.
+// base + 16 l), so the gathered rows never pass through registers.  A stage
+// holds the BM token rows then the BN weight rows, 64 bytes each; piece c of
+// row r sits at position c ^ ((r >> 2) & 3), which keeps the 32-row operand
+// reads conflict-free.  The wave tile sets the LDS traffic per MFMA; a
+// 128 x 128 wave tile (4 waves on 256 x 256) reads a third fewer bytes per
+// product than 128 x 64, but needs one wave per SIMD for its 256 accumulators,
+// hides less latency than two waves of 128 x 64 and measured slower.
+//   ProjCfg<4, 2, 4>: 256 x 256, 8 waves, wave tile 128 x 64 (large batches)
+//   ProjCfg<2, 2, 2>: 128 x 128, 4 waves, wave tile 64 x 64 (small batches such
+//                     as decode steps)
 constexpr int PL_K = 32, PL_NS = 4;
 
 __device__ __forceinline__ void lds_dma16(const void* g, bf16_t* lds_base) {
@@ -105,21 +109,26 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int NWN>
-struct ProjTile {
-  static constexpr int NW = 2 * NWN, THREADS = 64 * NW, BM = 64 * NWN, BN = 64 * NWN;
+template <int NWN_, int JF_, int IT_>
+struct ProjCfg {
+  static constexpr int NWN = NWN_, JF = JF_, IT = IT_;
+  static constexpr int NW = 2 * NWN, THREADS = 64 * NW;
+  static constexpr int BM = 2 * 32 * IT, BN = NWN * 32 * JF;
   static constexpr int STAGE = (BM + BN) * PL_K;  // bf16 elements per ring stage
+  static constexpr int LPW = (BM + BN) / (16 * NW);  // 16-row loads per wave per stage
   static constexpr size_t LDS = (size_t)PL_NS * STAGE * sizeof(bf16_t);
+  static_assert((BM + BN) % (16 * NW) == 0, "stage rows must split evenly over the waves");
+  static_assert(BM % 16 == 0, "a load never straddles the token and weight rows");
 };
 
-template <int NWN>
-__global__ __launch_bounds__(ProjTile<NWN>::THREADS) void k_project_bf16(
+template <class CF>
+__global__ __launch_bounds__(CF::THREADS) void k_project_bf16(
     int64_t NT, int D, int H, int dk, int dv, int M, int B, const bf16_t* __restrict__ x,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ seg_off, const bf16_t* __restrict__ wq,
     const bf16_t* __restrict__ wk, const bf16_t* __restrict__ wv, f16_t* __restrict__ q, f16_t* __restrict__ k,
     f16_t* __restrict__ v) {
-  using TL = ProjTile<NWN>;
-  constexpr int BM = TL::BM, BN = TL::BN, IT = NWN;
+  constexpr int BM = CF::BM, BN = CF::BN, IT = CF::IT, JF = CF::JF, NWN = CF::NWN, LPW = CF::LPW;
+  constexpr int RPW = 16 * LPW;  // stage rows copied by one wave
   extern __shared__ __attribute__((aligned(16))) bf16_t smem_l[];
   const int HK = H * dk, HV = H * dv;
   const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
@@ -133,34 +142,34 @@ __global__ __launch_bounds__(ProjTile<NWN>::THREADS) void k_project_bf16(
   else if (job.kind == 1) W = wk + ((int64_t)job.m * HK + job.col0) * D;
   else W = wv + ((int64_t)job.m * HV + job.col0) * D;
 
-  // loads: wave w, instruction j in {0,1} covers stage rows 32w + 16j + lane/4,
-  // LDS position lane%4 holding global piece (lane%4) ^ ((row >> 2) & 3)
-  const bf16_t* a_src[2];
-  const bf16_t* b_src[2];
+  // loads: wave w, instruction j covers stage rows RPW w + 16 j + lane/4 (token
+  // rows first, then weight rows), LDS position lane%4 holding global piece
+  // (lane%4) ^ ((row >> 2) & 3)
+  const bf16_t* src[LPW];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = 32 * w + 16 * j + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
-    int64_t gr = job.trow + r;
-    if (gr >= job.rows) gr = job.rows - 1;  // rows past the end reuse the last row; never stored
-    const int64_t tok = (job.kind == 0) ? gr : (int64_t)perm[job.row0 + gr];
-    a_src[j] = x + tok * D + 8 * c;
-    b_src[j] = W + (int64_t)r * D + 8 * c;
+  for (int j = 0; j < LPW; ++j) {
+    const int R = RPW * w + 16 * j + (lane >> 2);
+    const int c = (lane & 3) ^ ((R >> 2) & 3);
+    if (R < BM) {
+      int64_t gr = job.trow + R;
+      if (gr >= job.rows) gr = job.rows - 1;  // rows past the end reuse the last row; never stored
+      const int64_t tok = (job.kind == 0) ? gr : (int64_t)perm[job.row0 + gr];
+      src[j] = x + tok * D + 8 * c;
+    } else {
+      src[j] = W + (int64_t)(R - BM) * D + 8 * c;
+    }
   }
   auto issue = [&](int kt) {
-    bf16_t* st = smem_l + (kt % PL_NS) * TL::STAGE;
+    bf16_t* st = smem_l + (kt % PL_NS) * CF::STAGE;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      lds_dma16(a_src[j] + kt * PL_K, st + (32 * w + 16 * j) * PL_K);
-      lds_dma16(b_src[j] + kt * PL_K, st + BM * PL_K + (32 * w + 16 * j) * PL_K);
-    }
+    for (int j = 0; j < LPW; ++j) lds_dma16(src[j] + kt * PL_K, st + (RPW * w + 16 * j) * PL_K);
   };
 
-  // acc[jf][it]: element e holds feature 64 wn + 32 jf + 8 (e / 4) + 4 g + (e % 4)
+  // acc[jf][it]: element e holds feature (32 JF) wn + 32 jf + 8 (e / 4) + 4 g + (e % 4)
   // of token (BM / 2) wm + 32 it + l32 (g = lane / 32, l32 = lane % 32)
-  f32x16 acc[2][IT];
+  f32x16 acc[JF][IT];
 #pragma unroll
-  for (int jf = 0; jf < 2; ++jf)
+  for (int jf = 0; jf < JF; ++jf)
 #pragma unroll
     for (int it = 0; it < IT; ++it)
 #pragma unroll
@@ -169,12 +178,12 @@ __global__ __launch_bounds__(ProjTile<NWN>::THREADS) void k_project_bf16(
 
   // Operand pieces of one 16-deep k block of stage kt (ring slot kt % PL_NS).
   auto read_frags = [&](int kt, int kb, bfv8* wf, bfv8* xf) {
-    const bf16_t* As = smem_l + (kt % PL_NS) * TL::STAGE;
+    const bf16_t* As = smem_l + (kt % PL_NS) * CF::STAGE;
     const bf16_t* Bs = As + BM * PL_K;
     const int ch = 2 * kb + g;  // 16-byte piece of the 64-byte row
 #pragma unroll
-    for (int jf = 0; jf < 2; ++jf) {
-      const int r = 64 * wn + 32 * jf + l32;
+    for (int jf = 0; jf < JF; ++jf) {
+      const int r = 32 * JF * wn + 32 * jf + l32;
       wf[jf] = *reinterpret_cast<const bfv8*>(Bs + r * PL_K + 8 * (ch ^ ((r >> 2) & 3)));
     }
 #pragma unroll
@@ -185,16 +194,16 @@ __global__ __launch_bounds__(ProjTile<NWN>::THREADS) void k_project_bf16(
   };
   auto mfmas = [&](const bfv8* wf, const bfv8* xf) {
 #pragma unroll
-    for (int jf = 0; jf < 2; ++jf)
+    for (int jf = 0; jf < JF; ++jf)
 #pragma unroll
       for (int it = 0; it < IT; ++it)
         acc[jf][it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[jf], xf[it], acc[jf][it], 0, 0, 0);
   };
   // Stage kt has landed once at most the loads of the stages issued after it
-  // (4 per stage per wave) are outstanding.
+  // (LPW per stage per wave) are outstanding.
   auto wait_stage = [&](int later) {
-    if (later >= 2) wait_vm<8>();
-    else if (later == 1) wait_vm<4>();
+    if (later >= 2) wait_vm<2 * LPW>();
+    else if (later == 1) wait_vm<LPW>();
     else wait_vm<0>();
   };
 
@@ -208,7 +217,7 @@ __global__ __launch_bounds__(ProjTile<NWN>::THREADS) void k_project_bf16(
   wait_stage(min(PL_NS - 2, nk - 1));
   lds_sync();
   if (PL_NS - 1 < nk) issue(PL_NS - 1);
-  bfv8 w0[2], x0[IT], w1[2], x1[IT];
+  bfv8 w0[JF], x0[IT], w1[JF], x1[IT];
   read_frags(0, 0, w0, x0);
   for (int kt = 0; kt + 1 < nk; ++kt) {
     read_frags(kt, 1, w1, x1);
@@ -224,34 +233,61 @@ __global__ __launch_bounds__(ProjTile<NWN>::THREADS) void k_project_bf16(
   mfmas(w1, x1);
   lds_sync();  // every wave done with the ring: LDS is free for the epilogue
 
-  // ---- key rows normalised per head (head = dk features = dk / 64 waves)
+  // ---- key rows normalised per head: scl[it][jf] = 1 / |k| of the head that
+  // feature block jf belongs to (1 for queries and values), applied while the
+  // accumulators are converted below
+  float scl[IT][JF];
+#pragma unroll
+  for (int it = 0; it < IT; ++it)
+#pragma unroll
+    for (int jf = 0; jf < JF; ++jf) scl[it][jf] = 1.f;
   if (job.kind == 1) {
-    float* red = reinterpret_cast<float*>(smem_l);  // [NWN][BM tokens]
+    constexpr int FW = 32 * JF;  // features per wave
+    if (dk >= FW) {              // a head spans dk / FW waves: partial sums through LDS
+      float* red = reinterpret_cast<float*>(smem_l);  // [NWN][BM tokens]
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      float s = 0.f;
+      for (int it = 0; it < IT; ++it) {
+        float s = 0.f;
 #pragma unroll
-      for (int jf = 0; jf < 2; ++jf)
+        for (int jf = 0; jf < JF; ++jf)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s = fmaf(acc[jf][it][e], acc[jf][it][e], s);
-      s += __shfl_xor(s, 32, 64);  // sum over this wave's 64 features
-      if (g == 0) red[wn * BM + (BM / 2) * wm + 32 * it + l32] = s;
+          for (int e = 0; e < 16; ++e) s = fmaf(acc[jf][it][e], acc[jf][it][e], s);
+        s += __shfl_xor(s, 32, 64);  // sum over this wave's features
+        if (g == 0) red[wn * BM + (BM / 2) * wm + 32 * it + l32] = s;
+      }
+      lds_sync();
+      const int per_head = dk / FW;
+      const int w0h = (wn / per_head) * per_head;
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int tt = (BM / 2) * wm + 32 * it + l32;
+        float s = 0.f;
+        for (int u = 0; u < per_head; ++u) s += red[(w0h + u) * BM + tt];
+        const float inv_n = 1.0f / sqrtf(s);
+#pragma unroll
+        for (int jf = 0; jf < JF; ++jf) scl[it][jf] = inv_n;
+      }
+      lds_sync();
+    } else {  // a wave holds FW / dk whole heads of dk / 32 feature blocks each
+      const int jph = dk / 32;
+#pragma unroll
+      for (int it = 0; it < IT; ++it)
+#pragma unroll
+        for (int h0 = 0; h0 < JF; ++h0) {
+          if (h0 % jph) continue;
+          float s = 0.f;
+#pragma unroll
+          for (int jf = 0; jf < JF; ++jf)
+            if (jf >= h0 && jf < h0 + jph)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) s = fmaf(acc[jf][it][e], acc[jf][it][e], s);
+          s += __shfl_xor(s, 32, 64);
+          const float inv_n = 1.0f / sqrtf(s);
+#pragma unroll
+          for (int jf = 0; jf < JF; ++jf)
+            if (jf >= h0 && jf < h0 + jph) scl[it][jf] = inv_n;
+        }
     }
-    lds_sync();
-    const int per_head = dk / 64;
-    const int w0h = (wn / per_head) * per_head;
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int tt = (BM / 2) * wm + 32 * it + l32;
-      float s = 0.f;
-      for (int u = 0; u < per_head; ++u) s += red[(w0h + u) * BM + tt];
-      const float inv_n = 1.0f / sqrtf(s);
-#pragma unroll
-      for (int jf = 0; jf < 2; ++jf)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[jf][it][e] *= inv_n;
-    }
-    lds_sync();
   }
   // ---- output through LDS, BM / 2 tokens (one wm half) at a time, 16-byte stores
   f16_t* out;
@@ -273,25 +309,28 @@ __global__ __launch_bounds__(ProjTile<NWN>::THREADS) void k_project_bf16(
   const int64_t nrows = job.rows - job.trow < BM ? job.rows - job.trow : BM;
   constexpr int CLD = BN + 8;
   constexpr int HR = BM / 2;  // tokens per half
+  static_assert((size_t)HR * CLD * sizeof(f16_t) <= CF::LDS, "output staging fits the ring");
+  static_assert((HR * BN / 8) % CF::THREADS == 0, "output pieces split evenly");
   f16_t* Cs = reinterpret_cast<f16_t*>(smem_l);  // [HR tokens][CLD]
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     if (wm == half) {
 #pragma unroll
-      for (int jf = 0; jf < 2; ++jf)
+      for (int jf = 0; jf < JF; ++jf)
 #pragma unroll
         for (int it = 0; it < IT; ++it)
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
-            const half4 hv = {(f16_t)acc[jf][it][4 * qq], (f16_t)acc[jf][it][4 * qq + 1],
-                              (f16_t)acc[jf][it][4 * qq + 2], (f16_t)acc[jf][it][4 * qq + 3]};
-            *reinterpret_cast<half4*>(Cs + (32 * it + l32) * CLD + 64 * wn + 32 * jf + 8 * qq + 4 * g) = hv;
+            const float sc = scl[it][jf];
+            const half4 hv = {(f16_t)(acc[jf][it][4 * qq] * sc), (f16_t)(acc[jf][it][4 * qq + 1] * sc),
+                              (f16_t)(acc[jf][it][4 * qq + 2] * sc), (f16_t)(acc[jf][it][4 * qq + 3] * sc)};
+            *reinterpret_cast<half4*>(Cs + (32 * it + l32) * CLD + 32 * JF * wn + 32 * jf + 8 * qq + 4 * g) = hv;
           }
     }
     lds_sync();
 #pragma unroll
-    for (int p = 0; p < (HR * BN / 8) / TL::THREADS; ++p) {
-      const int c = tid + TL::THREADS * p;
+    for (int p = 0; p < (HR * BN / 8) / CF::THREADS; ++p) {
+      const int c = tid + CF::THREADS * p;
       const int r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
       const int64_t row = HR * half + r;
       if (row < nrows)
@@ -302,20 +341,19 @@ __global__ __launch_bounds__(ProjTile<NWN>::THREADS) void k_project_bf16(
   }
 }
 
-template <int NWN>
+template <class CF>
 static mom_status launch_project_bf16(const mom_dims& d, const Sizes& z, const void* x, const int32_t* perm,
                                       const int32_t* seg_off, const void* w_q, const void* w_k, const void* w_v,
                                       void* q, void* k, void* v, hipStream_t st) {
-  using TL = ProjTile<NWN>;
   static bool attr_set = false;  // idempotent; benign if two threads race
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_project_bf16<NWN>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)TL::LDS) != hipSuccess)
+    if (hipFuncSetAttribute((const void*)k_project_bf16<CF>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)CF::LDS) != hipSuccess)
       return MOM_ERR_LAUNCH;
     attr_set = true;
   }
-  const int64_t G = n_tiles_bound(d, TL::BM, TL::BN);
-  hipLaunchKernelGGL((k_project_bf16<NWN>), dim3((unsigned)G), dim3(TL::THREADS), TL::LDS, st, z.NT, d.D, d.H, d.dk,
+  const int64_t G = n_tiles_bound(d, CF::BM, CF::BN);
+  hipLaunchKernelGGL((k_project_bf16<CF>), dim3((unsigned)G), dim3(CF::THREADS), CF::LDS, st, z.NT, d.D, d.H, d.dk,
                      d.dv, d.M, d.B, (const bf16_t*)x, perm, seg_off, (const bf16_t*)w_q, (const bf16_t*)w_k,
                      (const bf16_t*)w_v, (f16_t*)q, (f16_t*)k, (f16_t*)v);
   return MOM_OK;
@@ -432,9 +470,9 @@ extern "C" mom_status mom_project(const mom_dims* dims, const void* x, const int
     if ((d.H * d.dk) % 128 || (d.H * d.dv) % 128) return MOM_ERR_UNSUPPORTED;
     mom_status r;
     if ((d.H * d.dk) % 256 == 0 && (d.H * d.dv) % 256 == 0 && z.NT >= 4096)
-      r = launch_project_bf16<4>(d, z, x, perm, seg_off, w_q, w_k, w_v, q, k, v, st);
+      r = launch_project_bf16<ProjCfg<4, 2, 4>>(d, z, x, perm, seg_off, w_q, w_k, w_v, q, k, v, st);
     else
-      r = launch_project_bf16<2>(d, z, x, perm, seg_off, w_q, w_k, w_v, q, k, v, st);
+      r = launch_project_bf16<ProjCfg<2, 2, 2>>(d, z, x, perm, seg_off, w_q, w_k, w_v, q, k, v, st);
     if (r != MOM_OK) return r;
   } else {
     const int64_t G = n_tiles_bound(d, PF_M, PF_N);

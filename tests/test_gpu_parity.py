@@ -122,6 +122,37 @@ def test_dispatch_forced_empty_memory():
     np.testing.assert_array_equal(b["perm"].cpu().numpy(), perm)
 
 
+@pytest.mark.parametrize("B,T,M,K", [(16, 4096, 64, 8), (3, 700, 5, 2)])
+def test_dispatch_random_routes(B, T, M, K):
+    """Random distinct memory choices per token.  The first shape has
+    64 * 16 * 16 per-tile counts, more than the scatter kernel scans itself, so
+    it takes the separate scan launch; the second takes the in-kernel scan."""
+    cfg = synth.LayerConfig(B, T, 64, 1, 64, 64, M, K, "bf16")
+    log("dispatch random", B, T, M, K)
+    rng = np.random.default_rng(11)
+    idx = np.argsort(rng.random((B * T, M)), axis=1)[:, :K].astype(np.int32)
+    alpha = rng.random((B * T, 1, M + 1)).astype(np.float32)
+    beta = rng.random((B * T, 1, M + 1)).astype(np.float32)
+    dims = mom.dims_of(cfg)
+    N = B * T * (K + 1)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    seg_off = torch.empty((M + 1) * B + 1, **i32)
+    perm, inv = torch.empty(N, **i32), torch.empty(B * T, K, **i32)
+    ap = torch.empty(N, 1, dtype=torch.float32, device="cuda")
+    bp = torch.empty_like(ap)
+    ws = torch.empty(max(mom.mom_workspace_bytes(dims, mom.WS_DISPATCH), 256), dtype=torch.uint8, device="cuda")
+    mom.mom_dispatch(dims, to_gpu(idx), None, to_gpu(alpha), to_gpu(beta), seg_off, perm, inv, None, ap, bp, ws)
+    torch.cuda.synchronize()
+    so_ref, perm_ref, inv_ref = oracle.dispatch(idx, B, T, M)
+    np.testing.assert_array_equal(seg_off.cpu().numpy(), so_ref)
+    np.testing.assert_array_equal(perm.cpu().numpy(), perm_ref)
+    np.testing.assert_array_equal(inv.cpu().numpy(), inv_ref)
+    counts = [so_ref[(m + 1) * B] - so_ref[m * B] for m in range(M)]
+    mem = np.concatenate([np.repeat(np.arange(M), counts), np.full(B * T, M)])
+    np.testing.assert_array_equal(ap.cpu().numpy()[:, 0], alpha[perm_ref, 0, mem])
+    np.testing.assert_array_equal(bp.cpu().numpy()[:, 0], beta[perm_ref, 0, mem])
+
+
 # ------------------------------------------------------------------ projections
 @pytest.mark.parametrize("name", list(CFG))
 def test_project_sampled_rows(name):
