@@ -4,30 +4,49 @@
 // the single-memory operators equals reading from the weighted mixture of
 // memories; Mixture-of-Memories section: every token passes the shared memory).
 //
-// Pure streaming: each thread owns four consecutive floats of one token's
-// [H][dv] row; shared read first, then j ascending, fixed order, no atomics.
+// Pure streaming: one wavefront per token; lane l owns the float4 pieces
+// l + 64 c of the token's [H][dv] row.  The token's row indices and weights are
+// wave-uniform (scalar loads); every o row is read once and out written once,
+// with non-temporal accesses (nothing here is read again soon).  Shared term
+// first, then j ascending, fixed order, no atomics.
 #include "common.h"
 
 namespace mom {
 
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+template <int KM>
 __global__ __launch_bounds__(256) void k_combine(int64_t n_tok, int K, int hdv4, const int32_t* __restrict__ inv,
-                                                 const float* __restrict__ w, const float4* __restrict__ o_routed,
-                                                 const float4* __restrict__ o_shared, float4* __restrict__ out) {
-  const int64_t total = n_tok * hdv4;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = i / hdv4;
-    const int e = (int)(i - t * hdv4);
-    float4 s = o_shared[i];
-    for (int j = 0; j < K; ++j) {
-      const int64_t r = inv ? (int64_t)inv[t * K + j] : t * K + j;
-      const float g = w[t * K + j];
-      const float4 o = o_routed[r * hdv4 + e];
-      s.x = fmaf(g, o.x, s.x);
-      s.y = fmaf(g, o.y, s.y);
-      s.z = fmaf(g, o.z, s.z);
-      s.w = fmaf(g, o.w, s.w);
+                                                 const float* __restrict__ w, const f4v* __restrict__ o_routed,
+                                                 const f4v* __restrict__ o_shared, f4v* __restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (t >= n_tok) return;
+  const int lane = threadIdx.x & 63;
+  int64_t r[KM];
+  float g[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    if (j < K) {
+      r[j] = inv ? (int64_t)inv[t * K + j] : t * K + j;
+      g[j] = w[t * K + j];
     }
-    out[i] = s;
+  }
+  for (int e = lane; e < hdv4; e += 64) {
+    f4v s = __builtin_nontemporal_load(o_shared + t * hdv4 + e);
+    f4v o[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < K) o[j] = __builtin_nontemporal_load(o_routed + r[j] * hdv4 + e);
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (j < K) {
+        s.x = fmaf(g[j], o[j].x, s.x);
+        s.y = fmaf(g[j], o[j].y, s.y);
+        s.z = fmaf(g[j], o[j].z, s.z);
+        s.w = fmaf(g[j], o[j].w, s.w);
+      }
+    }
+    __builtin_nontemporal_store(s, out + t * hdv4 + e);
   }
 }
 
@@ -46,9 +65,13 @@ extern "C" mom_status mom_combine(const mom_dims* dims, int32_t n_tok, const int
   MOM_CHECK_PTR(out);
   if (n_tok == 0) return MOM_OK;
   const int hdv4 = dims->H * dims->dv / 4;
-  const int64_t total = (int64_t)n_tok * hdv4;
-  const int blocks = (int)(total / 256 + 1 < 65536 ? total / 256 + 1 : 65536);
-  hipLaunchKernelGGL(k_combine, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (int64_t)n_tok, dims->topk, hdv4,
-                     inv, w, (const float4*)o_routed, (const float4*)o_shared, (float4*)out);
+  const unsigned blocks = (unsigned)(((int64_t)n_tok + 3) / 4);
+#define MOM_COMBINE(KM)                                                                                         \
+  hipLaunchKernelGGL((k_combine<KM>), dim3(blocks), dim3(256), 0, (hipStream_t)stream, (int64_t)n_tok,          \
+                     dims->topk, hdv4, inv, w, (const f4v*)o_routed, (const f4v*)o_shared, (f4v*)out)
+  if (dims->topk <= 2) MOM_COMBINE(2);
+  else if (dims->topk <= 4) MOM_COMBINE(4);
+  else MOM_COMBINE(8);
+#undef MOM_COMBINE
   return launch_status();
 }

@@ -10,11 +10,14 @@
 // the kernel streams the resident float32 states in column slices: one block
 // per (sequence, slot, head, DVB columns) holds its [dk][DVB] slice in
 // registers between the read and the write (64 registers per thread for
-// DVB = 128), so each state is read once and written once and many slices are
-// in flight per compute unit.
+// DVB = 128), so each state is read once and written once (non-temporal: a
+// state is not touched again within the step) and many slices are in flight
+// per compute unit.
 #include "common.h"
 
 namespace mom {
+
+typedef float dv4 __attribute__((ext_vector_type(4)));
 
 template <typename IT, int DK, int DV, int DVB>
 __global__ __launch_bounds__(256) void k_gdn_decode(int n_seq, int H, int M, int K, const int32_t* __restrict__ idx,
@@ -58,7 +61,10 @@ __global__ __launch_bounds__(256) void k_gdn_decode(int n_seq, int H, int M, int
   const int c4 = tid % CPR, rg = tid / CPR;
   float4 reg[RPT];
 #pragma unroll
-  for (int r = 0; r < RPT; ++r) reg[r] = S[(int64_t)(rg + RG * r) * RS4 + c4];
+  for (int r = 0; r < RPT; ++r) {
+    const dv4 t = __builtin_nontemporal_load(reinterpret_cast<const dv4*>(S) + (int64_t)(rg + RG * r) * RS4 + c4);
+    reg[r] = make_float4(t.x, t.y, t.z, t.w);
+  }
   __syncthreads();
   if (tid < 64) {
     float p = 0.f;
@@ -108,7 +114,8 @@ __global__ __launch_bounds__(256) void k_gdn_decode(int n_seq, int H, int M, int
     s2.y = fmaf(kd, u.y, ag * reg[r].y);
     s2.z = fmaf(kd, u.z, ag * reg[r].z);
     s2.w = fmaf(kd, u.w, ag * reg[r].w);
-    S[(int64_t)(rg + RG * r) * RS4 + c4] = s2;
+    const dv4 t2 = {s2.x, s2.y, s2.z, s2.w};
+    __builtin_nontemporal_store(t2, reinterpret_cast<dv4*>(S) + (int64_t)(rg + RG * r) * RS4 + c4);
   }
 }
 
