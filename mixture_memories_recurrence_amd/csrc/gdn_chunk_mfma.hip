@@ -87,9 +87,12 @@ typedef short s4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f16x16 mfma32(const h8v& a, const h8v& b, const f16x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef float f2v __attribute__((ext_vector_type(2)));
+// Two floats to a half pair (round to nearest even; one v_cvt_pk_f16_f32).
 __device__ __forceinline__ unsigned pack_h2(float a, float b) {
-  const _Float16 x = (_Float16)a, y = (_Float16)b;
-  return (unsigned)__builtin_bit_cast(unsigned short, x) | ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
+  const f2v v = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, h2v));
 }
 // Rows [16p, 16p+16) of a 32x32 accumulator tile as the 16-deep operand (k =
 // row) of a 32x32x16 product, row 8q+4g+t scaled by sc[4 (q - 2p) + t].
@@ -284,14 +287,8 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     const f16_t* Ps = Bc + LY::OFF_P;
     const float* Eg = reinterpret_cast<const float*>(Bc + LY::OFF_E);  // gamma_i, then gamma_L / gamma_i
 
-    // ---- the state as an operand (k = key rows)
-    h8v sb[NKD];
-#pragma unroll
-    for (int a = 0; a < ND; ++a) {
-      sb[2 * a] = acc_to_b(S[a], 0, ones);
-      sb[2 * a + 1] = acc_to_b(S[a], 1, ones);
-    }
-    // ---- Y = K S and O^T = S^T Q'^T, two 32-row tiles each (four chains)
+    // ---- Y = K S and O^T = S^T Q'^T, two 32-row tiles each (four chains); the
+    // state becomes an operand (k = key rows) one 16-row block at a time
     f16x16 Y[2], O[2];
 #pragma unroll
     for (int bt = 0; bt < 2; ++bt)
@@ -301,12 +298,14 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
         O[bt][i] = 0.f;
       }
 #pragma unroll
-    for (int kb = 0; kb < NKD; ++kb)
+    for (int kb = 0; kb < NKD; ++kb) {
+      const h8v sb = acc_to_b(S[kb / 2], kb % 2, ones);
 #pragma unroll
       for (int bt = 0; bt < 2; ++bt) {
-        Y[bt] = mfma32(row_frag<DK>(Ks, 32 * bt + c32, kb, g2), sb[kb], Y[bt]);
-        O[bt] = mfma32(sb[kb], row_frag<DK>(Qs, 32 * bt + c32, kb, g2), O[bt]);
+        Y[bt] = mfma32(row_frag<DK>(Ks, 32 * bt + c32, kb, g2), sb, Y[bt]);
+        O[bt] = mfma32(sb, row_frag<DK>(Qs, 32 * bt + c32, kb, g2), O[bt]);
       }
+    }
     CHAIN_PHASE();
     // ---- U = T V - T diag(gamma) Y
     f16x16 U[2];
@@ -314,16 +313,11 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     for (int bt = 0; bt < 2; ++bt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) U[bt][i] = 0.f;
-    h8v tf[2][GC / 16];
-#pragma unroll
-    for (int bt = 0; bt < 2; ++bt)
-#pragma unroll
-      for (int kb = 0; kb < GC / 16; ++kb) tf[bt][kb] = row_frag<GC>(Ts, 32 * bt + c32, kb, g2);
 #pragma unroll
     for (int kb = 0; kb < GC / 16; ++kb) {
       const h8v vb = col_frag<DVB>(Vs, kb, 32 * w, lane);
 #pragma unroll
-      for (int bt = 0; bt < 2; ++bt) U[bt] = mfma32(tf[bt][kb], vb, U[bt]);
+      for (int bt = 0; bt < 2; ++bt) U[bt] = mfma32(row_frag<GC>(Ts, 32 * bt + c32, kb, g2), vb, U[bt]);
     }
 #pragma unroll
     for (int bt = 0; bt < 2; ++bt)
@@ -337,7 +331,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
         }
         const h8v yb = acc_to_b(Y[bt], p, sc);
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi) U[bi] = mfma32(tf[bi][2 * bt + p], yb, U[bi]);
+        for (int bi = 0; bi < 2; ++bi) U[bi] = mfma32(row_frag<GC>(Ts, 32 * bi + c32, 2 * bt + p, g2), yb, U[bi]);
       }
     CHAIN_PHASE();
     // ---- U and diag(gamma_L / gamma) U as operands (k = chunk rows)
