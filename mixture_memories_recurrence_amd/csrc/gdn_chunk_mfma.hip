@@ -415,6 +415,8 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
   constexpr int NKD = DK / 16;
   __shared__ __attribute__((aligned(16))) float As_all[4][GC * PREP_ALD];
   __shared__ float gs_all[4][GC];
+  __shared__ __attribute__((aligned(16))) float cs_all[4][GC];
+  __shared__ __attribute__((aligned(16))) float ys_all[4][16 * 17];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c32 = lane & 31, g2 = lane >> 5;
@@ -433,6 +435,8 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
   const int L = (int)min((int64_t)GC, (int64_t)seg_off[lo + 1] - r0);
   float* As = As_all[w];
   float* gs = gs_all[w];
+  float* cs = cs_all[w];
+  float* ys = ys_all[w];
 
   // gates: lane i holds g_i (inclusive prefix of log alpha; 0 past L) and c_i
   float g = 0.f, bb = 0.f;
@@ -449,7 +453,8 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
   Ews[ch * 2 * GC + lane] = expf(g);
   Ews[ch * 2 * GC + GC + lane] = expf(gL - g);
   gs[lane] = g;
-  wave_lds_fence();  // gs visible to the whole wave
+  cs[lane] = bb;
+  wave_lds_fence();  // gs, cs visible to the whole wave
   // K row pieces (zero past L)
   h8v kf[2][NKD];
 #pragma unroll
@@ -477,7 +482,7 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int i = 32 * ti + 8 * (e / 4) + 4 * g2 + (e % 4);
-      As[i * PREP_ALD + j] = j < i ? expf(gs[i] - gj) * acc[e] : 0.f;
+      As[i * PREP_ALD + j] = j < i ? __expf(gs[i] - gj) * acc[e] : 0.f;
     }
   }
   PREP_PHASE();
@@ -522,35 +527,104 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int i = 32 * ti + 8 * (e / 4) + 4 * g2 + (e % 4);
-        Pout[i * GC + j] = (f16_t)(j <= i ? expf(gs[i] - gj) * acc[e] : 0.f);
+        Pout[i * GC + j] = (f16_t)(j <= i ? __expf(gs[i] - gj) * acc[e] : 0.f);
       }
     }
     PREP_PHASE();
   }
   wave_lds_fence();
-  // A_ij above carries k_i.k_j e^{g_i - g_j}; the row factor c_i is applied here.
-  // x = column `lane` of (I + A)^{-1}: x_i = [i == lane] - sum_{t<i} A_it x_t
-  float xc[GC];
+  // X = (I + A)^{-1}, A = diag(c) A' (A' above carries k_i.k_j e^{g_i - g_j}),
+  // in 16 x 16 blocks X_ij (block rows i, columns j):
+  //   X_bb = (I + A_bb)^{-1}       forward substitution, lane 16 b + cc owns
+  //                                column cc of X_bb (float32 VALU)
+  //   X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj   (i > j)   v_mfma_f32_16x16x4_f32
+  // X_bb overwrites A'_bb in place (no longer needed); X_ij for i > j is kept in
+  // the unused upper block (j, i) of the same array, row r at (16 j + r) * ld.
+  {
+    const int b = lane >> 4, cc = lane & 15;
+    float x[16];
 #pragma unroll
-  for (int i = 0; i < GC; ++i) {
-    const float ci = __shfl(bb, i, 64);
-    float acc = 0.f;
+    for (int r = 0; r < 16; ++r) {
+      const float* arow = As + (16 * b + r) * PREP_ALD + 16 * b;
+      float acc = 0.f;
 #pragma unroll
-    for (int t = 0; t < (i & ~3); t += 4) {
-      const float4 a4 = *reinterpret_cast<const float4*>(As + i * PREP_ALD + t);
-      acc = fmaf(a4.x, xc[t], acc);
-      acc = fmaf(a4.y, xc[t + 1], acc);
-      acc = fmaf(a4.z, xc[t + 2], acc);
-      acc = fmaf(a4.w, xc[t + 3], acc);
+      for (int t = 0; t < (r & ~3); t += 4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(arow + t);
+        acc = fmaf(a4.x, x[t], acc);
+        acc = fmaf(a4.y, x[t + 1], acc);
+        acc = fmaf(a4.z, x[t + 2], acc);
+        acc = fmaf(a4.w, x[t + 3], acc);
+      }
+#pragma unroll
+      for (int t = r & ~3; t < r; ++t) acc = fmaf(arow[t], x[t], acc);
+      x[r] = (r == cc ? 1.f : 0.f) - cs[16 * b + r] * acc;
     }
+    wave_lds_fence();  // every lane's reads of A'_bb are done
 #pragma unroll
-    for (int t = i & ~3; t < i; ++t) acc = fmaf(As[i * PREP_ALD + t], xc[t], acc);
-    xc[i] = (i == lane ? 1.f : 0.f) - ci * acc;
+    for (int r = 0; r < 16; ++r) As[(16 * b + r) * PREP_ALD + 16 * b + cc] = x[r];
+    wave_lds_fence();
   }
-  // T = X diag(c): lane j scales its column by c_j
-  f16_t* Tout = Tws + ch * GC * GC;
+  {
+    const int l16 = lane & 15, lg = lane >> 4;
+    // X_kj as the B operand (rows 4 kb + lg, column l16)
+    auto xblk = [&](int k, int j, int kb) {
+      const int r = 4 * kb + lg;
+      return k == j ? As[(16 * j + r) * PREP_ALD + 16 * j + l16] : As[(16 * j + r) * PREP_ALD + 16 * k + l16];
+    };
 #pragma unroll
-  for (int i = 0; i < GC; ++i) Tout[i * GC + lane] = (f16_t)(xc[i] * bb);
+    for (int i = 1; i < 4; ++i) {
+      const float ci = cs[16 * i + l16];  // row factor of the A operand rows
+#pragma unroll
+      for (int j = i - 1; j >= 0; --j) {
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = j; k < i; ++k)
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const float a = ci * As[(16 * i + l16) * PREP_ALD + 16 * k + 4 * kb + lg];
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, xblk(k, j, kb), y, 0, 0, 0);
+          }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ys[(4 * lg + e) * 17 + l16] = y[e];
+        wave_lds_fence();
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const float a = As[(16 * i + l16) * PREP_ALD + 16 * i + 4 * kb + lg];  // X_ii
+          z = __builtin_amdgcn_mfma_f32_16x16x4f32(a, ys[(4 * kb + lg) * 17 + l16], z, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) As[(16 * j + 4 * lg + e) * PREP_ALD + 16 * i + l16] = -z[e];
+        wave_lds_fence();
+      }
+    }
+  }
+  // T = X diag(c), row i = lane, eight 16-byte pieces (zero above the diagonal)
+  {
+    const int i = lane, ib = i >> 4;
+    f16_t* trow = Tws + (ch * GC + i) * GC;
+#pragma unroll
+    for (int m = 0; m < GC / 8; ++m) {
+      const int jb = m >> 1;
+      half8 hv;
+      if (jb > ib) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hv[e] = (f16_t)0.f;
+      } else {
+        const float* src = jb == ib ? As + i * PREP_ALD + 8 * m
+                                    : As + (16 * jb + (i & 15)) * PREP_ALD + 16 * ib + 8 * (m & 1);
+        const float4 v0 = *reinterpret_cast<const float4*>(src);
+        const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+        const float4 c0 = *reinterpret_cast<const float4*>(cs + 8 * m);
+        const float4 c1 = *reinterpret_cast<const float4*>(cs + 8 * m + 4);
+        const float xv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hv[e] = (f16_t)((jb == ib && 8 * m + e > i) ? 0.f : xv[e] * cv[e]);
+      }
+      *reinterpret_cast<half8*>(trow + 8 * m) = hv;
+    }
+  }
 }
 
 // ------------------------------------------------------------------ workspace + launch
