@@ -166,18 +166,20 @@ __device__ __forceinline__ h8v col_frag(const f16_t* X, int kb, int c0, int lane
   const s4v v8[2] = {a, b};
   return __builtin_bit_cast(h8v, v8);
 }
-// A 64-row tile of RH-half rows, copied by waves [0, NW) into its swizzled LDS
-// image; src(r, c) is the global address of piece c of tile row r.
-template <int RH, int NW, class Src>
-__device__ __forceinline__ void dma_tile(f16_t* dst, int w, int lane, Src src) {
-  constexpr int CPR = RH / 8, RPI = 64 / CPR, NI = GC / RPI;
-#pragma unroll
-  for (int j = 0; j < NI / NW; ++j) {
+// Copy instruction j (of GC / RPI / NW per wave) of a 64-row tile of RH-half
+// rows, copied by waves [0, NW) into its swizzled LDS image; src(r, c) is the
+// global address of piece c of tile row r.
+template <int RH, int NW>
+struct TileCopy {
+  static constexpr int CPR = RH / 8, RPI = 64 / CPR, PER_WAVE = GC / RPI / NW;
+  static_assert(GC % (RPI * NW) == 0, "tile rows split evenly over the waves");
+  template <class Src>
+  __device__ static __forceinline__ void issue(f16_t* dst, int w, int lane, int j, Src src) {
     const int it = w + NW * j;
     const int r = RPI * it + lane / CPR;
     dma_b128(src(r, swz<RH>(r, lane % CPR)), dst + RPI * it * RH);
   }
-}
+};
 
 // Keeps the scheduler from mixing the phases of a chunk, which would raise the
 // number of live registers past the 256 architectural VGPRs.
@@ -231,24 +233,45 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
   const int64_t rbeg = seg_off[s], rend = seg_off[s + 1];
   const int cbase = chunk_base[s];
 
-  // Inputs of the chunk at row r0n into buffer b.  Rows past the segment end
-  // repeat its last row; T is zero in those rows and columns and Q' is zero in
-  // those rows, so they contribute nothing.
-  auto prefetch = [&](int64_t r0n, int b) {
-    const int Ln = (int)min((int64_t)GC, rend - r0n);
-    const int64_t chk = (int64_t)(cbase + (r0n - rbeg) / GC) * H + h;
-    f16_t* B = smem + b * LY::BUF;
-    dma_tile<DK, NW>(B + LY::OFF_K, w, lane, [&](int r, int c) {
-      return k + ((r0n + min(r, Ln - 1)) * H + h) * DK + 8 * c;
-    });
-    dma_tile<DK, NW>(B + LY::OFF_Q, w, lane, [&](int r, int c) { return Qws + (chk * GC + r) * DK + 8 * c; });
-    dma_tile<DVB, NW>(B + LY::OFF_V, w, lane, [&](int r, int c) {
-      return v + ((r0n + min(r, Ln - 1)) * H + h) * dv + cb * DVB + 8 * c;
-    });
-    dma_tile<GC, NW>(B + LY::OFF_T, w, lane, [&](int r, int c) { return Tws + (chk * GC + r) * GC + 8 * c; });
-    dma_tile<GC, NW>(B + LY::OFF_P, w, lane, [&](int r, int c) { return Pws + (chk * GC + r) * GC + 8 * c; });
-    if (w < 2) dma_b32(Ews + chk * 2 * GC + GC * w + lane, B + LY::OFF_E + 2 * GC * w);
+  // Inputs of the chunk at row r0n into buffer b, as NPF copy instructions
+  // per wave (pf_issue(i), i = 0 .. NPF - 1) that can be spread over the
+  // previous chunk's products.  Rows past the segment end repeat its last row;
+  // T is zero in those rows and columns and Q' is zero in those rows, so they
+  // contribute nothing.
+  using CK = TileCopy<DK, NW>;
+  using CV = TileCopy<DVB, NW>;
+  using CT = TileCopy<GC, NW>;
+  constexpr int NPF = 2 * CK::PER_WAVE + CV::PER_WAVE + 2 * CT::PER_WAVE + 1;
+  int64_t pf_r0 = 0, pf_chk = 0;
+  int pf_L = 0;
+  f16_t* pf_B = smem;
+  auto pf_setup = [&](int64_t r0n, int b) {
+    pf_r0 = r0n;
+    pf_L = (int)min((int64_t)GC, rend - r0n);
+    pf_chk = (int64_t)(cbase + (r0n - rbeg) / GC) * H + h;
+    pf_B = smem + b * LY::BUF;
   };
+  auto pf_issue = [&](int i) {
+    if (i < CK::PER_WAVE) {
+      CK::issue(pf_B + LY::OFF_K, w, lane, i, [&](int r, int c) {
+        return k + ((pf_r0 + min(r, pf_L - 1)) * H + h) * DK + 8 * c;
+      });
+    } else if ((i -= CK::PER_WAVE) < CK::PER_WAVE) {
+      CK::issue(pf_B + LY::OFF_Q, w, lane, i, [&](int r, int c) { return Qws + (pf_chk * GC + r) * DK + 8 * c; });
+    } else if ((i -= CK::PER_WAVE) < CV::PER_WAVE) {
+      CV::issue(pf_B + LY::OFF_V, w, lane, i, [&](int r, int c) {
+        return v + ((pf_r0 + min(r, pf_L - 1)) * H + h) * dv + cb * DVB + 8 * c;
+      });
+    } else if ((i -= CV::PER_WAVE) < CT::PER_WAVE) {
+      CT::issue(pf_B + LY::OFF_T, w, lane, i, [&](int r, int c) { return Tws + (pf_chk * GC + r) * GC + 8 * c; });
+    } else if ((i -= CT::PER_WAVE) < CT::PER_WAVE) {
+      CT::issue(pf_B + LY::OFF_P, w, lane, i, [&](int r, int c) { return Pws + (pf_chk * GC + r) * GC + 8 * c; });
+    } else if (w < 2) {
+      dma_b32(Ews + pf_chk * 2 * GC + GC * w + lane, pf_B + LY::OFF_E + 2 * GC * w);
+    }
+  };
+  // copies issued per step of the Y / O loop, the rest during the U loop
+  constexpr int PY = NPF / NKD, PU = (NPF - PY * NKD + GC / 16 - 1) / (GC / 16);
 
   f16x16 S[ND];
   if (state_in) {
@@ -266,7 +289,11 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
       for (int i = 0; i < 16; ++i) S[a][i] = 0.f;
   }
   const float ones[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-  if (rbeg < rend) prefetch(rbeg, 0);
+  if (rbeg < rend) {
+    pf_setup(rbeg, 0);
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) pf_issue(i);
+  }
 
   int buf = 0;
   for (int64_t r0 = rbeg; r0 < rend; r0 += GC, buf ^= 1) {
@@ -277,7 +304,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     if (r0 == rbeg) vm_wait_all();
     else vm_wait_8();
     lds_barrier();  // every wave's part has landed; every wave is done with the other buffer
-    prefetch(r0 + GC < rend ? r0 + GC : r0, buf ^ 1);
+    pf_setup(r0 + GC < rend ? r0 + GC : r0, buf ^ 1);
 
     const f16_t* Bc = smem + buf * LY::BUF;
     const f16_t* Ks = Bc + LY::OFF_K;
@@ -299,6 +326,8 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
       }
 #pragma unroll
     for (int kb = 0; kb < NKD; ++kb) {
+#pragma unroll
+      for (int i = PY * kb; i < PY * (kb + 1); ++i) pf_issue(i);
       const h8v sb = acc_to_b(S[kb / 2], kb % 2, ones);
 #pragma unroll
       for (int bt = 0; bt < 2; ++bt) {
@@ -315,6 +344,9 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
       for (int i = 0; i < 16; ++i) U[bt][i] = 0.f;
 #pragma unroll
     for (int kb = 0; kb < GC / 16; ++kb) {
+#pragma unroll
+      for (int i = PY * NKD + PU * kb; i < PY * NKD + PU * (kb + 1); ++i)
+        if (i < NPF) pf_issue(i);
       const h8v vb = col_frag<DVB>(Vs, kb, 32 * w, lane);
 #pragma unroll
       for (int bt = 0; bt < 2; ++bt) U[bt] = mfma32(row_frag<GC>(Ts, 32 * bt + c32, kb, g2), vb, U[bt]);

@@ -85,19 +85,20 @@ inline int64_t n_tiles_bound(const mom_dims& d, int BM, int BN) {
 // Tiles of BM tokens x BN output features, 2 x NWN waves; wave tile (32 IT)
 // tokens x (32 JF) features = IT x JF tiles of v_mfma_f32_32x32x16_bf16 with the
 // weights as the A operand, so each lane's accumulators hold four consecutive
-// output features.  K-steps of 32 through a 4-stage LDS ring filled by direct
+// output features.  K-steps of BK through an NS-stage LDS ring filled by direct
 // global->LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land at
 // base + 16 l), so the gathered rows never pass through registers.  A stage
-// holds the BM token rows then the BN weight rows, 64 bytes each; piece c of
-// row r sits at position c ^ ((r >> 2) & 3), which keeps the 32-row operand
-// reads conflict-free.  The wave tile sets the LDS traffic per MFMA; a
+// holds the BM token rows then the BN weight rows, 2 BK bytes each, with the
+// 16-byte pieces of each row permuted (ProjCfg::swz) so that the 32-row operand
+// reads are conflict-free.  The wave tile sets the LDS traffic per MFMA; a
 // 128 x 128 wave tile (4 waves on 256 x 256) reads a third fewer bytes per
 // product than 128 x 64, but needs one wave per SIMD for its 256 accumulators,
-// hides less latency than two waves of 128 x 64 and measured slower.
-//   ProjCfg<4, 2, 4>: 256 x 256, 8 waves, wave tile 128 x 64 (large batches)
-//   ProjCfg<2, 2, 2>: 128 x 128, 4 waves, wave tile 64 x 64 (small batches such
-//                     as decode steps)
-constexpr int PL_K = 32, PL_NS = 4;
+// hides less latency than two waves of 128 x 64 and measured slower.  A 64-deep
+// K step with two stages halves the barriers per MFMA of a 32-deep step with
+// four stages in the same LDS and measured 2% faster.
+//   ProjCfg<4, 2, 4, 64, 2>: 256 x 256, 8 waves, wave tile 128 x 64 (large batches)
+//   ProjCfg<2, 2, 2>: 128 x 128, 4 waves, wave tile 64 x 64, 32-deep K steps in
+//                     four stages (small batches such as decode steps)
 
 __device__ __forceinline__ void lds_dma16(const void* g, bf16_t* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
@@ -109,16 +110,22 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int NWN_, int JF_, int IT_>
+template <int NWN_, int JF_, int IT_, int BK_ = 32, int NS_ = 4>
 struct ProjCfg {
-  static constexpr int NWN = NWN_, JF = JF_, IT = IT_;
+  static constexpr int NWN = NWN_, JF = JF_, IT = IT_, BK = BK_, NS = NS_;
   static constexpr int NW = 2 * NWN, THREADS = 64 * NW;
   static constexpr int BM = 2 * 32 * IT, BN = NWN * 32 * JF;
-  static constexpr int STAGE = (BM + BN) * PL_K;  // bf16 elements per ring stage
-  static constexpr int LPW = (BM + BN) / (16 * NW);  // 16-row loads per wave per stage
-  static constexpr size_t LDS = (size_t)PL_NS * STAGE * sizeof(bf16_t);
-  static_assert((BM + BN) % (16 * NW) == 0, "stage rows must split evenly over the waves");
-  static_assert(BM % 16 == 0, "a load never straddles the token and weight rows");
+  static constexpr int CPR = BK / 8;          // 16-byte pieces per stage row
+  static constexpr int RPI = 64 / CPR;        // stage rows per load instruction
+  static constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per ring stage
+  static constexpr int LPW = (BM + BN) / (RPI * NW);  // loads per wave per stage
+  static constexpr size_t LDS = (size_t)NS * STAGE * sizeof(bf16_t);
+  static_assert((BM + BN) % (RPI * NW) == 0, "stage rows must split evenly over the waves");
+  static_assert(BM % RPI == 0, "a load never straddles the token and weight rows");
+  static_assert(BK == 32 || BK == 64, "stage rows of 64 or 128 bytes");
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  // position of 16-byte piece c of stage row r: 32-row operand reads conflict-free
+  __device__ static int swz(int r, int c) { return BK == 32 ? c ^ ((r >> 2) & 3) : c ^ ((r >> 1) & 7); }
 };
 
 template <class CF>
@@ -128,7 +135,8 @@ __global__ __launch_bounds__(CF::THREADS) void k_project_bf16(
     const bf16_t* __restrict__ wk, const bf16_t* __restrict__ wv, f16_t* __restrict__ q, f16_t* __restrict__ k,
     f16_t* __restrict__ v) {
   constexpr int BM = CF::BM, BN = CF::BN, IT = CF::IT, JF = CF::JF, NWN = CF::NWN, LPW = CF::LPW;
-  constexpr int RPW = 16 * LPW;  // stage rows copied by one wave
+  constexpr int BK = CF::BK, NS = CF::NS, CPR = CF::CPR, RPI = CF::RPI;
+  constexpr int RPW = RPI * LPW;  // stage rows copied by one wave
   extern __shared__ __attribute__((aligned(16))) bf16_t smem_l[];
   const int HK = H * dk, HV = H * dv;
   const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
@@ -142,14 +150,14 @@ __global__ __launch_bounds__(CF::THREADS) void k_project_bf16(
   else if (job.kind == 1) W = wk + ((int64_t)job.m * HK + job.col0) * D;
   else W = wv + ((int64_t)job.m * HV + job.col0) * D;
 
-  // loads: wave w, instruction j covers stage rows RPW w + 16 j + lane/4 (token
-  // rows first, then weight rows), LDS position lane%4 holding global piece
-  // (lane%4) ^ ((row >> 2) & 3)
+  // loads: wave w, instruction j covers stage rows RPW w + RPI j + lane / CPR
+  // (token rows first, then weight rows), LDS position lane % CPR holding the
+  // global piece swz(row, lane % CPR)
   const bf16_t* src[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
-    const int R = RPW * w + 16 * j + (lane >> 2);
-    const int c = (lane & 3) ^ ((R >> 2) & 3);
+    const int R = RPW * w + RPI * j + lane / CPR;
+    const int c = CF::swz(R, lane % CPR);
     if (R < BM) {
       int64_t gr = job.trow + R;
       if (gr >= job.rows) gr = job.rows - 1;  // rows past the end reuse the last row; never stored
@@ -160,9 +168,9 @@ __global__ __launch_bounds__(CF::THREADS) void k_project_bf16(
     }
   }
   auto issue = [&](int kt) {
-    bf16_t* st = smem_l + (kt % PL_NS) * CF::STAGE;
+    bf16_t* st = smem_l + (kt % NS) * CF::STAGE;
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) lds_dma16(src[j] + kt * PL_K, st + (RPW * w + 16 * j) * PL_K);
+    for (int j = 0; j < LPW; ++j) lds_dma16(src[j] + kt * BK, st + (RPW * w + RPI * j) * BK);
   };
 
   // acc[jf][it]: element e holds feature (32 JF) wn + 32 jf + 8 (e / 4) + 4 g + (e % 4)
@@ -176,20 +184,20 @@ __global__ __launch_bounds__(CF::THREADS) void k_project_bf16(
       for (int e = 0; e < 16; ++e) acc[jf][it][e] = 0.f;
   const int l32 = lane & 31, g = lane >> 5;
 
-  // Operand pieces of one 16-deep k block of stage kt (ring slot kt % PL_NS).
+  // Operand pieces of one 16-deep k block of stage kt (ring slot kt % NS).
   auto read_frags = [&](int kt, int kb, bfv8* wf, bfv8* xf) {
-    const bf16_t* As = smem_l + (kt % PL_NS) * CF::STAGE;
-    const bf16_t* Bs = As + BM * PL_K;
-    const int ch = 2 * kb + g;  // 16-byte piece of the 64-byte row
+    const bf16_t* As = smem_l + (kt % NS) * CF::STAGE;
+    const bf16_t* Bs = As + BM * BK;
+    const int ch = 2 * kb + g;  // 16-byte piece of the stage row
 #pragma unroll
     for (int jf = 0; jf < JF; ++jf) {
       const int r = 32 * JF * wn + 32 * jf + l32;
-      wf[jf] = *reinterpret_cast<const bfv8*>(Bs + r * PL_K + 8 * (ch ^ ((r >> 2) & 3)));
+      wf[jf] = *reinterpret_cast<const bfv8*>(Bs + r * BK + 8 * CF::swz(r, ch));
     }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int r = (BM / 2) * wm + 32 * it + l32;
-      xf[it] = *reinterpret_cast<const bfv8*>(As + r * PL_K + 8 * (ch ^ ((r >> 2) & 3)));
+      xf[it] = *reinterpret_cast<const bfv8*>(As + r * BK + 8 * CF::swz(r, ch));
     }
   };
   auto mfmas = [&](const bfv8* wf, const bfv8* xf) {
@@ -202,35 +210,42 @@ __global__ __launch_bounds__(CF::THREADS) void k_project_bf16(
   // Stage kt has landed once at most the loads of the stages issued after it
   // (LPW per stage per wave) are outstanding.
   auto wait_stage = [&](int later) {
-    if (later >= 2) wait_vm<2 * LPW>();
-    else if (later == 1) wait_vm<LPW>();
+    if (NS >= 4 && later >= 2) wait_vm<2 * LPW>();
+    else if (NS >= 3 && later >= 1) wait_vm<LPW>();
     else wait_vm<0>();
   };
 
-  // Software pipeline over the two 16-deep halves of each stage: the MFMAs of
-  // one half run while the operand reads of the next half are in flight; the
-  // barrier that publishes stage kt + 1 sits between the two halves of kt.
-  const int nk = D / PL_K;
+  // Software pipeline over the BK / 16 sub-blocks of each stage: the MFMAs of
+  // one sub-block run while the operand reads of the next are in flight; the
+  // barrier that publishes stage kt + 1 sits before the last sub-block of kt.
+  constexpr int KB = BK / 16;
+  const int nk = D / BK;
 #pragma unroll
-  for (int s = 0; s < PL_NS - 1; ++s)
-    if (s < nk) issue(s);
-  wait_stage(min(PL_NS - 2, nk - 1));
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) issue(st);
+  wait_stage(min(NS - 2, nk - 1));
   lds_sync();
-  if (PL_NS - 1 < nk) issue(PL_NS - 1);
-  bfv8 w0[JF], x0[IT], w1[JF], x1[IT];
-  read_frags(0, 0, w0, x0);
+  if (NS - 1 < nk) issue(NS - 1);
+  bfv8 wfr[2][JF], xfr[2][IT];
+  read_frags(0, 0, wfr[0], xfr[0]);
   for (int kt = 0; kt + 1 < nk; ++kt) {
-    read_frags(kt, 1, w1, x1);
-    mfmas(w0, x0);
-    wait_stage(min(PL_NS - 2, nk - 2 - kt));
+#pragma unroll
+    for (int kb = 0; kb + 1 < KB; ++kb) {
+      read_frags(kt, kb + 1, wfr[(kb + 1) & 1], xfr[(kb + 1) & 1]);
+      mfmas(wfr[kb & 1], xfr[kb & 1]);
+    }
+    wait_stage(min(NS - 2, nk - 2 - kt));
     lds_sync();  // stage kt + 1 visible; every wave is done reading stage kt
-    if (kt + PL_NS < nk) issue(kt + PL_NS);
-    read_frags(kt + 1, 0, w0, x0);
-    mfmas(w1, x1);
+    if (kt + NS < nk) issue(kt + NS);
+    read_frags(kt + 1, 0, wfr[KB & 1], xfr[KB & 1]);
+    mfmas(wfr[(KB - 1) & 1], xfr[(KB - 1) & 1]);
   }
-  read_frags(nk - 1, 1, w1, x1);
-  mfmas(w0, x0);
-  mfmas(w1, x1);
+#pragma unroll
+  for (int kb = 0; kb + 1 < KB; ++kb) {
+    read_frags(nk - 1, kb + 1, wfr[(kb + 1) & 1], xfr[(kb + 1) & 1]);
+    mfmas(wfr[kb & 1], xfr[kb & 1]);
+  }
+  mfmas(wfr[(KB - 1) & 1], xfr[(KB - 1) & 1]);
   lds_sync();  // every wave done with the ring: LDS is free for the epilogue
 
   // ---- key rows normalised per head: scl[it][jf] = 1 / |k| of the head that
@@ -470,7 +485,7 @@ extern "C" mom_status mom_project(const mom_dims* dims, const void* x, const int
     if ((d.H * d.dk) % 128 || (d.H * d.dv) % 128) return MOM_ERR_UNSUPPORTED;
     mom_status r;
     if ((d.H * d.dk) % 256 == 0 && (d.H * d.dv) % 256 == 0 && z.NT >= 4096)
-      r = launch_project_bf16<ProjCfg<4, 2, 4>>(d, z, x, perm, seg_off, w_q, w_k, w_v, q, k, v, st);
+      r = launch_project_bf16<ProjCfg<4, 2, 4, 64, 2>>(d, z, x, perm, seg_off, w_q, w_k, w_v, q, k, v, st);
     else
       r = launch_project_bf16<ProjCfg<2, 2, 2>>(d, z, x, perm, seg_off, w_q, w_k, w_v, q, k, v, st);
     if (r != MOM_OK) return r;
