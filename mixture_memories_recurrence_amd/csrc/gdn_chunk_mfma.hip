@@ -14,10 +14,10 @@
 // Only U, O and the new S depend on the entering state, so the work splits in
 // two launches:
 //   k_gdn_prep   fully parallel over (chunk, head): g, A and P from
-//                v_mfma_f32_16x16x32_f16 products, then T by a blocked solve
+//                v_mfma_f32_32x32x16_f16 products, then T by a blocked solve
 //                (16x16 diagonal blocks by forward substitution, off-diagonal
-//                blocks by block products), all in float32.  It stores T, P and
-//                Q' = diag(gamma) Q as half and gamma, gamma_L / gamma as float32.
+//                blocks by block products), all in float32.  It stores T and P
+//                as half and gamma, gamma_L / gamma as float32.
 //   k_gdn_chain  one block per (segment, head, 64 or 128 value columns); it
 //                walks the segment's chunks in order with the state in float32
 //                matrix-core accumulators (see the comment at the kernel).
@@ -63,10 +63,10 @@ __global__ __launch_bounds__(1024) void k_chunk_base(int n_seg, const int32_t* _
 // columns of the state evolve independently, so wave w owns columns
 // [32w, 32w + 32) of its block for every key row: its part of S stays in the
 // float32 accumulators of v_mfma_f32_32x32x16_f16 for the whole segment.
-// Per chunk (rows i, j; K, V, Q' = diag(gamma) Q, T, P from LDS):
+// Per chunk (rows i, j; K, V, Q, T, P and gamma from LDS):
 //   Y   = K S                           (depends on the entering state)
 //   U   = T V - T diag(gamma) Y         (= T V - W S with W = T diag(gamma) K)
-//   O^T = S^T Q'^T + U^T P^T
+//   O^T = S^T Q^T diag(gamma) + U^T P^T
 //   S  <- gamma_L S + K^T diag(gamma_L / gamma) U
 // Every product reads its state-side operand from registers: accumulator rows
 // 8q + 4g + t (lane group g = lane / 32) become the 16-deep operand of the next
@@ -173,6 +173,8 @@ template <int RH, int NW>
 struct TileCopy {
   static constexpr int CPR = RH / 8, RPI = 64 / CPR, PER_WAVE = GC / RPI / NW;
   static_assert(GC % (RPI * NW) == 0, "tile rows split evenly over the waves");
+  // tile row whose piece lane `lane` of wave w copies in instruction j
+  __device__ static __forceinline__ int row(int w, int lane, int j) { return RPI * (w + NW * j) + lane / CPR; }
   template <class Src>
   __device__ static __forceinline__ void issue(f16_t* dst, int w, int lane, int j, Src src) {
     const int it = w + NW * j;
@@ -189,8 +191,8 @@ template <int DK, int NW>
 struct ChainLds {
   static constexpr int DVB = 32 * NW;
   static constexpr int OFF_K = 0, OFF_Q = GC * DK, OFF_V = 2 * GC * DK, OFF_T = OFF_V + GC * DVB,
-                       OFF_P = OFF_T + GC * GC, OFF_E = OFF_P + GC * GC;
-  static constexpr int BUF = OFF_E + 2 * 2 * GC;  // halfs per buffer (E: 2 x 64 float32)
+                       OFF_P = OFF_T + GC * GC, OFF_E = OFF_P + GC * GC, OFF_TOK = OFF_E + 2 * 2 * GC;
+  static constexpr int BUF = OFF_TOK + 2 * GC;  // halfs per buffer (E: 2 x 64 float32, TOK: 64 int32)
   static constexpr size_t BYTES = (size_t)2 * BUF * sizeof(f16_t);
 };
 
@@ -199,8 +201,8 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     int H, int dv, int n_seg, const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_state,
     const int32_t* __restrict__ chunk_base, const f16_t* __restrict__ k, const f16_t* __restrict__ v,
     const f16_t* __restrict__ Tws, const f16_t* __restrict__ Pws, const float* __restrict__ Ews,
-    const f16_t* __restrict__ Qws, const float* __restrict__ state_in, float* __restrict__ state_out,
-    float* __restrict__ o) {
+    const int32_t* __restrict__ row_token, const f16_t* __restrict__ q, const float* __restrict__ state_in,
+    float* __restrict__ state_out, float* __restrict__ o) {
   using LY = ChainLds<DK, NW>;
   constexpr int DVB = LY::DVB, ND = DK / 32, NKD = DK / 16;
   extern __shared__ __attribute__((aligned(16))) f16_t smem[];
@@ -236,20 +238,32 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
   // Inputs of the chunk at row r0n into buffer b, as NPF copy instructions
   // per wave (pf_issue(i), i = 0 .. NPF - 1) that can be spread over the
   // previous chunk's products.  Rows past the segment end repeat its last row;
-  // T is zero in those rows and columns and Q' is zero in those rows, so they
-  // contribute nothing.
+  // T is zero in those rows and columns, so they contribute nothing to the
+  // state, and their outputs are not stored.  Query rows are gathered by token
+  // (row_token; the packed row itself when it is null).  The tokens of a
+  // chunk's rows travel one chunk ahead, in the TOK area of the previous
+  // chunk's buffer, so that no copy waits for an index load (without
+  // row_token the area holds the row numbers).
   using CK = TileCopy<DK, NW>;
   using CV = TileCopy<DVB, NW>;
   using CT = TileCopy<GC, NW>;
-  constexpr int NPF = 2 * CK::PER_WAVE + CV::PER_WAVE + 2 * CT::PER_WAVE + 1;
+  constexpr int NPF = 2 * CK::PER_WAVE + CV::PER_WAVE + 2 * CT::PER_WAVE + 2;
   int64_t pf_r0 = 0, pf_chk = 0;
   int pf_L = 0;
   f16_t* pf_B = smem;
-  auto pf_setup = [&](int64_t r0n, int b) {
+  int qtok[CK::PER_WAVE];  // token of this lane's row in each query copy
+  // tok_lds: the tokens of the chunk's rows in LDS, or null to read them here
+  auto pf_setup = [&](int64_t r0n, int b, const int32_t* tok_lds) {
     pf_r0 = r0n;
     pf_L = (int)min((int64_t)GC, rend - r0n);
     pf_chk = (int64_t)(cbase + (r0n - rbeg) / GC) * H + h;
     pf_B = smem + b * LY::BUF;
+#pragma unroll
+    for (int j = 0; j < CK::PER_WAVE; ++j) {
+      const int r = min(CK::row(w, lane, j), pf_L - 1);
+      if (tok_lds) qtok[j] = tok_lds[r];
+      else qtok[j] = row_token ? row_token[r0n + r] : (int)(r0n + r);
+    }
   };
   auto pf_issue = [&](int i) {
     if (i < CK::PER_WAVE) {
@@ -257,7 +271,8 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
         return k + ((pf_r0 + min(r, pf_L - 1)) * H + h) * DK + 8 * c;
       });
     } else if ((i -= CK::PER_WAVE) < CK::PER_WAVE) {
-      CK::issue(pf_B + LY::OFF_Q, w, lane, i, [&](int r, int c) { return Qws + (pf_chk * GC + r) * DK + 8 * c; });
+      const int64_t t = qtok[i];
+      CK::issue(pf_B + LY::OFF_Q, w, lane, i, [&](int r, int c) { return q + (t * H + h) * DK + 8 * c; });
     } else if ((i -= CK::PER_WAVE) < CV::PER_WAVE) {
       CV::issue(pf_B + LY::OFF_V, w, lane, i, [&](int r, int c) {
         return v + ((pf_r0 + min(r, pf_L - 1)) * H + h) * dv + cb * DVB + 8 * c;
@@ -266,8 +281,12 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
       CT::issue(pf_B + LY::OFF_T, w, lane, i, [&](int r, int c) { return Tws + (pf_chk * GC + r) * GC + 8 * c; });
     } else if ((i -= CT::PER_WAVE) < CT::PER_WAVE) {
       CT::issue(pf_B + LY::OFF_P, w, lane, i, [&](int r, int c) { return Pws + (pf_chk * GC + r) * GC + 8 * c; });
-    } else if (w < 2) {
-      dma_b32(Ews + pf_chk * 2 * GC + GC * w + lane, pf_B + LY::OFF_E + 2 * GC * w);
+    } else if (i == CT::PER_WAVE) {
+      if (w < 2) dma_b32(Ews + pf_chk * 2 * GC + GC * w + lane, pf_B + LY::OFF_E + 2 * GC * w);
+    } else if (w == NW - 1) {  // tokens of the following chunk's rows
+      const int64_t rn = min(pf_r0 + GC + lane, rend - 1);
+      if (row_token) dma_b32(row_token + rn, pf_B + LY::OFF_TOK);
+      else reinterpret_cast<int32_t*>(pf_B + LY::OFF_TOK)[lane] = (int32_t)rn;
     }
   };
   // copies issued per step of the Y / O loop, the rest during the U loop
@@ -290,7 +309,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
   }
   const float ones[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
   if (rbeg < rend) {
-    pf_setup(rbeg, 0);
+    pf_setup(rbeg, 0, nullptr);
 #pragma unroll
     for (int i = 0; i < NPF; ++i) pf_issue(i);
   }
@@ -304,7 +323,8 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     if (r0 == rbeg) vm_wait_all();
     else vm_wait_8();
     lds_barrier();  // every wave's part has landed; every wave is done with the other buffer
-    pf_setup(r0 + GC < rend ? r0 + GC : r0, buf ^ 1);
+    pf_setup(r0 + GC < rend ? r0 + GC : r0, buf ^ 1,
+             reinterpret_cast<const int32_t*>(smem + buf * LY::BUF + LY::OFF_TOK));
 
     const f16_t* Bc = smem + buf * LY::BUF;
     const f16_t* Ks = Bc + LY::OFF_K;
@@ -314,7 +334,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     const f16_t* Ps = Bc + LY::OFF_P;
     const float* Eg = reinterpret_cast<const float*>(Bc + LY::OFF_E);  // gamma_i, then gamma_L / gamma_i
 
-    // ---- Y = K S and O^T = S^T Q'^T, two 32-row tiles each (four chains); the
+    // ---- Y = K S and O^T = S^T Q^T, two 32-row tiles each (four chains); the
     // state becomes an operand (k = key rows) one 16-row block at a time
     f16x16 Y[2], O[2];
 #pragma unroll
@@ -381,7 +401,13 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
         ub[2 * bt + p] = acc_to_b(U[bt], p, ones);
         u2b[2 * bt + p] = acc_to_b(U[bt], p, sc);
       }
-    // ---- O^T += U^T P^T
+    // ---- O^T += U^T P^T, after S^T Q^T is scaled to S^T Q'^T (column i by gamma_i)
+#pragma unroll
+    for (int bt = 0; bt < 2; ++bt) {
+      const float gm = Eg[32 * bt + c32];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) O[bt][i] *= gm;
+    }
 #pragma unroll
     for (int kb = 0; kb < GC / 16; ++kb)
 #pragma unroll
@@ -426,9 +452,8 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
 //   row 32 t + l % 32, halfs 16 kb + 8 (l / 32) .. + 7, for either side);
 //   A_ij = c_i e^{g_i - g_j} k_i.k_j (j < i) to LDS as float32, P_ij =
 //   e^{g_i - g_j} q_i.k_j (j <= i) to global as half;
-//   X = (I + A)^{-1} by forward substitution in float32 with lane j owning
-//   column j (A's rows are read as LDS broadcasts), T = X diag(c) as half;
-//   Q' = diag(gamma) Q as half.
+//   X = (I + A)^{-1} by blocked substitution in float32 (below), T = X diag(c)
+//   as half.
 // Rows at or past the chunk length L are zero in K, Q, A and P; T is then zero
 // in those rows and columns (c = 0 there).
 constexpr int PREP_ALD = GC + 4;  // float row stride of A in LDS
@@ -442,8 +467,7 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
                                                   const int32_t* __restrict__ row_token, const f16_t* __restrict__ q,
                                                   const f16_t* __restrict__ k, const float* __restrict__ alpha_p,
                                                   const float* __restrict__ beta_p, f16_t* __restrict__ Tws,
-                                                  f16_t* __restrict__ Pws, float* __restrict__ Ews,
-                                                  f16_t* __restrict__ Qws) {
+                                                  f16_t* __restrict__ Pws, float* __restrict__ Ews) {
   constexpr int NKD = DK / 16;
   __shared__ __attribute__((aligned(16))) float As_all[4][GC * PREP_ALD];
   __shared__ float gs_all[4][GC];
@@ -518,7 +542,7 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
     }
   }
   PREP_PHASE();
-  // Q row pieces: Q' = diag(gamma) Q, and P = (e^{g_i - g_j} q_i.k_j) for j <= i
+  // Q row pieces and P = (e^{g_i - g_j} q_i.k_j) for j <= i
   f16_t* Pout = Pws + ch * GC * GC;
 #pragma unroll
   for (int ti = 0; ti < 2; ++ti) {
@@ -532,15 +556,6 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
     for (int kb = 0; kb < NKD; ++kb) {
       const h8v z = {}, qv = *reinterpret_cast<const h8v*>(qp + 16 * kb);
       qf[kb] = ok ? qv : z;
-    }
-    const float gam = expf(gs[row]);
-    f16_t* dst = Qws + (ch * GC + row) * DK + 8 * g2;
-#pragma unroll
-    for (int kb = 0; kb < NKD; ++kb) {
-      h8v x = qf[kb];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (f16_t)((float)x[e] * gam);
-      *reinterpret_cast<h8v*>(dst + 16 * kb) = x;
     }
 #pragma unroll
     for (int tj = 0; tj < 2; ++tj) {
@@ -664,7 +679,6 @@ struct ChunkWs {
   int32_t* chunk_base;
   f16_t* T;
   f16_t* P;
-  f16_t* Q;
   float* E;
   size_t bytes;
 };
@@ -682,13 +696,11 @@ inline ChunkWs chunk_ws_layout(void* base, int64_t n_seg, int64_t n_rows, int H,
   const size_t o_t = take((size_t)nch * H * GC * GC * 2);
   const size_t o_p = take((size_t)nch * H * GC * GC * 2);
   const size_t o_e = take((size_t)nch * H * 2 * GC * 4);
-  const size_t o_q = take((size_t)nch * H * GC * dk * 2);
   char* b = (char*)base;
   w.chunk_base = (int32_t*)(b + o_cb);
   w.T = (f16_t*)(b + o_t);
   w.P = (f16_t*)(b + o_p);
   w.E = (float*)(b + o_e);
-  w.Q = (f16_t*)(b + o_q);
   w.bytes = off;
   return w;
 }
@@ -699,8 +711,8 @@ size_t gdn_chunk_ws_bytes(int64_t n_seg, int64_t n_rows, int H, int dk) {
 
 template <int DK, int NW>
 static mom_status launch_chain(const mom_dims& d, int n_seg, const int32_t* seg_off, const int32_t* seg_state,
-                               const ChunkWs& W, const void* k, const void* v, const float* state_in,
-                               float* state_out, float* o, hipStream_t st) {
+                               const ChunkWs& W, const int32_t* row_token, const void* q, const void* k,
+                               const void* v, const float* state_in, float* state_out, float* o, hipStream_t st) {
   using LY = ChainLds<DK, NW>;
   static bool attr = false;  // the dynamic LDS limit is raised once per kernel
   if (!attr) {
@@ -712,8 +724,8 @@ static mom_status launch_chain(const mom_dims& d, int n_seg, const int32_t* seg_
   const int64_t blocks = (int64_t)n_seg * d.H * (d.dv / LY::DVB);
   if (blocks > 0)
     hipLaunchKernelGGL((k_gdn_chain<DK, NW>), dim3((unsigned)blocks), dim3(64 * NW), LY::BYTES, st, d.H, d.dv,
-                       n_seg, seg_off, seg_state, W.chunk_base, (const f16_t*)k, (const f16_t*)v, W.T, W.P, W.E, W.Q,
-                       state_in, state_out, o);
+                       n_seg, seg_off, seg_state, W.chunk_base, (const f16_t*)k, (const f16_t*)v, W.T, W.P, W.E,
+                       row_token, (const f16_t*)q, state_in, state_out, o);
   return MOM_OK;
 }
 
@@ -729,17 +741,15 @@ mom_status launch_gdn_chunk_mfma(const mom_dims& d, int n_seg, int n_rows, const
   if (d.dk == 64) {
     if (prep_blocks > 0)
       hipLaunchKernelGGL((k_gdn_prep<64>), dim3((unsigned)prep_blocks), dim3(256), 0, st, d.H, n_seg, seg_off,
-                         W.chunk_base, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.E,
-                         W.Q);
-    r = d.dv % 128 == 0 ? launch_chain<64, 4>(d, n_seg, seg_off, seg_state, W, k, v, state_in, state_out, o, st)
-                        : launch_chain<64, 2>(d, n_seg, seg_off, seg_state, W, k, v, state_in, state_out, o, st);
+                         W.chunk_base, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.E);
+    r = d.dv % 128 == 0 ? launch_chain<64, 4>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o, st)
+                        : launch_chain<64, 2>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o, st);
   } else {
     if (prep_blocks > 0)
       hipLaunchKernelGGL((k_gdn_prep<128>), dim3((unsigned)prep_blocks), dim3(256), 0, st, d.H, n_seg, seg_off,
-                         W.chunk_base, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.E,
-                         W.Q);
-    r = d.dv % 128 == 0 ? launch_chain<128, 4>(d, n_seg, seg_off, seg_state, W, k, v, state_in, state_out, o, st)
-                        : launch_chain<128, 2>(d, n_seg, seg_off, seg_state, W, k, v, state_in, state_out, o, st);
+                         W.chunk_base, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.E);
+    r = d.dv % 128 == 0 ? launch_chain<128, 4>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o, st)
+                        : launch_chain<128, 2>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o, st);
   }
   if (r != MOM_OK) return r;
   return launch_status();
