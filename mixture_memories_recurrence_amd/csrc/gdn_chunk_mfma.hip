@@ -193,7 +193,9 @@ struct ChainLds {
   static constexpr int OFF_K = 0, OFF_Q = GC * DK, OFF_V = 2 * GC * DK, OFF_T = OFF_V + GC * DVB,
                        OFF_P = OFF_T + GC * GC, OFF_E = OFF_P + GC * GC, OFF_TOK = OFF_E + 2 * 2 * GC;
   static constexpr int BUF = OFF_TOK + 2 * GC;  // halfs per buffer (E: 2 x 64 float32, TOK: 64 int32)
-  static constexpr size_t BYTES = (size_t)2 * BUF * sizeof(f16_t);
+  // after the two buffers: one 32 x 32 float32 output tile per wave
+  static constexpr size_t OST = (size_t)2 * BUF * sizeof(f16_t);
+  static constexpr size_t BYTES = OST + (size_t)NW * 32 * 32 * sizeof(float);
 };
 
 template <int DK, int NW>
@@ -308,6 +310,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
       for (int i = 0; i < 16; ++i) S[a][i] = 0.f;
   }
   const float ones[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+  float* ost = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + LY::OST) + 32 * 32 * w;
   if (rbeg < rend) {
     pf_setup(rbeg, 0, nullptr);
 #pragma unroll
@@ -412,16 +415,24 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     for (int kb = 0; kb < GC / 16; ++kb)
 #pragma unroll
       for (int bt = 0; bt < 2; ++bt) O[bt] = mfma32(ub[kb], row_frag<GC>(Ps, 32 * bt + c32, kb, g2), O[bt]);
+    // O out through this wave's LDS tile, so that each store writes 8 whole
+    // 128-byte rows (lane l: row 8 j + l / 8, columns 4 (l % 8) .. + 3) rather
+    // than 32-byte pieces of 32 rows.  Piece c of tile row r sits at position
+    // c ^ (r & 7).  8 stores (all lanes active unless this is the last chunk).
 #pragma unroll
-    for (int bt = 0; bt < 2; ++bt) {  // 8 stores (all lanes active unless this is the last chunk)
-      const int ri = 32 * bt + c32;
-      if (ri < L) {
-        float* orow = o + ((r0 + ri) * H + h) * dv + ncol0 + 4 * g2;
+    for (int bt = 0; bt < 2; ++bt) {
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-          *reinterpret_cast<float4*>(orow + 8 * qq) =
-              make_float4(O[bt][4 * qq], O[bt][4 * qq + 1], O[bt][4 * qq + 2], O[bt][4 * qq + 3]);
+      for (int qq = 0; qq < 4; ++qq)
+        *reinterpret_cast<float4*>(ost + 32 * c32 + 4 * ((2 * qq + g2) ^ (c32 & 7))) =
+            make_float4(O[bt][4 * qq], O[bt][4 * qq + 1], O[bt][4 * qq + 2], O[bt][4 * qq + 3]);
+      wave_lds_fence();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = 8 * j + (lane >> 3), pc = lane & 7;
+        const float4 val = *reinterpret_cast<const float4*>(ost + 32 * rr + 4 * (pc ^ (rr & 7)));
+        if (32 * bt + rr < L) *reinterpret_cast<float4*>(o + ((r0 + 32 * bt + rr) * H + h) * dv + ncol0 + 4 * pc) = val;
       }
+      wave_lds_fence();  // the tile is read before the next half overwrites it
     }
     // ---- S <- gamma_L S + K^T U', U' = diag(gamma_L / gamma) U
     const float eL = Eg[GC - 1];
