@@ -97,8 +97,12 @@ inline int64_t n_tiles_bound(const mom_dims& d, int BM, int BN) {
 // K step with two stages halves the barriers per MFMA of a 32-deep step with
 // four stages in the same LDS and measured 2% faster.
 //   ProjCfg<4, 2, 4, 64, 2>: 256 x 256, 8 waves, wave tile 128 x 64 (large batches)
-//   ProjCfg<2, 2, 2>: 128 x 128, 4 waves, wave tile 64 x 64, 32-deep K steps in
-//                     four stages (small batches such as decode steps)
+//   ProjCfg<2, 2, 1, 64, 2>: 64 x 128, 4 waves, wave tile 32 x 64 (small batches
+//                     such as decode steps, where a few hundred tiles each walk
+//                     the whole K = D: many short tiles and two 64-deep stages
+//                     in 48 KB of LDS measured 28 us for the 256-sequence
+//                     decode projections against 41 us for 128 x 128 tiles with
+//                     four 32-deep stages)
 
 __device__ __forceinline__ void lds_dma16(const void* g, bf16_t* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
@@ -487,7 +491,7 @@ extern "C" mom_status mom_project(const mom_dims* dims, const void* x, const int
     if ((d.H * d.dk) % 256 == 0 && (d.H * d.dv) % 256 == 0 && z.NT >= 4096)
       r = launch_project_bf16<ProjCfg<4, 2, 4, 64, 2>>(d, z, x, perm, seg_off, w_q, w_k, w_v, q, k, v, st);
     else
-      r = launch_project_bf16<ProjCfg<2, 2, 2>>(d, z, x, perm, seg_off, w_q, w_k, w_v, q, k, v, st);
+      r = launch_project_bf16<ProjCfg<2, 2, 1, 64, 2>>(d, z, x, perm, seg_off, w_q, w_k, w_v, q, k, v, st);
     if (r != MOM_OK) return r;
   } else {
     const int64_t G = n_tiles_bound(d, PF_M, PF_N);
