@@ -29,33 +29,48 @@ constexpr int GC = 64;     // chunk rows
 
 
 // ------------------------------------------------------------------ chunk numbering
-// chunk_base[s] = number of chunks in segments before s; chunk_base[n_seg] = total.
-__global__ __launch_bounds__(1024) void k_chunk_base(int n_seg, const int32_t* __restrict__ seg_off,
-                                                     int32_t* __restrict__ chunk_base) {
-  __shared__ int32_t wsum[16];
-  __shared__ int32_t carry_s;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  if (threadIdx.x == 0) carry_s = 0;
-  __syncthreads();
-  for (int base = 0; base < n_seg; base += 1024) {
-    const int i = base + threadIdx.x;
-    const int32_t v = i < n_seg ? (seg_off[i + 1] - seg_off[i] + GC - 1) / GC : 0;
-    int32_t s = v;
+// The chunks of segment s are numbered from the count of chunks (ceil(len / 64)
+// each) in the segments before it.  Each wave that needs the numbering scans
+// the segments' chunk counts itself, 64 segments per step, so no separate
+// launch computes it.
+__device__ __forceinline__ int seg_chunks(const int32_t* seg_off, int i) {
+  return (seg_off[i + 1] - seg_off[i] + GC - 1) / GC;
+}
+// Chunks in segments [0, s); the same value in every lane.
+__device__ __forceinline__ int chunks_before(const int32_t* __restrict__ seg_off, int s, int lane) {
+  int sum = 0;
+  for (int s0 = 0; s0 < s; s0 += 64) {
+    int n = s0 + lane < s ? seg_chunks(seg_off, s0 + lane) : 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o, 64);
+    sum += n;
+  }
+  return sum;
+}
+// Segment holding chunk c and the number of its first chunk; false when c is
+// at or past the last chunk.  The same result in every lane.
+__device__ __forceinline__ bool locate_chunk(const int32_t* __restrict__ seg_off, int n_seg, int c, int lane,
+                                             int& seg, int& base) {
+  int before = 0;
+  for (int s0 = 0; s0 < n_seg; s0 += 64) {
+    const int n = s0 + lane < n_seg ? seg_chunks(seg_off, s0 + lane) : 0;
+    int incl = n;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int32_t u = __shfl_up(s, o, 64);
-      if (lane >= o) s += u;
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
     }
-    if (lane == 63) wsum[wv] = s;
-    __syncthreads();
-    int32_t pre = carry_s;
-    for (int w2 = 0; w2 < wv; ++w2) pre += wsum[w2];
-    if (i < n_seg) chunk_base[i] = pre + s - v;
-    __syncthreads();
-    if (threadIdx.x == 1023) carry_s = pre + s;
-    __syncthreads();
+    const int first = before + incl - n;  // number of this lane's segment's first chunk
+    const uint64_t hit = __ballot(n > 0 && first <= c && c < first + n);
+    if (hit) {
+      const int l = __ffsll((unsigned long long)hit) - 1;
+      seg = s0 + l;
+      base = __shfl(first, l, 64);
+      return true;
+    }
+    before += __shfl(incl, 63, 64);
   }
-  if (threadIdx.x == 0) chunk_base[n_seg] = carry_s;
+  return false;
 }
 
 // ------------------------------------------------------------------ chain
@@ -201,7 +216,7 @@ struct ChainLds {
 template <int DK, int NW>
 __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     int H, int dv, int n_seg, const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_state,
-    const int32_t* __restrict__ chunk_base, const f16_t* __restrict__ k, const f16_t* __restrict__ v,
+    const f16_t* __restrict__ k, const f16_t* __restrict__ v,
     const f16_t* __restrict__ Tws, const f16_t* __restrict__ Pws, const float* __restrict__ Ews,
     const int32_t* __restrict__ row_token, const f16_t* __restrict__ q, const float* __restrict__ state_in,
     float* __restrict__ state_out, float* __restrict__ o) {
@@ -235,7 +250,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
   const int ncol0 = cb * DVB + 32 * w;
   const int64_t sbase = ((int64_t)slot * H + h) * DK * dv + ncol0;
   const int64_t rbeg = seg_off[s], rend = seg_off[s + 1];
-  const int cbase = chunk_base[s];
+  const int cbase = chunks_before(seg_off, s, lane);
 
   // Inputs of the chunk at row r0n into buffer b, as NPF copy instructions
   // per wave (pf_issue(i), i = 0 .. NPF - 1) that can be spread over the
@@ -474,7 +489,6 @@ constexpr int PREP_ALD = GC + 4;  // float row stride of A in LDS
 
 template <int DK>
 __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_t* __restrict__ seg_off,
-                                                  const int32_t* __restrict__ chunk_base,
                                                   const int32_t* __restrict__ row_token, const f16_t* __restrict__ q,
                                                   const f16_t* __restrict__ k, const float* __restrict__ alpha_p,
                                                   const float* __restrict__ beta_p, f16_t* __restrict__ Tws,
@@ -488,17 +502,10 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c32 = lane & 31, g2 = lane >> 5;
   const int64_t ch = (int64_t)blockIdx.x * 4 + w;  // chunk * H + head
-  const int total = chunk_base[n_seg];
-  if (ch >= (int64_t)total * H) return;  // whole wave; no block barrier below
   const int c = (int)(ch / H), h = (int)(ch % H);
-  // segment of chunk c: the last s with chunk_base[s] <= c
-  int lo = 0, hi = n_seg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (chunk_base[mid] <= c) lo = mid;
-    else hi = mid - 1;
-  }
-  const int64_t r0 = seg_off[lo] + (int64_t)(c - chunk_base[lo]) * GC;
+  int lo, cb0;
+  if (!locate_chunk(seg_off, n_seg, c, lane, lo, cb0)) return;  // whole wave; no block barrier below
+  const int64_t r0 = seg_off[lo] + (int64_t)(c - cb0) * GC;
   const int L = (int)min((int64_t)GC, (int64_t)seg_off[lo + 1] - r0);
   float* As = As_all[w];
   float* gs = gs_all[w];
@@ -687,7 +694,6 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
 
 // ------------------------------------------------------------------ workspace + launch
 struct ChunkWs {
-  int32_t* chunk_base;
   f16_t* T;
   f16_t* P;
   float* E;
@@ -703,12 +709,10 @@ inline ChunkWs chunk_ws_layout(void* base, int64_t n_seg, int64_t n_rows, int H,
     off += (b + 255) / 256 * 256;
     return o;
   };
-  const size_t o_cb = take((size_t)(n_seg + 1) * 4);
   const size_t o_t = take((size_t)nch * H * GC * GC * 2);
   const size_t o_p = take((size_t)nch * H * GC * GC * 2);
   const size_t o_e = take((size_t)nch * H * 2 * GC * 4);
   char* b = (char*)base;
-  w.chunk_base = (int32_t*)(b + o_cb);
   w.T = (f16_t*)(b + o_t);
   w.P = (f16_t*)(b + o_p);
   w.E = (float*)(b + o_e);
@@ -735,7 +739,7 @@ static mom_status launch_chain(const mom_dims& d, int n_seg, const int32_t* seg_
   const int64_t blocks = (int64_t)n_seg * d.H * (d.dv / LY::DVB);
   if (blocks > 0)
     hipLaunchKernelGGL((k_gdn_chain<DK, NW>), dim3((unsigned)blocks), dim3(64 * NW), LY::BYTES, st, d.H, d.dv,
-                       n_seg, seg_off, seg_state, W.chunk_base, (const f16_t*)k, (const f16_t*)v, W.T, W.P, W.E,
+                       n_seg, seg_off, seg_state, (const f16_t*)k, (const f16_t*)v, W.T, W.P, W.E,
                        row_token, (const f16_t*)q, state_in, state_out, o);
   return MOM_OK;
 }
@@ -747,18 +751,17 @@ mom_status launch_gdn_chunk_mfma(const mom_dims& d, int n_seg, int n_rows, const
   const ChunkWs W = chunk_ws_layout(ws, n_seg, n_rows, d.H, d.dk);
   const int64_t nch = (int64_t)n_rows / GC + n_seg;
   const int64_t prep_blocks = (nch * d.H + 3) / 4;  // one wave per (chunk, head)
-  hipLaunchKernelGGL(k_chunk_base, dim3(1), dim3(1024), 0, st, n_seg, seg_off, W.chunk_base);
   mom_status r;
   if (d.dk == 64) {
     if (prep_blocks > 0)
       hipLaunchKernelGGL((k_gdn_prep<64>), dim3((unsigned)prep_blocks), dim3(256), 0, st, d.H, n_seg, seg_off,
-                         W.chunk_base, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.E);
+                         row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.E);
     r = d.dv % 128 == 0 ? launch_chain<64, 4>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o, st)
                         : launch_chain<64, 2>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o, st);
   } else {
     if (prep_blocks > 0)
       hipLaunchKernelGGL((k_gdn_prep<128>), dim3((unsigned)prep_blocks), dim3(256), 0, st, d.H, n_seg, seg_off,
-                         W.chunk_base, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.E);
+                         row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.E);
     r = d.dv % 128 == 0 ? launch_chain<128, 4>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o, st)
                         : launch_chain<128, 2>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o, st);
   }

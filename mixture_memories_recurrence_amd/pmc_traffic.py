@@ -39,7 +39,7 @@ STAGES = {
     "route": (("k_route",), ("route.hip",)),
     "dispatch": (("k_count", "k_scan", "k_scatter"), ("dispatch.hip",)),
     "project": (("k_project",), ("project.hip",)),
-    "chunk": (("k_chunk_base", "k_gdn_prep", "k_gdn_chain", "k_gdn_chunk_valu"),
+    "chunk": (("k_gdn_prep", "k_gdn_chain", "k_gdn_chunk_valu"),
               ("gdn_chunk_mfma.hip", "gdn_chunk_valu.hip")),
     "combine": (("k_combine",), ("combine.hip",)),
 }
