@@ -126,6 +126,108 @@ __global__ __launch_bounds__(256) void k_route(int64_t NT, int D, int M, int K, 
   }
 }
 
+// bfloat16 rows, at most four memories: a wave takes TPW consecutive tokens and
+// loads all their rows at once.  Lane l handles elements 8 l + 512 j + i
+// (i < 8) of every row; its slice of the router rows (EPL = D / 64 values per
+// memory) is loaded once per wave.  Each product goes into float64 by one fma
+// of the two exactly converted inputs, which rounds exactly like the float32
+// product (exact) added in float64.  The four sums of a token are reduced
+// across the 64 lanes by halving exchanges (xor 32, 16: each lane keeps fewer
+// memories) and then a 16-lane butterfly, so every memory's total comes from
+// the same tree and equal router rows give bit-equal logits.  Token i's logits
+// stay in lane i, and lanes 0 .. TPW - 1 then run the top-k and the softmax
+// of their tokens side by side.
+template <int EPL, int TPW>
+__global__ __launch_bounds__(256) void k_route_wave4(int64_t NT, int D, int M, int K, const bf16_t* __restrict__ x,
+                                                     const bf16_t* __restrict__ wr, const float* __restrict__ bias,
+                                                     int32_t* __restrict__ idx, float* __restrict__ w) {
+  constexpr int MT = 4, NL = EPL / 8;
+  using P = ExactProd<bf16_t>;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t n_wave = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  float wf[MT][EPL];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const bf16_t* row = wr + (int64_t)(m < M ? m : M - 1) * D + 8 * lane;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) P::unpack(P::raw(row + 512 * j), &wf[m][8 * j]);
+  }
+  for (int64_t t0 = wave * TPW; t0 < NT; t0 += n_wave * TPW) {
+    typename P::Raw xr[TPW][NL];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int64_t t = t0 + i < NT ? t0 + i : NT - 1;  // past the end: a valid row, never written
+#pragma unroll
+      for (int j = 0; j < NL; ++j) xr[i][j] = P::raw(x + t * D + 8 * lane + 512 * j);
+    }
+    double mine[MT] = {0.0, 0.0, 0.0, 0.0};  // logits of token t0 + lane (lanes < TPW)
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      double acc[MT] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        float xv[8];
+        P::unpack(xr[i][j], xv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double xd = (double)xv[e];
+#pragma unroll
+          for (int m = 0; m < MT; ++m) acc[m] = ::fma(xd, (double)wf[m][8 * j + e], acc[m]);
+        }
+      }
+      // lanes < 32 keep memories 0, 1 and lanes >= 32 keep 2, 3; then bit 4
+      // of the lane picks one of the two: lane l ends with memory l / 16
+      const bool hi = lane >= 32;
+      const double s0 = __shfl_xor(hi ? acc[0] : acc[2], 32, kWave);
+      const double s1 = __shfl_xor(hi ? acc[1] : acc[3], 32, kWave);
+      const double k0 = (hi ? acc[2] : acc[0]) + s0;
+      const double k1 = (hi ? acc[3] : acc[1]) + s1;
+      const bool b = (lane >> 4) & 1;
+      double v = (b ? k1 : k0) + __shfl_xor(b ? k0 : k1, 16, kWave);
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const double lm = __shfl(v, 16 * m, kWave);
+        if (lane == i) mine[m] = lm;
+      }
+    }
+    const int64_t t = t0 + lane;
+    if (lane < TPW && t < NT) {
+      double logit[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) logit[m] = mine[m] + (bias && m < M ? (double)bias[m] : 0.0);
+      uint32_t taken = 0;
+      int sel[MT];
+      double ls[MT];
+      for (int j = 0; j < K; ++j) {
+        int best = -1;
+        double bl = 0.0;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (m < M && !((taken >> m) & 1u) && (best < 0 || logit[m] > bl)) {
+            best = m;
+            bl = logit[m];
+          }
+        }
+        taken |= 1u << best;
+        sel[j] = best;
+        ls[j] = bl;
+      }
+      double z = 0.0, e[MT];
+      for (int j = 0; j < K; ++j) {
+        e[j] = exp(ls[j] - ls[0]);
+        z += e[j];
+      }
+      for (int j = 0; j < K; ++j) {
+        idx[t * K + j] = sel[j];
+        w[t * K + j] = (float)(e[j] / z);
+      }
+    }
+  }
+}
+
 template <typename XT, int G>
 static void launch_route_g(const mom_dims& d, const void* x, const void* wr, const float* bias, int32_t* idx,
                            float* w, hipStream_t st) {
@@ -145,12 +247,26 @@ static void launch_route_g(const mom_dims& d, const void* x, const void* wr, con
 #undef MOM_ROUTE_CASE
 }
 
-// Few tokens (decode): a whole wave per token, so the row is read in few steps;
-// many tokens: 16 lanes per token, four tokens per wave.
+// bfloat16 with at most four memories and D = 1024: k_route_wave4.
+// Otherwise few tokens (decode): a whole wave per token, so the row is read in
+// few steps; many tokens: 16 lanes per token, four tokens per wave.
 template <typename XT>
 static void launch_route(const mom_dims& d, const void* x, const void* wr, const float* bias, int32_t* idx,
                          float* w, hipStream_t st) {
-  if ((int64_t)d.B * d.T < 8192) launch_route_g<XT, 64>(d, x, wr, bias, idx, w, st);
+  const int64_t NT = (int64_t)d.B * d.T;
+  if constexpr (sizeof(XT) == 2) {
+    if (d.M <= 4 && d.D == 1024) {
+      // four rows of x in flight per wave; the router slice, held as float64,
+      // takes 128 registers, so two waves fit per SIMD
+      constexpr int TPW = 4;
+      const int64_t waves = (NT + TPW - 1) / TPW;
+      const int blocks = (int)(((waves < 8192 ? waves : 8192) + 3) / 4);
+      hipLaunchKernelGGL((k_route_wave4<16, TPW>), dim3(blocks), dim3(256), 0, st, NT, d.D, d.M, d.topk,
+                         (const bf16_t*)x, (const bf16_t*)wr, bias, idx, w);
+      return;
+    }
+  }
+  if (NT < 8192) launch_route_g<XT, 64>(d, x, wr, bias, idx, w, st);
   else launch_route_g<XT, 16>(d, x, wr, bias, idx, w, st);
 }
 

@@ -70,6 +70,26 @@ def test_route_ties_and_dense():
         np.testing.assert_allclose(b["w"].cpu().numpy(), w_ref, rtol=0, atol=2e-7)
 
 
+@pytest.mark.parametrize("D", [1024, 2048])
+def test_route_ties_four_memories(D):
+    """Ties and degenerate routers with at most four memories (the wave-per-token
+    router): duplicated router rows, an all-zero router and k = M."""
+    cfg = small(CFG["l380m"], 2, 300, D=D, M=4, K=2)
+    inp = synth.make_layer_inputs(cfg, seed=5)
+    inp["w_r"][3] = inp["w_r"][1]
+    inp["w_r"][2] = inp["w_r"][0]
+    for wr, K, bias in ((inp["w_r"], 2, None), (np.zeros_like(inp["w_r"]), 2, None), (inp["w_r"], 4, None),
+                        (inp["w_r"], 3, np.array([0.5, -0.25, 0.5, 0.0], np.float32))):
+        c = dataclasses.replace(cfg, K=K)
+        layer = mom.MomLayer(c, wr, bias, inp["w_q"], inp["w_k"], inp["w_v"])
+        b = layer.buffers(c.B, c.T)
+        mom.mom_route(b["dims"], gpu_inputs(c, inp)["x"], layer.w_r, layer.bias, b["idx"], b["w"])
+        torch.cuda.synchronize()
+        idx_ref, w_ref = oracle.route(inp["x"], wr, bias, K)
+        np.testing.assert_array_equal(b["idx"].cpu().numpy(), idx_ref)
+        np.testing.assert_allclose(b["w"].cpu().numpy(), w_ref, rtol=0, atol=2e-7)
+
+
 # ------------------------------------------------------------------ dispatch
 @pytest.mark.parametrize("name", list(CFG))
 def test_dispatch_full_size(name):
