@@ -126,14 +126,47 @@ __global__ __launch_bounds__(256) void k_route(int64_t NT, int D, int M, int K, 
   }
 }
 
+// Cross-lane moves of float64 values, one 32-bit half at a time.
+typedef unsigned route_u2 __attribute__((ext_vector_type(2)));
+// a <- [a of lanes 0..31, b of lanes 0..31], b <- [a of lanes 32..63, b of lanes 32..63]
+__device__ __forceinline__ void swap_halves(double& a, double& b) {
+  const route_u2 A = __builtin_bit_cast(route_u2, a), B = __builtin_bit_cast(route_u2, b);
+  const auto lo = __builtin_amdgcn_permlane32_swap(A.x, B.x, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap(A.y, B.y, false, false);
+  a = __builtin_bit_cast(double, route_u2{lo[0], hi[0]});
+  b = __builtin_bit_cast(double, route_u2{lo[1], hi[1]});
+}
+// With 16-lane rows r0..r3: a <- [a.r0, b.r0, a.r2, b.r2], b <- [a.r1, b.r1, a.r3, b.r3]
+__device__ __forceinline__ void swap_rows(double& a, double& b) {
+  const route_u2 A = __builtin_bit_cast(route_u2, a), B = __builtin_bit_cast(route_u2, b);
+  const auto lo = __builtin_amdgcn_permlane16_swap(A.x, B.x, false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap(A.y, B.y, false, false);
+  a = __builtin_bit_cast(double, route_u2{lo[0], hi[0]});
+  b = __builtin_bit_cast(double, route_u2{lo[1], hi[1]});
+}
+// Lane l of each 16-lane row gets lane l - N's value, 0 for the first N lanes (DPP row_shr).
+template <int N>
+__device__ __forceinline__ double row_shr(double v) {
+  const route_u2 V = __builtin_bit_cast(route_u2, v);
+  const route_u2 R = {(unsigned)__builtin_amdgcn_update_dpp(0, (int)V.x, 0x110 + N, 0xF, 0xF, true),
+                      (unsigned)__builtin_amdgcn_update_dpp(0, (int)V.y, 0x110 + N, 0xF, 0xF, true)};
+  return __builtin_bit_cast(double, R);
+}
+__device__ __forceinline__ double read_lane(double v, int l) {
+  const route_u2 V = __builtin_bit_cast(route_u2, v);
+  const route_u2 R = {(unsigned)__builtin_amdgcn_readlane((int)V.x, l), (unsigned)__builtin_amdgcn_readlane((int)V.y, l)};
+  return __builtin_bit_cast(double, R);
+}
+
 // bfloat16 rows, at most four memories: a wave takes TPW consecutive tokens and
 // loads all their rows at once.  Lane l handles elements 8 l + 512 j + i
 // (i < 8) of every row; its slice of the router rows (EPL = D / 64 values per
 // memory) is loaded once per wave.  Each product goes into float64 by one fma
 // of the two exactly converted inputs, which rounds exactly like the float32
 // product (exact) added in float64.  The four sums of a token are reduced
-// across the 64 lanes by halving exchanges (xor 32, 16: each lane keeps fewer
-// memories) and then a 16-lane butterfly, so every memory's total comes from
+// across the 64 lanes by halving exchanges (v_permlane32_swap, then
+// v_permlane16_swap: each lane keeps fewer memories) and then a running sum
+// along each 16-lane row (DPP row shifts), so every memory's total comes from
 // the same tree and equal router rows give bit-equal logits.  Token i's logits
 // stay in lane i, and lanes 0 .. TPW - 1 then run the top-k and the softmax
 // of their tokens side by side.
@@ -176,20 +209,22 @@ __global__ __launch_bounds__(256) void k_route_wave4(int64_t NT, int D, int M, i
           for (int m = 0; m < MT; ++m) acc[m] = ::fma(xd, (double)wf[m][8 * j + e], acc[m]);
         }
       }
-      // lanes < 32 keep memories 0, 1 and lanes >= 32 keep 2, 3; then bit 4
-      // of the lane picks one of the two: lane l ends with memory l / 16
-      const bool hi = lane >= 32;
-      const double s0 = __shfl_xor(hi ? acc[0] : acc[2], 32, kWave);
-      const double s1 = __shfl_xor(hi ? acc[1] : acc[3], 32, kWave);
-      const double k0 = (hi ? acc[2] : acc[0]) + s0;
-      const double k1 = (hi ? acc[3] : acc[1]) + s1;
-      const bool b = (lane >> 4) & 1;
-      double v = (b ? k1 : k0) + __shfl_xor(b ? k0 : k1, 16, kWave);
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+      // lanes 0..31 collect memories 0, 1 and lanes 32..63 memories 2, 3 (pairs
+      // of lanes l, l + 32 added); then row r of 16 lanes collects memory r
+      // (pairs of rows added); a running sum along each row leaves the total
+      // in its last lane.  Vector-ALU lane moves only (no LDS round trips).
+      swap_halves(acc[0], acc[2]);
+      swap_halves(acc[1], acc[3]);
+      double k0 = acc[0] + acc[2], k1 = acc[1] + acc[3];
+      swap_rows(k0, k1);
+      double v = k0 + k1;
+      v += row_shr<1>(v);
+      v += row_shr<2>(v);
+      v += row_shr<4>(v);
+      v += row_shr<8>(v);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const double lm = __shfl(v, 16 * m, kWave);
+        const double lm = read_lane(v, 16 * m + 15);
         if (lane == i) mine[m] = lm;
       }
     }
