@@ -35,6 +35,7 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=20)
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-single", action="store_true", help="skip the single enlarged-memory line")
     p.add_argument("--traffic", default=None,
                    help="summary of measured HBM bytes per call (default: profiles/traffic_<workload>.json)")
     return p.parse_args()
@@ -85,6 +86,49 @@ def time_cpu_baseline(cfg, inp):
     return {"value": NT / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": "fp64 oracle, one layer forward over the whole step batch (%d sequences x %d tokens, %.1f s)"
                       % (B, T, dt)}
+
+
+def time_single_memory(steps, warmup):
+    """One Gated DeltaNet memory with the 380M layer's active state width (value
+    width 768, no router): gdn_chunk_fwd over B sequences as B segments."""
+    import torch
+    from mixture_memories_recurrence_amd import mom, synth
+    sm = synth.SINGLE_MEMORY
+    B, T, H, dk, dv = sm["B"], sm["T"], sm["H"], sm["dk"], sm["dv"]
+    inp = synth.make_single_memory_inputs(B, T, H, dk, dv, seed=11)
+    N = B * T
+    cfg = synth.LayerConfig(B, T, 64, H, dk, dv, 1, 1, "bf16", "none", 64, "single")
+    dims = mom.dims_of(cfg)
+    g = lambda a, dt=torch.float32: torch.from_numpy(a).to(dt).cuda()
+    q, k, v = g(inp["q"], torch.float16), g(inp["k"], torch.float16), g(inp["v"], torch.float16)
+    alpha, beta = g(inp["alpha"]), g(inp["beta"])
+    seg_off = torch.arange(0, N + 1, T, dtype=torch.int32, device="cuda")
+    state = torch.empty(B, H, dk, dv, dtype=torch.float32, device="cuda")
+    o = torch.empty(N, H, dv, dtype=torch.float32, device="cuda")
+    ws = mom.chunk_workspace(dims, B, N)
+
+    def step():
+        mom.gdn_chunk_fwd(dims, B, N, N, B, seg_off, None, None, q, k, v, alpha, beta, None, state, o, ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for _ in range(steps):
+        step()
+    ev[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    # algorithmic bytes: q, k, v read, o written (fp32), state written, gates read
+    nbytes = N * H * (2 * dk * 2 + dv * 2 + 8 + dv * 4) + B * H * dk * dv * 4
+    return {"workload": "single Gated DeltaNet memory: B=%d T=%d H=%d dk=%d dv=%d (the 380M layer's active "
+                        "state width), half q/k/v, fp32 state and output" % (B, T, H, dk, dv),
+            "tokens_per_s": round(N / (wall / steps), 1), "ms_per_step": round(wall * 1e3 / steps, 4),
+            "kernel_ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def main():
@@ -227,6 +271,9 @@ def main():
                          "decode_kernel_ms": round(dk_ms, 4),
                          "decode_kernel_GB/s": round(dc["bytes"] / (dk_ms * 1e-3) / 1e9, 1),
                          "decode_kernel_hbm_frac": round(dc["bytes"] / (dk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    if not args.no_single:
+        res["single_memory"] = time_single_memory(args.steps, args.warmup)
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = time_cpu_baseline(cfg, inp)

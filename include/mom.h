@@ -57,7 +57,8 @@
  * carries 8x the precision of bfloat16 into the recurrence's matrix-core
  * products.  Gates, router weights, outputs and states are always float32.
  *
- * Supported shapes: dk in {64,128}; dv in {64,128,256}; chunk == 64;
+ * Supported shapes: dk in {64,128}; dv in {64,128,256}, and for every entry
+ * point but gdn_decode_step also any multiple of 128 up to 1024; chunk == 64;
  * D % 64 == 0, 64 <= D <= 8192; 1 <= topk <= M <= 64, topk <= 8; B,T >= 1;
  * N < 2^31.
  */

@@ -54,7 +54,9 @@ inline mom_status check_dims(const mom_dims* d) {
   if (d->topk > d->M) return MOM_ERR_DIMS;
   if (d->M > 64 || d->topk > 8) return MOM_ERR_UNSUPPORTED;
   if (d->dk != 64 && d->dk != 128) return MOM_ERR_UNSUPPORTED;
-  if (d->dv != 64 && d->dv != 128 && d->dv != 256) return MOM_ERR_UNSUPPORTED;
+  // 64, 128 or 256 everywhere; a multiple of 128 up to 1024 for the entry points
+  // other than gdn_decode_step (which rejects it)
+  if (d->dv != 64 && !(d->dv % 128 == 0 && d->dv >= 128 && d->dv <= 1024)) return MOM_ERR_UNSUPPORTED;
   if (d->chunk != 64) return MOM_ERR_UNSUPPORTED;
   if (d->dtype != MOM_DTYPE_F32 && d->dtype != MOM_DTYPE_BF16) return MOM_ERR_UNSUPPORTED;
   if (d->D < 64 || d->D > 8192 || d->D % 64 != 0) return MOM_ERR_UNSUPPORTED;

@@ -151,6 +151,7 @@ extern "C" mom_status gdn_decode_step(const mom_dims* dims, int32_t n_seq, const
   using namespace mom;
   mom_status s = check_dims(dims);
   if (s != MOM_OK) return s;
+  if (dims->dv != 64 && dims->dv != 128 && dims->dv != 256) return MOM_ERR_UNSUPPORTED;
   if (n_seq < 0) return MOM_ERR_DIMS;
   MOM_CHECK_PTR(idx);
   MOM_CHECK_PTR(inv);

@@ -63,6 +63,11 @@ CONFIGS = {
 # decode workload that follows the long-context prefill
 DECODE_SEQS = 256
 
+# One Gated DeltaNet memory whose value width equals the 380M layer's active
+# state (k + 1 = 3 memories of 256 value columns): the single enlarged memory
+# the pages compare the mixture with, with no router.
+SINGLE_MEMORY = dict(B=8, T=2048, H=4, dk=128, dv=768)
+
 
 def round_bf16(a: np.ndarray) -> np.ndarray:
     """fp32 -> nearest bfloat16 (ties to even), returned as fp32 values."""
@@ -141,3 +146,19 @@ def make_chain_inputs(n_rows: int, H: int, dk: int, dv: int, seed: int, store: s
     cast = np.float16 if store == "f16" else np.float32
     return dict(q=q.astype(cast).astype(np.float32), k=k.astype(cast).astype(np.float32),
                 v=v.astype(cast).astype(np.float32), alpha=alpha, beta=beta)
+
+
+def make_single_memory_inputs(B: int, T: int, H: int, dk: int, dv: int, seed: int) -> dict:
+    """Inputs of one plain Gated DeltaNet memory over B sequences of T tokens
+    (rows in token order): q ~ N(0,1), keys normalised per head, values ~
+    N(0,1), gates as in the layer.  q, k, v are exact in half precision."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    n = B * T
+    q = g.standard_normal((n, H, dk))
+    k = g.standard_normal((n, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = g.standard_normal((n, H, dv))
+    alpha = g.uniform(0.9, 1.0, (n, H)).astype(np.float32)
+    beta = g.uniform(0.0, 1.0, (n, H)).astype(np.float32)
+    h = lambda a: a.astype(np.float16).astype(np.float32)
+    return dict(q=h(q), k=h(k), v=h(v), alpha=alpha, beta=beta)

@@ -51,8 +51,8 @@ ODD = ctypes.c_void_p(0x10004)
 
 @needs_lib
 @pytest.mark.parametrize("field,value,status", [
-    ("dk", 96, -3), ("dv", 32, -3), ("chunk", 32, -3), ("D", 1000, -3), ("M", 65, -3), ("topk", 9, -3),
-    ("topk", 0, -2), ("B", 0, -2), ("T", -1, -2), ("dtype", 7, -3), ("topk", 5, -2)])
+    ("dk", 96, -3), ("dv", 32, -3), ("dv", 192, -3), ("dv", 1152, -3), ("chunk", 32, -3), ("D", 1000, -3),
+    ("M", 65, -3), ("topk", 9, -3), ("topk", 0, -2), ("B", 0, -2), ("T", -1, -2), ("dtype", 7, -3), ("topk", 5, -2)])
 def test_bad_dims_are_rejected(field, value, status):
     d = _dims(**{field: value})
     if field == "topk" and value == 9:
@@ -60,6 +60,16 @@ def test_bad_dims_are_rejected(field, value, status):
     L = mom.lib()
     assert L.mom_route(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, None) == status
     assert L.mom_workspace_bytes(ctypes.byref(d), 0) == 0
+
+
+@needs_lib
+def test_wide_values_only_outside_decode():
+    """A value width that is a multiple of 128 above 256 passes the shared
+    checks (the chunk recurrence takes it) but gdn_decode_step rejects it."""
+    d = _dims(dv=768)
+    L = mom.lib()
+    assert L.mom_workspace_bytes(ctypes.byref(d), 0) > 0
+    assert L.gdn_decode_step(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -3
 
 
 @needs_lib

@@ -268,6 +268,38 @@ def test_chunk_segments(store, dk, dv):
     assert np.all(np.isnan(sg[unused]))
 
 
+@pytest.mark.parametrize("B,T,full", [(2, 300, False), (8, 2048, True)])
+def test_single_memory_enlarged(B, T, full):
+    """One plain Gated DeltaNet memory of value width 768 (the 380M layer's
+    active state width) through gdn_chunk_fwd, one segment per sequence, no
+    router: at a ragged small size every (sequence, head), at the benchmark's
+    full size two (sequence, head) slices the oracle recomputes."""
+    sm = synth.SINGLE_MEMORY
+    H, dk, dv = sm["H"], sm["dk"], sm["dv"]
+    inp = synth.make_single_memory_inputs(B, T, H, dk, dv, seed=11)
+    N = B * T
+    cfg = synth.LayerConfig(B, T, 64, H, dk, dv, 1, 1, "bf16", "none", 64, "single")
+    dims = mom.dims_of(cfg)
+    f16 = lambda a: to_gpu(a, torch.float16)
+    so = torch.full((B, H, dk, dv), float("nan"), device="cuda")
+    o = torch.full((N, H, dv), float("nan"), device="cuda")
+    seg_off = np.arange(0, N + 1, T, dtype=np.int32)
+    log("single memory", B, T)
+    mom.gdn_chunk_fwd(dims, B, N, N, B, to_gpu(seg_off), None, None, f16(inp["q"]), f16(inp["k"]), f16(inp["v"]),
+                      to_gpu(inp["alpha"]), to_gpu(inp["beta"]), None, so, o, mom.chunk_workspace(dims, B, N))
+    torch.cuda.synchronize()
+    og, sg = o.cpu().numpy(), so.cpu().numpy()
+    pairs = [(0, 0), (B - 1, H - 1)] if full else [(b, h) for b in range(B) for h in range(H)]
+    o_got, o_ref, s_got, s_ref = [], [], [], []
+    for b, h in pairs:
+        r = slice(b * T, (b + 1) * T)
+        ref, S = oracle.gdn_chain(inp["q"][r, h], inp["k"][r, h], inp["v"][r, h], inp["alpha"][r, h],
+                                  inp["beta"][r, h])
+        o_got.append(og[r, h]); o_ref.append(ref); s_got.append(sg[b, h]); s_ref.append(S)
+    assert_close("o", np.stack(o_got), np.stack(o_ref), *TOL["bf16"])
+    assert_close("state", np.stack(s_got), np.stack(s_ref), *TOL["bf16"])
+
+
 def test_chunk_in_place_and_zero_state():
     H, dk, dv = 1, 128, 128
     lens = np.array([100, 64])
