@@ -182,8 +182,41 @@ void oracle_gdn_step(int dk, int dv, double a, double c, const double* q, const 
   }
 }
 
+/* One step of gated linear attention, the plain linear recurrence that the
+ * other update rules modify ([p1] "Linear Recurrent Memory": the basic
+ * linear-attention RNN update, with gates and update rules as variations of
+ * it; [p2] "Summary": MoM works with different update rules).  The formula
+ * on [p1] was lost in extraction; the reading taken here keeps the Gated
+ * DeltaNet gate inputs and drops the delta correction:
+ *   forget:  S~ = a * S
+ *   write:   S  = S~ + c * k v^T
+ *   read:    o  = S^T q          (after the write)
+ * a = c = 1 is plain causal linear attention.                                */
+void oracle_gla_step(int dk, int dv, double a, double c, const double* q, const double* k,
+                     const double* v, double* S, double* o) {
+  for (int i = 0; i < dk * dv; ++i) S[i] *= a;
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) S[i * dv + j] += c * k[i] * v[j];
+  for (int j = 0; j < dv; ++j) {
+    double s = 0.0;
+    for (int i = 0; i < dk; ++i) s += S[i * dv + j] * q[i];
+    o[j] = s;
+  }
+}
+
+/* Update rules of a memory: 0 = Gated DeltaNet, 1 = gated linear attention. */
+typedef void (*oracle_step_fn)(int, int, double, double, const double*, const double*, const double*,
+                               double*, double*);
+static oracle_step_fn step_of(int rule) { return rule == 1 ? oracle_gla_step : oracle_gdn_step; }
+
 /* The recurrence over one memory's own token sequence (length L): rows are the
  * tokens routed to that memory, in order.  q/k [L][dk], v/o [L][dv], a/c [L]. */
+void oracle_gla_chain(int64_t L, int dk, int dv, const double* q, const double* k, const double* v,
+                      const double* a, const double* c, double* S, double* o) {
+  for (int64_t i = 0; i < L; ++i)
+    oracle_gla_step(dk, dv, a[i], c[i], q + i * dk, k + i * dk, v + i * dv, S, o + i * dv);
+}
+
 void oracle_gdn_chain(int64_t L, int dk, int dv, const double* q, const double* k, const double* v,
                       const double* a, const double* c, double* S, double* o) {
   for (int64_t i = 0; i < L; ++i)
@@ -215,11 +248,12 @@ void oracle_gdn_chain(int64_t L, int dk, int dv, const double* q, const double* 
  *   q_out [NT][H][dk], k_out/v_out [NT][K+1][H][dk|dv]  projected vectors
  *                                 (slot K = shared memory)
  * Work is split over (b, h) pairs, which are independent.                    */
-void oracle_layer(const int32_t* dims, const double* x, const double* wr, const double* bias,
-                  const double* wq, const double* wk, const double* wv, const double* alpha,
-                  const double* beta, const double* state0, int32_t* idx, double* w,
-                  double* o_routed, double* o_shared, double* out, double* out_mixed,
-                  double* state, double* q_out, double* k_out, double* v_out) {
+void oracle_layer_rule(int rule, const int32_t* dims, const double* x, const double* wr, const double* bias,
+                       const double* wq, const double* wk, const double* wv, const double* alpha,
+                       const double* beta, const double* state0, int32_t* idx, double* w,
+                       double* o_routed, double* o_shared, double* out, double* out_mixed,
+                       double* state, double* q_out, double* k_out, double* v_out) {
+  const oracle_step_fn step = step_of(rule);
   const int B = dims[0], T = dims[1], D = dims[2], H = dims[3], dk = dims[4], dv = dims[5];
   const int M = dims[6], K = dims[7];
   const int64_t NT = (int64_t)B * T;
@@ -271,7 +305,7 @@ void oracle_layer(const int32_t* dims, const double* x, const double* wr, const 
         const double* vt = v_all + ((tok * (K + 1) + j) * H + h) * dv;
         const double a = alpha[(tok * H + h) * (M + 1) + m];
         const double c = beta[(tok * H + h) * (M + 1) + m];
-        oracle_gdn_step(dk, dv, a, c, qt, kt, vt, S + m * ssz, o + j * dv);
+        step(dk, dv, a, c, qt, kt, vt, S + m * ssz, o + j * dv);
       }
       for (int e = 0; e < dv; ++e) {
         double s = o[K * dv + e];
@@ -311,6 +345,16 @@ void oracle_layer(const int32_t* dims, const double* x, const double* wr, const 
   if (!w) free(w_l);
 }
 
+/* The layer with Gated DeltaNet memories. */
+void oracle_layer(const int32_t* dims, const double* x, const double* wr, const double* bias,
+                  const double* wq, const double* wk, const double* wv, const double* alpha,
+                  const double* beta, const double* state0, int32_t* idx, double* w,
+                  double* o_routed, double* o_shared, double* out, double* out_mixed,
+                  double* state, double* q_out, double* k_out, double* v_out) {
+  oracle_layer_rule(0, dims, x, wr, bias, wq, wk, wv, alpha, beta, state0, idx, w, o_routed, o_shared, out,
+                    out_mixed, state, q_out, k_out, v_out);
+}
+
 /* The sum out[t][h][:] = o_shared[t][h][:] + sum_j w[t][j] * o_routed[row(t,j)][h][:],
  * shared memory first, then j ascending.  o_routed rows are addressed through
  * inv (NULL = row t*K + j).  Used to check the combine step on its own.        */
@@ -334,10 +378,11 @@ void oracle_combine(int64_t n_tok, int K, int H, int dv, const int32_t* inv, con
  * row_token[row] (q [n_tok][H][dk]); k/v/a/c/o are indexed by row
  * (k [N][H][dk], v/o [N][H][dv], a/c [N][H]).  Only the segments listed in
  * `which` (n_which of them) are run; NULL = all.  Parallel over (segment, head). */
-void oracle_segments(int n_seg, const int32_t* seg_off, const int32_t* seg_state,
-                     const int32_t* row_token, int H, int dk, int dv, const double* q,
-                     const double* k, const double* v, const double* a, const double* c,
-                     double* state, double* o, int n_which, const int32_t* which) {
+void oracle_segments_rule(int rule, int n_seg, const int32_t* seg_off, const int32_t* seg_state,
+                          const int32_t* row_token, int H, int dk, int dv, const double* q,
+                          const double* k, const double* v, const double* a, const double* c,
+                          double* state, double* o, int n_which, const int32_t* which) {
+  const oracle_step_fn step = step_of(rule);
   const int n_jobs = (which ? n_which : n_seg) * H;
   const int64_t ssz = (int64_t)dk * dv;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -347,10 +392,18 @@ void oracle_segments(int n_seg, const int32_t* seg_off, const int32_t* seg_state
     double* S = state + ((int64_t)seg_state[s] * H + h) * ssz;
     for (int64_t r = seg_off[s]; r < seg_off[s + 1]; ++r) {
       const int64_t tk = row_token ? row_token[r] : r;
-      oracle_gdn_step(dk, dv, a[r * H + h], c[r * H + h], q + (tk * H + h) * dk,
-                      k + (r * H + h) * dk, v + (r * H + h) * dv, S, o + (r * H + h) * dv);
+      step(dk, dv, a[r * H + h], c[r * H + h], q + (tk * H + h) * dk, k + (r * H + h) * dk,
+           v + (r * H + h) * dv, S, o + (r * H + h) * dv);
     }
   }
+}
+
+void oracle_segments(int n_seg, const int32_t* seg_off, const int32_t* seg_state,
+                     const int32_t* row_token, int H, int dk, int dv, const double* q,
+                     const double* k, const double* v, const double* a, const double* c,
+                     double* state, double* o, int n_which, const int32_t* which) {
+  oracle_segments_rule(0, n_seg, seg_off, seg_state, row_token, H, dk, dv, q, k, v, a, c, state, o, n_which,
+                       which);
 }
 
 /* Projections of one head for a list of tokens: for i < n with token

@@ -100,9 +100,36 @@ def gdn_chain(q, k, v, a, c, S0=None):
     return o, S
 
 
+# update rules of a memory (mom_oracle.c): Gated DeltaNet, gated linear attention
+RULES = {"gdn": 0, "gla": 1}
+
+
+def gla_step(q, k, v, a, c, S):
+    """One gated linear attention step; S [dk][dv] is updated in place (float64)."""
+    q, k, v = _d(q), _d(k), _d(v)
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    dk, dv = S.shape
+    o = np.empty(dv, np.float64)
+    lib().oracle_gla_step(dk, dv, ctypes.c_double(a), ctypes.c_double(c), _p(q), _p(k), _p(v),
+                          _p(S), _p(o))
+    return o
+
+
+def gla_chain(q, k, v, a, c, S0=None):
+    """Gated linear attention over one memory's rows: returns (o [L][dv], S_final)."""
+    q, k, v, a, c = _d(q), _d(k), _d(v), _d(a), _d(c)
+    L, dk = k.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else _d(S0).copy()
+    o = np.empty((L, dv), np.float64)
+    lib().oracle_gla_chain(ctypes.c_int64(L), dk, dv, _p(q), _p(k), _p(v), _p(a), _p(c), _p(S), _p(o))
+    return o, S
+
+
 def layer(dims, x, w_r, bias, w_q, w_k, w_v, alpha, beta, state0=None, mixed=False,
-          want_qkv=False):
-    """Whole layer forward.  dims = (B, T, D, H, dk, dv, M, K)."""
+          want_qkv=False, rule="gdn"):
+    """Whole layer forward.  dims = (B, T, D, H, dk, dv, M, K); rule "gdn" (Gated
+    DeltaNet memories) or "gla" (gated linear attention memories)."""
     B, T, D, H, dk, dv, M, K = [int(v) for v in dims]
     NT = B * T
     args = [_d(a) for a in (x, w_r, bias, w_q, w_k, w_v, alpha, beta, state0)]
@@ -115,7 +142,7 @@ def layer(dims, x, w_r, bias, w_q, w_k, w_v, alpha, beta, state0=None, mixed=Fal
         k=np.empty((NT, K + 1, H, dk)) if want_qkv else None,
         v=np.empty((NT, K + 1, H, dv)) if want_qkv else None)
     dims_a = np.array([B, T, D, H, dk, dv, M, K], np.int32)
-    lib().oracle_layer(_p(dims_a), *[_p(a) for a in args], _p(res["idx"]), _p(res["w"]),
+    lib().oracle_layer_rule(RULES[rule], _p(dims_a), *[_p(a) for a in args], _p(res["idx"]), _p(res["w"]),
                        _p(res["o_routed"]), _p(res["o_shared"]), _p(res["out"]),
                        _p(res["out_mixed"]), _p(res["state"]), _p(res["q"]), _p(res["k"]),
                        _p(res["v"]))
@@ -133,7 +160,7 @@ def combine(inv, w, o_routed, o_shared):
     return out
 
 
-def segments(seg_off, seg_state, row_token, q, k, v, a, c, state, which=None):
+def segments(seg_off, seg_state, row_token, q, k, v, a, c, state, which=None, rule="gdn"):
     """Run the recurrence over packed segments.  `state` (float64 [n_state][H][dk][dv])
     is updated in place; returns o [N][H][dv] (rows of segments not run are NaN)."""
     seg_off, seg_state, row_token, which = _i(seg_off), _i(seg_state), _i(row_token), _i(which)
@@ -143,7 +170,7 @@ def segments(seg_off, seg_state, row_token, q, k, v, a, c, state, which=None):
     dv = v.shape[2]
     o = np.full((N, H, dv), np.nan)
     n_seg = seg_off.shape[0] - 1
-    lib().oracle_segments(n_seg, _p(seg_off), _p(seg_state), _p(row_token), H, dk, dv, _p(q), _p(k),
+    lib().oracle_segments_rule(RULES[rule], n_seg, _p(seg_off), _p(seg_state), _p(row_token), H, dk, dv, _p(q), _p(k),
                           _p(v), _p(a), _p(c), _p(state), _p(o), 0 if which is None else len(which),
                           _p(which))
     return o

@@ -21,10 +21,10 @@ def _tiny_inputs(B=2, T=7, D=8, H=2, dk=3, dv=3, M=3, K=2, seed=0, bias="none"):
     return cfg, synth.make_layer_inputs(cfg, seed)
 
 
-def _run_layer(cfg, inp, state0=None, mixed=False, want_qkv=False):
+def _run_layer(cfg, inp, state0=None, mixed=False, want_qkv=False, rule="gdn"):
     dims = (cfg.B, cfg.T, cfg.D, cfg.H, cfg.dk, cfg.dv, cfg.M, cfg.K)
     return oracle.layer(dims, inp["x"], inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"],
-                        inp["alpha"], inp["beta"], state0=state0, mixed=mixed, want_qkv=want_qkv)
+                        inp["alpha"], inp["beta"], state0=state0, mixed=mixed, want_qkv=want_qkv, rule=rule)
 
 
 # --------------------------------------------------------------------------- router
@@ -263,8 +263,95 @@ def test_chunk_form_equals_token_recurrence(C):
     np.testing.assert_allclose(S2, S, rtol=1e-10, atol=1e-10)
 
 
+# --------------------------------------------------------------------------- gated linear attention
+def _gla_closed_form(q, k, v, a, c, S0):
+    """o_t = sum_{s<=t} (prod_{s<r<=t} a_r) c_s (q_t . k_s) v_s + (prod_{r<=t} a_r) S0^T q_t,
+    summed directly (no recurrence)."""
+    L = q.shape[0]
+    o = np.zeros((L, v.shape[1]))
+    for t in range(L):
+        o[t] = np.prod(a[:t + 1]) * (S0.T @ q[t])
+        for s_ in range(t + 1):
+            o[t] += np.prod(a[s_ + 1:t + 1]) * c[s_] * (q[t] @ k[s_]) * v[s_]
+    S = np.prod(a) * S0 + sum(np.prod(a[s_ + 1:]) * c[s_] * np.outer(k[s_], v[s_]) for s_ in range(L))
+    return o, S
+
+
+@pytest.mark.parametrize("L", [1, 2, 9])
+def test_gla_matches_closed_form(L):
+    rng = np.random.default_rng(40 + L)
+    dk, dv = 4, 3
+    q, k, v = rng.standard_normal((L, dk)), rng.standard_normal((L, dk)), rng.standard_normal((L, dv))
+    a, c = rng.uniform(0.5, 1.0, L), rng.uniform(0.0, 1.0, L)
+    S0 = rng.standard_normal((dk, dv))
+    o, S = oracle.gla_chain(q, k, v, a, c, S0)
+    o2, S2 = _gla_closed_form(q, k, v, a, c, S0)
+    np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S, S2, rtol=1e-12, atol=1e-12)
+
+
+def test_gla_without_gates_is_causal_linear_attention():
+    """a = c = 1 from a zero state: O = tril(Q K^T) V."""
+    rng = np.random.default_rng(7)
+    L, dk, dv = 40, 8, 5
+    q, k, v = rng.standard_normal((L, dk)), rng.standard_normal((L, dk)), rng.standard_normal((L, dv))
+    o, S = oracle.gla_chain(q, k, v, np.ones(L), np.ones(L))
+    np.testing.assert_allclose(o, np.tril(q @ k.T) @ v, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(S, k.T @ v, rtol=1e-12, atol=1e-12)
+
+
+def _chunk_la(q, k, v, a, c, S0, C):
+    """The chunk form the GPU path uses for gated linear attention: per chunk,
+    U = diag(c) V, O = diag(gamma) Q S + P U, S <- gamma_L S + (diag(gamma_L/gamma) K)^T U."""
+    L = q.shape[0]
+    out = np.zeros((L, v.shape[1]))
+    S = S0.copy()
+    for s in range(0, L, C):
+        e = min(L, s + C)
+        g = np.cumsum(np.log(a[s:e]))
+        G = np.exp(g[:, None] - g[None, :])
+        U = c[s:e, None] * v[s:e]
+        P = np.tril(G * (q[s:e] @ k[s:e].T))
+        out[s:e] = np.exp(g)[:, None] * (q[s:e] @ S) + P @ U
+        S = np.exp(g[-1]) * S + (np.exp(g[-1] - g)[:, None] * k[s:e]).T @ U
+    return out, S
+
+
+@pytest.mark.parametrize("C", [1, 5, 64])
+def test_gla_chunk_form_equals_token_recurrence(C):
+    rng = np.random.default_rng(100 + C)
+    L, dk, dv = 130, 16, 8
+    q, k, v = rng.standard_normal((L, dk)), rng.standard_normal((L, dk)), rng.standard_normal((L, dv))
+    a, c = rng.uniform(0.9, 1.0, L), rng.uniform(0.0, 1.0, L)
+    S0 = rng.standard_normal((dk, dv)) * 0.1
+    o, S = oracle.gla_chain(q, k, v, a, c, S0)
+    o2, S2 = _chunk_la(q, k, v, a, c, S0, C)
+    np.testing.assert_allclose(o2, o, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(S2, S, rtol=1e-10, atol=1e-10)
+
+
+def test_gla_layer_matches_independent_numpy():
+    cfg, inp = _tiny_inputs(B=2, T=6, D=8, H=2, dk=3, dv=2, M=3, K=2, seed=3, bias="normal")
+    S0 = synth.make_state(cfg, cfg.B, seed=9, scale=0.5).astype(np.float64)
+    r = _run_layer(cfg, inp, state0=S0, rule="gla")
+    out, S_fin, sel = _numpy_layer(cfg, inp, S0, rec=_gla_closed_form)
+    np.testing.assert_array_equal(r["idx"], sel)
+    np.testing.assert_allclose(r["out"], out, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(r["state"], S_fin, rtol=1e-11, atol=1e-12)
+
+
+def test_gla_mixture_equivalence():
+    """The weighted sum of per-memory reads equals the read from the weighted
+    mixture of memories for this update rule too (the read is linear in S)."""
+    cfg, inp = _tiny_inputs(B=2, T=20, D=16, H=2, dk=8, dv=6, M=4, K=2)
+    r = _run_layer(cfg, inp, mixed=True, rule="gla")
+    np.testing.assert_allclose(r["out"], r["out_mixed"], rtol=1e-12, atol=1e-12)
+    r2 = _run_layer(cfg, inp)
+    assert np.abs(r["out"] - r2["out"]).max() > 1e-3  # a different rule gives a different layer
+
+
 # --------------------------------------------------------------------------- layer
-def _numpy_layer(cfg, inp, S0):
+def _numpy_layer(cfg, inp, S0, rec=None):
     """Independent tiny layer: subset-enumeration routing, scipy softmax,
     product-form recurrence per memory, weighted sum of reads."""
     x = inp["x"].astype(np.float64)
@@ -288,7 +375,7 @@ def _numpy_layer(cfg, inp, S0):
                 vs = np.stack([(inp["w_v"][m].astype(np.float64) @ x[t])[h * dv:(h + 1) * dv] for t in toks])
                 a = np.array([inp["alpha"][t, h, m] for t in toks], np.float64)
                 c = np.array([inp["beta"][t, h, m] for t in toks], np.float64)
-                o, S = _product_form(qs, ks, vs, a, c, S0[b, m, h])
+                o, S = (rec or _product_form)(qs, ks, vs, a, c, S0[b, m, h])
                 S_fin[b, m, h] = S
                 for i, t in enumerate(toks):
                     wgt = 1.0 if m == M else scipy.special.softmax(lg[t, sel[t]])[sel[t].index(m)]
