@@ -36,6 +36,7 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-single", action="store_true", help="skip the single enlarged-memory line")
+    p.add_argument("--no-gla", action="store_true", help="skip the gated linear attention layer line")
     p.add_argument("--traffic", default=None,
                    help="summary of measured HBM bytes per call (default: profiles/traffic_<workload>.json)")
     return p.parse_args()
@@ -86,6 +87,26 @@ def time_cpu_baseline(cfg, inp):
     return {"value": NT / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": "fp64 oracle, one layer forward over the whole step batch (%d sequences x %d tokens, %.1f s)"
                       % (B, T, dt)}
+
+
+def time_gla_layer(cfg, inp, x, alpha, beta, steps, warmup):
+    """The same layer, inputs and weights with gated linear attention memories
+    (S <- a S + c k v^T) in place of Gated DeltaNet: whole forward steps."""
+    import torch
+    from mixture_memories_recurrence_amd import mom
+    layer = mom.MomLayer(cfg, inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"], rule="gla")
+    state = torch.empty(cfg.B, cfg.M + 1, cfg.H, cfg.dk, cfg.dv, dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        layer.forward(x, alpha, beta, state_out=state)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.forward(x, alpha, beta, state_out=state)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    NT = cfg.B * cfg.T
+    return {"workload": "%s layer with gated linear attention memories (same shapes, inputs and weights)" % cfg.name,
+            "tokens_per_s": round(NT / (wall / steps), 1), "ms_per_step": round(wall * 1e3 / steps, 4)}
 
 
 def time_single_memory(steps, warmup):
@@ -271,6 +292,9 @@ def main():
                          "decode_kernel_ms": round(dk_ms, 4),
                          "decode_kernel_GB/s": round(dc["bytes"] / (dk_ms * 1e-3) / 1e9, 1),
                          "decode_kernel_hbm_frac": round(dc["bytes"] / (dk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    if not args.no_gla:
+        res["gla_layer"] = time_gla_layer(cfg, inp, x, alpha, beta, args.steps, args.warmup)
 
     if not args.no_single:
         res["single_memory"] = time_single_memory(args.steps, args.warmup)

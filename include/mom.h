@@ -18,6 +18,11 @@
  *                    implementation section: each memory reuses the
  *                    single-memory operator; the gist.science page, "Core
  *                    mechanism", restates the forget/delta update).
+ *   gla_chunk_fwd    the same operator for memories that use gated linear
+ *                    attention, the plain linear update that the other rules
+ *                    modify (jxzklqfsx.com write-up, "Linear Recurrent Memory";
+ *                    research.elamur.ai summary: MoM works with different
+ *                    update rules).
  *   gdn_decode_step  one recurrent step per sequence (constant-cost inference,
  *                    jxzklqfsx.com write-up, introduction and inference section).
  *   mom_combine      router-weighted sum of the per-memory reads plus the
@@ -150,6 +155,18 @@ mom_status mom_project(const mom_dims* dims, const void* x, const int32_t* perm,
  * gdn_chunk_workspace_bytes(dims, n_seg, n_rows) bytes (may be NULL when that
  * is 0); its contents on entry do not matter.                                */
 mom_status gdn_chunk_fwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
+                         int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
+                         const int32_t* row_token, const void* q, const void* k, const void* v,
+                         const float* alpha_p, const float* beta_p, const float* state_in,
+                         float* state_out, float* o, void* ws, size_t ws_bytes, void* stream);
+
+/* gla_chunk_fwd: as gdn_chunk_fwd (same arguments, layouts, workspace,
+ * ownership and errors) for memories whose update is gated linear attention:
+ *   S <- a S;  S <- S + c k v^T;  o = S^T q      (a = alpha, c = beta)
+ * (a = c = 1: plain causal linear attention).  The pages' formula for this
+ * basic linear update was lost in extraction; this reading keeps the Gated
+ * DeltaNet gate inputs and drops the delta correction. */
+mom_status gla_chunk_fwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
                          int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
                          const int32_t* row_token, const void* q, const void* k, const void* v,
                          const float* alpha_p, const float* beta_p, const float* state_in,

@@ -8,11 +8,11 @@ template <typename IT>
 mom_status launch_gdn_chunk_valu(const mom_dims& d, int n_seg, const int32_t* seg_off, const int32_t* seg_state,
                                  const int32_t* row_token, const void* q, const void* k, const void* v,
                                  const float* alpha_p, const float* beta_p, const float* state_in, float* state_out,
-                                 float* o, hipStream_t st);
+                                 float* o, bool delta, hipStream_t st);
 mom_status launch_gdn_chunk_mfma(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
                                  const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
                                  const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
-                                 float* state_out, float* o, void* ws, hipStream_t st);
+                                 float* state_out, float* o, void* ws, bool delta, hipStream_t st);
 size_t gdn_chunk_ws_bytes(int64_t n_seg, int64_t n_rows, int H, int dk);
 }  // namespace mom
 
@@ -23,12 +23,13 @@ extern "C" size_t gdn_chunk_workspace_bytes(const mom_dims* dims, int32_t n_seg,
   return gdn_chunk_ws_bytes(n_seg, n_rows, dims->H, dims->dk);
 }
 
-extern "C" mom_status gdn_chunk_fwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
-                                    int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
-                                    const int32_t* row_token, const void* q, const void* k, const void* v,
-                                    const float* alpha_p, const float* beta_p, const float* state_in,
-                                    float* state_out, float* o, void* ws, size_t ws_bytes, void* stream) {
-  using namespace mom;
+namespace mom {
+// Validation and dispatch shared by the two update rules.
+static mom_status chunk_fwd(bool delta, const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
+                            int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
+                            const int32_t* row_token, const void* q, const void* k, const void* v,
+                            const float* alpha_p, const float* beta_p, const float* state_in, float* state_out,
+                            float* o, void* ws, size_t ws_bytes, void* stream) {
   mom_status s = check_dims(dims);
   if (s != MOM_OK) return s;
   if (n_seg < 0 || n_rows < 0 || n_tok < 0 || n_state < 0) return MOM_ERR_DIMS;
@@ -53,9 +54,28 @@ extern "C" mom_status gdn_chunk_fwd(const mom_dims* dims, int32_t n_seg, int32_t
   hipStream_t st = (hipStream_t)stream;
   if (dims->dtype == MOM_DTYPE_BF16)
     return launch_gdn_chunk_mfma(*dims, n_seg, n_rows, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
-                                 state_in, state_out, o, ws, st);
+                                 state_in, state_out, o, ws, delta, st);
   return launch_gdn_chunk_valu<float>(*dims, n_seg, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
-                                      state_in, state_out, o, st);
+                                      state_in, state_out, o, delta, st);
+}
+}  // namespace mom
+
+extern "C" mom_status gdn_chunk_fwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
+                                    int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
+                                    const int32_t* row_token, const void* q, const void* k, const void* v,
+                                    const float* alpha_p, const float* beta_p, const float* state_in,
+                                    float* state_out, float* o, void* ws, size_t ws_bytes, void* stream) {
+  return mom::chunk_fwd(true, dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v, alpha_p,
+                        beta_p, state_in, state_out, o, ws, ws_bytes, stream);
+}
+
+extern "C" mom_status gla_chunk_fwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
+                                    int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
+                                    const int32_t* row_token, const void* q, const void* k, const void* v,
+                                    const float* alpha_p, const float* beta_p, const float* state_in,
+                                    float* state_out, float* o, void* ws, size_t ws_bytes, void* stream) {
+  return mom::chunk_fwd(false, dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v,
+                        alpha_p, beta_p, state_in, state_out, o, ws, ws_bytes, stream);
 }
 
 extern "C" size_t mom_workspace_bytes(const mom_dims* dims, int32_t which) {

@@ -12,7 +12,9 @@
 //   O = diag(gamma) Q S + P U,          P_ij = e^{g_i-g_j} q_i.k_j (j<=i)
 //   S <- gamma_L S + (diag(gamma_L / gamma) K)^T U
 // Only U, O and the new S depend on the entering state, so the work splits in
-// two launches:
+// two launches.  The same two kernels, with DELTA false, run memories that use
+// gated linear attention instead (S_i = a_i S_{i-1} + c_i k_i v_i^T): there
+// A = 0, so T = diag(c), W is not needed and U = T V.
 //   k_gdn_prep   fully parallel over (chunk, head): g, A and P from
 //                v_mfma_f32_32x32x16_f16 products, then T by a blocked solve
 //                (16x16 diagonal blocks by forward substitution, off-diagonal
@@ -213,7 +215,7 @@ struct ChainLds {
   static constexpr size_t BYTES = OST + (size_t)NW * 32 * 32 * sizeof(float);
 };
 
-template <int DK, int NW>
+template <int DK, int NW, bool DELTA>
 __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     int H, int dv, int n_seg, const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_state,
     const f16_t* __restrict__ k, const f16_t* __restrict__ v,
@@ -393,6 +395,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     for (int bt = 0; bt < 2; ++bt)
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
+        if (!DELTA) continue;  // gated linear attention: U = T V (T = diag(c)); Y is then unused
         float sc[8];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -487,7 +490,7 @@ constexpr int PREP_ALD = GC + 4;  // float row stride of A in LDS
 // every operand of the kernel in registers at once.
 #define PREP_PHASE() __builtin_amdgcn_sched_barrier(0)
 
-template <int DK>
+template <int DK, bool DELTA>
 __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_t* __restrict__ seg_off,
                                                   const int32_t* __restrict__ row_token, const f16_t* __restrict__ q,
                                                   const f16_t* __restrict__ k, const float* __restrict__ alpha_p,
@@ -544,7 +547,7 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
   }
   // A' = e^{g_i - g_j} k_i.k_j (j < i), lower tiles (ti, tj) = (0,0), (1,0), (1,1)
 #pragma unroll
-  for (int x = 0; x < 3; ++x) {
+  for (int x = 0; x < (DELTA ? 3 : 0); ++x) {
     const int ti = x == 0 ? 0 : 1, tj = x == 2 ? 1 : 0;
     f16x16 acc;
 #pragma unroll
@@ -598,6 +601,18 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
     PREP_PHASE();
   }
   wave_lds_fence();
+  if constexpr (!DELTA) {
+    // gated linear attention: T = diag(c), row i = lane (zero past L: c = 0 there)
+    f16_t* trow = Tws + (ch * GC + lane) * GC;
+#pragma unroll
+    for (int m = 0; m < GC / 8; ++m) {
+      half8 hv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = (f16_t)(8 * m + e == lane ? cs[lane] : 0.f);
+      *reinterpret_cast<half8*>(trow + 8 * m) = hv;
+    }
+    return;
+  }
   // X = (I + A)^{-1}, A = diag(c) A' (A' above carries k_i.k_j e^{g_i - g_j}),
   // in 16 x 16 blocks X_ij (block rows i, columns j):
   //   X_bb = (I + A_bb)^{-1}       forward substitution, lane 16 b + cc owns
@@ -724,49 +739,60 @@ size_t gdn_chunk_ws_bytes(int64_t n_seg, int64_t n_rows, int H, int dk) {
   return chunk_ws_layout(nullptr, n_seg, n_rows, H, dk).bytes;
 }
 
-template <int DK, int NW>
+template <int DK, int NW, bool DELTA>
 static mom_status launch_chain(const mom_dims& d, int n_seg, const int32_t* seg_off, const int32_t* seg_state,
                                const ChunkWs& W, const int32_t* row_token, const void* q, const void* k,
                                const void* v, const float* state_in, float* state_out, float* o, hipStream_t st) {
   using LY = ChainLds<DK, NW>;
   static bool attr = false;  // the dynamic LDS limit is raised once per kernel
   if (!attr) {
-    if (hipFuncSetAttribute((const void*)k_gdn_chain<DK, NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    if (hipFuncSetAttribute((const void*)k_gdn_chain<DK, NW, DELTA>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)LY::BYTES) != hipSuccess)
       return MOM_ERR_LAUNCH;
     attr = true;
   }
   const int64_t blocks = (int64_t)n_seg * d.H * (d.dv / LY::DVB);
   if (blocks > 0)
-    hipLaunchKernelGGL((k_gdn_chain<DK, NW>), dim3((unsigned)blocks), dim3(64 * NW), LY::BYTES, st, d.H, d.dv,
+    hipLaunchKernelGGL((k_gdn_chain<DK, NW, DELTA>), dim3((unsigned)blocks), dim3(64 * NW), LY::BYTES, st, d.H, d.dv,
                        n_seg, seg_off, seg_state, (const f16_t*)k, (const f16_t*)v, W.T, W.P, W.E,
                        row_token, (const f16_t*)q, state_in, state_out, o);
   return MOM_OK;
 }
 
-mom_status launch_gdn_chunk_mfma(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
-                                 const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
-                                 const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
-                                 float* state_out, float* o, void* ws, hipStream_t st) {
+template <int DK, bool DELTA>
+static mom_status launch_chunk(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
+                               const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
+                               const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
+                               float* state_out, float* o, void* ws, hipStream_t st) {
   const ChunkWs W = chunk_ws_layout(ws, n_seg, n_rows, d.H, d.dk);
   const int64_t nch = (int64_t)n_rows / GC + n_seg;
   const int64_t prep_blocks = (nch * d.H + 3) / 4;  // one wave per (chunk, head)
-  mom_status r;
-  if (d.dk == 64) {
-    if (prep_blocks > 0)
-      hipLaunchKernelGGL((k_gdn_prep<64>), dim3((unsigned)prep_blocks), dim3(256), 0, st, d.H, n_seg, seg_off,
-                         row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.E);
-    r = d.dv % 128 == 0 ? launch_chain<64, 4>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o, st)
-                        : launch_chain<64, 2>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o, st);
-  } else {
-    if (prep_blocks > 0)
-      hipLaunchKernelGGL((k_gdn_prep<128>), dim3((unsigned)prep_blocks), dim3(256), 0, st, d.H, n_seg, seg_off,
-                         row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.E);
-    r = d.dv % 128 == 0 ? launch_chain<128, 4>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o, st)
-                        : launch_chain<128, 2>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o, st);
-  }
+  if (prep_blocks > 0)
+    hipLaunchKernelGGL((k_gdn_prep<DK, DELTA>), dim3((unsigned)prep_blocks), dim3(256), 0, st, d.H, n_seg,
+                       seg_off, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.E);
+  const mom_status r =
+      d.dv % 128 == 0
+          ? launch_chain<DK, 4, DELTA>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o, st)
+          : launch_chain<DK, 2, DELTA>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o, st);
   if (r != MOM_OK) return r;
   return launch_status();
+}
+
+// delta: Gated DeltaNet memories; otherwise gated linear attention (T = diag(c)
+// and no W S term).
+mom_status launch_gdn_chunk_mfma(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
+                                 const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
+                                 const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
+                                 float* state_out, float* o, void* ws, bool delta, hipStream_t st) {
+  if (d.dk == 64)
+    return delta ? launch_chunk<64, true>(d, n_seg, n_rows, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
+                                          state_in, state_out, o, ws, st)
+                 : launch_chunk<64, false>(d, n_seg, n_rows, seg_off, seg_state, row_token, q, k, v, alpha_p,
+                                           beta_p, state_in, state_out, o, ws, st);
+  return delta ? launch_chunk<128, true>(d, n_seg, n_rows, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
+                                         state_in, state_out, o, ws, st)
+               : launch_chunk<128, false>(d, n_seg, n_rows, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
+                                          state_in, state_out, o, ws, st);
 }
 
 }  // namespace mom

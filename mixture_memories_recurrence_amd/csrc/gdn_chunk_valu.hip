@@ -13,6 +13,9 @@
 //   S  <- e^{g_L} S + sum_j e^{g_L-g_j} k_j u_j^T
 // Value columns evolve independently, so one block owns (segment, head,
 // 32-column block) and the grid spreads over all of them.
+// With DELTA false the memories use gated linear attention instead
+// (S_i = a_i S_{i-1} + c_i k_i v_i^T): A = 0 and R = diag(c) V, so the
+// substitution and the K S product drop out.
 #include "common.h"
 
 namespace mom {
@@ -20,7 +23,7 @@ namespace mom {
 constexpr int VC = 64;    // chunk rows
 constexpr int VDVB = 32;  // value columns per block
 
-template <typename IT, int DK>
+template <typename IT, int DK, bool DELTA>
 __global__ __launch_bounds__(256) void k_gdn_chunk_valu(int H, int dv, int n_seg, const int32_t* __restrict__ seg_off,
                                                         const int32_t* __restrict__ seg_state,
                                                         const int32_t* __restrict__ row_token, const IT* __restrict__ q,
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(256) void k_gdn_chunk_valu(int H, int dv, int n_seg
           qk = fmaf(Qs[i][d], Ks[j][d], qk);
         }
         const float dec = expf(gs[i] - gs[j]);
-        if (j < i) a = bs[i] * dec * kk;
+        if (DELTA && j < i) a = bs[i] * dec * kk;
         p = dec * qk;
       }
       As[i][j] = a;
@@ -91,16 +94,20 @@ __global__ __launch_bounds__(256) void k_gdn_chunk_valu(int H, int dv, int n_seg
       const int i = e / VDVB, n = e % VDVB;
       float r = 0.f;
       if (i < L) {
-        float ks = 0.f;
-        for (int d = 0; d < DK; ++d) ks = fmaf(Ks[i][d], Ss[d][n], ks);
         const float vv = load_as_f32(v + ((r0 + i) * H + h) * dv + cb * VDVB + n);
-        r = bs[i] * (vv - expf(gs[i]) * ks);
+        if (DELTA) {
+          float ks = 0.f;
+          for (int d = 0; d < DK; ++d) ks = fmaf(Ks[i][d], Ss[d][n], ks);
+          r = bs[i] * (vv - expf(gs[i]) * ks);
+        } else {
+          r = bs[i] * vv;
+        }
       }
       Us[i][n] = r;
     }
     __syncthreads();
     // (I + A) U = R, one thread per value column
-    if (tid < VDVB) {
+    if (DELTA && tid < VDVB) {
       for (int i = 1; i < L; ++i) {
         float u = Us[i][tid];
         for (int j = 0; j < i; ++j) u = fmaf(-As[i][j], Us[j][tid], u);
@@ -140,15 +147,20 @@ template <typename IT>
 mom_status launch_gdn_chunk_valu(const mom_dims& d, int n_seg, const int32_t* seg_off, const int32_t* seg_state,
                                  const int32_t* row_token, const void* q, const void* k, const void* v,
                                  const float* alpha_p, const float* beta_p, const float* state_in, float* state_out,
-                                 float* o, hipStream_t st) {
+                                 float* o, bool delta, hipStream_t st) {
   const int64_t blocks = (int64_t)n_seg * d.H * (d.dv / VDVB);
   if (blocks == 0) return MOM_OK;
-#define MOM_VALU_CASE(DK)                                                                                         \
-  hipLaunchKernelGGL((k_gdn_chunk_valu<IT, DK>), dim3((unsigned)blocks), dim3(256), 0, st, d.H, d.dv, n_seg,     \
-                     seg_off, seg_state, row_token, (const IT*)q, (const IT*)k, (const IT*)v, alpha_p, beta_p,     \
-                     state_in, state_out, o)
-  if (d.dk == 64) MOM_VALU_CASE(64);
-  else MOM_VALU_CASE(128);
+#define MOM_VALU_CASE(DK, DELTA)                                                                                  \
+  hipLaunchKernelGGL((k_gdn_chunk_valu<IT, DK, DELTA>), dim3((unsigned)blocks), dim3(256), 0, st, d.H, d.dv,     \
+                     n_seg, seg_off, seg_state, row_token, (const IT*)q, (const IT*)k, (const IT*)v, alpha_p,      \
+                     beta_p, state_in, state_out, o)
+  if (d.dk == 64) {
+    if (delta) MOM_VALU_CASE(64, true);
+    else MOM_VALU_CASE(64, false);
+  } else {
+    if (delta) MOM_VALU_CASE(128, true);
+    else MOM_VALU_CASE(128, false);
+  }
 #undef MOM_VALU_CASE
   return launch_status();
 }
@@ -156,10 +168,10 @@ mom_status launch_gdn_chunk_valu(const mom_dims& d, int n_seg, const int32_t* se
 template mom_status launch_gdn_chunk_valu<float>(const mom_dims&, int, const int32_t*, const int32_t*,
                                                  const int32_t*, const void*, const void*, const void*,
                                                  const float*, const float*, const float*, float*, float*,
-                                                 hipStream_t);
+                                                 bool, hipStream_t);
 template mom_status launch_gdn_chunk_valu<f16_t>(const mom_dims&, int, const int32_t*, const int32_t*,
                                                  const int32_t*, const void*, const void*, const void*,
                                                  const float*, const float*, const float*, float*, float*,
-                                                 hipStream_t);
+                                                 bool, hipStream_t);
 
 }  // namespace mom

@@ -52,6 +52,8 @@ def lib():
         "mom_project": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
         "gdn_chunk_fwd": [D, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                           _VP, ctypes.c_size_t, _VP],
+        "gla_chunk_fwd": [D, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                          _VP, ctypes.c_size_t, _VP],
         "gdn_decode_step": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
         "mom_combine": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP],
         "mom_workspace_bytes": [D, _I32],
@@ -69,8 +71,8 @@ def lib():
     return L
 
 
-EXPORTS = ("mom_route", "mom_dispatch", "mom_project", "gdn_chunk_fwd", "gdn_decode_step", "mom_combine",
-           "mom_workspace_bytes", "gdn_chunk_workspace_bytes", "mom_status_string")
+EXPORTS = ("mom_route", "mom_dispatch", "mom_project", "gdn_chunk_fwd", "gla_chunk_fwd", "gdn_decode_step",
+           "mom_combine", "mom_workspace_bytes", "gdn_chunk_workspace_bytes", "mom_status_string")
 
 
 def dims_of(cfg: LayerConfig, B: int | None = None, T: int | None = None) -> MomDims:
@@ -122,6 +124,15 @@ def gdn_chunk_fwd(dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_t
                                _p(state_out), _p(o), _p(ws), nbytes, _s(stream)), "gdn_chunk_fwd")
 
 
+def gla_chunk_fwd(dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
+                  state_in, state_out, o, ws=None, stream=None):
+    """As gdn_chunk_fwd, for gated linear attention memories (S <- a S + c k v^T)."""
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().gla_chunk_fwd(ctypes.byref(dims), n_seg, n_rows, n_tok, n_state, _p(seg_off), _p(seg_state),
+                               _p(row_token), _p(q), _p(k), _p(v), _p(alpha_p), _p(beta_p), _p(state_in),
+                               _p(state_out), _p(o), _p(ws), nbytes, _s(stream)), "gla_chunk_fwd")
+
+
 def gdn_decode_step(dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, stream=None):
     _check(lib().gdn_decode_step(ctypes.byref(dims), n_seq, _p(idx), _p(inv), _p(q), _p(k), _p(v), _p(alpha),
                                  _p(beta), _p(states), _p(o), _s(stream)), "gdn_decode_step")
@@ -160,8 +171,12 @@ class MomLayer:
     """One MoM layer on the GPU: weights resident, intermediates allocated once
     per (B, T).  forward() and decode_step() only enqueue library calls."""
 
-    def __init__(self, cfg: LayerConfig, w_r, bias, w_q, w_k, w_v, device="cuda"):
+    def __init__(self, cfg: LayerConfig, w_r, bias, w_q, w_k, w_v, device="cuda", rule="gdn"):
+        """rule: "gdn" (Gated DeltaNet memories) or "gla" (gated linear attention)."""
+        if rule not in ("gdn", "gla"):
+            raise MomError("unknown update rule %r" % rule)
         self.cfg = cfg
+        self.rule = rule
         sd = storage_dtype(cfg)
         t = lambda a, dt: None if a is None else torch.as_tensor(a).to(device=device, dtype=dt).contiguous()
         self.w_r, self.w_q, self.w_k, self.w_v = t(w_r, sd), t(w_q, sd), t(w_k, sd), t(w_v, sd)
@@ -214,15 +229,17 @@ class MomLayer:
         if state_out is None:
             state_out = torch.empty(B, c.M + 1, c.H, c.dk, c.dv, dtype=torch.float32, device=self.device)
         self.route_dispatch_project(x, alpha, beta, b, stream)
-        gdn_chunk_fwd(b["dims"], b["n_seg"], b["N"], b["NT"], B * (c.M + 1), b["seg_off"], b["seg_state"], b["perm"],
-                      b["q"], b["k"], b["v"], b["alpha_p"], b["beta_p"], state_in, state_out, b["o"], b["ws_chunk"],
-                      stream)
+        chunk = gdn_chunk_fwd if self.rule == "gdn" else gla_chunk_fwd
+        chunk(b["dims"], b["n_seg"], b["N"], b["NT"], B * (c.M + 1), b["seg_off"], b["seg_state"], b["perm"],
+              b["q"], b["k"], b["v"], b["alpha_p"], b["beta_p"], state_in, state_out, b["o"], b["ws_chunk"], stream)
         mom_combine(b["dims"], b["NT"], b["inv"], b["w"], b["o"], b["o"][b["NR"]:], b["out"], stream)
         return b["out"], state_out, b
 
     def decode_step(self, x_t, alpha, beta, states, stream=None):
         """One token for each of n_seq sequences: x_t [n_seq, D], alpha/beta
         [n_seq, H, M+1], states [n_seq, M+1, H, dk, dv] updated in place."""
+        if self.rule != "gdn":
+            raise MomError("the decode step is built for Gated DeltaNet memories only")
         n_seq = x_t.shape[0]
         b = self.buffers(n_seq, 1)
         self.route_dispatch_project(x_t, alpha, beta, b, stream)

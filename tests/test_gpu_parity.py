@@ -227,10 +227,12 @@ def test_combine(with_inv):
 SEG_LENGTHS = [0, 1, 63, 64, 65, 130, 200, 7, 128, 0, 300]
 
 
-@pytest.mark.parametrize("store,dk,dv", [("f32", 64, 64), ("f32", 128, 256), ("f16", 128, 256), ("f16", 64, 128)])
-def test_chunk_segments(store, dk, dv):
+@pytest.mark.parametrize("store,dk,dv,rule", [("f32", 64, 64, "gdn"), ("f32", 128, 256, "gdn"), ("f16", 128, 256, "gdn"),
+                                               ("f16", 64, 128, "gdn"), ("f32", 64, 64, "gla"),
+                                               ("f16", 128, 256, "gla"), ("f16", 64, 128, "gla")])
+def test_chunk_segments(store, dk, dv, rule):
     """Packed segments of ragged lengths (empty, one row, chunk +- 1, several
-    chunks) with random entering states."""
+    chunks) with random entering states, for both update rules."""
     H = 2
     lens = np.array(SEG_LENGTHS)
     seg_off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
@@ -248,15 +250,17 @@ def test_chunk_segments(store, dk, dv):
     ad = torch.float16 if store == "f16" else torch.float32
     so = torch.full((n_state, H, dk, dv), float("nan"), device="cuda")
     o = torch.full((N, H, dv), float("nan"), device="cuda")
-    log("chunk", store, dk, dv)
+    log("chunk", store, dk, dv, rule)
     dims = mom.dims_of(cfg)
-    mom.gdn_chunk_fwd(dims, n_seg, N, n_tok, n_state, to_gpu(seg_off), to_gpu(seg_state),
-                      to_gpu(row_token), to_gpu(qtok, ad), to_gpu(ch["k"], ad), to_gpu(ch["v"], ad),
-                      to_gpu(ch["alpha"]), to_gpu(ch["beta"]), to_gpu(S0), so, o,
-                      mom.chunk_workspace(dims, n_seg, N))
+    chunk = mom.gdn_chunk_fwd if rule == "gdn" else mom.gla_chunk_fwd
+    chunk(dims, n_seg, N, n_tok, n_state, to_gpu(seg_off), to_gpu(seg_state),
+          to_gpu(row_token), to_gpu(qtok, ad), to_gpu(ch["k"], ad), to_gpu(ch["v"], ad),
+          to_gpu(ch["alpha"]), to_gpu(ch["beta"]), to_gpu(S0), so, o,
+          mom.chunk_workspace(dims, n_seg, N))
     torch.cuda.synchronize()
     st = S0.astype(np.float64).copy()
-    o_ref = oracle.segments(seg_off, seg_state, row_token, qtok, ch["k"], ch["v"], ch["alpha"], ch["beta"], st)
+    o_ref = oracle.segments(seg_off, seg_state, row_token, qtok, ch["k"], ch["v"], ch["alpha"], ch["beta"], st,
+                            rule=rule)
     tol = TOL["bf16"] if store == "f16" else (2e-5, 1e-5)
     assert_close("o", o.cpu().numpy(), o_ref, *tol)
     sg = so.cpu().numpy()
@@ -324,8 +328,8 @@ def test_chunk_in_place_and_zero_state():
 
 
 # ------------------------------------------------------------------ whole layer
-def run_layer_gpu(cfg, inp, S0=None):
-    layer = make_layer(cfg, inp)
+def run_layer_gpu(cfg, inp, S0=None, rule="gdn"):
+    layer = mom.MomLayer(cfg, inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"], rule=rule)
     g = gpu_inputs(cfg, inp)
     st_in = None if S0 is None else to_gpu(S0)
     out, st, b = layer.forward(g["x"], g["alpha"], g["beta"], state_in=st_in)
@@ -359,6 +363,24 @@ def test_layer_reduced_length(name, B, T):
     np.testing.assert_array_equal(b["idx"].cpu().numpy(), ref["idx"])
     assert_close("out", out, ref["out"], *TOL[cfg.dtype])
     assert_close("state", st, ref["state"], *TOL[cfg.dtype])
+
+
+@pytest.mark.parametrize("name,B,T", [("tiny_f32", 1, 256), ("l380m", 2, 300), ("m16", 2, 200)])
+def test_gla_layer(name, B, T):
+    """The layer with gated linear attention memories behind the same route,
+    dispatch, projections and combine, against the checker's layer with that
+    rule, from a non-zero entering state."""
+    cfg = small(CFG[name], B, T)
+    log("gla layer", name, B, T)
+    inp = synth.make_layer_inputs(cfg, seed=2)
+    S0 = synth.make_state(cfg, B, seed=6)
+    out, st, b = run_layer_gpu(cfg, inp, S0, rule="gla")
+    ref = oracle.layer(dims_tuple(cfg), inp["x"], inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"],
+                       inp["alpha"], inp["beta"], state0=S0, rule="gla")
+    np.testing.assert_array_equal(b["idx"].cpu().numpy(), ref["idx"])
+    tol = TOL[cfg.dtype]
+    assert_close("out", out, ref["out"], *tol)
+    assert_close("state", st, ref["state"], *tol)
 
 
 def oracle_bh_slice(cfg, inp, idx, w, b_sel, h, t_max):
