@@ -187,6 +187,13 @@ mom_status gdn_decode_step(const mom_dims* dims, int32_t n_seq, const int32_t* i
                            const float* alpha, const float* beta, float* states, float* o,
                            void* stream);
 
+/* gla_decode_step: as gdn_decode_step (same arguments, layouts and errors) for
+ * gated linear attention memories: S <- a S + c k v^T, o = S^T q. */
+mom_status gla_decode_step(const mom_dims* dims, int32_t n_seq, const int32_t* idx,
+                           const int32_t* inv, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, float* states, float* o,
+                           void* stream);
+
 /* Combine: out[t] = o_shared[t] + sum_j w[t][j] * o_routed[row(t, j)], shared
  * first then j ascending, float32, row(t, j) = inv[t][j] (NULL: t*topk + j).
  *   o_routed [*][H][dv], o_shared [n_tok][H][dv], out [n_tok][H][dv] float32  */

@@ -13,13 +13,15 @@
 // DVB = 128), so each state is read once and written once (non-temporal: a
 // state is not touched again within the step) and many slices are in flight
 // per compute unit.
+// With DELTA false the memories use gated linear attention: u = c v (no
+// a = S^T k term), the rest unchanged.
 #include "common.h"
 
 namespace mom {
 
 typedef float dv4 __attribute__((ext_vector_type(4)));
 
-template <typename IT, int DK, int DV, int DVB>
+template <typename IT, int DK, int DV, int DVB, bool DELTA>
 __global__ __launch_bounds__(256) void k_gdn_decode(int n_seq, int H, int M, int K, const int32_t* __restrict__ idx,
                                                     const int32_t* __restrict__ inv, const IT* __restrict__ q,
                                                     const IT* __restrict__ k, const IT* __restrict__ v,
@@ -94,10 +96,17 @@ __global__ __launch_bounds__(256) void k_gdn_decode(int n_seq, int H, int M, int
   const float kq = kq_s;
   const float4 vv = reinterpret_cast<const float4*>(vs)[c4];
   float4 u;
-  u.x = cg * (vv.x - ag * sa.x);
-  u.y = cg * (vv.y - ag * sa.y);
-  u.z = cg * (vv.z - ag * sa.z);
-  u.w = cg * (vv.w - ag * sa.w);
+  if (DELTA) {
+    u.x = cg * (vv.x - ag * sa.x);
+    u.y = cg * (vv.y - ag * sa.y);
+    u.z = cg * (vv.z - ag * sa.z);
+    u.w = cg * (vv.w - ag * sa.w);
+  } else {
+    u.x = cg * vv.x;
+    u.y = cg * vv.y;
+    u.z = cg * vv.z;
+    u.w = cg * vv.w;
+  }
   if (rg == 0) {
     float4 ov;
     ov.x = fmaf(kq, u.x, ag * sb.x);
@@ -122,14 +131,18 @@ __global__ __launch_bounds__(256) void k_gdn_decode(int n_seq, int H, int M, int
 template <typename IT>
 static void launch_decode(const mom_dims& d, int n_seq, const int32_t* idx, const int32_t* inv, const void* q,
                           const void* k, const void* v, const float* alpha, const float* beta, float* states,
-                          float* o, hipStream_t st) {
+                          float* o, bool delta, hipStream_t st) {
   const int64_t slots = (int64_t)n_seq * (d.topk + 1) * d.H;
-#define MOM_DEC(DK, DV)                                                                                          \
-  do {                                                                                                           \
-    constexpr int DVB = DV < 128 ? DV : 128;                                                                     \
-    hipLaunchKernelGGL((k_gdn_decode<IT, DK, DV, DVB>), dim3((unsigned)(slots * (DV / DVB))), dim3(256), 0, st,  \
-                       n_seq, d.H, d.M, d.topk, idx, inv, (const IT*)q, (const IT*)k, (const IT*)v, alpha, beta, \
-                       states, o);                                                                               \
+#define MOM_DEC2(DK, DV, DELTA)                                                                                  \
+  hipLaunchKernelGGL((k_gdn_decode<IT, DK, DV, (DV < 128 ? DV : 128), DELTA>),                                    \
+                     dim3((unsigned)(slots * (DV / (DV < 128 ? DV : 128)))), dim3(256), 0, st, n_seq, d.H, d.M,     \
+                     d.topk, idx, inv, (const IT*)q, (const IT*)k, (const IT*)v, alpha, beta, states, o)
+#define MOM_DEC(DK, DV)           \
+  do {                            \
+    if (delta)                    \
+      MOM_DEC2(DK, DV, true);     \
+    else                          \
+      MOM_DEC2(DK, DV, false);    \
   } while (0)
   if (d.dk == 64) {
     if (d.dv == 64) MOM_DEC(64, 64);
@@ -141,14 +154,15 @@ static void launch_decode(const mom_dims& d, int n_seq, const int32_t* idx, cons
     else MOM_DEC(128, 256);
   }
 #undef MOM_DEC
+#undef MOM_DEC2
 }
 
 }  // namespace mom
 
-extern "C" mom_status gdn_decode_step(const mom_dims* dims, int32_t n_seq, const int32_t* idx, const int32_t* inv,
-                                      const void* q, const void* k, const void* v, const float* alpha,
-                                      const float* beta, float* states, float* o, void* stream) {
-  using namespace mom;
+namespace mom {
+static mom_status decode_step(bool delta, const mom_dims* dims, int32_t n_seq, const int32_t* idx,
+                              const int32_t* inv, const void* q, const void* k, const void* v, const float* alpha,
+                              const float* beta, float* states, float* o, void* stream) {
   mom_status s = check_dims(dims);
   if (s != MOM_OK) return s;
   if (dims->dv != 64 && dims->dv != 128 && dims->dv != 256) return MOM_ERR_UNSUPPORTED;
@@ -165,8 +179,21 @@ extern "C" mom_status gdn_decode_step(const mom_dims* dims, int32_t n_seq, const
   if (n_seq == 0) return MOM_OK;
   hipStream_t st = (hipStream_t)stream;
   if (dims->dtype == MOM_DTYPE_BF16)
-    launch_decode<f16_t>(*dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, st);
+    launch_decode<f16_t>(*dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, delta, st);
   else
-    launch_decode<float>(*dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, st);
+    launch_decode<float>(*dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, delta, st);
   return launch_status();
+}
+}  // namespace mom
+
+extern "C" mom_status gdn_decode_step(const mom_dims* dims, int32_t n_seq, const int32_t* idx, const int32_t* inv,
+                                      const void* q, const void* k, const void* v, const float* alpha,
+                                      const float* beta, float* states, float* o, void* stream) {
+  return mom::decode_step(true, dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, stream);
+}
+
+extern "C" mom_status gla_decode_step(const mom_dims* dims, int32_t n_seq, const int32_t* idx, const int32_t* inv,
+                                      const void* q, const void* k, const void* v, const float* alpha,
+                                      const float* beta, float* states, float* o, void* stream) {
+  return mom::decode_step(false, dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, stream);
 }

@@ -55,6 +55,7 @@ def lib():
         "gla_chunk_fwd": [D, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                           _VP, ctypes.c_size_t, _VP],
         "gdn_decode_step": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+        "gla_decode_step": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
         "mom_combine": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP],
         "mom_workspace_bytes": [D, _I32],
         "gdn_chunk_workspace_bytes": [D, _I32, _I32],
@@ -72,7 +73,7 @@ def lib():
 
 
 EXPORTS = ("mom_route", "mom_dispatch", "mom_project", "gdn_chunk_fwd", "gla_chunk_fwd", "gdn_decode_step",
-           "mom_combine", "mom_workspace_bytes", "gdn_chunk_workspace_bytes", "mom_status_string")
+           "gla_decode_step", "mom_combine", "mom_workspace_bytes", "gdn_chunk_workspace_bytes", "mom_status_string")
 
 
 def dims_of(cfg: LayerConfig, B: int | None = None, T: int | None = None) -> MomDims:
@@ -136,6 +137,12 @@ def gla_chunk_fwd(dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_t
 def gdn_decode_step(dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, stream=None):
     _check(lib().gdn_decode_step(ctypes.byref(dims), n_seq, _p(idx), _p(inv), _p(q), _p(k), _p(v), _p(alpha),
                                  _p(beta), _p(states), _p(o), _s(stream)), "gdn_decode_step")
+
+
+def gla_decode_step(dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, stream=None):
+    """As gdn_decode_step, for gated linear attention memories."""
+    _check(lib().gla_decode_step(ctypes.byref(dims), n_seq, _p(idx), _p(inv), _p(q), _p(k), _p(v), _p(alpha),
+                                 _p(beta), _p(states), _p(o), _s(stream)), "gla_decode_step")
 
 
 def mom_combine(dims, n_tok, inv, w, o_routed, o_shared, out, stream=None):
@@ -238,12 +245,10 @@ class MomLayer:
     def decode_step(self, x_t, alpha, beta, states, stream=None):
         """One token for each of n_seq sequences: x_t [n_seq, D], alpha/beta
         [n_seq, H, M+1], states [n_seq, M+1, H, dk, dv] updated in place."""
-        if self.rule != "gdn":
-            raise MomError("the decode step is built for Gated DeltaNet memories only")
         n_seq = x_t.shape[0]
         b = self.buffers(n_seq, 1)
         self.route_dispatch_project(x_t, alpha, beta, b, stream)
-        gdn_decode_step(b["dims"], n_seq, b["idx"], b["inv"], b["q"], b["k"], b["v"], alpha, beta, states, b["o"],
-                        stream)
+        step = gdn_decode_step if self.rule == "gdn" else gla_decode_step
+        step(b["dims"], n_seq, b["idx"], b["inv"], b["q"], b["k"], b["v"], alpha, beta, states, b["o"], stream)
         mom_combine(b["dims"], n_seq, b["inv"], b["w"], b["o"], b["o"][b["NR"]:], b["out"], stream)
         return b["out"], b

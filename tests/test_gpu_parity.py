@@ -229,16 +229,21 @@ SEG_LENGTHS = [0, 1, 63, 64, 65, 130, 200, 7, 128, 0, 300]
 
 @pytest.mark.parametrize("store,dk,dv,rule", [("f32", 64, 64, "gdn"), ("f32", 128, 256, "gdn"), ("f16", 128, 256, "gdn"),
                                                ("f16", 64, 128, "gdn"), ("f32", 64, 64, "gla"),
-                                               ("f16", 128, 256, "gla"), ("f16", 64, 128, "gla")])
+                                               ("f16", 128, 256, "gla"), ("f16", 64, 128, "gla"),
+                                               ("f32", 64, 64, "deltanet"), ("f16", 128, 256, "deltanet")])
 def test_chunk_segments(store, dk, dv, rule):
     """Packed segments of ragged lengths (empty, one row, chunk +- 1, several
-    chunks) with random entering states, for both update rules."""
+    chunks) with random entering states, for the update rules: Gated DeltaNet,
+    gated linear attention, and DeltaNet (Gated DeltaNet with the forget gate
+    fixed at 1)."""
     H = 2
     lens = np.array(SEG_LENGTHS)
     seg_off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     N = int(seg_off[-1])
     n_seg = len(lens)
     ch = synth.make_chain_inputs(N, H, dk, dv, seed=dk + dv, store=store)
+    if rule == "deltanet":
+        ch["alpha"] = np.ones_like(ch["alpha"])
     n_tok = N + 5
     row_token = np.random.default_rng(1).permutation(n_tok)[:N].astype(np.int32)
     qtok = np.zeros((n_tok, H, dk), np.float32)
@@ -252,7 +257,7 @@ def test_chunk_segments(store, dk, dv, rule):
     o = torch.full((N, H, dv), float("nan"), device="cuda")
     log("chunk", store, dk, dv, rule)
     dims = mom.dims_of(cfg)
-    chunk = mom.gdn_chunk_fwd if rule == "gdn" else mom.gla_chunk_fwd
+    chunk = mom.gla_chunk_fwd if rule == "gla" else mom.gdn_chunk_fwd
     chunk(dims, n_seg, N, n_tok, n_state, to_gpu(seg_off), to_gpu(seg_state),
           to_gpu(row_token), to_gpu(qtok, ad), to_gpu(ch["k"], ad), to_gpu(ch["v"], ad),
           to_gpu(ch["alpha"]), to_gpu(ch["beta"]), to_gpu(S0), so, o,
@@ -260,7 +265,7 @@ def test_chunk_segments(store, dk, dv, rule):
     torch.cuda.synchronize()
     st = S0.astype(np.float64).copy()
     o_ref = oracle.segments(seg_off, seg_state, row_token, qtok, ch["k"], ch["v"], ch["alpha"], ch["beta"], st,
-                            rule=rule)
+                            rule="gla" if rule == "gla" else "gdn")
     tol = TOL["bf16"] if store == "f16" else (2e-5, 1e-5)
     assert_close("o", o.cpu().numpy(), o_ref, *tol)
     sg = so.cpu().numpy()
@@ -466,13 +471,15 @@ def test_split_resume_and_determinism():
     assert_close("resumed state", s2, st_full, *TOL["bf16"])
 
 
-@pytest.mark.parametrize("name,n_seq,steps", [("tiny_f32", 5, 2), ("long32k", 256, 1), ("m16", 33, 2)])
-def test_decode_step(name, n_seq, steps):
+@pytest.mark.parametrize("name,n_seq,steps,rule", [("tiny_f32", 5, 2, "gdn"), ("long32k", 256, 1, "gdn"),
+                                                   ("m16", 33, 2, "gdn"), ("tiny_f32", 5, 2, "gla"),
+                                                   ("l380m", 40, 2, "gla")])
+def test_decode_step(name, n_seq, steps, rule):
     """decode_step = the layer with T = 1 from the given states; two steps in a row."""
     cfg = CFG[name]
-    log("decode", name, n_seq)
+    log("decode", name, n_seq, rule)
     inp = synth.make_layer_inputs(dataclasses.replace(cfg, B=1, T=1), seed=0)
-    layer = make_layer(cfg, inp)
+    layer = mom.MomLayer(cfg, inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"], rule=rule)
     S = synth.make_state(cfg, n_seq, seed=8)
     states = to_gpu(S)
     S_ref = S.astype(np.float64)
@@ -482,7 +489,7 @@ def test_decode_step(name, n_seq, steps):
                                    states)
         torch.cuda.synchronize()
         ref = oracle.layer(dims_tuple(cfg, n_seq, 1), d["x"], inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"],
-                           inp["w_v"], d["alpha"], d["beta"], state0=S_ref)
+                           inp["w_v"], d["alpha"], d["beta"], state0=S_ref, rule=rule)
         np.testing.assert_array_equal(b["idx"].cpu().numpy(), ref["idx"])
         assert_close("decode out step %d" % step, out.cpu().numpy(), ref["out"], *TOL[cfg.dtype])
         assert_close("decode states step %d" % step, states.cpu().numpy(), ref["state"], *TOL[cfg.dtype])
