@@ -132,20 +132,18 @@ struct ProjCfg {
   __device__ static int swz(int r, int c) { return BK == 32 ? c ^ ((r >> 2) & 3) : c ^ ((r >> 1) & 7); }
 };
 
+// One tile (rows job.trow .. + CF::BM of the job's group, columns job.col0 ..
+// + CF::BN) with the CF wave layout; smem_l is the block's dynamic LDS.
 template <class CF>
-__global__ __launch_bounds__(CF::THREADS) void k_project_bf16(
-    int64_t NT, int D, int H, int dk, int dv, int M, int B, const bf16_t* __restrict__ x,
-    const int32_t* __restrict__ perm, const int32_t* __restrict__ seg_off, const bf16_t* __restrict__ wq,
-    const bf16_t* __restrict__ wk, const bf16_t* __restrict__ wv, f16_t* __restrict__ q, f16_t* __restrict__ k,
-    f16_t* __restrict__ v) {
+__device__ __forceinline__ void project_tile(const TileJob& job, bf16_t* smem_l, int D, int H, int dk, int dv,
+                                             const bf16_t* __restrict__ x, const int32_t* __restrict__ perm,
+                                             const bf16_t* __restrict__ wq, const bf16_t* __restrict__ wk,
+                                             const bf16_t* __restrict__ wv, f16_t* __restrict__ q,
+                                             f16_t* __restrict__ k, f16_t* __restrict__ v) {
   constexpr int BM = CF::BM, BN = CF::BN, IT = CF::IT, JF = CF::JF, NWN = CF::NWN, LPW = CF::LPW;
   constexpr int BK = CF::BK, NS = CF::NS, CPR = CF::CPR, RPI = CF::RPI;
   constexpr int RPW = RPI * LPW;  // stage rows copied by one wave
-  extern __shared__ __attribute__((aligned(16))) bf16_t smem_l[];
   const int HK = H * dk, HV = H * dv;
-  const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
-  const TileJob job = decode_tile<BM, BN>(L, NT, M, B, HK, HV, seg_off);
-  if (job.kind < 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / NWN, wn = w % NWN;
 
@@ -360,21 +358,69 @@ __global__ __launch_bounds__(CF::THREADS) void k_project_bf16(
   }
 }
 
-template <class CF>
+// Tiles of CF (the first n_main tiles of the tile map) then, when the last
+// round of tiles would leave most compute units idle, the remaining tiles cut
+// into CF::BM / CFT::BM sub-tiles of CFT::BM rows each (same columns), so the
+// last round is a fraction of a tile long.  Block p < n_main takes tile
+// xcd_remap(p); block n_main + s takes sub-tile s % SPLIT of tile
+// n_main + s / SPLIT.
+template <class CF, class CFT>
+__global__ __launch_bounds__(CF::THREADS) void k_project_bf16(
+    int64_t n_main, int64_t NT, int D, int H, int dk, int dv, int M, int B, const bf16_t* __restrict__ x,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ seg_off, const bf16_t* __restrict__ wq,
+    const bf16_t* __restrict__ wk, const bf16_t* __restrict__ wv, f16_t* __restrict__ q, f16_t* __restrict__ k,
+    f16_t* __restrict__ v) {
+  static_assert(CF::THREADS == CFT::THREADS && CF::BN == CFT::BN && CF::BM % CFT::BM == 0, "sub-tiles of CF");
+  constexpr int SPLIT = CF::BM / CFT::BM;
+  extern __shared__ __attribute__((aligned(16))) bf16_t smem_l[];
+  const int HK = H * dk, HV = H * dv;
+  const int64_t p = blockIdx.x;
+  if (p < n_main) {
+    const TileJob job = decode_tile<CF::BM, CF::BN>(xcd_remap(p, n_main), NT, M, B, HK, HV, seg_off);
+    if (job.kind < 0) return;
+    project_tile<CF>(job, smem_l, D, H, dk, dv, x, perm, wq, wk, wv, q, k, v);
+  } else {
+    const int64_t t = p - n_main;
+    TileJob job = decode_tile<CF::BM, CF::BN>(n_main + t / SPLIT, NT, M, B, HK, HV, seg_off);
+    if (job.kind < 0) return;
+    job.trow += (t % SPLIT) * CFT::BM;
+    if (job.trow >= job.rows) return;  // a sub-tile past the end of the group
+    project_tile<CFT>(job, smem_l, D, H, dk, dv, x, perm, wq, wk, wv, q, k, v);
+  }
+}
+
+template <class CF, class CFT>
 static mom_status launch_project_bf16(const mom_dims& d, const Sizes& z, const void* x, const int32_t* perm,
                                       const int32_t* seg_off, const void* w_q, const void* w_k, const void* w_v,
                                       void* q, void* k, void* v, hipStream_t st) {
-  static bool attr_set = false;  // idempotent; benign if two threads race
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_project_bf16<CF>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  // blocks that fit on the device at once, found once per device
+  static int slots_dev = -1, slots = 0;  // benign if two threads race
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOM_ERR_LAUNCH;
+  if (dev != slots_dev) {
+    if (hipFuncSetAttribute((const void*)k_project_bf16<CF, CFT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)CF::LDS) != hipSuccess)
       return MOM_ERR_LAUNCH;
-    attr_set = true;
+    int n_cu = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_project_bf16<CF, CFT>, CF::THREADS,
+                                                     CF::LDS) != hipSuccess)
+      return MOM_ERR_LAUNCH;
+    slots = n_cu * (per_cu > 0 ? per_cu : 1);
+    slots_dev = dev;
   }
-  const int64_t G = n_tiles_bound(d, CF::BM, CF::BN);
-  hipLaunchKernelGGL((k_project_bf16<CF>), dim3((unsigned)G), dim3(CF::THREADS), CF::LDS, st, z.NT, d.D, d.H, d.dk,
-                     d.dv, d.M, d.B, (const bf16_t*)x, perm, seg_off, (const bf16_t*)w_q, (const bf16_t*)w_k,
-                     (const bf16_t*)w_v, (f16_t*)q, (f16_t*)k, (f16_t*)v);
+  // The tile map's tile count is a bound (the exact count depends on seg_off,
+  // which stays on the device); a last round of at most half the slots is cut
+  // into sub-tiles.
+  constexpr int SPLIT = CF::BM / CFT::BM;
+  const int64_t n_tiles = n_tiles_bound(d, CF::BM, CF::BN);
+  const int64_t rem = slots > 0 ? n_tiles % slots : 0;
+  const int64_t n_main = (rem > 0 && 2 * rem <= slots) ? n_tiles - rem : n_tiles;
+  const int64_t G = n_main + (n_tiles - n_main) * SPLIT;
+  static_assert(CF::LDS >= CFT::LDS, "one LDS size serves both tile shapes");
+  hipLaunchKernelGGL((k_project_bf16<CF, CFT>), dim3((unsigned)G), dim3(CF::THREADS), CF::LDS, st, n_main, z.NT,
+                     d.D, d.H, d.dk, d.dv, d.M, d.B, (const bf16_t*)x, perm, seg_off, (const bf16_t*)w_q,
+                     (const bf16_t*)w_k, (const bf16_t*)w_v, (f16_t*)q, (f16_t*)k, (f16_t*)v);
   return MOM_OK;
 }
 
@@ -489,9 +535,11 @@ extern "C" mom_status mom_project(const mom_dims* dims, const void* x, const int
     if ((d.H * d.dk) % 128 || (d.H * d.dv) % 128) return MOM_ERR_UNSUPPORTED;
     mom_status r;
     if ((d.H * d.dk) % 256 == 0 && (d.H * d.dv) % 256 == 0 && z.NT >= 4096)
-      r = launch_project_bf16<ProjCfg<4, 2, 4, 64, 2>>(d, z, x, perm, seg_off, w_q, w_k, w_v, q, k, v, st);
+      r = launch_project_bf16<ProjCfg<4, 2, 4, 64, 2>, ProjCfg<4, 2, 1, 64, 2>>(d, z, x, perm, seg_off, w_q, w_k,
+                                                                               w_v, q, k, v, st);
     else
-      r = launch_project_bf16<ProjCfg<2, 2, 1, 64, 2>>(d, z, x, perm, seg_off, w_q, w_k, w_v, q, k, v, st);
+      r = launch_project_bf16<ProjCfg<2, 2, 1, 64, 2>, ProjCfg<2, 2, 1, 64, 2>>(d, z, x, perm, seg_off, w_q, w_k,
+                                                                               w_v, q, k, v, st);
     if (r != MOM_OK) return r;
   } else {
     const int64_t G = n_tiles_bound(d, PF_M, PF_N);
