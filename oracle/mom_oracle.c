@@ -423,3 +423,169 @@ void oracle_project_head(int64_t n, const int32_t* rows_tok, int D, int dk, int 
     if (wv_h) proj_rows(D, dv, wv_h, xt, v + i * dv);
   }
 }
+
+/* ------------------------------------------------------------------------- */
+/* Gradients of the recurrence: reverse-mode differentiation of the steps
+ * above, what training needs ([p1] introduction: linear-complexity training;
+ * [p2] "Summary": the layer is trained end to end).  The pages give no
+ * backward formulas; these are the chain rule applied to each step as written.
+ *
+ * Gated DeltaNet step, forward from S_prev:
+ *   S~ = a S_prev,  p = S~^T k,  e = c (v - p),  S = S~ + k e^T,  o = S^T q.
+ * Reverse, given g = dL/dS (from later steps) and d_o = dL/do:
+ *   g   += q d_o^T                  dq  = S d_o
+ *   de   = g^T k                    dk  = g e
+ *   dc   = de . (v - p)             dv  = c de          dp = -c de
+ *   g~   = g + k dp^T               dk += S~ dp
+ *   da   = <g~, S_prev>             dL/dS_prev = a g~
+ * On entry dS holds g, on exit dL/dS_prev.  S_prev and S are the states
+ * before and after the step.  dq, dk, dv are written, not accumulated.      */
+void oracle_gdn_step_bwd(int dk, int dv, double a, double c, const double* q, const double* k,
+                         const double* v, const double* S_prev, const double* S, const double* d_o,
+                         double* dS, double* dq, double* dk_out, double* dv_out, double* da,
+                         double* dc) {
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) dS[i * dv + j] += q[i] * d_o[j];
+  for (int i = 0; i < dk; ++i) {
+    double s = 0.0;
+    for (int j = 0; j < dv; ++j) s += S[i * dv + j] * d_o[j];
+    dq[i] = s;
+  }
+  double dcs = 0.0;
+  for (int i = 0; i < dk; ++i) dk_out[i] = 0.0;
+  for (int j = 0; j < dv; ++j) {
+    double p = 0.0, de = 0.0;
+    for (int i = 0; i < dk; ++i) {
+      p += a * S_prev[i * dv + j] * k[i];
+      de += dS[i * dv + j] * k[i];
+    }
+    const double r = v[j] - p;
+    const double e = c * r;
+    for (int i = 0; i < dk; ++i) dk_out[i] += dS[i * dv + j] * e;
+    dcs += de * r;
+    dv_out[j] = c * de;
+    const double dp = -c * de;
+    for (int i = 0; i < dk; ++i) {
+      dk_out[i] += a * S_prev[i * dv + j] * dp;
+      dS[i * dv + j] += k[i] * dp;
+    }
+  }
+  double das = 0.0;
+  for (int i = 0; i < dk * dv; ++i) {
+    das += dS[i] * S_prev[i];
+    dS[i] *= a;
+  }
+  *da = das;
+  *dc = dcs;
+}
+
+/* Gated linear attention step, forward S = a S_prev + c k v^T, o = S^T q.
+ * Reverse: g += q d_o^T; dq = S d_o; dk = c g v; dv = c g^T k;
+ * dc = k^T g v; da = <g, S_prev>; dL/dS_prev = a g.                          */
+void oracle_gla_step_bwd(int dk, int dv, double a, double c, const double* q, const double* k,
+                         const double* v, const double* S_prev, const double* S, const double* d_o,
+                         double* dS, double* dq, double* dk_out, double* dv_out, double* da,
+                         double* dc) {
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) dS[i * dv + j] += q[i] * d_o[j];
+  for (int i = 0; i < dk; ++i) {
+    double s = 0.0, t = 0.0;
+    for (int j = 0; j < dv; ++j) {
+      s += S[i * dv + j] * d_o[j];
+      t += dS[i * dv + j] * v[j];
+    }
+    dq[i] = s;
+    dk_out[i] = c * t;
+  }
+  double dcs = 0.0;
+  for (int j = 0; j < dv; ++j) {
+    double s = 0.0;
+    for (int i = 0; i < dk; ++i) s += dS[i * dv + j] * k[i];
+    dv_out[j] = c * s;
+    dcs += s * v[j];
+  }
+  double das = 0.0;
+  for (int i = 0; i < dk * dv; ++i) {
+    das += dS[i] * S_prev[i];
+    dS[i] *= a;
+  }
+  *da = das;
+  *dc = dcs;
+}
+
+typedef void (*oracle_step_bwd_fn)(int, int, double, double, const double*, const double*, const double*,
+                                   const double*, const double*, const double*, double*, double*, double*,
+                                   double*, double*, double*);
+
+/* Steps between stored states in the reverse sweep.  The states inside a span
+ * are recomputed from the span's first state by the same forward steps, so
+ * they are bit-identical to a sweep that stores every state.                */
+#define ORACLE_BWD_SPAN 64
+
+/* Gradients of the recurrences over packed segments (the layout of
+ * oracle_segments_rule).  Inputs: the forward's inputs, state0
+ * [n_state][H][dk][dv] (the entering states; NULL = zeros), d_o [N][H][dv]
+ * (dL/do) and dstate [n_state][H][dk][dv] (dL/d(final state); NULL = zeros).
+ * Outputs: dq [N][H][dk] per row (the gradient of the query as used at that
+ * row; rows that share a token are not summed), dk [N][H][dk], dv [N][H][dv],
+ * da, dc [N][H], dstate0 [n_state][H][dk][dv] = dL/d(entering state).  A state
+ * slot may be used by at most one segment; slots that no segment uses pass
+ * dstate through.  Parallel over (segment, head).                            */
+void oracle_segments_bwd_rule(int rule, int n_seg, const int32_t* seg_off, const int32_t* seg_state,
+                              int n_state, const int32_t* row_token, int H, int dk, int dv,
+                              const double* q, const double* k, const double* v, const double* a,
+                              const double* c, const double* state0, const double* d_o,
+                              const double* dstate, double* dq, double* dk_out, double* dv_out,
+                              double* da, double* dc, double* dstate0) {
+  const oracle_step_fn step = step_of(rule);
+  const oracle_step_bwd_fn step_bwd = rule == 1 ? oracle_gla_step_bwd : oracle_gdn_step_bwd;
+  const int64_t ssz = (int64_t)dk * dv;
+  const int64_t n_all = (int64_t)n_state * H * ssz;
+  for (int64_t i = 0; i < n_all; ++i) dstate0[i] = dstate ? dstate[i] : 0.0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int job = 0; job < n_seg * H; ++job) {
+    const int s = job / H, h = job % H;
+    const int64_t r0 = seg_off[s], L = seg_off[s + 1] - seg_off[s];
+    const int64_t slot = ((int64_t)seg_state[s] * H + h) * ssz;
+    const int64_t n_span = (L + ORACLE_BWD_SPAN - 1) / ORACLE_BWD_SPAN;
+    double* ck = (double*)malloc(sizeof(double) * (size_t)((n_span + 1) * ssz));
+    double* st = (double*)malloc(sizeof(double) * (size_t)((ORACLE_BWD_SPAN + 1) * ssz));
+    double* o = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* g = dstate0 + slot;
+    /* forward sweep: the state at the start of every span */
+    for (int64_t i = 0; i < ssz; ++i) ck[i] = state0 ? state0[slot + i] : 0.0;
+    for (int64_t sp = 0; sp < n_span; ++sp) {
+      double* S = ck + (sp + 1) * ssz;
+      memcpy(S, ck + sp * ssz, sizeof(double) * (size_t)ssz);
+      const int64_t e = (sp + 1) * ORACLE_BWD_SPAN < L ? (sp + 1) * ORACLE_BWD_SPAN : L;
+      for (int64_t i = sp * ORACLE_BWD_SPAN; i < e; ++i) {
+        const int64_t r = r0 + i, tk = row_token ? row_token[r] : r;
+        step(dk, dv, a[r * H + h], c[r * H + h], q + (tk * H + h) * dk, k + (r * H + h) * dk,
+             v + (r * H + h) * dv, S, o);
+      }
+    }
+    /* reverse sweep, span by span from the last */
+    for (int64_t sp = n_span - 1; sp >= 0; --sp) {
+      const int64_t b = sp * ORACLE_BWD_SPAN;
+      const int64_t e = b + ORACLE_BWD_SPAN < L ? b + ORACLE_BWD_SPAN : L;
+      memcpy(st, ck + sp * ssz, sizeof(double) * (size_t)ssz);
+      for (int64_t i = b; i < e; ++i) {
+        const int64_t r = r0 + i, tk = row_token ? row_token[r] : r;
+        double* S = st + (i - b + 1) * ssz;
+        memcpy(S, S - ssz, sizeof(double) * (size_t)ssz);
+        step(dk, dv, a[r * H + h], c[r * H + h], q + (tk * H + h) * dk, k + (r * H + h) * dk,
+             v + (r * H + h) * dv, S, o);
+      }
+      for (int64_t i = e - 1; i >= b; --i) {
+        const int64_t r = r0 + i, tk = row_token ? row_token[r] : r;
+        step_bwd(dk, dv, a[r * H + h], c[r * H + h], q + (tk * H + h) * dk, k + (r * H + h) * dk,
+                 v + (r * H + h) * dv, st + (i - b) * ssz, st + (i - b + 1) * ssz, d_o + (r * H + h) * dv, g,
+                 dq + (r * H + h) * dk, dk_out + (r * H + h) * dk, dv_out + (r * H + h) * dv, da + r * H + h,
+                 dc + r * H + h);
+      }
+    }
+    free(ck);
+    free(st);
+    free(o);
+  }
+}

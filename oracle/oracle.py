@@ -190,3 +190,28 @@ def project_head(rows_tok, x, wq_h, wk_h, wv_h):
     lib().oracle_project_head(ctypes.c_int64(n), _p(rows_tok), D, dk, dv, _p(x), _p(wq_h), _p(wk_h),
                               _p(wv_h), _p(q), _p(k), _p(v))
     return q, k, v
+
+
+def segments_bwd(seg_off, seg_state, row_token, q, k, v, a, c, state0, d_o, dstate=None, n_state=None,
+                 rule="gdn"):
+    """Gradients of ``segments``: given dL/do (d_o [N][H][dv]) and dL/d(final
+    state) (dstate [n_state][H][dk][dv], None = zeros), return a dict with
+    dq [N][H][dk] (per row, as the query is used at that row), dk, dv, da, dc and
+    dstate0 (dL/d(entering state)).  state0 None = zeros.  Each state slot may be
+    used by at most one segment."""
+    seg_off, seg_state, row_token = _i(seg_off), _i(seg_state), _i(row_token)
+    q, k, v, a, c, state0, d_o, dstate = (_d(t) for t in (q, k, v, a, c, state0, d_o, dstate))
+    N, H, dk = k.shape
+    dv = v.shape[2]
+    n_seg = seg_off.shape[0] - 1
+    if n_state is None:
+        n_state = (state0.shape[0] if state0 is not None else
+                   dstate.shape[0] if dstate is not None else int(seg_state.max()) + 1)
+    assert len(set(seg_state.tolist())) == n_seg, "a state slot may serve one segment only"
+    res = dict(dq=np.zeros((N, H, dk)), dk=np.zeros((N, H, dk)), dv=np.zeros((N, H, dv)),
+               da=np.zeros((N, H)), dc=np.zeros((N, H)), dstate0=np.empty((n_state, H, dk, dv)))
+    lib().oracle_segments_bwd_rule(RULES[rule], n_seg, _p(seg_off), _p(seg_state), n_state, _p(row_token), H, dk,
+                                   dv, _p(q), _p(k), _p(v), _p(a), _p(c), _p(state0), _p(d_o), _p(dstate),
+                                   _p(res["dq"]), _p(res["dk"]), _p(res["dv"]), _p(res["da"]), _p(res["dc"]),
+                                   _p(res["dstate0"]))
+    return res

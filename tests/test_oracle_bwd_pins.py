@@ -1,0 +1,203 @@
+"""Pins of the fp64 checker's gradients (``oracle.segments_bwd``) against what
+fixes them independently of their own code: central finite differences of the
+forward recurrence (itself pinned in test_oracle_pins.py), and the closed form
+of the no-write case.  CPU only."""
+import numpy as np
+import pytest
+
+from oracle import oracle
+
+
+def _problem(lens, H=2, dk=4, dv=3, n_tok=None, seed=0, c_zero=False):
+    rng = np.random.default_rng(seed)
+    n_seg = len(lens)
+    seg_off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N = int(seg_off[-1])
+    n_tok = n_tok or max(N, 1)
+    n_state = n_seg + 1                                   # one slot is never used
+    seg_state = rng.permutation(n_state)[:n_seg].astype(np.int32)
+    row_token = rng.integers(0, n_tok, N).astype(np.int32)
+    k = rng.standard_normal((N, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    p = dict(seg_off=seg_off, seg_state=seg_state, row_token=row_token,
+             q=rng.standard_normal((n_tok, H, dk)), k=k, v=rng.standard_normal((N, H, dv)),
+             a=rng.uniform(0.8, 1.0, (N, H)), c=np.zeros((N, H)) if c_zero else rng.uniform(0.0, 1.0, (N, H)),
+             state0=0.5 * rng.standard_normal((n_state, H, dk, dv)))
+    d_o = rng.standard_normal((N, H, dv))
+    dstate = rng.standard_normal((n_state, H, dk, dv))
+    return p, d_o, dstate
+
+
+def _loss(p, d_o, dstate, rule):
+    S = p["state0"].copy()
+    o = oracle.segments(p["seg_off"], p["seg_state"], p["row_token"], p["q"], p["k"], p["v"], p["a"], p["c"], S,
+                        rule=rule)
+    return float(np.sum(d_o * o) + np.sum(dstate * S))
+
+
+def _grads(p, d_o, dstate, rule):
+    g = oracle.segments_bwd(p["seg_off"], p["seg_state"], p["row_token"], p["q"], p["k"], p["v"], p["a"], p["c"],
+                            p["state0"], d_o, dstate, rule=rule)
+    # the query of a token is used by every row that reads it
+    dq_tok = np.zeros_like(p["q"])
+    np.add.at(dq_tok, p["row_token"], g["dq"])
+    return dict(q=dq_tok, k=g["dk"], v=g["dv"], a=g["da"], c=g["dc"], state0=g["dstate0"])
+
+
+def _fd_check(p, d_o, dstate, rule, names, max_per_tensor=None, seed=1, eps=1e-6):
+    g = _grads(p, d_o, dstate, rule)
+    rng = np.random.default_rng(seed)
+    for name in names:
+        x = p[name]
+        flat = np.arange(x.size)
+        if max_per_tensor is not None and x.size > max_per_tensor:
+            flat = rng.choice(x.size, max_per_tensor, replace=False)
+        for i in flat:
+            ix = np.unravel_index(i, x.shape)
+            x0 = x[ix]
+            x[ix] = x0 + eps
+            lp = _loss(p, d_o, dstate, rule)
+            x[ix] = x0 - eps
+            lm = _loss(p, d_o, dstate, rule)
+            x[ix] = x0
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - g[name][ix]) <= 1e-6 * (1.0 + abs(fd)), (name, ix, fd, g[name][ix])
+
+
+@pytest.mark.parametrize("rule", ["gdn", "gla"])
+def test_gradients_match_finite_differences(rule):
+    # three segments (one empty), rows reading shared tokens, an unused slot
+    p, d_o, dstate = _problem([5, 0, 7], n_tok=6)
+    _fd_check(p, d_o, dstate, rule, ["q", "k", "v", "a", "c", "state0"])
+
+
+@pytest.mark.parametrize("rule", ["gdn", "gla"])
+def test_gradients_across_stored_state_spans(rule):
+    # longer than the reverse sweep's span of stored states (64 steps)
+    p, d_o, dstate = _problem([150, 3], H=1, dk=3, dv=2, n_tok=40, seed=3)
+    _fd_check(p, d_o, dstate, rule, ["q", "k", "v", "a", "c", "state0"], max_per_tensor=60)
+
+
+def test_no_write_closed_form():
+    """With c = 0 nothing is written: S_i = g_i S0 with g_i = a_1...a_i, and
+    o_i = g_i S0^T q_i.  Then
+      dS0   = sum_i g_i q_i do_i^T + g_L dS_L
+      dq_i  = g_i S0 do_i,   dv_i = 0
+      da_j  = (sum_{i>=j} g_i q_i^T S0 do_i + g_L <S0, dS_L>) / a_j
+      dc_j  = (G_j^T k_j) . (v_j - g_j S0^T k_j),
+              G_j = sum_{i>=j} (g_i/g_j) q_i do_i^T + (g_L/g_j) dS_L
+      dk_j  = -c_j ... = 0 (every dk term carries c or e = 0)."""
+    p, d_o, dstate = _problem([9], H=1, dk=3, dv=4, seed=5, c_zero=True)
+    g = oracle.segments_bwd(p["seg_off"], p["seg_state"], p["row_token"], p["q"], p["k"], p["v"], p["a"], p["c"],
+                            p["state0"], d_o, dstate)
+    slot = p["seg_state"][0]
+    S0, dSL = p["state0"][slot, 0], dstate[slot, 0]
+    a, k, v = p["a"][:, 0], p["k"][:, 0], p["v"][:, 0]
+    qr = p["q"][p["row_token"], 0]
+    do = d_o[:, 0]
+    L = len(a)
+    gam = np.cumprod(a)
+    dS0 = sum(gam[i] * np.outer(qr[i], do[i]) for i in range(L)) + gam[-1] * dSL
+    np.testing.assert_allclose(g["dstate0"][slot, 0], dS0, rtol=1e-12, atol=1e-12)
+    for i in range(L):
+        np.testing.assert_allclose(g["dq"][i, 0], gam[i] * S0 @ do[i], rtol=1e-12, atol=1e-12)
+        tail = sum(gam[j] * qr[j] @ S0 @ do[j] for j in range(i, L)) + gam[-1] * np.sum(S0 * dSL)
+        np.testing.assert_allclose(g["da"][i, 0], tail / a[i], rtol=1e-12, atol=1e-12)
+        G = sum((gam[j] / gam[i]) * np.outer(qr[j], do[j]) for j in range(i, L)) + (gam[-1] / gam[i]) * dSL
+        dc = (G.T @ k[i]) @ (v[i] - gam[i] * S0.T @ k[i])
+        np.testing.assert_allclose(g["dc"][i, 0], dc, rtol=1e-12, atol=1e-12)
+    assert np.all(g["dv"] == 0) and np.all(g["dk"] == 0)
+    # the slot no segment uses passes dL/d(final state) through
+    unused = sorted(set(range(p["state0"].shape[0])) - set(p["seg_state"].tolist()))
+    np.testing.assert_array_equal(g["dstate0"][unused], dstate[unused])
+
+
+def _chunk_bwd(q, k, v, a, c, S0, d_o, dSL, C, rule):
+    """Gradients of one segment by the chunk form (UT transform, the algebra the
+    GPU path uses), written independently of the checker.  Per chunk, from the
+    entering state S, with g = cumsum(log a), gm = exp(g), gL = gm[-1],
+    A = strict lower of c_i exp(g_i - g_j) k_i.k_j (zero for gated linear
+    attention), X = (I + A)^-1, T = X diag(c), R = V - diag(gm) K S (R = V for gated
+    linear attention), U = T R, P = lower of exp(g_i - g_j) q_i.k_j:
+      O = diag(gm) Q S + P U,   S' = gL S + K^T diag(exp(gL - g)) U."""
+    delta = rule == "gdn"
+    L, dk = k.shape
+    starts = list(range(0, L, C))
+    Ss, S = [], S0.copy()
+    for s in starts:                                   # forward: entering states
+        Ss.append(S.copy())
+        sl = slice(s, min(s + C, L))
+        K, V, Q, al, be = k[sl], v[sl], q[sl], a[sl], c[sl]
+        g = np.cumsum(np.log(al))
+        gm, ek = np.exp(g), np.exp(g[-1] - g)
+        n = len(al)
+        A = np.tril(be[:, None] * np.exp(g[:, None] - g[None, :]) * (K @ K.T), -1) if delta else np.zeros((n, n))
+        T = np.linalg.inv(np.eye(n) + A) * be[None, :]
+        U = T @ ((V - gm[:, None] * (K @ S)) if delta else V)
+        S = gm[-1] * S + K.T @ (ek[:, None] * U)
+    out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v), da=np.zeros_like(a),
+               dc=np.zeros_like(c))
+    dS = dSL.copy()
+    for s, S in reversed(list(zip(starts, Ss))):
+        sl = slice(s, min(s + C, L))
+        K, V, Q, al, be, dO = k[sl], v[sl], q[sl], a[sl], c[sl], d_o[sl]
+        n = len(al)
+        g = np.cumsum(np.log(al))
+        gm, ek, gL = np.exp(g), np.exp(g[-1] - g), np.exp(g[-1])
+        Eg = np.exp(np.minimum(g[:, None] - g[None, :], 0.0))        # exp(g_i - g_j), used where j <= i
+        A = np.tril(be[:, None] * Eg * (K @ K.T), -1) if delta else np.zeros((n, n))
+        X = np.linalg.inv(np.eye(n) + A)
+        T = X * be[None, :]
+        R = (V - gm[:, None] * (K @ S)) if delta else V
+        U = T @ R
+        P = np.tril(Eg * (Q @ K.T))
+        dU = P.T @ dO + ek[:, None] * (K @ dS)
+        dR = T.T @ dU
+        dSp = dS
+        dS = gL * dSp + Q.T @ (gm[:, None] * dO) - (K.T @ (gm[:, None] * dR) if delta else 0.0)
+        PQ, PK = dO @ S.T, U @ dSp.T
+        dT = np.tril(dU @ R.T)
+        dP = np.tril(dO @ U.T)
+        dg = np.zeros(n)
+        dQ = gm[:, None] * PQ
+        dg += gm * np.sum(PQ * Q, 1)
+        dK = ek[:, None] * PK
+        e = ek * np.sum(PK * K, 1)
+        dg[-1] += e.sum()
+        dg -= e
+        dg[-1] += gL * np.sum(S * dSp)
+        dbe = np.sum(dT * X, 0)
+        if delta:
+            PR = dR @ S.T
+            dK -= gm[:, None] * PR
+            dg -= gm * np.sum(PR * K, 1)
+            dA = np.tril(-X.T @ (dT * be[None, :]) @ X.T, -1)
+            Bm = dA * be[:, None] * Eg
+            dbe += np.sum(dA * Eg * (K @ K.T), 1)
+            dK += Bm @ K + Bm.T @ K
+            Cm = Bm * (K @ K.T)
+            dg += Cm.sum(1) - Cm.sum(0)
+        Dm = dP * Eg
+        dQ += Dm @ K
+        dK += Dm.T @ Q
+        Em = Dm * (Q @ K.T)
+        dg += Em.sum(1) - Em.sum(0)
+        out["dq"][sl], out["dk"][sl], out["dv"][sl], out["dc"][sl] = dQ, dK, dR, dbe
+        out["da"][sl] = np.cumsum(dg[::-1])[::-1] / al
+    out["dS0"] = dS
+    return out
+
+
+@pytest.mark.parametrize("rule", ["gdn", "gla"])
+@pytest.mark.parametrize("C", [1, 3, 16, 64])
+def test_chunk_form_gradients_equal_token_gradients(rule, C):
+    p, d_o, dstate = _problem([70], H=1, dk=5, dv=4, n_tok=70, seed=7)
+    p["row_token"] = np.arange(70, dtype=np.int32)
+    g = oracle.segments_bwd(p["seg_off"], p["seg_state"], p["row_token"], p["q"], p["k"], p["v"], p["a"], p["c"],
+                            p["state0"], d_o, dstate, rule=rule)
+    slot = p["seg_state"][0]
+    r = _chunk_bwd(p["q"][:, 0], p["k"][:, 0], p["v"][:, 0], p["a"][:, 0], p["c"][:, 0], p["state0"][slot, 0],
+                   d_o[:, 0], dstate[slot, 0], C, rule)
+    for name in ("dq", "dk", "dv", "da", "dc"):
+        np.testing.assert_allclose(r[name], g[name][:, 0], rtol=1e-9, atol=1e-10, err_msg=name)
+    np.testing.assert_allclose(r["dS0"], g["dstate0"][slot, 0], rtol=1e-9, atol=1e-10)
