@@ -37,6 +37,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-single", action="store_true", help="skip the single enlarged-memory line")
     p.add_argument("--no-gla", action="store_true", help="skip the gated linear attention layer line")
+    p.add_argument("--no-bwd", action="store_true", help="skip the recurrence-gradient line")
     p.add_argument("--traffic", default=None,
                    help="summary of measured HBM bytes per call (default: profiles/traffic_<workload>.json)")
     return p.parse_args()
@@ -107,6 +108,40 @@ def time_gla_layer(cfg, inp, x, alpha, beta, steps, warmup):
     NT = cfg.B * cfg.T
     return {"workload": "%s layer with gated linear attention memories (same shapes, inputs and weights)" % cfg.name,
             "tokens_per_s": round(NT / (wall / steps), 1), "ms_per_step": round(wall * 1e3 / steps, 4)}
+
+
+def time_chunk_bwd(cfg, inp, x, alpha, beta, steps, warmup):
+    """Gradients of the memories' recurrence (gdn_chunk_bwd) over the layer's own
+    segments: route, dispatch and projections run once, then K timed calls with
+    random upstream gradients dL/do (per packed row) and dL/d(final states)."""
+    import torch
+    from mixture_memories_recurrence_amd import mom, synth
+    layer = mom.MomLayer(cfg, inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"])
+    _, _, b = layer.forward(x, alpha, beta)
+    gr = synth.make_chain_grads(b["N"], cfg.H, cfg.dk, cfg.dv, b["n_seg"], seed=9)
+    d_o = torch.from_numpy(gr["d_o"]).cuda()
+    dstate = torch.from_numpy(gr["dstate"]).cuda()
+    for _ in range(warmup):
+        layer.chunk_backward(b, d_o, dstate)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        layer.chunk_backward(b, d_o, dstate)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    N, NT, H, dk, dv = b["N"], b["NT"], cfg.H, cfg.dk, cfg.dv
+    # algorithmic bytes: q (per token), k, v (half), gates, dL/do, dL/dS_out read once;
+    # dq, dk, dv, d_alpha, d_beta, dL/dS_in written once (float32)
+    n_st = b["n_seg"] * H * dk * dv * 4
+    nbytes = (NT * H * dk * 2 + N * H * (dk + dv) * 2 + N * H * 8 + N * H * dv * 4 + n_st
+              + N * H * (2 * dk + dv) * 4 + N * H * 8 + n_st)
+    return {"workload": "%s recurrence gradients (gdn_chunk_bwd over the layer's %d segments, %d rows)"
+                        % (cfg.name, b["n_seg"], N),
+            "ms": round(ms, 4), "tokens_per_s": round(NT / (ms * 1e-3), 1),
+            "algorithmic_bytes": nbytes, "achieved_gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
 def time_single_memory(steps, warmup):
@@ -298,6 +333,8 @@ def main():
 
     if not args.no_single:
         res["single_memory"] = time_single_memory(args.steps, args.warmup)
+    if not args.no_bwd:
+        res["chunk_bwd"] = time_chunk_bwd(cfg, inp, x, alpha, beta, args.steps, args.warmup)
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = time_cpu_baseline(cfg, inp)

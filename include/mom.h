@@ -23,6 +23,8 @@
  *                    modify (jxzklqfsx.com write-up, "Linear Recurrent Memory";
  *                    research.elamur.ai summary: MoM works with different
  *                    update rules).
+ *   gdn_chunk_bwd    the gradients of gdn_chunk_fwd (and gla_chunk_bwd of
+ *                    gla_chunk_fwd), for training.
  *   gdn_decode_step  one recurrent step per sequence (constant-cost inference,
  *                    jxzklqfsx.com write-up, introduction and inference section).
  *   mom_combine      router-weighted sum of the per-memory reads plus the
@@ -172,6 +174,47 @@ mom_status gla_chunk_fwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, in
                          const float* alpha_p, const float* beta_p, const float* state_in,
                          float* state_out, float* o, void* ws, size_t ws_bytes, void* stream);
 
+/* Gradients of gdn_chunk_fwd (reverse mode), for training: given
+ * d_o = dL/do and dstate_out = dL/d(final states), the gradients of L with
+ * respect to the forward's inputs.  The pages give no backward formulas (the
+ * jxzklqfsx.com write-up, introduction, states that the layer trains in linear
+ * time); these are the chain rule applied to the recurrence above, evaluated
+ * in the same chunk form (half operands on the matrix cores, float32
+ * accumulation and states).  Only the half (dims->dtype == MOM_DTYPE_BF16)
+ * storage is supported; float32 returns MOM_ERR_UNSUPPORTED.
+ *   inputs:   as gdn_chunk_fwd (dims, segments, slots, row_token, q, k, v,
+ *             alpha_p, beta_p, state_in or NULL = zeros)
+ *   d_o        [N][H][dv] float32
+ *   dstate_out [n_state][H][dk][dv] float32 or NULL (zeros)
+ *   dq         [N][H][dk] float32 out: per packed row, the gradient of the
+ *              query as that row uses it (rows that read the same token are
+ *              not summed; the caller adds them)
+ *   dk [N][H][dk], dv [N][H][dv], d_alpha, d_beta [N][H] float32 out
+ *   dstate_in  [n_state][H][dk][dv] float32 out: dL/d(entering state); the
+ *              slots of the segments given are written (an empty segment
+ *              copies its dstate_out), others are left as they are
+ * Rows outside every segment are not written.  Different segments must use
+ * different slots.  ws holds at least gdn_chunk_bwd_workspace_bytes(dims,
+ * n_seg, n_rows) bytes; its contents on entry do not matter.  Other errors as
+ * gdn_chunk_fwd. */
+mom_status gdn_chunk_bwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
+                         int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
+                         const int32_t* row_token, const void* q, const void* k, const void* v,
+                         const float* alpha_p, const float* beta_p, const float* state_in,
+                         const float* d_o, const float* dstate_out, float* dq, float* dk, float* dv,
+                         float* d_alpha, float* d_beta, float* dstate_in, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* gla_chunk_bwd: the gradients of gla_chunk_fwd, with the arguments, layouts,
+ * workspace and errors of gdn_chunk_bwd. */
+mom_status gla_chunk_bwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
+                         int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
+                         const int32_t* row_token, const void* q, const void* k, const void* v,
+                         const float* alpha_p, const float* beta_p, const float* state_in,
+                         const float* d_o, const float* dstate_out, float* dq, float* dk, float* dv,
+                         float* d_alpha, float* d_beta, float* dstate_in, void* ws, size_t ws_bytes,
+                         void* stream);
+
 /* One recurrent step for n_seq sequences with one new token each (T = 1 view:
  * rows as written by mom_dispatch/mom_project for dims with B = n_seq, T = 1).
  * For sequence b and slot j < topk the memory is idx[b][j] and the packed row
@@ -212,6 +255,12 @@ size_t mom_workspace_bytes(const mom_dims* dims, int32_t which);
  * masked, decayed query-key products (half) and the log-decay prefix sums
  * (float32).  0 for invalid arguments. */
 size_t gdn_chunk_workspace_bytes(const mom_dims* dims, int32_t n_seg, int32_t n_rows);
+
+/* Workspace bytes gdn_chunk_bwd / gla_chunk_bwd need for n_seg segments over
+ * n_rows packed rows: the forward's per-chunk factors, X = (I + A)^{-1} in
+ * float32, and the states entering and the state gradients leaving every
+ * chunk (half).  0 for invalid arguments or float32 storage. */
+size_t gdn_chunk_bwd_workspace_bytes(const mom_dims* dims, int32_t n_seg, int32_t n_rows);
 
 /* Static text for a status code. */
 const char* mom_status_string(int32_t status);

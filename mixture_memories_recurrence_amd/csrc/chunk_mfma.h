@@ -1,0 +1,201 @@
+// Device helpers shared by the chunkwise kernels on the gfx950 matrix cores
+// (forward and gradients): chunk numbering over packed segments, LDS fences,
+// the 32x32x16 half product and its accumulator-to-operand move, asynchronous
+// global -> LDS copies, and the swizzled LDS tile reads.
+#pragma once
+#include "common.h"
+
+namespace mom {
+
+constexpr int GC = 64;     // chunk rows
+
+
+// ------------------------------------------------------------------ chunk numbering
+// The chunks of segment s are numbered from the count of chunks (ceil(len / 64)
+// each) in the segments before it.  Each wave that needs the numbering scans
+// the segments' chunk counts itself, 64 segments per step, so no separate
+// launch computes it.
+__device__ __forceinline__ int seg_chunks(const int32_t* seg_off, int i) {
+  return (seg_off[i + 1] - seg_off[i] + GC - 1) / GC;
+}
+// Chunks in segments [0, s); the same value in every lane.
+__device__ __forceinline__ int chunks_before(const int32_t* __restrict__ seg_off, int s, int lane) {
+  int sum = 0;
+  for (int s0 = 0; s0 < s; s0 += 64) {
+    int n = s0 + lane < s ? seg_chunks(seg_off, s0 + lane) : 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o, 64);
+    sum += n;
+  }
+  return sum;
+}
+// Segment holding chunk c and the number of its first chunk; false when c is
+// at or past the last chunk.  The same result in every lane.
+__device__ __forceinline__ bool locate_chunk(const int32_t* __restrict__ seg_off, int n_seg, int c, int lane,
+                                             int& seg, int& base) {
+  int before = 0;
+  for (int s0 = 0; s0 < n_seg; s0 += 64) {
+    const int n = s0 + lane < n_seg ? seg_chunks(seg_off, s0 + lane) : 0;
+    int incl = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
+    }
+    const int first = before + incl - n;  // number of this lane's segment's first chunk
+    const uint64_t hit = __ballot(n > 0 && first <= c && c < first + n);
+    if (hit) {
+      const int l = __ffsll((unsigned long long)hit) - 1;
+      seg = s0 + l;
+      base = __shfl(first, l, 64);
+      return true;
+    }
+    before += __shfl(incl, 63, 64);
+  }
+  return false;
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void vm_wait_8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
+
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef float f16x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u2v __attribute__((ext_vector_type(2)));
+typedef short s4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f16x16 mfma32(const h8v& a, const h8v& b, const f16x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef float f2v __attribute__((ext_vector_type(2)));
+// Two floats to a half pair (round to nearest even; one v_cvt_pk_f16_f32).
+__device__ __forceinline__ unsigned pack_h2(float a, float b) {
+  const f2v v = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, h2v));
+}
+// Rows [16p, 16p+16) of a 32x32 accumulator tile as the 16-deep operand (k =
+// row) of a 32x32x16 product, row 8q+4g+t scaled by sc[4 (q - 2p) + t].
+__device__ __forceinline__ h8v acc_to_b(const f16x16& d, int p, const float* sc) {
+  const unsigned X0 = pack_h2(d[8 * p + 0] * sc[0], d[8 * p + 1] * sc[1]);
+  const unsigned X1 = pack_h2(d[8 * p + 2] * sc[2], d[8 * p + 3] * sc[3]);
+  const unsigned Y0 = pack_h2(d[8 * p + 4] * sc[4], d[8 * p + 5] * sc[5]);
+  const unsigned Y1 = pack_h2(d[8 * p + 6] * sc[6], d[8 * p + 7] * sc[7]);
+  const u2v s0 = __builtin_amdgcn_permlane32_swap(X0, Y0, false, false);
+  const u2v s1 = __builtin_amdgcn_permlane32_swap(X1, Y1, false, false);
+  const unsigned w4[4] = {s0.x, s1.x, s0.y, s1.y};
+  return __builtin_bit_cast(h8v, *reinterpret_cast<const __attribute__((ext_vector_type(4))) unsigned*>(w4));
+}
+
+// Asynchronous global -> LDS copies (global_load_lds_dwordx4 / _dword): lane
+// l's 16 (4) bytes land at lds_base + 16 l (4 l); lds_base must be the same in
+// every lane.  They are issued from inline assembly so that the compiler, which
+// cannot tell the two halves of the double buffer apart, does not wait for them
+// before every LDS read; the kernel waits for them itself (vm_wait_all) before
+// the barrier that publishes the data.  M0 is restored after the issue.
+__device__ __forceinline__ unsigned lds_offset(const void* p) {
+  return __builtin_amdgcn_readfirstlane((unsigned)(size_t)(const __attribute__((address_space(3))) void*)p);
+}
+__device__ __forceinline__ void dma_b128(const void* g, const void* lds_base) {
+  unsigned save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(save)
+               : "s"(lds_offset(lds_base)), "v"(g)
+               : "memory");
+}
+__device__ __forceinline__ void dma_b32(const void* g, const void* lds_base) {
+  unsigned save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(save)
+               : "s"(lds_offset(lds_base)), "v"(g)
+               : "memory");
+}
+
+// LDS tiles are stored without padding, the 16-byte piece c of row r at piece
+// position c ^ swz(r), so that both access patterns below are conflict-free:
+// 16 consecutive rows read at one piece (operands with k along the row), and 4
+// consecutive rows read 32 bytes each (transposed operands).
+//   256-byte rows: swz = 2 (r & 3) + 8 ((r >> 2) & 1) + ((r >> 3) & 1)
+//   128-byte rows: swz = 2 ((r >> 1) & 3) + ((r >> 3) & 1)
+template <int RH>  // halfs per row: 128 or 64
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (RH == 128) return c ^ (((r & 3) << 1) | (((r >> 2) & 1) << 3) | ((r >> 3) & 1));
+  else return c ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+}
+// Operand with k along the row: X[row][16 kb + 8 g .. + 7] (g = lane / 32).
+template <int RH>
+__device__ __forceinline__ h8v row_frag(const f16_t* X, int row, int kb, int g) {
+  return *reinterpret_cast<const h8v*>(X + row * RH + 8 * swz<RH>(row, 2 * kb + g));
+}
+// Transposing LDS read (ds_read_b64_tr_b16): inside each 16-lane group, lane i
+// receives element i % 4 of the 8-byte values addressed by lanes i / 4,
+// 4 + i / 4, 8 + i / 4 and 12 + i / 4 of the group.  Pointing lane j at
+// X[k0 + j / 4][n0 + 4 (j % 4)] hands lane i the column n0 + i of rows
+// k0 .. k0 + 3, so a k-major operand comes straight from a row-major tile.
+__device__ __forceinline__ s4v lds_tr4(const f16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)p);
+}
+// Operand with k down the rows: X[16 kb + 8 g + t][c0 + lane % 32], t = 0..7.
+template <int RH>
+__device__ __forceinline__ h8v col_frag(const f16_t* X, int kb, int c0, int lane) {
+  const int row = 16 * kb + 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int ch = col >> 3, sub = col & 7;
+  const s4v a = lds_tr4(X + row * RH + 8 * swz<RH>(row, ch) + sub);
+  const s4v b = lds_tr4(X + (row + 4) * RH + 8 * swz<RH>(row + 4, ch) + sub);
+  const s4v v8[2] = {a, b};
+  return __builtin_bit_cast(h8v, v8);
+}
+// Copy instruction j (of GC / RPI / NW per wave) of a 64-row tile of RH-half
+// rows, copied by waves [0, NW) into its swizzled LDS image; src(r, c) is the
+// global address of piece c of tile row r.
+template <int RH, int NW>
+struct TileCopy {
+  static constexpr int CPR = RH / 8, RPI = 64 / CPR, PER_WAVE = GC / RPI / NW;
+  static_assert(GC % (RPI * NW) == 0, "tile rows split evenly over the waves");
+  // tile row whose piece lane `lane` of wave w copies in instruction j
+  __device__ static __forceinline__ int row(int w, int lane, int j) { return RPI * (w + NW * j) + lane / CPR; }
+  template <class Src>
+  __device__ static __forceinline__ void issue(f16_t* dst, int w, int lane, int j, Src src) {
+    const int it = w + NW * j;
+    const int r = RPI * it + lane / CPR;
+    dma_b128(src(r, swz<RH>(r, lane % CPR)), dst + RPI * it * RH);
+  }
+};
+
+// Keeps the scheduler from mixing the phases of a chunk, which would raise the
+// number of live registers past the 256 architectural VGPRs.
+#define CHAIN_PHASE() __builtin_amdgcn_sched_barrier(0)
+
+// Workspace of the chunkwise path, per (chunk, head): the solved triangular
+// factor T and the decayed query-key products P (half), and gamma,
+// gamma_L / gamma (float32).  n_rows / 64 + n_seg bounds the chunk count.
+struct ChunkWs {
+  f16_t* T;
+  f16_t* P;
+  float* E;
+  size_t bytes;
+};
+
+inline ChunkWs chunk_ws_layout(void* base, int64_t n_seg, int64_t n_rows, int H, int dk) {
+  const int64_t nch = n_rows / GC + n_seg;  // bound on the number of chunks
+  ChunkWs w;
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    const size_t o = off;
+    off += (b + 255) / 256 * 256;
+    return o;
+  };
+  const size_t o_t = take((size_t)nch * H * GC * GC * 2);
+  const size_t o_p = take((size_t)nch * H * GC * GC * 2);
+  const size_t o_e = take((size_t)nch * H * 2 * GC * 4);
+  char* b = (char*)base;
+  w.T = (f16_t*)(b + o_t);
+  w.P = (f16_t*)(b + o_p);
+  w.E = (float*)(b + o_e);
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace mom

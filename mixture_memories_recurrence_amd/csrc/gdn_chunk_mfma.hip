@@ -23,57 +23,9 @@
 //   k_gdn_chain  one block per (segment, head, 64 or 128 value columns); it
 //                walks the segment's chunks in order with the state in float32
 //                matrix-core accumulators (see the comment at the kernel).
-#include "common.h"
+#include "chunk_mfma.h"
 
 namespace mom {
-
-constexpr int GC = 64;     // chunk rows
-
-
-// ------------------------------------------------------------------ chunk numbering
-// The chunks of segment s are numbered from the count of chunks (ceil(len / 64)
-// each) in the segments before it.  Each wave that needs the numbering scans
-// the segments' chunk counts itself, 64 segments per step, so no separate
-// launch computes it.
-__device__ __forceinline__ int seg_chunks(const int32_t* seg_off, int i) {
-  return (seg_off[i + 1] - seg_off[i] + GC - 1) / GC;
-}
-// Chunks in segments [0, s); the same value in every lane.
-__device__ __forceinline__ int chunks_before(const int32_t* __restrict__ seg_off, int s, int lane) {
-  int sum = 0;
-  for (int s0 = 0; s0 < s; s0 += 64) {
-    int n = s0 + lane < s ? seg_chunks(seg_off, s0 + lane) : 0;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o, 64);
-    sum += n;
-  }
-  return sum;
-}
-// Segment holding chunk c and the number of its first chunk; false when c is
-// at or past the last chunk.  The same result in every lane.
-__device__ __forceinline__ bool locate_chunk(const int32_t* __restrict__ seg_off, int n_seg, int c, int lane,
-                                             int& seg, int& base) {
-  int before = 0;
-  for (int s0 = 0; s0 < n_seg; s0 += 64) {
-    const int n = s0 + lane < n_seg ? seg_chunks(seg_off, s0 + lane) : 0;
-    int incl = n;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += u;
-    }
-    const int first = before + incl - n;  // number of this lane's segment's first chunk
-    const uint64_t hit = __ballot(n > 0 && first <= c && c < first + n);
-    if (hit) {
-      const int l = __ffsll((unsigned long long)hit) - 1;
-      seg = s0 + l;
-      base = __shfl(first, l, 64);
-      return true;
-    }
-    before += __shfl(incl, 63, 64);
-  }
-  return false;
-}
 
 // ------------------------------------------------------------------ chain
 // One block per (segment, head, DVB = 32 NW value columns), NW waves.  Value
@@ -91,119 +43,9 @@ __device__ __forceinline__ bool locate_chunk(const int32_t* __restrict__ seg_off
 // exchanged between waves, so the only block barrier per chunk publishes the
 // next chunk's inputs, which every wave prefetches into the idle half of a
 // double buffer with asynchronous global -> LDS copies.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-__device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void vm_wait_8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
-
-typedef _Float16 h8v __attribute__((ext_vector_type(8)));
-typedef float f16x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u2v __attribute__((ext_vector_type(2)));
-typedef short s4v __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f16x16 mfma32(const h8v& a, const h8v& b, const f16x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-typedef _Float16 h2v __attribute__((ext_vector_type(2)));
-typedef float f2v __attribute__((ext_vector_type(2)));
-// Two floats to a half pair (round to nearest even; one v_cvt_pk_f16_f32).
-__device__ __forceinline__ unsigned pack_h2(float a, float b) {
-  const f2v v = {a, b};
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, h2v));
-}
-// Rows [16p, 16p+16) of a 32x32 accumulator tile as the 16-deep operand (k =
-// row) of a 32x32x16 product, row 8q+4g+t scaled by sc[4 (q - 2p) + t].
-__device__ __forceinline__ h8v acc_to_b(const f16x16& d, int p, const float* sc) {
-  const unsigned X0 = pack_h2(d[8 * p + 0] * sc[0], d[8 * p + 1] * sc[1]);
-  const unsigned X1 = pack_h2(d[8 * p + 2] * sc[2], d[8 * p + 3] * sc[3]);
-  const unsigned Y0 = pack_h2(d[8 * p + 4] * sc[4], d[8 * p + 5] * sc[5]);
-  const unsigned Y1 = pack_h2(d[8 * p + 6] * sc[6], d[8 * p + 7] * sc[7]);
-  const u2v s0 = __builtin_amdgcn_permlane32_swap(X0, Y0, false, false);
-  const u2v s1 = __builtin_amdgcn_permlane32_swap(X1, Y1, false, false);
-  const unsigned w4[4] = {s0.x, s1.x, s0.y, s1.y};
-  return __builtin_bit_cast(h8v, *reinterpret_cast<const __attribute__((ext_vector_type(4))) unsigned*>(w4));
-}
-
-// Asynchronous global -> LDS copies (global_load_lds_dwordx4 / _dword): lane
-// l's 16 (4) bytes land at lds_base + 16 l (4 l); lds_base must be the same in
-// every lane.  They are issued from inline assembly so that the compiler, which
-// cannot tell the two halves of the double buffer apart, does not wait for them
-// before every LDS read; the kernel waits for them itself (vm_wait_all) before
-// the barrier that publishes the data.  M0 is restored after the issue.
-__device__ __forceinline__ unsigned lds_offset(const void* p) {
-  return __builtin_amdgcn_readfirstlane((unsigned)(size_t)(const __attribute__((address_space(3))) void*)p);
-}
-__device__ __forceinline__ void dma_b128(const void* g, const void* lds_base) {
-  unsigned save;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(save)
-               : "s"(lds_offset(lds_base)), "v"(g)
-               : "memory");
-}
-__device__ __forceinline__ void dma_b32(const void* g, const void* lds_base) {
-  unsigned save;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(save)
-               : "s"(lds_offset(lds_base)), "v"(g)
-               : "memory");
-}
-
-// LDS tiles are stored without padding, the 16-byte piece c of row r at piece
-// position c ^ swz(r), so that both access patterns below are conflict-free:
-// 16 consecutive rows read at one piece (operands with k along the row), and 4
-// consecutive rows read 32 bytes each (transposed operands).
-//   256-byte rows: swz = 2 (r & 3) + 8 ((r >> 2) & 1) + ((r >> 3) & 1)
-//   128-byte rows: swz = 2 ((r >> 1) & 3) + ((r >> 3) & 1)
-template <int RH>  // halfs per row: 128 or 64
-__device__ __forceinline__ int swz(int r, int c) {
-  if constexpr (RH == 128) return c ^ (((r & 3) << 1) | (((r >> 2) & 1) << 3) | ((r >> 3) & 1));
-  else return c ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
-}
-// Operand with k along the row: X[row][16 kb + 8 g .. + 7] (g = lane / 32).
-template <int RH>
-__device__ __forceinline__ h8v row_frag(const f16_t* X, int row, int kb, int g) {
-  return *reinterpret_cast<const h8v*>(X + row * RH + 8 * swz<RH>(row, 2 * kb + g));
-}
-// Transposing LDS read (ds_read_b64_tr_b16): inside each 16-lane group, lane i
-// receives element i % 4 of the 8-byte values addressed by lanes i / 4,
-// 4 + i / 4, 8 + i / 4 and 12 + i / 4 of the group.  Pointing lane j at
-// X[k0 + j / 4][n0 + 4 (j % 4)] hands lane i the column n0 + i of rows
-// k0 .. k0 + 3, so a k-major operand comes straight from a row-major tile.
-__device__ __forceinline__ s4v lds_tr4(const f16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)p);
-}
-// Operand with k down the rows: X[16 kb + 8 g + t][c0 + lane % 32], t = 0..7.
-template <int RH>
-__device__ __forceinline__ h8v col_frag(const f16_t* X, int kb, int c0, int lane) {
-  const int row = 16 * kb + 8 * (lane >> 5) + ((lane & 15) >> 2);
-  const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int ch = col >> 3, sub = col & 7;
-  const s4v a = lds_tr4(X + row * RH + 8 * swz<RH>(row, ch) + sub);
-  const s4v b = lds_tr4(X + (row + 4) * RH + 8 * swz<RH>(row + 4, ch) + sub);
-  const s4v v8[2] = {a, b};
-  return __builtin_bit_cast(h8v, v8);
-}
-// Copy instruction j (of GC / RPI / NW per wave) of a 64-row tile of RH-half
-// rows, copied by waves [0, NW) into its swizzled LDS image; src(r, c) is the
-// global address of piece c of tile row r.
-template <int RH, int NW>
-struct TileCopy {
-  static constexpr int CPR = RH / 8, RPI = 64 / CPR, PER_WAVE = GC / RPI / NW;
-  static_assert(GC % (RPI * NW) == 0, "tile rows split evenly over the waves");
-  // tile row whose piece lane `lane` of wave w copies in instruction j
-  __device__ static __forceinline__ int row(int w, int lane, int j) { return RPI * (w + NW * j) + lane / CPR; }
-  template <class Src>
-  __device__ static __forceinline__ void issue(f16_t* dst, int w, int lane, int j, Src src) {
-    const int it = w + NW * j;
-    const int r = RPI * it + lane / CPR;
-    dma_b128(src(r, swz<RH>(r, lane % CPR)), dst + RPI * it * RH);
-  }
-};
-
-// Keeps the scheduler from mixing the phases of a chunk, which would raise the
-// number of live registers past the 256 architectural VGPRs.
-#define CHAIN_PHASE() __builtin_amdgcn_sched_barrier(0)
-
+// With SAVE the kernel only walks the states, for the gradients: it stores the
+// state entering every chunk (transposed, half: hws[chunk][head][dv][DK]) and
+// skips the read-out (no Q, P or O); state_out may then be null.
 template <int DK, int NW>
 struct ChainLds {
   static constexpr int DVB = 32 * NW;
@@ -215,13 +57,13 @@ struct ChainLds {
   static constexpr size_t BYTES = OST + (size_t)NW * 32 * 32 * sizeof(float);
 };
 
-template <int DK, int NW, bool DELTA>
+template <int DK, int NW, bool DELTA, bool SAVE>
 __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     int H, int dv, int n_seg, const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_state,
     const f16_t* __restrict__ k, const f16_t* __restrict__ v,
     const f16_t* __restrict__ Tws, const f16_t* __restrict__ Pws, const float* __restrict__ Ews,
     const int32_t* __restrict__ row_token, const f16_t* __restrict__ q, const float* __restrict__ state_in,
-    float* __restrict__ state_out, float* __restrict__ o) {
+    float* __restrict__ state_out, float* __restrict__ o, f16_t* __restrict__ hws) {
   using LY = ChainLds<DK, NW>;
   constexpr int DVB = LY::DVB, ND = DK / 32, NKD = DK / 16;
   extern __shared__ __attribute__((aligned(16))) f16_t smem[];
@@ -290,6 +132,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
         return k + ((pf_r0 + min(r, pf_L - 1)) * H + h) * DK + 8 * c;
       });
     } else if ((i -= CK::PER_WAVE) < CK::PER_WAVE) {
+      if (SAVE) return;  // no read-out: Q is not needed
       const int64_t t = qtok[i];
       CK::issue(pf_B + LY::OFF_Q, w, lane, i, [&](int r, int c) { return q + (t * H + h) * DK + 8 * c; });
     } else if ((i -= CK::PER_WAVE) < CV::PER_WAVE) {
@@ -299,6 +142,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     } else if ((i -= CV::PER_WAVE) < CT::PER_WAVE) {
       CT::issue(pf_B + LY::OFF_T, w, lane, i, [&](int r, int c) { return Tws + (pf_chk * GC + r) * GC + 8 * c; });
     } else if ((i -= CT::PER_WAVE) < CT::PER_WAVE) {
+      if (SAVE) return;
       CT::issue(pf_B + LY::OFF_P, w, lane, i, [&](int r, int c) { return Pws + (pf_chk * GC + r) * GC + 8 * c; });
     } else if (i == CT::PER_WAVE) {
       if (w < 2) dma_b32(Ews + pf_chk * 2 * GC + GC * w + lane, pf_B + LY::OFF_E + 2 * GC * w);
@@ -340,7 +184,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     // This wave's part of the chunk's inputs has landed.  Vector memory
     // operations complete in issue order; the only ones issued after the
     // prefetch are the previous chunk's 8 output stores, which need not wait.
-    if (r0 == rbeg) vm_wait_all();
+    if (r0 == rbeg || SAVE) vm_wait_all();
     else vm_wait_8();
     lds_barrier();  // every wave's part has landed; every wave is done with the other buffer
     pf_setup(r0 + GC < rend ? r0 + GC : r0, buf ^ 1,
@@ -353,6 +197,18 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     const f16_t* Ts = Bc + LY::OFF_T;
     const f16_t* Ps = Bc + LY::OFF_P;
     const float* Eg = reinterpret_cast<const float*>(Bc + LY::OFF_E);  // gamma_i, then gamma_L / gamma_i
+    if constexpr (SAVE) {
+      // the entering state, transposed: this lane's column, key rows
+      // 32 a + 8 qq + 4 g + 0..3 as one 8-byte piece
+      f16_t* hc = hws + ((int64_t)(cbase + (r0 - rbeg) / GC) * H + h) * dv * DK + (int64_t)(ncol0 + c32) * DK;
+#pragma unroll
+      for (int a = 0; a < ND; ++a)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const u2v pc = {pack_h2(S[a][4 * qq], S[a][4 * qq + 1]), pack_h2(S[a][4 * qq + 2], S[a][4 * qq + 3])};
+          *reinterpret_cast<u2v*>(hc + 32 * a + 8 * qq + 4 * g2) = pc;
+        }
+    }
 
     // ---- Y = K S and O^T = S^T Q^T, two 32-row tiles each (four chains); the
     // state becomes an operand (k = key rows) one 16-row block at a time
@@ -372,7 +228,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
 #pragma unroll
       for (int bt = 0; bt < 2; ++bt) {
         Y[bt] = mfma32(row_frag<DK>(Ks, 32 * bt + c32, kb, g2), sb, Y[bt]);
-        O[bt] = mfma32(sb, row_frag<DK>(Qs, 32 * bt + c32, kb, g2), O[bt]);
+        if (!SAVE) O[bt] = mfma32(sb, row_frag<DK>(Qs, 32 * bt + c32, kb, g2), O[bt]);
       }
     }
     CHAIN_PHASE();
@@ -422,35 +278,37 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
         ub[2 * bt + p] = acc_to_b(U[bt], p, ones);
         u2b[2 * bt + p] = acc_to_b(U[bt], p, sc);
       }
-    // ---- O^T += U^T P^T, after S^T Q^T is scaled to S^T Q'^T (column i by gamma_i)
+    if constexpr (!SAVE) {
+      // ---- O^T += U^T P^T, after S^T Q^T is scaled to S^T Q'^T (column i by gamma_i)
 #pragma unroll
-    for (int bt = 0; bt < 2; ++bt) {
-      const float gm = Eg[32 * bt + c32];
+      for (int bt = 0; bt < 2; ++bt) {
+        const float gm = Eg[32 * bt + c32];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) O[bt][i] *= gm;
-    }
-#pragma unroll
-    for (int kb = 0; kb < GC / 16; ++kb)
-#pragma unroll
-      for (int bt = 0; bt < 2; ++bt) O[bt] = mfma32(ub[kb], row_frag<GC>(Ps, 32 * bt + c32, kb, g2), O[bt]);
-    // O out through this wave's LDS tile, so that each store writes 8 whole
-    // 128-byte rows (lane l: row 8 j + l / 8, columns 4 (l % 8) .. + 3) rather
-    // than 32-byte pieces of 32 rows.  Piece c of tile row r sits at position
-    // c ^ (r & 7).  8 stores (all lanes active unless this is the last chunk).
-#pragma unroll
-    for (int bt = 0; bt < 2; ++bt) {
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        *reinterpret_cast<float4*>(ost + 32 * c32 + 4 * ((2 * qq + g2) ^ (c32 & 7))) =
-            make_float4(O[bt][4 * qq], O[bt][4 * qq + 1], O[bt][4 * qq + 2], O[bt][4 * qq + 3]);
-      wave_lds_fence();
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rr = 8 * j + (lane >> 3), pc = lane & 7;
-        const float4 val = *reinterpret_cast<const float4*>(ost + 32 * rr + 4 * (pc ^ (rr & 7)));
-        if (32 * bt + rr < L) *reinterpret_cast<float4*>(o + ((r0 + 32 * bt + rr) * H + h) * dv + ncol0 + 4 * pc) = val;
+        for (int i = 0; i < 16; ++i) O[bt][i] *= gm;
       }
-      wave_lds_fence();  // the tile is read before the next half overwrites it
+#pragma unroll
+      for (int kb = 0; kb < GC / 16; ++kb)
+#pragma unroll
+        for (int bt = 0; bt < 2; ++bt) O[bt] = mfma32(ub[kb], row_frag<GC>(Ps, 32 * bt + c32, kb, g2), O[bt]);
+      // O out through this wave's LDS tile, so that each store writes 8 whole
+      // 128-byte rows (lane l: row 8 j + l / 8, columns 4 (l % 8) .. + 3) rather
+      // than 32-byte pieces of 32 rows.  Piece c of tile row r sits at position
+      // c ^ (r & 7).  8 stores (all lanes active unless this is the last chunk).
+#pragma unroll
+      for (int bt = 0; bt < 2; ++bt) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          *reinterpret_cast<float4*>(ost + 32 * c32 + 4 * ((2 * qq + g2) ^ (c32 & 7))) =
+              make_float4(O[bt][4 * qq], O[bt][4 * qq + 1], O[bt][4 * qq + 2], O[bt][4 * qq + 3]);
+        wave_lds_fence();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rr = 8 * j + (lane >> 3), pc = lane & 7;
+          const float4 val = *reinterpret_cast<const float4*>(ost + 32 * rr + 4 * (pc ^ (rr & 7)));
+          if (32 * bt + rr < L) *reinterpret_cast<float4*>(o + ((r0 + 32 * bt + rr) * H + h) * dv + ncol0 + 4 * pc) = val;
+        }
+        wave_lds_fence();  // the tile is read before the next half overwrites it
+      }
     }
     // ---- S <- gamma_L S + K^T U', U' = diag(gamma_L / gamma) U
     const float eL = Eg[GC - 1];
@@ -464,6 +322,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
       for (int a = 0; a < ND; ++a) S[a] = mfma32(col_frag<DK>(Ks, kb, 32 * a, lane), u2b[kb], S[a]);
   }
   vm_wait_all();  // the last (repeated) prefetch has landed before the block ends
+  if (SAVE && !state_out) return;
 #pragma unroll
   for (int a = 0; a < ND; ++a)
 #pragma unroll
@@ -482,7 +341,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
 //   A_ij = c_i e^{g_i - g_j} k_i.k_j (j < i) to LDS as float32, P_ij =
 //   e^{g_i - g_j} q_i.k_j (j <= i) to global as half;
 //   X = (I + A)^{-1} by blocked substitution in float32 (below), T = X diag(c)
-//   as half.
+//   as half, and X itself as float32 when Xws is given (for the gradients).
 // Rows at or past the chunk length L are zero in K, Q, A and P; T is then zero
 // in those rows and columns (c = 0 there).
 constexpr int PREP_ALD = GC + 4;  // float row stride of A in LDS
@@ -495,7 +354,8 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
                                                   const int32_t* __restrict__ row_token, const f16_t* __restrict__ q,
                                                   const f16_t* __restrict__ k, const float* __restrict__ alpha_p,
                                                   const float* __restrict__ beta_p, f16_t* __restrict__ Tws,
-                                                  f16_t* __restrict__ Pws, float* __restrict__ Ews) {
+                                                  f16_t* __restrict__ Pws, float* __restrict__ Ews,
+                                                  float* __restrict__ Xws) {
   constexpr int NKD = DK / 16;
   __shared__ __attribute__((aligned(16))) float As_all[4][GC * PREP_ALD];
   __shared__ float gs_all[4][GC];
@@ -683,6 +543,7 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
   {
     const int i = lane, ib = i >> 4;
     f16_t* trow = Tws + (ch * GC + i) * GC;
+    float* xrow = Xws ? Xws + (ch * GC + i) * GC : nullptr;
 #pragma unroll
     for (int m = 0; m < GC / 8; ++m) {
       const int jb = m >> 1;
@@ -690,6 +551,10 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
       if (jb > ib) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) hv[e] = (f16_t)0.f;
+        if (xrow) {
+          *reinterpret_cast<float4*>(xrow + 8 * m) = make_float4(0.f, 0.f, 0.f, 0.f);
+          *reinterpret_cast<float4*>(xrow + 8 * m + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       } else {
         const float* src = jb == ib ? As + i * PREP_ALD + 8 * m
                                     : As + (16 * jb + (i & 15)) * PREP_ALD + 16 * ib + 8 * (m & 1);
@@ -701,6 +566,13 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
         const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) hv[e] = (f16_t)((jb == ib && 8 * m + e > i) ? 0.f : xv[e] * cv[e]);
+        if (xrow) {
+          float xz[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xz[e] = (jb == ib && 8 * m + e > i) ? 0.f : xv[e];
+          *reinterpret_cast<float4*>(xrow + 8 * m) = make_float4(xz[0], xz[1], xz[2], xz[3]);
+          *reinterpret_cast<float4*>(xrow + 8 * m + 4) = make_float4(xz[4], xz[5], xz[6], xz[7]);
+        }
       }
       *reinterpret_cast<half8*>(trow + 8 * m) = hv;
     }
@@ -708,54 +580,28 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
 }
 
 // ------------------------------------------------------------------ workspace + launch
-struct ChunkWs {
-  f16_t* T;
-  f16_t* P;
-  float* E;
-  size_t bytes;
-};
-
-inline ChunkWs chunk_ws_layout(void* base, int64_t n_seg, int64_t n_rows, int H, int dk) {
-  const int64_t nch = n_rows / GC + n_seg;  // bound on the number of chunks
-  ChunkWs w;
-  size_t off = 0;
-  auto take = [&](size_t b) {
-    const size_t o = off;
-    off += (b + 255) / 256 * 256;
-    return o;
-  };
-  const size_t o_t = take((size_t)nch * H * GC * GC * 2);
-  const size_t o_p = take((size_t)nch * H * GC * GC * 2);
-  const size_t o_e = take((size_t)nch * H * 2 * GC * 4);
-  char* b = (char*)base;
-  w.T = (f16_t*)(b + o_t);
-  w.P = (f16_t*)(b + o_p);
-  w.E = (float*)(b + o_e);
-  w.bytes = off;
-  return w;
-}
-
 size_t gdn_chunk_ws_bytes(int64_t n_seg, int64_t n_rows, int H, int dk) {
   return chunk_ws_layout(nullptr, n_seg, n_rows, H, dk).bytes;
 }
 
-template <int DK, int NW, bool DELTA>
+template <int DK, int NW, bool DELTA, bool SAVE>
 static mom_status launch_chain(const mom_dims& d, int n_seg, const int32_t* seg_off, const int32_t* seg_state,
                                const ChunkWs& W, const int32_t* row_token, const void* q, const void* k,
-                               const void* v, const float* state_in, float* state_out, float* o, hipStream_t st) {
+                               const void* v, const float* state_in, float* state_out, float* o, f16_t* hws,
+                               hipStream_t st) {
   using LY = ChainLds<DK, NW>;
   static bool attr = false;  // the dynamic LDS limit is raised once per kernel
   if (!attr) {
-    if (hipFuncSetAttribute((const void*)k_gdn_chain<DK, NW, DELTA>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    if (hipFuncSetAttribute((const void*)k_gdn_chain<DK, NW, DELTA, SAVE>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)LY::BYTES) != hipSuccess)
       return MOM_ERR_LAUNCH;
     attr = true;
   }
   const int64_t blocks = (int64_t)n_seg * d.H * (d.dv / LY::DVB);
   if (blocks > 0)
-    hipLaunchKernelGGL((k_gdn_chain<DK, NW, DELTA>), dim3((unsigned)blocks), dim3(64 * NW), LY::BYTES, st, d.H, d.dv,
-                       n_seg, seg_off, seg_state, (const f16_t*)k, (const f16_t*)v, W.T, W.P, W.E,
-                       row_token, (const f16_t*)q, state_in, state_out, o);
+    hipLaunchKernelGGL((k_gdn_chain<DK, NW, DELTA, SAVE>), dim3((unsigned)blocks), dim3(64 * NW), LY::BYTES, st,
+                       d.H, d.dv, n_seg, seg_off, seg_state, (const f16_t*)k, (const f16_t*)v, W.T, W.P, W.E,
+                       row_token, (const f16_t*)q, state_in, state_out, o, hws);
   return MOM_OK;
 }
 
@@ -769,11 +615,14 @@ static mom_status launch_chunk(const mom_dims& d, int n_seg, int n_rows, const i
   const int64_t prep_blocks = (nch * d.H + 3) / 4;  // one wave per (chunk, head)
   if (prep_blocks > 0)
     hipLaunchKernelGGL((k_gdn_prep<DK, DELTA>), dim3((unsigned)prep_blocks), dim3(256), 0, st, d.H, n_seg,
-                       seg_off, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.E);
+                       seg_off, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.E,
+                       nullptr);
   const mom_status r =
       d.dv % 128 == 0
-          ? launch_chain<DK, 4, DELTA>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o, st)
-          : launch_chain<DK, 2, DELTA>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o, st);
+          ? launch_chain<DK, 4, DELTA, false>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in,
+                                              state_out, o, nullptr, st)
+          : launch_chain<DK, 2, DELTA, false>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in,
+                                              state_out, o, nullptr, st);
   if (r != MOM_OK) return r;
   return launch_status();
 }
@@ -793,6 +642,39 @@ mom_status launch_gdn_chunk_mfma(const mom_dims& d, int n_seg, int n_rows, const
                                          state_in, state_out, o, ws, st)
                : launch_chunk<128, false>(d, n_seg, n_rows, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
                                           state_in, state_out, o, ws, st);
+}
+
+
+// For the gradients: prep (with X = (I + A)^{-1} in float32 for Gated DeltaNet)
+// and the state walk that stores the state entering every chunk (transposed,
+// half) in hws, without the read-out.
+template <int DK, bool DELTA>
+static mom_status launch_states(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
+                                const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
+                                const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
+                                const ChunkWs& W, float* Xws, f16_t* hws, hipStream_t st) {
+  const int64_t nch = (int64_t)n_rows / GC + n_seg;
+  const int64_t prep_blocks = (nch * d.H + 3) / 4;
+  if (prep_blocks > 0)
+    hipLaunchKernelGGL((k_gdn_prep<DK, DELTA>), dim3((unsigned)prep_blocks), dim3(256), 0, st, d.H, n_seg,
+                       seg_off, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.E,
+                       DELTA ? Xws : nullptr);
+  return d.dv % 128 == 0 ? launch_chain<DK, 4, DELTA, true>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v,
+                                                             state_in, nullptr, nullptr, hws, st)
+                         : launch_chain<DK, 2, DELTA, true>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v,
+                                                             state_in, nullptr, nullptr, hws, st);
+}
+
+mom_status launch_chunk_states(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
+                               const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
+                               const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
+                               const ChunkWs& W, float* Xws, f16_t* hws, bool delta, hipStream_t st) {
+#define MOM_STATES(DK, DELTA) \
+  launch_states<DK, DELTA>(d, n_seg, n_rows, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p, state_in, W, \
+                           Xws, hws, st)
+  if (d.dk == 64) return delta ? MOM_STATES(64, true) : MOM_STATES(64, false);
+  return delta ? MOM_STATES(128, true) : MOM_STATES(128, false);
+#undef MOM_STATES
 }
 
 }  // namespace mom

@@ -54,6 +54,9 @@ def lib():
                           _VP, ctypes.c_size_t, _VP],
         "gla_chunk_fwd": [D, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                           _VP, ctypes.c_size_t, _VP],
+        "gdn_chunk_bwd": [D, _I32, _I32, _I32, _I32] + [_VP] * 18 + [ctypes.c_size_t, _VP],
+        "gla_chunk_bwd": [D, _I32, _I32, _I32, _I32] + [_VP] * 18 + [ctypes.c_size_t, _VP],
+        "gdn_chunk_bwd_workspace_bytes": [D, _I32, _I32],
         "gdn_decode_step": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
         "gla_decode_step": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
         "mom_combine": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP],
@@ -67,13 +70,15 @@ def lib():
         f.restype = _I32
     L.mom_workspace_bytes.restype = ctypes.c_size_t
     L.gdn_chunk_workspace_bytes.restype = ctypes.c_size_t
+    L.gdn_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.mom_status_string.restype = ctypes.c_char_p
     _lib = L
     return L
 
 
-EXPORTS = ("mom_route", "mom_dispatch", "mom_project", "gdn_chunk_fwd", "gla_chunk_fwd", "gdn_decode_step",
-           "gla_decode_step", "mom_combine", "mom_workspace_bytes", "gdn_chunk_workspace_bytes", "mom_status_string")
+EXPORTS = ("mom_route", "mom_dispatch", "mom_project", "gdn_chunk_fwd", "gla_chunk_fwd", "gdn_chunk_bwd",
+           "gla_chunk_bwd", "gdn_decode_step", "gla_decode_step", "mom_combine", "mom_workspace_bytes",
+           "gdn_chunk_workspace_bytes", "gdn_chunk_bwd_workspace_bytes", "mom_status_string")
 
 
 def dims_of(cfg: LayerConfig, B: int | None = None, T: int | None = None) -> MomDims:
@@ -132,6 +137,33 @@ def gla_chunk_fwd(dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_t
     _check(lib().gla_chunk_fwd(ctypes.byref(dims), n_seg, n_rows, n_tok, n_state, _p(seg_off), _p(seg_state),
                                _p(row_token), _p(q), _p(k), _p(v), _p(alpha_p), _p(beta_p), _p(state_in),
                                _p(state_out), _p(o), _p(ws), nbytes, _s(stream)), "gla_chunk_fwd")
+
+
+def _chunk_bwd(name, dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
+               state_in, d_o, dstate_out, dq, dk, dv, d_alpha, d_beta, dstate_in, ws, stream):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(getattr(lib(), name)(ctypes.byref(dims), n_seg, n_rows, n_tok, n_state, _p(seg_off), _p(seg_state),
+                                _p(row_token), _p(q), _p(k), _p(v), _p(alpha_p), _p(beta_p), _p(state_in), _p(d_o),
+                                _p(dstate_out), _p(dq), _p(dk), _p(dv), _p(d_alpha), _p(d_beta), _p(dstate_in),
+                                _p(ws), nbytes, _s(stream)), name)
+
+
+def gdn_chunk_bwd(dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
+                  state_in, d_o, dstate_out, dq, dk, dv, d_alpha, d_beta, dstate_in, ws, stream=None):
+    """Gradients of gdn_chunk_fwd: dq (per row), dk, dv, d_alpha, d_beta, dstate_in."""
+    _chunk_bwd("gdn_chunk_bwd", dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v,
+               alpha_p, beta_p, state_in, d_o, dstate_out, dq, dk, dv, d_alpha, d_beta, dstate_in, ws, stream)
+
+
+def gla_chunk_bwd(dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
+                  state_in, d_o, dstate_out, dq, dk, dv, d_alpha, d_beta, dstate_in, ws, stream=None):
+    """Gradients of gla_chunk_fwd (same arguments as gdn_chunk_bwd)."""
+    _chunk_bwd("gla_chunk_bwd", dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v,
+               alpha_p, beta_p, state_in, d_o, dstate_out, dq, dk, dv, d_alpha, d_beta, dstate_in, ws, stream)
+
+
+def gdn_chunk_bwd_workspace_bytes(dims, n_seg, n_rows):
+    return int(lib().gdn_chunk_bwd_workspace_bytes(ctypes.byref(dims), n_seg, n_rows))
 
 
 def gdn_decode_step(dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, stream=None):
@@ -241,6 +273,31 @@ class MomLayer:
               b["q"], b["k"], b["v"], b["alpha_p"], b["beta_p"], state_in, state_out, b["o"], b["ws_chunk"], stream)
         mom_combine(b["dims"], b["NT"], b["inv"], b["w"], b["o"], b["o"][b["NR"]:], b["out"], stream)
         return b["out"], state_out, b
+
+    def chunk_backward(self, b, d_o, dstate_out=None, state_in=None, stream=None):
+        """Gradients of the memories' recurrence over the segments of the last
+        forward with buffers b: d_o [N, H, dv] fp32 = dL/do per packed row,
+        dstate_out [B, M+1, H, dk, dv] fp32 or None (zeros), state_in as given to
+        forward.  Returns a dict of dq [N, H, dk] (per row), dk, dv, d_alpha,
+        d_beta [N, H] and dstate_in, all fp32 (buffers reused per shape)."""
+        c = self.cfg
+        if "grad" not in b:
+            dev, f32 = self.device, torch.float32
+            N, H = b["N"], c.H
+            nbytes = gdn_chunk_bwd_workspace_bytes(b["dims"], b["n_seg"], N)
+            b["grad"] = dict(dq=torch.empty(N, H, c.dk, dtype=f32, device=dev),
+                             dk=torch.empty(N, H, c.dk, dtype=f32, device=dev),
+                             dv=torch.empty(N, H, c.dv, dtype=f32, device=dev),
+                             d_alpha=torch.empty(N, H, dtype=f32, device=dev),
+                             d_beta=torch.empty(N, H, dtype=f32, device=dev),
+                             dstate_in=torch.empty(b["n_seg"], H, c.dk, c.dv, dtype=f32, device=dev),
+                             ws=torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev))
+        g = b["grad"]
+        fn = gdn_chunk_bwd if self.rule == "gdn" else gla_chunk_bwd
+        fn(b["dims"], b["n_seg"], b["N"], b["NT"], b["n_seg"], b["seg_off"], b["seg_state"], b["perm"], b["q"],
+           b["k"], b["v"], b["alpha_p"], b["beta_p"], state_in, d_o, dstate_out, g["dq"], g["dk"], g["dv"],
+           g["d_alpha"], g["d_beta"], g["dstate_in"], g["ws"], stream)
+        return g
 
     def decode_step(self, x_t, alpha, beta, states, stream=None):
         """One token for each of n_seq sequences: x_t [n_seq, D], alpha/beta

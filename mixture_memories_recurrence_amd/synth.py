@@ -148,6 +148,15 @@ def make_chain_inputs(n_rows: int, H: int, dk: int, dv: int, seed: int, store: s
                 v=v.astype(cast).astype(np.float32), alpha=alpha, beta=beta)
 
 
+def make_chain_grads(n_rows: int, H: int, dk: int, dv: int, n_state: int, seed: int) -> dict:
+    """Upstream gradients for the recurrence's backward pass: d_o = dL/do [n_rows][H][dv]
+    and dstate = dL/d(final state) [n_state][H][dk][dv], both N(0,1) float32 (the
+    gradient of a loss that sums random projections of the outputs and states)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    return dict(d_o=g.standard_normal((n_rows, H, dv)).astype(np.float32),
+                dstate=g.standard_normal((n_state, H, dk, dv)).astype(np.float32))
+
+
 def make_single_memory_inputs(B: int, T: int, H: int, dk: int, dv: int, seed: int) -> dict:
     """Inputs of one plain Gated DeltaNet memory over B sequences of T tokens
     (rows in token order): q ~ N(0,1), keys normalised per head, values ~

@@ -123,3 +123,30 @@ def test_chunk_workspace_sizes():
                            FAKE, FAKE, None, FAKE, FAKE, None, 0, None) == -5
     d32 = _dims(dtype=0)
     assert L.gdn_chunk_workspace_bytes(ctypes.byref(d32), n_seg, n_rows) == 0
+
+
+@needs_lib
+def test_chunk_bwd_checks():
+    """The gradient entry points: workspace size (forward factors, X, and two
+    half states per chunk and head), half storage only, and the usual refusals."""
+    L = mom.lib()
+    d = _dims()
+    n_seg, n_rows = (d.M + 1) * d.B, d.B * d.T * (d.topk + 1)
+    need = L.gdn_chunk_bwd_workspace_bytes(ctypes.byref(d), n_seg, n_rows)
+    n_chunks = n_rows // 64 + n_seg
+    per = 64 * 64 * 2 * 2 + 64 * 4 * 2 + 64 * 64 * 4 + 2 * d.dk * d.dv * 2
+    assert need >= n_chunks * d.H * per and need % 256 == 0
+    assert need > L.gdn_chunk_workspace_bytes(ctypes.byref(d), n_seg, n_rows)
+    args = [FAKE] * 5 + [None, FAKE, None] + [FAKE] * 6  # q..beta, state_in, d_o, dstate_out, outputs
+    for f in (L.gdn_chunk_bwd, L.gla_chunk_bwd):
+        # no workspace, a short one, a missing output, float32 storage
+        assert f(ctypes.byref(d), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, *args, None, 0, None) == -5
+        assert f(ctypes.byref(d), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, *args, FAKE, need - 1,
+                 None) == -5
+        bad = list(args)
+        bad[8] = None  # dq
+        assert f(ctypes.byref(d), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, *bad, FAKE, need, None) == -1
+        d32 = _dims(dtype=0)
+        assert f(ctypes.byref(d32), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, *args, FAKE, need,
+                 None) == -3
+    assert L.gdn_chunk_bwd_workspace_bytes(ctypes.byref(_dims(dtype=0)), n_seg, n_rows) == 0

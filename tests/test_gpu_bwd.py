@@ -1,0 +1,130 @@
+"""GPU parity of the recurrence's gradients (gdn_chunk_bwd, gla_chunk_bwd)
+against the fp64 checker's reverse sweep (oracle.segments_bwd), element by
+element, through the C ABI.
+
+Tolerance: each gradient tensor has rel-L2 <= 5e-3 (the layer's bound) and
+max-abs <= 5e-3 * max|reference|.  Gradients scale with the upstream gradient
+(here N(0,1) per output element) and reach magnitudes in the hundreds, so the
+layer's absolute 2e-2 is stated relative to the tensor's largest value; the
+operands are rounded to half (unit roundoff 2^-11 = 4.9e-4) and products
+accumulate in float32, and the measured errors sit near one unit roundoff."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+from mixture_memories_recurrence_amd import mom, synth  # noqa: E402
+from oracle import oracle  # noqa: E402
+from parity import errors, log, to_gpu  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+GRAD_REL = 5e-3
+SEG_LENGTHS = [0, 1, 63, 64, 65, 130, 200, 7, 128, 0, 300]
+
+
+def assert_grad(name, got, ref):
+    ma, rl = errors(got, ref)
+    bound = GRAD_REL * max(float(np.max(np.abs(ref))), 1e-30)
+    log("  %-10s max-abs %.3e (<= %.2e)  rel-L2 %.3e (<= %.1e)" % (name, ma, bound, rl, GRAD_REL))
+    assert ma <= bound and rl <= GRAD_REL, "%s: max-abs %.3e rel-L2 %.3e" % (name, ma, rl)
+
+
+def nan(*shape):
+    return torch.full(shape, float("nan"), device="cuda")
+
+
+def run_bwd_segments(rule, dk, dv, with_state, with_dstate, shared_tokens, H=2, seed=0):
+    lens = np.array(SEG_LENGTHS)
+    seg_off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N, n_seg = int(seg_off[-1]), len(lens)
+    ch = synth.make_chain_inputs(N, H, dk, dv, seed=dk + dv + seed, store="f16")
+    rng = np.random.default_rng(seed + 1)
+    n_tok = N // 3 if shared_tokens else N + 5
+    row_token = (rng.integers(0, n_tok, N) if shared_tokens else rng.permutation(n_tok)[:N]).astype(np.int32)
+    qtok = synth.make_chain_inputs(n_tok, H, dk, dv, seed=seed + 7, store="f16")["q"]
+    n_state = n_seg + 3
+    seg_state = rng.permutation(n_state)[:n_seg].astype(np.int32)
+    S0 = (rng.standard_normal((n_state, H, dk, dv)) * 0.1).astype(np.float32)
+    gr = synth.make_chain_grads(N, H, dk, dv, n_state, seed=seed + 4)
+    dims = mom.dims_of(synth.LayerConfig(1, 1, 64, H, dk, dv, 1, 1, "bf16"))
+    out = dict(dq=nan(N, H, dk), dk=nan(N, H, dk), dv=nan(N, H, dv), da=nan(N, H), dc=nan(N, H),
+               ds0=nan(n_state, H, dk, dv))
+    ws = torch.empty(mom.gdn_chunk_bwd_workspace_bytes(dims, n_seg, N), dtype=torch.uint8, device="cuda")
+    f16 = torch.float16
+    fn = mom.gla_chunk_bwd if rule == "gla" else mom.gdn_chunk_bwd
+    args = (dims, n_seg, N, n_tok, n_state, to_gpu(seg_off), to_gpu(seg_state), to_gpu(row_token), to_gpu(qtok, f16),
+            to_gpu(ch["k"], f16), to_gpu(ch["v"], f16), to_gpu(ch["alpha"]), to_gpu(ch["beta"]),
+            to_gpu(S0) if with_state else None, to_gpu(gr["d_o"]), to_gpu(gr["dstate"]) if with_dstate else None)
+    fn(*args, out["dq"], out["dk"], out["dv"], out["da"], out["dc"], out["ds0"], ws)
+    torch.cuda.synchronize()
+    ref = oracle.segments_bwd(seg_off, seg_state, row_token, qtok, ch["k"], ch["v"], ch["alpha"], ch["beta"],
+                              S0 if with_state else None, gr["d_o"], gr["dstate"] if with_dstate else None,
+                              n_state=n_state, rule=rule)
+    return dict(lens=lens, seg_state=seg_state, n_state=n_state, out={k: v.cpu().numpy() for k, v in out.items()},
+                ref=ref, dstate=gr["dstate"] if with_dstate else np.zeros_like(S0), args=args, fn=fn, ws=ws)
+
+
+@pytest.mark.parametrize("rule,dk,dv,with_state,with_dstate,shared_tokens", [
+    ("gdn", 128, 256, True, True, False), ("gdn", 128, 256, False, False, True), ("gdn", 64, 64, True, True, True),
+    ("gdn", 128, 128, True, False, False), ("gdn", 64, 256, False, True, False), ("gla", 128, 256, True, True, True),
+    ("gla", 64, 128, False, True, False)])
+def test_chunk_bwd_segments(rule, dk, dv, with_state, with_dstate, shared_tokens):
+    """Ragged packed segments (empty, one row, chunk +- 1, several chunks), with
+    and without entering states and final-state gradients, queries gathered by
+    token (some tokens read by several rows)."""
+    log("chunk_bwd", rule, dk, dv, "state" if with_state else "-", "dstate" if with_dstate else "-",
+        "shared" if shared_tokens else "")
+    r = run_bwd_segments(rule, dk, dv, with_state, with_dstate, shared_tokens)
+    got, ref, ss = r["out"], r["ref"], r["seg_state"]
+    for name, rn in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("d_alpha", "da"), ("d_beta", "dc")):
+        assert_grad(name, got[rn], ref[rn])
+    assert_grad("dstate_in", got["ds0"][ss], ref["dstate0"][ss])
+    # empty segments pass dstate_out through bit for bit; slots not used stay untouched
+    for s in np.nonzero(r["lens"] == 0)[0]:
+        assert np.array_equal(got["ds0"][ss[s]], r["dstate"][ss[s]])
+    unused = sorted(set(range(r["n_state"])) - set(ss.tolist()))
+    assert np.all(np.isnan(got["ds0"][unused]))
+
+
+def test_chunk_bwd_deterministic():
+    """Identical inputs give bit-identical gradients."""
+    r = run_bwd_segments("gdn", 128, 256, True, True, True)
+    out = dict(dq=nan(*r["out"]["dq"].shape), dk=nan(*r["out"]["dk"].shape), dv=nan(*r["out"]["dv"].shape),
+               da=nan(*r["out"]["da"].shape), dc=nan(*r["out"]["dc"].shape), ds0=nan(*r["out"]["ds0"].shape))
+    r["fn"](*r["args"], out["dq"], out["dk"], out["dv"], out["da"], out["dc"], out["ds0"], r["ws"])
+    torch.cuda.synchronize()
+    for k, v in out.items():
+        assert np.array_equal(v.cpu().numpy(), r["out"][k], equal_nan=True), k
+
+
+@pytest.mark.parametrize("rule", ["gdn", "gla"])
+def test_chunk_bwd_layer_full_size_sampled(rule):
+    """The 380M layer's shape (8 x 2048 tokens, 4 memories, top-2, shared
+    memory): route, dispatch and projections on the GPU give the segments and
+    q/k/v; the gradients of every segment run in one call (the benchmark's
+    launch), and two segments (a routed one and a 2048-row shared one, all
+    heads) are checked against the checker."""
+    cfg = synth.CONFIGS["l380m"]
+    inp = synth.make_layer_inputs(cfg, seed=5)
+    layer = mom.MomLayer(cfg, inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"], rule=rule)
+    x = torch.from_numpy(inp["x"]).to(torch.bfloat16).cuda()
+    log("chunk_bwd full size", rule)
+    _, _, b = layer.forward(x, torch.from_numpy(inp["alpha"]).cuda(), torch.from_numpy(inp["beta"]).cuda())
+    n_state = b["n_seg"]
+    gr = synth.make_chain_grads(b["N"], cfg.H, cfg.dk, cfg.dv, n_state, seed=9)
+    g = layer.chunk_backward(b, to_gpu(gr["d_o"]), to_gpu(gr["dstate"]))
+    torch.cuda.synchronize()
+    seg_off = b["seg_off"].cpu().numpy()
+    seg_state = b["seg_state"].cpu().numpy()
+    perm = b["perm"].cpu().numpy()
+    pick = [1, b["n_seg"] - 1]  # memory 0 of sequence 1; the shared memory of the last sequence
+    rows = np.concatenate([np.arange(seg_off[s], seg_off[s + 1]) for s in pick])
+    sub_off = np.concatenate([[0], np.cumsum([seg_off[s + 1] - seg_off[s] for s in pick])]).astype(np.int32)
+    f = lambda t: t.float().cpu().numpy()
+    q, k, v = f(b["q"]), f(b["k"])[rows], f(b["v"])[rows]
+    ap, bp = f(b["alpha_p"])[rows], f(b["beta_p"])[rows]
+    ref = oracle.segments_bwd(sub_off, np.arange(len(pick), dtype=np.int32), perm[rows], q, k, v, ap, bp, None,
+                              gr["d_o"][rows], gr["dstate"][seg_state[pick]], rule=rule)
+    for name, rn in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("d_alpha", "da"), ("d_beta", "dc")):
+        assert_grad(name, f(g[name])[rows], ref[rn])
+    assert_grad("dstate_in", f(g["dstate_in"])[seg_state[pick]], ref["dstate0"])
