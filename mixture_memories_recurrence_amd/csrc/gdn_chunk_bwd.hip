@@ -39,7 +39,7 @@ namespace mom {
 mom_status launch_chunk_states(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
                                const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
                                const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
-                               const ChunkWs& W, float* Xws, f16_t* hws, bool delta, hipStream_t st);
+                               const ChunkWs& W, f16_t* Xws, f16_t* hws, bool delta, hipStream_t st);
 
 // ------------------------------------------------------------------ reverse chain
 // One block per (segment, head, DVB = 32 NW value columns), NW waves, mapped to
@@ -311,33 +311,35 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain_bwd(
 // ------------------------------------------------------------------ per-chunk gradients
 // One block of 8 waves per (chunk, head).  The value columns are taken 64 at a
 // time (a slice); per slice, with S^T and dS'^T of the slice (from the walks),
-// V and dO of the slice, and K, T, P of the chunk in LDS:
-//   stage 1  waves 0-3: Y = K S (tile t = w) and R = V - diag(gm) Y to LDS
-//            waves 4-7: Z = K dS', dU = P^T dO + diag(ek) Z to LDS
-//   stage 2  waves 0-3: dR = T^T dU; dV = dR out; -diag(gm) dR to LDS;
+// V and dO of the slice, and K, T, P of the chunk in LDS (products of two
+// transposed factors give the transposed tiles, so that a lane holds one chunk
+// row and 4 consecutive columns and writes 8-byte row pieces):
+//   stage 1  waves 0-3: Y^T = S^T K^T (tile t = w), R = V - diag(gm) Y to LDS
+//            waves 4-7: Z^T = dS'^T K^T, dU = P^T dO + diag(ek) Z to LDS
+//   stage 2  waves 0-3: dR^T = dU^T T; dV = dR out; -diag(gm) dR to LDS;
 //                       row sums of dR o Y (= k_i.PR_i) kept per lane
-//            waves 4-7: U = T R; U and diag(ek) U to LDS; row sums of U o Z
+//            waves 4-7: U^T = R^T T^T; U and diag(ek) U to LDS; row sums of U o Z
 //   stage 3  every wave: its tile of PQ += dO S^T and of
 //            PK' += diag(ek) U dS'^T - diag(gm) dR S^T  (64 x DK), and of
 //            dT += dU R^T (waves 0-3) or dP += dO U^T (waves 4-7)  (64 x 64)
 // The next slice's inputs are loaded into registers during the current one.
-// Then, in float32 through LDS: dc, dA = -X^T (dT diag(c)) X^T, the products
-// K K^T and Q K^T again (matrix cores), B, D, G and the row and column sums for
-// dg; then dQ and dK on the matrix cores, and da from the reverse prefix sum
-// of dg.  Tiles with k along their rows are read with row_frag, with k down
-// their rows with col_frag (all swizzled as in the walks).
-constexpr int GRAD_FLD = GC + 1;
-typedef _Float16 h4v __attribute__((ext_vector_type(4)));  // float row stride of the 64 x 64 float32 tiles
+// Then, all products on the matrix cores and every row / column sum taken in
+// registers by the wave that holds the tile:
+//   waves 0-3  dc's share sum_r dT_ri X_ri; (dT diag(c)) to LDS; then
+//              X^T (dT diag(c)); then dA = -(that) X^T and K K^T, giving G, B
+//   waves 4-7  D = dP o e^{g_i - g_j}, then Q K^T and the sums of D o QK
+// and finally dQ, dK (matrix cores), dg and da (reverse prefix sum).
+typedef _Float16 h4v __attribute__((ext_vector_type(4)));
 
 template <int DK>
 struct GradLds {
   // bytes; the slice phase and the final phase share the region after K
-  static constexpr int KT = GC * DK * 2, HT = GC * GC * 2, FT = GC * GRAD_FLD * 4;
+  static constexpr int KT = GC * DK * 2, HT = GC * GC * 2;
   static constexpr int OFF_K = 0, OFF_T = KT, OFF_P = OFF_T + HT, OFF_ST = OFF_P + HT, OFF_DST = OFF_ST + KT,
                        OFF_V = OFF_DST + KT, OFF_DO = OFF_V + HT, OFF_R = OFF_DO + HT, OFF_DU = OFF_R + HT,
                        OFF_U = OFF_DU + HT, OFF_EU = OFF_U + HT, OFF_GR = OFF_EU + HT, END1 = OFF_GR + HT;
-  static constexpr int OFF_FDT = KT, OFF_FDP = OFF_FDT + FT, OFF_FX = OFF_FDP + FT, OFF_FG = OFF_FX + FT,
-                       OFF_Q = OFF_FG + FT, OFF_DM = OFF_Q + KT, OFF_BS = OFF_DM + HT, END2 = OFF_BS + HT;
+  static constexpr int OFF_Q = KT, OFF_X = OFF_Q + KT, OFF_DTC = OFF_X + HT, OFF_XTD = OFF_DTC + HT,
+                       OFF_DM = OFF_XTD + HT, OFF_BS = OFF_DM + HT, END2 = OFF_BS + HT;
   static constexpr size_t BYTES = END1 > END2 ? END1 : END2;
 };
 
@@ -349,21 +351,41 @@ template <int RH>
 __device__ __forceinline__ int tile_elem(int r, int col) {
   return r * RH + 8 * swz<RH>(r, col >> 3) + (col & 7);
 }
+// Cross-lane sums: DPP within rows of 16 lanes (quad swaps, then the 8- and
+// 16-lane mirrors), then one lane exchange between the rows.  (The swap
+// instructions that exchange rows are not used here: the compiler takes both
+// of their results to be equal when they are added.)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// sum over the 32 lanes of this lane's half wave, in every lane
+__device__ __forceinline__ float half_wave_sum(float x) {
+  x += dpp_f<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_f<0x141>(x);  // row_half_mirror
+  x += dpp_f<0x140>(x);  // row_mirror
+  return x + __shfl_xor(x, 16, 64);
+}
+// x(lane) + x(lane ^ 32)
+__device__ __forceinline__ float halves_sum(float x) { return x + __shfl_xor(x, 32, 64); }
 
 template <int DK, bool DELTA>
 __global__ __launch_bounds__(512) void k_gdn_grad(
     int H, int dv, int n_seg, const int32_t* __restrict__ seg_off, const int32_t* __restrict__ row_token,
     const f16_t* __restrict__ q, const f16_t* __restrict__ k, const f16_t* __restrict__ v,
     const float* __restrict__ alpha_p, const float* __restrict__ beta_p, const f16_t* __restrict__ Tws,
-    const f16_t* __restrict__ Pws, const float* __restrict__ Xws, const f16_t* __restrict__ hws,
+    const f16_t* __restrict__ Pws, const f16_t* __restrict__ Xws, const f16_t* __restrict__ hws,
     const f16_t* __restrict__ dhws, const float* __restrict__ d_o, float* __restrict__ dq, float* __restrict__ dk,
     float* __restrict__ dvo, float* __restrict__ da, float* __restrict__ dc) {
   using LY = GradLds<DK>;
   constexpr int NKD = DK / 16, NDT = DK / 32;  // k-steps over DK, 32-column tiles of DK
-  constexpr int NS = DK / 64;                  // 16-byte pieces of S^T per thread and slice
+  constexpr int NS = DK / 64;                  // 16-byte pieces of S^T (or Q) per thread and slice
   extern __shared__ __attribute__((aligned(16))) char gsm[];
   __shared__ float g_s[GC], gm_s[GC], ek_s[GC], c_s[GC], a_s[GC];
-  __shared__ float rdy_s[2][GC], ruz_s[2][GC], rpq_s[NDT][GC], red_s[16];
+  // per-row (or per-column) partial sums, [32-wide tile][row or column]
+  __shared__ float rdy_s[2][GC], ruz_s[2][GC], rpq_s[NDT][GC], red_s[8];
+  __shared__ float dct_s[2][GC], rsg_s[2][GC], csg_s[2][GC], rse_s[2][GC], cse_s[2][GC];
   f16_t* Kt = reinterpret_cast<f16_t*>(gsm + LY::OFF_K);
   f16_t* Tt = reinterpret_cast<f16_t*>(gsm + LY::OFF_T);
   f16_t* Pt = reinterpret_cast<f16_t*>(gsm + LY::OFF_P);
@@ -387,6 +409,21 @@ __global__ __launch_bounds__(512) void k_gdn_grad(
   const int64_t r0 = seg_off[seg] + (int64_t)(c - cb0) * GC;
   const int L = (int)min((int64_t)GC, (int64_t)seg_off[seg + 1] - r0);
 
+  // Q (gathered by token; zero past L) and X of the chunk, needed only at the
+  // end, are loaded first and kept in registers.
+  h8v rq[NS], rx;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int p = tid + 512 * j, r = p / (DK / 8), cc = p % (DK / 8);
+    const h8v z = {};
+    rq[j] = z;
+    if (r < L) {
+      const int64_t tk = row_token ? (int64_t)row_token[r0 + r] : r0 + r;
+      rq[j] = *reinterpret_cast<const h8v*>(q + (tk * H + h) * DK + 8 * cc);
+    }
+  }
+  const int vr = tid >> 3, vc = tid & 7;  // a 64 x 64 half tile: row, 8-column piece of this thread
+  if constexpr (DELTA) rx = *reinterpret_cast<const h8v*>(Xws + (ch * GC + vr) * GC + 8 * vc);
   // gates (as the prep kernel computes them): g prefix of log a (0 past L)
   if (w == 0) {
     float g = 0.f, aa = 1.f, bb = 0.f;
@@ -414,11 +451,8 @@ __global__ __launch_bounds__(512) void k_gdn_grad(
     if (r < L) val = *reinterpret_cast<const h8v*>(k + ((r0 + r) * H + h) * DK + 8 * cc);
     *reinterpret_cast<h8v*>(tile_piece<DK>(Kt, r, cc)) = val;
   }
-  for (int p = tid; p < GC * GC / 8; p += 512) {
-    const int r = p / 8, cc = p % 8;
-    *reinterpret_cast<h8v*>(tile_piece<GC>(Tt, r, cc)) = *reinterpret_cast<const h8v*>(Tws + (ch * GC + r) * GC + 8 * cc);
-    *reinterpret_cast<h8v*>(tile_piece<GC>(Pt, r, cc)) = *reinterpret_cast<const h8v*>(Pws + (ch * GC + r) * GC + 8 * cc);
-  }
+  *reinterpret_cast<h8v*>(tile_piece<GC>(Tt, vr, vc)) = *reinterpret_cast<const h8v*>(Tws + (ch * GC + vr) * GC + 8 * vc);
+  *reinterpret_cast<h8v*>(tile_piece<GC>(Pt, vr, vc)) = *reinterpret_cast<const h8v*>(Pws + (ch * GC + vr) * GC + 8 * vc);
 
   // slice inputs in registers: S^T and dS'^T pieces (rows = value columns),
   // one V piece, one dO piece (8 floats)
@@ -426,7 +460,6 @@ __global__ __launch_bounds__(512) void k_gdn_grad(
   const f16_t* dhc = dhws + ch * (int64_t)dv * DK;
   h8v rs[NS], rds[NS], rv;
   float4 ro0, ro1;
-  const int vr = tid >> 3, vc = tid & 7;  // V / dO piece: row, 8-column piece
   auto load_slice = [&](int cs) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
@@ -589,163 +622,139 @@ __global__ __launch_bounds__(512) void k_gdn_grad(
   __syncthreads();  // the slice buffers are free: the final phase reuses them
 
   // ---- final phase
-  float* fdT = reinterpret_cast<float*>(gsm + LY::OFF_FDT);  // dT, then dA
-  float* fdP = reinterpret_cast<float*>(gsm + LY::OFF_FDP);  // dP, then D o (Q K^T)
-  float* fX = reinterpret_cast<float*>(gsm + LY::OFF_FX);
-  float* fG = reinterpret_cast<float*>(gsm + LY::OFF_FG);    // X^T dT diag(c), then G
   f16_t* Qt = reinterpret_cast<f16_t*>(gsm + LY::OFF_Q);
+  f16_t* Xt = reinterpret_cast<f16_t*>(gsm + LY::OFF_X);
+  f16_t* dTc = reinterpret_cast<f16_t*>(gsm + LY::OFF_DTC);  // dT diag(c)
+  f16_t* XtD = reinterpret_cast<f16_t*>(gsm + LY::OFF_XTD);  // X^T dT diag(c)
   f16_t* Dm = reinterpret_cast<f16_t*>(gsm + LY::OFF_DM);
   f16_t* Bs = reinterpret_cast<f16_t*>(gsm + LY::OFF_BS);
-  // row sums of dR o Y / U o Z over this wave's 32 columns (two lane halves)
-  {
-    const float x = prow + __shfl_xor(prow, 32, 64);
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int p = tid + 512 * j, r = p / (DK / 8), cc = p % (DK / 8);
+    *reinterpret_cast<h8v*>(tile_piece<DK>(Qt, r, cc)) = rq[j];
+  }
+  if constexpr (DELTA) *reinterpret_cast<h8v*>(tile_piece<GC>(Xt, vr, vc)) = rx;
+  {  // row sums of dR o Y / U o Z over this wave's 32 columns (two lane halves)
+    const float x = halves_sum(prow);
     if (g2 == 0) (w < 4 ? rdy_s : ruz_s)[ct][32 * bt + c32] = x;
   }
-  // dT (lower, incl. diagonal) and dP to LDS
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = rowof(bt, i), j = 32 * ct + c32;
-    (w < 4 ? fdT : fdP)[r * GRAD_FLD + j] = j <= r ? DTP[i] : 0.f;
-  }
-  // X (Gated DeltaNet), Q (gathered by token; zero past L)
-  if constexpr (DELTA) {
-    for (int p = tid; p < GC * GC / 4; p += 512) {
-      const int r = p / 16, cc = p % 16;
-      const float4 x4 = *reinterpret_cast<const float4*>(Xws + (ch * GC + r) * GC + 4 * cc);
-      float* d = fX + r * GRAD_FLD + 4 * cc;
-      d[0] = x4.x;
-      d[1] = x4.y;
-      d[2] = x4.z;
-      d[3] = x4.w;
-    }
-  }
-  for (int p = tid; p < GC * DK / 8; p += 512) {
-    const int r = p / (DK / 8), cc = p % (DK / 8);
-    h8v val = {};
-    if (r < L) {
-      const int64_t tk = row_token ? (int64_t)row_token[r0 + r] : r0 + r;
-      val = *reinterpret_cast<const h8v*>(q + (tk * H + h) * DK + 8 * cc);
-    }
-    *reinterpret_cast<h8v*>(tile_piece<DK>(Qt, r, cc)) = val;
-  }
   {
-    float x = sds;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
+    const float x = halves_sum(half_wave_sum(sds));
     if (lane == 0) red_s[w] = x;
   }
   __syncthreads();
-  // rows of q_i.PQ_i: this wave's PQ tile against Q
+  // entries (r, j) of this wave's 64 x 64 tile: r = rowof(bt, e), j = 32 ct + c32
+  const int j = 32 * ct + c32;
+  float Dv[16];  // waves 4-7: D = dP o e^{g_r - g_j} (j <= r)
+  if (w < 4) {
+    // dc's share from T: sum_r dT_rj X_rj (X = I for gated linear attention);
+    // dT diag(c) to LDS
+    float x = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = rowof(bt, e);
+      const float t = j <= r ? DTP[e] : 0.f;
+      if constexpr (DELTA) {
+        x = fmaf(t, (float)Xt[tile_elem<GC>(r, j)], x);
+        dTc[tile_elem<GC>(r, j)] = (f16_t)(t * c_s[j]);
+      } else {
+        x += r == j ? t : 0.f;
+      }
+    }
+    x = halves_sum(x);
+    if (g2 == 0) dct_s[bt][j] = x;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = rowof(bt, e);
+      Dv[e] = j <= r ? DTP[e] * __expf(g_s[r] - g_s[j]) : 0.f;
+      Dm[tile_elem<GC>(r, j)] = (f16_t)Dv[e];
+    }
+  }
+  // q_i.PQ_i: this wave's PQ tile against Q
   if (has_pq) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = rowof(bq, i);
-      float x = PQ[i] * (float)Qt[tile_elem<DK>(r, 32 * dq_t + c32)];
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o, 64);
+    for (int e = 0; e < 16; ++e) {
+      const int r = rowof(bq, e);
+      const float x = half_wave_sum(PQ[e] * (float)Qt[tile_elem<DK>(r, 32 * dq_t + c32)]);
       if (c32 == 0) rpq_s[dq_t][r] = x;
     }
   }
-  // dc from T: sum_r dT_ri X_ri (dT_ii for gated linear attention); X^T dT diag(c)
-  float dcr = 0.f;
-  if (tid < GC) {
-    if constexpr (DELTA) {
-#pragma unroll 8
-      for (int r = 0; r < GC; ++r) dcr = fmaf(fdT[r * GRAD_FLD + tid], fX[r * GRAD_FLD + tid], dcr);
-    } else {
-      dcr = fdT[tid * GRAD_FLD + tid];
-    }
-  }
-  if constexpr (DELTA) {
-    const int i = tid >> 3;
+  __syncthreads();
+  f16x16 acc;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int j = (tid & 7) + 8 * m;
-      float x = 0.f;
-#pragma unroll 8
-      for (int r = 0; r < GC; ++r) x = fmaf(fX[r * GRAD_FLD + i], fdT[r * GRAD_FLD + j], x);
-      fG[i * GRAD_FLD + j] = x * c_s[j];
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  if (w < 4) {
+    if constexpr (DELTA) {
+      // X^T (dT diag(c)), tile (bt, ct)
+#pragma unroll
+      for (int kb = 0; kb < GC / 16; ++kb)
+        acc = mfma32(col_frag<GC>(Xt, kb, 32 * bt, lane), col_frag<GC>(dTc, kb, 32 * ct, lane), acc);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) XtD[tile_elem<GC>(rowof(bt, e), j)] = (f16_t)acc[e];
     }
+  } else {
+    // Q K^T, tile (bt, ct); E = D o QK, its row and column sums
+#pragma unroll
+    for (int kb = 0; kb < NKD; ++kb)
+      acc = mfma32(row_frag<DK>(Qt, 32 * bt + c32, kb, g2), row_frag<DK>(Kt, 32 * ct + c32, kb, g2), acc);
+    float cs_ = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float em = Dv[e] * acc[e];
+      cs_ += em;
+      const float rsum = half_wave_sum(em);
+      if (c32 == 0) rse_s[ct][rowof(bt, e)] = rsum;
+    }
+    cs_ = halves_sum(cs_);
+    if (g2 == 0) cse_s[bt][j] = cs_;
   }
   __syncthreads();
-  // dA = -(X^T dT diag(c)) X^T, strictly lower, over dT
-  if constexpr (DELTA) {
-    const int i = tid >> 3;
-    float res[8];
+  if (DELTA && w < 4) {
+    // dA = -(X^T dT diag(c)) X^T (j < r), K K^T; G = dA o e^{g_r - g_j} o KK,
+    // B = dA o c_r e^{g_r - g_j} (both halves of B + B^T)
+    f16x16 dA, kk;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int j = (tid & 7) + 8 * m;
-      float x = 0.f;
-      if (j < i) {
-#pragma unroll 8
-        for (int r = 0; r < GC; ++r) x = fmaf(fG[i * GRAD_FLD + r], fX[j * GRAD_FLD + r], x);
-      }
-      res[m] = -x;
+    for (int e = 0; e < 16; ++e) {
+      dA[e] = 0.f;
+      kk[e] = 0.f;
     }
-    __syncthreads();  // every read of dT and of X^T dT diag(c) is done
 #pragma unroll
-    for (int m = 0; m < 8; ++m) fdT[i * GRAD_FLD + (tid & 7) + 8 * m] = res[m];
-    __syncthreads();
-  }
-  // K K^T (waves 0-3): G = dA o e^{g_i-g_j} o KK, B = dA o c_i e^{g_i-g_j} (both
-  // halves of B + B^T); Q K^T (waves 4-7): D = dP o e^{g_i-g_j} (j <= i), and
-  // D o QK over dP.
-  {
-    f16x16 acc;
+    for (int kb = 0; kb < GC / 16; ++kb)
+      dA = mfma32(row_frag<GC>(XtD, 32 * bt + c32, kb, g2), row_frag<GC>(Xt, j, kb, g2), dA);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    if (w >= 4 || DELTA) {
-      const f16_t* Ar = w < 4 ? Kt : Qt;
+    for (int kb = 0; kb < NKD; ++kb)
+      kk = mfma32(row_frag<DK>(Kt, 32 * bt + c32, kb, g2), row_frag<DK>(Kt, j, kb, g2), kk);
+    float csg = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < NKD; ++kb)
-        acc = mfma32(row_frag<DK>(Ar, 32 * bt + c32, kb, g2), row_frag<DK>(Kt, 32 * ct + c32, kb, g2), acc);
-    }
-    const int j = 32 * ct + c32;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = rowof(bt, i);
-      const float eg = j <= r ? __expf(g_s[r] - g_s[j]) : 0.f;  // e^{g_i - g_j} may overflow above the diagonal
-      if (w < 4) {
-        if constexpr (DELTA) {
-          const float dA = fdT[r * GRAD_FLD + j];  // zero unless j < r
-          fG[r * GRAD_FLD + j] = dA * eg * acc[i];
-          const f16_t bm = (f16_t)(j < r ? dA * c_s[r] * eg : 0.f);
-          if (j <= r) {
-            Bs[tile_elem<GC>(r, j)] = bm;
-            Bs[tile_elem<GC>(j, r)] = bm;
-          }
-        }
-      } else {
-        const float dm = j <= r ? fdP[r * GRAD_FLD + j] * eg : 0.f;
-        Dm[tile_elem<GC>(r, j)] = (f16_t)dm;
-        fdP[r * GRAD_FLD + j] = dm * acc[i];
+    for (int e = 0; e < 16; ++e) {
+      const int r = rowof(bt, e);
+      const float eg = j < r ? __expf(g_s[r] - g_s[j]) : 0.f;  // e^{g_r - g_j} may overflow above the diagonal
+      const float a_ = -dA[e] * eg;
+      const float gg = a_ * kk[e];
+      csg = fmaf(c_s[r], gg, csg);
+      const float rsum = half_wave_sum(gg);
+      if (c32 == 0) rsg_s[ct][r] = rsum;
+      if (j <= r) {
+        const f16_t bm = (f16_t)(a_ * c_s[r]);
+        Bs[tile_elem<GC>(r, j)] = bm;
+        Bs[tile_elem<GC>(j, r)] = bm;
       }
     }
+    csg = halves_sum(csg);
+    if (g2 == 0) csg_s[bt][j] = csg;
   }
   __syncthreads();
   // dg per row, then d log a by a reverse prefix sum, da and dc out
   if (w == 0) {
     const int i = lane;
-    float dg = 0.f;
+    float dcr = dct_s[0][i] + dct_s[1][i];
+    float dg = rse_s[0][i] + rse_s[1][i] - cse_s[0][i] - cse_s[1][i];
     if constexpr (DELTA) {
-      float rs_ = 0.f, cs_ = 0.f;
-#pragma unroll 8
-      for (int j = 0; j < GC; ++j) {
-        rs_ += fG[i * GRAD_FLD + j];
-        cs_ = fmaf(c_s[j], fG[j * GRAD_FLD + i], cs_);
-      }
-      dcr += rs_;
-      dg += c_s[i] * rs_ - cs_;
+      const float rg = rsg_s[0][i] + rsg_s[1][i];
+      dcr += rg;
+      dg += c_s[i] * rg - csg_s[0][i] - csg_s[1][i];
       dg -= gm_s[i] * (rdy_s[0][i] + rdy_s[1][i]);
-    }
-    {
-      float rs_ = 0.f, cs_ = 0.f;
-#pragma unroll 8
-      for (int j = 0; j < GC; ++j) {
-        rs_ += fdP[i * GRAD_FLD + j];
-        cs_ += fdP[j * GRAD_FLD + i];
-      }
-      dg += rs_ - cs_;
     }
     float pq = 0.f;
 #pragma unroll
@@ -775,14 +784,14 @@ __global__ __launch_bounds__(512) void k_gdn_grad(
   // dQ = diag(gm) PQ + D K and dK = PK' + (B + B^T) K + D^T Q, this wave's tiles
   if (has_pq) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) PQ[i] *= gm_s[rowof(bq, i)];
+    for (int e = 0; e < 16; ++e) PQ[e] *= gm_s[rowof(bq, e)];
 #pragma unroll
     for (int kb = 0; kb < GC / 16; ++kb)
       PQ = mfma32(row_frag<GC>(Dm, 32 * bq + c32, kb, g2), col_frag<DK>(Kt, kb, 32 * dq_t, lane), PQ);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = rowof(bq, i);
-      if (r < L) dq[((r0 + r) * H + h) * DK + 32 * dq_t + c32] = PQ[i];
+    for (int e = 0; e < 16; ++e) {
+      const int r = rowof(bq, e);
+      if (r < L) dq[((r0 + r) * H + h) * DK + 32 * dq_t + c32] = PQ[e];
     }
   }
   if (has_pk) {
@@ -792,20 +801,20 @@ __global__ __launch_bounds__(512) void k_gdn_grad(
       PK = mfma32(col_frag<GC>(Dm, kb, 32 * bq, lane), col_frag<DK>(Qt, kb, 32 * dq_t, lane), PK);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = rowof(bq, i);
-      if (r < L) dk[((r0 + r) * H + h) * DK + 32 * dq_t + c32] = PK[i];
+    for (int e = 0; e < 16; ++e) {
+      const int r = rowof(bq, e);
+      if (r < L) dk[((r0 + r) * H + h) * DK + 32 * dq_t + c32] = PK[e];
     }
   }
 }
 
 // ------------------------------------------------------------------ workspace + launch
-// After the forward workspace (T, P, decays): X (float32 64 x 64), and the
+// After the forward workspace (T, P, decays): X (half 64 x 64), and the
 // transposed states S^T and dS'^T entering / leaving every chunk (half dv x dk),
 // all per (chunk, head).
 struct ChunkBwdWs {
   ChunkWs fw;
-  float* X;
+  f16_t* X;
   f16_t* h;
   f16_t* dh;
   size_t bytes;
@@ -821,11 +830,11 @@ inline ChunkBwdWs chunk_bwd_ws_layout(void* base, int64_t n_seg, int64_t n_rows,
     off += (b + 255) / 256 * 256;
     return o;
   };
-  const size_t o_x = take((size_t)nch * H * GC * GC * 4);
+  const size_t o_x = take((size_t)nch * H * GC * GC * 2);
   const size_t o_h = take((size_t)nch * H * dk * dv * 2);
   const size_t o_dh = take((size_t)nch * H * dk * dv * 2);
   char* b = (char*)base;
-  w.X = (float*)(b + o_x);
+  w.X = (f16_t*)(b + o_x);
   w.h = (f16_t*)(b + o_h);
   w.dh = (f16_t*)(b + o_dh);
   w.bytes = off;

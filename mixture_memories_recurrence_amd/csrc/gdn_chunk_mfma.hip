@@ -341,7 +341,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
 //   A_ij = c_i e^{g_i - g_j} k_i.k_j (j < i) to LDS as float32, P_ij =
 //   e^{g_i - g_j} q_i.k_j (j <= i) to global as half;
 //   X = (I + A)^{-1} by blocked substitution in float32 (below), T = X diag(c)
-//   as half, and X itself as float32 when Xws is given (for the gradients).
+//   as half, and X itself as half when Xws is given (for the gradients).
 // Rows at or past the chunk length L are zero in K, Q, A and P; T is then zero
 // in those rows and columns (c = 0 there).
 constexpr int PREP_ALD = GC + 4;  // float row stride of A in LDS
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
                                                   const f16_t* __restrict__ k, const float* __restrict__ alpha_p,
                                                   const float* __restrict__ beta_p, f16_t* __restrict__ Tws,
                                                   f16_t* __restrict__ Pws, float* __restrict__ Ews,
-                                                  float* __restrict__ Xws) {
+                                                  f16_t* __restrict__ Xws) {
   constexpr int NKD = DK / 16;
   __shared__ __attribute__((aligned(16))) float As_all[4][GC * PREP_ALD];
   __shared__ float gs_all[4][GC];
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
   {
     const int i = lane, ib = i >> 4;
     f16_t* trow = Tws + (ch * GC + i) * GC;
-    float* xrow = Xws ? Xws + (ch * GC + i) * GC : nullptr;
+    f16_t* xrow = Xws ? Xws + (ch * GC + i) * GC : nullptr;
 #pragma unroll
     for (int m = 0; m < GC / 8; ++m) {
       const int jb = m >> 1;
@@ -551,10 +551,7 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
       if (jb > ib) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) hv[e] = (f16_t)0.f;
-        if (xrow) {
-          *reinterpret_cast<float4*>(xrow + 8 * m) = make_float4(0.f, 0.f, 0.f, 0.f);
-          *reinterpret_cast<float4*>(xrow + 8 * m + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+        if (xrow) *reinterpret_cast<half8*>(xrow + 8 * m) = hv;
       } else {
         const float* src = jb == ib ? As + i * PREP_ALD + 8 * m
                                     : As + (16 * jb + (i & 15)) * PREP_ALD + 16 * ib + 8 * (m & 1);
@@ -567,11 +564,10 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
 #pragma unroll
         for (int e = 0; e < 8; ++e) hv[e] = (f16_t)((jb == ib && 8 * m + e > i) ? 0.f : xv[e] * cv[e]);
         if (xrow) {
-          float xz[8];
+          half8 xh;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xz[e] = (jb == ib && 8 * m + e > i) ? 0.f : xv[e];
-          *reinterpret_cast<float4*>(xrow + 8 * m) = make_float4(xz[0], xz[1], xz[2], xz[3]);
-          *reinterpret_cast<float4*>(xrow + 8 * m + 4) = make_float4(xz[4], xz[5], xz[6], xz[7]);
+          for (int e = 0; e < 8; ++e) xh[e] = (f16_t)((jb == ib && 8 * m + e > i) ? 0.f : xv[e]);
+          *reinterpret_cast<half8*>(xrow + 8 * m) = xh;
         }
       }
       *reinterpret_cast<half8*>(trow + 8 * m) = hv;
@@ -652,7 +648,7 @@ template <int DK, bool DELTA>
 static mom_status launch_states(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
                                 const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
                                 const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
-                                const ChunkWs& W, float* Xws, f16_t* hws, hipStream_t st) {
+                                const ChunkWs& W, f16_t* Xws, f16_t* hws, hipStream_t st) {
   const int64_t nch = (int64_t)n_rows / GC + n_seg;
   const int64_t prep_blocks = (nch * d.H + 3) / 4;
   if (prep_blocks > 0)
@@ -668,7 +664,7 @@ static mom_status launch_states(const mom_dims& d, int n_seg, int n_rows, const 
 mom_status launch_chunk_states(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
                                const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
                                const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
-                               const ChunkWs& W, float* Xws, f16_t* hws, bool delta, hipStream_t st) {
+                               const ChunkWs& W, f16_t* Xws, f16_t* hws, bool delta, hipStream_t st) {
 #define MOM_STATES(DK, DELTA) \
   launch_states<DK, DELTA>(d, n_seg, n_rows, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p, state_in, W, \
                            Xws, hws, st)
