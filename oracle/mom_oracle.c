@@ -589,3 +589,95 @@ void oracle_segments_bwd_rule(int rule, int n_seg, const int32_t* seg_off, const
     free(o);
   }
 }
+
+/* ------------------------------------------------------------------------- */
+/* Gradients of the combine, the router and the dispatch gathers (the chain
+ * rule applied to their definitions above).
+ *
+ * Combine, out[t] = o_shared[t] + sum_j w[t][j] o_routed[row(t, j)]:
+ *   d_routed[row(t, j)] = w[t][j] dout[t],   d_shared[t] = dout[t],
+ *   dw[t][j] = <dout[t], o_routed[row(t, j)]>     (sums over H * dv)
+ * row(t, j) = inv[t][j] (NULL: t*K + j).  d_routed rows no token reads are not
+ * written.                                                                    */
+void oracle_combine_bwd(int64_t n_tok, int K, int H, int dv, const int32_t* inv, const double* w,
+                        const double* o_routed, const double* dout, double* d_routed, double* d_shared,
+                        double* dw) {
+  const int64_t E = (int64_t)H * dv;
+  for (int64_t t = 0; t < n_tok; ++t) {
+    for (int64_t e = 0; e < E; ++e) d_shared[t * E + e] = dout[t * E + e];
+    for (int j = 0; j < K; ++j) {
+      const int64_t r = inv ? inv[t * K + j] : t * K + j;
+      double s = 0.0;
+      for (int64_t e = 0; e < E; ++e) {
+        d_routed[r * E + e] = w[t * K + j] * dout[t * E + e];
+        s += dout[t * E + e] * o_routed[r * E + e];
+      }
+      dw[t * K + j] = s;
+    }
+  }
+}
+
+/* Router, with the top-k choice held fixed (straight-through: no gradient
+ * flows through the selection, only through the weights).  With
+ * w_j = exp(l_{idx_j}) / sum_j' exp(l_{idx_j'}) (the renormalised softmax):
+ *   dl[idx_j] = w_j (dw_j - sum_j' w_j' dw_j'),   dl[m] = 0 for m not selected
+ *   dx[t] = sum_m dl[t][m] wr[m],  dwr[m] = sum_t dl[t][m] x[t],
+ *   dbias[m] = sum_t dl[t][m]
+ * x [n_tok][D], wr [M][D], idx/w/dw [n_tok][K]; dx [n_tok][D], dwr [M][D],
+ * dbias [M] out.                                                              */
+void oracle_route_bwd(int64_t n_tok, int D, int M, int K, const double* x, const double* wr,
+                      const int32_t* idx, const double* w, const double* dw, double* dx, double* dwr,
+                      double* dbias) {
+  double* dl = (double*)malloc(sizeof(double) * (size_t)M);
+  for (int64_t i = 0; i < (int64_t)M * D; ++i) dwr[i] = 0.0;
+  for (int m = 0; m < M; ++m) dbias[m] = 0.0;
+  for (int64_t t = 0; t < n_tok; ++t) {
+    double sw = 0.0;
+    for (int j = 0; j < K; ++j) sw += w[t * K + j] * dw[t * K + j];
+    for (int m = 0; m < M; ++m) dl[m] = 0.0;
+    for (int j = 0; j < K; ++j) dl[idx[t * K + j]] = w[t * K + j] * (dw[t * K + j] - sw);
+    for (int d = 0; d < D; ++d) {
+      double s = 0.0;
+      for (int m = 0; m < M; ++m) s += dl[m] * wr[(int64_t)m * D + d];
+      dx[t * D + d] = s;
+    }
+    for (int m = 0; m < M; ++m) {
+      for (int d = 0; d < D; ++d) dwr[(int64_t)m * D + d] += dl[m] * x[t * D + d];
+      dbias[m] += dl[m];
+    }
+  }
+  free(dl);
+}
+
+/* The dispatch gathers in reverse.  Forward: packed row inv[t][j] takes the
+ * gates alpha/beta[t][h][idx[t][j]] and reads q[t]; shared row NR + t takes
+ * alpha/beta[t][h][M] and reads q[t].  Reverse:
+ *   d_alpha[t][h][idx_j] = d_alpha_p[inv[t][j]][h], d_alpha[t][h][M] =
+ *   d_alpha_p[NR + t][h], other memories 0 (the same for beta);
+ *   dq[t] = dq_rows[NR + t] + sum_j dq_rows[inv[t][j]]   (shared first, then j)
+ * d_alpha_p/d_beta_p [N][H], dq_rows [N][H][dk]; d_alpha/d_beta [n_tok][H][M+1],
+ * dq [n_tok][H][dk] out.                                                      */
+void oracle_dispatch_bwd(int64_t n_tok, int H, int dk, int M, int K, const int32_t* idx, const int32_t* inv,
+                         const double* d_alpha_p, const double* d_beta_p, const double* dq_rows, double* d_alpha,
+                         double* d_beta, double* dq) {
+  const int64_t NR = n_tok * K;
+  for (int64_t t = 0; t < n_tok; ++t) {
+    for (int h = 0; h < H; ++h) {
+      double* da = d_alpha + (t * H + h) * (M + 1);
+      double* db = d_beta + (t * H + h) * (M + 1);
+      for (int m = 0; m <= M; ++m) da[m] = db[m] = 0.0;
+      da[M] = d_alpha_p[(NR + t) * H + h];
+      db[M] = d_beta_p[(NR + t) * H + h];
+      for (int j = 0; j < K; ++j) {
+        const int64_t r = inv[t * K + j];
+        da[idx[t * K + j]] = d_alpha_p[r * H + h];
+        db[idx[t * K + j]] = d_beta_p[r * H + h];
+      }
+      for (int i = 0; i < dk; ++i) {
+        double s = dq_rows[((NR + t) * H + h) * dk + i];
+        for (int j = 0; j < K; ++j) s += dq_rows[((int64_t)inv[t * K + j] * H + h) * dk + i];
+        dq[(t * H + h) * dk + i] = s;
+      }
+    }
+  }
+}

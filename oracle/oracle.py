@@ -215,3 +215,94 @@ def segments_bwd(seg_off, seg_state, row_token, q, k, v, a, c, state0, d_o, dsta
                                    _p(res["dq"]), _p(res["dk"]), _p(res["dv"]), _p(res["da"]), _p(res["dc"]),
                                    _p(res["dstate0"]))
     return res
+
+
+def combine_bwd(inv, w, o_routed, dout, n_rows=None):
+    """Gradients of ``combine``: (d_routed [rows][H][dv] (rows no token reads are
+    zero), d_shared [n][H][dv], dw [n][K])."""
+    w, o_routed, dout = _d(w), _d(o_routed), _d(dout)
+    inv = _i(inv)
+    n, K = w.shape
+    H, dv = dout.shape[1], dout.shape[2]
+    rows = o_routed.shape[0] if n_rows is None else n_rows
+    d_routed = np.zeros((rows, H, dv))
+    d_shared = np.empty((n, H, dv))
+    dw = np.empty((n, K))
+    lib().oracle_combine_bwd(ctypes.c_int64(n), K, H, dv, _p(inv), _p(w), _p(o_routed), _p(dout), _p(d_routed),
+                             _p(d_shared), _p(dw))
+    return d_routed, d_shared, dw
+
+
+def route_bwd(x, w_r, idx, w, dw):
+    """Gradients of the router weights' loss with the top-k choice held fixed:
+    (dx [n][D], dw_r [M][D], dbias [M])."""
+    x, w_r, w, dw = _d(x), _d(w_r), _d(w), _d(dw)
+    idx = _i(idx)
+    n, D = x.shape
+    M = w_r.shape[0]
+    K = idx.shape[1]
+    dx = np.empty((n, D))
+    dwr = np.empty((M, D))
+    db = np.empty(M)
+    lib().oracle_route_bwd(ctypes.c_int64(n), D, M, K, _p(x), _p(w_r), _p(idx), _p(w), _p(dw), _p(dx), _p(dwr),
+                           _p(db))
+    return dx, dwr, db
+
+
+def dispatch_bwd(idx, inv, M, d_alpha_p, d_beta_p, dq_rows):
+    """The dispatch gathers in reverse: (d_alpha, d_beta [n][H][M+1], dq [n][H][dk])."""
+    idx, inv = _i(idx), _i(inv)
+    d_alpha_p, d_beta_p, dq_rows = _d(d_alpha_p), _d(d_beta_p), _d(dq_rows)
+    n, K = idx.shape
+    H, dk = dq_rows.shape[1], dq_rows.shape[2]
+    da = np.empty((n, H, M + 1))
+    db = np.empty((n, H, M + 1))
+    dq = np.empty((n, H, dk))
+    lib().oracle_dispatch_bwd(ctypes.c_int64(n), H, dk, M, K, _p(idx), _p(inv), _p(d_alpha_p), _p(d_beta_p),
+                              _p(dq_rows), _p(da), _p(db), _p(dq))
+    return da, db, dq
+
+
+def layer_bwd(dims, x, w_r, bias, w_q, w_k, w_v, alpha, beta, dout, state0=None, dstate=None, rule="gdn"):
+    """Gradients of the layer for the parts the layer's backward pass covers:
+    combine, recurrence (all memories), dispatch gathers and router weights, the
+    top-k choice held fixed.  Returns a dict with d_alpha, d_beta [NT][H][M+1],
+    dq [NT][H][dk] (w.r.t. the projected queries), dk_rows/dv_rows (w.r.t. the
+    packed projected keys and values), dx_router [NT][D] (the router's share of
+    dx), dw_r [M][D], dbias [M], dstate0 [B][M+1][H][dk][dv], and the forward's
+    routing (idx, w, seg_off, perm, inv) and packed rows for reference."""
+    B, T, D, H, dk, dv, M, K = [int(v) for v in dims]
+    NT, NR = B * T, B * T * K
+    fw = layer(dims, x, w_r, bias, w_q, w_k, w_v, alpha, beta, state0=state0, want_qkv=True, rule=rule)
+    idx, wgt = fw["idx"], fw["w"]
+    seg_off, perm, inv = dispatch(idx, B, T, M)
+    N = NR + NT
+    # packed rows: k/v of (token, j) at inv[t][j], shared at NR + t; gates per row
+    kp, vp = np.empty((N, H, dk)), np.empty((N, H, dv))
+    ap, bp = np.empty((N, H)), np.empty((N, H))
+    al = _d(alpha).reshape(NT, H, M + 1)
+    be = _d(beta).reshape(NT, H, M + 1)
+    for j in range(K):
+        r = inv[:, j]
+        kp[r], vp[r] = fw["k"][:, j], fw["v"][:, j]
+        ap[r] = al[np.arange(NT), :, idx[:, j]]
+        bp[r] = be[np.arange(NT), :, idx[:, j]]
+    kp[NR:], vp[NR:] = fw["k"][:, K], fw["v"][:, K]
+    ap[NR:], bp[NR:] = al[:, :, M], be[:, :, M]
+    o_rows = np.zeros((N, H, dv))
+    for j in range(K):
+        o_rows[inv[:, j]] = fw["o_routed"][:, j]
+    o_rows[NR:] = fw["o_shared"]
+    d_rows, d_shared, dw = combine_bwd(inv, wgt, o_rows, dout, n_rows=N)
+    d_rows[NR:] = d_shared
+    n_seg = (M + 1) * B
+    seg_state = np.array([(s % B) * (M + 1) + s // B for s in range(n_seg)], np.int32)
+    S0 = None if state0 is None else _d(state0).reshape(B * (M + 1), H, dk, dv)
+    dS = None if dstate is None else _d(dstate).reshape(B * (M + 1), H, dk, dv)
+    g = segments_bwd(seg_off, seg_state, perm, fw["q"], kp, vp, ap, bp, S0, d_rows, dS, n_state=B * (M + 1),
+                     rule=rule)
+    da, db, dq = dispatch_bwd(idx, inv, M, g["da"], g["dc"], g["dq"])
+    dx, dwr, dbias = route_bwd(x, w_r, idx, wgt, dw)
+    return dict(d_alpha=da, d_beta=db, dq=dq, dk_rows=g["dk"], dv_rows=g["dv"], dx_router=dx, dw_r=dwr, dbias=dbias,
+                dstate0=g["dstate0"].reshape(B, M + 1, H, dk, dv), idx=idx, w=wgt, seg_off=seg_off, perm=perm,
+                inv=inv, dw=dw, d_rows=d_rows)
