@@ -127,14 +127,14 @@ def test_chunk_workspace_sizes():
 
 @needs_lib
 def test_chunk_bwd_checks():
-    """The gradient entry points: workspace size (forward factors, X, and two
+    """The gradient entry points: workspace size (forward factors, X (half), and two
     half states per chunk and head), half storage only, and the usual refusals."""
     L = mom.lib()
     d = _dims()
     n_seg, n_rows = (d.M + 1) * d.B, d.B * d.T * (d.topk + 1)
     need = L.gdn_chunk_bwd_workspace_bytes(ctypes.byref(d), n_seg, n_rows)
     n_chunks = n_rows // 64 + n_seg
-    per = 64 * 64 * 2 * 2 + 64 * 4 * 2 + 64 * 64 * 4 + 2 * d.dk * d.dv * 2
+    per = 64 * 64 * 2 * 2 + 64 * 4 * 2 + 64 * 64 * 2 + 2 * d.dk * d.dv * 2
     assert need >= n_chunks * d.H * per and need % 256 == 0
     assert need > L.gdn_chunk_workspace_bytes(ctypes.byref(d), n_seg, n_rows)
     args = [FAKE] * 5 + [None, FAKE, None] + [FAKE] * 6  # q..beta, state_in, d_o, dstate_out, outputs
