@@ -111,9 +111,11 @@ def time_gla_layer(cfg, inp, x, alpha, beta, steps, warmup):
 
 
 def time_chunk_bwd(cfg, inp, x, alpha, beta, steps, warmup):
-    """Gradients of the memories' recurrence (gdn_chunk_bwd) over the layer's own
-    segments: route, dispatch and projections run once, then K timed calls with
-    random upstream gradients dL/do (per packed row) and dL/d(final states)."""
+    """Gradients for training over the layer's own segments: route, dispatch and
+    projections run once (forward), then K timed calls of the recurrence's
+    gradients alone (gdn_chunk_bwd) and K of the layer's backward (combine,
+    recurrence, dispatch gathers, router weights), with random upstream
+    gradients dL/dout and dL/d(final states)."""
     import torch
     from mixture_memories_recurrence_amd import mom, synth
     layer = mom.MomLayer(cfg, inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"])
@@ -121,17 +123,24 @@ def time_chunk_bwd(cfg, inp, x, alpha, beta, steps, warmup):
     gr = synth.make_chain_grads(b["N"], cfg.H, cfg.dk, cfg.dv, b["n_seg"], seed=9)
     d_o = torch.from_numpy(gr["d_o"]).cuda()
     dstate = torch.from_numpy(gr["dstate"]).cuda()
-    for _ in range(warmup):
-        layer.chunk_backward(b, d_o, dstate)
+    dout = d_o[:b["NT"]].contiguous()
+    dstate_l = dstate.view(cfg.B, cfg.M + 1, cfg.H, cfg.dk, cfg.dv)
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(steps):
-        layer.chunk_backward(b, d_o, dstate)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(lambda: layer.chunk_backward(b, d_o, dstate))
+    ms_layer = timed(lambda: layer.backward(x, dout, b, dstate_out=dstate_l))
     N, NT, H, dk, dv = b["N"], b["NT"], cfg.H, cfg.dk, cfg.dv
     # algorithmic bytes: q (per token), k, v (half), gates, dL/do, dL/dS_out read once;
     # dq, dk, dv, d_alpha, d_beta, dL/dS_in written once (float32)
@@ -141,7 +150,10 @@ def time_chunk_bwd(cfg, inp, x, alpha, beta, steps, warmup):
     return {"workload": "%s recurrence gradients (gdn_chunk_bwd over the layer's %d segments, %d rows)"
                         % (cfg.name, b["n_seg"], N),
             "ms": round(ms, 4), "tokens_per_s": round(NT / (ms * 1e-3), 1),
-            "algorithmic_bytes": nbytes, "achieved_gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+            "algorithmic_bytes": nbytes, "achieved_gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "layer_bwd": {"workload": "%s layer gradients: combine, recurrence, dispatch gathers, router weights "
+                                      "(top-k held fixed); not the projections" % cfg.name,
+                          "ms": round(ms_layer, 4), "tokens_per_s": round(NT / (ms_layer * 1e-3), 1)}}
 
 
 def time_single_memory(steps, warmup):

@@ -1,5 +1,6 @@
 /*
- * mom.h -- C ABI of the MI355X Mixture-of-Memories (MoM) layer forward library
+ * mom.h -- C ABI of the MI355X Mixture-of-Memories (MoM) layer library (forward, decode,
+ * and the gradients for training)
  * (libmom.so, HIP kernels for gfx950).
  *
  * The layer (arXiv 2502.13685, "MoM: Linear Sequence Modeling with
@@ -31,6 +32,10 @@
  *                    always-on shared memory (jxzklqfsx.com write-up,
  *                    Mixture-of-Memories section and hardware-efficient
  *                    implementation section).
+ *   mom_combine_bwd, mom_route_bwd, mom_dispatch_bwd
+ *                    the gradients of the combine, of the router weights
+ *                    (top-k held fixed) and of the dispatch gathers, for
+ *                    training.
  *
  * Recurrence of one memory, per head, on a state S [dk][dv] (float32):
  *   S <- a S;  S <- S + c k (v - S^T k)^T;  o = S^T q      (a = alpha, c = beta)
@@ -243,10 +248,49 @@ mom_status gla_decode_step(const mom_dims* dims, int32_t n_seq, const int32_t* i
 mom_status mom_combine(const mom_dims* dims, int32_t n_tok, const int32_t* inv, const float* w,
                        const float* o_routed, const float* o_shared, float* out, void* stream);
 
-enum { MOM_WS_DISPATCH = 0, MOM_WS_CHUNK = 1 };
+/* Gradients of the combine (for training; the chain rule of the sum above):
+ *   d_o_routed[row(t, j)] = w[t][j] dout[t],  d_o_shared[t] = dout[t],
+ *   dw[t][j] = <dout[t], o_routed[row(t, j)]>  (sum over H * dv, one wave per
+ *   token, fixed order).  Rows of d_o_routed no token reads are not written.
+ *   dout [n_tok][H][dv], d_o_shared [n_tok][H][dv], d_o_routed [*][H][dv],
+ *   dw [n_tok][topk] float32 out; other arguments as mom_combine.        */
+mom_status mom_combine_bwd(const mom_dims* dims, int32_t n_tok, const int32_t* inv, const float* w,
+                           const float* o_routed, const float* dout, float* d_o_routed, float* d_o_shared,
+                           float* dw, void* stream);
+
+/* Gradients of the router weights (for training), with the top-k choice held
+ * fixed: no gradient flows through the selection, only through the
+ * renormalised softmax weights of the selected memories.
+ *   dl[t][idx_j] = w_j (dw_j - sum_j' w_j' dw_j'),  dl = 0 for the others
+ *   dx[t] = sum_m dl[t][m] w_r[m]        ([NT][D] float32 out)
+ *   dw_r[m] = sum_t dl[t][m] x[t]        ([M][D] float32 out)
+ *   dbias[m] = sum_t dl[t][m]            ([M] float32 out, or NULL)
+ * x, w_r as mom_route; idx, w as written by mom_route; dw [NT][topk] float32
+ * (e.g. from mom_combine_bwd).  Sums over tokens run in a fixed order (tiles
+ * of 256 tokens, then the tiles in order).  ws holds at least
+ * mom_workspace_bytes(dims, MOM_WS_ROUTE_BWD) bytes. */
+mom_status mom_route_bwd(const mom_dims* dims, const void* x, const void* w_r, const int32_t* idx,
+                         const float* w, const float* dw, float* dx, float* dw_r, float* dbias, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* The dispatch gathers in reverse (for training): gate gradients per packed
+ * row go back to [token][head][memory] (d_alpha[t][h][idx[t][j]] =
+ * d_alpha_p[inv[t][j]][h], d_alpha[t][h][M] = d_alpha_p[NR + t][h], every
+ * other memory 0; the same for beta), and the query gradients of a token's
+ * rows are summed: dq[t] = dq_rows[NR + t] + sum_j dq_rows[inv[t][j]] (shared
+ * row first, then j).
+ *   idx, inv [NT][topk] int32 (mom_route, mom_dispatch)
+ *   d_alpha_p, d_beta_p [N][H], dq_rows [N][H][dk] float32 (gdn_chunk_bwd)
+ *   d_alpha, d_beta [NT][H][M+1], dq [NT][H][dk] float32 out               */
+mom_status mom_dispatch_bwd(const mom_dims* dims, const int32_t* idx, const int32_t* inv,
+                            const float* d_alpha_p, const float* d_beta_p, const float* dq_rows,
+                            float* d_alpha, float* d_beta, float* dq, void* stream);
+
+enum { MOM_WS_DISPATCH = 0, MOM_WS_CHUNK = 1, MOM_WS_ROUTE_BWD = 2 };
 /* Workspace bytes an entry point needs for the layer's own sizes (0 = none):
  * MOM_WS_DISPATCH for mom_dispatch, MOM_WS_CHUNK for gdn_chunk_fwd over the
- * layer's n_seg = (M+1)*B segments and N rows.  0 for invalid dims. */
+ * layer's n_seg = (M+1)*B segments and N rows, MOM_WS_ROUTE_BWD for
+ * mom_route_bwd.  0 for invalid dims. */
 size_t mom_workspace_bytes(const mom_dims* dims, int32_t which);
 
 /* Workspace bytes gdn_chunk_fwd needs for n_seg segments over n_rows packed

@@ -14,6 +14,7 @@ mom_status launch_gdn_chunk_mfma(const mom_dims& d, int n_seg, int n_rows, const
                                  const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
                                  float* state_out, float* o, void* ws, bool delta, hipStream_t st);
 size_t gdn_chunk_ws_bytes(int64_t n_seg, int64_t n_rows, int H, int dk);
+size_t route_bwd_ws_bytes(const mom_dims& d);
 }  // namespace mom
 
 extern "C" size_t gdn_chunk_workspace_bytes(const mom_dims* dims, int32_t n_seg, int32_t n_rows) {
@@ -91,6 +92,7 @@ extern "C" size_t mom_workspace_bytes(const mom_dims* dims, int32_t which) {
     const Sizes z = sizes_of(d);
     return gdn_chunk_workspace_bytes(dims, (int32_t)z.n_seg, (int32_t)z.N);
   }
+  if (which == MOM_WS_ROUTE_BWD) return route_bwd_ws_bytes(d);
   return 0;
 }
 

@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmom.so")
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
-WS_DISPATCH, WS_CHUNK = 0, 1
+WS_DISPATCH, WS_CHUNK, WS_ROUTE_BWD = 0, 1, 2
 
 
 class MomError(RuntimeError):
@@ -60,6 +60,9 @@ def lib():
         "gdn_decode_step": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
         "gla_decode_step": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
         "mom_combine": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP],
+        "mom_combine_bwd": [D, _I32] + [_VP] * 8,
+        "mom_route_bwd": [D] + [_VP] * 9 + [ctypes.c_size_t, _VP],
+        "mom_dispatch_bwd": [D] + [_VP] * 9,
         "mom_workspace_bytes": [D, _I32],
         "gdn_chunk_workspace_bytes": [D, _I32, _I32],
         "mom_status_string": [_I32],
@@ -77,8 +80,9 @@ def lib():
 
 
 EXPORTS = ("mom_route", "mom_dispatch", "mom_project", "gdn_chunk_fwd", "gla_chunk_fwd", "gdn_chunk_bwd",
-           "gla_chunk_bwd", "gdn_decode_step", "gla_decode_step", "mom_combine", "mom_workspace_bytes",
-           "gdn_chunk_workspace_bytes", "gdn_chunk_bwd_workspace_bytes", "mom_status_string")
+           "gla_chunk_bwd", "gdn_decode_step", "gla_decode_step", "mom_combine", "mom_combine_bwd",
+           "mom_route_bwd", "mom_dispatch_bwd", "mom_workspace_bytes", "gdn_chunk_workspace_bytes",
+           "gdn_chunk_bwd_workspace_bytes", "mom_status_string")
 
 
 def dims_of(cfg: LayerConfig, B: int | None = None, T: int | None = None) -> MomDims:
@@ -180,6 +184,22 @@ def gla_decode_step(dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, stre
 def mom_combine(dims, n_tok, inv, w, o_routed, o_shared, out, stream=None):
     _check(lib().mom_combine(ctypes.byref(dims), n_tok, _p(inv), _p(w), _p(o_routed), _p(o_shared), _p(out),
                              _s(stream)), "mom_combine")
+
+
+def mom_combine_bwd(dims, n_tok, inv, w, o_routed, dout, d_o_routed, d_o_shared, dw, stream=None):
+    _check(lib().mom_combine_bwd(ctypes.byref(dims), n_tok, _p(inv), _p(w), _p(o_routed), _p(dout), _p(d_o_routed),
+                                 _p(d_o_shared), _p(dw), _s(stream)), "mom_combine_bwd")
+
+
+def mom_route_bwd(dims, x, w_r, idx, w, dw, dx, dw_r, dbias, ws, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().mom_route_bwd(ctypes.byref(dims), _p(x), _p(w_r), _p(idx), _p(w), _p(dw), _p(dx), _p(dw_r),
+                               _p(dbias), _p(ws), nbytes, _s(stream)), "mom_route_bwd")
+
+
+def mom_dispatch_bwd(dims, idx, inv, d_alpha_p, d_beta_p, dq_rows, d_alpha, d_beta, dq, stream=None):
+    _check(lib().mom_dispatch_bwd(ctypes.byref(dims), _p(idx), _p(inv), _p(d_alpha_p), _p(d_beta_p), _p(dq_rows),
+                                  _p(d_alpha), _p(d_beta), _p(dq), _s(stream)), "mom_dispatch_bwd")
 
 
 def mom_workspace_bytes(dims, which):
@@ -298,6 +318,40 @@ class MomLayer:
            b["k"], b["v"], b["alpha_p"], b["beta_p"], state_in, d_o, dstate_out, g["dq"], g["dk"], g["dv"],
            g["d_alpha"], g["d_beta"], g["dstate_in"], g["ws"], stream)
         return g
+
+    def backward(self, x, dout, b, dstate_out=None, state_in=None, stream=None):
+        """Gradients of the layer's last forward (buffers b, input x) for the
+        parts its backward pass covers: combine, the memories' recurrence, the
+        dispatch gathers and the router weights (top-k held fixed).  dout
+        [B*T, H, dv] fp32 = dL/dout; dstate_out = dL/d(final states) or None.
+        Returns a dict (buffers reused per shape) of d_alpha, d_beta [B*T, H, M+1],
+        dq [B*T, H, dk] (w.r.t. the projected queries), dk, dv [N, H, dk|dv]
+        (w.r.t. the packed projected keys and values), dx_router [B*T, D] (the
+        router's share of dL/dx), dw_r [M, D], dbias [M], dstate_in."""
+        c, d = self.cfg, b["dims"]
+        if "lgrad" not in b:
+            dev, f32 = self.device, torch.float32
+            NT, N, H = b["NT"], b["N"], c.H
+            b["lgrad"] = dict(d_o=torch.empty(N, H, c.dv, dtype=f32, device=dev),
+                              dw=torch.empty(NT, c.K, dtype=f32, device=dev),
+                              d_alpha=torch.empty(NT, H, c.M + 1, dtype=f32, device=dev),
+                              d_beta=torch.empty(NT, H, c.M + 1, dtype=f32, device=dev),
+                              dq=torch.empty(NT, H, c.dk, dtype=f32, device=dev),
+                              dx_router=torch.empty(NT, c.D, dtype=f32, device=dev),
+                              dw_r=torch.empty(c.M, c.D, dtype=f32, device=dev),
+                              dbias=torch.empty(c.M, dtype=f32, device=dev),
+                              ws=torch.empty(max(mom_workspace_bytes(d, WS_ROUTE_BWD), 256), dtype=torch.uint8,
+                                             device=dev))
+        lg = b["lgrad"]
+        mom_combine_bwd(d, b["NT"], b["inv"], b["w"], b["o"], dout, lg["d_o"], lg["d_o"][b["NR"]:], lg["dw"], stream)
+        g = self.chunk_backward(b, lg["d_o"], dstate_out, state_in, stream)
+        mom_dispatch_bwd(d, b["idx"], b["inv"], g["d_alpha"], g["d_beta"], g["dq"], lg["d_alpha"], lg["d_beta"],
+                         lg["dq"], stream)
+        mom_route_bwd(d, x, self.w_r, b["idx"], b["w"], lg["dw"], lg["dx_router"], lg["dw_r"], lg["dbias"], lg["ws"],
+                      stream)
+        return dict(d_alpha=lg["d_alpha"], d_beta=lg["d_beta"], dq=lg["dq"], dk=g["dk"], dv=g["dv"],
+                    dx_router=lg["dx_router"], dw_r=lg["dw_r"], dbias=lg["dbias"],
+                    dstate_in=g["dstate_in"].view(-1, c.M + 1, c.H, c.dk, c.dv))
 
     def decode_step(self, x_t, alpha, beta, states, stream=None):
         """One token for each of n_seq sequences: x_t [n_seq, D], alpha/beta
