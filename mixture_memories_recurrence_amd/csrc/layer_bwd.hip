@@ -105,37 +105,164 @@ __global__ __launch_bounds__(256) void k_route_bwd_dx(int64_t n_tok, int D, int 
 
 // Weight gradient, first pass: block (column chunk c of 256, token tile tt of
 // kRouteTile) sums dl[t][m] x[t][d] over its tokens for its 256 columns, one
-// column per thread, into LDS rows per memory (no two threads share an
-// address), then writes the tile's partial [M][256]; thread 0 also sums the
-// bias gradient of the tile.
-constexpr int kRouteTile = 256;
-template <typename IT>
+// column per thread, then writes the tile's partial [M][256]; in chunk 0,
+// thread m < M also sums memory m's bias gradient over the tile.  The tile's selections and
+// dl are staged in LDS and x is read 8 tokens at a time, so 8 loads per thread
+// are in flight.  With MB > 0 (M <= MB) the sums live in registers, one per
+// memory (each token adds its K terms through selects); with MB = 0 they live
+// in LDS rows per memory.
+constexpr int kRouteTile = 128;
+template <typename IT, int MB>
 __global__ __launch_bounds__(256) void k_route_bwd_dw(int64_t n_tok, int D, int M, int K, const IT* __restrict__ x,
                                                       const int32_t* __restrict__ idx, const float* __restrict__ dl,
                                                       float* __restrict__ part, float* __restrict__ part_b) {
-  extern __shared__ float acc[];  // [M][256], then [M] for the bias
+  extern __shared__ float acc_l[];  // MB = 0: [M][256]
+  __shared__ int s_idx[kRouteTile * 8];
+  __shared__ float s_dl[kRouteTile * 8];
   const int nc = (D + 255) / 256;
   const int c = blockIdx.x % nc, tt = blockIdx.x / nc;
   const int tid = threadIdx.x;
   const int d = 256 * c + tid;
   const bool col = d < D;
-  for (int m = 0; m < M; ++m) acc[m * 256 + tid] = 0.f;
-  if (tid < M) acc[M * 256 + tid] = 0.f;
+  const int64_t t0 = (int64_t)tt * kRouteTile;
+  const int nt = (int)min((int64_t)kRouteTile, n_tok - t0);
+  for (int i = tid; i < nt * K; i += 256) {
+    s_idx[i] = idx[t0 * K + i];
+    s_dl[i] = dl[t0 * K + i];
+  }
+  float acc[MB > 0 ? MB : 1];
+#pragma unroll
+  for (int m = 0; m < (MB > 0 ? MB : 1); ++m) acc[m] = 0.f;
+  if (MB == 0)
+    for (int m = 0; m < M; ++m) acc_l[m * 256 + tid] = 0.f;
   __syncthreads();
-  const int64_t t0 = (int64_t)tt * kRouteTile, t1 = min(n_tok, t0 + kRouteTile);
-  for (int64_t t = t0; t < t1; ++t) {
-    const float xv = col ? load_as_f32(x + t * D + d) : 0.f;
-    for (int j = 0; j < K; ++j) {
-      const int m = idx[t * K + j];
-      const float g = dl[t * K + j];
-      acc[m * 256 + tid] = fmaf(g, xv, acc[m * 256 + tid]);
-      if (tid == 0 && c == 0) acc[M * 256 + m] += g;
+  for (int tb = 0; tb < nt; tb += 8) {
+    float xv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) xv[u] = (col && tb + u < nt) ? load_as_f32(x + (t0 + tb + u) * D + d) : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (tb + u >= nt) break;
+      for (int j = 0; j < K; ++j) {
+        const int m = s_idx[(tb + u) * K + j];
+        const float g = s_dl[(tb + u) * K + j];
+        if constexpr (MB > 0) {
+#pragma unroll
+          for (int mm = 0; mm < MB; ++mm) acc[mm] = fmaf(m == mm ? g : 0.f, xv[u], acc[mm]);
+        } else {
+          acc_l[m * 256 + tid] = fmaf(g, xv[u], acc_l[m * 256 + tid]);
+        }
+      }
     }
   }
-  __syncthreads();  // thread 0's bias sums are read below by threads 0..M-1
-  if (col)
-    for (int m = 0; m < M; ++m) part[((int64_t)tt * M + m) * D + d] = acc[m * 256 + tid];
-  if (c == 0 && tid < M) part_b[(int64_t)tt * M + tid] = acc[M * 256 + tid];
+  const int64_t tile = tt;
+  if (col) {
+    if constexpr (MB > 0) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+        if (m < M) part[(tile * M + m) * D + d] = acc[m];
+    } else {
+      for (int m = 0; m < M; ++m) part[(tile * M + m) * D + d] = acc_l[m * 256 + tid];
+    }
+  }
+  if (c == 0 && tid < M) {
+    float sb = 0.f;
+    for (int i = 0; i < nt * K; ++i)
+      if (s_idx[i] == tid) sb += s_dl[i];
+    part_b[tile * M + tid] = sb;
+  }
+}
+
+// The same first pass for M <= MB <= 8 with 16-byte loads: 256 threads = 32
+// groups of 8 columns x 8 token lanes; thread (tl, cg) takes tokens tl, tl + 8,
+// ... of the tile and columns 8 cg .. 8 cg + 7 of the chunk of 256, with its
+// sums in registers [memory][column]; the 8 token lanes are then added in
+// order through LDS.
+template <typename IT>
+__device__ __forceinline__ void load8(const IT* p, float* v);
+template <>
+__device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float* v) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <typename IT, int MB>
+__global__ __launch_bounds__(256) void k_route_bwd_dw8(int64_t n_tok, int D, int M, int K, const IT* __restrict__ x,
+                                                       const int32_t* __restrict__ idx, const float* __restrict__ dl,
+                                                       float* __restrict__ part, float* __restrict__ part_b) {
+  __shared__ int s_idx[kRouteTile * 8];
+  __shared__ float s_dl[kRouteTile * 8];
+  __shared__ float red[8][MB][257];
+  const int nc = (D + 255) / 256;
+  const int c = blockIdx.x % nc, tt = blockIdx.x / nc;
+  const int tid = threadIdx.x, tl = tid >> 5, cg = tid & 31;
+  const int d0 = 256 * c + 8 * cg;
+  const bool col = d0 < D;  // D is a multiple of 64
+  const int64_t t0 = (int64_t)tt * kRouteTile;
+  const int nt = (int)min((int64_t)kRouteTile, n_tok - t0);
+  for (int i = tid; i < nt * K; i += 256) {
+    s_idx[i] = idx[t0 * K + i];
+    s_dl[i] = dl[t0 * K + i];
+  }
+  float acc[MB][8];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[m][e] = 0.f;
+  __syncthreads();
+  for (int tb = tl; tb < nt; tb += 16) {
+    float xa[8], xb[8];
+    const bool hb = tb + 8 < nt;
+    if (col) {
+      load8<IT>(x + (t0 + tb) * D + d0, xa);
+      if (hb) load8<IT>(x + (t0 + tb + 8) * D + d0, xb);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && !hb) break;
+      const int t = tb + 8 * u;
+      const float* xv = u ? xb : xa;
+      for (int j = 0; j < K; ++j) {
+        const int m = s_idx[t * K + j];
+        const float g = s_dl[t * K + j];
+#pragma unroll
+        for (int mm = 0; mm < MB; ++mm) {
+          const float gg = m == mm ? g : 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[mm][e] = fmaf(gg, xv[e], acc[mm][e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[tl][m][8 * cg + e] = acc[m][e];
+  __syncthreads();
+  const int64_t tile = tt;
+  for (int i = tid; i < M * 256; i += 256) {
+    const int m = i >> 8, cc = i & 255;
+    float sum = 0.f;
+#pragma unroll
+    for (int l = 0; l < 8; ++l) sum += red[l][m][cc];
+    if (256 * c + cc < D) part[(tile * M + m) * D + 256 * c + cc] = sum;
+  }
+  if (c == 0 && tid < M) {
+    float sb = 0.f;
+    for (int i = 0; i < nt * K; ++i)
+      if (s_idx[i] == tid) sb += s_dl[i];
+    part_b[tile * M + tid] = sb;
+  }
 }
 
 // Second pass: tiles summed in order.
@@ -143,9 +270,18 @@ __global__ __launch_bounds__(256) void k_route_bwd_sum(int n_tiles, int D, int M
                                                        const float* __restrict__ part_b, float* __restrict__ dw_r,
                                                        float* __restrict__ dbias) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < (int64_t)M * D) {
+  const int64_t MD = (int64_t)M * D;
+  if (i < MD) {
     float s = 0.f;
-    for (int tt = 0; tt < n_tiles; ++tt) s += part[(int64_t)tt * M * D + i];
+    int tt = 0;
+    for (; tt + 8 <= n_tiles; tt += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(tt + u) * MD + i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; tt < n_tiles; ++tt) s += part[(int64_t)tt * MD + i];
     dw_r[i] = s;
   }
   if (dbias && i < M) {
@@ -255,33 +391,42 @@ extern "C" mom_status mom_route_bwd(const mom_dims* dims, const void* x, const v
   float* part_b = (float*)((char*)part + up(n_tiles * d.M * d.D * 4));
   hipStream_t st = (hipStream_t)stream;
   const unsigned tb = (unsigned)((NT + 3) / 4);
-  const size_t lds = ((size_t)d.M * 256 + 64) * sizeof(float);  // up to 66 KB (M = 64)
   const unsigned wb = (unsigned)(n_tiles * ((d.D + 255) / 256));
-  static bool attr[2] = {false, false};  // the dynamic LDS limit is raised once per kernel
-  const int ai = d.dtype == MOM_DTYPE_BF16 ? 0 : 1;
-  if (!attr[ai]) {
-    const void* f = ai == 0 ? (const void*)k_route_bwd_dw<bf16_t> : (const void*)k_route_bwd_dw<float>;
-    if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(((size_t)64 * 256 + 64) * 4)) !=
-        hipSuccess)
-      return MOM_ERR_LAUNCH;
-    attr[ai] = true;
+  const size_t lds = d.M > 16 ? (size_t)d.M * 256 * sizeof(float) : 0;  // M > 16: LDS sums, up to 64 KB
+  if (d.M > 16) {
+    static bool attr[2] = {false, false};  // the dynamic LDS limit is raised once per kernel
+    const int ai = d.dtype == MOM_DTYPE_BF16 ? 0 : 1;
+    if (!attr[ai]) {
+      const void* f = ai == 0 ? (const void*)k_route_bwd_dw<bf16_t, 0> : (const void*)k_route_bwd_dw<float, 0>;
+      if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 256 * 4) != hipSuccess)
+        return MOM_ERR_LAUNCH;
+      attr[ai] = true;
+    }
   }
 #define MOM_RBWD(IT, KM)                                                                                         \
   hipLaunchKernelGGL((k_route_bwd_dx<IT, KM>), dim3(tb), dim3(256), 0, st, NT, d.D, d.topk, (const IT*)w_r, idx, \
                      w, dw, dl, dx)
-  if (d.dtype == MOM_DTYPE_BF16) {
-    if (d.topk <= 2) MOM_RBWD(bf16_t, 2);
-    else if (d.topk <= 4) MOM_RBWD(bf16_t, 4);
-    else MOM_RBWD(bf16_t, 8);
-    hipLaunchKernelGGL((k_route_bwd_dw<bf16_t>), dim3(wb), dim3(256), lds, st, NT,
-                       d.D, d.M, d.topk, (const bf16_t*)x, idx, dl, part, part_b);
-  } else {
-    if (d.topk <= 2) MOM_RBWD(float, 2);
-    else if (d.topk <= 4) MOM_RBWD(float, 4);
-    else MOM_RBWD(float, 8);
-    hipLaunchKernelGGL((k_route_bwd_dw<float>), dim3(wb), dim3(256), lds, st, NT,
-                       d.D, d.M, d.topk, (const float*)x, idx, dl, part, part_b);
-  }
+#define MOM_RBWD_DW(IT, MB)                                                                                       \
+  hipLaunchKernelGGL((k_route_bwd_dw<IT, MB>), dim3(wb), dim3(256), lds, st, NT, d.D, d.M, d.topk, (const IT*)x, \
+                     idx, dl, part, part_b)
+#define MOM_RBWD_DW8(IT, MB)                                                                                   \
+  hipLaunchKernelGGL((k_route_bwd_dw8<IT, MB>), dim3(wb), dim3(256), 0, st, NT, d.D, d.M, d.topk, (const IT*)x, \
+                     idx, dl, part, part_b)
+#define MOM_RBWD_ALL(IT)           \
+  do {                             \
+    if (d.topk <= 2) MOM_RBWD(IT, 2); \
+    else if (d.topk <= 4) MOM_RBWD(IT, 4); \
+    else MOM_RBWD(IT, 8);          \
+    if (d.M <= 4) MOM_RBWD_DW8(IT, 4); \
+    else if (d.M <= 8) MOM_RBWD_DW8(IT, 8); \
+    else if (d.M <= 16) MOM_RBWD_DW(IT, 16); \
+    else MOM_RBWD_DW(IT, 0);       \
+  } while (0)
+  if (d.dtype == MOM_DTYPE_BF16) MOM_RBWD_ALL(bf16_t);
+  else MOM_RBWD_ALL(float);
+#undef MOM_RBWD_ALL
+#undef MOM_RBWD_DW8
+#undef MOM_RBWD_DW
 #undef MOM_RBWD
   hipLaunchKernelGGL(k_route_bwd_sum, dim3((unsigned)(((int64_t)d.M * d.D + 255) / 256)), dim3(256), 0, st,
                      (int)n_tiles, d.D, d.M, part, part_b, dw_r, dbias);

@@ -93,3 +93,32 @@ def test_combine_route_dispatch_bwd_full_size():
     assert_grad("router dx", f(dx), dx_ref)
     assert_grad("router dw_r", f(dwr), dwr_ref)
     assert_grad("router dbias", f(dbias), db_ref2)
+
+
+@pytest.mark.parametrize("M,K,D,NT", [(64, 8, 192, 700), (5, 2, 320, 513), (16, 4, 1024, 300)])
+def test_route_bwd_shapes(M, K, D, NT):
+    """mom_route_bwd alone over random selections and upstream gradients: many
+    memories (sums kept in LDS), column counts that are not a multiple of 256,
+    and token counts that leave a partial tile."""
+    rng = np.random.default_rng(M + K + D)
+    x = rng.standard_normal((NT, D)).astype(np.float32)
+    w_r = (rng.standard_normal((M, D)) / np.sqrt(D)).astype(np.float32)
+    idx = np.stack([rng.permutation(M)[:K] for _ in range(NT)]).astype(np.int32)
+    w = rng.uniform(0.1, 1.0, (NT, K)).astype(np.float32)
+    w /= w.sum(1, keepdims=True)
+    dw = rng.standard_normal((NT, K)).astype(np.float32)
+    cfg = synth.LayerConfig(1, NT, D, 2, 64, 64, M, K, "bf16")
+    d = mom.dims_of(cfg)
+    xb, wb = to_gpu(x, torch.bfloat16), to_gpu(w_r, torch.bfloat16)
+    dx = torch.empty(NT, D, device="cuda")
+    dwr = torch.empty(M, D, device="cuda")
+    db = torch.empty(M, device="cuda")
+    ws = torch.empty(mom.mom_workspace_bytes(d, mom.WS_ROUTE_BWD), dtype=torch.uint8, device="cuda")
+    log("route_bwd", M, K, D, NT)
+    mom.mom_route_bwd(d, xb, wb, to_gpu(idx), to_gpu(w), to_gpu(dw), dx, dwr, db, ws)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy()
+    dx_ref, dwr_ref, db_ref = oracle.route_bwd(f(xb), f(wb), idx, w, dw)
+    assert_grad("router dx", f(dx), dx_ref)
+    assert_grad("router dw_r", f(dwr), dwr_ref)
+    assert_grad("router dbias", f(db), db_ref)
