@@ -6,9 +6,9 @@ Two steps, both run on the GPU host:
     rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/copy_fetch -o p -- \
         python3 -m mixture_memories_recurrence_amd.pmc_traffic copy --mib 1024
     rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/copy_write -o p -- (same command)
-    # 2. the bench steps, without the decode part
+    # 2. the bench steps, without the decode and gradient parts
     rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/fetch -o p -- python3 bench.py --steps 2 --warmup 1 \
-        --no-decode --no-cpu-baseline --no-gla --no-single
+        --no-decode --no-cpu-baseline --no-gla --no-single --no-bwd
     rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/write -o p -- (same command)
     python3 -m mixture_memories_recurrence_amd.pmc_traffic summarize --dir OUT --copy-mib 1024 \
         --workload l380m --out profiles/traffic_l380m.json
@@ -40,7 +40,7 @@ STAGES = {
     "dispatch": (("k_count", "k_scan", "k_scatter"), ("dispatch.hip",)),
     "project": (("k_project",), ("project.hip",)),
     "chunk": (("k_gdn_prep", "k_gdn_chain", "k_gdn_chunk_valu"),
-              ("gdn_chunk_mfma.hip", "gdn_chunk_valu.hip")),
+              ("gdn_chunk_mfma.hip", "chunk_mfma.h", "gdn_chunk_valu.hip")),
     "combine": (("k_combine",), ("combine.hip",)),
 }
 
@@ -98,7 +98,7 @@ def cmd_summarize(a):
     out = {"workload": a.workload, "copy_mib": a.copy_mib, "fetch_scale": round(f_scale, 4),
            "write_scale": round(w_scale, 4), "stages": {}}
     for st, (prefixes, _) in STAGES.items():
-        ks = sorted(k for k in fetch if any(p in k for p in prefixes))
+        ks = sorted(k for k in fetch if any(p in k for p in prefixes) and "_bwd" not in k)
         if not ks:
             continue
         rd = sum(fetch[k] for k in ks) * 1024 * f_scale
