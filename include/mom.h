@@ -145,6 +145,28 @@ mom_status mom_project(const mom_dims* dims, const void* x, const int32_t* perm,
                        const int32_t* seg_off, const void* w_q, const void* w_k, const void* w_v,
                        void* q, void* k, void* v, void* stream);
 
+/* The same two steps in parts, so that the shared memory's path, which
+ * needs no routing, can run on another stream beside the routed one:
+ *   part 0 = everything (mom_dispatch / mom_project);
+ *   part 1 = the shared memory: mom_dispatch_part writes its rows (row NR + t
+ *            holds token t: perm, alpha_p, beta_p) and seg_off[M*B .. (M+1)*B]
+ *            and reads neither idx nor inv nor ws (may be NULL);
+ *            mom_project_part writes q (all tokens) and k, v of rows
+ *            NR .. N and reads neither perm nor seg_off (may be NULL);
+ *   part 2 = the routed memories: mom_dispatch_part writes their rows, inv and
+ *            seg_off[0 .. M*B]; mom_project_part writes k, v of rows 0 .. NR
+ *            (reads perm and seg_off as written by part 2).
+ * Parts 1 and 2 write disjoint rows and only the common entry seg_off[M*B] =
+ * NR twice (the same value).  Other arguments, layouts and errors as
+ * mom_dispatch / mom_project; part outside 0..2 returns MOM_ERR_DIMS. */
+mom_status mom_dispatch_part(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
+                             const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv,
+                             void* x_packed, float* alpha_p, float* beta_p, void* ws, size_t ws_bytes,
+                             int32_t part, void* stream);
+mom_status mom_project_part(const mom_dims* dims, const void* x, const int32_t* perm,
+                            const int32_t* seg_off, const void* w_q, const void* w_k, const void* w_v,
+                            void* q, void* k, void* v, int32_t part, void* stream);
+
 /* Chunkwise Gated DeltaNet over packed segments.  Segment s (rows
  * [seg_off[s], seg_off[s+1]) of the row arrays) runs the recurrence above in
  * row order from state slot seg_state[s] (NULL: slot s); different segments

@@ -16,6 +16,8 @@
 //             the order inside a segment is increasing position.  The block
 //             then writes perm/inv, gathers the gates of the routed memory and,
 //             if asked, the x rows.
+#include <algorithm>
+
 #include "common.h"
 
 namespace mom {
@@ -42,8 +44,8 @@ __global__ __launch_bounds__(kTile) void k_count(int B, int T, int M, int K, int
 }
 
 // Exclusive scan of n counts in place (single block of 1024 threads).
-__global__ __launch_bounds__(1024) void k_scan(int B, int T, int M, int K, int ntile, int32_t* __restrict__ cnt,
-                                               int32_t* __restrict__ seg_off) {
+__global__ __launch_bounds__(1024) void k_scan(int B, int T, int M, int K, int ntile, int last_seg,
+                                               int32_t* __restrict__ cnt, int32_t* __restrict__ seg_off) {
   __shared__ int32_t wsum[16];
   __shared__ int32_t carry_s;
   const int n = M * B * ntile;
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(1024) void k_scan(int B, int T, int M, int K, int n
     __syncthreads();
   }
   const int64_t NR = (int64_t)B * T * K;
-  for (int s = threadIdx.x; s <= (M + 1) * B; s += 1024) {
+  for (int s = threadIdx.x; s <= last_seg; s += 1024) {
     int64_t off;
     if (s < M * B) off = cnt[(int64_t)s * ntile];
     else if (s < (M + 1) * B) off = NR + (int64_t)(s - M * B) * T;
@@ -108,7 +110,8 @@ __device__ void block_exclusive_scan(const int32_t* __restrict__ cnt, int n, int
 }
 
 template <typename XT, bool FUSED>
-__global__ __launch_bounds__(kTile) void k_scatter(int B, int T, int D, int H, int M, int K, int ntile,
+__global__ __launch_bounds__(kTile) void k_scatter(int B, int T, int D, int H, int M, int K, int ntile, int last_seg,
+                                                   bool shared_rows,
                                                    const int32_t* __restrict__ idx, const int32_t* __restrict__ base,
                                                    int32_t* __restrict__ seg_off,
                                                    const float* __restrict__ alpha, const float* __restrict__ beta,
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(kTile) void k_scatter(int B, int T, int D, int H, i
   if (FUSED) {
     block_exclusive_scan(base, M * B * ntile, cs, wsum);
     if (tile == 0 && b == 0)
-      for (int sg = threadIdx.x; sg <= (M + 1) * B; sg += kTile) {
+      for (int sg = threadIdx.x; sg <= last_seg; sg += kTile) {
         int64_t off;
         if (sg < M * B) off = cs[(int64_t)sg * ntile];
         else if (sg < (M + 1) * B) off = NR + (int64_t)(sg - M * B) * T;
@@ -175,12 +178,14 @@ __global__ __launch_bounds__(kTile) void k_scatter(int B, int T, int D, int H, i
         }
       }
     }
-    const int64_t srow = NR + tok;
-    perm[srow] = (int32_t)tok;
-    for (int h = 0; h < H; ++h) {
-      const int64_t src = (tok * H + h) * (M + 1) + M;
-      alpha_p[srow * H + h] = alpha[src];
-      beta_p[srow * H + h] = beta[src];
+    if (shared_rows) {
+      const int64_t srow = NR + tok;
+      perm[srow] = (int32_t)tok;
+      for (int h = 0; h < H; ++h) {
+        const int64_t src = (tok * H + h) * (M + 1) + M;
+        alpha_p[srow * H + h] = alpha[src];
+        beta_p[srow * H + h] = beta[src];
+      }
     }
   }
   if (x_packed == nullptr) return;
@@ -198,40 +203,69 @@ __global__ __launch_bounds__(kTile) void k_scatter(int B, int T, int D, int H, i
   }
 }
 
+// The shared memory's rows alone (they need no routing): row NR + t holds
+// token t, its gates are alpha/beta[t][h][M]; the shared segments start at
+// NR + b T.  One thread per (token, head).
+__global__ __launch_bounds__(256) void k_dispatch_shared(int B, int T, int H, int M, int K,
+                                                         const float* __restrict__ alpha,
+                                                         const float* __restrict__ beta, int32_t* __restrict__ seg_off,
+                                                         int32_t* __restrict__ perm, float* __restrict__ alpha_p,
+                                                         float* __restrict__ beta_p) {
+  const int64_t NT = (int64_t)B * T, NR = NT * K;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i <= B) seg_off[(int64_t)M * B + i] = (int32_t)(NR + i * T);
+  if (i >= NT * H) return;
+  const int64_t t = i / H, h = i % H;
+  const int64_t src = (t * H + h) * (M + 1) + M;
+  alpha_p[(NR + t) * H + h] = alpha[src];
+  beta_p[(NR + t) * H + h] = beta[src];
+  if (h == 0) perm[NR + t] = (int32_t)t;
+}
+
 }  // namespace mom
 
-extern "C" mom_status mom_dispatch(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
-                                   const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv,
-                                   void* x_packed, float* alpha_p, float* beta_p, void* ws, size_t ws_bytes,
-                                   void* stream) {
-  using namespace mom;
+namespace mom {
+static mom_status dispatch(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
+                           const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv, void* x_packed,
+                           float* alpha_p, float* beta_p, void* ws, size_t ws_bytes, int part, void* stream) {
   mom_status s = check_dims(dims);
   if (s != MOM_OK) return s;
-  MOM_CHECK_PTR(idx);
+  if (part < 0 || part > 2) return MOM_ERR_DIMS;
   MOM_CHECK_PTR(alpha);
   MOM_CHECK_PTR(beta);
   MOM_CHECK_PTR(seg_off);
   MOM_CHECK_PTR(perm);
-  MOM_CHECK_PTR(inv);
   MOM_CHECK_PTR(alpha_p);
   MOM_CHECK_PTR(beta_p);
+  hipStream_t st = (hipStream_t)stream;
+  const mom_dims& d = *dims;
+  if (part == 1) {  // the shared memory's rows: no routing needed
+    const int64_t n = std::max((int64_t)d.B * d.T * d.H, (int64_t)d.B + 1);  // rows x heads, and B + 1 offsets
+    hipLaunchKernelGGL(k_dispatch_shared, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, d.B, d.T, d.H, d.M,
+                       d.topk, alpha, beta, seg_off, perm, alpha_p, beta_p);
+    return launch_status();
+  }
+  MOM_CHECK_PTR(idx);
+  MOM_CHECK_PTR(inv);
   MOM_CHECK_OPT_PTR(x_packed);
   if (x_packed) MOM_CHECK_PTR(x);
   const size_t need = mom_workspace_bytes(dims, MOM_WS_DISPATCH);
   if (!ws || ws_bytes < need) return MOM_ERR_WORKSPACE;
   MOM_CHECK_PTR(ws);
-  const mom_dims& d = *dims;
   const int ntile = ceil_div(d.T, kTile);
   if ((int64_t)ntile * d.B > 0x7fffffff / 2) return MOM_ERR_DIMS;
-  hipStream_t st = (hipStream_t)stream;
+  // part 2 leaves the shared rows and the shared segments' offsets (past M B) to part 1
+  const int last_seg = part == 2 ? d.M * d.B : (d.M + 1) * d.B;
+  const bool shared_rows = part == 0;
   int32_t* cnt = (int32_t*)ws;
   hipLaunchKernelGGL(k_count, dim3(ntile, d.B), dim3(kTile), 0, st, d.B, d.T, d.M, d.topk, ntile, idx, cnt);
   const bool fused = (int64_t)d.M * d.B * ntile <= kFuseScan;
   if (!fused)
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, d.B, d.T, d.M, d.topk, ntile, cnt, seg_off);
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, d.B, d.T, d.M, d.topk, ntile, last_seg, cnt, seg_off);
 #define MOM_SCATTER(XT, F)                                                                                         \
   hipLaunchKernelGGL((k_scatter<XT, F>), dim3(ntile, d.B), dim3(kTile), 0, st, d.B, d.T, d.D, d.H, d.M, d.topk,    \
-                     ntile, idx, cnt, seg_off, alpha, beta, perm, inv, alpha_p, beta_p, (const XT*)x, (XT*)x_packed)
+                     ntile, last_seg, shared_rows, idx, cnt, seg_off, alpha, beta, perm, inv, alpha_p, beta_p,     \
+                     (const XT*)x, (XT*)x_packed)
   if (d.dtype == MOM_DTYPE_BF16) {
     if (fused) MOM_SCATTER(bf16_t, true);
     else MOM_SCATTER(bf16_t, false);
@@ -241,4 +275,21 @@ extern "C" mom_status mom_dispatch(const mom_dims* dims, const int32_t* idx, con
   }
 #undef MOM_SCATTER
   return launch_status();
+}
+}  // namespace mom
+
+extern "C" mom_status mom_dispatch(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
+                                   const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv,
+                                   void* x_packed, float* alpha_p, float* beta_p, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  return mom::dispatch(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_p, beta_p, ws, ws_bytes, 0,
+                       stream);
+}
+
+extern "C" mom_status mom_dispatch_part(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
+                                        const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv,
+                                        void* x_packed, float* alpha_p, float* beta_p, void* ws, size_t ws_bytes,
+                                        int32_t part, void* stream) {
+  return mom::dispatch(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_p, beta_p, ws, ws_bytes, part,
+                       stream);
 }

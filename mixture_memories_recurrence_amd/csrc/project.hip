@@ -25,22 +25,27 @@ namespace mom {
 struct TileJob {
   int kind;        // 0 = query, 1 = key, 2 = value, -1 = none
   int m;           // memory (key/value)
+  bool direct;     // rows are tokens in order (queries, the shared memory): no perm read
   int64_t row0;    // first row of the group (packed row for k/v, token for q)
   int64_t rows;    // rows in the group
   int64_t trow;    // first row of this tile inside the group
   int col0;        // first output column inside the k or v matrix
 };
 
+// Parts of the tile map: 0 = everything; 1 = the queries and the shared
+// memory's keys and values (rows NR .. NR + NT, which are the tokens in order:
+// neither seg_off nor perm is read); 2 = the routed memories' keys and values.
 template <int BM, int BN>
-__device__ TileJob decode_tile(int64_t L, int64_t NT, int M, int B, int HK, int HV,
-                               const int32_t* __restrict__ seg_off) {
+__device__ TileJob decode_tile(int64_t L, int64_t NT, int64_t NR, int M, int B, int HK, int HV,
+                               const int32_t* __restrict__ seg_off, int part) {
   TileJob j;
   j.kind = -1;
   const int qcols = HK / BN;
-  const int64_t qtiles = (int64_t)((NT + BM - 1) / BM) * qcols;
+  const int64_t qtiles = part == 2 ? 0 : (int64_t)((NT + BM - 1) / BM) * qcols;
   if (L < qtiles) {
     j.kind = 0;
     j.m = 0;
+    j.direct = true;
     j.row0 = 0;
     j.rows = NT;
     j.trow = (L / qcols) * BM;
@@ -49,13 +54,14 @@ __device__ TileJob decode_tile(int64_t L, int64_t NT, int M, int B, int HK, int 
   }
   L -= qtiles;
   const int kvcols = (HK + HV) / BN;
-  for (int m = 0; m <= M; ++m) {
-    const int64_t r0 = seg_off[m * B];
-    const int64_t r1 = seg_off[(m + 1) * B];
+  for (int m = part == 1 ? M : 0; m <= (part == 2 ? M - 1 : M); ++m) {
+    const int64_t r0 = m == M ? NR : seg_off[m * B];
+    const int64_t r1 = m == M ? NR + NT : seg_off[(m + 1) * B];
     const int64_t nt = ((r1 - r0 + BM - 1) / BM) * kvcols;
     if (L < nt) {
       const int ct = (int)(L % kvcols);
       j.m = m;
+      j.direct = m == M;
       j.row0 = r0;
       j.rows = r1 - r0;
       j.trow = (L / kvcols) * BM;
@@ -74,11 +80,13 @@ __device__ TileJob decode_tile(int64_t L, int64_t NT, int M, int B, int HK, int 
 }
 
 
-inline int64_t n_tiles_bound(const mom_dims& d, int BM, int BN) {
+inline int64_t n_tiles_bound(const mom_dims& d, int BM, int BN, int part = 0) {
   const Sizes s = sizes_of(d);
+  const int64_t kvc = (d.H * d.dk + d.H * d.dv) / BN;
   const int64_t qt = ((s.NT + BM - 1) / BM) * (d.H * d.dk / BN);
-  const int64_t kvt = ((s.N + BM - 1) / BM + d.M + 1) * ((d.H * d.dk + d.H * d.dv) / BN);
-  return qt + kvt;
+  const int64_t shared = ((s.NT + BM - 1) / BM) * kvc;
+  const int64_t routed = ((s.NR + BM - 1) / BM + d.M) * kvc;
+  return part == 1 ? qt + shared : part == 2 ? routed : qt + shared + routed;
 }
 
 // ------------------------------------------------------------------ bf16 MFMA GEMM
@@ -163,7 +171,7 @@ __device__ __forceinline__ void project_tile(const TileJob& job, bf16_t* smem_l,
     if (R < BM) {
       int64_t gr = job.trow + R;
       if (gr >= job.rows) gr = job.rows - 1;  // rows past the end reuse the last row; never stored
-      const int64_t tok = (job.kind == 0) ? gr : (int64_t)perm[job.row0 + gr];
+      const int64_t tok = job.direct ? gr : (int64_t)perm[job.row0 + gr];
       src[j] = x + tok * D + 8 * c;
     } else {
       src[j] = W + (int64_t)(R - BM) * D + 8 * c;
@@ -366,7 +374,8 @@ __device__ __forceinline__ void project_tile(const TileJob& job, bf16_t* smem_l,
 // n_main + s / SPLIT.
 template <class CF, class CFT>
 __global__ __launch_bounds__(CF::THREADS) void k_project_bf16(
-    int64_t n_main, int64_t NT, int D, int H, int dk, int dv, int M, int B, const bf16_t* __restrict__ x,
+    int64_t n_main, int64_t NT, int64_t NR, int part, int D, int H, int dk, int dv, int M, int B,
+    const bf16_t* __restrict__ x,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ seg_off, const bf16_t* __restrict__ wq,
     const bf16_t* __restrict__ wk, const bf16_t* __restrict__ wv, f16_t* __restrict__ q, f16_t* __restrict__ k,
     f16_t* __restrict__ v) {
@@ -376,12 +385,12 @@ __global__ __launch_bounds__(CF::THREADS) void k_project_bf16(
   const int HK = H * dk, HV = H * dv;
   const int64_t p = blockIdx.x;
   if (p < n_main) {
-    const TileJob job = decode_tile<CF::BM, CF::BN>(xcd_remap(p, n_main), NT, M, B, HK, HV, seg_off);
+    const TileJob job = decode_tile<CF::BM, CF::BN>(xcd_remap(p, n_main), NT, NR, M, B, HK, HV, seg_off, part);
     if (job.kind < 0) return;
     project_tile<CF>(job, smem_l, D, H, dk, dv, x, perm, wq, wk, wv, q, k, v);
   } else {
     const int64_t t = p - n_main;
-    TileJob job = decode_tile<CF::BM, CF::BN>(n_main + t / SPLIT, NT, M, B, HK, HV, seg_off);
+    TileJob job = decode_tile<CF::BM, CF::BN>(n_main + t / SPLIT, NT, NR, M, B, HK, HV, seg_off, part);
     if (job.kind < 0) return;
     job.trow += (t % SPLIT) * CFT::BM;
     if (job.trow >= job.rows) return;  // a sub-tile past the end of the group
@@ -392,7 +401,7 @@ __global__ __launch_bounds__(CF::THREADS) void k_project_bf16(
 template <class CF, class CFT>
 static mom_status launch_project_bf16(const mom_dims& d, const Sizes& z, const void* x, const int32_t* perm,
                                       const int32_t* seg_off, const void* w_q, const void* w_k, const void* w_v,
-                                      void* q, void* k, void* v, hipStream_t st) {
+                                      void* q, void* k, void* v, int part, hipStream_t st) {
   // blocks that fit on the device at once, found once per device
   static int slots_dev = -1, slots = 0;  // benign if two threads race
   int dev = 0;
@@ -413,13 +422,13 @@ static mom_status launch_project_bf16(const mom_dims& d, const Sizes& z, const v
   // which stays on the device); a last round of at most half the slots is cut
   // into sub-tiles.
   constexpr int SPLIT = CF::BM / CFT::BM;
-  const int64_t n_tiles = n_tiles_bound(d, CF::BM, CF::BN);
+  const int64_t n_tiles = n_tiles_bound(d, CF::BM, CF::BN, part);
   const int64_t rem = slots > 0 ? n_tiles % slots : 0;
   const int64_t n_main = (rem > 0 && 2 * rem <= slots) ? n_tiles - rem : n_tiles;
   const int64_t G = n_main + (n_tiles - n_main) * SPLIT;
   static_assert(CF::LDS >= CFT::LDS, "one LDS size serves both tile shapes");
   hipLaunchKernelGGL((k_project_bf16<CF, CFT>), dim3((unsigned)G), dim3(CF::THREADS), CF::LDS, st, n_main, z.NT,
-                     d.D, d.H, d.dk, d.dv, d.M, d.B, (const bf16_t*)x, perm, seg_off, (const bf16_t*)w_q,
+                     z.NR, part, d.D, d.H, d.dk, d.dv, d.M, d.B, (const bf16_t*)x, perm, seg_off, (const bf16_t*)w_q,
                      (const bf16_t*)w_k, (const bf16_t*)w_v, (f16_t*)q, (f16_t*)k, (f16_t*)v);
   return MOM_OK;
 }
@@ -427,7 +436,8 @@ static mom_status launch_project_bf16(const mom_dims& d, const Sizes& z, const v
 // ------------------------------------------------------------------ fp32 VALU GEMM
 constexpr int PF_M = 64, PF_N = 64, PF_K = 16;
 
-__global__ __launch_bounds__(256) void k_project_f32(int64_t NT, int D, int H, int dk, int dv, int M, int B,
+__global__ __launch_bounds__(256) void k_project_f32(int64_t NT, int64_t NR, int part, int D, int H, int dk, int dv,
+                                                     int M, int B,
                                                      const float* __restrict__ x, const int32_t* __restrict__ perm,
                                                      const int32_t* __restrict__ seg_off, const float* __restrict__ wq,
                                                      const float* __restrict__ wk, const float* __restrict__ wv,
@@ -436,7 +446,7 @@ __global__ __launch_bounds__(256) void k_project_f32(int64_t NT, int D, int H, i
   __shared__ float Bs[PF_K][PF_N + 4];
   const int HK = H * dk, HV = H * dv;
   const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
-  const TileJob job = decode_tile<PF_M, PF_N>(L, NT, M, B, HK, HV, seg_off);
+  const TileJob job = decode_tile<PF_M, PF_N>(L, NT, NR, M, B, HK, HV, seg_off, part);
   if (job.kind < 0) return;
   const float* W;
   if (job.kind == 0) W = wq + (int64_t)job.col0 * D;
@@ -446,7 +456,7 @@ __global__ __launch_bounds__(256) void k_project_f32(int64_t NT, int D, int H, i
   const int lr = tid >> 2, lk = (tid & 3) * 4;
   int64_t gr = job.trow + lr;
   if (gr >= job.rows) gr = job.rows - 1;
-  const int64_t tok = (job.kind == 0) ? gr : (int64_t)perm[job.row0 + gr];
+  const int64_t tok = job.direct ? gr : (int64_t)perm[job.row0 + gr];
   const float* a_src = x + tok * D + lk;
   const float* b_src = W + (int64_t)lr * D + lk;
   const int ty = tid >> 4, tx = tid & 15;
@@ -513,15 +523,18 @@ __global__ __launch_bounds__(256) void k_l2norm_rows_f32(int64_t rows, int n, fl
 
 }  // namespace mom
 
-extern "C" mom_status mom_project(const mom_dims* dims, const void* x, const int32_t* perm, const int32_t* seg_off,
-                                  const void* w_q, const void* w_k, const void* w_v, void* q, void* k, void* v,
-                                  void* stream) {
-  using namespace mom;
+namespace mom {
+static mom_status project(const mom_dims* dims, const void* x, const int32_t* perm, const int32_t* seg_off,
+                          const void* w_q, const void* w_k, const void* w_v, void* q, void* k, void* v, int part,
+                          void* stream) {
   mom_status s = check_dims(dims);
   if (s != MOM_OK) return s;
+  if (part < 0 || part > 2) return MOM_ERR_DIMS;
   MOM_CHECK_PTR(x);
-  MOM_CHECK_PTR(perm);
-  MOM_CHECK_PTR(seg_off);
+  if (part != 1) {  // the queries and the shared memory's rows read neither
+    MOM_CHECK_PTR(perm);
+    MOM_CHECK_PTR(seg_off);
+  }
   MOM_CHECK_PTR(w_q);
   MOM_CHECK_PTR(w_k);
   MOM_CHECK_PTR(w_v);
@@ -536,18 +549,34 @@ extern "C" mom_status mom_project(const mom_dims* dims, const void* x, const int
     mom_status r;
     if ((d.H * d.dk) % 256 == 0 && (d.H * d.dv) % 256 == 0 && z.NT >= 4096)
       r = launch_project_bf16<ProjCfg<4, 2, 4, 64, 2>, ProjCfg<4, 2, 1, 64, 2>>(d, z, x, perm, seg_off, w_q, w_k,
-                                                                               w_v, q, k, v, st);
+                                                                               w_v, q, k, v, part, st);
     else
       r = launch_project_bf16<ProjCfg<2, 2, 1, 64, 2>, ProjCfg<2, 2, 1, 64, 2>>(d, z, x, perm, seg_off, w_q, w_k,
-                                                                               w_v, q, k, v, st);
+                                                                               w_v, q, k, v, part, st);
     if (r != MOM_OK) return r;
   } else {
-    const int64_t G = n_tiles_bound(d, PF_M, PF_N);
-    hipLaunchKernelGGL(k_project_f32, dim3((unsigned)G), dim3(256), 0, st, z.NT, d.D, d.H, d.dk, d.dv, d.M, d.B,
-                       (const float*)x, perm, seg_off, (const float*)w_q, (const float*)w_k, (const float*)w_v,
-                       (float*)q, (float*)k, (float*)v);
-    const int64_t rows = z.N * d.H;
-    hipLaunchKernelGGL(k_l2norm_rows_f32, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, rows, d.dk, (float*)k);
+    const int64_t G = n_tiles_bound(d, PF_M, PF_N, part);
+    hipLaunchKernelGGL(k_project_f32, dim3((unsigned)G), dim3(256), 0, st, z.NT, z.NR, part, d.D, d.H, d.dk, d.dv,
+                       d.M, d.B, (const float*)x, perm, seg_off, (const float*)w_q, (const float*)w_k,
+                       (const float*)w_v, (float*)q, (float*)k, (float*)v);
+    // keys of the part's rows: routed rows [0, NR), shared rows [NR, N)
+    const int64_t r0 = part == 1 ? z.NR : 0, r1 = part == 2 ? z.NR : z.N;
+    const int64_t rows = (r1 - r0) * d.H;
+    hipLaunchKernelGGL(k_l2norm_rows_f32, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, rows, d.dk,
+                       (float*)k + r0 * d.H * d.dk);
   }
   return launch_status();
+}
+}  // namespace mom
+
+extern "C" mom_status mom_project(const mom_dims* dims, const void* x, const int32_t* perm, const int32_t* seg_off,
+                                  const void* w_q, const void* w_k, const void* w_v, void* q, void* k, void* v,
+                                  void* stream) {
+  return mom::project(dims, x, perm, seg_off, w_q, w_k, w_v, q, k, v, 0, stream);
+}
+
+extern "C" mom_status mom_project_part(const mom_dims* dims, const void* x, const int32_t* perm,
+                                       const int32_t* seg_off, const void* w_q, const void* w_k, const void* w_v,
+                                       void* q, void* k, void* v, int32_t part, void* stream) {
+  return mom::project(dims, x, perm, seg_off, w_q, w_k, w_v, q, k, v, part, stream);
 }

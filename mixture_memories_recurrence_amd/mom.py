@@ -50,6 +50,8 @@ def lib():
         "mom_route": [D, _VP, _VP, _VP, _VP, _VP, _VP],
         "mom_dispatch": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
         "mom_project": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+        "mom_project_part": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP],
+        "mom_dispatch_part": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _I32, _VP],
         "gdn_chunk_fwd": [D, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                           _VP, ctypes.c_size_t, _VP],
         "gla_chunk_fwd": [D, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -79,7 +81,7 @@ def lib():
     return L
 
 
-EXPORTS = ("mom_route", "mom_dispatch", "mom_project", "gdn_chunk_fwd", "gla_chunk_fwd", "gdn_chunk_bwd",
+EXPORTS = ("mom_route", "mom_dispatch", "mom_dispatch_part", "mom_project", "mom_project_part", "gdn_chunk_fwd", "gla_chunk_fwd", "gdn_chunk_bwd",
            "gla_chunk_bwd", "gdn_decode_step", "gla_decode_step", "mom_combine", "mom_combine_bwd",
            "mom_route_bwd", "mom_dispatch_bwd", "mom_workspace_bytes", "gdn_chunk_workspace_bytes",
            "gdn_chunk_bwd_workspace_bytes", "mom_status_string")
@@ -119,6 +121,22 @@ def mom_dispatch(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_
     _check(lib().mom_dispatch(ctypes.byref(dims), _p(idx), _p(x), _p(alpha), _p(beta), _p(seg_off), _p(perm),
                               _p(inv), _p(x_packed), _p(alpha_p), _p(beta_p), _p(ws), nbytes, _s(stream)),
            "mom_dispatch")
+
+
+PART_ALL, PART_SHARED, PART_ROUTED = 0, 1, 2
+
+
+def mom_dispatch_part(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_p, beta_p, ws, part,
+                      stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().mom_dispatch_part(ctypes.byref(dims), _p(idx), _p(x), _p(alpha), _p(beta), _p(seg_off), _p(perm),
+                                   _p(inv), _p(x_packed), _p(alpha_p), _p(beta_p), _p(ws), nbytes, part, _s(stream)),
+           "mom_dispatch_part")
+
+
+def mom_project_part(dims, x, perm, seg_off, w_q, w_k, w_v, q, k, v, part, stream=None):
+    _check(lib().mom_project_part(ctypes.byref(dims), _p(x), _p(perm), _p(seg_off), _p(w_q), _p(w_k), _p(w_v),
+                                  _p(q), _p(k), _p(v), part, _s(stream)), "mom_project_part")
 
 
 def mom_project(dims, x, perm, seg_off, w_q, w_k, w_v, q, k, v, stream=None):
@@ -259,7 +277,11 @@ class MomLayer:
         n_seg = (c.M + 1) * B
         seg_state = torch.tensor([(s % B) * (c.M + 1) + s // B for s in range(n_seg)], **i32)
         b = dict(
-            dims=dims, NT=NT, NR=NR, N=N, n_seg=n_seg, seg_state=seg_state,
+            dims=dims, B=B, NT=NT, NR=NR, N=N, n_seg=n_seg, seg_state=seg_state,
+            # the shared memory's segments alone (rows NR + b T ..), for the overlapped forward
+            seg_off_s=torch.tensor([NR + i * T for i in range(B + 1)], **i32),
+            seg_state_s=seg_state[c.M * B:].clone(),
+            ws_chunk_s=chunk_workspace(dims, B, N, dev),
             idx=torch.empty(NT, c.K, **i32), w=torch.empty(NT, c.K, **f32),
             seg_off=torch.empty(n_seg + 1, **i32), perm=torch.empty(N, **i32), inv=torch.empty(NT, c.K, **i32),
             alpha_p=torch.empty(N, c.H, **f32), beta_p=torch.empty(N, c.H, **f32),
@@ -278,20 +300,64 @@ class MomLayer:
                      b["beta_p"], b["ws"], stream)
         mom_project(d, x, b["perm"], b["seg_off"], self.w_q, self.w_k, self.w_v, b["q"], b["k"], b["v"], stream)
 
-    def forward(self, x, alpha, beta, state_in=None, state_out=None, B=None, T=None, stream=None):
+    def forward(self, x, alpha, beta, state_in=None, state_out=None, B=None, T=None, stream=None, overlap=True):
         """x [B*T, D], alpha/beta [B*T, H, M+1]; state_in/out [B, M+1, H, dk, dv] fp32.
-        Returns (out [B*T, H, dv] fp32, state_out, buffers)."""
+        Returns (out [B*T, H, dv] fp32, state_out, buffers).
+
+        overlap (default, on the current stream): the shared memory needs no
+        routing, so its rows, the queries with its keys and values, and its
+        recurrence run on a second stream while the main stream routes and
+        dispatches; the routed projection follows the shared one (so the shared
+        recurrence runs beside it), then the routed recurrence; the combine
+        waits for both.  Otherwise (or with an explicit
+        stream) the same steps run in order on one stream."""
         c = self.cfg
         B = c.B if B is None else B
         T = c.T if T is None else T
         b = self.buffers(B, T)
         if state_out is None:
             state_out = torch.empty(B, c.M + 1, c.H, c.dk, c.dv, dtype=torch.float32, device=self.device)
+        if overlap and stream is None:
+            return self._forward_overlapped(x, alpha, beta, b, state_in, state_out)
         self.route_dispatch_project(x, alpha, beta, b, stream)
         chunk = gdn_chunk_fwd if self.rule == "gdn" else gla_chunk_fwd
         chunk(b["dims"], b["n_seg"], b["N"], b["NT"], B * (c.M + 1), b["seg_off"], b["seg_state"], b["perm"],
               b["q"], b["k"], b["v"], b["alpha_p"], b["beta_p"], state_in, state_out, b["o"], b["ws_chunk"], stream)
         mom_combine(b["dims"], b["NT"], b["inv"], b["w"], b["o"], b["o"][b["NR"]:], b["out"], stream)
+        return b["out"], state_out, b
+
+    def _forward_overlapped(self, x, alpha, beta, b, state_in, state_out):
+        c, d = self.cfg, b["dims"]
+        B, N, NT = b["B"], b["N"], b["NT"]
+        n_state = B * (c.M + 1)
+        chunk = gdn_chunk_fwd if self.rule == "gdn" else gla_chunk_fwd
+        main = torch.cuda.current_stream()
+        if getattr(self, "_side", None) is None:
+            self._side = torch.cuda.Stream(device=self.device)  # default priority
+            self._ev = [torch.cuda.Event() for _ in range(3)]
+        side, ev = self._side, self._ev
+        ev[0].record(main)  # inputs ready
+        side.wait_event(ev[0])
+        s = side.cuda_stream
+        mom_dispatch_part(d, None, x, alpha, beta, b["seg_off"], b["perm"], None, None, b["alpha_p"], b["beta_p"],
+                          None, PART_SHARED, s)
+        mom_project_part(d, x, None, None, self.w_q, self.w_k, self.w_v, b["q"], b["k"], b["v"], PART_SHARED, s)
+        ev[1].record(side)  # queries ready
+        chunk(d, B, N, NT, n_state, b["seg_off_s"], b["seg_state_s"], b["perm"], b["q"], b["k"], b["v"], b["alpha_p"],
+              b["beta_p"], state_in, state_out, b["o"], b["ws_chunk_s"], s)
+        ev[2].record(side)  # shared memory done
+        mom_route(d, x, self.w_r, self.bias, b["idx"], b["w"])
+        mom_dispatch_part(d, b["idx"], x, alpha, beta, b["seg_off"], b["perm"], b["inv"], None, b["alpha_p"],
+                          b["beta_p"], b["ws"], PART_ROUTED)
+        # the routed projection starts when the shared one is done, so that the
+        # shared recurrence (a few long chains) runs beside it, not behind it
+        main.wait_event(ev[1])
+        mom_project_part(d, x, b["perm"], b["seg_off"], self.w_q, self.w_k, self.w_v, b["q"], b["k"], b["v"],
+                         PART_ROUTED)
+        chunk(d, c.M * B, N, NT, n_state, b["seg_off"], b["seg_state"], b["perm"], b["q"], b["k"], b["v"],
+              b["alpha_p"], b["beta_p"], state_in, state_out, b["o"], b["ws_chunk"])
+        main.wait_event(ev[2])
+        mom_combine(d, NT, b["inv"], b["w"], b["o"], b["o"][b["NR"]:], b["out"])
         return b["out"], state_out, b
 
     def chunk_backward(self, b, d_o, dstate_out=None, state_in=None, stream=None):

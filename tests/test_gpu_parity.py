@@ -515,3 +515,56 @@ def test_prefill_then_decode():
     last = out_full.reshape(cfg.B, cfg.T, cfg.H, cfg.dv)[:, -1]
     assert_close("decode vs prefill row", out.cpu().numpy(), last, *TOL["bf16"])
     assert_close("decode vs prefill state", states.cpu().numpy(), st_full, *TOL["bf16"])
+
+
+@pytest.mark.parametrize("name,B,T,rule", [("l380m", 8, 2048, "gdn"), ("l380m", 2, 300, "gla"), ("m16", 2, 200, "gdn"),
+                                           ("tiny_f32", 1, 256, "gdn")])
+def test_overlapped_forward_matches_serial(name, B, T, rule):
+    """The forward with the shared memory's path on a second stream gives the
+    same bits as the same steps in order on one stream (the kernels compute
+    every tile and segment the same way in either schedule)."""
+    cfg = dataclasses.replace(synth.CONFIGS[name], B=B, T=T)
+    inp = synth.make_layer_inputs(cfg, seed=31)
+    layer = mom.MomLayer(cfg, inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"], rule=rule)
+    g = gpu_inputs(cfg, inp)
+    x, al, be = g["x"], g["alpha"], g["beta"]
+    S0 = to_gpu((0.1 * np.random.default_rng(32).standard_normal((B, cfg.M + 1, cfg.H, cfg.dk, cfg.dv)))
+                .astype(np.float32))
+    log("overlapped vs serial", name, B, T, rule)
+    out_s, st_s, _ = layer.forward(x, al, be, state_in=S0, overlap=False)
+    out_s, st_s = out_s.clone(), st_s.clone()
+    for _ in range(2):  # twice: the second call reuses the streams and events
+        out_o, st_o, _ = layer.forward(x, al, be, state_in=S0)
+        torch.cuda.synchronize()
+        assert torch.equal(out_o, out_s) and torch.equal(st_o, st_s)
+
+
+def test_dispatch_and_project_parts_equal_whole():
+    """Parts 1 (shared memory) and 2 (routed memories) of mom_dispatch_part and
+    mom_project_part together write exactly what the whole calls write."""
+    cfg = dataclasses.replace(synth.CONFIGS["l380m"], B=3, T=700)
+    inp = synth.make_layer_inputs(cfg, seed=33)
+    layer = make_layer(cfg, inp)
+    g = gpu_inputs(cfg, inp)
+    x, al, be = g["x"], g["alpha"], g["beta"]
+    b = layer.buffers(cfg.B, cfg.T)
+    d = b["dims"]
+    mom.mom_route(d, x, layer.w_r, layer.bias, b["idx"], b["w"])
+    names = ("seg_off", "perm", "inv", "alpha_p", "beta_p", "q", "k", "v")
+    whole = {}
+    mom.mom_dispatch(d, b["idx"], x, al, be, b["seg_off"], b["perm"], b["inv"], None, b["alpha_p"], b["beta_p"], b["ws"])
+    mom.mom_project(d, x, b["perm"], b["seg_off"], layer.w_q, layer.w_k, layer.w_v, b["q"], b["k"], b["v"])
+    torch.cuda.synchronize()
+    for n in names:
+        whole[n] = b[n].clone()
+        b[n].fill_(-7) if b[n].dtype == torch.int32 else b[n].fill_(float("nan"))
+    mom.mom_dispatch_part(d, None, x, al, be, b["seg_off"], b["perm"], None, None, b["alpha_p"], b["beta_p"], None,
+                          mom.PART_SHARED)
+    mom.mom_dispatch_part(d, b["idx"], x, al, be, b["seg_off"], b["perm"], b["inv"], None, b["alpha_p"], b["beta_p"],
+                          b["ws"], mom.PART_ROUTED)
+    mom.mom_project_part(d, x, None, None, layer.w_q, layer.w_k, layer.w_v, b["q"], b["k"], b["v"], mom.PART_SHARED)
+    mom.mom_project_part(d, x, b["perm"], b["seg_off"], layer.w_q, layer.w_k, layer.w_v, b["q"], b["k"], b["v"],
+                         mom.PART_ROUTED)
+    torch.cuda.synchronize()
+    for n in names:
+        assert torch.equal(b[n], whole[n]), n
