@@ -117,7 +117,9 @@ def time_chunk_bwd(cfg, inp, x, alpha, beta, steps, warmup):
     projections run once (forward), then K timed calls of the recurrence's
     gradients alone (gdn_chunk_bwd) and K of the layer's backward (combine,
     recurrence, dispatch gathers, router weights), with random upstream
-    gradients dL/dout and dL/d(final states)."""
+    gradients dL/dout and dL/d(final states).  Then K training steps (forward
+    and backward) twice: with the forward keeping its chunk factors and states
+    for the backward (train=True), and with the backward recomputing them."""
     import torch
     from mixture_memories_recurrence_amd import mom, synth
     layer = mom.MomLayer(cfg, inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"])
@@ -143,6 +145,13 @@ def time_chunk_bwd(cfg, inp, x, alpha, beta, steps, warmup):
 
     ms = timed(lambda: layer.chunk_backward(b, d_o, dstate))
     ms_layer = timed(lambda: layer.backward(x, dout, b, dstate_out=dstate_l))
+
+    def step(train):
+        layer.forward(x, alpha, beta, train=train)
+        layer.backward(x, dout, b, dstate_out=dstate_l)
+
+    ms_saved = timed(lambda: step(True))
+    ms_recompute = timed(lambda: step(False))
     N, NT, H, dk, dv = b["N"], b["NT"], cfg.H, cfg.dk, cfg.dv
     # algorithmic bytes: q (per token), k, v (half), gates, dL/do, dL/dS_out read once;
     # dq, dk, dv, d_alpha, d_beta, dL/dS_in written once (float32)
@@ -155,7 +164,10 @@ def time_chunk_bwd(cfg, inp, x, alpha, beta, steps, warmup):
             "algorithmic_bytes": nbytes, "achieved_gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "layer_bwd": {"workload": "%s layer gradients: combine, recurrence, dispatch gathers, router weights "
                                       "(top-k held fixed); not the projections" % cfg.name,
-                          "ms": round(ms_layer, 4), "tokens_per_s": round(NT / (ms_layer * 1e-3), 1)}}
+                          "ms": round(ms_layer, 4), "tokens_per_s": round(NT / (ms_layer * 1e-3), 1)},
+            "train_step": {"workload": "%s layer forward + the gradients above, one training step" % cfg.name,
+                           "ms_saved": round(ms_saved, 4), "ms_recompute": round(ms_recompute, 4),
+                           "tokens_per_s": round(NT / (ms_saved * 1e-3), 1)}}
 
 
 def time_single_memory(steps, warmup):

@@ -26,6 +26,10 @@
  *                    update rules).
  *   gdn_chunk_bwd    the gradients of gdn_chunk_fwd (and gla_chunk_bwd of
  *                    gla_chunk_fwd), for training.
+ *   gdn_chunk_fwd_train, gdn_chunk_bwd_saved
+ *                    the same forward and gradients split for a training
+ *                    step: the forward keeps its chunk factors and states for
+ *                    the backward, which then does not recompute them.
  *   gdn_decode_step  one recurrent step per sequence (constant-cost inference,
  *                    jxzklqfsx.com write-up, introduction and inference section).
  *   mom_combine      router-weighted sum of the per-memory reads plus the
@@ -242,6 +246,51 @@ mom_status gla_chunk_bwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, in
                          float* d_alpha, float* d_beta, float* dstate_in, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* The forward pass of a training step: the outputs of gdn_chunk_fwd (same
+ * arguments, layouts and errors; half storage only, as gdn_chunk_bwd), and ws,
+ * which must hold gdn_chunk_bwd_workspace_bytes(dims, n_seg, n_rows) bytes,
+ * keeps what gdn_chunk_bwd_saved reads: each chunk's solved triangular factor,
+ * its inverse, the masked query-key products, the decay prefix sums and the
+ * state entering the chunk.  o and state_out equal gdn_chunk_fwd's bit for
+ * bit. */
+mom_status gdn_chunk_fwd_train(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
+                               int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
+                               const int32_t* row_token, const void* q, const void* k, const void* v,
+                               const float* alpha_p, const float* beta_p, const float* state_in,
+                               float* state_out, float* o, void* ws, size_t ws_bytes, void* stream);
+
+/* gla_chunk_fwd_train: gla_chunk_fwd's outputs, with ws kept as in
+ * gdn_chunk_fwd_train. */
+mom_status gla_chunk_fwd_train(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
+                               int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
+                               const int32_t* row_token, const void* q, const void* k, const void* v,
+                               const float* alpha_p, const float* beta_p, const float* state_in,
+                               float* state_out, float* o, void* ws, size_t ws_bytes, void* stream);
+
+/* gdn_chunk_bwd_saved: gdn_chunk_bwd when ws still holds what
+ * gdn_chunk_fwd_train wrote for the same dims, segments, slots, rows, inputs
+ * and state_in (the caller keeps them unchanged in between); it skips the
+ * factor and state recomputation and its results equal gdn_chunk_bwd's bit
+ * for bit.  Arguments, layouts and errors as gdn_chunk_bwd; ws is read and
+ * then overwritten, so one training forward serves one backward. */
+mom_status gdn_chunk_bwd_saved(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
+                               int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
+                               const int32_t* row_token, const void* q, const void* k, const void* v,
+                               const float* alpha_p, const float* beta_p, const float* state_in,
+                               const float* d_o, const float* dstate_out, float* dq, float* dk,
+                               float* dv, float* d_alpha, float* d_beta, float* dstate_in, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* gla_chunk_bwd_saved: gdn_chunk_bwd_saved for gla_chunk_fwd_train's
+ * workspace. */
+mom_status gla_chunk_bwd_saved(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
+                               int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
+                               const int32_t* row_token, const void* q, const void* k, const void* v,
+                               const float* alpha_p, const float* beta_p, const float* state_in,
+                               const float* d_o, const float* dstate_out, float* dq, float* dk,
+                               float* dv, float* d_alpha, float* d_beta, float* dstate_in, void* ws,
+                               size_t ws_bytes, void* stream);
+
 /* One recurrent step for n_seq sequences with one new token each (T = 1 view:
  * rows as written by mom_dispatch/mom_project for dims with B = n_seq, T = 1).
  * For sequence b and slot j < topk the memory is idx[b][j] and the packed row
@@ -323,9 +372,9 @@ size_t mom_workspace_bytes(const mom_dims* dims, int32_t which);
 size_t gdn_chunk_workspace_bytes(const mom_dims* dims, int32_t n_seg, int32_t n_rows);
 
 /* Workspace bytes gdn_chunk_bwd / gla_chunk_bwd need for n_seg segments over
- * n_rows packed rows: the forward's per-chunk factors, X = (I + A)^{-1} in
- * float32, and the states entering and the state gradients leaving every
- * chunk (half).  0 for invalid arguments or float32 storage. */
+ * n_rows packed rows: the forward's per-chunk factors, X = (I + A)^{-1}, and
+ * the states entering and the state gradients leaving every chunk (all
+ * half but the float32 decay sums).  0 for invalid arguments or float32 storage. */
 size_t gdn_chunk_bwd_workspace_bytes(const mom_dims* dims, int32_t n_seg, int32_t n_rows);
 
 /* Static text for a status code. */

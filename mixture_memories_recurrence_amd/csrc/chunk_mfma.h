@@ -88,6 +88,39 @@ __device__ __forceinline__ h8v acc_to_b(const f16x16& d, int p, const float* sc)
   return __builtin_bit_cast(h8v, *reinterpret_cast<const __attribute__((ext_vector_type(4))) unsigned*>(w4));
 }
 
+// A wave's 32 value columns of a DK x dv state (accumulator tiles S[a], rows
+// 32 a + 8 (i / 4) + 4 g + i % 4 of this lane's column), stored as half,
+// transposed (each column's DK key rows contiguous) at dst = the wave's first
+// column.  The columns are contiguous, so the wave's piece is one DK x 64-byte
+// run; it goes out through the wave's 4 KB LDS tile in rounds of 64 key rows,
+// and each of a round's 4 stores writes 8 whole 128-byte lines rather than 32
+// separate 16-byte pieces.  Piece c (16 bytes) of column r sits at tile
+// position c ^ (r & 7), so that neither the 8-byte writes nor the 16-byte reads
+// conflict.  The tile must not be in use by other code of the wave meanwhile.
+template <int DK>
+__device__ __forceinline__ void store_state_t(f16_t* __restrict__ dst, const f16x16* S, f16_t* tile, int lane) {
+  const int c32 = lane & 31, g2 = lane >> 5;
+#pragma unroll
+  for (int rd = 0; rd < DK / 64; ++rd) {
+#pragma unroll
+    for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const f16x16& t = S[2 * rd + a2];
+        const u2v pc = {pack_h2(t[4 * qq], t[4 * qq + 1]), pack_h2(t[4 * qq + 2], t[4 * qq + 3])};
+        *reinterpret_cast<u2v*>(tile + 64 * c32 + 8 * ((4 * a2 + qq) ^ (c32 & 7)) + 4 * g2) = pc;
+      }
+    wave_lds_fence();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = 8 * j + (lane >> 3), pcs = lane & 7;
+      const h8v val = *reinterpret_cast<const h8v*>(tile + 64 * col + 8 * (pcs ^ (col & 7)));
+      *reinterpret_cast<h8v*>(dst + (int64_t)col * DK + 64 * rd + 8 * pcs) = val;
+    }
+    wave_lds_fence();  // read before the next round (or other code) overwrites the tile
+  }
+}
+
 // Asynchronous global -> LDS copies (global_load_lds_dwordx4 / _dword): lane
 // l's 16 (4) bytes land at lds_base + 16 l (4 l); lds_base must be the same in
 // every lane.  They are issued from inline assembly so that the compiler, which

@@ -32,6 +32,10 @@
 //                      matrix-core accumulators; stores dS' of every chunk
 //                      (transposed half) and dL/d(entering state)
 //   k_gdn_grad         one block per (chunk, head): everything else
+// A training step can skip the first two: gdn_chunk_fwd_train runs the forward
+// pass with the prep that also writes X and a walk that also stores the
+// states (k_gdn_chain mode 2), into this workspace, and gdn_chunk_bwd_saved
+// then starts at the reverse walk.
 #include "chunk_mfma.h"
 
 namespace mom {
@@ -39,7 +43,8 @@ namespace mom {
 mom_status launch_chunk_states(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
                                const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
                                const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
-                               const ChunkWs& W, f16_t* Xws, f16_t* hws, bool delta, hipStream_t st);
+                               float* state_out, float* o, const ChunkWs& W, f16_t* Xws, f16_t* hws, bool delta,
+                               bool with_output, hipStream_t st);
 
 // ------------------------------------------------------------------ reverse chain
 // One block per (segment, head, DVB = 32 NW value columns), NW waves, mapped to
@@ -58,7 +63,9 @@ struct ChainBwdLds {
   static constexpr int OFF_K = 0, OFF_Q = GC * DK, OFF_T = 2 * GC * DK, OFF_P = OFF_T + GC * GC,
                        OFF_E = OFF_P + GC * GC, OFF_TOK = OFF_E + 2 * 2 * GC;
   static constexpr int BUF = OFF_TOK + 2 * GC;  // halfs per buffer
-  static constexpr size_t BYTES = (size_t)2 * BUF * sizeof(f16_t);
+  // after the two buffers: one 4 KB tile per wave for the dS' stores
+  static constexpr size_t OST = (size_t)2 * BUF * sizeof(f16_t);
+  static constexpr size_t BYTES = OST + (size_t)NW * 4096;
 };
 
 template <int DK, int NW, bool DELTA>
@@ -211,18 +218,9 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain_bwd(
     const int64_t rnext = ci > 0 ? r0 - GC : r0;
     pf_setup(rnext, buf ^ 1, reinterpret_cast<const int32_t*>(Bc + LY::OFF_TOK));
     if (ci > 0) load_do(rnext);
-    // dS' of this chunk, transposed: key rows 32 a + 8 qq + 4 g + 0..3 of this
-    // lane's column as one 8-byte piece
-    {
-      f16_t* hc = dhws + ((int64_t)(cbase + ci) * H + h) * dv * DK + (int64_t)(ncol0 + c32) * DK;
-#pragma unroll
-      for (int a = 0; a < ND; ++a)
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const u2v pc = {pack_h2(dS[a][4 * qq], dS[a][4 * qq + 1]), pack_h2(dS[a][4 * qq + 2], dS[a][4 * qq + 3])};
-          *reinterpret_cast<u2v*>(hc + 32 * a + 8 * qq + 4 * g2) = pc;
-        }
-    }
+    // dS' of this chunk, transposed, through the wave's tile
+    store_state_t<DK>(dhws + ((int64_t)(cbase + ci) * H + h) * dv * DK + (int64_t)ncol0 * DK, dS,
+                      reinterpret_cast<f16_t*>(reinterpret_cast<char*>(smem) + LY::OST) + 2048 * w, lane);
 
     // ---- Z = K dS (two 32-row tiles)
     f16x16 Z[2], dU[2];
@@ -866,11 +864,14 @@ static mom_status launch_bwd(const mom_dims& d, int n_seg, int n_rows, const int
                              const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
                              const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
                              const float* d_o, const float* dstate_out, float* dq, float* dk, float* dv, float* da,
-                             float* dc, float* dstate_in, void* ws, hipStream_t st) {
+                             float* dc, float* dstate_in, void* ws, bool saved, hipStream_t st) {
   const ChunkBwdWs W = chunk_bwd_ws_layout(ws, n_seg, n_rows, d.H, d.dk, d.dv);
-  mom_status r = launch_chunk_states(d, n_seg, n_rows, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
-                                     state_in, W.fw, W.X, W.h, DELTA, st);
-  if (r != MOM_OK) return r;
+  mom_status r = MOM_OK;
+  if (!saved) {  // otherwise the workspace holds the forward's factors and states
+    r = launch_chunk_states(d, n_seg, n_rows, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p, state_in,
+                            nullptr, nullptr, W.fw, W.X, W.h, DELTA, false, st);
+    if (r != MOM_OK) return r;
+  }
   r = d.dv % 128 == 0
           ? launch_chain_bwd<DK, 4, DELTA>(d, n_seg, seg_off, seg_state, W, row_token, q, k, d_o, dstate_out,
                                            dstate_in, st)
@@ -899,8 +900,8 @@ static size_t chunk_bwd_ws_bytes(const mom_dims* dims, int32_t n_seg, int32_t n_
   return chunk_bwd_ws_layout(nullptr, n_seg, n_rows, dims->H, dims->dk, dims->dv).bytes;
 }
 
-static mom_status chunk_bwd(bool delta, const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
-                            int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
+static mom_status chunk_bwd(bool delta, bool saved, const mom_dims* dims, int32_t n_seg, int32_t n_rows,
+                            int32_t n_tok, int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
                             const int32_t* row_token, const void* q, const void* k, const void* v,
                             const float* alpha_p, const float* beta_p, const float* state_in, const float* d_o,
                             const float* dstate_out, float* dq, float* dk, float* dv, float* da, float* dc,
@@ -936,10 +937,44 @@ static mom_status chunk_bwd(bool delta, const mom_dims* dims, int32_t n_seg, int
   hipStream_t st = (hipStream_t)stream;
 #define MOM_BWD(DK, DELTA)                                                                                       \
   launch_bwd<DK, DELTA>(*dims, n_seg, n_rows, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p, state_in, \
-                        d_o, dstate_out, dq, dk, dv, da, dc, dstate_in, ws, st)
+                        d_o, dstate_out, dq, dk, dv, da, dc, dstate_in, ws, saved, st)
   if (dims->dk == 64) return delta ? MOM_BWD(64, true) : MOM_BWD(64, false);
   return delta ? MOM_BWD(128, true) : MOM_BWD(128, false);
 #undef MOM_BWD
+}
+
+// The forward pass of a training step: as gdn_chunk_fwd, and the gradient
+// workspace keeps T, P, the decays, X and the chunk-entry states.
+static mom_status chunk_fwd_train(bool delta, const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
+                                  int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
+                                  const int32_t* row_token, const void* q, const void* k, const void* v,
+                                  const float* alpha_p, const float* beta_p, const float* state_in, float* state_out,
+                                  float* o, void* ws, size_t ws_bytes, void* stream) {
+  mom_status s = check_dims(dims);
+  if (s != MOM_OK) return s;
+  if (dims->dtype != MOM_DTYPE_BF16) return MOM_ERR_UNSUPPORTED;
+  if (n_seg < 0 || n_rows < 0 || n_tok < 0 || n_state < 0) return MOM_ERR_DIMS;
+  if (!seg_state && n_state < n_seg) return MOM_ERR_DIMS;
+  MOM_CHECK_PTR(seg_off);
+  MOM_CHECK_OPT_PTR(seg_state);
+  MOM_CHECK_OPT_PTR(row_token);
+  MOM_CHECK_OPT_PTR(state_in);
+  MOM_CHECK_PTR(state_out);
+  if (n_rows > 0) {
+    MOM_CHECK_PTR(q);
+    MOM_CHECK_PTR(k);
+    MOM_CHECK_PTR(v);
+    MOM_CHECK_PTR(alpha_p);
+    MOM_CHECK_PTR(beta_p);
+    MOM_CHECK_PTR(o);
+  }
+  if (!ws || ws_bytes < chunk_bwd_ws_bytes(dims, n_seg, n_rows)) return MOM_ERR_WORKSPACE;
+  MOM_CHECK_PTR(ws);
+  if (n_seg == 0) return MOM_OK;
+  const mom_dims& d = *dims;
+  const ChunkBwdWs W = chunk_bwd_ws_layout(ws, n_seg, n_rows, d.H, d.dk, d.dv);
+  return launch_chunk_states(d, n_seg, n_rows, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p, state_in,
+                             state_out, o, W.fw, W.X, W.h, delta, true, (hipStream_t)stream);
 }
 
 }  // namespace mom
@@ -955,9 +990,9 @@ extern "C" mom_status gdn_chunk_bwd(const mom_dims* dims, int32_t n_seg, int32_t
                                     const float* d_o, const float* dstate_out, float* dq, float* dk, float* dv,
                                     float* d_alpha, float* d_beta, float* dstate_in, void* ws, size_t ws_bytes,
                                     void* stream) {
-  return mom::chunk_bwd(true, dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v, alpha_p,
-                        beta_p, state_in, d_o, dstate_out, dq, dk, dv, d_alpha, d_beta, dstate_in, ws, ws_bytes,
-                        stream);
+  return mom::chunk_bwd(true, false, dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v,
+                        alpha_p, beta_p, state_in, d_o, dstate_out, dq, dk, dv, d_alpha, d_beta, dstate_in, ws,
+                        ws_bytes, stream);
 }
 
 extern "C" mom_status gla_chunk_bwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
@@ -967,7 +1002,40 @@ extern "C" mom_status gla_chunk_bwd(const mom_dims* dims, int32_t n_seg, int32_t
                                     const float* d_o, const float* dstate_out, float* dq, float* dk, float* dv,
                                     float* d_alpha, float* d_beta, float* dstate_in, void* ws, size_t ws_bytes,
                                     void* stream) {
-  return mom::chunk_bwd(false, dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v,
+  return mom::chunk_bwd(false, false, dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v,
                         alpha_p, beta_p, state_in, d_o, dstate_out, dq, dk, dv, d_alpha, d_beta, dstate_in, ws,
                         ws_bytes, stream);
 }
+
+#define MOM_FWD_TRAIN_ARGS                                                                                        \
+  const mom_dims *dims, int32_t n_seg, int32_t n_rows, int32_t n_tok, int32_t n_state, const int32_t *seg_off,   \
+      const int32_t *seg_state, const int32_t *row_token, const void *q, const void *k, const void *v,           \
+      const float *alpha_p, const float *beta_p, const float *state_in, float *state_out, float *o, void *ws,     \
+      size_t ws_bytes, void *stream
+extern "C" mom_status gdn_chunk_fwd_train(MOM_FWD_TRAIN_ARGS) {
+  return mom::chunk_fwd_train(true, dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v,
+                              alpha_p, beta_p, state_in, state_out, o, ws, ws_bytes, stream);
+}
+extern "C" mom_status gla_chunk_fwd_train(MOM_FWD_TRAIN_ARGS) {
+  return mom::chunk_fwd_train(false, dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v,
+                              alpha_p, beta_p, state_in, state_out, o, ws, ws_bytes, stream);
+}
+#undef MOM_FWD_TRAIN_ARGS
+
+#define MOM_BWD_ARGS                                                                                              \
+  const mom_dims *dims, int32_t n_seg, int32_t n_rows, int32_t n_tok, int32_t n_state, const int32_t *seg_off,   \
+      const int32_t *seg_state, const int32_t *row_token, const void *q, const void *k, const void *v,           \
+      const float *alpha_p, const float *beta_p, const float *state_in, const float *d_o,                        \
+      const float *dstate_out, float *dq, float *dk, float *dv, float *d_alpha, float *d_beta, float *dstate_in,  \
+      void *ws, size_t ws_bytes, void *stream
+extern "C" mom_status gdn_chunk_bwd_saved(MOM_BWD_ARGS) {
+  return mom::chunk_bwd(true, true, dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v,
+                        alpha_p, beta_p, state_in, d_o, dstate_out, dq, dk, dv, d_alpha, d_beta, dstate_in, ws,
+                        ws_bytes, stream);
+}
+extern "C" mom_status gla_chunk_bwd_saved(MOM_BWD_ARGS) {
+  return mom::chunk_bwd(false, true, dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v,
+                        alpha_p, beta_p, state_in, d_o, dstate_out, dq, dk, dv, d_alpha, d_beta, dstate_in, ws,
+                        ws_bytes, stream);
+}
+#undef MOM_BWD_ARGS

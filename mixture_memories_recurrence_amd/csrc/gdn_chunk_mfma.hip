@@ -43,9 +43,11 @@ namespace mom {
 // exchanged between waves, so the only block barrier per chunk publishes the
 // next chunk's inputs, which every wave prefetches into the idle half of a
 // double buffer with asynchronous global -> LDS copies.
-// With SAVE the kernel only walks the states, for the gradients: it stores the
-// state entering every chunk (transposed, half: hws[chunk][head][dv][DK]) and
-// skips the read-out (no Q, P or O); state_out may then be null.
+// MODE 0 is the forward pass.  For the gradients, MODE 1 only walks the
+// states: it stores the state entering every chunk (transposed, half:
+// hws[chunk][head][dv][DK]) and skips the read-out (no Q, P or O; state_out may
+// then be null); MODE 2 does both, the forward pass of a training step that
+// keeps the states for the backward pass.
 template <int DK, int NW>
 struct ChainLds {
   static constexpr int DVB = 32 * NW;
@@ -57,7 +59,7 @@ struct ChainLds {
   static constexpr size_t BYTES = OST + (size_t)NW * 32 * 32 * sizeof(float);
 };
 
-template <int DK, int NW, bool DELTA, bool SAVE>
+template <int DK, int NW, bool DELTA, int MODE>
 __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     int H, int dv, int n_seg, const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_state,
     const f16_t* __restrict__ k, const f16_t* __restrict__ v,
@@ -66,6 +68,8 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     float* __restrict__ state_out, float* __restrict__ o, f16_t* __restrict__ hws) {
   using LY = ChainLds<DK, NW>;
   constexpr int DVB = LY::DVB, ND = DK / 32, NKD = DK / 16;
+  constexpr bool SAVE = MODE == 1;            // states only
+  constexpr bool STORE_H = MODE != 0;         // the chunk-entry states are stored
   extern __shared__ __attribute__((aligned(16))) f16_t smem[];
 
   // Blocks of a (segment, head) group are dealt round-robin over the 8 XCDs
@@ -197,18 +201,9 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     const f16_t* Ts = Bc + LY::OFF_T;
     const f16_t* Ps = Bc + LY::OFF_P;
     const float* Eg = reinterpret_cast<const float*>(Bc + LY::OFF_E);  // gamma_i, then gamma_L / gamma_i
-    if constexpr (SAVE) {
-      // the entering state, transposed: this lane's column, key rows
-      // 32 a + 8 qq + 4 g + 0..3 as one 8-byte piece
-      f16_t* hc = hws + ((int64_t)(cbase + (r0 - rbeg) / GC) * H + h) * dv * DK + (int64_t)(ncol0 + c32) * DK;
-#pragma unroll
-      for (int a = 0; a < ND; ++a)
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const u2v pc = {pack_h2(S[a][4 * qq], S[a][4 * qq + 1]), pack_h2(S[a][4 * qq + 2], S[a][4 * qq + 3])};
-          *reinterpret_cast<u2v*>(hc + 32 * a + 8 * qq + 4 * g2) = pc;
-        }
-    }
+    if constexpr (STORE_H)  // the entering state, transposed, through the wave's output tile
+      store_state_t<DK>(hws + ((int64_t)(cbase + (r0 - rbeg) / GC) * H + h) * dv * DK + (int64_t)ncol0 * DK, S,
+                        reinterpret_cast<f16_t*>(ost), lane);
 
     // ---- Y = K S and O^T = S^T Q^T, two 32-row tiles each (four chains); the
     // state becomes an operand (k = key rows) one 16-row block at a time
@@ -580,7 +575,7 @@ size_t gdn_chunk_ws_bytes(int64_t n_seg, int64_t n_rows, int H, int dk) {
   return chunk_ws_layout(nullptr, n_seg, n_rows, H, dk).bytes;
 }
 
-template <int DK, int NW, bool DELTA, bool SAVE>
+template <int DK, int NW, bool DELTA, int MODE>
 static mom_status launch_chain(const mom_dims& d, int n_seg, const int32_t* seg_off, const int32_t* seg_state,
                                const ChunkWs& W, const int32_t* row_token, const void* q, const void* k,
                                const void* v, const float* state_in, float* state_out, float* o, f16_t* hws,
@@ -588,14 +583,14 @@ static mom_status launch_chain(const mom_dims& d, int n_seg, const int32_t* seg_
   using LY = ChainLds<DK, NW>;
   static bool attr = false;  // the dynamic LDS limit is raised once per kernel
   if (!attr) {
-    if (hipFuncSetAttribute((const void*)k_gdn_chain<DK, NW, DELTA, SAVE>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    if (hipFuncSetAttribute((const void*)k_gdn_chain<DK, NW, DELTA, MODE>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)LY::BYTES) != hipSuccess)
       return MOM_ERR_LAUNCH;
     attr = true;
   }
   const int64_t blocks = (int64_t)n_seg * d.H * (d.dv / LY::DVB);
   if (blocks > 0)
-    hipLaunchKernelGGL((k_gdn_chain<DK, NW, DELTA, SAVE>), dim3((unsigned)blocks), dim3(64 * NW), LY::BYTES, st,
+    hipLaunchKernelGGL((k_gdn_chain<DK, NW, DELTA, MODE>), dim3((unsigned)blocks), dim3(64 * NW), LY::BYTES, st,
                        d.H, d.dv, n_seg, seg_off, seg_state, (const f16_t*)k, (const f16_t*)v, W.T, W.P, W.E,
                        row_token, (const f16_t*)q, state_in, state_out, o, hws);
   return MOM_OK;
@@ -615,10 +610,10 @@ static mom_status launch_chunk(const mom_dims& d, int n_seg, int n_rows, const i
                        nullptr);
   const mom_status r =
       d.dv % 128 == 0
-          ? launch_chain<DK, 4, DELTA, false>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in,
-                                              state_out, o, nullptr, st)
-          : launch_chain<DK, 2, DELTA, false>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in,
-                                              state_out, o, nullptr, st);
+          ? launch_chain<DK, 4, DELTA, 0>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in,
+                                          state_out, o, nullptr, st)
+          : launch_chain<DK, 2, DELTA, 0>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in,
+                                          state_out, o, nullptr, st);
   if (r != MOM_OK) return r;
   return launch_status();
 }
@@ -644,32 +639,43 @@ mom_status launch_gdn_chunk_mfma(const mom_dims& d, int n_seg, int n_rows, const
 // For the gradients: prep (with X = (I + A)^{-1} in float32 for Gated DeltaNet)
 // and the state walk that stores the state entering every chunk (transposed,
 // half) in hws, without the read-out.
-template <int DK, bool DELTA>
+template <int DK, bool DELTA, int MODE>
 static mom_status launch_states(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
                                 const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
                                 const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
-                                const ChunkWs& W, f16_t* Xws, f16_t* hws, hipStream_t st) {
+                                float* state_out, float* o, const ChunkWs& W, f16_t* Xws, f16_t* hws,
+                                hipStream_t st) {
   const int64_t nch = (int64_t)n_rows / GC + n_seg;
   const int64_t prep_blocks = (nch * d.H + 3) / 4;
   if (prep_blocks > 0)
     hipLaunchKernelGGL((k_gdn_prep<DK, DELTA>), dim3((unsigned)prep_blocks), dim3(256), 0, st, d.H, n_seg,
                        seg_off, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.E,
                        DELTA ? Xws : nullptr);
-  return d.dv % 128 == 0 ? launch_chain<DK, 4, DELTA, true>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v,
-                                                             state_in, nullptr, nullptr, hws, st)
-                         : launch_chain<DK, 2, DELTA, true>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v,
-                                                             state_in, nullptr, nullptr, hws, st);
+  const mom_status r =
+      d.dv % 128 == 0 ? launch_chain<DK, 4, DELTA, MODE>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in,
+                                                         state_out, o, hws, st)
+                      : launch_chain<DK, 2, DELTA, MODE>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in,
+                                                         state_out, o, hws, st);
+  return r != MOM_OK ? r : launch_status();
 }
 
+// with_output: also the forward's read-out and final states (a training
+// step's forward pass); otherwise the states only (recomputed for the
+// gradients).
 mom_status launch_chunk_states(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
                                const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
                                const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
-                               const ChunkWs& W, f16_t* Xws, f16_t* hws, bool delta, hipStream_t st) {
-#define MOM_STATES(DK, DELTA) \
-  launch_states<DK, DELTA>(d, n_seg, n_rows, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p, state_in, W, \
-                           Xws, hws, st)
-  if (d.dk == 64) return delta ? MOM_STATES(64, true) : MOM_STATES(64, false);
-  return delta ? MOM_STATES(128, true) : MOM_STATES(128, false);
+                               float* state_out, float* o, const ChunkWs& W, f16_t* Xws, f16_t* hws, bool delta,
+                               bool with_output, hipStream_t st) {
+#define MOM_STATES(DK, DELTA, MODE)                                                                                 \
+  launch_states<DK, DELTA, MODE>(d, n_seg, n_rows, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,       \
+                                 state_in, state_out, o, W, Xws, hws, st)
+  if (with_output) {
+    if (d.dk == 64) return delta ? MOM_STATES(64, true, 2) : MOM_STATES(64, false, 2);
+    return delta ? MOM_STATES(128, true, 2) : MOM_STATES(128, false, 2);
+  }
+  if (d.dk == 64) return delta ? MOM_STATES(64, true, 1) : MOM_STATES(64, false, 1);
+  return delta ? MOM_STATES(128, true, 1) : MOM_STATES(128, false, 1);
 #undef MOM_STATES
 }
 

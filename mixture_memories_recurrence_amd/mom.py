@@ -58,6 +58,10 @@ def lib():
                           _VP, ctypes.c_size_t, _VP],
         "gdn_chunk_bwd": [D, _I32, _I32, _I32, _I32] + [_VP] * 18 + [ctypes.c_size_t, _VP],
         "gla_chunk_bwd": [D, _I32, _I32, _I32, _I32] + [_VP] * 18 + [ctypes.c_size_t, _VP],
+        "gdn_chunk_fwd_train": [D, _I32, _I32, _I32, _I32] + [_VP] * 12 + [ctypes.c_size_t, _VP],
+        "gla_chunk_fwd_train": [D, _I32, _I32, _I32, _I32] + [_VP] * 12 + [ctypes.c_size_t, _VP],
+        "gdn_chunk_bwd_saved": [D, _I32, _I32, _I32, _I32] + [_VP] * 18 + [ctypes.c_size_t, _VP],
+        "gla_chunk_bwd_saved": [D, _I32, _I32, _I32, _I32] + [_VP] * 18 + [ctypes.c_size_t, _VP],
         "gdn_chunk_bwd_workspace_bytes": [D, _I32, _I32],
         "gdn_decode_step": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
         "gla_decode_step": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
@@ -81,10 +85,11 @@ def lib():
     return L
 
 
-EXPORTS = ("mom_route", "mom_dispatch", "mom_dispatch_part", "mom_project", "mom_project_part", "gdn_chunk_fwd", "gla_chunk_fwd", "gdn_chunk_bwd",
-           "gla_chunk_bwd", "gdn_decode_step", "gla_decode_step", "mom_combine", "mom_combine_bwd",
-           "mom_route_bwd", "mom_dispatch_bwd", "mom_workspace_bytes", "gdn_chunk_workspace_bytes",
-           "gdn_chunk_bwd_workspace_bytes", "mom_status_string")
+EXPORTS = ("mom_route", "mom_dispatch", "mom_dispatch_part", "mom_project", "mom_project_part", "gdn_chunk_fwd",
+           "gla_chunk_fwd", "gdn_chunk_bwd", "gla_chunk_bwd", "gdn_chunk_fwd_train", "gla_chunk_fwd_train",
+           "gdn_chunk_bwd_saved", "gla_chunk_bwd_saved", "gdn_decode_step", "gla_decode_step", "mom_combine",
+           "mom_combine_bwd", "mom_route_bwd", "mom_dispatch_bwd", "mom_workspace_bytes",
+           "gdn_chunk_workspace_bytes", "gdn_chunk_bwd_workspace_bytes", "mom_status_string")
 
 
 def dims_of(cfg: LayerConfig, B: int | None = None, T: int | None = None) -> MomDims:
@@ -159,6 +164,27 @@ def gla_chunk_fwd(dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_t
     _check(lib().gla_chunk_fwd(ctypes.byref(dims), n_seg, n_rows, n_tok, n_state, _p(seg_off), _p(seg_state),
                                _p(row_token), _p(q), _p(k), _p(v), _p(alpha_p), _p(beta_p), _p(state_in),
                                _p(state_out), _p(o), _p(ws), nbytes, _s(stream)), "gla_chunk_fwd")
+
+
+def chunk_fwd_train(rule, dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v, alpha_p,
+                    beta_p, state_in, state_out, o, ws, stream=None):
+    """gdn_chunk_fwd_train (rule "gdn") or gla_chunk_fwd_train (rule "gla"): the
+    forward's outputs, and ws (gdn_chunk_bwd_workspace_bytes) keeps its chunk
+    factors and states for chunk_bwd_saved."""
+    name = {"gdn": "gdn_chunk_fwd_train", "gla": "gla_chunk_fwd_train"}[rule]
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(getattr(lib(), name)(ctypes.byref(dims), n_seg, n_rows, n_tok, n_state, _p(seg_off), _p(seg_state),
+                                _p(row_token), _p(q), _p(k), _p(v), _p(alpha_p), _p(beta_p), _p(state_in),
+                                _p(state_out), _p(o), _p(ws), nbytes, _s(stream)), name)
+
+
+def chunk_bwd_saved(rule, dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v, alpha_p,
+                    beta_p, state_in, d_o, dstate_out, dq, dk, dv, d_alpha, d_beta, dstate_in, ws, stream=None):
+    """gdn_chunk_bwd_saved / gla_chunk_bwd_saved: the gradients, from the ws a
+    chunk_fwd_train call of the same rule and inputs left."""
+    name = {"gdn": "gdn_chunk_bwd_saved", "gla": "gla_chunk_bwd_saved"}[rule]
+    _chunk_bwd(name, dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
+               state_in, d_o, dstate_out, dq, dk, dv, d_alpha, d_beta, dstate_in, ws, stream)
 
 
 def _chunk_bwd(name, dims, n_seg, n_rows, n_tok, n_state, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p,
@@ -300,9 +326,14 @@ class MomLayer:
                      b["beta_p"], b["ws"], stream)
         mom_project(d, x, b["perm"], b["seg_off"], self.w_q, self.w_k, self.w_v, b["q"], b["k"], b["v"], stream)
 
-    def forward(self, x, alpha, beta, state_in=None, state_out=None, B=None, T=None, stream=None, overlap=True):
+    def forward(self, x, alpha, beta, state_in=None, state_out=None, B=None, T=None, stream=None, overlap=True,
+                train=False):
         """x [B*T, D], alpha/beta [B*T, H, M+1]; state_in/out [B, M+1, H, dk, dv] fp32.
         Returns (out [B*T, H, dv] fp32, state_out, buffers).
+
+        train: the recurrence runs as chunk_fwd_train (same outputs, bit for
+        bit) and keeps its chunk factors and states for the next backward(),
+        which then skips recomputing them.
 
         overlap (default, on the current stream): the shared memory needs no
         routing, so its rows, the queries with its keys and values, and its
@@ -317,25 +348,33 @@ class MomLayer:
         b = self.buffers(B, T)
         if state_out is None:
             state_out = torch.empty(B, c.M + 1, c.H, c.dk, c.dv, dtype=torch.float32, device=self.device)
+        b["saved"] = None  # the forward overwrites what a saved pass read
         if overlap and stream is None:
-            return self._forward_overlapped(x, alpha, beta, b, state_in, state_out)
+            return self._forward_overlapped(x, alpha, beta, b, state_in, state_out, train)
         self.route_dispatch_project(x, alpha, beta, b, stream)
-        chunk = gdn_chunk_fwd if self.rule == "gdn" else gla_chunk_fwd
-        chunk(b["dims"], b["n_seg"], b["N"], b["NT"], B * (c.M + 1), b["seg_off"], b["seg_state"], b["perm"],
-              b["q"], b["k"], b["v"], b["alpha_p"], b["beta_p"], state_in, state_out, b["o"], b["ws_chunk"], stream)
+        args = (b["dims"], b["n_seg"], b["N"], b["NT"], B * (c.M + 1), b["seg_off"], b["seg_state"], b["perm"],
+                b["q"], b["k"], b["v"], b["alpha_p"], b["beta_p"], state_in, state_out, b["o"])
+        if train:
+            chunk_fwd_train(self.rule, *args, self._grad_bufs(b)["ws"], stream)
+            b["saved"] = "all"
+        else:
+            (gdn_chunk_fwd if self.rule == "gdn" else gla_chunk_fwd)(*args, b["ws_chunk"], stream)
         mom_combine(b["dims"], b["NT"], b["inv"], b["w"], b["o"], b["o"][b["NR"]:], b["out"], stream)
         return b["out"], state_out, b
 
-    def _forward_overlapped(self, x, alpha, beta, b, state_in, state_out):
+    def _forward_overlapped(self, x, alpha, beta, b, state_in, state_out, train=False):
         c, d = self.cfg, b["dims"]
         B, N, NT = b["B"], b["N"], b["NT"]
         n_state = B * (c.M + 1)
-        chunk = gdn_chunk_fwd if self.rule == "gdn" else gla_chunk_fwd
+        if train:
+            g = self._grad_bufs(b, split=True)
+            chunk = lambda *a: chunk_fwd_train(self.rule, *a)
+            ws_r, ws_s = g["ws"], g["ws_s"]
+        else:
+            chunk = gdn_chunk_fwd if self.rule == "gdn" else gla_chunk_fwd
+            ws_r, ws_s = b["ws_chunk"], b["ws_chunk_s"]
         main = torch.cuda.current_stream()
-        if getattr(self, "_side", None) is None:
-            self._side = torch.cuda.Stream(device=self.device)  # default priority
-            self._ev = [torch.cuda.Event() for _ in range(3)]
-        side, ev = self._side, self._ev
+        side, ev = self._side_stream()
         ev[0].record(main)  # inputs ready
         side.wait_event(ev[0])
         s = side.cuda_stream
@@ -344,7 +383,7 @@ class MomLayer:
         mom_project_part(d, x, None, None, self.w_q, self.w_k, self.w_v, b["q"], b["k"], b["v"], PART_SHARED, s)
         ev[1].record(side)  # queries ready
         chunk(d, B, N, NT, n_state, b["seg_off_s"], b["seg_state_s"], b["perm"], b["q"], b["k"], b["v"], b["alpha_p"],
-              b["beta_p"], state_in, state_out, b["o"], b["ws_chunk_s"], s)
+              b["beta_p"], state_in, state_out, b["o"], ws_s, s)
         ev[2].record(side)  # shared memory done
         mom_route(d, x, self.w_r, self.bias, b["idx"], b["w"])
         mom_dispatch_part(d, b["idx"], x, alpha, beta, b["seg_off"], b["perm"], b["inv"], None, b["alpha_p"],
@@ -355,17 +394,24 @@ class MomLayer:
         mom_project_part(d, x, b["perm"], b["seg_off"], self.w_q, self.w_k, self.w_v, b["q"], b["k"], b["v"],
                          PART_ROUTED)
         chunk(d, c.M * B, N, NT, n_state, b["seg_off"], b["seg_state"], b["perm"], b["q"], b["k"], b["v"],
-              b["alpha_p"], b["beta_p"], state_in, state_out, b["o"], b["ws_chunk"])
+              b["alpha_p"], b["beta_p"], state_in, state_out, b["o"], ws_r)
         main.wait_event(ev[2])
         mom_combine(d, NT, b["inv"], b["w"], b["o"], b["o"][b["NR"]:], b["out"])
+        if train:
+            b["saved"] = "split"
         return b["out"], state_out, b
 
-    def chunk_backward(self, b, d_o, dstate_out=None, state_in=None, stream=None):
-        """Gradients of the memories' recurrence over the segments of the last
-        forward with buffers b: d_o [N, H, dv] fp32 = dL/do per packed row,
-        dstate_out [B, M+1, H, dk, dv] fp32 or None (zeros), state_in as given to
-        forward.  Returns a dict of dq [N, H, dk] (per row), dk, dv, d_alpha,
-        d_beta [N, H] and dstate_in, all fp32 (buffers reused per shape)."""
+    def _side_stream(self):
+        """The second stream (default priority) and its events."""
+        if getattr(self, "_side", None) is None:
+            self._side = torch.cuda.Stream(device=self.device)
+            self._ev = [torch.cuda.Event() for _ in range(5)]
+        return self._side, self._ev
+
+    def _grad_bufs(self, b, split=False):
+        """Gradient buffers of shape b; ws serves the recompute backward, the
+        training forward over all segments, or (split) its routed call, and
+        ws_s its shared call (chunk slots are counted per call)."""
         c = self.cfg
         if "grad" not in b:
             dev, f32 = self.device, torch.float32
@@ -379,11 +425,44 @@ class MomLayer:
                              dstate_in=torch.empty(b["n_seg"], H, c.dk, c.dv, dtype=f32, device=dev),
                              ws=torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev))
         g = b["grad"]
-        fn = gdn_chunk_bwd if self.rule == "gdn" else gla_chunk_bwd
-        fn(b["dims"], b["n_seg"], b["N"], b["NT"], b["n_seg"], b["seg_off"], b["seg_state"], b["perm"], b["q"],
-           b["k"], b["v"], b["alpha_p"], b["beta_p"], state_in, d_o, dstate_out, g["dq"], g["dk"], g["dv"],
-           g["d_alpha"], g["d_beta"], g["dstate_in"], g["ws"], stream)
+        if split and "ws_s" not in g:
+            nbytes = gdn_chunk_bwd_workspace_bytes(b["dims"], b["B"], b["N"])
+            g["ws_s"] = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
         return g
+
+    def chunk_backward(self, b, d_o, dstate_out=None, state_in=None, stream=None):
+        """Gradients of the memories' recurrence over the segments of the last
+        forward with buffers b: d_o [N, H, dv] fp32 = dL/do per packed row,
+        dstate_out [B, M+1, H, dk, dv] fp32 or None (zeros), state_in as given to
+        forward.  Returns a dict of dq [N, H, dk] (per row), dk, dv, d_alpha,
+        d_beta [N, H] and dstate_in, all fp32 (buffers reused per shape).
+        After a train=True forward it reads the factors and states that forward
+        kept (once: the next call recomputes them)."""
+        g = self._grad_bufs(b)
+        saved, b["saved"] = b.get("saved"), None
+        if saved == "split":  # routed and shared segments, as the overlapped forward ran them
+            self._chunk_bwd_call(b, PART_ROUTED, True, d_o, dstate_out, state_in, stream)
+            self._chunk_bwd_call(b, PART_SHARED, True, d_o, dstate_out, state_in, stream)
+        else:
+            self._chunk_bwd_call(b, PART_ALL, saved == "all", d_o, dstate_out, state_in, stream)
+        return g
+
+    def _chunk_bwd_call(self, b, part, saved, d_o, dstate_out, state_in, stream):
+        """One recurrence-gradient call over the routed segments, the shared
+        memory's, or all; from the saved factors or recomputing them."""
+        g, n_state = b["grad"], b["n_seg"]
+        if part == PART_SHARED:
+            n, off, st, ws = b["B"], b["seg_off_s"], b["seg_state_s"], g["ws_s"]
+        else:
+            n = n_state - b["B"] if part == PART_ROUTED else n_state
+            off, st, ws = b["seg_off"], b["seg_state"], g["ws"]
+        args = (b["dims"], n, b["N"], b["NT"], n_state, off, st, b["perm"], b["q"], b["k"], b["v"], b["alpha_p"],
+                b["beta_p"], state_in, d_o, dstate_out, g["dq"], g["dk"], g["dv"], g["d_alpha"], g["d_beta"],
+                g["dstate_in"], ws, stream)
+        if saved:
+            chunk_bwd_saved(self.rule, *args)
+        else:
+            (gdn_chunk_bwd if self.rule == "gdn" else gla_chunk_bwd)(*args)
 
     def backward(self, x, dout, b, dstate_out=None, state_in=None, stream=None):
         """Gradients of the layer's last forward (buffers b, input x) for the
@@ -410,11 +489,28 @@ class MomLayer:
                                              device=dev))
         lg = b["lgrad"]
         mom_combine_bwd(d, b["NT"], b["inv"], b["w"], b["o"], dout, lg["d_o"], lg["d_o"][b["NR"]:], lg["dw"], stream)
-        g = self.chunk_backward(b, lg["d_o"], dstate_out, state_in, stream)
+        route = lambda s: mom_route_bwd(d, x, self.w_r, b["idx"], b["w"], lg["dw"], lg["dx_router"], lg["dw_r"],
+                                        lg["dbias"], lg["ws"], s)
+        if b.get("saved") == "split" and stream is None:
+            # after an overlapped training forward: the shared memory's
+            # recurrence gradients (a few long walks that fill few CUs) and the
+            # router's run on the second stream beside the routed memories'
+            b["saved"] = None
+            g = b["grad"]
+            main = torch.cuda.current_stream()
+            side, ev = self._side_stream()
+            ev[3].record(main)  # dL/do and dL/dw ready
+            side.wait_event(ev[3])
+            self._chunk_bwd_call(b, PART_SHARED, True, lg["d_o"], dstate_out, state_in, side.cuda_stream)
+            route(side.cuda_stream)
+            ev[4].record(side)
+            self._chunk_bwd_call(b, PART_ROUTED, True, lg["d_o"], dstate_out, state_in, None)
+            main.wait_event(ev[4])
+        else:
+            g = self.chunk_backward(b, lg["d_o"], dstate_out, state_in, stream)
+            route(stream)
         mom_dispatch_bwd(d, b["idx"], b["inv"], g["d_alpha"], g["d_beta"], g["dq"], lg["d_alpha"], lg["d_beta"],
                          lg["dq"], stream)
-        mom_route_bwd(d, x, self.w_r, b["idx"], b["w"], lg["dw"], lg["dx_router"], lg["dw_r"], lg["dbias"], lg["ws"],
-                      stream)
         return dict(d_alpha=lg["d_alpha"], d_beta=lg["d_beta"], dq=lg["dq"], dk=g["dk"], dv=g["dv"],
                     dx_router=lg["dx_router"], dw_r=lg["dw_r"], dbias=lg["dbias"],
                     dstate_in=g["dstate_in"].view(-1, c.M + 1, c.H, c.dk, c.dv))

@@ -138,7 +138,7 @@ def test_chunk_bwd_checks():
     assert need >= n_chunks * d.H * per and need % 256 == 0
     assert need > L.gdn_chunk_workspace_bytes(ctypes.byref(d), n_seg, n_rows)
     args = [FAKE] * 5 + [None, FAKE, None] + [FAKE] * 6  # q..beta, state_in, d_o, dstate_out, outputs
-    for f in (L.gdn_chunk_bwd, L.gla_chunk_bwd):
+    for f in (L.gdn_chunk_bwd, L.gla_chunk_bwd, L.gdn_chunk_bwd_saved, L.gla_chunk_bwd_saved):
         # no workspace, a short one, a missing output, float32 storage
         assert f(ctypes.byref(d), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, *args, None, 0, None) == -5
         assert f(ctypes.byref(d), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, *args, FAKE, need - 1,
@@ -150,3 +150,17 @@ def test_chunk_bwd_checks():
         assert f(ctypes.byref(d32), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, *args, FAKE, need,
                  None) == -3
     assert L.gdn_chunk_bwd_workspace_bytes(ctypes.byref(_dims(dtype=0)), n_seg, n_rows) == 0
+    fargs = [FAKE] * 5 + [None, FAKE, FAKE]  # q..beta, state_in, state_out, o
+    for f in (L.gdn_chunk_fwd_train, L.gla_chunk_fwd_train):
+        # the training forward needs the gradient workspace, not the forward's
+        small = L.gdn_chunk_workspace_bytes(ctypes.byref(d), n_seg, n_rows)
+        assert f(ctypes.byref(d), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, *fargs, None, 0, None) == -5
+        assert f(ctypes.byref(d), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, *fargs, FAKE, small,
+                 None) == -5
+        for i in (6, 7):  # state_out, o
+            bad = list(fargs)
+            bad[i] = None
+            assert f(ctypes.byref(d), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, *bad, FAKE, need,
+                     None) == -1
+        assert f(ctypes.byref(_dims(dtype=0)), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, *fargs, FAKE,
+                 need, None) == -3

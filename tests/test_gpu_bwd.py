@@ -128,3 +128,33 @@ def test_chunk_bwd_layer_full_size_sampled(rule):
     for name, rn in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("d_alpha", "da"), ("d_beta", "dc")):
         assert_grad(name, f(g[name])[rows], ref[rn])
     assert_grad("dstate_in", f(g["dstate_in"])[seg_state[pick]], ref["dstate0"])
+
+
+@pytest.mark.parametrize("rule,dk,dv,with_state", [("gdn", 128, 256, True), ("gdn", 64, 64, False),
+                                                   ("gdn", 128, 128, True), ("gla", 128, 256, True),
+                                                   ("gla", 64, 128, False)])
+def test_chunk_fwd_train_bwd_saved(rule, dk, dv, with_state):
+    """The split training pair: chunk_fwd_train's o and final states equal the
+    plain forward's bit for bit, and chunk_bwd_saved, reading the factors and
+    states the training forward kept, gives gdn_chunk_bwd's gradients bit for
+    bit (same segments as above, queries shared between rows)."""
+    log("fwd_train/bwd_saved", rule, dk, dv, "state" if with_state else "-")
+    r = run_bwd_segments(rule, dk, dv, with_state, True, True)
+    (dims, n_seg, N, n_tok, n_state, seg_off, seg_state, row_token, q, k, v, a, c, s0, d_o, dst) = r["args"]
+    fwd = mom.gla_chunk_fwd if rule == "gla" else mom.gdn_chunk_fwd
+    H = dims.H
+    o_ref, st_ref = nan(N, H, dv), nan(n_state, H, dk, dv)
+    o, st = nan(N, H, dv), nan(n_state, H, dk, dv)
+    fws = torch.empty(mom.gdn_chunk_workspace_bytes(dims, n_seg, N), dtype=torch.uint8, device="cuda")
+    fwd(dims, n_seg, N, n_tok, n_state, seg_off, seg_state, row_token, q, k, v, a, c, s0, st_ref, o_ref, fws)
+    ws = torch.full_like(r["ws"], 0xFF)  # contents on entry do not matter
+    mom.chunk_fwd_train(rule, dims, n_seg, N, n_tok, n_state, seg_off, seg_state, row_token, q, k, v, a, c, s0, st,
+                        o, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o.isnan(), o_ref.isnan()) and torch.equal(o.nan_to_num(), o_ref.nan_to_num())
+    assert torch.equal(st.isnan(), st_ref.isnan()) and torch.equal(st.nan_to_num(), st_ref.nan_to_num())
+    out = {kk: nan(*vv.shape) for kk, vv in r["out"].items()}
+    mom.chunk_bwd_saved(rule, *r["args"], out["dq"], out["dk"], out["dv"], out["da"], out["dc"], out["ds0"], ws)
+    torch.cuda.synchronize()
+    for kk, vv in out.items():
+        assert np.array_equal(vv.cpu().numpy(), r["out"][kk], equal_nan=True), kk

@@ -122,3 +122,39 @@ def test_route_bwd_shapes(M, K, D, NT):
     assert_grad("router dx", f(dx), dx_ref)
     assert_grad("router dw_r", f(dwr), dwr_ref)
     assert_grad("router dbias", f(db), db_ref)
+
+
+@pytest.mark.parametrize("name,B,T,rule,overlap", [("l380m", 8, 2048, "gdn", True), ("l380m", 8, 2048, "gdn", False),
+                                                   ("l380m", 2, 300, "gla", True), ("m16", 2, 200, "gdn", True)])
+def test_layer_train_forward_saved_backward(name, B, T, rule, overlap):
+    """A training step (forward with train=True, then backward reading what it
+    kept) gives the plain forward's outputs and the recompute backward's
+    gradients bit for bit, on one stream and on two; the next backward after it
+    recomputes and agrees too."""
+    cfg = small(name, B, T)
+    inp = synth.make_layer_inputs(cfg, seed=23)
+    NT = B * T
+    rng = np.random.default_rng(24)
+    dout = to_gpu(rng.standard_normal((NT, cfg.H, cfg.dv)).astype(np.float32))
+    S0 = to_gpu((0.1 * rng.standard_normal((B, cfg.M + 1, cfg.H, cfg.dk, cfg.dv))).astype(np.float32))
+    dS = to_gpu(rng.standard_normal(tuple(S0.shape)).astype(np.float32))
+    layer = mom.MomLayer(cfg, inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"], rule=rule)
+    x = torch.from_numpy(inp["x"]).to(torch.bfloat16).cuda()
+    a, c = to_gpu(inp["alpha"]), to_gpu(inp["beta"])
+    log("layer train/saved", name, B, T, rule, "overlap" if overlap else "serial")
+    res = []
+    for train, backwards in ((False, 1), (True, 2)):
+        st = torch.empty_like(S0)
+        out, _, b = layer.forward(x, a, c, state_in=S0, state_out=st, overlap=overlap, train=train)
+        r = dict(out=out.clone(), st=st)
+        # the training forward left its factors for the backward (two workspaces when on two streams)
+        assert b["saved"] == (("split" if overlap else "all") if train else None)
+        for i in range(backwards):
+            g = layer.backward(x, dout, b, dstate_out=dS, state_in=S0)
+            r.update({"%s%d" % (k, i): v.clone() for k, v in g.items()})
+        torch.cuda.synchronize()
+        res.append(r)
+    ref, got = res
+    for k in got:
+        base = k[:-1] + "0" if k[-1] == "1" else k
+        assert torch.equal(got[k], ref[base]), k
