@@ -6,9 +6,10 @@ Two steps, both run on the GPU host:
     rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/copy_fetch -o p -- \
         python3 -m mixture_memories_recurrence_amd.pmc_traffic copy --mib 1024
     rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/copy_write -o p -- (same command)
-    # 2. the bench steps, without the decode and gradient parts
+    # 2. the bench steps on one stream (each stage one launch per step, as the
+    #    roofline pass times it), without the decode and gradient parts
     rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/fetch -o p -- python3 bench.py --steps 2 --warmup 1 \
-        --no-decode --no-cpu-baseline --no-gla --no-single --no-bwd
+        --no-decode --no-cpu-baseline --no-gla --no-single --no-bwd --serial
     rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/write -o p -- (same command)
     python3 -m mixture_memories_recurrence_amd.pmc_traffic summarize --dir OUT --copy-mib 1024 \
         --workload l380m --out profiles/traffic_l380m.json
