@@ -57,6 +57,12 @@ __device__ __forceinline__ bool locate_chunk(const int32_t* __restrict__ seg_off
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Program order of one wave's LDS accesses to the same addresses, for the
+// compiler only: a wave's LDS operations are performed in issue order, so a
+// read after a write (or a write after a read) of the same location by the
+// same wave needs no wait; the compiler still waits before a read's data is
+// used.
+__device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void vm_wait_8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
 
@@ -110,14 +116,19 @@ __device__ __forceinline__ void store_state_t(f16_t* __restrict__ dst, const f16
         const u2v pc = {pack_h2(t[4 * qq], t[4 * qq + 1]), pack_h2(t[4 * qq + 2], t[4 * qq + 3])};
         *reinterpret_cast<u2v*>(tile + 64 * c32 + 8 * ((4 * a2 + qq) ^ (c32 & 7)) + 4 * g2) = pc;
       }
-    wave_lds_fence();
+    wave_lds_order();
+    h8v val[4];  // all four reads in flight before the first store
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int col = 8 * j + (lane >> 3), pcs = lane & 7;
-      const h8v val = *reinterpret_cast<const h8v*>(tile + 64 * col + 8 * (pcs ^ (col & 7)));
-      *reinterpret_cast<h8v*>(dst + (int64_t)col * DK + 64 * rd + 8 * pcs) = val;
+      val[j] = *reinterpret_cast<const h8v*>(tile + 64 * col + 8 * (pcs ^ (col & 7)));
     }
-    wave_lds_fence();  // read before the next round (or other code) overwrites the tile
+    wave_lds_order();  // read before the next round (or other code) overwrites the tile
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = 8 * j + (lane >> 3), pcs = lane & 7;
+      *reinterpret_cast<h8v*>(dst + (int64_t)col * DK + 64 * rd + 8 * pcs) = val[j];
+    }
   }
 }
 
