@@ -26,8 +26,8 @@
 // slice from tiles the kernel has anyway.
 //
 // Launches:
-//   k_gdn_prep         T, P, decays and X (float32) per (chunk, head)
-//   k_gdn_chain SAVE   the state entering every chunk, transposed half S^T
+//   k_gdn_prep         T, P, decays and X (half) per (chunk, head)
+//   k_gdn_chain mode 1 the state entering every chunk, transposed half S^T
 //   k_gdn_chain_bwd    reverse walk over each segment's chunks with dS in
 //                      matrix-core accumulators; stores dS' of every chunk
 //                      (transposed half) and dL/d(entering state)

@@ -636,9 +636,10 @@ mom_status launch_gdn_chunk_mfma(const mom_dims& d, int n_seg, int n_rows, const
 }
 
 
-// For the gradients: prep (with X = (I + A)^{-1} in float32 for Gated DeltaNet)
-// and the state walk that stores the state entering every chunk (transposed,
-// half) in hws, without the read-out.
+// For the gradients: prep (also writing X = (I + A)^{-1}, solved in float32 and
+// stored as half, for Gated DeltaNet) and the walk that stores the state
+// entering every chunk (transposed, half) in hws: without the read-out (MODE 1)
+// or with it, o and state_out written as in the forward pass (MODE 2).
 template <int DK, bool DELTA, int MODE>
 static mom_status launch_states(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
                                 const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
