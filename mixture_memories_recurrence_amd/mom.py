@@ -405,8 +405,14 @@ class MomLayer:
         """The second stream (default priority) and its events."""
         if getattr(self, "_side", None) is None:
             self._side = torch.cuda.Stream(device=self.device)
-            self._ev = [torch.cuda.Event() for _ in range(5)]
+            self._ev = [torch.cuda.Event() for _ in range(7)]
         return self._side, self._ev
+
+    def _third_stream(self):
+        """A third stream (default priority), for the router's gradients."""
+        if getattr(self, "_side2", None) is None:
+            self._side2 = torch.cuda.Stream(device=self.device)
+        return self._side2
 
     def _grad_bufs(self, b, split=False):
         """Gradient buffers of shape b; ws serves the recompute backward, the
@@ -493,19 +499,35 @@ class MomLayer:
                                         lg["dbias"], lg["ws"], s)
         if b.get("saved") == "split" and stream is None:
             # after an overlapped training forward: the shared memory's
-            # recurrence gradients (a few long walks that fill few CUs) and the
-            # router's run on the second stream beside the routed memories'
+            # recurrence gradients (a few long walks that fill few CUs) run on
+            # the second stream beside the routed memories', and the router's
+            # (which need only dL/dw) on a third from the start
             b["saved"] = None
             g = b["grad"]
             main = torch.cuda.current_stream()
             side, ev = self._side_stream()
+            side2 = self._third_stream()
             ev[3].record(main)  # dL/do and dL/dw ready
             side.wait_event(ev[3])
+            side2.wait_event(ev[3])
+            route(side2.cuda_stream)
+            ev[5].record(side2)
             self._chunk_bwd_call(b, PART_SHARED, True, lg["d_o"], dstate_out, state_in, side.cuda_stream)
-            route(side.cuda_stream)
             ev[4].record(side)
             self._chunk_bwd_call(b, PART_ROUTED, True, lg["d_o"], dstate_out, state_in, None)
             main.wait_event(ev[4])
+            main.wait_event(ev[5])
+        elif stream is None:
+            # the router's gradients (which need only dL/dw) beside the recurrence's
+            main = torch.cuda.current_stream()
+            side2 = self._third_stream()
+            _, ev = self._side_stream()
+            ev[3].record(main)
+            side2.wait_event(ev[3])
+            route(side2.cuda_stream)
+            ev[5].record(side2)
+            g = self.chunk_backward(b, lg["d_o"], dstate_out, state_in)
+            main.wait_event(ev[5])
         else:
             g = self.chunk_backward(b, lg["d_o"], dstate_out, state_in, stream)
             route(stream)
