@@ -2,10 +2,11 @@
 costs per launch that the roofline divides by.  Per token at the 380M-shape
 layer (every tensor read or written once at its stored width) they are route
 2,064 B, combine 16,400 B, chunk 24,672 B and 3.77 MFLOP, projections 10.5
-MFLOP, with two choices of this design counted as they are: the dispatch writes no gathered copy of x (the projection's
-loads gather the rows), so it moves 292 B (index arrays and gates) instead of
-6,296; and the chunk stage also counts reading and writing the recurrent
-states, 2 x 40 slots x 4 heads x 128 x 256 x 4 B over 16,384 tokens = 2,560 B."""
+MFLOP, with two choices of this design counted as they are: the dispatch
+writes no gathered copy of x (the projection's loads gather the rows), so it
+moves 292 B (index arrays and gates) instead of 6,296; and the chunk stage
+also counts reading and writing the recurrent states, 2 x 40 slots x 4 heads
+x 128 x 256 x 4 B over 16,384 tokens = 2,560 B."""
 import os
 import subprocess
 import sys
