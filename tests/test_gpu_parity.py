@@ -142,11 +142,14 @@ def test_dispatch_forced_empty_memory():
     np.testing.assert_array_equal(b["perm"].cpu().numpy(), perm)
 
 
-@pytest.mark.parametrize("B,T,M,K", [(16, 4096, 64, 8), (3, 700, 5, 2)])
+@pytest.mark.parametrize("B,T,M,K", [(16, 4096, 64, 8), (3, 700, 5, 2), (256, 1, 4, 2), (1000, 1, 8, 3),
+                                     (2000, 1, 8, 2)])
 def test_dispatch_random_routes(B, T, M, K):
     """Random distinct memory choices per token.  The first shape has
     64 * 16 * 16 per-tile counts, more than the scatter kernel scans itself, so
-    it takes the separate scan launch; the second takes the in-kernel scan."""
+    it takes the separate scan launch; the second takes the in-kernel scan; the
+    one-position shapes are decode steps (one token per sequence), with M B
+    below and above the in-kernel scan's limit of 8192 counts."""
     cfg = synth.LayerConfig(B, T, 64, 1, 64, 64, M, K, "bf16")
     log("dispatch random", B, T, M, K)
     rng = np.random.default_rng(11)
@@ -171,6 +174,42 @@ def test_dispatch_random_routes(B, T, M, K):
     mem = np.concatenate([np.repeat(np.arange(M), counts), np.full(B * T, M)])
     np.testing.assert_array_equal(ap.cpu().numpy()[:, 0], alpha[perm_ref, 0, mem])
     np.testing.assert_array_equal(bp.cpu().numpy()[:, 0], beta[perm_ref, 0, mem])
+
+
+def test_dispatch_one_position_parts_and_gather():
+    """One position per sequence (a decode step): routed part then shared part
+    equal the whole dispatch, and the gathered x rows are the tokens' rows
+    (bf16, bit for bit)."""
+    B, M, K, D = 300, 6, 3, 128
+    cfg = synth.LayerConfig(B, 1, D, 2, 64, 64, M, K, "bf16")
+    rng = np.random.default_rng(12)
+    idx = np.argsort(rng.random((B, M)), axis=1)[:, :K].astype(np.int32)
+    alpha = rng.random((B, 2, M + 1)).astype(np.float32)
+    beta = rng.random((B, 2, M + 1)).astype(np.float32)
+    x = torch.randn(B, D, device="cuda").to(torch.bfloat16)
+    dims = mom.dims_of(cfg)
+    N = B * (K + 1)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(mom.mom_workspace_bytes(dims, mom.WS_DISPATCH), 256), dtype=torch.uint8, device="cuda")
+    out = {}
+    for mode in ("whole", "parts"):
+        so, perm, inv = torch.full(((M + 1) * B + 1,), -7, **i32), torch.full((N,), -7, **i32), torch.empty(B, K, **i32)
+        ap, bp = torch.empty(N, 2, device="cuda"), torch.empty(N, 2, device="cuda")
+        xp = torch.zeros(B * K, D, device="cuda", dtype=torch.bfloat16)
+        args = (dims, to_gpu(idx), x, to_gpu(alpha), to_gpu(beta), so, perm, inv, xp, ap, bp, ws)
+        if mode == "whole":
+            mom.mom_dispatch(*args)
+        else:
+            mom.mom_dispatch_part(*args, mom.PART_ROUTED)
+            mom.mom_dispatch_part(*args, mom.PART_SHARED)
+        torch.cuda.synchronize()
+        out[mode] = [t.cpu() for t in (so, perm, inv, ap, bp, xp)]
+    for a_, b_ in zip(out["whole"], out["parts"]):
+        assert torch.equal(a_, b_)
+    so_ref, perm_ref, inv_ref = oracle.dispatch(idx, B, 1, M)
+    np.testing.assert_array_equal(out["whole"][0].numpy(), so_ref)
+    np.testing.assert_array_equal(out["whole"][1].numpy(), perm_ref)
+    assert torch.equal(out["whole"][5], x.cpu()[torch.from_numpy(perm_ref[:B * K]).long()])
 
 
 # ------------------------------------------------------------------ projections
