@@ -535,6 +535,31 @@ def test_decode_step(name, n_seq, steps, rule):
         S_ref = ref["state"]
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 256), (128, 64)])
+def test_decode_step_head_shapes(dk, dv):
+    """decode_step on the other head shapes the decode kernel is built for
+    (512 threads for dv = 128, 256 for dv = 64, dk = 64 with 1024), half
+    storage: the layer with T = 1 from given states, two steps."""
+    cfg = dataclasses.replace(CFG["l380m"], dk=dk, dv=dv)
+    n_seq = 40
+    log("decode shapes", dk, dv)
+    inp = synth.make_layer_inputs(dataclasses.replace(cfg, B=1, T=1), seed=3)
+    layer = mom.MomLayer(cfg, inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"])
+    S = synth.make_state(cfg, n_seq, seed=8)
+    states = to_gpu(S)
+    S_ref = S.astype(np.float64)
+    for step in range(2):
+        d = synth.make_decode_step_inputs(cfg, n_seq, seed=200 + step)
+        out, b = layer.decode_step(to_gpu(d["x"], torch.bfloat16), to_gpu(d["alpha"]), to_gpu(d["beta"]), states)
+        torch.cuda.synchronize()
+        ref = oracle.layer(dims_tuple(cfg, n_seq, 1), d["x"], inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"],
+                           inp["w_v"], d["alpha"], d["beta"], state0=S_ref)
+        np.testing.assert_array_equal(b["idx"].cpu().numpy(), ref["idx"])
+        assert_close("decode out step %d" % step, out.cpu().numpy(), ref["out"], *TOL["bf16"])
+        assert_close("decode states step %d" % step, states.cpu().numpy(), ref["state"], *TOL["bf16"])
+        S_ref = ref["state"]
+
+
 def test_prefill_then_decode():
     """Decoding token T from the prefill's final state equals the last row of a
     prefill over T+1 tokens."""
