@@ -30,6 +30,8 @@
  *                    the same forward and gradients split for a training
  *                    step: the forward keeps its chunk factors and states for
  *                    the backward, which then does not recompute them.
+ *   mom_route_count, mom_dispatch_counted
+ *                    route and histogram in one launch for a decode step.
  *   gdn_decode_step  one recurrent step per sequence (constant-cost inference,
  *                    jxzklqfsx.com write-up, introduction and inference section).
  *   mom_combine      router-weighted sum of the per-memory reads plus the
@@ -138,6 +140,25 @@ mom_status mom_dispatch(const mom_dims* dims, const int32_t* idx, const void* x,
                         const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv,
                         void* x_packed, float* alpha_p, float* beta_p, void* ws, size_t ws_bytes,
                         void* stream);
+
+/* Route and histogram in one launch, for one position per sequence (a decode
+ * step, dims->T == 1; otherwise MOM_ERR_UNSUPPORTED): the outputs of
+ * mom_route (same arithmetic as its general kernel), and the dispatch's
+ * per-(memory, sequence) counts written into ws (at least
+ * mom_workspace_bytes(dims, MOM_WS_DISPATCH) bytes), which
+ * mom_dispatch_counted then reads instead of counting again (podcast.do-not-
+ * panic.com page, "Solving scatter-gather without new kernels": the counting
+ * sort's histogram comes from the router's own pass). */
+mom_status mom_route_count(const mom_dims* dims, const void* x, const void* w_r, const float* bias,
+                           int32_t* idx, float* w, void* ws, size_t ws_bytes, void* stream);
+
+/* mom_dispatch for dims->T == 1 (else MOM_ERR_UNSUPPORTED) when ws holds the
+ * counts mom_route_count wrote for the same idx: the same outputs, one launch
+ * fewer. */
+mom_status mom_dispatch_counted(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
+                                const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv,
+                                void* x_packed, float* alpha_p, float* beta_p, void* ws, size_t ws_bytes,
+                                void* stream);
 
 /* Projections.  q[t] = w_q x[t] for every token; for packed row r of memory m
  * (from seg_off): k[r] = w_k[m] x[perm[r]] normalised to unit L2 norm per head

@@ -225,9 +225,11 @@ __global__ __launch_bounds__(256) void k_dispatch_shared(int B, int T, int H, in
 }  // namespace mom
 
 namespace mom {
+// counted: ws already holds the counts (mom_route_count, one position per sequence)
 static mom_status dispatch(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
                            const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv, void* x_packed,
-                           float* alpha_p, float* beta_p, void* ws, size_t ws_bytes, int part, void* stream) {
+                           float* alpha_p, float* beta_p, void* ws, size_t ws_bytes, int part, void* stream,
+                           bool counted = false) {
   mom_status s = check_dims(dims);
   if (s != MOM_OK) return s;
   if (part < 0 || part > 2) return MOM_ERR_DIMS;
@@ -258,7 +260,8 @@ static mom_status dispatch(const mom_dims* dims, const int32_t* idx, const void*
   const int last_seg = part == 2 ? d.M * d.B : (d.M + 1) * d.B;
   const bool shared_rows = part == 0;
   int32_t* cnt = (int32_t*)ws;
-  hipLaunchKernelGGL(k_count, dim3(ntile, d.B), dim3(kTile), 0, st, d.B, d.T, d.M, d.topk, ntile, idx, cnt);
+  if (!counted)
+    hipLaunchKernelGGL(k_count, dim3(ntile, d.B), dim3(kTile), 0, st, d.B, d.T, d.M, d.topk, ntile, idx, cnt);
   const bool fused = (int64_t)d.M * d.B * ntile <= kFuseScan;
   if (!fused)
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, d.B, d.T, d.M, d.topk, ntile, last_seg, cnt, seg_off);
@@ -284,6 +287,15 @@ extern "C" mom_status mom_dispatch(const mom_dims* dims, const int32_t* idx, con
                                    void* stream) {
   return mom::dispatch(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_p, beta_p, ws, ws_bytes, 0,
                        stream);
+}
+
+extern "C" mom_status mom_dispatch_counted(const mom_dims* dims, const int32_t* idx, const void* x,
+                                           const float* alpha, const float* beta, int32_t* seg_off, int32_t* perm,
+                                           int32_t* inv, void* x_packed, float* alpha_p, float* beta_p, void* ws,
+                                           size_t ws_bytes, void* stream) {
+  if (dims && dims->T != 1) return MOM_ERR_UNSUPPORTED;
+  return mom::dispatch(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_p, beta_p, ws, ws_bytes, 0,
+                       stream, true);
 }
 
 extern "C" mom_status mom_dispatch_part(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,

@@ -47,11 +47,14 @@ struct ExactProd<float> {
 
 // G lanes per token: lane s of a group handles elements 8 s + 8 G i of
 // the row; the group's partial sums are combined with the same xor butterfly
-// for every memory.
+// for every memory.  With cnt (one position per sequence: token t is sequence
+// t) the kernel also writes the dispatch's counts, cnt[m][t] = 1 when token t
+// selected memory m, else 0, so the dispatch needs no counting launch.
 template <typename XT, int MT, int G>
 __global__ __launch_bounds__(256) void k_route(int64_t NT, int D, int M, int K, const XT* __restrict__ x,
                                                const XT* __restrict__ wr, const float* __restrict__ bias,
-                                               int32_t* __restrict__ idx, float* __restrict__ w) {
+                                               int32_t* __restrict__ idx, float* __restrict__ w,
+                                               int32_t* __restrict__ cnt) {
   using P = ExactProd<XT>;
   const int sub = threadIdx.x % G;
   const int64_t grp = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / G;
@@ -122,6 +125,8 @@ __global__ __launch_bounds__(256) void k_route(int64_t NT, int D, int M, int K, 
         idx[t * K + j] = sel[j];
         w[t * K + j] = (float)(e[j] / z);
       }
+      if (cnt)
+        for (int m = 0; m < M; ++m) cnt[(int64_t)m * NT + t] = (int32_t)((taken >> m) & 1ull);
     }
   }
 }
@@ -265,7 +270,7 @@ __global__ __launch_bounds__(256) void k_route_wave4(int64_t NT, int D, int M, i
 
 template <typename XT, int G>
 static void launch_route_g(const mom_dims& d, const void* x, const void* wr, const float* bias, int32_t* idx,
-                           float* w, hipStream_t st) {
+                           float* w, hipStream_t st, int32_t* cnt = nullptr) {
   const int64_t NT = (int64_t)d.B * d.T;
   const int64_t need = (NT + 256 / G - 1) / (256 / G);
   const int blocks = (int)(need < 8192 ? need : 8192);
@@ -273,7 +278,7 @@ static void launch_route_g(const mom_dims& d, const void* x, const void* wr, con
   const XT* wp = (const XT*)wr;
 #define MOM_ROUTE_CASE(MT)                                                                                 \
   hipLaunchKernelGGL((k_route<XT, MT, G>), dim3(blocks), dim3(256), 0, st, NT, d.D, d.M, d.topk, xp, wp, \
-                     bias, idx, w)
+                     bias, idx, w, cnt)
   if (d.M <= 4) MOM_ROUTE_CASE(4);
   else if (d.M <= 8) MOM_ROUTE_CASE(8);
   else if (d.M <= 16) MOM_ROUTE_CASE(16);
@@ -306,6 +311,32 @@ static void launch_route(const mom_dims& d, const void* x, const void* wr, const
 }
 
 }  // namespace mom
+
+extern "C" mom_status mom_route_count(const mom_dims* dims, const void* x, const void* w_r, const float* bias,
+                                      int32_t* idx, float* w, void* ws, size_t ws_bytes, void* stream) {
+  using namespace mom;
+  mom_status s = check_dims(dims);
+  if (s != MOM_OK) return s;
+  if (dims->T != 1) return MOM_ERR_UNSUPPORTED;
+  MOM_CHECK_PTR(x);
+  MOM_CHECK_PTR(w_r);
+  MOM_CHECK_OPT_PTR(bias);
+  MOM_CHECK_PTR(idx);
+  MOM_CHECK_PTR(w);
+  if (!ws || ws_bytes < mom_workspace_bytes(dims, MOM_WS_DISPATCH)) return MOM_ERR_WORKSPACE;
+  MOM_CHECK_PTR(ws);
+  hipStream_t st = (hipStream_t)stream;
+  int32_t* cnt = (int32_t*)ws;  // the dispatch's count array [M][B][tiles], one tile per sequence here
+  const int64_t NT = dims->B;
+  if (dims->dtype == MOM_DTYPE_BF16) {
+    if (NT < 8192) launch_route_g<bf16_t, 64>(*dims, x, w_r, bias, idx, w, st, cnt);
+    else launch_route_g<bf16_t, 16>(*dims, x, w_r, bias, idx, w, st, cnt);
+  } else {
+    if (NT < 8192) launch_route_g<float, 64>(*dims, x, w_r, bias, idx, w, st, cnt);
+    else launch_route_g<float, 16>(*dims, x, w_r, bias, idx, w, st, cnt);
+  }
+  return launch_status();
+}
 
 extern "C" mom_status mom_route(const mom_dims* dims, const void* x, const void* w_r, const float* bias,
                                 int32_t* idx, float* w, void* stream) {

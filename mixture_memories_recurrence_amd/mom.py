@@ -48,6 +48,8 @@ def lib():
     D = ctypes.POINTER(MomDims)
     sigs = {
         "mom_route": [D, _VP, _VP, _VP, _VP, _VP, _VP],
+        "mom_route_count": [D, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+        "mom_dispatch_counted": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
         "mom_dispatch": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
         "mom_project": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
         "mom_project_part": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP],
@@ -85,11 +87,12 @@ def lib():
     return L
 
 
-EXPORTS = ("mom_route", "mom_dispatch", "mom_dispatch_part", "mom_project", "mom_project_part", "gdn_chunk_fwd",
-           "gla_chunk_fwd", "gdn_chunk_bwd", "gla_chunk_bwd", "gdn_chunk_fwd_train", "gla_chunk_fwd_train",
-           "gdn_chunk_bwd_saved", "gla_chunk_bwd_saved", "gdn_decode_step", "gla_decode_step", "mom_combine",
-           "mom_combine_bwd", "mom_route_bwd", "mom_dispatch_bwd", "mom_workspace_bytes",
-           "gdn_chunk_workspace_bytes", "gdn_chunk_bwd_workspace_bytes", "mom_status_string")
+EXPORTS = ("mom_route", "mom_route_count", "mom_dispatch", "mom_dispatch_counted", "mom_dispatch_part",
+           "mom_project", "mom_project_part", "gdn_chunk_fwd", "gla_chunk_fwd", "gdn_chunk_bwd", "gla_chunk_bwd",
+           "gdn_chunk_fwd_train", "gla_chunk_fwd_train", "gdn_chunk_bwd_saved", "gla_chunk_bwd_saved",
+           "gdn_decode_step", "gla_decode_step", "mom_combine", "mom_combine_bwd", "mom_route_bwd",
+           "mom_dispatch_bwd", "mom_workspace_bytes", "gdn_chunk_workspace_bytes", "gdn_chunk_bwd_workspace_bytes",
+           "mom_status_string")
 
 
 def dims_of(cfg: LayerConfig, B: int | None = None, T: int | None = None) -> MomDims:
@@ -119,6 +122,23 @@ def _check(status, name):
 
 def mom_route(dims, x, w_r, bias, idx, w, stream=None):
     _check(lib().mom_route(ctypes.byref(dims), _p(x), _p(w_r), _p(bias), _p(idx), _p(w), _s(stream)), "mom_route")
+
+
+def mom_route_count(dims, x, w_r, bias, idx, w, ws, stream=None):
+    """mom_route for one position per sequence, also writing the dispatch's
+    counts into ws for mom_dispatch_counted."""
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().mom_route_count(ctypes.byref(dims), _p(x), _p(w_r), _p(bias), _p(idx), _p(w), _p(ws), nbytes,
+                                 _s(stream)), "mom_route_count")
+
+
+def mom_dispatch_counted(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_p, beta_p, ws,
+                         stream=None):
+    """mom_dispatch reading the counts mom_route_count left in ws."""
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().mom_dispatch_counted(ctypes.byref(dims), _p(idx), _p(x), _p(alpha), _p(beta), _p(seg_off),
+                                      _p(perm), _p(inv), _p(x_packed), _p(alpha_p), _p(beta_p), _p(ws), nbytes,
+                                      _s(stream)), "mom_dispatch_counted")
 
 
 def mom_dispatch(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_p, beta_p, ws, stream=None):
@@ -542,7 +562,12 @@ class MomLayer:
         [n_seq, H, M+1], states [n_seq, M+1, H, dk, dv] updated in place."""
         n_seq = x_t.shape[0]
         b = self.buffers(n_seq, 1)
-        self.route_dispatch_project(x_t, alpha, beta, b, stream)
+        d = b["dims"]
+        # route and histogram in one launch, then the dispatch without its count
+        mom_route_count(d, x_t, self.w_r, self.bias, b["idx"], b["w"], b["ws"], stream)
+        mom_dispatch_counted(d, b["idx"], x_t, alpha, beta, b["seg_off"], b["perm"], b["inv"], None, b["alpha_p"],
+                             b["beta_p"], b["ws"], stream)
+        mom_project(d, x_t, b["perm"], b["seg_off"], self.w_q, self.w_k, self.w_v, b["q"], b["k"], b["v"], stream)
         step = gdn_decode_step if self.rule == "gdn" else gla_decode_step
         step(b["dims"], n_seq, b["idx"], b["inv"], b["q"], b["k"], b["v"], alpha, beta, states, b["o"], stream)
         mom_combine(b["dims"], n_seq, b["inv"], b["w"], b["o"], b["o"][b["NR"]:], b["out"], stream)

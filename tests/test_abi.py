@@ -126,6 +126,20 @@ def test_chunk_workspace_sizes():
 
 
 @needs_lib
+def test_route_count_checks():
+    """The one-launch route and histogram serve one position per sequence only,
+    and need the dispatch workspace."""
+    L = mom.lib()
+    d = _dims(T=1)
+    need = L.mom_workspace_bytes(ctypes.byref(d), 0)
+    assert L.mom_route_count(ctypes.byref(_dims(T=2)), FAKE, FAKE, None, FAKE, FAKE, FAKE, need, None) == -3
+    assert L.mom_route_count(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, need - 1, None) == -5
+    assert L.mom_route_count(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, None, 0, None) == -5
+    assert L.mom_dispatch_counted(ctypes.byref(_dims(T=2)), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                  FAKE, FAKE, need, None) == -3
+
+
+@needs_lib
 def test_chunk_bwd_checks():
     """The gradient entry points: workspace size (forward factors, X (half), and two
     half states per chunk and head), half storage only, and the usual refusals."""

@@ -212,6 +212,46 @@ def test_dispatch_one_position_parts_and_gather():
     assert torch.equal(out["whole"][5], x.cpu()[torch.from_numpy(perm_ref[:B * K]).long()])
 
 
+@pytest.mark.parametrize("B,M,K,D", [(256, 4, 2, 2048), (300, 16, 4, 1024), (50, 64, 8, 256)])
+def test_route_count_then_dispatch_counted(B, M, K, D):
+    """Route and histogram in one launch for a decode step: the selections equal
+    the checker's, the counts are the selection flags, and the counted
+    dispatch gives the plain dispatch's outputs bit for bit."""
+    cfg = synth.LayerConfig(B, 1, D, 2, 64, 64, M, K, "bf16")
+    log("route_count", B, M, K, D)
+    inp = synth.make_layer_inputs(cfg, seed=14)
+    dims = mom.dims_of(cfg)
+    x = to_gpu(inp["x"], torch.bfloat16)
+    wr = to_gpu(inp["w_r"], torch.bfloat16)
+    bias = to_gpu(inp["bias"]) if inp["bias"] is not None else None
+    i32 = dict(dtype=torch.int32, device="cuda")
+    nbytes = max(mom.mom_workspace_bytes(dims, mom.WS_DISPATCH), 256)
+    ws = torch.full((nbytes // 4,), -9, **i32)
+    idx, w = torch.empty(B, K, **i32), torch.empty(B, K, device="cuda")
+    mom.mom_route_count(dims, x, wr, bias, idx, w, ws)
+    torch.cuda.synchronize()
+    ref_idx, ref_w = oracle.route(inp["x"], inp["w_r"], inp["bias"], K)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=0, atol=1e-6)
+    flags = np.zeros((M, B), np.int32)
+    for b_ in range(B):
+        flags[ref_idx[b_], b_] = 1
+    np.testing.assert_array_equal(ws[:M * B].cpu().numpy().reshape(M, B), flags)
+    a_, be = to_gpu(inp["alpha"]), to_gpu(inp["beta"])
+    N = B * (K + 1)
+    outs = []
+    for counted in (False, True):
+        so, perm, inv = torch.empty((M + 1) * B + 1, **i32), torch.empty(N, **i32), torch.empty(B, K, **i32)
+        ap, bp = torch.empty(N, 2, device="cuda"), torch.empty(N, 2, device="cuda")
+        ws2 = ws.clone()
+        fn = mom.mom_dispatch_counted if counted else mom.mom_dispatch
+        fn(dims, idx, None, a_, be, so, perm, inv, None, ap, bp, ws2)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (so, perm, inv, ap, bp)])
+    for u, v in zip(*outs):
+        assert torch.equal(u, v)
+
+
 # ------------------------------------------------------------------ projections
 @pytest.mark.parametrize("name", list(CFG))
 def test_project_sampled_rows(name):
