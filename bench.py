@@ -307,7 +307,9 @@ def main():
     res = {
         "metric": "MoM layer fwd tokens/s (T=2048, M=4 top-2+shared) + decode tokens/s; % roofline",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4), "gpu_ms_per_step": round(step_ev[0].elapsed_time(step_ev[1]) / args.steps, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step": round(ms_per_step, 4),
+        "gpu_ms_per_step": round(step_ev[0].elapsed_time(step_ev[1]) / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": "%s: B=%d T=%d D=%d H=%d dk=%d dv=%d M=%d top-%d + shared, %s inputs, fp32 state"
                                % (cfg.name, cfg.B, cfg.T, cfg.D, cfg.H, cfg.dk, cfg.dv, cfg.M, cfg.K, cfg.dtype),
