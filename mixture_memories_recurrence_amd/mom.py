@@ -498,7 +498,13 @@ class MomLayer:
         Returns a dict (buffers reused per shape) of d_alpha, d_beta [B*T, H, M+1],
         dq [B*T, H, dk] (w.r.t. the projected queries), dk, dv [N, H, dk|dv]
         (w.r.t. the packed projected keys and values), dx_router [B*T, D] (the
-        router's share of dL/dx), dw_r [M, D], dbias [M], dstate_in."""
+        router's share of dL/dx), dw_r [M, D], dbias [M], dstate_in.
+
+        Without an explicit stream the router's gradients run on a third stream
+        beside the recurrence's, and after a train=True forward on two streams
+        the shared memory's recurrence gradients run on the second; the current
+        stream waits for both before the dispatch gradients, so the results are
+        ordered on it.  With a stream everything runs in order on that stream."""
         c, d = self.cfg, b["dims"]
         if "lgrad" not in b:
             dev, f32 = self.device, torch.float32
