@@ -334,6 +334,26 @@ mom_status gla_decode_step(const mom_dims* dims, int32_t n_seq, const int32_t* i
                            const float* alpha, const float* beta, float* states, float* o,
                            void* stream);
 
+/* gdn_decode_step_combined / gla_decode_step_combined: the decode step with
+ * mom_combine folded in (jxzklqfsx.com write-up, Mixture-of-Memories section:
+ * the layer's output is the weighted mixture of the memories' reads plus the
+ * shared memory's).  One block per (sequence, head) updates the shared
+ * memory's state and then the routed ones in order, and adds their reads as
+ * mom_combine does (shared first, then w[s][j] times slot j's read, j
+ * ascending, one fused multiply-add each), so out equals gdn_decode_step
+ * followed by mom_combine bit for bit; no per-slot outputs are written.
+ *   w   [n_seq][topk] float32 (from mom_route)
+ *   out [n_seq][H][dv] float32 out
+ * Other arguments, layouts and errors as gdn_decode_step (o replaced by out). */
+mom_status gdn_decode_step_combined(const mom_dims* dims, int32_t n_seq, const int32_t* idx,
+                                    const int32_t* inv, const float* w, const void* q, const void* k,
+                                    const void* v, const float* alpha, const float* beta, float* states,
+                                    float* out, void* stream);
+mom_status gla_decode_step_combined(const mom_dims* dims, int32_t n_seq, const int32_t* idx,
+                                    const int32_t* inv, const float* w, const void* q, const void* k,
+                                    const void* v, const float* alpha, const float* beta, float* states,
+                                    float* out, void* stream);
+
 /* Combine: out[t] = o_shared[t] + sum_j w[t][j] * o_routed[row(t, j)], shared
  * first then j ascending, float32, row(t, j) = inv[t][j] (NULL: t*topk + j).
  *   o_routed [*][H][dv], o_shared [n_tok][H][dv], out [n_tok][H][dv] float32  */

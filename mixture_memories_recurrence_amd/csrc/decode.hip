@@ -23,12 +23,17 @@ namespace mom {
 
 typedef float dv4 __attribute__((ext_vector_type(4)));
 
+// One slot j of the decode step of sequence b, head h (slot K: the shared
+// memory): the state is read and written in place, and the row-group-0
+// threads get their four output columns in ov.  Returns false, before any
+// barrier, when the slot's memory is out of range (nothing is done).  Every
+// thread of the block takes part; the caller separates two calls by a barrier.
 template <typename IT, int DK, int DV, int NT, bool DELTA>
-__global__ __launch_bounds__(NT) void k_gdn_decode(int n_seq, int H, int M, int K, const int32_t* __restrict__ idx,
-                                                    const int32_t* __restrict__ inv, const IT* __restrict__ q,
-                                                    const IT* __restrict__ k, const IT* __restrict__ v,
-                                                    const float* __restrict__ alpha, const float* __restrict__ beta,
-                                                    float* __restrict__ states, float* __restrict__ o) {
+__device__ __forceinline__ bool decode_slot(int n_seq, int H, int M, int K, int b, int h, int j,
+                                            const int32_t* __restrict__ idx, const int32_t* __restrict__ inv,
+                                            const IT* __restrict__ q, const IT* __restrict__ k,
+                                            const IT* __restrict__ v, const float* __restrict__ alpha,
+                                            const float* __restrict__ beta, float* __restrict__ states, float4& ov) {
   constexpr int CPR = DV / 4;     // threads per state row (float4 each)
   constexpr int RG = NT / CPR;    // row groups
   constexpr int RPT = DK / RG;    // rows per thread
@@ -37,10 +42,6 @@ __global__ __launch_bounds__(NT) void k_gdn_decode(int n_seq, int H, int M, int 
   __shared__ float4 red_a[RG][CPR], red_b[RG][CPR];
   __shared__ float kq_s;
 
-  const int bid = blockIdx.x;
-  const int h = bid % H;
-  const int j = (bid / H) % (K + 1);
-  const int b = bid / (H * (K + 1));
   const int tid = threadIdx.x;
   int m;
   int64_t row;
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(NT) void k_gdn_decode(int n_seq, int H, int M, int 
     m = M;
     row = (int64_t)n_seq * K + b;
   }
-  if ((unsigned)m > (unsigned)M) return;
+  if ((unsigned)m > (unsigned)M) return false;
   const float ag = alpha[((int64_t)b * H + h) * (M + 1) + m];
   const float cg = beta[((int64_t)b * H + h) * (M + 1) + m];
   for (int e = tid; e < DK; e += NT) {
@@ -116,12 +117,10 @@ __global__ __launch_bounds__(NT) void k_gdn_decode(int n_seq, int H, int M, int 
     u.w = cg * vv.w;
   }
   if (rg == 0) {
-    float4 ov;
     ov.x = fmaf(kq, u.x, ag * sb.x);
     ov.y = fmaf(kq, u.y, ag * sb.y);
     ov.z = fmaf(kq, u.z, ag * sb.z);
     ov.w = fmaf(kq, u.w, ag * sb.w);
-    reinterpret_cast<float4*>(o + (row * H + h) * DV)[c4] = ov;
   }
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
@@ -134,17 +133,79 @@ __global__ __launch_bounds__(NT) void k_gdn_decode(int n_seq, int H, int M, int 
     const dv4 t2 = {s2.x, s2.y, s2.z, s2.w};
     __builtin_nontemporal_store(t2, reinterpret_cast<dv4*>(S) + (int64_t)(rg + RG * r) * RS4 + c4);
   }
+  return true;
 }
 
+template <typename IT, int DK, int DV, int NT, bool DELTA>
+__global__ __launch_bounds__(NT) void k_gdn_decode(int n_seq, int H, int M, int K, const int32_t* __restrict__ idx,
+                                                    const int32_t* __restrict__ inv, const IT* __restrict__ q,
+                                                    const IT* __restrict__ k, const IT* __restrict__ v,
+                                                    const float* __restrict__ alpha, const float* __restrict__ beta,
+                                                    float* __restrict__ states, float* __restrict__ o) {
+  const int bid = blockIdx.x;
+  const int h = bid % H;
+  const int j = (bid / H) % (K + 1);
+  const int b = bid / (H * (K + 1));
+  float4 ov = {0.f, 0.f, 0.f, 0.f};
+  if (!decode_slot<IT, DK, DV, NT, DELTA>(n_seq, H, M, K, b, h, j, idx, inv, q, k, v, alpha, beta, states, ov))
+    return;
+  const int64_t row = j < K ? (int64_t)inv[(int64_t)b * K + j] : (int64_t)n_seq * K + b;
+  if ((int)threadIdx.x < DV / 4) reinterpret_cast<float4*>(o + (row * H + h) * DV)[threadIdx.x] = ov;
+}
+
+// The decode step with the combine folded in: one block per (sequence, head)
+// runs the shared memory's slot and then the routed slots in order, and adds
+// their outputs as mom_combine does (the shared one, then one fma w_j o_j per
+// routed slot, j ascending), writing out[b][h] directly; no per-slot outputs
+// are stored.  A slot whose memory is out of range (idx not from mom_route)
+// adds nothing.
+template <typename IT, int DK, int DV, int NT, bool DELTA>
+__global__ __launch_bounds__(NT) void k_gdn_decode_combined(int n_seq, int H, int M, int K,
+                                                             const int32_t* __restrict__ idx,
+                                                             const int32_t* __restrict__ inv,
+                                                             const float* __restrict__ w, const IT* __restrict__ q,
+                                                             const IT* __restrict__ k, const IT* __restrict__ v,
+                                                             const float* __restrict__ alpha,
+                                                             const float* __restrict__ beta,
+                                                             float* __restrict__ states, float* __restrict__ out) {
+  const int h = blockIdx.x % H, b = blockIdx.x / H;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int jj = 0; jj <= K; ++jj) {  // the shared memory's slot K first, then 0 .. K - 1
+    const int j = jj == 0 ? K : jj - 1;
+    if (jj > 0) __syncthreads();  // the previous slot is done with the shared arrays
+    float4 ov = {0.f, 0.f, 0.f, 0.f};
+    if (!decode_slot<IT, DK, DV, NT, DELTA>(n_seq, H, M, K, b, h, j, idx, inv, q, k, v, alpha, beta, states, ov))
+      continue;
+    if (jj == 0) {
+      acc = ov;
+    } else {
+      const float g = w[(int64_t)b * K + j];
+      acc.x = fmaf(g, ov.x, acc.x);
+      acc.y = fmaf(g, ov.y, acc.y);
+      acc.z = fmaf(g, ov.z, acc.z);
+      acc.w = fmaf(g, ov.w, acc.w);
+    }
+  }
+  if ((int)threadIdx.x < DV / 4) reinterpret_cast<float4*>(out + ((int64_t)b * H + h) * DV)[threadIdx.x] = acc;
+}
+
+// w non-null: the combined kernel (o is then the layer's output [n_seq][H][dv]).
 template <typename IT>
 static void launch_decode(const mom_dims& d, int n_seq, const int32_t* idx, const int32_t* inv, const void* q,
                           const void* k, const void* v, const float* alpha, const float* beta, float* states,
-                          float* o, bool delta, hipStream_t st) {
+                          float* o, bool delta, hipStream_t st, const float* w = nullptr) {
   const int64_t slots = (int64_t)n_seq * (d.topk + 1) * d.H;
 #define MOM_DEC2(DK, DV, DELTA)                                                                                  \
-  hipLaunchKernelGGL((k_gdn_decode<IT, DK, DV, 4 * DV, DELTA>), dim3((unsigned)slots), dim3(4 * DV), 0, st,     \
-                     n_seq, d.H, d.M, d.topk, idx, inv, (const IT*)q, (const IT*)k, (const IT*)v, alpha, beta,      \
-                     states, o)
+  do {                                                                                                           \
+    if (w)                                                                                                       \
+      hipLaunchKernelGGL((k_gdn_decode_combined<IT, DK, DV, 4 * DV, DELTA>), dim3((unsigned)(n_seq * d.H)),      \
+                         dim3(4 * DV), 0, st, n_seq, d.H, d.M, d.topk, idx, inv, w, (const IT*)q, (const IT*)k,  \
+                         (const IT*)v, alpha, beta, states, o);                                                \
+    else                                                                                                         \
+      hipLaunchKernelGGL((k_gdn_decode<IT, DK, DV, 4 * DV, DELTA>), dim3((unsigned)slots), dim3(4 * DV), 0, st, \
+                         n_seq, d.H, d.M, d.topk, idx, inv, (const IT*)q, (const IT*)k, (const IT*)v, alpha,     \
+                         beta, states, o);                                                                     \
+  } while (0)
 #define MOM_DEC(DK, DV)           \
   do {                            \
     if (delta)                    \
@@ -170,7 +231,8 @@ static void launch_decode(const mom_dims& d, int n_seq, const int32_t* idx, cons
 namespace mom {
 static mom_status decode_step(bool delta, const mom_dims* dims, int32_t n_seq, const int32_t* idx,
                               const int32_t* inv, const void* q, const void* k, const void* v, const float* alpha,
-                              const float* beta, float* states, float* o, void* stream) {
+                              const float* beta, float* states, float* o, void* stream, bool combined = false,
+                              const float* w = nullptr) {
   mom_status s = check_dims(dims);
   if (s != MOM_OK) return s;
   if (dims->dv != 64 && dims->dv != 128 && dims->dv != 256) return MOM_ERR_UNSUPPORTED;
@@ -184,12 +246,13 @@ static mom_status decode_step(bool delta, const mom_dims* dims, int32_t n_seq, c
   MOM_CHECK_PTR(beta);
   MOM_CHECK_PTR(states);
   MOM_CHECK_PTR(o);
+  if (combined) MOM_CHECK_PTR(w);
   if (n_seq == 0) return MOM_OK;
   hipStream_t st = (hipStream_t)stream;
   if (dims->dtype == MOM_DTYPE_BF16)
-    launch_decode<f16_t>(*dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, delta, st);
+    launch_decode<f16_t>(*dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, delta, st, w);
   else
-    launch_decode<float>(*dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, delta, st);
+    launch_decode<float>(*dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, delta, st, w);
   return launch_status();
 }
 }  // namespace mom
@@ -204,4 +267,18 @@ extern "C" mom_status gla_decode_step(const mom_dims* dims, int32_t n_seq, const
                                       const void* q, const void* k, const void* v, const float* alpha,
                                       const float* beta, float* states, float* o, void* stream) {
   return mom::decode_step(false, dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, stream);
+}
+
+extern "C" mom_status gdn_decode_step_combined(const mom_dims* dims, int32_t n_seq, const int32_t* idx,
+                                               const int32_t* inv, const float* w, const void* q, const void* k,
+                                               const void* v, const float* alpha, const float* beta, float* states,
+                                               float* out, void* stream) {
+  return mom::decode_step(true, dims, n_seq, idx, inv, q, k, v, alpha, beta, states, out, stream, true, w);
+}
+
+extern "C" mom_status gla_decode_step_combined(const mom_dims* dims, int32_t n_seq, const int32_t* idx,
+                                               const int32_t* inv, const float* w, const void* q, const void* k,
+                                               const void* v, const float* alpha, const float* beta, float* states,
+                                               float* out, void* stream) {
+  return mom::decode_step(false, dims, n_seq, idx, inv, q, k, v, alpha, beta, states, out, stream, true, w);
 }

@@ -67,6 +67,8 @@ def lib():
         "gdn_chunk_bwd_workspace_bytes": [D, _I32, _I32],
         "gdn_decode_step": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
         "gla_decode_step": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+        "gdn_decode_step_combined": [D, _I32] + [_VP] * 11,
+        "gla_decode_step_combined": [D, _I32] + [_VP] * 11,
         "mom_combine": [D, _I32, _VP, _VP, _VP, _VP, _VP, _VP],
         "mom_combine_bwd": [D, _I32] + [_VP] * 8,
         "mom_route_bwd": [D] + [_VP] * 9 + [ctypes.c_size_t, _VP],
@@ -90,9 +92,9 @@ def lib():
 EXPORTS = ("mom_route", "mom_route_count", "mom_dispatch", "mom_dispatch_counted", "mom_dispatch_part",
            "mom_project", "mom_project_part", "gdn_chunk_fwd", "gla_chunk_fwd", "gdn_chunk_bwd", "gla_chunk_bwd",
            "gdn_chunk_fwd_train", "gla_chunk_fwd_train", "gdn_chunk_bwd_saved", "gla_chunk_bwd_saved",
-           "gdn_decode_step", "gla_decode_step", "mom_combine", "mom_combine_bwd", "mom_route_bwd",
-           "mom_dispatch_bwd", "mom_workspace_bytes", "gdn_chunk_workspace_bytes", "gdn_chunk_bwd_workspace_bytes",
-           "mom_status_string")
+           "gdn_decode_step", "gla_decode_step", "gdn_decode_step_combined", "gla_decode_step_combined",
+           "mom_combine", "mom_combine_bwd", "mom_route_bwd", "mom_dispatch_bwd", "mom_workspace_bytes",
+           "gdn_chunk_workspace_bytes", "gdn_chunk_bwd_workspace_bytes", "mom_status_string")
 
 
 def dims_of(cfg: LayerConfig, B: int | None = None, T: int | None = None) -> MomDims:
@@ -237,6 +239,14 @@ def gdn_chunk_bwd_workspace_bytes(dims, n_seg, n_rows):
 def gdn_decode_step(dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, stream=None):
     _check(lib().gdn_decode_step(ctypes.byref(dims), n_seq, _p(idx), _p(inv), _p(q), _p(k), _p(v), _p(alpha),
                                  _p(beta), _p(states), _p(o), _s(stream)), "gdn_decode_step")
+
+
+def decode_step_combined(rule, dims, n_seq, idx, inv, w, q, k, v, alpha, beta, states, out, stream=None):
+    """gdn_decode_step_combined (rule "gdn") or gla_decode_step_combined: the
+    decode step with the combine folded in; out [n_seq, H, dv] fp32."""
+    name = {"gdn": "gdn_decode_step_combined", "gla": "gla_decode_step_combined"}[rule]
+    _check(getattr(lib(), name)(ctypes.byref(dims), n_seq, _p(idx), _p(inv), _p(w), _p(q), _p(k), _p(v), _p(alpha),
+                                _p(beta), _p(states), _p(out), _s(stream)), name)
 
 
 def gla_decode_step(dims, n_seq, idx, inv, q, k, v, alpha, beta, states, o, stream=None):
@@ -574,7 +584,7 @@ class MomLayer:
         mom_dispatch_counted(d, b["idx"], x_t, alpha, beta, b["seg_off"], b["perm"], b["inv"], None, b["alpha_p"],
                              b["beta_p"], b["ws"], stream)
         mom_project(d, x_t, b["perm"], b["seg_off"], self.w_q, self.w_k, self.w_v, b["q"], b["k"], b["v"], stream)
-        step = gdn_decode_step if self.rule == "gdn" else gla_decode_step
-        step(b["dims"], n_seq, b["idx"], b["inv"], b["q"], b["k"], b["v"], alpha, beta, states, b["o"], stream)
-        mom_combine(b["dims"], n_seq, b["inv"], b["w"], b["o"], b["o"][b["NR"]:], b["out"], stream)
+        # the recurrent step with the combine folded in (no per-memory outputs)
+        decode_step_combined(self.rule, d, n_seq, b["idx"], b["inv"], b["w"], b["q"], b["k"], b["v"], alpha, beta,
+                             states, b["out"], stream)
         return b["out"], b

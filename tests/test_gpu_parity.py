@@ -600,6 +600,35 @@ def test_decode_step_head_shapes(dk, dv):
         S_ref = ref["state"]
 
 
+@pytest.mark.parametrize("name,dk,dv,rule", [("long32k", 128, 256, "gdn"), ("long32k", 128, 256, "gla"),
+                                          ("l380m", 64, 128, "gdn"), ("tiny_f32", 64, 64, "gdn")])
+def test_decode_combined_equals_step_and_combine(name, dk, dv, rule):
+    """The decode step with the combine folded in equals the per-slot decode
+    step followed by mom_combine bit for bit, outputs and states."""
+    cfg = dataclasses.replace(CFG[name], dk=dk, dv=dv)
+    n_seq = 64
+    log("decode combined", name, dk, dv, rule)
+    inp = synth.make_layer_inputs(dataclasses.replace(cfg, B=1, T=1), seed=4)
+    layer = mom.MomLayer(cfg, inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"], rule=rule)
+    S = to_gpu(synth.make_state(cfg, n_seq, seed=8))
+    d = synth.make_decode_step_inputs(cfg, n_seq, seed=300)
+    x = to_gpu(d["x"], mom.storage_dtype(cfg))
+    a_, be = to_gpu(d["alpha"]), to_gpu(d["beta"])
+    b = layer.buffers(n_seq, 1)
+    layer.route_dispatch_project(x, a_, be, b)
+    dims = b["dims"]
+    s1, s2 = S.clone(), S.clone()
+    out1 = torch.empty_like(b["out"])
+    step = mom.gdn_decode_step if rule == "gdn" else mom.gla_decode_step
+    step(dims, n_seq, b["idx"], b["inv"], b["q"], b["k"], b["v"], a_, be, s1, b["o"])
+    mom.mom_combine(dims, n_seq, b["inv"], b["w"], b["o"], b["o"][b["NR"]:], out1)
+    out2 = torch.full_like(out1, float("nan"))
+    mom.decode_step_combined(rule, dims, n_seq, b["idx"], b["inv"], b["w"], b["q"], b["k"], b["v"], a_, be, s2, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    assert torch.equal(s1, s2)
+
+
 def test_prefill_then_decode():
     """Decoding token T from the prefill's final state equals the last row of a
     prefill over T+1 tokens."""
