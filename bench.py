@@ -68,9 +68,12 @@ def stage_costs(cfg):
 
 
 def decode_costs(cfg, n_seq):
+    """Algorithmic bytes of the decode kernel (the recurrent step with the
+    combine folded in): every state read and written once, q, k, v and the
+    gates read, the layer's output row and the router weights."""
     K, H, dk, dv, D, M = cfg.K, cfg.H, cfg.dk, cfg.dv, cfg.D, cfg.M
     state = 2 * n_seq * (K + 1) * H * dk * dv * 4
-    io = n_seq * (H * dk * 2 + (K + 1) * H * (dk + dv) * 2 + 2 * H * (M + 1) * 4 + (K + 1) * H * dv * 4)
+    io = n_seq * (H * dk * 2 + (K + 1) * H * (dk + dv) * 2 + 2 * H * (M + 1) * 4 + H * dv * 4 + K * 4)
     return dict(bytes=state + io, flops=n_seq * (K + 1) * H * 6 * dk * dv)
 
 
@@ -338,16 +341,16 @@ def main():
             dlayer.decode_step(*steps_in[i % 4], states)
         torch.cuda.synchronize()
         dwall = time.perf_counter() - t0
-        # the decode kernel alone, from events around it in further steps
+        # the decode kernel alone (the recurrent step with the combine folded
+        # in), from events around it in further steps
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.decode_steps)]
         for i in range(args.decode_steps):
             xx, aa, bb = steps_in[i % 4]
             dlayer.route_dispatch_project(xx, aa, bb, db)
             ev[i][0].record()
-            mom.gdn_decode_step(db["dims"], n_seq, db["idx"], db["inv"], db["q"], db["k"], db["v"], aa, bb, states,
-                                db["o"])
+            mom.decode_step_combined("gdn", db["dims"], n_seq, db["idx"], db["inv"], db["w"], db["q"], db["k"],
+                                     db["v"], aa, bb, states, db["out"])
             ev[i][1].record()
-            mom.mom_combine(db["dims"], n_seq, db["inv"], db["w"], db["o"], db["o"][db["NR"]:], db["out"])
         torch.cuda.synchronize()
         dk_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
         dc = decode_costs(dcfg, n_seq)
