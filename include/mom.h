@@ -32,6 +32,8 @@
  *                    the backward, which then does not recompute them.
  *   mom_route_count, mom_dispatch_counted
  *                    route and histogram in one launch for a decode step.
+ *   gdn_decode_step_combined
+ *                    the decode step with the combine folded in.
  *   gdn_decode_step  one recurrent step per sequence (constant-cost inference,
  *                    jxzklqfsx.com write-up, introduction and inference section).
  *   mom_combine      router-weighted sum of the per-memory reads plus the
