@@ -126,6 +126,20 @@ def test_chunk_workspace_sizes():
 
 
 @needs_lib
+def test_decode_combined_checks():
+    """The decode step with the combine folded in needs the router weights and
+    takes the value widths gdn_decode_step takes."""
+    L = mom.lib()
+    d = _dims()
+    for f in (L.gdn_decode_step_combined, L.gla_decode_step_combined):
+        assert f(ctypes.byref(d), 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+        assert f(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+        assert f(ctypes.byref(_dims(dv=768)), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 None) == -3
+        assert f(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 0
+
+
+@needs_lib
 def test_route_count_checks():
     """The one-launch route and histogram serve one position per sequence only,
     and need the dispatch workspace."""
