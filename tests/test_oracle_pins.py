@@ -142,6 +142,42 @@ def test_projections_match_matmul():
             np.testing.assert_allclose(r["v"][t, j], v, rtol=1e-12, atol=1e-13)
 
 
+def test_project_head_rows():
+    """oracle.project_head (the checker of the GPU projections and of the
+    full-size layer slices) on a ragged token list with repeats, in an order
+    that is not token order, for every head and memory: its rows equal a numpy
+    matmul of the gathered x rows with that head's block of W_q / W_k[m] /
+    W_v[m] (keys then divided by their L2 norm), and equal the layer's own
+    projections of the tokens routed to m (slot j of token t)."""
+    cfg, inp = _tiny_inputs(B=2, T=37, D=24, H=2, dk=5, dv=7, M=4, K=2, seed=3)
+    r = _run_layer(cfg, inp, want_qkv=True)
+    x = inp["x"].astype(np.float64)
+    rng = np.random.default_rng(7)
+    toks = np.concatenate([rng.permutation(cfg.n_tok)[:41], [0, cfg.n_tok - 1, 17, 17]]).astype(np.int32)
+    for h in range(cfg.H):
+        sk, sv = slice(h * cfg.dk, (h + 1) * cfg.dk), slice(h * cfg.dv, (h + 1) * cfg.dv)
+        wq = inp["w_q"][sk].astype(np.float64)
+        q, k0, v0 = oracle.project_head(toks, x, wq, None, None)
+        assert k0 is None and v0 is None
+        np.testing.assert_allclose(q, x[toks] @ wq.T, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(q, r["q"][toks, h], rtol=1e-12, atol=1e-13)
+        for m in range(cfg.M + 1):
+            wk = inp["w_k"][m][sk].astype(np.float64)
+            wv = inp["w_v"][m][sv].astype(np.float64)
+            q2, k, v = oracle.project_head(toks, x, None, wk, wv)
+            assert q2 is None
+            kh = x[toks] @ wk.T
+            np.testing.assert_allclose(k, kh / np.linalg.norm(kh, axis=1, keepdims=True), rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(np.linalg.norm(k, axis=1), 1.0, rtol=1e-14)
+            np.testing.assert_allclose(v, x[toks] @ wv.T, rtol=1e-12, atol=1e-13)
+            # the layer's projections of the tokens this memory serves
+            for t, j in zip(*np.nonzero(np.concatenate([r["idx"], np.full((cfg.n_tok, 1), cfg.M)], 1) == m)):
+                row = np.nonzero(toks == t)[0]
+                if len(row):
+                    np.testing.assert_allclose(k[row[0]], r["k"][t, j, h], rtol=1e-12, atol=1e-13)
+                    np.testing.assert_allclose(v[row[0]], r["v"][t, j, h], rtol=1e-12, atol=1e-13)
+
+
 # --------------------------------------------------------------------------- recurrence
 def test_gdn_hand_example():
     g = json.load(open(os.path.join(GOLD, "gdn_hand_2x2.json")))
