@@ -58,6 +58,10 @@
  *     negative mom_status and enqueues nothing.  A launch error returns
  *     MOM_ERR_LAUNCH.  Kernel faults surface on the stream, as with any HIP call.
  *   - Every pointer must be 16-byte aligned.  Inputs must be finite.
+ *   - Forget gates alpha lie in [0, 1]; alpha = 0 clears the state at that row
+ *     (the chunked entry points hold log alpha at or above -30, a decay of
+ *     ~9e-14, so the result stays finite and equals the clearing to float32
+ *     resolution).  The gradient entry points need alpha > 0.
  *   - Identical inputs give bit-identical outputs (no floating-point atomics).
  *   - Layouts are row-major with the shapes given below.
  *
@@ -235,7 +239,8 @@ mom_status gla_chunk_fwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, in
  * time); these are the chain rule applied to the recurrence above, evaluated
  * in the same chunk form (half operands on the matrix cores, float32
  * accumulation and states).  Only the half (dims->dtype == MOM_DTYPE_BF16)
- * storage is supported; float32 returns MOM_ERR_UNSUPPORTED.
+ * storage is supported; float32 returns MOM_ERR_UNSUPPORTED.  Every alpha
+ * of the rows run must be > 0 (d_alpha = d(log alpha) / alpha).
  *   inputs:   as gdn_chunk_fwd (dims, segments, slots, row_token, q, k, v,
  *             alpha_p, beta_p, state_in or NULL = zeros)
  *   d_o        [N][H][dv] float32

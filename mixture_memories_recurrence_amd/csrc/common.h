@@ -29,6 +29,17 @@ __device__ __forceinline__ float load_as_f32(const f16_t* p) { return (float)*p;
 __device__ __forceinline__ void store_from_f32(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_from_f32(f16_t* p, float v) { *p = (f16_t)v; }
 
+// ---------------------------------------------------------------- forget gates
+// The chunk form works with prefix sums of log alpha.  A gate of 0 (log = -inf)
+// would turn the decay ratios e^{g_i - g_j} into NaN, so each row's log gate is
+// held at or above -30: e^{-30} ~ 9e-14 is already a zero decay at float32's
+// resolution of the state, and every sum stays finite.
+constexpr float kLogGateFloor = -30.f;
+__device__ __forceinline__ float log_gate(float a) { return fmaxf(logf(a), kLogGateFloor); }
+// The same in float64, for prefix sums whose differences must keep float32's
+// relative precision after a floored row (a sum near -30 loses 5 bits in float32).
+__device__ __forceinline__ double log_gate_f64(float a) { return fmax(log((double)a), (double)kLogGateFloor); }
+
 // ---------------------------------------------------------------- derived sizes
 struct Sizes {
   int64_t NT, NR, N, n_seg, n_state;

@@ -52,7 +52,8 @@ __device__ __forceinline__ bool decode_slot(int n_seq, int H, int M, int K, int 
     m = M;
     row = (int64_t)n_seq * K + b;
   }
-  if ((unsigned)m > (unsigned)M) return false;
+  // a routed slot names one of the M routed memories; only the shared slot (j = K) is memory M
+  if (j < K && (unsigned)m >= (unsigned)M) return false;
   const float ag = alpha[((int64_t)b * H + h) * (M + 1) + m];
   const float cg = beta[((int64_t)b * H + h) * (M + 1) + m];
   for (int e = tid; e < DK; e += NT) {

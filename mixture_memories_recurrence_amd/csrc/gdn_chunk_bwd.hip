@@ -428,7 +428,7 @@ __global__ __launch_bounds__(512) void k_gdn_grad(
     if (lane < L) {
       aa = alpha_p[(r0 + lane) * H + h];
       bb = beta_p[(r0 + lane) * H + h];
-      g = logf(aa);
+      g = log_gate(aa);
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {

@@ -373,7 +373,7 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
   // gates: lane i holds g_i (inclusive prefix of log alpha; 0 past L) and c_i
   float g = 0.f, bb = 0.f;
   if (lane < L) {
-    g = logf(alpha_p[(r0 + lane) * H + h]);
+    g = log_gate(alpha_p[(r0 + lane) * H + h]);
     bb = beta_p[(r0 + lane) * H + h];
   }
 #pragma unroll

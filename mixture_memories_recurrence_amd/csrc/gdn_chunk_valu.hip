@@ -38,7 +38,8 @@ __global__ __launch_bounds__(256) void k_gdn_chunk_valu(int H, int dv, int n_seg
   __shared__ float As[VC][VC + 1];
   __shared__ float Ps[VC][VC + 1];
   __shared__ float Us[VC][VDVB + 1];
-  __shared__ float gs[VC], bs[VC];
+  __shared__ double gs[VC];  // prefix sums of log a in float64 (see log_gate_f64)
+  __shared__ float bs[VC];
 
   const int nb = dv / VDVB;
   const int cb = blockIdx.x % nb;
@@ -64,9 +65,9 @@ __global__ __launch_bounds__(256) void k_gdn_chunk_valu(int H, int dv, int n_seg
       Qs[i][d] = load_as_f32(q + (tk * H + h) * DK + d);
     }
     if (tid == 0) {
-      float g = 0.f;
+      double g = 0.0;
       for (int i = 0; i < L; ++i) {
-        g += logf(alpha_p[(r0 + i) * H + h]);
+        g += log_gate_f64(alpha_p[(r0 + i) * H + h]);
         gs[i] = g;
         bs[i] = beta_p[(r0 + i) * H + h];
       }
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(256) void k_gdn_chunk_valu(int H, int dv, int n_seg
           kk = fmaf(Ks[i][d], Ks[j][d], kk);
           qk = fmaf(Qs[i][d], Ks[j][d], qk);
         }
-        const float dec = expf(gs[i] - gs[j]);
+        const float dec = expf((float)(gs[i] - gs[j]));
         if (DELTA && j < i) a = bs[i] * dec * kk;
         p = dec * qk;
       }
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(256) void k_gdn_chunk_valu(int H, int dv, int n_seg
         if (DELTA) {
           float ks = 0.f;
           for (int d = 0; d < DK; ++d) ks = fmaf(Ks[i][d], Ss[d][n], ks);
-          r = bs[i] * (vv - expf(gs[i]) * ks);
+          r = bs[i] * (vv - expf((float)gs[i]) * ks);
         } else {
           r = bs[i] * vv;
         }
@@ -121,18 +122,18 @@ __global__ __launch_bounds__(256) void k_gdn_chunk_valu(int H, int dv, int n_seg
       if (i < L) {
         float qs = 0.f;
         for (int d = 0; d < DK; ++d) qs = fmaf(Qs[i][d], Ss[d][n], qs);
-        float acc = expf(gs[i]) * qs;
+        float acc = expf((float)gs[i]) * qs;
         for (int j = 0; j <= i; ++j) acc = fmaf(Ps[i][j], Us[j][n], acc);
         o[((r0 + i) * H + h) * dv + cb * VDVB + n] = acc;
       }
     }
     __syncthreads();
     // S <- e^{g_L} S + K~^T U
-    const float gL = gs[L - 1];
+    const double gL = gs[L - 1];
     for (int e = tid; e < DK * VDVB; e += 256) {
       const int d = e / VDVB, n = e % VDVB;
-      float acc = expf(gL) * Ss[d][n];
-      for (int j = 0; j < L; ++j) acc = fmaf(expf(gL - gs[j]) * Ks[j][d], Us[j][n], acc);
+      float acc = expf((float)gL) * Ss[d][n];
+      for (int j = 0; j < L; ++j) acc = fmaf(expf((float)(gL - gs[j])) * Ks[j][d], Us[j][n], acc);
       Ss[d][n] = acc;
     }
   }

@@ -3,6 +3,7 @@ same seeded inputs.  Integer results (router indices, dispatch permutation)
 must match bit for bit; floating-point results must meet the layer's
 tolerances (bf16 inputs: max-abs 2e-2, rel-L2 5e-3; float32: 1e-5)."""
 import dataclasses
+import functools
 
 import numpy as np
 import pytest
@@ -309,12 +310,15 @@ SEG_LENGTHS = [0, 1, 63, 64, 65, 130, 200, 7, 128, 0, 300]
 @pytest.mark.parametrize("store,dk,dv,rule", [("f32", 64, 64, "gdn"), ("f32", 128, 256, "gdn"), ("f16", 128, 256, "gdn"),
                                                ("f16", 64, 128, "gdn"), ("f32", 64, 64, "gla"),
                                                ("f16", 128, 256, "gla"), ("f16", 64, 128, "gla"),
-                                               ("f32", 64, 64, "deltanet"), ("f16", 128, 256, "deltanet")])
+                                               ("f32", 64, 64, "deltanet"), ("f16", 128, 256, "deltanet"),
+                                               ("f32", 64, 64, "gate0"), ("f16", 128, 256, "gate0")])
 def test_chunk_segments(store, dk, dv, rule):
     """Packed segments of ragged lengths (empty, one row, chunk +- 1, several
     chunks) with random entering states, for the update rules: Gated DeltaNet,
     gated linear attention, and DeltaNet (Gated DeltaNet with the forget gate
-    fixed at 1)."""
+    fixed at 1).  "gate0": Gated DeltaNet with forget gates of exactly 0 at
+    rows inside chunks (the state is cleared there; the chunk form's log gates
+    must stay finite)."""
     H = 2
     lens = np.array(SEG_LENGTHS)
     seg_off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
@@ -323,6 +327,8 @@ def test_chunk_segments(store, dk, dv, rule):
     ch = synth.make_chain_inputs(N, H, dk, dv, seed=dk + dv, store=store)
     if rule == "deltanet":
         ch["alpha"] = np.ones_like(ch["alpha"])
+    if rule == "gate0":  # rows 5, 42, 79, ...: mid-chunk in every segment longer than 5 rows
+        ch["alpha"][5::37] = 0.0
     n_tok = N + 5
     row_token = np.random.default_rng(1).permutation(n_tok)[:N].astype(np.int32)
     qtok = np.zeros((n_tok, H, dk), np.float32)
@@ -503,28 +509,60 @@ def oracle_bh_slice(cfg, inp, idx, w, b_sel, h, t_max):
     return o_rows, out, states
 
 
-@pytest.mark.parametrize("name,t_max", [("l380m", None), ("l1b3", 700), ("m16", 700), ("long32k", 800)])
-def test_layer_full_size_sampled(name, t_max):
-    """Full-size forward in the benchmark's launch configuration; the checker
-    recomputes one (sequence, head) slice: every memory's reads up to t_max,
-    the combined outputs, and (when t_max = T) the final states."""
+# (sequence, head) slices the checker recomputes at full size and full length
+FULL_SLICES = {"l380m": [(7, 3), (0, 0)], "l1b3": [(3, 7), (0, 2)], "m16": [(3, 3), (1, 0)],
+               "long32k": [(0, 7), (0, 2)]}
+
+
+@functools.lru_cache(maxsize=1)
+def full_size_run(name):
+    """One full-size forward of config `name` in the benchmark's launch
+    configuration (two-stream schedule, zero entering state); keeps on the host
+    the inputs, the router's outputs and, for the heads of FULL_SLICES, the
+    per-row reads, the outputs and the final states."""
     cfg = CFG[name]
     log("layer full", name)
     inp = synth.make_layer_inputs(cfg, seed=0)
-    out, st, b = run_layer_gpu(cfg, inp)
-    idx = b["idx"].cpu().numpy()
+    layer = make_layer(cfg, inp)
+    g = gpu_inputs(cfg, inp)
+    out, st, b = layer.forward(g["x"], g["alpha"], g["beta"])
+    torch.cuda.synchronize()
+    heads = sorted({h for _, h in FULL_SLICES[name]})
+    res = dict(cfg=cfg, inp=inp, idx=b["idx"].cpu().numpy(),
+               o={h: b["o"][:, h].cpu().numpy() for h in heads},
+               out={h: out[:, h].cpu().numpy() for h in heads},
+               state={h: st[:, :, h].cpu().numpy() for h in heads})
+    del out, st, b, layer, g
+    torch.cuda.empty_cache()
     idx_ref, w_ref = oracle.route(inp["x"], inp["w_r"], inp["bias"], cfg.K)
-    np.testing.assert_array_equal(idx, idx_ref)
-    o_gpu = b["o"].cpu().numpy()
-    T = cfg.T if t_max is None else t_max
-    b_sel, h = cfg.B - 1, cfg.H - 1
-    o_rows, out_ref, states = oracle_bh_slice(cfg, inp, idx_ref, w_ref, b_sel, h, T)
+    np.testing.assert_array_equal(res["idx"], idx_ref)
+    res["w_ref"] = w_ref
+    return res
+
+
+@pytest.mark.parametrize("name,b_sel,h", [(n, b, h) for n, sl in FULL_SLICES.items() for b, h in sl])
+def test_layer_full_size(name, b_sel, h):
+    """Full-size, full-length forward in the benchmark's launch configuration;
+    the checker recomputes one (sequence, head) slice over the whole sequence:
+    every memory's reads at its rows, the combined outputs, and every memory's
+    final state (for the long-context shape, the end of its 512-chunk shared
+    chain and 256-chunk routed chains).  The last 512 outputs are also checked
+    on their own."""
+    r = full_size_run(name)
+    cfg, inp = r["cfg"], r["inp"]
+    log("  slice b=%d h=%d" % (b_sel, h))
+    o_rows, out_ref, states = oracle_bh_slice(cfg, inp, r["idx"], r["w_ref"], b_sel, h, cfg.T)
     rows = np.array(sorted(o_rows))
-    assert_close("o (slice)", o_gpu[rows, h], np.stack([o_rows[r] for r in rows]), *TOL[cfg.dtype])
-    assert_close("out (slice)", out[b_sel * cfg.T:b_sel * cfg.T + T, h], out_ref, *TOL[cfg.dtype])
-    if t_max is None:
-        for m, S in states.items():
-            assert_close("state m=%d" % m, st[b_sel, m, h], S, *TOL[cfg.dtype])
+    tol = TOL[cfg.dtype]
+    assert_close("o (slice)", r["o"][h][rows], np.stack([o_rows[rr] for rr in rows]), *tol)
+    out_got = r["out"][h][b_sel * cfg.T:(b_sel + 1) * cfg.T]
+    assert_close("out (slice)", out_got, out_ref, *tol)
+    assert_close("out (last 512)", out_got[-512:], out_ref[-512:], *tol)
+    for m in range(cfg.M + 1):
+        if m in states:
+            assert_close("state m=%d" % m, r["state"][h][b_sel, m], states[m], *tol)
+        else:  # a memory this sequence never reached keeps its (zero) entering state
+            assert not np.any(r["state"][h][b_sel, m]), "unreached memory %d changed" % m
 
 
 # ------------------------------------------------------------------ resume, decode, determinism
@@ -627,6 +665,49 @@ def test_decode_combined_equals_step_and_combine(name, dk, dv, rule):
     torch.cuda.synchronize()
     assert torch.equal(out1, out2)
     assert torch.equal(s1, s2)
+
+
+def test_decode_routed_slot_naming_shared_memory_does_nothing():
+    """A routed slot whose index names the shared memory (idx == M, not a
+    routed memory) is out of range: it must not update the shared memory's
+    state a second time, write an output row, or add to the combined output."""
+    cfg = CFG["l380m"]
+    n_seq, bad_b, bad_j = 8, 3, 1
+    inp = synth.make_layer_inputs(dataclasses.replace(cfg, B=1, T=1), seed=5)
+    layer = make_layer(cfg, inp)
+    S = to_gpu(synth.make_state(cfg, n_seq, seed=8))
+    d = synth.make_decode_step_inputs(cfg, n_seq, seed=400)
+    a_, be = to_gpu(d["alpha"]), to_gpu(d["beta"])
+    b = layer.buffers(n_seq, 1)
+    layer.route_dispatch_project(to_gpu(d["x"], torch.bfloat16), a_, be, b)
+    dims, M = b["dims"], cfg.M
+    idx_bad = b["idx"].clone()
+    routed_m = int(b["idx"][bad_b, bad_j])
+    idx_bad[bad_b, bad_j] = M
+    s_ref, s_bad = S.clone(), S.clone()
+    o_ref = torch.full_like(b["o"], float("nan"))
+    o_bad = torch.full_like(b["o"], float("nan"))
+    mom.gdn_decode_step(dims, n_seq, b["idx"], b["inv"], b["q"], b["k"], b["v"], a_, be, s_ref, o_ref)
+    mom.gdn_decode_step(dims, n_seq, idx_bad, b["inv"], b["q"], b["k"], b["v"], a_, be, s_bad, o_bad)
+    out_bad = torch.full_like(b["out"], float("nan"))
+    s_bad2 = S.clone()
+    mom.decode_step_combined("gdn", dims, n_seq, idx_bad, b["inv"], b["w"], b["q"], b["k"], b["v"], a_, be, s_bad2,
+                             out_bad)
+    torch.cuda.synchronize()
+    assert torch.equal(s_bad[bad_b, M], s_ref[bad_b, M])            # shared memory updated once
+    assert torch.equal(s_bad[bad_b, routed_m], S[bad_b, routed_m])  # the dropped slot's memory untouched
+    keep = [i for i in range(n_seq) if i != bad_b]
+    assert torch.equal(s_bad[keep], s_ref[keep])
+    bad_row = int(b["inv"][bad_b, bad_j])
+    assert torch.isnan(o_bad[bad_row]).all()                          # no output row written
+    assert torch.equal(s_bad2, s_bad)
+    # combined output of that sequence: the shared read plus the other slots only
+    NR = b["NR"]
+    exp = o_ref[NR + bad_b].double()
+    for j in range(cfg.K):
+        if j != bad_j:
+            exp = exp + b["w"][bad_b, j].double() * o_ref[int(b["inv"][bad_b, j])].double()
+    assert_close("combined out, dropped slot", out_bad[bad_b].cpu().numpy(), exp.cpu().numpy(), 1e-5, 1e-6)
 
 
 def test_prefill_then_decode():
