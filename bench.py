@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--no-single", action="store_true", help="skip the single enlarged-memory line")
     p.add_argument("--no-gla", action="store_true", help="skip the gated linear attention layer line")
     p.add_argument("--no-bwd", action="store_true", help="skip the recurrence-gradient line")
+    p.add_argument("--prefill", default="l1b3,m16,long32k",
+                   help="other prefill workloads timed after the headline one (comma list; '' for none)")
     p.add_argument("--serial", action="store_true",
                    help="time the steps in order on one stream (default: the layer's two-stream schedule)")
     p.add_argument("--traffic", default=None,
@@ -45,9 +47,11 @@ def parse():
     return p.parse_args()
 
 
-def stage_costs(cfg):
+def stage_costs(cfg, state_in=False):
     """Algorithmic bytes and flops of one launch of each stage for one layer
-    forward: every tensor read or written once at its stored width."""
+    forward: every tensor read or written once at its stored width.  The chunk
+    stage writes the final states, and reads entering states only when the
+    step is given them (state_in)."""
     NT = cfg.B * cfg.T
     K, H, dk, dv, D, M, C = cfg.K, cfg.H, cfg.dk, cfg.dv, cfg.D, cfg.M, cfg.chunk
     N = NT * (K + 1)
@@ -61,10 +65,42 @@ def stage_costs(cfg):
     c["project"] = dict(bytes=NT * D * xb * (K + 2) + proj_w + (NT * H * dk + N * H * (dk + dv)) * ab,
                         flops=2 * D * (NT * H * dk + N * H * (dk + dv)))
     chunk_flops_row = 6 * C * dk + 4 * C * dv + 6 * dk * dv + (2 * C * C) // 3
-    c["chunk"] = dict(bytes=N * H * (2 * dk * ab + dv * ab + 8 + dv * 4) + 2 * n_state * H * dk * dv * 4,
+    c["chunk"] = dict(bytes=N * H * (2 * dk * ab + dv * ab + 8 + dv * 4) + (2 if state_in else 1) * n_state * H * dk * dv * 4,
                       flops=N * H * chunk_flops_row)
     c["combine"] = dict(bytes=NT * H * dv * 4 * (K + 2) + NT * K * 8, flops=2 * NT * K * H * dv)
     return c
+
+
+def layer_bound(cfg):
+    """Throughput bound of one layer forward from the per-token costs of the
+    unfused design: route, dispatch (with a gathered copy of x), combine and
+    the chunk recurrence at the HBM peak, the projections at the MFMA peak
+    (the chunk stage at whichever of its bytes or flops takes longer).
+    Returns (tokens/s, per-stage microseconds)."""
+    NT = cfg.B * cfg.T
+    K, H, dk, dv, D, C = cfg.K, cfg.H, cfg.dk, cfg.dv, cfg.D, cfg.chunk
+    A = K + 1
+    bw, mf = HBM_PEAK_GBS * 1e9, MFMA_PEAK_TFLOPS * 1e12
+    per_tok = {"route": (2 * D + 8 * K) / bw,
+               "dispatch": (2 * D * (1 + K) + 16 * K * H + 12 * K) / bw,
+               "project": (2 * D * H * dk + A * 2 * D * H * (dk + dv)) / mf,
+               "chunk": max(A * (2 * H * dk * 2 + 2 * H * dv + 8 * H + 4 * H * dv) / bw,
+                            A * H * (6 * C * dk + 4 * C * dv + 6 * dk * dv + (2 * C * C) / 3) / mf),
+               "combine": (4 * A * H * dv + 8 * K + 4 * H * dv) / bw}
+    us = {k: v * NT * 1e6 for k, v in per_tok.items()}
+    return NT / (sum(us.values()) * 1e-6), us
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def decode_costs(cfg, n_seq):
@@ -90,9 +126,23 @@ def time_cpu_baseline(cfg, inp):
     oracle.layer((B, T, cfg.D, cfg.H, cfg.dk, cfg.dv, cfg.M, cfg.K), x, inp["w_r"], inp["bias"], inp["w_q"],
                  inp["w_k"], inp["w_v"], al, be)
     dt = time.perf_counter() - t0
-    return {"value": NT / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+    return {"value": NT / dt, "unit": "tokens/s", "cores": oracle.threads(), "cpu": cpu_model(), "kind": "oracle",
             "sample": "fp64 oracle, one layer forward over the whole step batch (%d sequences x %d tokens, %.1f s)"
                       % (B, T, dt)}
+
+
+def time_oracle_sample(cfg, inp, T):
+    """The fp64 oracle on the first T tokens of the first sequence of cfg's
+    inputs (a bounded sample, a few seconds): tokens/s."""
+    from oracle import oracle
+    x, al, be = inp["x"][:T], inp["alpha"][:T], inp["beta"][:T]
+    oracle.lib()
+    t0 = time.perf_counter()
+    oracle.layer((1, T, cfg.D, cfg.H, cfg.dk, cfg.dv, cfg.M, cfg.K), x, inp["w_r"], inp["bias"], inp["w_q"],
+                 inp["w_k"], inp["w_v"], al, be)
+    dt = time.perf_counter() - t0
+    return {"value": round(T / dt, 1), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": "fp64 oracle, one sequence x %d tokens of this workload (%.1f s)" % (T, dt)}
 
 
 def time_gla_layer(cfg, inp, x, alpha, beta, steps, warmup):
@@ -216,29 +266,33 @@ def time_single_memory(steps, warmup):
             "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
-              file=sys.stderr)
-        sys.exit(2)
-    import torch
-    from mixture_memories_recurrence_amd import mom, synth
+STAGES = ["route", "dispatch", "project", "chunk", "combine"]
 
-    cfg = synth.CONFIGS[args.workload]
-    inp = synth.make_layer_inputs(cfg, seed=0)
-    layer = mom.MomLayer(cfg, inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"])
-    sd = mom.storage_dtype(cfg)
-    x = torch.from_numpy(inp["x"]).to(sd).cuda()
-    alpha = torch.from_numpy(inp["alpha"]).cuda()
-    beta = torch.from_numpy(inp["beta"]).cuda()
-    state = torch.empty(cfg.B, cfg.M + 1, cfg.H, cfg.dk, cfg.dv, dtype=torch.float32, device="cuda")
-    b = layer.buffers(cfg.B, cfg.T)
-    NT, N = b["NT"], b["N"]
-    stages = ["route", "dispatch", "project", "chunk", "combine"]
 
-    def step(ev=None):
-        d = b["dims"]
+class Workload:
+    """One prefill workload on the GPU: inputs resident in HBM, the layer, its
+    buffers, and the two ways of running a step (the layer's own two-stream
+    schedule, and the stages in order on one stream with optional events
+    between them)."""
+
+    def __init__(self, name):
+        import torch
+        from mixture_memories_recurrence_amd import mom, synth
+        self.mom = mom
+        self.cfg = cfg = synth.CONFIGS[name]
+        self.inp = inp = synth.make_layer_inputs(cfg, seed=0)
+        self.layer = mom.MomLayer(cfg, inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"])
+        sd = mom.storage_dtype(cfg)
+        self.x = torch.from_numpy(inp["x"]).to(sd).cuda()
+        self.alpha = torch.from_numpy(inp["alpha"]).cuda()
+        self.beta = torch.from_numpy(inp["beta"]).cuda()
+        self.state = torch.empty(cfg.B, cfg.M + 1, cfg.H, cfg.dk, cfg.dv, dtype=torch.float32, device="cuda")
+        self.b = self.layer.buffers(cfg.B, cfg.T)
+
+    def step_serial(self, ev=None):
+        mom, cfg, b, layer = self.mom, self.cfg, self.b, self.layer
+        x, alpha, beta = self.x, self.alpha, self.beta
+        d, N, NT = b["dims"], b["N"], b["NT"]
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         rec(0)
         mom.mom_route(d, x, layer.w_r, layer.bias, b["idx"], b["w"])
@@ -249,50 +303,103 @@ def main():
         mom.mom_project(d, x, b["perm"], b["seg_off"], layer.w_q, layer.w_k, layer.w_v, b["q"], b["k"], b["v"])
         rec(3)
         mom.gdn_chunk_fwd(d, b["n_seg"], N, NT, cfg.B * (cfg.M + 1), b["seg_off"], b["seg_state"], b["perm"],
-                          b["q"], b["k"], b["v"], b["alpha_p"], b["beta_p"], None, state, b["o"], b["ws_chunk"])
+                          b["q"], b["k"], b["v"], b["alpha_p"], b["beta_p"], None, self.state, b["o"], b["ws_chunk"])
         rec(4)
         mom.mom_combine(d, NT, b["inv"], b["w"], b["o"], b["o"][b["NR"]:], b["out"])
         rec(5)
 
-    def step_overlapped():
+    def step_overlapped(self):
         # the layer's own schedule: the shared memory's path on a second stream
-        layer.forward(x, alpha, beta, state_out=state)
+        self.layer.forward(self.x, self.alpha, self.beta, state_out=self.state)
 
-    timed_step = step if args.serial else step_overlapped
-    for _ in range(args.warmup):
-        timed_step()
-    # timed region: K whole steps, nothing recorded between the kernels
-    torch.cuda.synchronize()
-    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    t0 = time.perf_counter()
-    step_ev[0].record()
-    for i in range(args.steps):
-        timed_step()
-    step_ev[1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    value = NT / (wall / args.steps)
-    # per-stage breakdown: the same K steps again with an event between the
-    # stages (each record adds a few microseconds between kernels, so these
-    # steps are not the timed ones)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    st_ms = {s: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]))
-             for j, s in enumerate(stages)}
+    def time_steps(self, steps, warmup, serial=False):
+        """K whole steps after W warm-up steps, nothing recorded between the
+        kernels; returns (wall ms per step, GPU-event ms per step)."""
+        import torch
+        fn = self.step_serial if serial else self.step_overlapped
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        t0 = time.perf_counter()
+        ev[0].record()
+        for _ in range(steps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall * 1e3 / steps, ev[0].elapsed_time(ev[1]) / steps
 
+    def stage_ms(self, steps):
+        """Per-stage times: K more steps in order on one stream with an event
+        between the stages (each record adds a few microseconds between
+        kernels, so these steps are not the timed ones)."""
+        import torch
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            self.step_serial(events[i])
+        torch.cuda.synchronize()
+        return {s: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(steps)]))
+                for j, s in enumerate(STAGES)}
+
+
+def stage_table(cfg, st_ms):
     costs = stage_costs(cfg)
     kern = {}
-    for s in stages:
+    for s in STAGES:
         t = st_ms[s] * 1e-3
         kern[s] = {"ms": round(st_ms[s], 4), "GB/s": round(costs[s]["bytes"] / t / 1e9, 1),
                    "TFLOP/s": round(costs[s]["flops"] / t / 1e12, 2),
                    "hbm_frac": round(costs[s]["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
                    "mfma_frac": round(costs[s]["flops"] / t / 1e12 / MFMA_PEAK_TFLOPS, 4)}
-    dom = max(stages, key=lambda s: st_ms[s])
+    return kern
+
+
+def describe(cfg):
+    return ("%s: B=%d T=%d D=%d H=%d dk=%d dv=%d M=%d top-%d + shared, %s inputs, fp32 state"
+            % (cfg.name, cfg.B, cfg.T, cfg.D, cfg.H, cfg.dk, cfg.dv, cfg.M, cfg.K, cfg.dtype))
+
+
+def time_prefill(name, steps, warmup, cpu_tokens):
+    """Tokens/s of another prefill workload (the layer's two-stream schedule),
+    its per-stage times, the fraction of its layer bound, and the oracle on a
+    bounded sample of it."""
+    import torch
+    w = Workload(name)
+    cfg = w.cfg
+    ms, gpu_ms = w.time_steps(steps, warmup)
+    st = w.stage_ms(steps)
+    NT = cfg.B * cfg.T
+    bound, _ = layer_bound(cfg)
+    r = {"workload": describe(cfg), "tokens_per_s": round(NT / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+         "gpu_ms_per_step": round(gpu_ms, 4), "bound_tokens_per_s": round(bound, 1),
+         "frac_of_bound": round(NT / (ms * 1e-3) / bound, 4), "stages": stage_table(cfg, st)}
+    if cpu_tokens:
+        r["cpu_baseline"] = time_oracle_sample(cfg, w.inp, min(cpu_tokens, cfg.T))
+    del w
+    torch.cuda.empty_cache()
+    return r
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mixture_memories_recurrence_amd import mom, synth
+
+    w = Workload(args.workload)
+    cfg, inp, x, alpha, beta = w.cfg, w.inp, w.x, w.alpha, w.beta
+    NT = cfg.B * cfg.T
+    ms_per_step, gpu_ms = w.time_steps(args.steps, args.warmup, serial=args.serial)
+    value = NT / (ms_per_step * 1e-3)
+    st_ms = w.stage_ms(args.steps)
+    kern = stage_table(cfg, st_ms)
+    costs = stage_costs(cfg)
+    dom = max(STAGES, key=lambda s: st_ms[s])
     t = st_ms[dom] * 1e-3
     ai = costs[dom]["flops"] / max(costs[dom]["bytes"], 1)
     if ai > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
@@ -304,23 +411,24 @@ def main():
                                          "traffic_%s.json" % cfg.name)
     traffic = pmc_traffic.load_traffic(tpath, dom, cfg.name)
     roofline = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
-                "traffic": traffic, "kernel": "%s (%s)" % (dom, ", ".join(pmc_traffic.STAGES[dom][0])),
+                "traffic": traffic, "kernel": "%s (%s)" % (dom, ", ".join(pmc_traffic.stage_kernels(dom, cfg.dtype))),
                 "algorithmic_bytes": costs[dom]["bytes"], "algorithmic_flops": costs[dom]["flops"]}
+    lb, lb_us = layer_bound(cfg)
 
     res = {
         "metric": "MoM layer fwd tokens/s (T=2048, M=4 top-2+shared) + decode tokens/s; % roofline",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
-        "gpu_ms_per_step": round(step_ev[0].elapsed_time(step_ev[1]) / args.steps, 4),
+        "gpu_ms_per_step": round(gpu_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": "%s: B=%d T=%d D=%d H=%d dk=%d dv=%d M=%d top-%d + shared, %s inputs, fp32 state"
-                               % (cfg.name, cfg.B, cfg.T, cfg.D, cfg.H, cfg.dk, cfg.dv, cfg.M, cfg.K, cfg.dtype),
-                   "tokens_per_step": NT, "chunk": cfg.chunk},
+        "config": {"workload": describe(cfg), "tokens_per_step": NT, "chunk": cfg.chunk},
         "roofline": roofline,
+        "layer_bound": {"tokens_per_s": round(lb, 1), "frac": round(value / lb, 4),
+                        "stage_us": {k: round(v, 1) for k, v in lb_us.items()}},
         "stages": kern,
     }
-
+    del w
     if not args.no_decode:
         dcfg = synth.CONFIGS["long32k"]
         n_seq = synth.DECODE_SEQS
@@ -371,6 +479,10 @@ def main():
         res["single_memory"] = time_single_memory(args.steps, args.warmup)
     if not args.no_bwd:
         res["chunk_bwd"] = time_chunk_bwd(cfg, inp, x, alpha, beta, args.steps, args.warmup)
+
+    if args.prefill:
+        res["prefill"] = {n: time_prefill(n, args.steps, args.warmup, 0 if args.no_cpu_baseline else 512)
+                          for n in args.prefill.split(",") if n and n != cfg.name}
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = time_cpu_baseline(cfg, inp)

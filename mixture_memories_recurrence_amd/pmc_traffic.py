@@ -46,6 +46,13 @@ STAGES = {
 }
 
 
+def stage_kernels(stage: str, dtype: str = "bf16"):
+    """Kernels the stage launches for the given storage type ("bf16" or "f32")."""
+    if stage == "chunk":
+        return ("k_gdn_prep", "k_gdn_chain") if dtype == "bf16" else ("k_gdn_chunk_valu",)
+    return STAGES[stage][0]
+
+
 def source_hash(stage: str) -> str:
     h = hashlib.sha256()
     for f in STAGES[stage][1] + ("common.h",):

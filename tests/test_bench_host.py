@@ -5,8 +5,12 @@ layer (every tensor read or written once at its stored width) they are route
 MFLOP, with two choices of this design counted as they are: the dispatch
 writes no gathered copy of x (the projection's loads gather the rows), so it
 moves 292 B (index arrays and gates) instead of 6,296; and the chunk stage
-also counts reading and writing the recurrent states, 2 x 40 slots x 4 heads
-x 128 x 256 x 4 B over 16,384 tokens = 2,560 B."""
+also counts writing the final recurrent states, 40 slots x 4 heads x 128 x
+256 x 4 B over 16,384 tokens = 1,280 B (and as much again for reading them
+when the step is given entering states; the timed step starts from zeros).
+The layer bounds (unfused design, every stage at its peak) are 96.4, 34.3,
+60.6 and 34.3 M tokens/s for the 380M, 1.3B, 16-memory and long-context
+shapes."""
 import os
 import subprocess
 import sys
@@ -36,6 +40,22 @@ def test_stage_costs_per_token():
     assert per_tok["route"] == pytest.approx(2064, abs=1)
     assert per_tok["dispatch"] == pytest.approx(292, abs=0.01)
     assert per_tok["combine"] == pytest.approx(16400, abs=0.01)
-    assert per_tok["chunk"] == pytest.approx(24672 + 2560, abs=0.01)
+    assert per_tok["chunk"] == pytest.approx(24672 + 1280, abs=0.01)
+    c_in = bench.stage_costs(cfg, state_in=True)
+    assert c_in["chunk"]["bytes"] / NT == pytest.approx(24672 + 2560, abs=0.01)
     assert c["chunk"]["flops"] / NT / 1e6 == pytest.approx(3.77, abs=0.01)
     assert c["project"]["flops"] / NT / 1e6 == pytest.approx(10.5, abs=0.05)
+
+
+@pytest.mark.parametrize("name,mtok", [("l380m", 96.4), ("l1b3", 34.3), ("m16", 60.6), ("long32k", 34.3)])
+def test_layer_bound(name, mtok):
+    import bench
+    from mixture_memories_recurrence_amd import synth
+    tok_s, us = bench.layer_bound(synth.CONFIGS[name])
+    assert tok_s / 1e6 == pytest.approx(mtok, abs=0.05)
+    if name == "l380m":  # route 2,064 B, dispatch 6,296 B, combine 16,400 B, chunk 24,672 B per token at 8 TB/s
+        NT = 16384
+        assert us["route"] == pytest.approx(2064 * NT / 8e12 * 1e6, rel=1e-9)
+        assert us["dispatch"] == pytest.approx(6296 * NT / 8e12 * 1e6, rel=1e-9)
+        assert us["combine"] == pytest.approx(16400 * NT / 8e12 * 1e6, rel=1e-9)
+        assert us["chunk"] == pytest.approx(24672 * NT / 8e12 * 1e6, rel=1e-9)
