@@ -103,7 +103,8 @@ typedef enum mom_status {
   MOM_ERR_UNSUPPORTED = -3, /* a shape or dtype outside the supported set */
   MOM_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
   MOM_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
-  MOM_ERR_LAUNCH = -6       /* the HIP runtime refused a kernel launch */
+  MOM_ERR_LAUNCH = -6,      /* the HIP runtime refused a kernel launch */
+  MOM_ERR_TOO_LARGE = -7    /* sizes exceed the fixed scratch of an allocation-free entry point */
 } mom_status;
 
 enum { MOM_DTYPE_F32 = 0, MOM_DTYPE_BF16 = 1 };
@@ -146,6 +147,23 @@ mom_status mom_dispatch(const mom_dims* dims, const int32_t* idx, const void* x,
                         const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv,
                         void* x_packed, float* alpha_p, float* beta_p, void* ws, size_t ws_bytes,
                         void* stream);
+
+/* mom_dispatch without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The same outputs as mom_dispatch (bit for bit);
+ * every other argument, layout and error as there.  The dispatch's counts
+ * (int32 [M][B][ceil(T / 256)], M*B*ceil(T / 256) <= 65536) live in a fixed
+ * 256 KiB array of the library's own in each GPU's memory, held from the
+ * first call on that GPU until the process ends; larger sizes return
+ * MOM_ERR_TOO_LARGE before any launch.  The call allocates nothing.  The
+ * array's device address is looked up on the first call on each GPU, so
+ * stream (NULL = the null stream) must belong to the current device (else
+ * MOM_ERR_DIMS).  Every call on one GPU uses the same array: calls that can
+ * overlap on that GPU (e.g. on two streams without ordering between them)
+ * race and must be serialised by the caller. */
+mom_status mom_dispatch_noalloc(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
+                                const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv,
+                                void* x_packed, float* alpha_p, float* beta_p, void* stream);
 
 /* Route and histogram in one launch, for one position per sequence (a decode
  * step, dims->T == 1; otherwise MOM_ERR_UNSUPPORTED): the outputs of

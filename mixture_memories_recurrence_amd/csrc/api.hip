@@ -105,6 +105,7 @@ extern "C" const char* mom_status_string(int32_t status) {
     case MOM_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case MOM_ERR_WORKSPACE: return "workspace missing or too small";
     case MOM_ERR_LAUNCH: return "kernel launch failed";
+    case MOM_ERR_TOO_LARGE: return "sizes exceed the fixed scratch of an allocation-free entry point";
     default: return "unknown status";
   }
 }

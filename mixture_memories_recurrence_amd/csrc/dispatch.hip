@@ -17,6 +17,7 @@
 //             then writes perm/inv, gathers the gates of the routed memory and,
 //             if asked, the x rows.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -225,11 +226,11 @@ __global__ __launch_bounds__(256) void k_dispatch_shared(int B, int T, int H, in
 }  // namespace mom
 
 namespace mom {
-// counted: ws already holds the counts (mom_route_count, one position per sequence)
-static mom_status dispatch(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
-                           const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv, void* x_packed,
-                           float* alpha_p, float* beta_p, void* ws, size_t ws_bytes, int part, void* stream,
-                           bool counted = false) {
+// Argument checks of the dispatch entry points other than the workspace
+// (part as in mom_dispatch_part).
+static mom_status dispatch_check(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
+                                 const float* beta, const int32_t* seg_off, const int32_t* perm, const int32_t* inv,
+                                 const void* x_packed, const float* alpha_p, const float* beta_p, int part) {
   mom_status s = check_dims(dims);
   if (s != MOM_OK) return s;
   if (part < 0 || part > 2) return MOM_ERR_DIMS;
@@ -239,6 +240,22 @@ static mom_status dispatch(const mom_dims* dims, const int32_t* idx, const void*
   MOM_CHECK_PTR(perm);
   MOM_CHECK_PTR(alpha_p);
   MOM_CHECK_PTR(beta_p);
+  if (part == 1) return MOM_OK;
+  MOM_CHECK_PTR(idx);
+  MOM_CHECK_PTR(inv);
+  MOM_CHECK_OPT_PTR(x_packed);
+  if (x_packed) MOM_CHECK_PTR(x);
+  if ((int64_t)ceil_div(dims->T, kTile) * dims->B > 0x7fffffff / 2) return MOM_ERR_DIMS;
+  return MOM_OK;
+}
+
+// counted: ws already holds the counts (mom_route_count, one position per sequence)
+static mom_status dispatch(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
+                           const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv, void* x_packed,
+                           float* alpha_p, float* beta_p, void* ws, size_t ws_bytes, int part, void* stream,
+                           bool counted = false) {
+  const mom_status s = dispatch_check(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_p, beta_p, part);
+  if (s != MOM_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   const mom_dims& d = *dims;
   if (part == 1) {  // the shared memory's rows: no routing needed
@@ -247,15 +264,10 @@ static mom_status dispatch(const mom_dims* dims, const int32_t* idx, const void*
                        d.topk, alpha, beta, seg_off, perm, alpha_p, beta_p);
     return launch_status();
   }
-  MOM_CHECK_PTR(idx);
-  MOM_CHECK_PTR(inv);
-  MOM_CHECK_OPT_PTR(x_packed);
-  if (x_packed) MOM_CHECK_PTR(x);
   const size_t need = mom_workspace_bytes(dims, MOM_WS_DISPATCH);
   if (!ws || ws_bytes < need) return MOM_ERR_WORKSPACE;
   MOM_CHECK_PTR(ws);
   const int ntile = ceil_div(d.T, kTile);
-  if ((int64_t)ntile * d.B > 0x7fffffff / 2) return MOM_ERR_DIMS;
   // part 2 leaves the shared rows and the shared segments' offsets (past M B) to part 1
   const int last_seg = part == 2 ? d.M * d.B : (d.M + 1) * d.B;
   const bool shared_rows = part == 0;
@@ -304,4 +316,65 @@ extern "C" mom_status mom_dispatch_part(const mom_dims* dims, const int32_t* idx
                                         int32_t part, void* stream) {
   return mom::dispatch(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_p, beta_p, ws, ws_bytes, part,
                        stream);
+}
+
+// ------------------------------------------------------------------ allocation-free dispatch
+// mom_dispatch_noalloc keeps the dispatch's counts (int32 [M][B][ceil(T/256)],
+// written in full by k_count before k_scan or k_scatter read them, so nothing
+// needs clearing) in this array instead of a caller workspace.  In host code
+// `scratch` only names the symbol: its device address is looked up once per
+// device with hipGetSymbolAddress and kept in scratch_ptr.
+namespace mom {
+constexpr int64_t kNoAllocCounts = 65536;  // 256 KiB
+static __device__ __align__(256) int32_t scratch[kNoAllocCounts];
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];  // device address of `scratch` on device i, null until looked up
+
+// Address of `scratch` on the current device (the stream's device), or null
+// with *st set.
+void* scratch_address(hipStream_t stream, mom_status* st) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    *st = MOM_ERR_LAUNCH;
+    return nullptr;
+  }
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev) {
+      *st = MOM_ERR_DIMS;  // the stream belongs to another device than the current one
+      return nullptr;
+    }
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *st = MOM_ERR_UNSUPPORTED;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      *st = MOM_ERR_LAUNCH;
+      return nullptr;
+    }
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+}  // namespace
+}  // namespace mom
+
+extern "C" mom_status mom_dispatch_noalloc(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
+                                           const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv,
+                                           void* x_packed, float* alpha_p, float* beta_p, void* stream) {
+  using namespace mom;
+  mom_status s = dispatch_check(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_p, beta_p, 0);
+  if (s != MOM_OK) return s;
+  const size_t need = mom_workspace_bytes(dims, MOM_WS_DISPATCH);
+  if (need > (size_t)kNoAllocCounts * sizeof(int32_t)) return MOM_ERR_TOO_LARGE;
+  void* ws = scratch_address((hipStream_t)stream, &s);
+  if (!ws) return s;
+  return dispatch(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_p, beta_p, ws,
+                  (size_t)kNoAllocCounts * sizeof(int32_t), 0, stream);
 }

@@ -51,6 +51,7 @@ def lib():
         "mom_route_count": [D, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
         "mom_dispatch_counted": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
         "mom_dispatch": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+        "mom_dispatch_noalloc": [D] + [_VP] * 11,
         "mom_project": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
         "mom_project_part": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP],
         "mom_dispatch_part": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _I32, _VP],
@@ -89,7 +90,8 @@ def lib():
     return L
 
 
-EXPORTS = ("mom_route", "mom_route_count", "mom_dispatch", "mom_dispatch_counted", "mom_dispatch_part",
+EXPORTS = ("mom_route", "mom_route_count", "mom_dispatch", "mom_dispatch_noalloc", "mom_dispatch_counted",
+           "mom_dispatch_part",
            "mom_project", "mom_project_part", "gdn_chunk_fwd", "gla_chunk_fwd", "gdn_chunk_bwd", "gla_chunk_bwd",
            "gdn_chunk_fwd_train", "gla_chunk_fwd_train", "gdn_chunk_bwd_saved", "gla_chunk_bwd_saved",
            "gdn_decode_step", "gla_decode_step", "gdn_decode_step_combined", "gla_decode_step_combined",
@@ -148,6 +150,14 @@ def mom_dispatch(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_
     _check(lib().mom_dispatch(ctypes.byref(dims), _p(idx), _p(x), _p(alpha), _p(beta), _p(seg_off), _p(perm),
                               _p(inv), _p(x_packed), _p(alpha_p), _p(beta_p), _p(ws), nbytes, _s(stream)),
            "mom_dispatch")
+
+
+def mom_dispatch_noalloc(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_p, beta_p, stream=None):
+    """mom_dispatch with the library's fixed scratch instead of a workspace (no
+    allocation; calls that overlap on one GPU race)."""
+    _check(lib().mom_dispatch_noalloc(ctypes.byref(dims), _p(idx), _p(x), _p(alpha), _p(beta), _p(seg_off),
+                                      _p(perm), _p(inv), _p(x_packed), _p(alpha_p), _p(beta_p), _s(stream)),
+           "mom_dispatch_noalloc")
 
 
 PART_ALL, PART_SHARED, PART_ROUTED = 0, 1, 2

@@ -192,3 +192,24 @@ def test_chunk_bwd_checks():
                      None) == -1
         assert f(ctypes.byref(_dims(dtype=0)), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, *fargs, FAKE,
                  need, None) == -3
+
+
+@needs_lib
+def test_dispatch_noalloc_checks_before_any_launch():
+    """The allocation-free dispatch validates like mom_dispatch and rejects
+    sizes past its fixed scratch (M*B*ceil(T/256) <= 65536 counts) with
+    MOM_ERR_TOO_LARGE, all before any HIP call (so without a GPU)."""
+    L = mom.lib()
+    f = lambda d, *p: L.mom_dispatch_noalloc(ctypes.byref(d), *p, None)
+    ok = [FAKE] * 10
+    assert L.mom_dispatch_noalloc(None, *ok, None) == -1
+    assert f(_dims(), None, *ok[1:]) == -1                  # idx
+    assert f(_dims(), FAKE, None, FAKE, *ok[3:]) == -1      # beta
+    assert f(_dims(), FAKE, FAKE, FAKE, FAKE, ODD, *ok[5:]) == -4   # seg_off misaligned
+    assert f(_dims(topk=0), *ok) == -2
+    # 16 memories x 64 sequences x 65 tiles = 66560 counts > 65536
+    big = _dims(M=16, topk=4, B=64, T=65 * 256)
+    assert f(big, *ok) == -7
+    assert L.mom_status_string(-7).decode().startswith("sizes exceed")
+    # exactly at the limit passes the size check (then needs a GPU, not called here)
+    assert 16 * 64 * 64 == 65536
