@@ -351,7 +351,10 @@ def test_chunk_segments(store, dk, dv, rule):
     st = S0.astype(np.float64).copy()
     o_ref = oracle.segments(seg_off, seg_state, row_token, qtok, ch["k"], ch["v"], ch["alpha"], ch["beta"], st,
                             rule="gla" if rule == "gla" else "gdn")
-    tol = TOL["bf16"] if store == "f16" else (2e-5, 1e-5)
+    # float32: the configs' 1e-5 for both norms, except DeltaNet (forget gate 1,
+    # outside the configs' gate range [0.9, 1)): nothing decays, the outputs
+    # grow with the whole history, and max-abs is held to 2e-5
+    tol = TOL["bf16"] if store == "f16" else ((2e-5, 1e-5) if rule == "deltanet" else TOL["f32"])
     assert_close("o", o.cpu().numpy(), o_ref, *tol)
     sg = so.cpu().numpy()
     assert_close("state", sg[seg_state], st[seg_state], *tol)
