@@ -65,6 +65,7 @@ __device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmc
 __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void vm_wait_8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
+__device__ __forceinline__ void vm_wait_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
 
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef float f16x16 __attribute__((ext_vector_type(16)));
@@ -91,6 +92,32 @@ __device__ __forceinline__ h8v acc_to_b(const f16x16& d, int p, const float* sc)
   const u2v s0 = __builtin_amdgcn_permlane32_swap(X0, Y0, false, false);
   const u2v s1 = __builtin_amdgcn_permlane32_swap(X1, Y1, false, false);
   const unsigned w4[4] = {s0.x, s1.x, s0.y, s1.y};
+  return __builtin_bit_cast(h8v, *reinterpret_cast<const __attribute__((ext_vector_type(4))) unsigned*>(w4));
+}
+
+// ------------------------------------------------------------------ 16 x 16 x 32 products
+// v_mfma_f32_16x16x32_f16: lane l = 16 G + c (G = l / 16) holds
+//   A[row c][k 8G .. 8G+7],  B[k 8G .. 8G+7][col c],  D[rows 4G .. 4G+3][col c].
+typedef float f4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f4v mfma16(const h8v& a, const h8v& b, const f4v& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// Two accumulator tiles of one 32-row block (t0: rows 0..15, t1: rows 16..31,
+// lane 16 G + c holding rows 4G .. 4G+3 of column c), row r scaled by s0[r % 4]
+// (t0) or s1[r % 4] (t1), as the 32-deep operand of a 16x16x32 product: lane
+// 16 G + c receives rows 8G .. 8G+7 of column c.  Lane group G needs the rows
+// of groups 2(G % 2) and 2(G % 2) + 1 of tile G / 2: one exchange between the
+// wave's halves (v_permlane32_swap) brings t1's groups 0, 1 next to t0's groups
+// 2, 3, and one between neighbouring 16-lane rows (v_permlane16_swap) pairs
+// each group with the one it needs.
+__device__ __forceinline__ h8v acc16_to_op(const f4v& t0, const f4v& t1, const float* s0, const float* s1) {
+  const unsigned X0 = pack_h2(t0[0] * s0[0], t0[1] * s0[1]), X1 = pack_h2(t0[2] * s0[2], t0[3] * s0[3]);
+  const unsigned Y0 = pack_h2(t1[0] * s1[0], t1[1] * s1[1]), Y1 = pack_h2(t1[2] * s1[2], t1[3] * s1[3]);
+  const u2v a0 = __builtin_amdgcn_permlane32_swap(X0, Y0, false, false);
+  const u2v a1 = __builtin_amdgcn_permlane32_swap(X1, Y1, false, false);
+  const u2v b0 = __builtin_amdgcn_permlane16_swap(a0.x, a0.y, false, false);
+  const u2v b1 = __builtin_amdgcn_permlane16_swap(a1.x, a1.y, false, false);
+  const unsigned w4[4] = {b0.x, b1.x, b0.y, b1.y};
   return __builtin_bit_cast(h8v, *reinterpret_cast<const __attribute__((ext_vector_type(4))) unsigned*>(w4));
 }
 
@@ -156,6 +183,22 @@ __device__ __forceinline__ void dma_b32(const void* g, const void* lds_base) {
                : "memory");
 }
 
+// The same copy with the LDS byte address given directly (wave-uniform).
+__device__ __forceinline__ void dma_b128_at(const void* g, unsigned lds_addr) {
+  unsigned save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(save)
+               : "s"(lds_addr), "v"(g)
+               : "memory");
+}
+__device__ __forceinline__ void dma_b32_at(const void* g, unsigned lds_addr) {
+  unsigned save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(save)
+               : "s"(lds_addr), "v"(g)
+               : "memory");
+}
+
 // LDS tiles are stored without padding, the 16-byte piece c of row r at piece
 // position c ^ swz(r), so that both access patterns below are conflict-free:
 // 16 consecutive rows read at one piece (operands with k along the row), and 4
@@ -191,6 +234,23 @@ __device__ __forceinline__ h8v col_frag(const f16_t* X, int kb, int c0, int lane
   const s4v v8[2] = {a, b};
   return __builtin_bit_cast(h8v, v8);
 }
+// 16x16x32 operand with k along the row: X[row][8 (4 kb + G) .. + 7], G = lane / 16.
+template <int RH>
+__device__ __forceinline__ h8v row_frag16(const f16_t* X, int row, int kb, int G) {
+  return *reinterpret_cast<const h8v*>(X + row * RH + 8 * swz<RH>(row, 4 * kb + G));
+}
+// 16x16x32 operand with k down the rows: X[32 kb + 8 G + t][c0 + lane % 16], t = 0..7.
+template <int RH>
+__device__ __forceinline__ h8v col_frag16(const f16_t* X, int kb, int c0, int lane) {
+  const int row = 32 * kb + 8 * (lane >> 4) + ((lane & 15) >> 2);
+  const int col = c0 + 4 * (lane & 3);
+  const int ch = col >> 3, sub = col & 7;
+  const s4v a = lds_tr4(X + row * RH + 8 * swz<RH>(row, ch) + sub);
+  const s4v b = lds_tr4(X + (row + 4) * RH + 8 * swz<RH>(row + 4, ch) + sub);
+  const s4v v8[2] = {a, b};
+  return __builtin_bit_cast(h8v, v8);
+}
+
 // Copy instruction j (of GC / RPI / NW per wave) of a 64-row tile of RH-half
 // rows, copied by waves [0, NW) into its swizzled LDS image; src(r, c) is the
 // global address of piece c of tile row r.

@@ -20,9 +20,12 @@
 //                (16x16 diagonal blocks by forward substitution, off-diagonal
 //                blocks by block products), all in float32.  It stores T and P
 //                as half and gamma, gamma_L / gamma as float32.
-//   k_gdn_chain  one block per (segment, head, 64 or 128 value columns); it
-//                walks the segment's chunks in order with the state in float32
-//                matrix-core accumulators (see the comment at the kernel).
+//   k_gdn_chain16  the forward walk: one block per (segment, head, 128 value
+//                columns; 64 when dv = 64) of eight (four) waves with 16 columns
+//                each, walking the segment's chunks in order with the state in
+//                float32 matrix-core accumulators (see the comment at the kernel).
+//   k_gdn_chain  the same walk with 32-column waves, and the modes that store
+//                each chunk's entering state for the gradients.
 #include "chunk_mfma.h"
 
 namespace mom {
@@ -327,6 +330,289 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
     }
 }
 
+// ------------------------------------------------------------------ chain, 16-column waves
+// The forward walk with NW waves of 16 value columns each (DVB = 16 NW columns
+// per block: 128 with eight waves, 64 with four), on v_mfma_f32_16x16x32_f16.
+// A wave's accumulators are a quarter of the 32-column wave's above, so the
+// kernel fits two waves per SIMD, and each SIMD switches to the other wave
+// while one waits on LDS reads or on its products.  The per-chunk algebra and
+// the inputs (K, Q, V, T, P, gamma in a double-buffered LDS image filled by
+// asynchronous copies, one block barrier per chunk) are those of k_gdn_chain:
+//   Y   = K S                         (4 row tiles, dk-deep)
+//   O^T = S^T Q^T                     (4 row tiles of the chunk, dk-deep)
+//   U   = T V - T diag(gamma) Y       (chunk-deep)
+//   O^T = O^T diag(gamma) + U^T P^T
+//   S  <- gamma_L S + K^T diag(gamma_L / gamma) U
+// The state S (DK x 16, float32) is held as DK / 16 accumulator tiles; its
+// 32-row blocks become the dk-deep operand of Y and of O^T (the same
+// registers serve as B of K S and as A of S^T Q^T) through acc16_to_op, and so
+// do the 32-row blocks of Y and U for the chunk-deep products.  Lane 16 G + c
+// ends with the read of chunk row 16 t + c at value columns 4G .. 4G+3 of its
+// wave in O[t], which it stores as one 16-byte piece (a row's 16 columns are
+// four lanes' contiguous 64 bytes).
+template <int DK, int NW, bool DELTA>
+__global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
+    int H, int dv, int n_seg, const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_state,
+    const f16_t* __restrict__ k, const f16_t* __restrict__ v, const f16_t* __restrict__ Tws,
+    const f16_t* __restrict__ Pws, const float* __restrict__ Ews, const int32_t* __restrict__ row_token,
+    const f16_t* __restrict__ q, const float* __restrict__ state_in, float* __restrict__ state_out,
+    float* __restrict__ o) {
+  constexpr int DVB = 16 * NW, ND = DK / 16, NKD = DK / 32;
+  constexpr int OFF_K = 0, OFF_Q = GC * DK, OFF_V = 2 * GC * DK, OFF_T = OFF_V + GC * DVB, OFF_P = OFF_T + GC * GC,
+                OFF_E = OFF_P + GC * GC, OFF_TOK = OFF_E + 2 * 2 * GC, BUF = OFF_TOK + 2 * GC;
+  extern __shared__ __attribute__((aligned(16))) f16_t smem[];
+
+  // blocks of a (segment, head) to one XCD, longest segments (highest s) first
+  const int nb = dv / DVB;
+  const int64_t pblk = blockIdx.x;
+  const int64_t n_grp = (int64_t)n_seg * H;
+  const int64_t full = (n_grp / 8) * 8;
+  int64_t grp;
+  int cb;
+  if (pblk < full * nb) {
+    const int64_t xi = pblk & 7, ii = pblk >> 3;
+    grp = (ii / nb) * 8 + xi;
+    cb = (int)(ii % nb);
+  } else {
+    const int64_t r = pblk - full * nb;
+    grp = full + r / nb;
+    cb = (int)(r % nb);
+  }
+  const int h = (int)(grp % H);
+  const int s = n_seg - 1 - (int)(grp / H);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, G = lane >> 4;
+  const int slot = seg_state ? seg_state[s] : s;
+  const int ncol0 = cb * DVB + 16 * w;  // this wave's first value column
+  const int64_t sbase = ((int64_t)slot * H + h) * DK * dv + ncol0;
+  const int64_t rbeg = seg_off[s], rend = seg_off[s + 1];
+  const int cbase = chunks_before(seg_off, s, lane);
+
+  // prefetch of the chunk at row r0n into buffer b, NPF copy instructions per
+  // wave; rows past the segment end repeat its last row (T is zero there).
+  // Each lane's tile row and swizzled 16-byte piece of every copy are fixed for
+  // the whole walk; per chunk only wave-uniform bases change, so a copy's
+  // address is one base plus a 32-bit element offset.
+  using CK = TileCopy<DK, NW>;
+  using CV = TileCopy<DVB, NW>;
+  using CT = TileCopy<GC, NW>;
+  constexpr int NPF = 2 * CK::PER_WAVE + CV::PER_WAVE + 2 * CT::PER_WAVE + 2;
+  int k_row[CK::PER_WAVE], k_pc[CK::PER_WAVE], v_row[CV::PER_WAVE], v_pc[CV::PER_WAVE];
+  unsigned t_off[CT::PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < CK::PER_WAVE; ++j) {
+    k_row[j] = CK::row(w, lane, j);
+    k_pc[j] = 8 * swz<DK>(k_row[j], lane % CK::CPR);
+  }
+#pragma unroll
+  for (int j = 0; j < CV::PER_WAVE; ++j) {
+    v_row[j] = CV::row(w, lane, j);
+    v_pc[j] = 8 * swz<DVB>(v_row[j], lane % CV::CPR);
+  }
+#pragma unroll
+  for (int j = 0; j < CT::PER_WAVE; ++j) {
+    const int r = CT::row(w, lane, j);
+    t_off[j] = (unsigned)(r * GC + 8 * swz<GC>(r, lane % CT::CPR));
+  }
+  const unsigned lds0 = lds_offset(smem);  // LDS byte address of the buffers
+  const int64_t hstride = (int64_t)H;
+  const f16_t* pf_k = k;
+  const f16_t* pf_v = v;
+  const f16_t* pf_t = Tws;
+  const f16_t* pf_p = Pws;
+  int pf_L = 0;
+  int64_t pf_r0 = 0, pf_chk = 0;
+  unsigned pf_lds = lds0;
+  int qtok[CK::PER_WAVE];
+  auto pf_setup = [&](int64_t r0n, int b, const int32_t* tok_lds) {
+    pf_r0 = r0n;
+    pf_L = (int)min((int64_t)GC, rend - r0n);
+    pf_chk = (int64_t)(cbase + (r0n - rbeg) / GC) * H + h;
+    pf_lds = lds0 + (unsigned)(b * BUF * (int)sizeof(f16_t));
+    pf_k = k + (r0n * hstride + h) * DK;
+    pf_v = v + (r0n * hstride + h) * dv + cb * DVB;
+    pf_t = Tws + pf_chk * GC * GC;
+    pf_p = Pws + pf_chk * GC * GC;
+#pragma unroll
+    for (int j = 0; j < CK::PER_WAVE; ++j) {
+      const int r = min(k_row[j], pf_L - 1);
+      if (tok_lds) qtok[j] = tok_lds[r];
+      else qtok[j] = row_token ? row_token[r0n + r] : (int)(r0n + r);
+    }
+  };
+  // LDS byte address of copy instruction j (tile row RPI (w + NW j)) of a tile at element offset off
+  auto lds_at = [&](int off, int rpi, int rh, int j) {
+    return pf_lds + (unsigned)((off + rpi * (w + NW * j) * rh) * (int)sizeof(f16_t));
+  };
+  auto pf_issue = [&](int i) {
+    if (i < CK::PER_WAVE) {
+      const unsigned e = (unsigned)(min(k_row[i], pf_L - 1) * H * DK + k_pc[i]);
+      dma_b128_at(pf_k + e, lds_at(OFF_K, CK::RPI, DK, i));
+    } else if ((i -= CK::PER_WAVE) < CK::PER_WAVE) {
+      dma_b128_at(q + ((int64_t)qtok[i] * H + h) * DK + k_pc[i], lds_at(OFF_Q, CK::RPI, DK, i));
+    } else if ((i -= CK::PER_WAVE) < CV::PER_WAVE) {
+      const unsigned e = (unsigned)(min(v_row[i], pf_L - 1) * H * dv + v_pc[i]);
+      dma_b128_at(pf_v + e, lds_at(OFF_V, CV::RPI, DVB, i));
+    } else if ((i -= CV::PER_WAVE) < CT::PER_WAVE) {
+      dma_b128_at(pf_t + t_off[i], lds_at(OFF_T, CT::RPI, GC, i));
+    } else if ((i -= CT::PER_WAVE) < CT::PER_WAVE) {
+      dma_b128_at(pf_p + t_off[i], lds_at(OFF_P, CT::RPI, GC, i));
+    } else if (i == CT::PER_WAVE) {
+      if (w < 2) dma_b32_at(Ews + pf_chk * 2 * GC + GC * w + lane, pf_lds + (unsigned)((OFF_E + 2 * GC * w) * 2));
+    } else if (w == NW - 1) {  // tokens of the following chunk's rows
+      const int64_t rn = min(pf_r0 + GC + lane, rend - 1);
+      if (row_token) dma_b32_at(row_token + rn, pf_lds + (unsigned)(OFF_TOK * 2));
+      else reinterpret_cast<int32_t*>(smem + (pf_lds - lds0) / 2 + OFF_TOK)[lane] = (int32_t)rn;
+    }
+  };
+  constexpr int PY = (NPF + NKD - 1) / NKD;  // copies issued per step of the Y / O loop
+
+  f4v S[ND];
+#pragma unroll
+  for (int a = 0; a < ND; ++a)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      S[a][e] = state_in ? state_in[sbase + (int64_t)(16 * a + 4 * G + e) * dv + c16] : 0.f;
+  const float ones[4] = {1.f, 1.f, 1.f, 1.f};
+  if (rbeg < rend) {
+    pf_setup(rbeg, 0, nullptr);
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) pf_issue(i);
+  }
+
+  int buf = 0;
+  for (int64_t r0 = rbeg; r0 < rend; r0 += GC, buf ^= 1) {
+    const int L = (int)min((int64_t)GC, rend - r0);
+    // this wave's copies have landed (only the previous chunk's 4 output
+    // stores were issued after them); then every wave's
+    if (r0 == rbeg) vm_wait_all();
+    else vm_wait_4();
+    lds_barrier();
+    pf_setup(r0 + GC < rend ? r0 + GC : r0, buf ^ 1, reinterpret_cast<const int32_t*>(smem + buf * BUF + OFF_TOK));
+
+    const f16_t* Bc = smem + buf * BUF;
+    const f16_t* Ks = Bc + OFF_K;
+    const f16_t* Qs = Bc + OFF_Q;
+    const f16_t* Vs = Bc + OFF_V;
+    const f16_t* Ts = Bc + OFF_T;
+    const f16_t* Ps = Bc + OFF_P;
+    const float* Eg = reinterpret_cast<const float*>(Bc + OFF_E);  // gamma_i, then gamma_L / gamma_i
+
+    // ---- Y = K S and O^T = S^T Q^T; the state's 32-row blocks as operands
+    f4v Y[4], O[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Y[t][e] = 0.f;
+        O[t][e] = 0.f;
+      }
+    // operand reads one k-block ahead of the products that use them
+    h8v kf[2][4], qf[2][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      kf[0][t] = row_frag16<DK>(Ks, 16 * t + c16, 0, G);
+      qf[0][t] = row_frag16<DK>(Qs, 16 * t + c16, 0, G);
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKD; ++kb) {
+      if (kb + 1 < NKD) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          kf[(kb + 1) & 1][t] = row_frag16<DK>(Ks, 16 * t + c16, kb + 1, G);
+          qf[(kb + 1) & 1][t] = row_frag16<DK>(Qs, 16 * t + c16, kb + 1, G);
+        }
+      }
+#pragma unroll
+      for (int i = PY * kb; i < PY * (kb + 1); ++i)
+        if (i < NPF) pf_issue(i);
+      const h8v sop = acc16_to_op(S[2 * kb], S[2 * kb + 1], ones, ones);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        Y[t] = mfma16(kf[kb & 1][t], sop, Y[t]);
+        O[t] = mfma16(sop, qf[kb & 1][t], O[t]);
+      }
+    }
+    CHAIN_PHASE();
+    // ---- U = T V - T diag(gamma) Y
+    f4v U[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) U[t][e] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < GC / 32; ++kb) {
+      const h8v vb = col_frag16<DVB>(Vs, kb, 16 * w, lane);
+      h8v yb;
+      if constexpr (DELTA) {
+        float s0[4], s1[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s0[e] = -Eg[32 * kb + 4 * G + e];
+          s1[e] = -Eg[32 * kb + 16 + 4 * G + e];
+        }
+        yb = acc16_to_op(Y[2 * kb], Y[2 * kb + 1], s0, s1);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const h8v tf = row_frag16<GC>(Ts, 16 * t + c16, kb, G);
+        U[t] = mfma16(tf, vb, U[t]);
+        if constexpr (DELTA) U[t] = mfma16(tf, yb, U[t]);
+      }
+    }
+    CHAIN_PHASE();
+    // ---- U and diag(gamma_L / gamma) U as chunk-deep operands
+    h8v ub[GC / 32], u2b[GC / 32];
+#pragma unroll
+    for (int kb = 0; kb < GC / 32; ++kb) {
+      float s0[4], s1[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s0[e] = Eg[GC + 32 * kb + 4 * G + e];
+        s1[e] = Eg[GC + 32 * kb + 16 + 4 * G + e];
+      }
+      ub[kb] = acc16_to_op(U[2 * kb], U[2 * kb + 1], ones, ones);
+      u2b[kb] = acc16_to_op(U[2 * kb], U[2 * kb + 1], s0, s1);
+    }
+    // ---- O^T = O^T diag(gamma) + U^T P^T, stored as 16-byte row pieces
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float gm = Eg[16 * t + c16];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) O[t][e] *= gm;
+#pragma unroll
+      for (int kb = 0; kb < GC / 32; ++kb) O[t] = mfma16(ub[kb], row_frag16<GC>(Ps, 16 * t + c16, kb, G), O[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (16 * t + c16 < L)
+        *reinterpret_cast<float4*>(o + ((r0 + 16 * t + c16) * H + h) * dv + ncol0 + 4 * G) =
+            make_float4(O[t][0], O[t][1], O[t][2], O[t][3]);
+    CHAIN_PHASE();
+    // ---- S <- gamma_L S + K^T U'
+    const float eL = Eg[GC - 1];
+#pragma unroll
+    for (int a = 0; a < ND; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[a][e] *= eL;
+#pragma unroll
+    for (int kb = 0; kb < GC / 32; ++kb)
+#pragma unroll
+      for (int a = 0; a < ND; ++a) S[a] = mfma16(col_frag16<DK>(Ks, kb, 16 * a, lane), u2b[kb], S[a]);
+  }
+  vm_wait_all();  // the last (repeated) prefetch has landed before the block ends
+#pragma unroll
+  for (int a = 0; a < ND; ++a)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) state_out[sbase + (int64_t)(16 * a + 4 * G + e) * dv + c16] = S[a][e];
+}
+
+template <int DK, int NW>
+constexpr size_t chain16_lds_bytes() {
+  return (size_t)2 * (2 * GC * DK + GC * 16 * NW + 2 * GC * GC + 4 * GC + 2 * GC) * sizeof(f16_t);
+}
+
 // ------------------------------------------------------------------ prep
 // One wave per (chunk, head), four per block; waves share nothing.
 //   g, gamma = e^g and gamma_L / gamma from a wave prefix sum of log alpha;
@@ -596,6 +882,26 @@ static mom_status launch_chain(const mom_dims& d, int n_seg, const int32_t* seg_
   return MOM_OK;
 }
 
+template <int DK, int NW, bool DELTA>
+static mom_status launch_chain16(const mom_dims& d, int n_seg, const int32_t* seg_off, const int32_t* seg_state,
+                                 const ChunkWs& W, const int32_t* row_token, const void* q, const void* k,
+                                 const void* v, const float* state_in, float* state_out, float* o, hipStream_t st) {
+  constexpr size_t lds = chain16_lds_bytes<DK, NW>();
+  static bool attr = false;  // the dynamic LDS limit is raised once per kernel
+  if (!attr) {
+    if (hipFuncSetAttribute((const void*)k_gdn_chain16<DK, NW, DELTA>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds) != hipSuccess)
+      return MOM_ERR_LAUNCH;
+    attr = true;
+  }
+  const int64_t blocks = (int64_t)n_seg * d.H * (d.dv / (16 * NW));
+  if (blocks > 0)
+    hipLaunchKernelGGL((k_gdn_chain16<DK, NW, DELTA>), dim3((unsigned)blocks), dim3(64 * NW), lds, st, d.H, d.dv,
+                       n_seg, seg_off, seg_state, (const f16_t*)k, (const f16_t*)v, W.T, W.P, W.E, row_token,
+                       (const f16_t*)q, state_in, state_out, o);
+  return MOM_OK;
+}
+
 template <int DK, bool DELTA>
 static mom_status launch_chunk(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
                                const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
@@ -610,10 +916,10 @@ static mom_status launch_chunk(const mom_dims& d, int n_seg, int n_rows, const i
                        nullptr);
   const mom_status r =
       d.dv % 128 == 0
-          ? launch_chain<DK, 4, DELTA, 0>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in,
-                                          state_out, o, nullptr, st)
-          : launch_chain<DK, 2, DELTA, 0>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in,
-                                          state_out, o, nullptr, st);
+          ? launch_chain16<DK, 8, DELTA>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o,
+                                         st)
+          : launch_chain16<DK, 4, DELTA>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o,
+                                         st);
   if (r != MOM_OK) return r;
   return launch_status();
 }
