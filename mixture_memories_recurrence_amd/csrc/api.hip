@@ -13,7 +13,7 @@ mom_status launch_gdn_chunk_mfma(const mom_dims& d, int n_seg, int n_rows, const
                                  const int32_t* seg_state, const int32_t* row_token, const void* q, const void* k,
                                  const void* v, const float* alpha_p, const float* beta_p, const float* state_in,
                                  float* state_out, float* o, void* ws, bool delta, hipStream_t st);
-size_t gdn_chunk_ws_bytes(int64_t n_seg, int64_t n_rows, int H, int dk);
+size_t gdn_chunk_ws_bytes(int64_t n_seg, int64_t n_rows, int H, int dk, int dv);
 size_t route_bwd_ws_bytes(const mom_dims& d);
 }  // namespace mom
 
@@ -21,7 +21,7 @@ extern "C" size_t gdn_chunk_workspace_bytes(const mom_dims* dims, int32_t n_seg,
   using namespace mom;
   if (check_dims(dims) != MOM_OK || n_seg < 0 || n_rows < 0) return 0;
   if (dims->dtype != MOM_DTYPE_BF16) return 0;
-  return gdn_chunk_ws_bytes(n_seg, n_rows, dims->H, dims->dk);
+  return gdn_chunk_ws_bytes(n_seg, n_rows, dims->H, dims->dk, dims->dv);
 }
 
 namespace mom {

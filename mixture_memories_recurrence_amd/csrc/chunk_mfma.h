@@ -3,6 +3,8 @@
 // the 32x32x16 half product and its accumulator-to-operand move, asynchronous
 // global -> LDS copies, and the swizzled LDS tile reads.
 #pragma once
+#include <algorithm>
+
 #include "common.h"
 
 namespace mom {
@@ -281,6 +283,74 @@ struct ChunkWs {
   float* E;
   size_t bytes;
 };
+
+// Long segments: when the walk would leave most compute units idle (few
+// (segment, head) pairs) and segments are long, gdn_chunk_fwd cuts them into
+// groups of lg chunks and scans the groups' affine state maps (see
+// launch_chunk_scan).  The plan depends only on host-known sizes, so the
+// workspace size and the launch agree.
+// The scan does about 2.5 times the walk's work to cut its serial length, so
+// it pays only where the walk would leave the GPU nearly idle: the host takes
+// it when the walk would run at most kScanMaxWalks blocks over segments of 16
+// or more chunks on average (a single long sequence with few heads; none of
+// the layer's configurations, whose other work fills the GPU meanwhile), and
+// reserves the workspace for groups of at least kScanMinGroup chunks.
+// k_make_groups then sets the group length from the segments' actual chunk
+// counts (about target groups in all, at most kScanMaxGroups per segment on
+// average, never shorter than kScanMinGroup chunks), and leaves every segment
+// whole when none is longer than kScanMinSeg chunks.
+constexpr int kScanCUs = 256;       // compute units the walk's grid is sized against
+constexpr int kScanMaxWalks = 8;    // walk blocks
+constexpr int kScanMinGroup = 8;    // chunks
+constexpr int kScanMinSeg = 64;     // chunks
+constexpr int kScanMaxGroups = 24;  // groups per segment (the chaining step is serial)
+struct ScanPlan {
+  bool on;
+  int target;        // groups wanted: two rounds of walk blocks
+  int64_t n_groups;  // bound on the number of groups
+};
+inline ScanPlan scan_plan(int64_t n_seg, int64_t n_rows, int H, int dv) {
+  ScanPlan p{false, 0, 0};
+  const int nvb = dv % 128 == 0 ? dv / 128 : 1;  // walk blocks per (segment, head)
+  const int64_t walk_blocks = n_seg * H * nvb, full_chunks = n_rows / GC;
+  if (n_seg == 0 || walk_blocks > kScanMaxWalks || full_chunks < 16 * n_seg) return p;
+  p.on = true;
+  p.target = (int)std::min<int64_t>(2 * kScanCUs / (H * nvb), kScanMaxGroups * n_seg);
+  p.n_groups = n_rows / ((int64_t)kScanMinGroup * GC) + n_seg;
+  return p;
+}
+// Scan workspace, after the chunk workspace: the groups' row offsets and
+// segments (n_groups + 1 each, a -1 sentinel), each segment's first group
+// (n_seg + 1), the groups' maps [group][H][dk][dv + dk] (B, then A) and
+// entering states [group][H][dk][dv], float32.
+struct ScanWs {
+  int32_t* grp_off;
+  int32_t* grp_seg;
+  int32_t* seg_grp0;
+  float* maps;
+  float* sg;
+  size_t bytes;
+};
+inline ScanWs scan_ws_layout(void* base, int64_t n_seg, int64_t n_groups, int H, int dk, int dv) {
+  ScanWs w;
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    const size_t o = off;
+    off += (b + 255) / 256 * 256;
+    return o;
+  };
+  const size_t o_go = take((size_t)(n_groups + 1) * 4), o_gs = take((size_t)(n_groups + 1) * 4);
+  const size_t o_s0 = take((size_t)(n_seg + 1) * 4);
+  const size_t o_m = take((size_t)n_groups * H * dk * (dv + dk) * 4), o_sg = take((size_t)n_groups * H * dk * dv * 4);
+  char* b = (char*)base;
+  w.grp_off = (int32_t*)(b + o_go);
+  w.grp_seg = (int32_t*)(b + o_gs);
+  w.seg_grp0 = (int32_t*)(b + o_s0);
+  w.maps = (float*)(b + o_m);
+  w.sg = (float*)(b + o_sg);
+  w.bytes = off;
+  return w;
+}
 
 inline ChunkWs chunk_ws_layout(void* base, int64_t n_seg, int64_t n_rows, int H, int dk) {
   const int64_t nch = n_rows / GC + n_seg;  // bound on the number of chunks

@@ -350,9 +350,18 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
 // ends with the read of chunk row 16 t + c at value columns 4G .. 4G+3 of its
 // wave in O[t], which it stores as one 16-byte piece (a row's 16 columns are
 // four lanes' contiguous 64 bytes).
-template <int DK, int NW, bool DELTA>
+//
+// MAP: the first phase of the long-segment scan (see launch_chunk_scan below).
+// The segments are then the groups of chunks the scan cuts, and each block
+// walks its group without read-out (no Q, P or O) from a zero state over the
+// real values (ident = 0) or from the identity over zero values (ident = 1, a
+// width of dk columns), giving the group's affine state map; groups that end
+// their segment are skipped (grp_seg[g + 1] != grp_seg[g]).  The state is
+// stored with row width sw at column col_base + the block's columns.
+template <int DK, int NW, bool DELTA, bool MAP>
 __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
-    int H, int dv, int n_seg, const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_state,
+    int H, int dv, int width, int col_base, int sw, int ident, int n_seg, const int32_t* __restrict__ seg_off,
+    const int32_t* __restrict__ seg_state, const int32_t* __restrict__ grp_seg,
     const f16_t* __restrict__ k, const f16_t* __restrict__ v, const f16_t* __restrict__ Tws,
     const f16_t* __restrict__ Pws, const float* __restrict__ Ews, const int32_t* __restrict__ row_token,
     const f16_t* __restrict__ q, const float* __restrict__ state_in, float* __restrict__ state_out,
@@ -363,7 +372,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
   extern __shared__ __attribute__((aligned(16))) f16_t smem[];
 
   // blocks of a (segment, head) to one XCD, longest segments (highest s) first
-  const int nb = dv / DVB;
+  const int nb = width / DVB;
   const int64_t pblk = blockIdx.x;
   const int64_t n_grp = (int64_t)n_seg * H;
   const int64_t full = (n_grp / 8) * 8;
@@ -380,12 +389,14 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
   }
   const int h = (int)(grp % H);
   const int s = n_seg - 1 - (int)(grp / H);
+  if (MAP && (grp_seg[s] < 0 || grp_seg[s + 1] != grp_seg[s])) return;  // whole block: no map needed
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15, G = lane >> 4;
   const int slot = seg_state ? seg_state[s] : s;
-  const int ncol0 = cb * DVB + 16 * w;  // this wave's first value column
-  const int64_t sbase = ((int64_t)slot * H + h) * DK * dv + ncol0;
+  const int ncol0 = cb * DVB + 16 * w;  // this wave's first column of the launch's width
+  const int64_t sbase = ((int64_t)slot * H + h) * DK * sw + col_base + ncol0;
+  const bool zero_v = MAP && ident;
   const int64_t rbeg = seg_off[s], rend = seg_off[s + 1];
   const int cbase = chunks_before(seg_off, s, lane);
 
@@ -450,13 +461,16 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
       const unsigned e = (unsigned)(min(k_row[i], pf_L - 1) * H * DK + k_pc[i]);
       dma_b128_at(pf_k + e, lds_at(OFF_K, CK::RPI, DK, i));
     } else if ((i -= CK::PER_WAVE) < CK::PER_WAVE) {
+      if (MAP) return;  // no read-out: Q is not needed
       dma_b128_at(q + ((int64_t)qtok[i] * H + h) * DK + k_pc[i], lds_at(OFF_Q, CK::RPI, DK, i));
     } else if ((i -= CK::PER_WAVE) < CV::PER_WAVE) {
+      if (zero_v) return;
       const unsigned e = (unsigned)(min(v_row[i], pf_L - 1) * H * dv + v_pc[i]);
       dma_b128_at(pf_v + e, lds_at(OFF_V, CV::RPI, DVB, i));
     } else if ((i -= CV::PER_WAVE) < CT::PER_WAVE) {
       dma_b128_at(pf_t + t_off[i], lds_at(OFF_T, CT::RPI, GC, i));
     } else if ((i -= CT::PER_WAVE) < CT::PER_WAVE) {
+      if (MAP) return;
       dma_b128_at(pf_p + t_off[i], lds_at(OFF_P, CT::RPI, GC, i));
     } else if (i == CT::PER_WAVE) {
       if (w < 2) dma_b32_at(Ews + pf_chk * 2 * GC + GC * w + lane, pf_lds + (unsigned)((OFF_E + 2 * GC * w) * 2));
@@ -472,8 +486,11 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
 #pragma unroll
   for (int a = 0; a < ND; ++a)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      S[a][e] = state_in ? state_in[sbase + (int64_t)(16 * a + 4 * G + e) * dv + c16] : 0.f;
+    for (int e = 0; e < 4; ++e) {
+      const int d = 16 * a + 4 * G + e;
+      if (zero_v) S[a][e] = d == ncol0 + c16 ? 1.f : 0.f;  // identity start
+      else S[a][e] = (!MAP && state_in) ? state_in[sbase + (int64_t)d * sw + c16] : 0.f;
+    }
   const float ones[4] = {1.f, 1.f, 1.f, 1.f};
   if (rbeg < rend) {
     pf_setup(rbeg, 0, nullptr);
@@ -486,7 +503,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
     const int L = (int)min((int64_t)GC, rend - r0);
     // this wave's copies have landed (only the previous chunk's 4 output
     // stores were issued after them); then every wave's
-    if (r0 == rbeg) vm_wait_all();
+    if (r0 == rbeg || MAP) vm_wait_all();
     else vm_wait_4();
     lds_barrier();
     pf_setup(r0 + GC < rend ? r0 + GC : r0, buf ^ 1, reinterpret_cast<const int32_t*>(smem + buf * BUF + OFF_TOK));
@@ -513,7 +530,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       kf[0][t] = row_frag16<DK>(Ks, 16 * t + c16, 0, G);
-      qf[0][t] = row_frag16<DK>(Qs, 16 * t + c16, 0, G);
+      if (!MAP) qf[0][t] = row_frag16<DK>(Qs, 16 * t + c16, 0, G);
     }
 #pragma unroll
     for (int kb = 0; kb < NKD; ++kb) {
@@ -521,7 +538,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           kf[(kb + 1) & 1][t] = row_frag16<DK>(Ks, 16 * t + c16, kb + 1, G);
-          qf[(kb + 1) & 1][t] = row_frag16<DK>(Qs, 16 * t + c16, kb + 1, G);
+          if (!MAP) qf[(kb + 1) & 1][t] = row_frag16<DK>(Qs, 16 * t + c16, kb + 1, G);
         }
       }
 #pragma unroll
@@ -531,7 +548,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         Y[t] = mfma16(kf[kb & 1][t], sop, Y[t]);
-        O[t] = mfma16(sop, qf[kb & 1][t], O[t]);
+        if (!MAP) O[t] = mfma16(sop, qf[kb & 1][t], O[t]);
       }
     }
     CHAIN_PHASE();
@@ -543,7 +560,8 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
       for (int e = 0; e < 4; ++e) U[t][e] = 0.f;
 #pragma unroll
     for (int kb = 0; kb < GC / 32; ++kb) {
-      const h8v vb = col_frag16<DVB>(Vs, kb, 16 * w, lane);
+      h8v vb = {};
+      if (!zero_v) vb = col_frag16<DVB>(Vs, kb, 16 * w, lane);
       h8v yb;
       if constexpr (DELTA) {
         float s0[4], s1[4];
@@ -557,7 +575,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const h8v tf = row_frag16<GC>(Ts, 16 * t + c16, kb, G);
-        U[t] = mfma16(tf, vb, U[t]);
+        if (!zero_v) U[t] = mfma16(tf, vb, U[t]);
         if constexpr (DELTA) U[t] = mfma16(tf, yb, U[t]);
       }
     }
@@ -577,7 +595,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
     }
     // ---- O^T = O^T diag(gamma) + U^T P^T, stored as 16-byte row pieces
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < (MAP ? 0 : 4); ++t) {
       const float gm = Eg[16 * t + c16];
 #pragma unroll
       for (int e = 0; e < 4; ++e) O[t][e] *= gm;
@@ -585,7 +603,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
       for (int kb = 0; kb < GC / 32; ++kb) O[t] = mfma16(ub[kb], row_frag16<GC>(Ps, 16 * t + c16, kb, G), O[t]);
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < (MAP ? 0 : 4); ++t)
       if (16 * t + c16 < L)
         *reinterpret_cast<float4*>(o + ((r0 + 16 * t + c16) * H + h) * dv + ncol0 + 4 * G) =
             make_float4(O[t][0], O[t][1], O[t][2], O[t][3]);
@@ -605,7 +623,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
 #pragma unroll
   for (int a = 0; a < ND; ++a)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) state_out[sbase + (int64_t)(16 * a + 4 * G + e) * dv + c16] = S[a][e];
+    for (int e = 0; e < 4; ++e) state_out[sbase + (int64_t)(16 * a + 4 * G + e) * sw + c16] = S[a][e];
 }
 
 template <int DK, int NW>
@@ -857,8 +875,170 @@ __global__ __launch_bounds__(256) void k_gdn_prep(int H, int n_seg, const int32_
 }
 
 // ------------------------------------------------------------------ workspace + launch
-size_t gdn_chunk_ws_bytes(int64_t n_seg, int64_t n_rows, int H, int dk) {
-  return chunk_ws_layout(nullptr, n_seg, n_rows, H, dk).bytes;
+size_t gdn_chunk_ws_bytes(int64_t n_seg, int64_t n_rows, int H, int dk, int dv) {
+  const size_t chunk = chunk_ws_layout(nullptr, n_seg, n_rows, H, dk).bytes;
+  const ScanPlan plan = scan_plan(n_seg, n_rows, H, dv);
+  return chunk + (plan.on ? scan_ws_layout(nullptr, n_seg, plan.n_groups, H, dk, dv).bytes : 0);
+}
+
+// ------------------------------------------------------------------ long-segment scan
+// The state map of a run of chunks is affine: S_out = A S_in + B, B the state
+// the run reaches from a zero state, A (dk x dk) the map the run applies to the
+// entering state (the state it reaches from the identity with zero values).
+// For segments much longer than the grid is wide, gdn_chunk_fwd cuts every
+// segment into groups of lg chunks (group boundaries on chunk boundaries, so
+// the chunk numbering of the prep's factors is unchanged) and
+//   1. walks every group except each segment's last in MAP mode: its B over
+//      the dv value columns and its A over dk identity columns, in parallel;
+//   2. k_scan_states chains them in order per (segment, head, 32 columns):
+//      S_{g+1} = A_g S_g + B_g from the segment's entering state, float32,
+//      storing every group's entering state;
+//   3. walks every group with read-out from its entering state, in parallel;
+//   4. copies each segment's last group's final state to state_out.
+// The serial part is the short step 2 instead of the segment's whole walk.
+
+// Groups of lg chunks per segment (one group for an empty segment): grp_off
+// [n_groups + 1], grp_seg [n_groups + 1] (-1 past the last group, the
+// sentinel), seg_grp0 [n_seg + 1].  lg = max(kScanMinGroup, chunks / target)
+// over the segments' actual chunks, or the longest segment's chunk count (no
+// segment split) when it is below kScanMinSeg.  One block.
+__global__ __launch_bounds__(256) void k_make_groups(int n_seg, const int32_t* __restrict__ seg_off, int target,
+                                                     int n_groups, int32_t* __restrict__ grp_off,
+                                                     int32_t* __restrict__ grp_seg, int32_t* __restrict__ seg_grp0) {
+  __shared__ int32_t wsum[4];
+  __shared__ int32_t carry;
+  __shared__ int64_t tot_s[4];
+  __shared__ int32_t max_s[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int64_t tot = 0;
+  int mx = 0;
+  for (int s = tid; s < n_seg; s += 256) {
+    const int c = seg_chunks(seg_off, s);
+    tot += c;
+    mx = max(mx, c);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    tot += __shfl_xor(tot, o, 64);
+    mx = max(mx, __shfl_xor(mx, o, 64));
+  }
+  if (lane == 0) {
+    tot_s[wv] = tot;
+    max_s[wv] = mx;
+  }
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  tot = tot_s[0] + tot_s[1] + tot_s[2] + tot_s[3];
+  mx = max(max(max_s[0], max_s[1]), max(max_s[2], max_s[3]));
+  int lg = (int)((tot + target - 1) / target);
+  if (lg < kScanMinGroup) lg = kScanMinGroup;
+  if (mx < kScanMinSeg) lg = max(mx, 1);
+  const int rows_g = lg * GC;
+  for (int base = 0; base < n_seg; base += 256) {
+    const int s = base + tid;
+    int ng = 0;
+    if (s < n_seg) {
+      const int len = seg_off[s + 1] - seg_off[s];
+      ng = len > 0 ? (len + rows_g - 1) / rows_g : 1;
+    }
+    int x = ng;  // inclusive scan of the group counts
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(x, o, 64);
+      if (lane >= o) x += u;
+    }
+    if (lane == 63) wsum[wv] = x;
+    __syncthreads();
+    int pre = carry;
+    for (int w2 = 0; w2 < wv; ++w2) pre += wsum[w2];
+    const int first = pre + x - ng;
+    if (s < n_seg) {
+      seg_grp0[s] = first;
+      for (int j = 0; j < ng; ++j) {
+        grp_off[first + j] = seg_off[s] + j * rows_g;
+        grp_seg[first + j] = s;
+      }
+    }
+    __syncthreads();
+    if (tid == 255) carry = pre + x;
+    __syncthreads();
+  }
+  const int total = carry;  // <= n_groups (the host's bound)
+  if (tid == 0) seg_grp0[n_seg] = total;
+  const int32_t end = seg_off[n_seg];
+  for (int g = total + tid; g <= n_groups; g += 256) {
+    grp_off[g] = end;
+    grp_seg[g] = -1;
+  }
+}
+
+// Step 2: one block per (segment, head, 32 value columns); the state block
+// (dk x 32) in LDS, each thread one row and 16 columns of the product.
+__global__ __launch_bounds__(256) void k_scan_states(int H, int dk, int dv, int n_seg,
+                                                     const int32_t* __restrict__ seg_state,
+                                                     const int32_t* __restrict__ seg_grp0,
+                                                     const float* __restrict__ maps,
+                                                     const float* __restrict__ state_in, float* __restrict__ sg) {
+  __shared__ float Sx[128][33];
+  const int nb = dv / 32;
+  const int cb = blockIdx.x % nb, h = (blockIdx.x / nb) % H, s = blockIdx.x / (nb * H);
+  const int slot = seg_state ? seg_state[s] : s;
+  const int sw = dv + dk, tid = threadIdx.x;
+  for (int e = tid; e < dk * 32; e += 256) {
+    const int d = e >> 5, c = e & 31;
+    Sx[d][c] = state_in ? state_in[(((int64_t)slot * H + h) * dk + d) * dv + 32 * cb + c] : 0.f;
+  }
+  __syncthreads();
+  const int g0 = seg_grp0[s], g1 = seg_grp0[s + 1];
+  const int d = min(tid >> 1, dk - 1), c0 = 16 * (tid & 1);  // threads past dk rows repeat the last one
+  // this thread's row of A_g (dk floats) and 16 entries of B_g, loaded one
+  // group ahead so the loads run under the previous group's products
+  float4 ar[32];
+  float br[16];
+  auto load = [&](int g) {
+    const float* mrow = maps + ((((int64_t)g * H + h) * dk) + d) * sw;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) br[c] = mrow[32 * cb + c0 + c];
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if (4 * i < dk) ar[i] = *reinterpret_cast<const float4*>(mrow + dv + 4 * i);
+  };
+  if (g0 + 1 < g1) load(g0);
+  for (int g = g0; g < g1; ++g) {
+    float* out = sg + (((int64_t)g * H + h) * dk) * dv + 32 * cb;
+    for (int e = tid; e < dk * 32; e += 256) out[(int64_t)(e >> 5) * dv + (e & 31)] = Sx[e >> 5][e & 31];
+    if (g + 1 == g1) break;
+    float acc[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) acc[c] = br[c];  // B_g
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (4 * i >= dk) break;
+      const float av[4] = {ar[i].x, ar[i].y, ar[i].z, ar[i].w};  // A_g[d][4i .. 4i + 3]
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < 16; ++c) acc[c] = fmaf(av[u], Sx[4 * i + u][c0 + c], acc[c]);
+    }
+    if (g + 2 < g1) load(g + 1);
+    __syncthreads();  // every thread has read the block
+    if ((tid >> 1) < dk)
+#pragma unroll
+      for (int c = 0; c < 16; ++c) Sx[d][c0 + c] = acc[c];
+    __syncthreads();
+  }
+}
+
+// Step 4: each segment's last group's final state to its slot.
+__global__ __launch_bounds__(256) void k_scan_final(int H, int dk, int dv, const int32_t* __restrict__ seg_state,
+                                                    const int32_t* __restrict__ seg_grp0, const float* __restrict__ sg,
+                                                    float* __restrict__ state_out) {
+  const int h = blockIdx.x % H, s = blockIdx.x / H;
+  const int slot = seg_state ? seg_state[s] : s;
+  const int g = seg_grp0[s + 1] - 1;
+  const float4* src = reinterpret_cast<const float4*>(sg + ((int64_t)g * H + h) * dk * dv);
+  float4* dst = reinterpret_cast<float4*>(state_out + ((int64_t)slot * H + h) * dk * dv);
+  for (int e = threadIdx.x; e < dk * dv / 4; e += 256) dst[e] = src[e];
 }
 
 template <int DK, int NW, bool DELTA, int MODE>
@@ -882,23 +1062,67 @@ static mom_status launch_chain(const mom_dims& d, int n_seg, const int32_t* seg_
   return MOM_OK;
 }
 
-template <int DK, int NW, bool DELTA>
+// The walk over n_seg segments (or, with MAP, groups): width columns of the
+// state from col_base, state rows sw wide (width = sw = dv for the forward).
+template <int DK, int NW, bool DELTA, bool MAP>
 static mom_status launch_chain16(const mom_dims& d, int n_seg, const int32_t* seg_off, const int32_t* seg_state,
                                  const ChunkWs& W, const int32_t* row_token, const void* q, const void* k,
-                                 const void* v, const float* state_in, float* state_out, float* o, hipStream_t st) {
+                                 const void* v, const float* state_in, float* state_out, float* o, hipStream_t st,
+                                 int width, int col_base, int sw, int ident, const int32_t* grp_seg) {
   constexpr size_t lds = chain16_lds_bytes<DK, NW>();
   static bool attr = false;  // the dynamic LDS limit is raised once per kernel
   if (!attr) {
-    if (hipFuncSetAttribute((const void*)k_gdn_chain16<DK, NW, DELTA>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess)
+    if (hipFuncSetAttribute((const void*)k_gdn_chain16<DK, NW, DELTA, MAP>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return MOM_ERR_LAUNCH;
     attr = true;
   }
-  const int64_t blocks = (int64_t)n_seg * d.H * (d.dv / (16 * NW));
+  const int64_t blocks = (int64_t)n_seg * d.H * (width / (16 * NW));
   if (blocks > 0)
-    hipLaunchKernelGGL((k_gdn_chain16<DK, NW, DELTA>), dim3((unsigned)blocks), dim3(64 * NW), lds, st, d.H, d.dv,
-                       n_seg, seg_off, seg_state, (const f16_t*)k, (const f16_t*)v, W.T, W.P, W.E, row_token,
-                       (const f16_t*)q, state_in, state_out, o);
+    hipLaunchKernelGGL((k_gdn_chain16<DK, NW, DELTA, MAP>), dim3((unsigned)blocks), dim3(64 * NW), lds, st, d.H,
+                       d.dv, width, col_base, sw, ident, n_seg, seg_off, seg_state, grp_seg, (const f16_t*)k,
+                       (const f16_t*)v, W.T, W.P, W.E, row_token, (const f16_t*)q, state_in, state_out, o);
+  return MOM_OK;
+}
+
+template <int DK, bool DELTA>
+static mom_status walk(const mom_dims& d, int n_seg, const int32_t* seg_off, const int32_t* seg_state,
+                       const ChunkWs& W, const int32_t* row_token, const void* q, const void* k, const void* v,
+                       const float* state_in, float* state_out, float* o, hipStream_t st) {
+  return d.dv % 128 == 0 ? launch_chain16<DK, 8, DELTA, false>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v,
+                                                               state_in, state_out, o, st, d.dv, 0, d.dv, 0, nullptr)
+                         : launch_chain16<DK, 4, DELTA, false>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v,
+                                                               state_in, state_out, o, st, d.dv, 0, d.dv, 0, nullptr);
+}
+
+template <int DK, bool DELTA>
+static mom_status launch_chunk_scan(const mom_dims& d, int n_seg, const int32_t* seg_off, const int32_t* seg_state,
+                                    const ChunkWs& W, const ScanWs& X, const ScanPlan& plan, const int32_t* row_token,
+                                    const void* q, const void* k, const void* v, const float* state_in,
+                                    float* state_out, float* o, hipStream_t st) {
+  const int G = (int)plan.n_groups, sw = d.dv + DK;
+  hipLaunchKernelGGL(k_make_groups, dim3(1), dim3(256), 0, st, n_seg, seg_off, plan.target, G, X.grp_off, X.grp_seg,
+                     X.seg_grp0);
+  // 1. the groups' maps: B over the values, A over identity columns
+  mom_status r =
+      d.dv % 128 == 0
+          ? launch_chain16<DK, 8, DELTA, true>(d, G, X.grp_off, nullptr, W, row_token, q, k, v, nullptr, X.maps,
+                                               nullptr, st, d.dv, 0, sw, 0, X.grp_seg)
+          : launch_chain16<DK, 4, DELTA, true>(d, G, X.grp_off, nullptr, W, row_token, q, k, v, nullptr, X.maps,
+                                               nullptr, st, d.dv, 0, sw, 0, X.grp_seg);
+  if (r != MOM_OK) return r;
+  r = launch_chain16<DK, DK / 16, DELTA, true>(d, G, X.grp_off, nullptr, W, row_token, q, k, v, nullptr, X.maps,
+                                               nullptr, st, DK, d.dv, sw, 1, X.grp_seg);
+  if (r != MOM_OK) return r;
+  // 2. entering state of every group
+  hipLaunchKernelGGL(k_scan_states, dim3((unsigned)((int64_t)n_seg * d.H * (d.dv / 32))), dim3(256), 0, st, d.H, DK,
+                     d.dv, n_seg, seg_state, X.seg_grp0, X.maps, state_in, X.sg);
+  // 3. every group's walk with read-out, from its entering state (in place)
+  r = walk<DK, DELTA>(d, G, X.grp_off, nullptr, W, row_token, q, k, v, X.sg, X.sg, o, st);
+  if (r != MOM_OK) return r;
+  // 4. final states
+  hipLaunchKernelGGL(k_scan_final, dim3((unsigned)((int64_t)n_seg * d.H)), dim3(256), 0, st, d.H, DK, d.dv, seg_state,
+                     X.seg_grp0, X.sg, state_out);
   return MOM_OK;
 }
 
@@ -914,12 +1138,12 @@ static mom_status launch_chunk(const mom_dims& d, int n_seg, int n_rows, const i
     hipLaunchKernelGGL((k_gdn_prep<DK, DELTA>), dim3((unsigned)prep_blocks), dim3(256), 0, st, d.H, n_seg,
                        seg_off, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.E,
                        nullptr);
+  const ScanPlan plan = scan_plan(n_seg, n_rows, d.H, d.dv);
   const mom_status r =
-      d.dv % 128 == 0
-          ? launch_chain16<DK, 8, DELTA>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o,
-                                         st)
-          : launch_chain16<DK, 4, DELTA>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o,
-                                         st);
+      plan.on ? launch_chunk_scan<DK, DELTA>(d, n_seg, seg_off, seg_state, W,
+                                             scan_ws_layout((char*)ws + W.bytes, n_seg, plan.n_groups, d.H, DK, d.dv),
+                                             plan, row_token, q, k, v, state_in, state_out, o, st)
+              : walk<DK, DELTA>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in, state_out, o, st);
   if (r != MOM_OK) return r;
   return launch_status();
 }

@@ -1,6 +1,7 @@
 """The C ABI without a GPU: the library loads, exports every function the header
 declares, sizes its workspace, and rejects bad arguments before any launch."""
 import ctypes
+import dataclasses
 import os
 import re
 import subprocess
@@ -213,3 +214,32 @@ def test_dispatch_noalloc_checks_before_any_launch():
     assert L.mom_status_string(-7).decode().startswith("sizes exceed")
     # exactly at the limit passes the size check (then needs a GPU, not called here)
     assert 16 * 64 * 64 == 65536
+
+
+@needs_lib
+def test_chunk_workspace_reserves_the_scan_only_for_few_long_segments():
+    """gdn_chunk_fwd's workspace: the per-chunk factors (T and P half, the
+    decays float32, per (chunk, head)), plus the long-segment scan's groups,
+    maps and entering states only when the walk would run at most 8 blocks
+    over long segments (one long sequence with 4 heads, two with 2), not for
+    any call the layer makes at its configurations."""
+    L = mom.lib()
+    a256 = lambda b: (b + 255) // 256 * 256
+
+    def factors(n_seg, n_rows, H):
+        nch = n_rows // 64 + n_seg
+        return 2 * a256(nch * H * 64 * 64 * 2) + a256(nch * H * 2 * 64 * 4)
+
+    for name, n_seg, scan, H in (("l380m", 40, False, None), ("l380m", 8, False, None), ("long32k", 5, False, None),
+                                 ("long32k", 1, False, None), ("long32k", 1, True, 4), ("long32k", 2, True, 2)):
+        c = CONFIGS[name] if H is None else dataclasses.replace(CONFIGS[name], H=H)
+        d = mom.dims_of(c)
+        N = c.B * c.T * (c.K + 1)
+        got = L.gdn_chunk_workspace_bytes(ctypes.byref(d), n_seg, N)
+        if scan:
+            n_groups = N // (8 * 64) + n_seg
+            extra = a256((n_groups + 1) * 4) * 2 + a256((n_seg + 1) * 4) + \
+                a256(n_groups * c.H * c.dk * (c.dv + c.dk) * 4) + a256(n_groups * c.H * c.dk * c.dv * 4)
+            assert got == factors(n_seg, N, c.H) + extra, (name, n_seg)
+        else:
+            assert got == factors(n_seg, N, c.H), (name, n_seg)

@@ -365,6 +365,54 @@ def test_chunk_segments(store, dk, dv, rule):
     assert np.all(np.isnan(sg[unused]))
 
 
+@pytest.mark.parametrize("dk,dv,rule", [(128, 128, "gdn"), (128, 256, "gdn"), (64, 64, "gdn"), (128, 256, "gla")])
+def test_chunk_long_segments_scan(dk, dv, rule):
+    """Few long segments (the walk alone would run at most 8 blocks): the
+    recurrence cuts them into groups of chunks, walks the groups' state maps in
+    parallel, chains the maps and walks every group from its entering state.
+    Ragged lengths (an empty segment, and a one-row one for the narrower heads),
+    random entering states in permuted slots, queries gathered by token;
+    checked against the token recurrence."""
+    H = 1 if dv == 256 else 2
+    lens = np.array([3000, 0, 2500, 4160]) if dv == 256 else np.array([3000, 0, 1, 4160])
+    seg_off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N = int(seg_off[-1])
+    n_seg = len(lens)
+    cfg = synth.LayerConfig(1, 1, 64, H, dk, dv, 1, 1, "bf16")
+    dims = mom.dims_of(cfg)
+    # the workspace holds the per-chunk factors and, only on the scan path, the groups' maps and states
+    a256 = lambda b: (b + 255) // 256 * 256
+    nch = N // 64 + n_seg
+    factors = 2 * a256(nch * H * 64 * 64 * 2) + a256(nch * H * 2 * 64 * 4)
+    assert mom.gdn_chunk_workspace_bytes(dims, n_seg, N) >= factors + 2 * H * dk * dv * 4, "scan path not taken"
+    ch = synth.make_chain_inputs(N, H, dk, dv, seed=dk + 3 * dv, store="f16")
+    n_tok = N + 7
+    row_token = np.random.default_rng(11).permutation(n_tok)[:N].astype(np.int32)
+    qtok = np.zeros((n_tok, H, dk), np.float32)
+    qtok[row_token] = ch["q"]
+    n_state = n_seg + 2
+    seg_state = np.random.default_rng(12).permutation(n_state)[:n_seg].astype(np.int32)
+    S0 = (np.random.default_rng(13).standard_normal((n_state, H, dk, dv)) * 0.1).astype(np.float32)
+    so = torch.full((n_state, H, dk, dv), float("nan"), device="cuda")
+    o = torch.full((N, H, dv), float("nan"), device="cuda")
+    log("chunk scan", dk, dv, rule)
+    chunk = mom.gla_chunk_fwd if rule == "gla" else mom.gdn_chunk_fwd
+    f16 = lambda a: to_gpu(a, torch.float16)
+    chunk(dims, n_seg, N, n_tok, n_state, to_gpu(seg_off), to_gpu(seg_state), to_gpu(row_token), f16(qtok),
+          f16(ch["k"]), f16(ch["v"]), to_gpu(ch["alpha"]), to_gpu(ch["beta"]), to_gpu(S0), so, o,
+          mom.chunk_workspace(dims, n_seg, N))
+    torch.cuda.synchronize()
+    st = S0.astype(np.float64).copy()
+    o_ref = oracle.segments(seg_off, seg_state, row_token, qtok, ch["k"], ch["v"], ch["alpha"], ch["beta"], st,
+                            rule=rule)
+    assert_close("o", o.cpu().numpy(), o_ref, *TOL["bf16"])
+    sg = so.cpu().numpy()
+    assert_close("state", sg[seg_state], st[seg_state], *TOL["bf16"])
+    assert np.array_equal(sg[seg_state[1]], S0[seg_state[1]])  # the empty segment copies its state
+    unused = sorted(set(range(n_state)) - set(seg_state.tolist()))
+    assert np.all(np.isnan(sg[unused]))
+
+
 @pytest.mark.parametrize("B,T,full", [(2, 300, False), (8, 2048, True)])
 def test_single_memory_enlarged(B, T, full):
     """One plain Gated DeltaNet memory of value width 768 (the 380M layer's
