@@ -82,7 +82,8 @@
  * products.  Gates, router weights, outputs and states are always float32.
  *
  * Supported shapes: dk in {64,128}; dv in {64,128,256}, and for every entry
- * point but gdn_decode_step also any multiple of 128 up to 1024; chunk == 64;
+ * point but gdn_decode_step also any multiple of 128 up to 1024; chunk == 64,
+ * or 16, 32 or 64 with float32 storage (MOM_DTYPE_F32);
  * D % 64 == 0, 64 <= D <= 8192; 1 <= topk <= M <= 64, topk <= 8; B,T >= 1;
  * N < 2^31.
  */
@@ -118,7 +119,7 @@ typedef struct mom_dims {
   int32_t dv;     /* value dimension per head */
   int32_t M;      /* routed memories (the shared memory is index M) */
   int32_t topk;   /* memories selected per token */
-  int32_t chunk;  /* chunk length of the chunkwise recurrence (64) */
+  int32_t chunk;  /* chunk length of the chunkwise recurrence (64; float32: 16, 32 or 64) */
   int32_t dtype;  /* MOM_DTYPE_F32 or MOM_DTYPE_BF16 */
 } mom_dims;
 

@@ -68,7 +68,8 @@ inline mom_status check_dims(const mom_dims* d) {
   // 64, 128 or 256 everywhere; a multiple of 128 up to 1024 for the entry points
   // other than gdn_decode_step (which rejects it)
   if (d->dv != 64 && !(d->dv % 128 == 0 && d->dv >= 128 && d->dv <= 1024)) return MOM_ERR_UNSUPPORTED;
-  if (d->chunk != 64) return MOM_ERR_UNSUPPORTED;
+  // chunk rows: 64 on the matrix cores; 16, 32 or 64 with float32 storage
+  if (d->chunk != 64 && !(d->dtype == MOM_DTYPE_F32 && (d->chunk == 16 || d->chunk == 32))) return MOM_ERR_UNSUPPORTED;
   if (d->dtype != MOM_DTYPE_F32 && d->dtype != MOM_DTYPE_BF16) return MOM_ERR_UNSUPPORTED;
   if (d->D < 64 || d->D > 8192 || d->D % 64 != 0) return MOM_ERR_UNSUPPORTED;
   if (d->H > 64) return MOM_ERR_UNSUPPORTED;

@@ -20,10 +20,11 @@
 
 namespace mom {
 
-constexpr int VC = 64;    // chunk rows
 constexpr int VDVB = 32;  // value columns per block
 
-template <typename IT, int DK, bool DELTA>
+// VC: chunk rows (16, 32 or 64; the chunk form's result does not depend on it
+// beyond rounding)
+template <typename IT, int DK, bool DELTA, int VC>
 __global__ __launch_bounds__(256) void k_gdn_chunk_valu(int H, int dv, int n_seg, const int32_t* __restrict__ seg_off,
                                                         const int32_t* __restrict__ seg_state,
                                                         const int32_t* __restrict__ row_token, const IT* __restrict__ q,
@@ -151,10 +152,19 @@ mom_status launch_gdn_chunk_valu(const mom_dims& d, int n_seg, const int32_t* se
                                  float* o, bool delta, hipStream_t st) {
   const int64_t blocks = (int64_t)n_seg * d.H * (d.dv / VDVB);
   if (blocks == 0) return MOM_OK;
-#define MOM_VALU_CASE(DK, DELTA)                                                                                  \
-  hipLaunchKernelGGL((k_gdn_chunk_valu<IT, DK, DELTA>), dim3((unsigned)blocks), dim3(256), 0, st, d.H, d.dv,     \
+#define MOM_VALU_VC(DK, DELTA, VC)                                                                                \
+  hipLaunchKernelGGL((k_gdn_chunk_valu<IT, DK, DELTA, VC>), dim3((unsigned)blocks), dim3(256), 0, st, d.H, d.dv, \
                      n_seg, seg_off, seg_state, row_token, (const IT*)q, (const IT*)k, (const IT*)v, alpha_p,      \
                      beta_p, state_in, state_out, o)
+#define MOM_VALU_CASE(DK, DELTA)        \
+  do {                                  \
+    if (d.chunk == 16)                  \
+      MOM_VALU_VC(DK, DELTA, 16);       \
+    else if (d.chunk == 32)             \
+      MOM_VALU_VC(DK, DELTA, 32);       \
+    else                                \
+      MOM_VALU_VC(DK, DELTA, 64);       \
+  } while (0)
   if (d.dk == 64) {
     if (delta) MOM_VALU_CASE(64, true);
     else MOM_VALU_CASE(64, false);
@@ -163,6 +173,7 @@ mom_status launch_gdn_chunk_valu(const mom_dims& d, int n_seg, const int32_t* se
     else MOM_VALU_CASE(128, false);
   }
 #undef MOM_VALU_CASE
+#undef MOM_VALU_VC
   return launch_status();
 }
 

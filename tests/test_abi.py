@@ -64,6 +64,20 @@ def test_bad_dims_are_rejected(field, value, status):
 
 
 @needs_lib
+def test_chunk_lengths_per_storage():
+    """Float32 storage takes chunks of 16, 32 or 64 rows; half precision (the
+    matrix-core path) only 64; other lengths are refused."""
+    L = mom.lib()
+    for dtype, chunk, ok in [(mom.DTYPE_F32, 16, True), (mom.DTYPE_F32, 32, True), (mom.DTYPE_F32, 64, True),
+                             (mom.DTYPE_F32, 48, False), (mom.DTYPE_F32, 128, False), (mom.DTYPE_F32, 8, False),
+                             (mom.DTYPE_BF16, 16, False), (mom.DTYPE_BF16, 32, False), (mom.DTYPE_BF16, 64, True)]:
+        d = _dims(dtype=dtype, chunk=chunk)
+        assert (L.mom_workspace_bytes(ctypes.byref(d), 0) > 0) == ok, (dtype, chunk)
+        if not ok:
+            assert L.mom_route(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, None) == -3
+
+
+@needs_lib
 def test_wide_values_only_outside_decode():
     """A value width that is a multiple of 128 above 256 passes the shared
     checks (the chunk recurrence takes it) but gdn_decode_step rejects it."""

@@ -365,6 +365,65 @@ def test_chunk_segments(store, dk, dv, rule):
     assert np.all(np.isnan(sg[unused]))
 
 
+CHUNK_LENGTHS = [15, 16, 17, 0, 1, 31, 32, 33, 100, 64, 129]
+
+
+@pytest.mark.parametrize("dk,dv,rule", [(64, 64, "gdn"), (128, 128, "gdn"), (64, 64, "gla"), (128, 256, "gla"),
+                                         (64, 64, "deltanet")])
+def test_chunk_length_invariance(dk, dv, rule):
+    """The chunkwise form computes the recurrence whatever the chunk length:
+    float32 segments at chunks of 16, 32 and 64 rows each match the
+    token-by-token oracle, and one another, on lengths around each chunk
+    boundary."""
+    H = 2
+    lens = np.array(CHUNK_LENGTHS)
+    seg_off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N = int(seg_off[-1])
+    n_seg = len(lens)
+    ch = synth.make_chain_inputs(N, H, dk, dv, seed=3 * dk + dv, store="f32")
+    if rule == "deltanet":
+        ch["alpha"] = np.ones_like(ch["alpha"])
+    row_token = np.arange(N, dtype=np.int32)
+    seg_state = np.arange(n_seg, dtype=np.int32)
+    S0 = (np.random.default_rng(5).standard_normal((n_seg, H, dk, dv)) * 0.1).astype(np.float32)
+    st = S0.astype(np.float64).copy()
+    o_ref = oracle.segments(seg_off, seg_state, row_token, ch["q"], ch["k"], ch["v"], ch["alpha"], ch["beta"], st,
+                            rule="gla" if rule == "gla" else "gdn")
+    tol = (2e-5, 1e-5) if rule == "deltanet" else TOL["f32"]
+    outs = {}
+    for C in (16, 32, 64):
+        cfg = synth.LayerConfig(1, 1, 64, H, dk, dv, 1, 1, "f32", chunk=C)
+        dims = mom.dims_of(cfg)
+        so = torch.full((n_seg, H, dk, dv), float("nan"), device="cuda")
+        o = torch.full((N, H, dv), float("nan"), device="cuda")
+        log("chunk length", C, dk, dv, rule)
+        chunk = mom.gla_chunk_fwd if rule == "gla" else mom.gdn_chunk_fwd
+        chunk(dims, n_seg, N, N, n_seg, to_gpu(seg_off), to_gpu(seg_state), to_gpu(row_token), to_gpu(ch["q"]),
+              to_gpu(ch["k"]), to_gpu(ch["v"]), to_gpu(ch["alpha"]), to_gpu(ch["beta"]), to_gpu(S0), so, o,
+              mom.chunk_workspace(dims, n_seg, N))
+        torch.cuda.synchronize()
+        outs[C] = (o.cpu().numpy(), so.cpu().numpy())
+        assert_close(f"o C={C}", outs[C][0], o_ref, *tol)
+        assert_close(f"state C={C}", outs[C][1], st, *tol)
+    for C in (16, 32):
+        assert_close(f"o C={C} vs 64", outs[C][0], outs[64][0], *tol)
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_layer_tiny_f32_chunk_lengths(chunk):
+    """The whole float32 layer at chunks of 16 and 32 rows against the oracle."""
+    cfg = dataclasses.replace(CFG["tiny_f32"], chunk=chunk)
+    log("layer", cfg.name, "chunk", chunk)
+    inp = synth.make_layer_inputs(cfg, seed=7)
+    S0 = synth.make_state(cfg, cfg.B, seed=8)
+    out, st, b = run_layer_gpu(cfg, inp, S0)
+    ref = oracle.layer(dims_tuple(cfg), inp["x"], inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"],
+                       inp["alpha"], inp["beta"], state0=S0)
+    np.testing.assert_array_equal(b["idx"].cpu().numpy(), ref["idx"])
+    assert_close("out", out, ref["out"], *TOL["f32"])
+    assert_close("state", st, ref["state"], *TOL["f32"])
+
+
 @pytest.mark.parametrize("dk,dv,rule", [(128, 128, "gdn"), (128, 256, "gdn"), (64, 64, "gdn"), (128, 256, "gla")])
 def test_chunk_long_segments_scan(dk, dv, rule):
     """Few long segments (the walk alone would run at most 8 blocks): the
@@ -522,6 +581,32 @@ def test_gla_layer(name, B, T):
     tol = TOL[cfg.dtype]
     assert_close("out", out, ref["out"], *tol)
     assert_close("state", st, ref["state"], *tol)
+
+
+@pytest.mark.parametrize("name,B,T", [("tiny_f32", 1, 256), ("l380m", 2, 300)])
+def test_deltanet_layer(name, B, T):
+    """DeltaNet memories (forget gates fixed at 1, no decay) behind the whole
+    layer, against the checker's layer with the same gates.  Without decay the
+    outputs carry the whole history and grow (to about 26 in float32 and 41
+    at the 380M widths here, 2.7x the gated case), so max-abs is held to the
+    configs' figure or a fixed fraction of the largest output, whichever is
+    larger: 1e-6 in float32 (about 8 ulp), 1e-3 with bf16 operands (half a
+    bf16 ulp); rel-L2 stays at the configs' figure."""
+    cfg = small(CFG[name], B, T)
+    log("deltanet layer", name, B, T)
+    inp = synth.make_layer_inputs(cfg, seed=9)
+    inp["alpha"] = np.ones_like(inp["alpha"])
+    S0 = synth.make_state(cfg, B, seed=10)
+    out, st, b = run_layer_gpu(cfg, inp, S0)
+    ref = oracle.layer(dims_tuple(cfg), inp["x"], inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"],
+                       inp["alpha"], inp["beta"], state0=S0)
+    np.testing.assert_array_equal(b["idx"].cpu().numpy(), ref["idx"])
+    max_abs, rel_l2 = TOL[cfg.dtype]
+    frac = 1e-3 if cfg.dtype == "bf16" else 1e-6
+    tol_o = (max(max_abs, frac * float(np.abs(ref["out"]).max())), rel_l2)
+    tol_s = (max(max_abs, frac * float(np.abs(ref["state"]).max())), rel_l2)
+    assert_close("out", out, ref["out"], *tol_o)
+    assert_close("state", st, ref["state"], *tol_s)
 
 
 def oracle_bh_slice(cfg, inp, idx, w, b_sel, h, t_max):
