@@ -295,10 +295,10 @@ class Workload:
         d, N, NT = b["dims"], b["N"], b["NT"]
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         rec(0)
-        mom.mom_route(d, x, layer.w_r, layer.bias, b["idx"], b["w"])
+        mom.mom_route_count(d, x, layer.w_r, layer.bias, b["idx"], b["w"], b["ws"])
         rec(1)
-        mom.mom_dispatch(d, b["idx"], x, alpha, beta, b["seg_off"], b["perm"], b["inv"], None, b["alpha_p"],
-                         b["beta_p"], b["ws"])
+        mom.mom_dispatch_counted(d, b["idx"], x, alpha, beta, b["seg_off"], b["perm"], b["inv"], None,
+                                 b["alpha_p"], b["beta_p"], b["ws"])
         rec(2)
         mom.mom_project(d, x, b["perm"], b["seg_off"], layer.w_q, layer.w_k, layer.w_v, b["q"], b["k"], b["v"])
         rec(3)

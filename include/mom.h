@@ -30,8 +30,8 @@
  *                    the same forward and gradients split for a training
  *                    step: the forward keeps its chunk factors and states for
  *                    the backward, which then does not recompute them.
- *   mom_route_count, mom_dispatch_counted
- *                    route and histogram in one launch for a decode step.
+ *   mom_route_count, mom_dispatch_counted, mom_dispatch_counted_part
+ *                    route and histogram in one launch (prefill and decode).
  *   gdn_decode_step_combined
  *                    the decode step with the combine folded in.
  *   gdn_decode_step  one recurrent step per sequence (constant-cost inference,
@@ -153,7 +153,7 @@ mom_status mom_dispatch(const mom_dims* dims, const int32_t* idx, const void* x,
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  The same outputs as mom_dispatch (bit for bit);
  * every other argument, layout and error as there.  The dispatch's counts
- * (int32 [M][B][ceil(T / 256)], M*B*ceil(T / 256) <= 65536) live in a fixed
+ * (int32 [M][B][ceil(T / 64)], M*B*ceil(T / 64) <= 65536) live in a fixed
  * 256 KiB array of the library's own in each GPU's memory, held from the
  * first call on that GPU until the process ends; larger sizes return
  * MOM_ERR_TOO_LARGE before any launch.  The call allocates nothing.  The
@@ -166,24 +166,33 @@ mom_status mom_dispatch_noalloc(const mom_dims* dims, const int32_t* idx, const 
                                 const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv,
                                 void* x_packed, float* alpha_p, float* beta_p, void* stream);
 
-/* Route and histogram in one launch, for one position per sequence (a decode
- * step, dims->T == 1; otherwise MOM_ERR_UNSUPPORTED): the outputs of
- * mom_route (same arithmetic as its general kernel), and the dispatch's
- * per-(memory, sequence) counts written into ws (at least
- * mom_workspace_bytes(dims, MOM_WS_DISPATCH) bytes), which
- * mom_dispatch_counted then reads instead of counting again (podcast.do-not-
- * panic.com page, "Solving scatter-gather without new kernels": the counting
- * sort's histogram comes from the router's own pass). */
+/* Route and histogram in one pass (podcast.do-not-panic.com page, "Solving
+ * scatter-gather without new kernels": the counting sort's histogram comes
+ * from the router's own pass): the outputs of mom_route, and the dispatch's
+ * counts of every 64 positions of every sequence per memory (int32
+ * [M][B][ceil(T / 64)], every entry written, nothing to clear) in ws (at
+ * least mom_workspace_bytes(dims, MOM_WS_DISPATCH) bytes), which
+ * mom_dispatch_counted and mom_dispatch_counted_part then read instead of
+ * counting again.  One launch for bfloat16 rows with D = 1024 and M <= 16 or
+ * D = 2048 and M <= 4, and for T == 1 (a decode step); other shapes run the
+ * router and then the dispatch's counting kernel.  idx and w are those of
+ * mom_route (the selections and weights of the same exact logits). */
 mom_status mom_route_count(const mom_dims* dims, const void* x, const void* w_r, const float* bias,
                            int32_t* idx, float* w, void* ws, size_t ws_bytes, void* stream);
 
-/* mom_dispatch for dims->T == 1 (else MOM_ERR_UNSUPPORTED) when ws holds the
- * counts mom_route_count wrote for the same idx: the same outputs, one launch
- * fewer. */
+/* mom_dispatch when ws holds the counts mom_route_count wrote for the same idx
+ * and dims: the same outputs, without the counting launch. */
 mom_status mom_dispatch_counted(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
                                 const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv,
                                 void* x_packed, float* alpha_p, float* beta_p, void* ws, size_t ws_bytes,
                                 void* stream);
+
+/* mom_dispatch_part (parts as there) reading the counts of mom_route_count
+ * from ws like mom_dispatch_counted; part 1 reads neither. */
+mom_status mom_dispatch_counted_part(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
+                                     const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv,
+                                     void* x_packed, float* alpha_p, float* beta_p, void* ws, size_t ws_bytes,
+                                     int32_t part, void* stream);
 
 /* Projections.  q[t] = w_q x[t] for every token; for packed row r of memory m
  * (from seg_off): k[r] = w_k[m] x[perm[r]] normalised to unit L2 norm per head

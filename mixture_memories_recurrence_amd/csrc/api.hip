@@ -84,8 +84,8 @@ extern "C" size_t mom_workspace_bytes(const mom_dims* dims, int32_t which) {
   if (check_dims(dims) != MOM_OK) return 0;
   const mom_dims& d = *dims;
   if (which == MOM_WS_DISPATCH) {
-    const int64_t ntile = (d.T + kDispatchTile - 1) / kDispatchTile;
-    const int64_t bytes = (int64_t)d.M * d.B * ntile * 4;
+    const int64_t nsub = (d.T + kCountTile - 1) / kCountTile;
+    const int64_t bytes = (int64_t)d.M * d.B * nsub * 4;
     return (size_t)((bytes + 255) / 256 * 256);
   }
   if (which == MOM_WS_CHUNK) {

@@ -66,7 +66,6 @@ __device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmc
 // used.
 __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void vm_wait_8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
 __device__ __forceinline__ void vm_wait_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
 
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));

@@ -19,7 +19,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
-constexpr int kDispatchTile = 256;  // positions per dispatch tile
+constexpr int kDispatchTile = 256;  // positions per dispatch tile (one scatter block)
+constexpr int kCountTile = 64;      // positions per dispatch count (one wave)
 
 // ---------------------------------------------------------------- conversions
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
@@ -96,6 +97,9 @@ inline mom_status launch_status() {
 }
 
 inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// dispatch.hip: the dispatch's per-64-position counts of idx into cnt
+mom_status dispatch_count_only(const mom_dims* dims, const int32_t* idx, int32_t* cnt, hipStream_t st);
 
 // ---------------------------------------------------------------- wave helpers
 template <typename T>

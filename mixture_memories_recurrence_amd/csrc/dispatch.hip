@@ -4,9 +4,12 @@
 // without new kernels").
 //
 // A stable counting sort, all integer work:
-//   k_count   one block per (tile of 256 positions, sequence): per-memory counts
-//             of the tile, written to cnt[m][b][tile];
-//   k_scan    one block: exclusive scan of cnt in (m, b, tile) order, which is
+//   k_count   one block per (tile of 256 positions, sequence), one wave per
+//             64 positions: per-memory counts of each 64 positions from wave
+//             ballots, written to cnt[m][b][sub] (sub = position / 64; no
+//             atomics, every entry written).  mom_route_count writes the same
+//             counts from the router's pass, which saves this launch;
+//   k_scan    one block: exclusive scan of cnt in (m, b, sub) order, which is
 //             exactly the packed row order; writes seg_off.  When cnt is small
 //             (at most kFuseScan entries) every k_scatter block scans it in
 //             LDS itself instead, which saves this launch;
@@ -24,32 +27,36 @@
 namespace mom {
 
 constexpr int kTile = kDispatchTile;
+constexpr int kSub = kCountTile;
+constexpr int kSubPerTile = kTile / kSub;
+static_assert(kSub == kWave && kTile % kSub == 0, "one wave per count");
 constexpr int kFuseScan = 8192;  // largest cnt scanned inside k_scatter
 
-__global__ __launch_bounds__(kTile) void k_count(int B, int T, int M, int K, int ntile,
+__global__ __launch_bounds__(kTile) void k_count(int B, int T, int M, int K, int nsub,
                                                  const int32_t* __restrict__ idx, int32_t* __restrict__ cnt) {
-  __shared__ int32_t c[64];
   const int tile = blockIdx.x, b = blockIdx.y;
-  if (threadIdx.x < 64) c[threadIdx.x] = 0;
-  __syncthreads();
-  const int t = tile * kTile + threadIdx.x;
-  if (t < T) {
-    const int64_t tok = (int64_t)b * T + t;
-    for (int j = 0; j < K; ++j) {
-      const int m = idx[tok * K + j];
-      if ((unsigned)m < (unsigned)M) atomicAdd(&c[m], 1);  // out-of-range entries are ignored
-    }
+  const int lane = threadIdx.x & 63, sub = tile * kSubPerTile + (threadIdx.x >> 6);
+  if (sub >= nsub) return;  // whole wave
+  const int t = sub * kSub + lane;
+  const int64_t tok = (int64_t)b * T + t;
+  int mem[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) mem[j] = (t < T && j < K) ? idx[tok * K + j] : -1;
+  for (int m = 0; m < M; ++m) {  // out-of-range entries are ignored
+    bool f = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f |= (mem[j] == m);
+    const int n = __popcll(__ballot(f));
+    if (lane == 0) cnt[((int64_t)m * B + b) * nsub + sub] = n;
   }
-  __syncthreads();
-  if (threadIdx.x < M) cnt[((int64_t)threadIdx.x * B + b) * ntile + tile] = c[threadIdx.x];
 }
 
 // Exclusive scan of n counts in place (single block of 1024 threads).
-__global__ __launch_bounds__(1024) void k_scan(int B, int T, int M, int K, int ntile, int last_seg,
+__global__ __launch_bounds__(1024) void k_scan(int B, int T, int M, int K, int nsub, int last_seg,
                                                int32_t* __restrict__ cnt, int32_t* __restrict__ seg_off) {
   __shared__ int32_t wsum[16];
   __shared__ int32_t carry_s;
-  const int n = M * B * ntile;
+  const int n = M * B * nsub;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   if (threadIdx.x == 0) carry_s = 0;
   __syncthreads();
@@ -75,7 +82,7 @@ __global__ __launch_bounds__(1024) void k_scan(int B, int T, int M, int K, int n
   const int64_t NR = (int64_t)B * T * K;
   for (int s = threadIdx.x; s <= last_seg; s += 1024) {
     int64_t off;
-    if (s < M * B) off = cnt[(int64_t)s * ntile];
+    if (s < M * B) off = cnt[(int64_t)s * nsub];
     else if (s < (M + 1) * B) off = NR + (int64_t)(s - M * B) * T;
     else off = NR + (int64_t)B * T;
     seg_off[s] = (int32_t)off;
@@ -110,8 +117,11 @@ __device__ void block_exclusive_scan(const int32_t* __restrict__ cnt, int n, int
   __syncthreads();
 }
 
+// base: the counts cnt[m][b][sub] (scanned in LDS when FUSED), else their
+// exclusive scan; the tile's rows of memory m start at the scan's entry of its
+// first 64 positions.
 template <typename XT, bool FUSED>
-__global__ __launch_bounds__(kTile) void k_scatter(int B, int T, int D, int H, int M, int K, int ntile, int last_seg,
+__global__ __launch_bounds__(kTile) void k_scatter(int B, int T, int D, int H, int M, int K, int nsub, int last_seg,
                                                    bool shared_rows,
                                                    const int32_t* __restrict__ idx, const int32_t* __restrict__ base,
                                                    int32_t* __restrict__ seg_off,
@@ -126,11 +136,11 @@ __global__ __launch_bounds__(kTile) void k_scatter(int B, int T, int D, int H, i
   const int tile = blockIdx.x, b = blockIdx.y;
   const int64_t NR = (int64_t)B * T * K;
   if (FUSED) {
-    block_exclusive_scan(base, M * B * ntile, cs, wsum);
+    block_exclusive_scan(base, M * B * nsub, cs, wsum);
     if (tile == 0 && b == 0)
       for (int sg = threadIdx.x; sg <= last_seg; sg += kTile) {
         int64_t off;
-        if (sg < M * B) off = cs[(int64_t)sg * ntile];
+        if (sg < M * B) off = cs[(int64_t)sg * nsub];
         else if (sg < (M + 1) * B) off = NR + (int64_t)(sg - M * B) * T;
         else off = NR + (int64_t)B * T;
         seg_off[sg] = (int32_t)off;
@@ -167,7 +177,7 @@ __global__ __launch_bounds__(kTile) void k_scatter(int B, int T, int D, int H, i
         const int m = mem[j];
         int r = rank[j];
         for (int w2 = 0; w2 < wv; ++w2) r += wave_tot[m][w2];
-        const int64_t bi = ((int64_t)m * B + b) * ntile + tile;
+        const int64_t bi = ((int64_t)m * B + b) * nsub + (int64_t)tile * kSubPerTile;
         const int32_t row = (FUSED ? cs[bi] : base[bi]) + r;
         perm[row] = (int32_t)tok;
         inv[tok * K + j] = row;
@@ -226,6 +236,15 @@ __global__ __launch_bounds__(256) void k_dispatch_shared(int B, int T, int H, in
 }  // namespace mom
 
 namespace mom {
+// The dispatch's counts alone (cnt[m][b][sub], every entry written), for
+// mom_route_count on shapes its fused kernel does not take.
+mom_status dispatch_count_only(const mom_dims* dims, const int32_t* idx, int32_t* cnt, hipStream_t st) {
+  const mom_dims& d = *dims;
+  const int ntile = ceil_div(d.T, kTile), nsub = ceil_div(d.T, kSub);
+  hipLaunchKernelGGL(k_count, dim3(ntile, d.B), dim3(kTile), 0, st, d.B, d.T, d.M, d.topk, nsub, idx, cnt);
+  return launch_status();
+}
+
 // Argument checks of the dispatch entry points other than the workspace
 // (part as in mom_dispatch_part).
 static mom_status dispatch_check(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
@@ -245,7 +264,7 @@ static mom_status dispatch_check(const mom_dims* dims, const int32_t* idx, const
   MOM_CHECK_PTR(inv);
   MOM_CHECK_OPT_PTR(x_packed);
   if (x_packed) MOM_CHECK_PTR(x);
-  if ((int64_t)ceil_div(dims->T, kTile) * dims->B > 0x7fffffff / 2) return MOM_ERR_DIMS;
+  if ((int64_t)ceil_div(dims->T, kSub) * dims->B * dims->M > 0x7fffffff / 2) return MOM_ERR_DIMS;
   return MOM_OK;
 }
 
@@ -267,19 +286,19 @@ static mom_status dispatch(const mom_dims* dims, const int32_t* idx, const void*
   const size_t need = mom_workspace_bytes(dims, MOM_WS_DISPATCH);
   if (!ws || ws_bytes < need) return MOM_ERR_WORKSPACE;
   MOM_CHECK_PTR(ws);
-  const int ntile = ceil_div(d.T, kTile);
+  const int ntile = ceil_div(d.T, kTile), nsub = ceil_div(d.T, kSub);
   // part 2 leaves the shared rows and the shared segments' offsets (past M B) to part 1
   const int last_seg = part == 2 ? d.M * d.B : (d.M + 1) * d.B;
   const bool shared_rows = part == 0;
   int32_t* cnt = (int32_t*)ws;
   if (!counted)
-    hipLaunchKernelGGL(k_count, dim3(ntile, d.B), dim3(kTile), 0, st, d.B, d.T, d.M, d.topk, ntile, idx, cnt);
-  const bool fused = (int64_t)d.M * d.B * ntile <= kFuseScan;
+    hipLaunchKernelGGL(k_count, dim3(ntile, d.B), dim3(kTile), 0, st, d.B, d.T, d.M, d.topk, nsub, idx, cnt);
+  const bool fused = (int64_t)d.M * d.B * nsub <= kFuseScan;
   if (!fused)
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, d.B, d.T, d.M, d.topk, ntile, last_seg, cnt, seg_off);
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, d.B, d.T, d.M, d.topk, nsub, last_seg, cnt, seg_off);
 #define MOM_SCATTER(XT, F)                                                                                         \
   hipLaunchKernelGGL((k_scatter<XT, F>), dim3(ntile, d.B), dim3(kTile), 0, st, d.B, d.T, d.D, d.H, d.M, d.topk,    \
-                     ntile, last_seg, shared_rows, idx, cnt, seg_off, alpha, beta, perm, inv, alpha_p, beta_p,     \
+                     nsub, last_seg, shared_rows, idx, cnt, seg_off, alpha, beta, perm, inv, alpha_p, beta_p,     \
                      (const XT*)x, (XT*)x_packed)
   if (d.dtype == MOM_DTYPE_BF16) {
     if (fused) MOM_SCATTER(bf16_t, true);
@@ -305,8 +324,16 @@ extern "C" mom_status mom_dispatch_counted(const mom_dims* dims, const int32_t* 
                                            const float* alpha, const float* beta, int32_t* seg_off, int32_t* perm,
                                            int32_t* inv, void* x_packed, float* alpha_p, float* beta_p, void* ws,
                                            size_t ws_bytes, void* stream) {
-  if (dims && dims->T != 1) return MOM_ERR_UNSUPPORTED;
   return mom::dispatch(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_p, beta_p, ws, ws_bytes, 0,
+                       stream, true);
+}
+
+extern "C" mom_status mom_dispatch_counted_part(const mom_dims* dims, const int32_t* idx, const void* x,
+                                                const float* alpha, const float* beta, int32_t* seg_off,
+                                                int32_t* perm, int32_t* inv, void* x_packed, float* alpha_p,
+                                                float* beta_p, void* ws, size_t ws_bytes, int32_t part,
+                                                void* stream) {
+  return mom::dispatch(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_p, beta_p, ws, ws_bytes, part,
                        stream, true);
 }
 
@@ -319,7 +346,7 @@ extern "C" mom_status mom_dispatch_part(const mom_dims* dims, const int32_t* idx
 }
 
 // ------------------------------------------------------------------ allocation-free dispatch
-// mom_dispatch_noalloc keeps the dispatch's counts (int32 [M][B][ceil(T/256)],
+// mom_dispatch_noalloc keeps the dispatch's counts (int32 [M][B][ceil(T/64)],
 // written in full by k_count before k_scan or k_scatter read them, so nothing
 // needs clearing) in this array instead of a caller workspace.  In host code
 // `scratch` only names the symbol: its device address is looked up once per

@@ -27,14 +27,14 @@
 //
 // Launches:
 //   k_gdn_prep         T, P, decays and X (half) per (chunk, head)
-//   k_gdn_chain mode 1 the state entering every chunk, transposed half S^T
+//   k_gdn_chain16 mode 1  the state entering every chunk, transposed half S^T
 //   k_gdn_chain_bwd    reverse walk over each segment's chunks with dS in
 //                      matrix-core accumulators; stores dS' of every chunk
 //                      (transposed half) and dL/d(entering state)
 //   k_gdn_grad         one block per (chunk, head): everything else
 // A training step can skip the first two: gdn_chunk_fwd_train runs the forward
 // pass with the prep that also writes X and a walk that also stores the
-// states (k_gdn_chain mode 2), into this workspace, and gdn_chunk_bwd_saved
+// states (k_gdn_chain16 mode 2), into this workspace, and gdn_chunk_bwd_saved
 // then starts at the reverse walk.
 #include "chunk_mfma.h"
 

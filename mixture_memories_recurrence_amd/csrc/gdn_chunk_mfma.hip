@@ -20,324 +20,28 @@
 //                (16x16 diagonal blocks by forward substitution, off-diagonal
 //                blocks by block products), all in float32.  It stores T and P
 //                as half and gamma, gamma_L / gamma as float32.
-//   k_gdn_chain16  the forward walk: one block per (segment, head, 128 value
+//   k_gdn_chain16  the walk: one block per (segment, head, 128 value
 //                columns; 64 when dv = 64) of eight (four) waves with 16 columns
 //                each, walking the segment's chunks in order with the state in
-//                float32 matrix-core accumulators (see the comment at the kernel).
-//   k_gdn_chain  the same walk with 32-column waves, and the modes that store
-//                each chunk's entering state for the gradients.
+//                float32 matrix-core accumulators (see the comment at the
+//                kernel), and the modes that store each chunk's entering state
+//                for the gradients.
 #include "chunk_mfma.h"
 
 namespace mom {
 
-// ------------------------------------------------------------------ chain
-// One block per (segment, head, DVB = 32 NW value columns), NW waves.  Value
-// columns of the state evolve independently, so wave w owns columns
-// [32w, 32w + 32) of its block for every key row: its part of S stays in the
-// float32 accumulators of v_mfma_f32_32x32x16_f16 for the whole segment.
-// Per chunk (rows i, j; K, V, Q, T, P and gamma from LDS):
-//   Y   = K S                           (depends on the entering state)
-//   U   = T V - T diag(gamma) Y         (= T V - W S with W = T diag(gamma) K)
-//   O^T = S^T Q^T diag(gamma) + U^T P^T
-//   S  <- gamma_L S + K^T diag(gamma_L / gamma) U
-// Every product reads its state-side operand from registers: accumulator rows
-// 8q + 4g + t (lane group g = lane / 32) become the 16-deep operand of the next
-// product after a v_permlane32_swap between lanes l and l + 32.  Nothing is
-// exchanged between waves, so the only block barrier per chunk publishes the
-// next chunk's inputs, which every wave prefetches into the idle half of a
-// double buffer with asynchronous global -> LDS copies.
-// MODE 0 is the forward pass.  For the gradients, MODE 1 only walks the
-// states: it stores the state entering every chunk (transposed, half:
-// hws[chunk][head][dv][DK]) and skips the read-out (no Q, P or O; state_out may
-// then be null); MODE 2 does both, the forward pass of a training step that
-// keeps the states for the backward pass.
-template <int DK, int NW>
-struct ChainLds {
-  static constexpr int DVB = 32 * NW;
-  static constexpr int OFF_K = 0, OFF_Q = GC * DK, OFF_V = 2 * GC * DK, OFF_T = OFF_V + GC * DVB,
-                       OFF_P = OFF_T + GC * GC, OFF_E = OFF_P + GC * GC, OFF_TOK = OFF_E + 2 * 2 * GC;
-  static constexpr int BUF = OFF_TOK + 2 * GC;  // halfs per buffer (E: 2 x 64 float32, TOK: 64 int32)
-  // after the two buffers: one 32 x 32 float32 output tile per wave
-  static constexpr size_t OST = (size_t)2 * BUF * sizeof(f16_t);
-  static constexpr size_t BYTES = OST + (size_t)NW * 32 * 32 * sizeof(float);
-};
-
-template <int DK, int NW, bool DELTA, int MODE>
-__global__ __launch_bounds__(64 * NW) void k_gdn_chain(
-    int H, int dv, int n_seg, const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_state,
-    const f16_t* __restrict__ k, const f16_t* __restrict__ v,
-    const f16_t* __restrict__ Tws, const f16_t* __restrict__ Pws, const float* __restrict__ Ews,
-    const int32_t* __restrict__ row_token, const f16_t* __restrict__ q, const float* __restrict__ state_in,
-    float* __restrict__ state_out, float* __restrict__ o, f16_t* __restrict__ hws) {
-  using LY = ChainLds<DK, NW>;
-  constexpr int DVB = LY::DVB, ND = DK / 32, NKD = DK / 16;
-  constexpr bool SAVE = MODE == 1;            // states only
-  constexpr bool STORE_H = MODE != 0;         // the chunk-entry states are stored
-  extern __shared__ __attribute__((aligned(16))) f16_t smem[];
-
-  // Blocks of a (segment, head) group are dealt round-robin over the 8 XCDs
-  // (block p runs on XCD p % 8), longest segments (highest s) first.
-  const int nb = dv / DVB;
-  const int64_t pblk = blockIdx.x;
-  const int64_t n_grp = (int64_t)n_seg * H;
-  const int64_t full = (n_grp / 8) * 8;
-  int64_t grp;
-  int cb;
-  if (pblk < full * nb) {
-    const int64_t xi = pblk & 7, ii = pblk >> 3;
-    grp = (ii / nb) * 8 + xi;
-    cb = (int)(ii % nb);
-  } else {
-    const int64_t r = pblk - full * nb;
-    grp = full + r / nb;
-    cb = (int)(r % nb);
-  }
-  const int h = (int)(grp % H);
-  const int s = n_seg - 1 - (int)(grp / H);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c32 = lane & 31, g2 = lane >> 5;
-  const int slot = seg_state ? seg_state[s] : s;
-  const int ncol0 = cb * DVB + 32 * w;
-  const int64_t sbase = ((int64_t)slot * H + h) * DK * dv + ncol0;
-  const int64_t rbeg = seg_off[s], rend = seg_off[s + 1];
-  const int cbase = chunks_before(seg_off, s, lane);
-
-  // Inputs of the chunk at row r0n into buffer b, as NPF copy instructions
-  // per wave (pf_issue(i), i = 0 .. NPF - 1) that can be spread over the
-  // previous chunk's products.  Rows past the segment end repeat its last row;
-  // T is zero in those rows and columns, so they contribute nothing to the
-  // state, and their outputs are not stored.  Query rows are gathered by token
-  // (row_token; the packed row itself when it is null).  The tokens of a
-  // chunk's rows travel one chunk ahead, in the TOK area of the previous
-  // chunk's buffer, so that no copy waits for an index load (without
-  // row_token the area holds the row numbers).
-  using CK = TileCopy<DK, NW>;
-  using CV = TileCopy<DVB, NW>;
-  using CT = TileCopy<GC, NW>;
-  constexpr int NPF = 2 * CK::PER_WAVE + CV::PER_WAVE + 2 * CT::PER_WAVE + 2;
-  int64_t pf_r0 = 0, pf_chk = 0;
-  int pf_L = 0;
-  f16_t* pf_B = smem;
-  int qtok[CK::PER_WAVE];  // token of this lane's row in each query copy
-  // tok_lds: the tokens of the chunk's rows in LDS, or null to read them here
-  auto pf_setup = [&](int64_t r0n, int b, const int32_t* tok_lds) {
-    pf_r0 = r0n;
-    pf_L = (int)min((int64_t)GC, rend - r0n);
-    pf_chk = (int64_t)(cbase + (r0n - rbeg) / GC) * H + h;
-    pf_B = smem + b * LY::BUF;
-#pragma unroll
-    for (int j = 0; j < CK::PER_WAVE; ++j) {
-      const int r = min(CK::row(w, lane, j), pf_L - 1);
-      if (tok_lds) qtok[j] = tok_lds[r];
-      else qtok[j] = row_token ? row_token[r0n + r] : (int)(r0n + r);
-    }
-  };
-  auto pf_issue = [&](int i) {
-    if (i < CK::PER_WAVE) {
-      CK::issue(pf_B + LY::OFF_K, w, lane, i, [&](int r, int c) {
-        return k + ((pf_r0 + min(r, pf_L - 1)) * H + h) * DK + 8 * c;
-      });
-    } else if ((i -= CK::PER_WAVE) < CK::PER_WAVE) {
-      if (SAVE) return;  // no read-out: Q is not needed
-      const int64_t t = qtok[i];
-      CK::issue(pf_B + LY::OFF_Q, w, lane, i, [&](int r, int c) { return q + (t * H + h) * DK + 8 * c; });
-    } else if ((i -= CK::PER_WAVE) < CV::PER_WAVE) {
-      CV::issue(pf_B + LY::OFF_V, w, lane, i, [&](int r, int c) {
-        return v + ((pf_r0 + min(r, pf_L - 1)) * H + h) * dv + cb * DVB + 8 * c;
-      });
-    } else if ((i -= CV::PER_WAVE) < CT::PER_WAVE) {
-      CT::issue(pf_B + LY::OFF_T, w, lane, i, [&](int r, int c) { return Tws + (pf_chk * GC + r) * GC + 8 * c; });
-    } else if ((i -= CT::PER_WAVE) < CT::PER_WAVE) {
-      if (SAVE) return;
-      CT::issue(pf_B + LY::OFF_P, w, lane, i, [&](int r, int c) { return Pws + (pf_chk * GC + r) * GC + 8 * c; });
-    } else if (i == CT::PER_WAVE) {
-      if (w < 2) dma_b32(Ews + pf_chk * 2 * GC + GC * w + lane, pf_B + LY::OFF_E + 2 * GC * w);
-    } else if (w == NW - 1) {  // tokens of the following chunk's rows
-      const int64_t rn = min(pf_r0 + GC + lane, rend - 1);
-      if (row_token) dma_b32(row_token + rn, pf_B + LY::OFF_TOK);
-      else reinterpret_cast<int32_t*>(pf_B + LY::OFF_TOK)[lane] = (int32_t)rn;
-    }
-  };
-  // copies issued per step of the Y / O loop, the rest during the U loop
-  constexpr int PY = NPF / NKD, PU = (NPF - PY * NKD + GC / 16 - 1) / (GC / 16);
-
-  f16x16 S[ND];
-  if (state_in) {
-#pragma unroll
-    for (int a = 0; a < ND; ++a)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int d = 32 * a + 8 * (i / 4) + 4 * g2 + (i % 4);
-        S[a][i] = state_in[sbase + (int64_t)d * dv + c32];
-      }
-  } else {
-#pragma unroll
-    for (int a = 0; a < ND; ++a)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) S[a][i] = 0.f;
-  }
-  const float ones[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-  float* ost = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + LY::OST) + 32 * 32 * w;
-  if (rbeg < rend) {
-    pf_setup(rbeg, 0, nullptr);
-#pragma unroll
-    for (int i = 0; i < NPF; ++i) pf_issue(i);
-  }
-
-  int buf = 0;
-  for (int64_t r0 = rbeg; r0 < rend; r0 += GC, buf ^= 1) {
-    const int L = (int)min((int64_t)GC, rend - r0);
-    // This wave's part of the chunk's inputs has landed.  Vector memory
-    // operations complete in issue order; the only ones issued after the
-    // prefetch are the previous chunk's 8 output stores, which need not wait.
-    if (r0 == rbeg || SAVE) vm_wait_all();
-    else vm_wait_8();
-    lds_barrier();  // every wave's part has landed; every wave is done with the other buffer
-    pf_setup(r0 + GC < rend ? r0 + GC : r0, buf ^ 1,
-             reinterpret_cast<const int32_t*>(smem + buf * LY::BUF + LY::OFF_TOK));
-
-    const f16_t* Bc = smem + buf * LY::BUF;
-    const f16_t* Ks = Bc + LY::OFF_K;
-    const f16_t* Qs = Bc + LY::OFF_Q;
-    const f16_t* Vs = Bc + LY::OFF_V;
-    const f16_t* Ts = Bc + LY::OFF_T;
-    const f16_t* Ps = Bc + LY::OFF_P;
-    const float* Eg = reinterpret_cast<const float*>(Bc + LY::OFF_E);  // gamma_i, then gamma_L / gamma_i
-    if constexpr (STORE_H)  // the entering state, transposed, through the wave's output tile
-      store_state_t<DK>(hws + ((int64_t)(cbase + (r0 - rbeg) / GC) * H + h) * dv * DK + (int64_t)ncol0 * DK, S,
-                        reinterpret_cast<f16_t*>(ost), lane);
-
-    // ---- Y = K S and O^T = S^T Q^T, two 32-row tiles each (four chains); the
-    // state becomes an operand (k = key rows) one 16-row block at a time
-    f16x16 Y[2], O[2];
-#pragma unroll
-    for (int bt = 0; bt < 2; ++bt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        Y[bt][i] = 0.f;
-        O[bt][i] = 0.f;
-      }
-#pragma unroll
-    for (int kb = 0; kb < NKD; ++kb) {
-#pragma unroll
-      for (int i = PY * kb; i < PY * (kb + 1); ++i) pf_issue(i);
-      const h8v sb = acc_to_b(S[kb / 2], kb % 2, ones);
-#pragma unroll
-      for (int bt = 0; bt < 2; ++bt) {
-        Y[bt] = mfma32(row_frag<DK>(Ks, 32 * bt + c32, kb, g2), sb, Y[bt]);
-        if (!SAVE) O[bt] = mfma32(sb, row_frag<DK>(Qs, 32 * bt + c32, kb, g2), O[bt]);
-      }
-    }
-    CHAIN_PHASE();
-    // ---- U = T V - T diag(gamma) Y
-    f16x16 U[2];
-#pragma unroll
-    for (int bt = 0; bt < 2; ++bt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) U[bt][i] = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < GC / 16; ++kb) {
-#pragma unroll
-      for (int i = PY * NKD + PU * kb; i < PY * NKD + PU * (kb + 1); ++i)
-        if (i < NPF) pf_issue(i);
-      const h8v vb = col_frag<DVB>(Vs, kb, 32 * w, lane);
-#pragma unroll
-      for (int bt = 0; bt < 2; ++bt) U[bt] = mfma32(row_frag<GC>(Ts, 32 * bt + c32, kb, g2), vb, U[bt]);
-    }
-#pragma unroll
-    for (int bt = 0; bt < 2; ++bt)
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        if (!DELTA) continue;  // gated linear attention: U = T V (T = diag(c)); Y is then unused
-        float sc[8];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          sc[t] = -Eg[32 * bt + 16 * p + 4 * g2 + t];
-          sc[4 + t] = -Eg[32 * bt + 16 * p + 8 + 4 * g2 + t];
-        }
-        const h8v yb = acc_to_b(Y[bt], p, sc);
-#pragma unroll
-        for (int bi = 0; bi < 2; ++bi) U[bi] = mfma32(row_frag<GC>(Ts, 32 * bi + c32, 2 * bt + p, g2), yb, U[bi]);
-      }
-    CHAIN_PHASE();
-    // ---- U and diag(gamma_L / gamma) U as operands (k = chunk rows)
-    h8v ub[GC / 16], u2b[GC / 16];
-#pragma unroll
-    for (int bt = 0; bt < 2; ++bt)
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        float sc[8];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          sc[t] = Eg[GC + 32 * bt + 16 * p + 4 * g2 + t];
-          sc[4 + t] = Eg[GC + 32 * bt + 16 * p + 8 + 4 * g2 + t];
-        }
-        ub[2 * bt + p] = acc_to_b(U[bt], p, ones);
-        u2b[2 * bt + p] = acc_to_b(U[bt], p, sc);
-      }
-    if constexpr (!SAVE) {
-      // ---- O^T += U^T P^T, after S^T Q^T is scaled to S^T Q'^T (column i by gamma_i)
-#pragma unroll
-      for (int bt = 0; bt < 2; ++bt) {
-        const float gm = Eg[32 * bt + c32];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) O[bt][i] *= gm;
-      }
-#pragma unroll
-      for (int kb = 0; kb < GC / 16; ++kb)
-#pragma unroll
-        for (int bt = 0; bt < 2; ++bt) O[bt] = mfma32(ub[kb], row_frag<GC>(Ps, 32 * bt + c32, kb, g2), O[bt]);
-      // O out through this wave's LDS tile, so that each store writes 8 whole
-      // 128-byte rows (lane l: row 8 j + l / 8, columns 4 (l % 8) .. + 3) rather
-      // than 32-byte pieces of 32 rows.  Piece c of tile row r sits at position
-      // c ^ (r & 7).  8 stores (all lanes active unless this is the last chunk).
-#pragma unroll
-      for (int bt = 0; bt < 2; ++bt) {
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-          *reinterpret_cast<float4*>(ost + 32 * c32 + 4 * ((2 * qq + g2) ^ (c32 & 7))) =
-              make_float4(O[bt][4 * qq], O[bt][4 * qq + 1], O[bt][4 * qq + 2], O[bt][4 * qq + 3]);
-        wave_lds_fence();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int rr = 8 * j + (lane >> 3), pc = lane & 7;
-          const float4 val = *reinterpret_cast<const float4*>(ost + 32 * rr + 4 * (pc ^ (rr & 7)));
-          if (32 * bt + rr < L) *reinterpret_cast<float4*>(o + ((r0 + 32 * bt + rr) * H + h) * dv + ncol0 + 4 * pc) = val;
-        }
-        wave_lds_fence();  // the tile is read before the next half overwrites it
-      }
-    }
-    // ---- S <- gamma_L S + K^T U', U' = diag(gamma_L / gamma) U
-    const float eL = Eg[GC - 1];
-#pragma unroll
-    for (int a = 0; a < ND; ++a)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) S[a][i] *= eL;
-#pragma unroll
-    for (int kb = 0; kb < GC / 16; ++kb)
-#pragma unroll
-      for (int a = 0; a < ND; ++a) S[a] = mfma32(col_frag<DK>(Ks, kb, 32 * a, lane), u2b[kb], S[a]);
-  }
-  vm_wait_all();  // the last (repeated) prefetch has landed before the block ends
-  if (SAVE && !state_out) return;
-#pragma unroll
-  for (int a = 0; a < ND; ++a)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int d = 32 * a + 8 * (i / 4) + 4 * g2 + (i % 4);
-      state_out[sbase + (int64_t)d * dv + c32] = S[a][i];
-    }
-}
-
 // ------------------------------------------------------------------ chain, 16-column waves
-// The forward walk with NW waves of 16 value columns each (DVB = 16 NW columns
-// per block: 128 with eight waves, 64 with four), on v_mfma_f32_16x16x32_f16.
-// A wave's accumulators are a quarter of the 32-column wave's above, so the
-// kernel fits two waves per SIMD, and each SIMD switches to the other wave
-// while one waits on LDS reads or on its products.  The per-chunk algebra and
-// the inputs (K, Q, V, T, P, gamma in a double-buffered LDS image filled by
-// asynchronous copies, one block barrier per chunk) are those of k_gdn_chain:
+// The walk with NW waves of 16 value columns each (DVB = 16 NW columns per
+// block: 128 with eight waves, 64 with four), on v_mfma_f32_16x16x32_f16.
+// Value columns of the state evolve independently, so a wave's part of S
+// stays in its float32 accumulators for the whole segment; the kernel fits
+// two waves per SIMD, and each SIMD switches to the other wave while one
+// waits on LDS reads or on its products.  A block's inputs per chunk (K, Q,
+// V, T, P, gamma) sit in a double-buffered LDS image that every wave fills in
+// part with asynchronous global -> LDS copies of the next chunk while the
+// current one is processed (rows past the segment end repeat its last row; T
+// is zero in those rows and columns), with one block barrier per chunk.  Per
+// chunk:
 //   Y   = K S                         (4 row tiles, dk-deep)
 //   O^T = S^T Q^T                     (4 row tiles of the chunk, dk-deep)
 //   U   = T V - T diag(gamma) Y       (chunk-deep)
@@ -358,14 +62,23 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain(
 // width of dk columns), giving the group's affine state map; groups that end
 // their segment are skipped (grp_seg[g + 1] != grp_seg[g]).  The state is
 // stored with row width sw at column col_base + the block's columns.
-template <int DK, int NW, bool DELTA, bool MAP>
+//
+// MODE 0 is the forward pass.  For the gradients, MODE 1 only walks the
+// states: it stores the state entering every chunk (transposed, half:
+// hws[chunk][head][dv][DK], lane 16 G + c writing rows 4G .. 4G+3 of each
+// 16-row block of its column) and skips the read-out (no Q, P or O; state_out
+// may then be null); MODE 2 does both, the forward pass of a training step,
+// whose o and states equal MODE 0's bit for bit.
+template <int DK, int NW, bool DELTA, bool MAP, int MODE = 0>
 __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
     int H, int dv, int width, int col_base, int sw, int ident, int n_seg, const int32_t* __restrict__ seg_off,
     const int32_t* __restrict__ seg_state, const int32_t* __restrict__ grp_seg,
     const f16_t* __restrict__ k, const f16_t* __restrict__ v, const f16_t* __restrict__ Tws,
     const f16_t* __restrict__ Pws, const float* __restrict__ Ews, const int32_t* __restrict__ row_token,
     const f16_t* __restrict__ q, const float* __restrict__ state_in, float* __restrict__ state_out,
-    float* __restrict__ o) {
+    float* __restrict__ o, f16_t* __restrict__ hws) {
+  static_assert(!MAP || MODE == 0, "the scan's map walk is a forward walk");
+  constexpr bool READ = !MAP && MODE != 1;  // the read-out (Q, P, O)
   constexpr int DVB = 16 * NW, ND = DK / 16, NKD = DK / 32;
   constexpr int OFF_K = 0, OFF_Q = GC * DK, OFF_V = 2 * GC * DK, OFF_T = OFF_V + GC * DVB, OFF_P = OFF_T + GC * GC,
                 OFF_E = OFF_P + GC * GC, OFF_TOK = OFF_E + 2 * 2 * GC, BUF = OFF_TOK + 2 * GC;
@@ -461,7 +174,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
       const unsigned e = (unsigned)(min(k_row[i], pf_L - 1) * H * DK + k_pc[i]);
       dma_b128_at(pf_k + e, lds_at(OFF_K, CK::RPI, DK, i));
     } else if ((i -= CK::PER_WAVE) < CK::PER_WAVE) {
-      if (MAP) return;  // no read-out: Q is not needed
+      if (!READ) return;  // no read-out: Q is not needed
       dma_b128_at(q + ((int64_t)qtok[i] * H + h) * DK + k_pc[i], lds_at(OFF_Q, CK::RPI, DK, i));
     } else if ((i -= CK::PER_WAVE) < CV::PER_WAVE) {
       if (zero_v) return;
@@ -470,7 +183,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
     } else if ((i -= CV::PER_WAVE) < CT::PER_WAVE) {
       dma_b128_at(pf_t + t_off[i], lds_at(OFF_T, CT::RPI, GC, i));
     } else if ((i -= CT::PER_WAVE) < CT::PER_WAVE) {
-      if (MAP) return;
+      if (!READ) return;
       dma_b128_at(pf_p + t_off[i], lds_at(OFF_P, CT::RPI, GC, i));
     } else if (i == CT::PER_WAVE) {
       if (w < 2) dma_b32_at(Ews + pf_chk * 2 * GC + GC * w + lane, pf_lds + (unsigned)((OFF_E + 2 * GC * w) * 2));
@@ -503,7 +216,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
     const int L = (int)min((int64_t)GC, rend - r0);
     // this wave's copies have landed (only the previous chunk's 4 output
     // stores were issued after them); then every wave's
-    if (r0 == rbeg || MAP) vm_wait_all();
+    if (r0 == rbeg || !READ) vm_wait_all();
     else vm_wait_4();
     lds_barrier();
     pf_setup(r0 + GC < rend ? r0 + GC : r0, buf ^ 1, reinterpret_cast<const int32_t*>(smem + buf * BUF + OFF_TOK));
@@ -515,6 +228,14 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
     const f16_t* Ts = Bc + OFF_T;
     const f16_t* Ps = Bc + OFF_P;
     const float* Eg = reinterpret_cast<const float*>(Bc + OFF_E);  // gamma_i, then gamma_L / gamma_i
+    if constexpr (MODE != 0) {  // the entering state, transposed, as half
+      f16_t* hc = hws + ((int64_t)(cbase + (r0 - rbeg) / GC) * H + h) * sw * DK + (int64_t)(ncol0 + c16) * DK + 4 * G;
+#pragma unroll
+      for (int a = 0; a < ND; ++a) {
+        const half4 hv = {(f16_t)S[a][0], (f16_t)S[a][1], (f16_t)S[a][2], (f16_t)S[a][3]};
+        *reinterpret_cast<half4*>(hc + 16 * a) = hv;
+      }
+    }
 
     // ---- Y = K S and O^T = S^T Q^T; the state's 32-row blocks as operands
     f4v Y[4], O[4];
@@ -530,7 +251,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       kf[0][t] = row_frag16<DK>(Ks, 16 * t + c16, 0, G);
-      if (!MAP) qf[0][t] = row_frag16<DK>(Qs, 16 * t + c16, 0, G);
+      if (READ) qf[0][t] = row_frag16<DK>(Qs, 16 * t + c16, 0, G);
     }
 #pragma unroll
     for (int kb = 0; kb < NKD; ++kb) {
@@ -538,7 +259,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           kf[(kb + 1) & 1][t] = row_frag16<DK>(Ks, 16 * t + c16, kb + 1, G);
-          if (!MAP) qf[(kb + 1) & 1][t] = row_frag16<DK>(Qs, 16 * t + c16, kb + 1, G);
+          if (READ) qf[(kb + 1) & 1][t] = row_frag16<DK>(Qs, 16 * t + c16, kb + 1, G);
         }
       }
 #pragma unroll
@@ -548,7 +269,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         Y[t] = mfma16(kf[kb & 1][t], sop, Y[t]);
-        if (!MAP) O[t] = mfma16(sop, qf[kb & 1][t], O[t]);
+        if (READ) O[t] = mfma16(sop, qf[kb & 1][t], O[t]);
       }
     }
     CHAIN_PHASE();
@@ -595,7 +316,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
     }
     // ---- O^T = O^T diag(gamma) + U^T P^T, stored as 16-byte row pieces
 #pragma unroll
-    for (int t = 0; t < (MAP ? 0 : 4); ++t) {
+    for (int t = 0; t < (READ ? 4 : 0); ++t) {
       const float gm = Eg[16 * t + c16];
 #pragma unroll
       for (int e = 0; e < 4; ++e) O[t][e] *= gm;
@@ -603,7 +324,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
       for (int kb = 0; kb < GC / 32; ++kb) O[t] = mfma16(ub[kb], row_frag16<GC>(Ps, 16 * t + c16, kb, G), O[t]);
     }
 #pragma unroll
-    for (int t = 0; t < (MAP ? 0 : 4); ++t)
+    for (int t = 0; t < (READ ? 4 : 0); ++t)
       if (16 * t + c16 < L)
         *reinterpret_cast<float4*>(o + ((r0 + 16 * t + c16) * H + h) * dv + ncol0 + 4 * G) =
             make_float4(O[t][0], O[t][1], O[t][2], O[t][3]);
@@ -620,6 +341,7 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
       for (int a = 0; a < ND; ++a) S[a] = mfma16(col_frag16<DK>(Ks, kb, 16 * a, lane), u2b[kb], S[a]);
   }
   vm_wait_all();  // the last (repeated) prefetch has landed before the block ends
+  if (MODE == 1 && !state_out) return;
 #pragma unroll
   for (int a = 0; a < ND; ++a)
 #pragma unroll
@@ -1041,47 +763,27 @@ __global__ __launch_bounds__(256) void k_scan_final(int H, int dk, int dv, const
   for (int e = threadIdx.x; e < dk * dv / 4; e += 256) dst[e] = src[e];
 }
 
-template <int DK, int NW, bool DELTA, int MODE>
-static mom_status launch_chain(const mom_dims& d, int n_seg, const int32_t* seg_off, const int32_t* seg_state,
-                               const ChunkWs& W, const int32_t* row_token, const void* q, const void* k,
-                               const void* v, const float* state_in, float* state_out, float* o, f16_t* hws,
-                               hipStream_t st) {
-  using LY = ChainLds<DK, NW>;
-  static bool attr = false;  // the dynamic LDS limit is raised once per kernel
-  if (!attr) {
-    if (hipFuncSetAttribute((const void*)k_gdn_chain<DK, NW, DELTA, MODE>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)LY::BYTES) != hipSuccess)
-      return MOM_ERR_LAUNCH;
-    attr = true;
-  }
-  const int64_t blocks = (int64_t)n_seg * d.H * (d.dv / LY::DVB);
-  if (blocks > 0)
-    hipLaunchKernelGGL((k_gdn_chain<DK, NW, DELTA, MODE>), dim3((unsigned)blocks), dim3(64 * NW), LY::BYTES, st,
-                       d.H, d.dv, n_seg, seg_off, seg_state, (const f16_t*)k, (const f16_t*)v, W.T, W.P, W.E,
-                       row_token, (const f16_t*)q, state_in, state_out, o, hws);
-  return MOM_OK;
-}
-
 // The walk over n_seg segments (or, with MAP, groups): width columns of the
 // state from col_base, state rows sw wide (width = sw = dv for the forward).
-template <int DK, int NW, bool DELTA, bool MAP>
+template <int DK, int NW, bool DELTA, bool MAP, int MODE = 0>
 static mom_status launch_chain16(const mom_dims& d, int n_seg, const int32_t* seg_off, const int32_t* seg_state,
                                  const ChunkWs& W, const int32_t* row_token, const void* q, const void* k,
                                  const void* v, const float* state_in, float* state_out, float* o, hipStream_t st,
-                                 int width, int col_base, int sw, int ident, const int32_t* grp_seg) {
+                                 int width, int col_base, int sw, int ident, const int32_t* grp_seg,
+                                 f16_t* hws = nullptr) {
   constexpr size_t lds = chain16_lds_bytes<DK, NW>();
   static bool attr = false;  // the dynamic LDS limit is raised once per kernel
   if (!attr) {
-    if (hipFuncSetAttribute((const void*)k_gdn_chain16<DK, NW, DELTA, MAP>,
+    if (hipFuncSetAttribute((const void*)k_gdn_chain16<DK, NW, DELTA, MAP, MODE>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return MOM_ERR_LAUNCH;
     attr = true;
   }
   const int64_t blocks = (int64_t)n_seg * d.H * (width / (16 * NW));
   if (blocks > 0)
-    hipLaunchKernelGGL((k_gdn_chain16<DK, NW, DELTA, MAP>), dim3((unsigned)blocks), dim3(64 * NW), lds, st, d.H,
-                       d.dv, width, col_base, sw, ident, n_seg, seg_off, seg_state, grp_seg, (const f16_t*)k,
-                       (const f16_t*)v, W.T, W.P, W.E, row_token, (const f16_t*)q, state_in, state_out, o);
+    hipLaunchKernelGGL((k_gdn_chain16<DK, NW, DELTA, MAP, MODE>), dim3((unsigned)blocks), dim3(64 * NW), lds, st,
+                       d.H, d.dv, width, col_base, sw, ident, n_seg, seg_off, seg_state, grp_seg, (const f16_t*)k,
+                       (const f16_t*)v, W.T, W.P, W.E, row_token, (const f16_t*)q, state_in, state_out, o, hws);
   return MOM_OK;
 }
 
@@ -1183,10 +885,11 @@ static mom_status launch_states(const mom_dims& d, int n_seg, int n_rows, const 
                        seg_off, row_token, (const f16_t*)q, (const f16_t*)k, alpha_p, beta_p, W.T, W.P, W.E,
                        DELTA ? Xws : nullptr);
   const mom_status r =
-      d.dv % 128 == 0 ? launch_chain<DK, 4, DELTA, MODE>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in,
-                                                         state_out, o, hws, st)
-                      : launch_chain<DK, 2, DELTA, MODE>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in,
-                                                         state_out, o, hws, st);
+      d.dv % 128 == 0
+          ? launch_chain16<DK, 8, DELTA, false, MODE>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in,
+                                                      state_out, o, st, d.dv, 0, d.dv, 0, nullptr, hws)
+          : launch_chain16<DK, 4, DELTA, false, MODE>(d, n_seg, seg_off, seg_state, W, row_token, q, k, v, state_in,
+                                                      state_out, o, st, d.dv, 0, d.dv, 0, nullptr, hws);
   return r != MOM_OK ? r : launch_status();
 }
 

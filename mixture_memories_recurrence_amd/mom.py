@@ -55,6 +55,8 @@ def lib():
         "mom_project": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
         "mom_project_part": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP],
         "mom_dispatch_part": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _I32, _VP],
+        "mom_dispatch_counted_part": [D, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
+                                      _I32, _VP],
         "gdn_chunk_fwd": [D, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                           _VP, ctypes.c_size_t, _VP],
         "gla_chunk_fwd": [D, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -91,7 +93,7 @@ def lib():
 
 
 EXPORTS = ("mom_route", "mom_route_count", "mom_dispatch", "mom_dispatch_noalloc", "mom_dispatch_counted",
-           "mom_dispatch_part",
+           "mom_dispatch_part", "mom_dispatch_counted_part",
            "mom_project", "mom_project_part", "gdn_chunk_fwd", "gla_chunk_fwd", "gdn_chunk_bwd", "gla_chunk_bwd",
            "gdn_chunk_fwd_train", "gla_chunk_fwd_train", "gdn_chunk_bwd_saved", "gla_chunk_bwd_saved",
            "gdn_decode_step", "gla_decode_step", "gdn_decode_step_combined", "gla_decode_step_combined",
@@ -129,8 +131,8 @@ def mom_route(dims, x, w_r, bias, idx, w, stream=None):
 
 
 def mom_route_count(dims, x, w_r, bias, idx, w, ws, stream=None):
-    """mom_route for one position per sequence, also writing the dispatch's
-    counts into ws for mom_dispatch_counted."""
+    """mom_route, also writing the dispatch's counts into ws for
+    mom_dispatch_counted / mom_dispatch_counted_part."""
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().mom_route_count(ctypes.byref(dims), _p(x), _p(w_r), _p(bias), _p(idx), _p(w), _p(ws), nbytes,
                                  _s(stream)), "mom_route_count")
@@ -169,6 +171,15 @@ def mom_dispatch_part(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, a
     _check(lib().mom_dispatch_part(ctypes.byref(dims), _p(idx), _p(x), _p(alpha), _p(beta), _p(seg_off), _p(perm),
                                    _p(inv), _p(x_packed), _p(alpha_p), _p(beta_p), _p(ws), nbytes, part, _s(stream)),
            "mom_dispatch_part")
+
+
+def mom_dispatch_counted_part(dims, idx, x, alpha, beta, seg_off, perm, inv, x_packed, alpha_p, beta_p, ws, part,
+                              stream=None):
+    """mom_dispatch_part reading the counts mom_route_count left in ws."""
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().mom_dispatch_counted_part(ctypes.byref(dims), _p(idx), _p(x), _p(alpha), _p(beta), _p(seg_off),
+                                           _p(perm), _p(inv), _p(x_packed), _p(alpha_p), _p(beta_p), _p(ws), nbytes,
+                                           part, _s(stream)), "mom_dispatch_counted_part")
 
 
 def mom_project_part(dims, x, perm, seg_off, w_q, w_k, w_v, q, k, v, part, stream=None):
@@ -361,9 +372,9 @@ class MomLayer:
 
     def route_dispatch_project(self, x, alpha, beta, b, stream=None):
         c, d = self.cfg, b["dims"]
-        mom_route(d, x, self.w_r, self.bias, b["idx"], b["w"], stream)
-        mom_dispatch(d, b["idx"], x, alpha, beta, b["seg_off"], b["perm"], b["inv"], None, b["alpha_p"],
-                     b["beta_p"], b["ws"], stream)
+        mom_route_count(d, x, self.w_r, self.bias, b["idx"], b["w"], b["ws"], stream)
+        mom_dispatch_counted(d, b["idx"], x, alpha, beta, b["seg_off"], b["perm"], b["inv"], None, b["alpha_p"],
+                             b["beta_p"], b["ws"], stream)
         mom_project(d, x, b["perm"], b["seg_off"], self.w_q, self.w_k, self.w_v, b["q"], b["k"], b["v"], stream)
 
     def forward(self, x, alpha, beta, state_in=None, state_out=None, B=None, T=None, stream=None, overlap=True,
@@ -425,9 +436,9 @@ class MomLayer:
         chunk(d, B, N, NT, n_state, b["seg_off_s"], b["seg_state_s"], b["perm"], b["q"], b["k"], b["v"], b["alpha_p"],
               b["beta_p"], state_in, state_out, b["o"], ws_s, s)
         ev[2].record(side)  # shared memory done
-        mom_route(d, x, self.w_r, self.bias, b["idx"], b["w"])
-        mom_dispatch_part(d, b["idx"], x, alpha, beta, b["seg_off"], b["perm"], b["inv"], None, b["alpha_p"],
-                          b["beta_p"], b["ws"], PART_ROUTED)
+        mom_route_count(d, x, self.w_r, self.bias, b["idx"], b["w"], b["ws"])
+        mom_dispatch_counted_part(d, b["idx"], x, alpha, beta, b["seg_off"], b["perm"], b["inv"], None,
+                                  b["alpha_p"], b["beta_p"], b["ws"], PART_ROUTED)
         # the routed projection starts when the shared one is done, so that the
         # shared recurrence (a few long chains) runs beside it, not behind it
         main.wait_event(ev[1])

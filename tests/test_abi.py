@@ -108,8 +108,8 @@ def test_dispatch_workspace_is_checked():
     L = mom.lib()
     d = _dims()
     need = L.mom_workspace_bytes(ctypes.byref(d), 0)
-    ntile = -(-d.T // 256)
-    assert need >= d.M * d.B * ntile * 4 and need % 256 == 0
+    nsub = -(-d.T // 64)  # counts of every 64 positions
+    assert need >= d.M * d.B * nsub * 4 and need % 256 == 0
     args = [FAKE] * 10
     assert L.mom_dispatch(ctypes.byref(d), *args, None, need, None) == -5
     assert L.mom_dispatch(ctypes.byref(d), *args, FAKE, need - 1, None) == -5
@@ -156,16 +156,21 @@ def test_decode_combined_checks():
 
 @needs_lib
 def test_route_count_checks():
-    """The one-launch route and histogram serve one position per sequence only,
-    and need the dispatch workspace."""
+    """The one-pass route and histogram needs the dispatch workspace (for one
+    position per sequence and for whole sequences), and the counted dispatch
+    validates like mom_dispatch / mom_dispatch_part, all before any launch."""
     L = mom.lib()
-    d = _dims(T=1)
-    need = L.mom_workspace_bytes(ctypes.byref(d), 0)
-    assert L.mom_route_count(ctypes.byref(_dims(T=2)), FAKE, FAKE, None, FAKE, FAKE, FAKE, need, None) == -3
-    assert L.mom_route_count(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, need - 1, None) == -5
-    assert L.mom_route_count(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, None, 0, None) == -5
-    assert L.mom_dispatch_counted(ctypes.byref(_dims(T=2)), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
-                                  FAKE, FAKE, need, None) == -3
+    for d in (_dims(T=1), _dims()):
+        need = L.mom_workspace_bytes(ctypes.byref(d), 0)
+        assert L.mom_route_count(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, need - 1, None) == -5
+        assert L.mom_route_count(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, None, 0, None) == -5
+        assert L.mom_route_count(ctypes.byref(d), None, FAKE, None, FAKE, FAKE, FAKE, need, None) == -1
+        args = [FAKE] * 10
+        assert L.mom_dispatch_counted(ctypes.byref(d), *args, None, need, None) == -5
+        assert L.mom_dispatch_counted(ctypes.byref(d), *args, FAKE, need - 1, None) == -5
+        assert L.mom_dispatch_counted_part(ctypes.byref(d), *args, FAKE, need, 3, None) == -2
+        assert L.mom_dispatch_counted_part(ctypes.byref(d), *args, None, need, 2, None) == -5
+    assert L.mom_route_count(ctypes.byref(_dims(topk=0)), FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 20, None) == -2
 
 
 @needs_lib
@@ -212,7 +217,7 @@ def test_chunk_bwd_checks():
 @needs_lib
 def test_dispatch_noalloc_checks_before_any_launch():
     """The allocation-free dispatch validates like mom_dispatch and rejects
-    sizes past its fixed scratch (M*B*ceil(T/256) <= 65536 counts) with
+    sizes past its fixed scratch (M*B*ceil(T/64) <= 65536 counts) with
     MOM_ERR_TOO_LARGE, all before any HIP call (so without a GPU)."""
     L = mom.lib()
     f = lambda d, *p: L.mom_dispatch_noalloc(ctypes.byref(d), *p, None)
@@ -222,12 +227,12 @@ def test_dispatch_noalloc_checks_before_any_launch():
     assert f(_dims(), FAKE, None, FAKE, *ok[3:]) == -1      # beta
     assert f(_dims(), FAKE, FAKE, FAKE, FAKE, ODD, *ok[5:]) == -4   # seg_off misaligned
     assert f(_dims(topk=0), *ok) == -2
-    # 16 memories x 64 sequences x 65 tiles = 66560 counts > 65536
-    big = _dims(M=16, topk=4, B=64, T=65 * 256)
+    # 16 memories x 64 sequences x 65 counts of 64 positions = 66560 counts > 65536
+    big = _dims(M=16, topk=4, B=64, T=65 * 64)
     assert f(big, *ok) == -7
     assert L.mom_status_string(-7).decode().startswith("sizes exceed")
     # exactly at the limit passes the size check (then needs a GPU, not called here)
-    assert 16 * 64 * 64 == 65536
+    assert L.mom_workspace_bytes(ctypes.byref(_dims(M=16, topk=4, B=64, T=64 * 64)), 0) == 65536 * 4
 
 
 @needs_lib

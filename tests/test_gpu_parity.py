@@ -91,6 +91,90 @@ def test_route_ties_four_memories(D):
         np.testing.assert_allclose(b["w"].cpu().numpy(), w_ref, rtol=0, atol=2e-7)
 
 
+def sub_counts(idx, B, T, M):
+    """Per-(memory, sequence, 64 positions) counts of the selections."""
+    K = idx.shape[1]
+    nsub = -(-T // 64)
+    c = np.zeros((M, B, nsub), np.int32)
+    for b_ in range(B):
+        for t in range(T):
+            for j in range(K):
+                c[idx[b_ * T + t, j], b_, t // 64] += 1
+    return c
+
+
+def route_count_and_check(cfg, inp, layer, g, b):
+    """mom_route_count on the layer's buffers: idx and w against the checker,
+    the dispatch counts against a count of the checker's selections."""
+    M = cfg.M
+    ws = b["ws"].view(torch.int32)
+    ws.fill_(-9)
+    mom.mom_route_count(b["dims"], g["x"], layer.w_r, layer.bias, b["idx"], b["w"], b["ws"])
+    torch.cuda.synchronize()
+    idx_ref, w_ref = oracle.route(inp["x"], inp["w_r"], inp["bias"], cfg.K)
+    np.testing.assert_array_equal(b["idx"].cpu().numpy(), idx_ref)
+    np.testing.assert_allclose(b["w"].cpu().numpy(), w_ref, rtol=0, atol=2e-7)
+    ref = sub_counts(idx_ref, cfg.B, cfg.T, M)
+    np.testing.assert_array_equal(ws[:ref.size].cpu().numpy().reshape(ref.shape), ref)
+    return idx_ref
+
+
+@pytest.mark.parametrize("name", list(CFG))
+def test_route_count_full_size(name):
+    """Route and histogram in one pass over whole sequences: the selections and
+    weights equal the checker's, the counts of every 64 positions equal a count
+    of those selections, and the counted dispatch (whole, and in its two
+    parts) gives the plain dispatch's outputs bit for bit."""
+    cfg = CFG[name]
+    log("route_count", name)
+    inp = synth.make_layer_inputs(cfg, seed=0)
+    layer = make_layer(cfg, inp)
+    g = gpu_inputs(cfg, inp)
+    b = layer.buffers(cfg.B, cfg.T)
+    route_count_and_check(cfg, inp, layer, g, b)
+    d = b["dims"]
+    counted = b["ws"].clone()
+    outs = []
+    for mode in ("plain", "counted", "parts"):
+        for t in (b["seg_off"], b["perm"], b["inv"]):
+            t.fill_(-1)
+        for t in (b["alpha_p"], b["beta_p"]):
+            t.fill_(float("nan"))
+        ws = counted.clone()
+        if mode == "plain":
+            mom.mom_dispatch(d, b["idx"], g["x"], g["alpha"], g["beta"], b["seg_off"], b["perm"], b["inv"], None,
+                             b["alpha_p"], b["beta_p"], ws)
+        elif mode == "counted":
+            mom.mom_dispatch_counted(d, b["idx"], g["x"], g["alpha"], g["beta"], b["seg_off"], b["perm"], b["inv"],
+                                     None, b["alpha_p"], b["beta_p"], ws)
+        else:
+            mom.mom_dispatch_counted_part(d, None, g["x"], g["alpha"], g["beta"], b["seg_off"], b["perm"], None,
+                                          None, b["alpha_p"], b["beta_p"], None, mom.PART_SHARED)
+            mom.mom_dispatch_counted_part(d, b["idx"], g["x"], g["alpha"], g["beta"], b["seg_off"], b["perm"],
+                                          b["inv"], None, b["alpha_p"], b["beta_p"], ws, mom.PART_ROUTED)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (b["seg_off"], b["perm"], b["inv"], b["alpha_p"], b["beta_p"])])
+    for o in outs[1:]:
+        for u, v in zip(outs[0], o):
+            assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("D,M,K,T", [(1024, 6, 3, 300), (2048, 4, 4, 130), (1024, 16, 4, 65), (512, 4, 2, 200)])
+def test_route_count_ragged_and_ties(D, M, K, T):
+    """The one-pass route and histogram on ragged lengths (the last 64
+    positions of each sequence partial), with duplicated router rows (ties go
+    to the lower index), k = M, and a shape outside the one-launch kernel
+    (D = 512: the router, then the counting kernel)."""
+    cfg = small(CFG["l380m"], 3, T, D=D, M=M, K=K)
+    inp = synth.make_layer_inputs(cfg, seed=21)
+    inp["w_r"][M - 1] = inp["w_r"][0]
+    for c in (cfg, dataclasses.replace(cfg, K=min(M, 8))):
+        log("route_count ragged", D, M, c.K, T)
+        layer = mom.MomLayer(c, inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"])
+        b = layer.buffers(c.B, c.T)
+        route_count_and_check(c, inp, layer, gpu_inputs(c, inp), b)
+
+
 # ------------------------------------------------------------------ dispatch
 @pytest.mark.parametrize("name", list(CFG))
 def test_dispatch_full_size(name):
