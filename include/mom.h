@@ -173,10 +173,10 @@ mom_status mom_dispatch_noalloc(const mom_dims* dims, const int32_t* idx, const 
  * [M][B][ceil(T / 64)], every entry written, nothing to clear) in ws (at
  * least mom_workspace_bytes(dims, MOM_WS_DISPATCH) bytes), which
  * mom_dispatch_counted and mom_dispatch_counted_part then read instead of
- * counting again.  One launch for bfloat16 rows with D = 1024 and M <= 16 or
- * D = 2048 and M <= 4, and for T == 1 (a decode step); other shapes run the
- * router and then the dispatch's counting kernel.  idx and w are those of
- * mom_route (the selections and weights of the same exact logits). */
+ * counting again.  One launch for bfloat16 rows with D = 1024 and M <= 4, and
+ * for T == 1 (a decode step); other shapes run mom_route's kernel and then the
+ * dispatch's counting kernel.  idx and w are those of mom_route (the
+ * selections and weights of the same exact logits). */
 mom_status mom_route_count(const mom_dims* dims, const void* x, const void* w_r, const float* bias,
                            int32_t* idx, float* w, void* ws, size_t ws_bytes, void* stream);
 

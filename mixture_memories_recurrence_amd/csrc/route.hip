@@ -268,118 +268,90 @@ __global__ __launch_bounds__(256) void k_route_wave4(int64_t NT, int D, int M, i
   }
 }
 
-// Route and dispatch counts for whole sequences (bfloat16 rows, D = 512 NJ,
-// M <= 4 MG): one block of four waves per 64 positions of one sequence, 16
-// positions per wave in groups of TPW, the next group's rows loaded while
-// the current group is reduced.  The products, the per-lane sums (lane l
-// holds elements 8 l + 512 j + i) and the cross-lane tree are those of
-// k_route_wave4, four memories at a time; the router rows sit in LDS, and
-// each lane's slice of a row, read once per group of positions, serves all
-// TPW positions.  Each wave counts its positions' selections per memory with
-// ballots; the block adds its four waves' counts and writes the dispatch's
+// Route and dispatch counts for whole sequences, bfloat16 rows, D = 1024 and
+// at most four memories: k_route_wave4's arithmetic (the router slice held in
+// registers, four positions at a time, the same products, sums and tree), in
+// blocks of eight waves per 64 positions of one sequence, each wave taking
+// two groups of four positions with the second group's rows loaded while the
+// first is reduced.  Each wave counts its positions' selections per memory
+// with ballots; the block adds its waves' counts and writes the dispatch's
 // count of its 64 positions, cnt[m][b][sub] (nsub = ceil(T / 64)), so the
 // dispatch needs no counting launch and nothing is cleared first.
-template <int NJ, int MG, int TPW>
-__global__ __launch_bounds__(256) void k_route_sub(int B, int T, int D, int M, int K, int nsub,
-                                                   const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr,
-                                                   const float* __restrict__ bias, int32_t* __restrict__ idx,
-                                                   float* __restrict__ w, int32_t* __restrict__ cnt) {
+__global__ __launch_bounds__(512) void k_route_sub4(int B, int T, int D, int M, int K, int nsub,
+                                                    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr,
+                                                    const float* __restrict__ bias, int32_t* __restrict__ idx,
+                                                    float* __restrict__ w, int32_t* __restrict__ cnt) {
   using P = ExactProd<bf16_t>;
-  constexpr int NG = 16 / TPW;  // groups of positions per wave
-  constexpr int MP = 4 * MG;    // router rows held (rows past M repeat row M - 1)
-  __shared__ __attribute__((aligned(16))) bf16_t wl[MP * 512 * NJ];
-  __shared__ int32_t wave_cnt[4][64];
+  constexpr int EPL = 16, NL = EPL / 8, TPW = 4;
+  __shared__ int32_t wave_cnt[8][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int sub = blockIdx.x, b = blockIdx.y;
-  const int p0 = sub * 64 + wv * 16;  // first position of this wave
+  const int p0 = sub * 64 + wv * 8;  // first position of this wave
   const int64_t tok0 = (int64_t)b * T;
-  typename P::Raw xr[2][TPW][NJ];
-  auto load = [&](int gi, int bufi) {
+  typename P::Raw xr[2][TPW][NL];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       int p = p0 + gi * TPW + i;
       p = p < T ? p : T - 1;  // past the end: a valid row, never written
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) xr[bufi][i][j] = P::raw(x + (tok0 + p) * D + 8 * lane + 512 * j);
+      for (int j = 0; j < NL; ++j) xr[gi][i][j] = P::raw(x + (tok0 + p) * D + 8 * lane + 512 * j);
     }
-  };
-  load(0, 0);
-  for (int e = threadIdx.x; e < MP * 64 * NJ; e += 256) {  // 16-byte pieces of the router rows
-    const int m = e / (64 * NJ), c = e % (64 * NJ);
-    *reinterpret_cast<uint4*>(wl + m * 512 * NJ + 8 * c) =
-        *reinterpret_cast<const uint4*>(wr + (int64_t)(m < M ? m : M - 1) * D + 8 * c);
+  float wf[4][EPL];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const bf16_t* row = wr + (int64_t)(m < M ? m : M - 1) * D + 8 * lane;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) P::unpack(P::raw(row + 512 * j), &wf[m][8 * j]);
   }
-  __syncthreads();
   int my_cnt = 0;  // lane m: this wave's selections of memory m
-  auto group = [&](int gi, const typename P::Raw (&xb)[TPW][NJ]) {
-    // the router reads are the same for every group: an opaque offset keeps
-    // the compiler from hoisting them (and their conversions) out of the loop,
-    // which would hold the whole slice in registers
-    int wofs = 8 * lane;
-    asm volatile("" : "+v"(wofs));
-    double mine[MP];  // logits of position p0 + gi TPW + lane (lanes < TPW)
 #pragma unroll
-    for (int m = 0; m < MP; ++m) mine[m] = 0.0;
+  for (int gi = 0; gi < 2; ++gi) {
+    double mine[4] = {0.0, 0.0, 0.0, 0.0};  // logits of position p0 + 4 gi + lane (lanes < 4)
 #pragma unroll
-    for (int g = 0; g < MG; ++g) {
-      double acc[TPW][4];
+    for (int i = 0; i < TPW; ++i) {
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int i = 0; i < TPW; ++i)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc[i][m] = 0.0;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        float xv[TPW][8], wf[4][8];
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) P::unpack(xb[i][j], xv[i]);
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          P::unpack(*reinterpret_cast<const uint4*>(wl + (4 * g + m) * 512 * NJ + 512 * j + wofs), wf[m]);
+      for (int j = 0; j < NL; ++j) {
+        float xv[8];
+        P::unpack(xr[gi][i][j], xv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          double xd[TPW];
+          const double xd = (double)xv[e];
 #pragma unroll
-          for (int i = 0; i < TPW; ++i) xd[i] = (double)xv[i][e];
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const double wd = (double)wf[m][e];
-#pragma unroll
-            for (int i = 0; i < TPW; ++i) acc[i][m] = ::fma(xd[i], wd, acc[i][m]);
-          }
+          for (int m = 0; m < 4; ++m) acc[m] = ::fma(xd, (double)wf[m][8 * j + e], acc[m]);
         }
       }
+      swap_halves(acc[0], acc[2]);
+      swap_halves(acc[1], acc[3]);
+      double k0 = acc[0] + acc[2], k1 = acc[1] + acc[3];
+      swap_rows(k0, k1);
+      double v = k0 + k1;
+      v += row_shr<1>(v);
+      v += row_shr<2>(v);
+      v += row_shr<4>(v);
+      v += row_shr<8>(v);
 #pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        swap_halves(acc[i][0], acc[i][2]);
-        swap_halves(acc[i][1], acc[i][3]);
-        double k0 = acc[i][0] + acc[i][2], k1 = acc[i][1] + acc[i][3];
-        swap_rows(k0, k1);
-        double v = k0 + k1;
-        v += row_shr<1>(v);
-        v += row_shr<2>(v);
-        v += row_shr<4>(v);
-        v += row_shr<8>(v);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const double lm = read_lane(v, 16 * m + 15);
-          if (lane == i) mine[4 * g + m] = lm;
-        }
+      for (int m = 0; m < 4; ++m) {
+        const double lm = read_lane(v, 16 * m + 15);
+        if (lane == i) mine[m] = lm;
       }
     }
     const int p = p0 + gi * TPW + lane;
     uint32_t taken = 0;
     if (lane < TPW && p < T) {
       const int64_t t = tok0 + p;
-      double logit[MP];
+      double logit[4];
 #pragma unroll
-      for (int m = 0; m < MP; ++m) logit[m] = mine[m] + (bias && m < M ? (double)bias[m] : 0.0);
-      double ls[8];
-      int sel[8];
+      for (int m = 0; m < 4; ++m) logit[m] = mine[m] + (bias && m < M ? (double)bias[m] : 0.0);
+      int sel[4];
+      double ls[4];
       for (int j = 0; j < K; ++j) {
         int best = -1;
         double bl = 0.0;
 #pragma unroll
-        for (int m = 0; m < MP; ++m) {
+        for (int m = 0; m < 4; ++m) {
           if (m < M && !((taken >> m) & 1u) && (best < 0 || logit[m] > bl)) {
             best = m;
             bl = logit[m];
@@ -389,7 +361,7 @@ __global__ __launch_bounds__(256) void k_route_sub(int B, int T, int D, int M, i
         sel[j] = best;
         ls[j] = bl;
       }
-      double z = 0.0, e[8];
+      double z = 0.0, e[4];
       for (int j = 0; j < K; ++j) {
         e[j] = exp(ls[j] - ls[0]);
         z += e[j];
@@ -403,18 +375,15 @@ __global__ __launch_bounds__(256) void k_route_sub(int B, int T, int D, int M, i
       const int n = __popcll(__ballot((taken >> m) & 1u));
       if (lane == m) my_cnt += n;
     }
-  };
-  for (int gi = 0; gi < NG; gi += 2) {  // the two halves of xr in turn
-    load(gi + 1, 1);
-    group(gi, xr[0]);
-    if (gi + 2 < NG) load(gi + 2, 0);
-    group(gi + 1, xr[1]);
   }
   wave_cnt[wv][lane] = my_cnt;
   __syncthreads();
-  if (threadIdx.x < M)
-    cnt[((int64_t)threadIdx.x * B + b) * nsub + sub] =
-        wave_cnt[0][threadIdx.x] + wave_cnt[1][threadIdx.x] + wave_cnt[2][threadIdx.x] + wave_cnt[3][threadIdx.x];
+  if (threadIdx.x < M) {
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c += wave_cnt[u][threadIdx.x];
+    cnt[((int64_t)threadIdx.x * B + b) * nsub + sub] = c;
+  }
 }
 
 template <typename XT, int G>
@@ -479,20 +448,9 @@ extern "C" mom_status mom_route_count(const mom_dims* dims, const void* x, const
     int32_t* cnt = (int32_t*)ws;
     const int nsub = (d.T + kCountTile - 1) / kCountTile;
     const dim3 grid((unsigned)nsub, (unsigned)d.B);
-    if (d.dtype == MOM_DTYPE_BF16 && ((d.D == 1024 && d.M <= 16) || (d.D == 2048 && d.M <= 4))) {
-      const bf16_t* xp = (const bf16_t*)x;
-      const bf16_t* wp = (const bf16_t*)w_r;
-#define MOM_ROUTE_SUB(NJ, MG, TPW)                                                                              \
-  hipLaunchKernelGGL((k_route_sub<NJ, MG, TPW>), grid, dim3(256), 0, st, d.B, d.T, d.D, d.M, d.topk, nsub, xp, wp, \
-                     bias, idx, w, cnt)
-      if (d.D == 1024) {
-        if (d.M <= 4) MOM_ROUTE_SUB(2, 1, 4);
-        else if (d.M <= 8) MOM_ROUTE_SUB(2, 2, 4);
-        else MOM_ROUTE_SUB(2, 4, 2);
-      } else {
-        MOM_ROUTE_SUB(4, 1, 2);
-      }
-#undef MOM_ROUTE_SUB
+    if (d.dtype == MOM_DTYPE_BF16 && d.D == 1024 && d.M <= 4) {
+      hipLaunchKernelGGL(k_route_sub4, grid, dim3(512), 0, st, d.B, d.T, d.D, d.M, d.topk, nsub, (const bf16_t*)x,
+                         (const bf16_t*)w_r, bias, idx, w, cnt);
       return launch_status();
     }
     // other shapes: the router, then the dispatch's own counting kernel

@@ -321,6 +321,23 @@ def act_dtype(cfg):
     return torch.float16 if cfg.dtype == "bf16" else torch.float32
 
 
+_AUX_STREAMS = {}
+
+
+def _aux_streams(device):
+    """The two extra streams every layer on this device shares, drawn once per
+    process.  torch hands out its pooled streams round-robin, and the pool's
+    streams share the GPU's few hardware queues (four by default) round-robin
+    too, so every fourth stream drawn shares a queue with the default stream:
+    a new pair per layer would, after a few layers, put a layer's second
+    stream behind the first and run its two halves one after the other."""
+    d = torch.device(device)
+    key = d.index if d.index is not None else torch.cuda.current_device()
+    if key not in _AUX_STREAMS:
+        _AUX_STREAMS[key] = (torch.cuda.Stream(device=key), torch.cuda.Stream(device=key))
+    return _AUX_STREAMS[key]
+
+
 class MomLayer:
     """One MoM layer on the GPU: weights resident, intermediates allocated once
     per (B, T).  forward() and decode_step() only enqueue library calls."""
@@ -453,17 +470,16 @@ class MomLayer:
         return b["out"], state_out, b
 
     def _side_stream(self):
-        """The second stream (default priority) and its events."""
-        if getattr(self, "_side", None) is None:
-            self._side = torch.cuda.Stream(device=self.device)
+        """The second stream (default priority, one per device for the whole
+        process) and this layer's events."""
+        if getattr(self, "_ev", None) is None:
             self._ev = [torch.cuda.Event() for _ in range(7)]
-        return self._side, self._ev
+        return _aux_streams(self.device)[0], self._ev
 
     def _third_stream(self):
-        """A third stream (default priority), for the router's gradients."""
-        if getattr(self, "_side2", None) is None:
-            self._side2 = torch.cuda.Stream(device=self.device)
-        return self._side2
+        """A third stream (default priority, one per device for the whole
+        process), for the router's gradients."""
+        return _aux_streams(self.device)[1]
 
     def _grad_bufs(self, b, split=False):
         """Gradient buffers of shape b; ws serves the recompute backward, the

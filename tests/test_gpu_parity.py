@@ -159,12 +159,13 @@ def test_route_count_full_size(name):
             assert torch.equal(u, v)
 
 
-@pytest.mark.parametrize("D,M,K,T", [(1024, 6, 3, 300), (2048, 4, 4, 130), (1024, 16, 4, 65), (512, 4, 2, 200)])
+@pytest.mark.parametrize("D,M,K,T", [(1024, 4, 2, 300), (1024, 3, 3, 130), (1024, 6, 3, 300), (2048, 4, 4, 130),
+                                     (1024, 16, 4, 65)])
 def test_route_count_ragged_and_ties(D, M, K, T):
-    """The one-pass route and histogram on ragged lengths (the last 64
-    positions of each sequence partial), with duplicated router rows (ties go
-    to the lower index), k = M, and a shape outside the one-launch kernel
-    (D = 512: the router, then the counting kernel)."""
+    """The route and histogram on ragged lengths (the last 64 positions of each
+    sequence partial), with duplicated router rows (ties go to the lower
+    index) and k = M, in one launch (D = 1024, M <= 4) and on the shapes that
+    run the router and then the counting kernel."""
     cfg = small(CFG["l380m"], 3, T, D=D, M=M, K=K)
     inp = synth.make_layer_inputs(cfg, seed=21)
     inp["w_r"][M - 1] = inp["w_r"][0]
