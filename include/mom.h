@@ -153,8 +153,8 @@ mom_status mom_dispatch(const mom_dims* dims, const int32_t* idx, const void* x,
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  The same outputs as mom_dispatch (bit for bit);
  * every other argument, layout and error as there.  The dispatch's counts
- * (int32 [M][B][ceil(T / 64)], M*B*ceil(T / 64) <= 65536) live in a fixed
- * 256 KiB array of the library's own in each GPU's memory, held from the
+ * (int32 [M][B][ceil(T / 64)], M*B*ceil(T / 64) <= 32768) and their scan live
+ * in a fixed 256 KiB array of the library's own in each GPU's memory, held from the
  * first call on that GPU until the process ends; larger sizes return
  * MOM_ERR_TOO_LARGE before any launch.  The call allocates nothing.  The
  * array's device address is looked up on the first call on each GPU, so
@@ -173,15 +173,16 @@ mom_status mom_dispatch_noalloc(const mom_dims* dims, const int32_t* idx, const 
  * [M][B][ceil(T / 64)], every entry written, nothing to clear) in ws (at
  * least mom_workspace_bytes(dims, MOM_WS_DISPATCH) bytes), which
  * mom_dispatch_counted and mom_dispatch_counted_part then read instead of
- * counting again.  One launch for bfloat16 rows with D = 1024 and M <= 4, and
- * for T == 1 (a decode step); other shapes run mom_route's kernel and then the
- * dispatch's counting kernel.  idx and w are those of mom_route (the
+ * counting again.  One launch for bfloat16 rows with D = 1024 and M <= 16 or
+ * D = 2048 and M <= 4, and for T == 1 (a decode step); other shapes run
+ * mom_route's kernel and then the dispatch's counting kernel.  idx and w are those of mom_route (the
  * selections and weights of the same exact logits). */
 mom_status mom_route_count(const mom_dims* dims, const void* x, const void* w_r, const float* bias,
                            int32_t* idx, float* w, void* ws, size_t ws_bytes, void* stream);
 
 /* mom_dispatch when ws holds the counts mom_route_count wrote for the same idx
- * and dims: the same outputs, without the counting launch. */
+ * and dims: the same outputs, without the counting launch.  The counts are
+ * left as they are, so the call can be repeated on them. */
 mom_status mom_dispatch_counted(const mom_dims* dims, const int32_t* idx, const void* x, const float* alpha,
                                 const float* beta, int32_t* seg_off, int32_t* perm, int32_t* inv,
                                 void* x_packed, float* alpha_p, float* beta_p, void* ws, size_t ws_bytes,

@@ -85,7 +85,7 @@ extern "C" size_t mom_workspace_bytes(const mom_dims* dims, int32_t which) {
   const mom_dims& d = *dims;
   if (which == MOM_WS_DISPATCH) {
     const int64_t nsub = (d.T + kCountTile - 1) / kCountTile;
-    const int64_t bytes = (int64_t)d.M * d.B * nsub * 4;
+    const int64_t bytes = (dispatch_offs_at(d) + (int64_t)d.M * d.B * nsub) * 4;  // counts, then their scan
     return (size_t)((bytes + 255) / 256 * 256);
   }
   if (which == MOM_WS_CHUNK) {

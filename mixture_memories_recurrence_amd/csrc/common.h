@@ -19,8 +19,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
-constexpr int kDispatchTile = 256;  // positions per dispatch tile (one scatter block)
-constexpr int kCountTile = 64;      // positions per dispatch count (one wave)
+constexpr int kDispatchTile = 64;  // positions per dispatch tile (one scatter block of one wave)
+constexpr int kCountTile = 64;     // positions per dispatch count (one wave)
 
 // ---------------------------------------------------------------- conversions
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
@@ -97,6 +97,13 @@ inline mom_status launch_status() {
 }
 
 inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// The dispatch's workspace: the counts (int32 [M][B][ceil(T / 64)]), then,
+// from this offset in int32 entries, their exclusive scan.
+inline int64_t dispatch_offs_at(const mom_dims& d) {
+  const int64_t n = (int64_t)d.M * d.B * ((d.T + kCountTile - 1) / kCountTile);
+  return (n + 63) / 64 * 64;
+}
 
 // dispatch.hip: the dispatch's per-64-position counts of idx into cnt
 mom_status dispatch_count_only(const mom_dims* dims, const int32_t* idx, int32_t* cnt, hipStream_t st);

@@ -3,22 +3,24 @@
 // (memory, sequence) (podcast.do-not-panic.com page, "Solving scatter-gather
 // without new kernels").
 //
-// A stable counting sort, all integer work:
-//   k_count   one block per (tile of 256 positions, sequence), one wave per
-//             64 positions: per-memory counts of each 64 positions from wave
-//             ballots, written to cnt[m][b][sub] (sub = position / 64; no
-//             atomics, every entry written).  mom_route_count writes the same
-//             counts from the router's pass, which saves this launch;
+// A stable counting sort, all integer work, in tiles of 64 positions of one
+// sequence (one wave each):
+//   k_count   per-memory counts of each tile from wave ballots, written to
+//             cnt[m][b][sub] (sub = position / 64; no atomics, every entry
+//             written).  mom_route_count writes the same counts from the
+//             router's pass, which saves this launch;
 //   k_scan    one block: exclusive scan of cnt in (m, b, sub) order, which is
-//             exactly the packed row order; writes seg_off.  When cnt is small
-//             (at most kFuseScan entries) every k_scatter block scans it in
-//             LDS itself instead, which saves this launch;
+//             exactly the packed row order, into a second area of the
+//             workspace (the counts stay as they are, so a counted dispatch
+//             can run again on them); writes seg_off.  When cnt is small (at
+//             most kFuseScan entries) every k_scatter block scans it in LDS
+//             itself instead, which saves this launch;
 //   k_scatter one block per tile again: a token's rank among the tile's tokens
 //             routed to the same memory comes from wavefront ballots (popcount
-//             of the lower lanes) plus the totals of the waves before it, so
-//             the order inside a segment is increasing position.  The block
-//             then writes perm/inv, gathers the gates of the routed memory and,
-//             if asked, the x rows.
+//             of the lower lanes; with tiles of several waves, plus the totals
+//             of the waves before it), so the order inside a segment is
+//             increasing position.  The block then writes perm/inv, gathers
+//             the gates of the routed memory and, if asked, the x rows.
 #include <algorithm>
 #include <mutex>
 
@@ -30,7 +32,7 @@ constexpr int kTile = kDispatchTile;
 constexpr int kSub = kCountTile;
 constexpr int kSubPerTile = kTile / kSub;
 static_assert(kSub == kWave && kTile % kSub == 0, "one wave per count");
-constexpr int kFuseScan = 8192;  // largest cnt scanned inside k_scatter
+constexpr int kFuseScan = 1024;  // largest cnt scanned inside every k_scatter block
 
 __global__ __launch_bounds__(kTile) void k_count(int B, int T, int M, int K, int nsub,
                                                  const int32_t* __restrict__ idx, int32_t* __restrict__ cnt) {
@@ -53,7 +55,8 @@ __global__ __launch_bounds__(kTile) void k_count(int B, int T, int M, int K, int
 
 // Exclusive scan of n counts in place (single block of 1024 threads).
 __global__ __launch_bounds__(1024) void k_scan(int B, int T, int M, int K, int nsub, int last_seg,
-                                               int32_t* __restrict__ cnt, int32_t* __restrict__ seg_off) {
+                                               const int32_t* __restrict__ cnt, int32_t* __restrict__ offs,
+                                               int32_t* __restrict__ seg_off) {
   __shared__ int32_t wsum[16];
   __shared__ int32_t carry_s;
   const int n = M * B * nsub;
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(1024) void k_scan(int B, int T, int M, int K, int n
     __syncthreads();
     int32_t pre = carry_s;
     for (int w2 = 0; w2 < wv; ++w2) pre += wsum[w2];
-    if (i < n) cnt[i] = pre + s - v;
+    if (i < n) offs[i] = pre + s - v;
     __syncthreads();
     if (threadIdx.x == 1023) carry_s = pre + s;
     __syncthreads();
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(1024) void k_scan(int B, int T, int M, int K, int n
   const int64_t NR = (int64_t)B * T * K;
   for (int s = threadIdx.x; s <= last_seg; s += 1024) {
     int64_t off;
-    if (s < M * B) off = cnt[(int64_t)s * nsub];
+    if (s < M * B) off = offs[(int64_t)s * nsub];
     else if (s < (M + 1) * B) off = NR + (int64_t)(s - M * B) * T;
     else off = NR + (int64_t)B * T;
     seg_off[s] = (int32_t)off;
@@ -290,16 +293,19 @@ static mom_status dispatch(const mom_dims* dims, const int32_t* idx, const void*
   // part 2 leaves the shared rows and the shared segments' offsets (past M B) to part 1
   const int last_seg = part == 2 ? d.M * d.B : (d.M + 1) * d.B;
   const bool shared_rows = part == 0;
+  // counts, then (when not scanned inside the scatter) their exclusive scan
   int32_t* cnt = (int32_t*)ws;
+  int32_t* offs = cnt + dispatch_offs_at(d);
   if (!counted)
     hipLaunchKernelGGL(k_count, dim3(ntile, d.B), dim3(kTile), 0, st, d.B, d.T, d.M, d.topk, nsub, idx, cnt);
   const bool fused = (int64_t)d.M * d.B * nsub <= kFuseScan;
   if (!fused)
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, d.B, d.T, d.M, d.topk, nsub, last_seg, cnt, seg_off);
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, d.B, d.T, d.M, d.topk, nsub, last_seg, cnt, offs,
+                       seg_off);
 #define MOM_SCATTER(XT, F)                                                                                         \
   hipLaunchKernelGGL((k_scatter<XT, F>), dim3(ntile, d.B), dim3(kTile), 0, st, d.B, d.T, d.D, d.H, d.M, d.topk,    \
-                     nsub, last_seg, shared_rows, idx, cnt, seg_off, alpha, beta, perm, inv, alpha_p, beta_p,     \
-                     (const XT*)x, (XT*)x_packed)
+                     nsub, last_seg, shared_rows, idx, F ? cnt : offs, seg_off, alpha, beta, perm, inv, alpha_p,  \
+                     beta_p, (const XT*)x, (XT*)x_packed)
   if (d.dtype == MOM_DTYPE_BF16) {
     if (fused) MOM_SCATTER(bf16_t, true);
     else MOM_SCATTER(bf16_t, false);
@@ -346,9 +352,9 @@ extern "C" mom_status mom_dispatch_part(const mom_dims* dims, const int32_t* idx
 }
 
 // ------------------------------------------------------------------ allocation-free dispatch
-// mom_dispatch_noalloc keeps the dispatch's counts (int32 [M][B][ceil(T/64)],
-// written in full by k_count before k_scan or k_scatter read them, so nothing
-// needs clearing) in this array instead of a caller workspace.  In host code
+// mom_dispatch_noalloc keeps the dispatch's workspace (the counts, int32
+// [M][B][ceil(T/64)], written in full by k_count before k_scan or k_scatter
+// read them, and their scan, so nothing needs clearing) in this array instead of a caller workspace.  In host code
 // `scratch` only names the symbol: its device address is looked up once per
 // device with hipGetSymbolAddress and kept in scratch_ptr.
 namespace mom {

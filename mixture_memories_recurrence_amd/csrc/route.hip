@@ -268,54 +268,63 @@ __global__ __launch_bounds__(256) void k_route_wave4(int64_t NT, int D, int M, i
   }
 }
 
-// Route and dispatch counts for whole sequences, bfloat16 rows, D = 1024 and
-// at most four memories: k_route_wave4's arithmetic (the router slice held in
-// registers, four positions at a time, the same products, sums and tree), in
-// blocks of eight waves per 64 positions of one sequence, each wave taking
-// two groups of four positions with the second group's rows loaded while the
-// first is reduced.  Each wave counts its positions' selections per memory
-// with ballots; the block adds its waves' counts and writes the dispatch's
-// count of its 64 positions, cnt[m][b][sub] (nsub = ceil(T / 64)), so the
-// dispatch needs no counting launch and nothing is cleared first.
-__global__ __launch_bounds__(512) void k_route_sub4(int B, int T, int D, int M, int K, int nsub,
-                                                    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr,
-                                                    const float* __restrict__ bias, int32_t* __restrict__ idx,
-                                                    float* __restrict__ w, int32_t* __restrict__ cnt) {
+// Route and dispatch counts for whole sequences (bfloat16 rows, D = 1024 DG,
+// M <= 4 MG): one block of eight waves per 64 positions of one sequence.  Wave
+// (mg, dg, nh) holds in registers its lanes' slice of router rows 4 mg ..
+// 4 mg + 3 over elements [1024 dg, 1024 dg + 1024) (lane l: 8 l + 512 j + i)
+// and walks positions nh 64 / NH .. in groups of four, the next group's rows
+// loaded while the current one is reduced.  The products, per-lane sums and
+// cross-lane tree are k_route_wave4's; each tree's total (a partial logit over
+// the wave's elements) goes to LDS, and the block's first wave adds the DG
+// partials of each memory in order, runs the top-k and the softmax for its
+// position (lane = position), and counts the selections per memory with
+// ballots: the dispatch's count of these 64 positions, cnt[m][b][sub] (nsub =
+// ceil(T / 64)), so the dispatch needs no counting launch and nothing is
+// cleared first.  With DG = MG = 1 the logits are k_route_wave4's bit for bit.
+template <int MG, int DG, int NH>
+__global__ __launch_bounds__(512) void k_route_blk(int B, int T, int D, int M, int K, int nsub,
+                                                   const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr,
+                                                   const float* __restrict__ bias, int32_t* __restrict__ idx,
+                                                   float* __restrict__ w, int32_t* __restrict__ cnt) {
+  static_assert(MG * DG * NH == 8, "eight waves");
   using P = ExactProd<bf16_t>;
-  constexpr int EPL = 16, NL = EPL / 8, TPW = 4;
-  __shared__ int32_t wave_cnt[8][64];
+  constexpr int MP = 4 * MG, TPW = 4, NGR = 64 / NH / TPW;  // memories held, groups per wave
+  __shared__ double part[DG][64][MP];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int mg = wv % MG, dg = (wv / MG) % DG, nh = wv / (MG * DG);
   const int sub = blockIdx.x, b = blockIdx.y;
-  const int p0 = sub * 64 + wv * 8;  // first position of this wave
+  const int lp0 = nh * (64 / NH);  // first position of this wave inside the 64
   const int64_t tok0 = (int64_t)b * T;
-  typename P::Raw xr[2][TPW][NL];
-#pragma unroll
-  for (int gi = 0; gi < 2; ++gi)
+  const int64_t col = 1024 * dg + 8 * lane;
+  typename P::Raw xr[2][TPW][2];
+  auto load = [&](int gi, int bufi) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      int p = p0 + gi * TPW + i;
+      int p = sub * 64 + lp0 + gi * TPW + i;
       p = p < T ? p : T - 1;  // past the end: a valid row, never written
 #pragma unroll
-      for (int j = 0; j < NL; ++j) xr[gi][i][j] = P::raw(x + (tok0 + p) * D + 8 * lane + 512 * j);
+      for (int j = 0; j < 2; ++j) xr[bufi][i][j] = P::raw(x + (tok0 + p) * D + col + 512 * j);
     }
-  float wf[4][EPL];
+  };
+  load(0, 0);
+  if (NGR > 1) load(1, 1);
+  float wf[4][16];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const bf16_t* row = wr + (int64_t)(m < M ? m : M - 1) * D + 8 * lane;
+    const int mm = 4 * mg + m;
+    const bf16_t* row = wr + (int64_t)(mm < M ? mm : M - 1) * D + col;
 #pragma unroll
-    for (int j = 0; j < NL; ++j) P::unpack(P::raw(row + 512 * j), &wf[m][8 * j]);
+    for (int j = 0; j < 2; ++j) P::unpack(P::raw(row + 512 * j), &wf[m][8 * j]);
   }
-  int my_cnt = 0;  // lane m: this wave's selections of memory m
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    double mine[4] = {0.0, 0.0, 0.0, 0.0};  // logits of position p0 + 4 gi + lane (lanes < 4)
+  for (int gi = 0; gi < NGR; ++gi) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int j = 0; j < NL; ++j) {
+      for (int j = 0; j < 2; ++j) {
         float xv[8];
-        P::unpack(xr[gi][i][j], xv);
+        P::unpack(xr[gi & 1][i][j], xv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const double xd = (double)xv[e];
@@ -332,57 +341,53 @@ __global__ __launch_bounds__(512) void k_route_sub4(int B, int T, int D, int M, 
       v += row_shr<2>(v);
       v += row_shr<4>(v);
       v += row_shr<8>(v);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const double lm = read_lane(v, 16 * m + 15);
-        if (lane == i) mine[m] = lm;
-      }
+      if ((lane & 15) == 15) part[dg][lp0 + gi * TPW + i][4 * mg + (lane >> 4)] = v;
     }
-    const int p = p0 + gi * TPW + lane;
-    uint32_t taken = 0;
-    if (lane < TPW && p < T) {
-      const int64_t t = tok0 + p;
-      double logit[4];
+    if (gi + 2 < NGR) load(gi + 2, gi & 1);
+  }
+  __syncthreads();
+  if (wv != 0) return;
+  const int p = sub * 64 + lane;
+  uint32_t taken = 0;
+  if (p < T) {
+    const int64_t t = tok0 + p;
+    double logit[MP];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) logit[m] = mine[m] + (bias && m < M ? (double)bias[m] : 0.0);
-      int sel[4];
-      double ls[4];
-      for (int j = 0; j < K; ++j) {
-        int best = -1;
-        double bl = 0.0;
+    for (int m = 0; m < MP; ++m) {
+      double l = part[0][lane][m];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          if (m < M && !((taken >> m) & 1u) && (best < 0 || logit[m] > bl)) {
-            best = m;
-            bl = logit[m];
-          }
+      for (int g = 1; g < DG; ++g) l += part[g][lane][m];
+      logit[m] = l + (bias && m < M ? (double)bias[m] : 0.0);
+    }
+    int sel[8];
+    double ls[8];
+    for (int j = 0; j < K; ++j) {
+      int best = -1;
+      double bl = 0.0;
+#pragma unroll
+      for (int m = 0; m < MP; ++m) {
+        if (m < M && !((taken >> m) & 1u) && (best < 0 || logit[m] > bl)) {
+          best = m;
+          bl = logit[m];
         }
-        taken |= 1u << best;
-        sel[j] = best;
-        ls[j] = bl;
       }
-      double z = 0.0, e[4];
-      for (int j = 0; j < K; ++j) {
-        e[j] = exp(ls[j] - ls[0]);
-        z += e[j];
-      }
-      for (int j = 0; j < K; ++j) {
-        idx[t * K + j] = sel[j];
-        w[t * K + j] = (float)(e[j] / z);
-      }
+      taken |= 1u << best;
+      sel[j] = best;
+      ls[j] = bl;
     }
-    for (int m = 0; m < M; ++m) {
-      const int n = __popcll(__ballot((taken >> m) & 1u));
-      if (lane == m) my_cnt += n;
+    double z = 0.0, e[8];
+    for (int j = 0; j < K; ++j) {
+      e[j] = exp(ls[j] - ls[0]);
+      z += e[j];
+    }
+    for (int j = 0; j < K; ++j) {
+      idx[t * K + j] = sel[j];
+      w[t * K + j] = (float)(e[j] / z);
     }
   }
-  wave_cnt[wv][lane] = my_cnt;
-  __syncthreads();
-  if (threadIdx.x < M) {
-    int c = 0;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) c += wave_cnt[u][threadIdx.x];
-    cnt[((int64_t)threadIdx.x * B + b) * nsub + sub] = c;
+  for (int m = 0; m < M; ++m) {
+    const int n = __popcll(__ballot((taken >> m) & 1u));
+    if (lane == 0) cnt[((int64_t)m * B + b) * nsub + sub] = n;
   }
 }
 
@@ -448,9 +453,17 @@ extern "C" mom_status mom_route_count(const mom_dims* dims, const void* x, const
     int32_t* cnt = (int32_t*)ws;
     const int nsub = (d.T + kCountTile - 1) / kCountTile;
     const dim3 grid((unsigned)nsub, (unsigned)d.B);
-    if (d.dtype == MOM_DTYPE_BF16 && d.D == 1024 && d.M <= 4) {
-      hipLaunchKernelGGL(k_route_sub4, grid, dim3(512), 0, st, d.B, d.T, d.D, d.M, d.topk, nsub, (const bf16_t*)x,
-                         (const bf16_t*)w_r, bias, idx, w, cnt);
+    if (d.dtype == MOM_DTYPE_BF16 && ((d.D == 1024 && d.M <= 16) || (d.D == 2048 && d.M <= 4))) {
+      const bf16_t* xp = (const bf16_t*)x;
+      const bf16_t* wp = (const bf16_t*)w_r;
+#define MOM_ROUTE_BLK(MG, DG, NH)                                                                                   \
+  hipLaunchKernelGGL((k_route_blk<MG, DG, NH>), grid, dim3(512), 0, st, d.B, d.T, d.D, d.M, d.topk, nsub, xp, wp, \
+                     bias, idx, w, cnt)
+      if (d.D == 2048) MOM_ROUTE_BLK(1, 2, 4);
+      else if (d.M <= 4) MOM_ROUTE_BLK(1, 1, 8);
+      else if (d.M <= 8) MOM_ROUTE_BLK(2, 1, 4);
+      else MOM_ROUTE_BLK(4, 1, 2);
+#undef MOM_ROUTE_BLK
       return launch_status();
     }
     // other shapes: the router, then the dispatch's own counting kernel

@@ -108,8 +108,8 @@ def test_dispatch_workspace_is_checked():
     L = mom.lib()
     d = _dims()
     need = L.mom_workspace_bytes(ctypes.byref(d), 0)
-    nsub = -(-d.T // 64)  # counts of every 64 positions
-    assert need >= d.M * d.B * nsub * 4 and need % 256 == 0
+    n = d.M * d.B * -(-d.T // 64)  # counts of every 64 positions, then their scan
+    assert need >= (-(-n // 64) * 64 + n) * 4 and need % 256 == 0
     args = [FAKE] * 10
     assert L.mom_dispatch(ctypes.byref(d), *args, None, need, None) == -5
     assert L.mom_dispatch(ctypes.byref(d), *args, FAKE, need - 1, None) == -5
@@ -217,7 +217,8 @@ def test_chunk_bwd_checks():
 @needs_lib
 def test_dispatch_noalloc_checks_before_any_launch():
     """The allocation-free dispatch validates like mom_dispatch and rejects
-    sizes past its fixed scratch (M*B*ceil(T/64) <= 65536 counts) with
+    sizes past its fixed scratch (M*B*ceil(T/64) <= 32768 counts, and as many
+    scanned offsets) with
     MOM_ERR_TOO_LARGE, all before any HIP call (so without a GPU)."""
     L = mom.lib()
     f = lambda d, *p: L.mom_dispatch_noalloc(ctypes.byref(d), *p, None)
@@ -227,12 +228,12 @@ def test_dispatch_noalloc_checks_before_any_launch():
     assert f(_dims(), FAKE, None, FAKE, *ok[3:]) == -1      # beta
     assert f(_dims(), FAKE, FAKE, FAKE, FAKE, ODD, *ok[5:]) == -4   # seg_off misaligned
     assert f(_dims(topk=0), *ok) == -2
-    # 16 memories x 64 sequences x 65 counts of 64 positions = 66560 counts > 65536
-    big = _dims(M=16, topk=4, B=64, T=65 * 64)
+    # 16 memories x 32 sequences x 65 counts of 64 positions = 33280 counts > 32768
+    big = _dims(M=16, topk=4, B=32, T=65 * 64)
     assert f(big, *ok) == -7
     assert L.mom_status_string(-7).decode().startswith("sizes exceed")
     # exactly at the limit passes the size check (then needs a GPU, not called here)
-    assert L.mom_workspace_bytes(ctypes.byref(_dims(M=16, topk=4, B=64, T=64 * 64)), 0) == 65536 * 4
+    assert L.mom_workspace_bytes(ctypes.byref(_dims(M=16, topk=4, B=32, T=64 * 64)), 0) == 65536 * 4
 
 
 @needs_lib

@@ -145,8 +145,11 @@ def test_route_count_full_size(name):
             mom.mom_dispatch(d, b["idx"], g["x"], g["alpha"], g["beta"], b["seg_off"], b["perm"], b["inv"], None,
                              b["alpha_p"], b["beta_p"], ws)
         elif mode == "counted":
-            mom.mom_dispatch_counted(d, b["idx"], g["x"], g["alpha"], g["beta"], b["seg_off"], b["perm"], b["inv"],
-                                     None, b["alpha_p"], b["beta_p"], ws)
+            # twice on the same counts: the call leaves them as they are (the
+            # configs past 1024 counts scan them in a launch of their own)
+            for _ in range(2):
+                mom.mom_dispatch_counted(d, b["idx"], g["x"], g["alpha"], g["beta"], b["seg_off"], b["perm"],
+                                         b["inv"], None, b["alpha_p"], b["beta_p"], ws)
         else:
             mom.mom_dispatch_counted_part(d, None, g["x"], g["alpha"], g["beta"], b["seg_off"], b["perm"], None,
                                           None, b["alpha_p"], b["beta_p"], None, mom.PART_SHARED)
