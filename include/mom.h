@@ -231,7 +231,11 @@ mom_status mom_project_part(const mom_dims* dims, const void* x, const int32_t* 
  * [seg_off[s], seg_off[s+1]) of the row arrays) runs the recurrence above in
  * row order from state slot seg_state[s] (NULL: slot s); different segments
  * must use different slots.  Chunks of dims->chunk rows are processed in the
- * WY/UT form, which equals the token recurrence up to rounding.
+ * WY/UT form, which equals the token recurrence up to rounding.  With half
+ * storage, when the call has so few segments and heads that the walk would
+ * run at most 8 blocks and its segments are long, each segment is cut into
+ * groups of chunks whose affine state maps are walked in parallel and then
+ * chained (the long-segment scan): the same result up to rounding.
  *   q         [n_tok][H][dk] read at row row_token[r] (NULL: row r itself)
  *   k [N][H][dk], v [N][H][dv] (float32 or half per dims->dtype)
  *   alpha_p, beta_p [N][H] float32
@@ -267,9 +271,11 @@ mom_status gla_chunk_fwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, in
  * jxzklqfsx.com write-up, introduction, states that the layer trains in linear
  * time); these are the chain rule applied to the recurrence above, evaluated
  * in the same chunk form (half operands on the matrix cores, float32
- * accumulation and states).  Only the half (dims->dtype == MOM_DTYPE_BF16)
- * storage is supported; float32 returns MOM_ERR_UNSUPPORTED.  Every alpha
- * of the rows run must be > 0 (d_alpha = d(log alpha) / alpha).
+ * accumulation and states) for half storage (dims->dtype == MOM_DTYPE_BF16),
+ * where every alpha of the rows run must be > 0 (d_alpha = d(log alpha) /
+ * alpha); with float32 storage as a row-by-row reverse sweep in float32 that
+ * recomputes the states from ones kept every 64 and every 8 rows (any alpha
+ * in [0, 1]).
  *   inputs:   as gdn_chunk_fwd (dims, segments, slots, row_token, q, k, v,
  *             alpha_p, beta_p, state_in or NULL = zeros)
  *   d_o        [N][H][dv] float32
@@ -304,12 +310,14 @@ mom_status gla_chunk_bwd(const mom_dims* dims, int32_t n_seg, int32_t n_rows, in
                          void* stream);
 
 /* The forward pass of a training step: the outputs of gdn_chunk_fwd (same
- * arguments, layouts and errors; half storage only, as gdn_chunk_bwd), and ws,
- * which must hold gdn_chunk_bwd_workspace_bytes(dims, n_seg, n_rows) bytes,
- * keeps what gdn_chunk_bwd_saved reads: each chunk's solved triangular factor,
- * its inverse, the masked query-key products, the decay prefix sums and the
- * state entering the chunk.  o and state_out equal gdn_chunk_fwd's bit for
- * bit. */
+ * arguments, layouts and errors), and ws, which must hold
+ * gdn_chunk_bwd_workspace_bytes(dims, n_seg, n_rows) bytes, keeps what
+ * gdn_chunk_bwd_saved reads: with half storage each chunk's solved triangular
+ * factor, its inverse, the masked query-key products, the decay prefix sums
+ * and the state entering the chunk (with float32 storage nothing: its
+ * backward recomputes the states).  o and state_out equal gdn_chunk_fwd's bit
+ * for bit when gdn_chunk_fwd walks every segment whole (with the
+ * long-segment scan they agree to rounding). */
 mom_status gdn_chunk_fwd_train(const mom_dims* dims, int32_t n_seg, int32_t n_rows, int32_t n_tok,
                                int32_t n_state, const int32_t* seg_off, const int32_t* seg_state,
                                const int32_t* row_token, const void* q, const void* k, const void* v,

@@ -894,9 +894,22 @@ static mom_status launch_bwd(const mom_dims& d, int n_seg, int n_rows, const int
   return launch_status();
 }
 
+// gdn_bwd_valu.hip: the float32 path
+size_t gdn_bwd_valu_ws_bytes(int64_t n_seg, int64_t n_rows, int H, int dk, int dv);
+mom_status launch_gdn_bwd_valu(const mom_dims& d, int n_seg, int n_rows, const int32_t* seg_off,
+                               const int32_t* seg_state, const int32_t* row_token, const float* q, const float* k,
+                               const float* v, const float* alpha_p, const float* beta_p, const float* state_in,
+                               const float* d_o, const float* dstate_out, float* dq, float* dk, float* dv_out,
+                               float* da, float* dc, float* dstate_in, void* ws, bool delta, hipStream_t st);
+template <typename IT>
+mom_status launch_gdn_chunk_valu(const mom_dims& d, int n_seg, const int32_t* seg_off, const int32_t* seg_state,
+                                 const int32_t* row_token, const void* q, const void* k, const void* v,
+                                 const float* alpha_p, const float* beta_p, const float* state_in, float* state_out,
+                                 float* o, bool delta, hipStream_t st);
+
 static size_t chunk_bwd_ws_bytes(const mom_dims* dims, int32_t n_seg, int32_t n_rows) {
   if (check_dims(dims) != MOM_OK || n_seg < 0 || n_rows < 0) return 0;
-  if (dims->dtype != MOM_DTYPE_BF16) return 0;
+  if (dims->dtype != MOM_DTYPE_BF16) return gdn_bwd_valu_ws_bytes(n_seg, n_rows, dims->H, dims->dk, dims->dv);
   return chunk_bwd_ws_layout(nullptr, n_seg, n_rows, dims->H, dims->dk, dims->dv).bytes;
 }
 
@@ -908,7 +921,6 @@ static mom_status chunk_bwd(bool delta, bool saved, const mom_dims* dims, int32_
                             float* dstate_in, void* ws, size_t ws_bytes, void* stream) {
   mom_status s = check_dims(dims);
   if (s != MOM_OK) return s;
-  if (dims->dtype != MOM_DTYPE_BF16) return MOM_ERR_UNSUPPORTED;
   if (n_seg < 0 || n_rows < 0 || n_tok < 0 || n_state < 0) return MOM_ERR_DIMS;
   if (!seg_state && n_state < n_seg) return MOM_ERR_DIMS;
   MOM_CHECK_PTR(seg_off);
@@ -935,6 +947,10 @@ static mom_status chunk_bwd(bool delta, bool saved, const mom_dims* dims, int32_
   MOM_CHECK_PTR(ws);
   if (n_seg == 0) return MOM_OK;
   hipStream_t st = (hipStream_t)stream;
+  if (dims->dtype != MOM_DTYPE_BF16)  // float32: the row-by-row reverse sweep (nothing is kept between calls)
+    return launch_gdn_bwd_valu(*dims, n_seg, n_rows, seg_off, seg_state, row_token, (const float*)q,
+                               (const float*)k, (const float*)v, alpha_p, beta_p, state_in, d_o, dstate_out, dq, dk,
+                               dv, da, dc, dstate_in, ws, delta, st);
 #define MOM_BWD(DK, DELTA)                                                                                       \
   launch_bwd<DK, DELTA>(*dims, n_seg, n_rows, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p, state_in, \
                         d_o, dstate_out, dq, dk, dv, da, dc, dstate_in, ws, saved, st)
@@ -952,7 +968,6 @@ static mom_status chunk_fwd_train(bool delta, const mom_dims* dims, int32_t n_se
                                   float* o, void* ws, size_t ws_bytes, void* stream) {
   mom_status s = check_dims(dims);
   if (s != MOM_OK) return s;
-  if (dims->dtype != MOM_DTYPE_BF16) return MOM_ERR_UNSUPPORTED;
   if (n_seg < 0 || n_rows < 0 || n_tok < 0 || n_state < 0) return MOM_ERR_DIMS;
   if (!seg_state && n_state < n_seg) return MOM_ERR_DIMS;
   MOM_CHECK_PTR(seg_off);
@@ -972,6 +987,9 @@ static mom_status chunk_fwd_train(bool delta, const mom_dims* dims, int32_t n_se
   MOM_CHECK_PTR(ws);
   if (n_seg == 0) return MOM_OK;
   const mom_dims& d = *dims;
+  if (d.dtype != MOM_DTYPE_BF16)  // float32: the forward pass; its backward recomputes what it needs
+    return launch_gdn_chunk_valu<float>(d, n_seg, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p, state_in,
+                                        state_out, o, delta, (hipStream_t)stream);
   const ChunkBwdWs W = chunk_bwd_ws_layout(ws, n_seg, n_rows, d.H, d.dk, d.dv);
   return launch_chunk_states(d, n_seg, n_rows, seg_off, seg_state, row_token, q, k, v, alpha_p, beta_p, state_in,
                              state_out, o, W.fw, W.X, W.h, delta, true, (hipStream_t)stream);

@@ -175,8 +175,10 @@ def test_route_count_checks():
 
 @needs_lib
 def test_chunk_bwd_checks():
-    """The gradient entry points: workspace size (forward factors, X (half), and two
-    half states per chunk and head), half storage only, and the usual refusals."""
+    """The gradient entry points: workspace size (half storage: forward factors, X
+    (half), and two half states per chunk and head; float32: the state entering
+    every chunk, checkpoints every 8 rows per block, and the column blocks'
+    partial sums), and the usual refusals, all before any launch."""
     L = mom.lib()
     d = _dims()
     n_seg, n_rows = (d.M + 1) * d.B, d.B * d.T * (d.topk + 1)
@@ -195,9 +197,14 @@ def test_chunk_bwd_checks():
         bad[8] = None  # dq
         assert f(ctypes.byref(d), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, *bad, FAKE, need, None) == -1
         d32 = _dims(dtype=0)
-        assert f(ctypes.byref(d32), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, *args, FAKE, need,
-                 None) == -3
-    assert L.gdn_chunk_bwd_workspace_bytes(ctypes.byref(_dims(dtype=0)), n_seg, n_rows) == 0
+        need32 = L.gdn_chunk_bwd_workspace_bytes(ctypes.byref(d32), n_seg, n_rows)
+        assert f(ctypes.byref(d32), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, *args, FAKE, need32 - 1,
+                 None) == -5
+    a256 = lambda b: (b + 255) // 256 * 256
+    nb = d.dv // 64
+    need32 = a256(n_chunks * d.H * d.dk * d.dv * 4) + a256(n_seg * d.H * nb * 8 * d.dk * 64 * 4) + \
+        2 * a256(nb * n_rows * d.H * d.dk * 4) + 2 * a256(nb * n_rows * d.H * 4)
+    assert L.gdn_chunk_bwd_workspace_bytes(ctypes.byref(_dims(dtype=0)), n_seg, n_rows) == need32
     fargs = [FAKE] * 5 + [None, FAKE, FAKE]  # q..beta, state_in, state_out, o
     for f in (L.gdn_chunk_fwd_train, L.gla_chunk_fwd_train):
         # the training forward needs the gradient workspace, not the forward's
@@ -211,7 +218,7 @@ def test_chunk_bwd_checks():
             assert f(ctypes.byref(d), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, *bad, FAKE, need,
                      None) == -1
         assert f(ctypes.byref(_dims(dtype=0)), n_seg, n_rows, d.B * d.T, n_seg, FAKE, None, None, *fargs, FAKE,
-                 need, None) == -3
+                 need32 - 1, None) == -5
 
 
 @needs_lib

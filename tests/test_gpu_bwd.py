@@ -22,35 +22,44 @@ GRAD_REL = 5e-3
 SEG_LENGTHS = [0, 1, 63, 64, 65, 130, 200, 7, 128, 0, 300]
 
 
-def assert_grad(name, got, ref):
+# float32 storage: the float32 config's 1e-5, stated the same way (relative to
+# each gradient tensor's largest value for max-abs)
+GRAD_REL_F32 = 1e-5
+
+
+def assert_grad(name, got, ref, rel=GRAD_REL):
     ma, rl = errors(got, ref)
-    bound = GRAD_REL * max(float(np.max(np.abs(ref))), 1e-30)
-    log("  %-10s max-abs %.3e (<= %.2e)  rel-L2 %.3e (<= %.1e)" % (name, ma, bound, rl, GRAD_REL))
-    assert ma <= bound and rl <= GRAD_REL, "%s: max-abs %.3e rel-L2 %.3e" % (name, ma, rl)
+    bound = rel * max(float(np.max(np.abs(ref))), 1e-30)
+    log("  %-10s max-abs %.3e (<= %.2e)  rel-L2 %.3e (<= %.1e)" % (name, ma, bound, rl, rel))
+    assert ma <= bound and rl <= rel, "%s: max-abs %.3e rel-L2 %.3e" % (name, ma, rl)
 
 
 def nan(*shape):
     return torch.full(shape, float("nan"), device="cuda")
 
 
-def run_bwd_segments(rule, dk, dv, with_state, with_dstate, shared_tokens, H=2, seed=0):
+def run_bwd_segments(rule, dk, dv, with_state, with_dstate, shared_tokens, H=2, seed=0, store="f16", gates=None):
     lens = np.array(SEG_LENGTHS)
     seg_off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     N, n_seg = int(seg_off[-1]), len(lens)
-    ch = synth.make_chain_inputs(N, H, dk, dv, seed=dk + dv + seed, store="f16")
+    ch = synth.make_chain_inputs(N, H, dk, dv, seed=dk + dv + seed, store=store)
+    if gates == "deltanet":  # forget gates fixed at 1
+        ch["alpha"] = np.ones_like(ch["alpha"])
+    elif gates == "gate0":  # forget gates of exactly 0 inside chunks
+        ch["alpha"][5::37] = 0.0
     rng = np.random.default_rng(seed + 1)
     n_tok = N // 3 if shared_tokens else N + 5
     row_token = (rng.integers(0, n_tok, N) if shared_tokens else rng.permutation(n_tok)[:N]).astype(np.int32)
-    qtok = synth.make_chain_inputs(n_tok, H, dk, dv, seed=seed + 7, store="f16")["q"]
+    qtok = synth.make_chain_inputs(n_tok, H, dk, dv, seed=seed + 7, store=store)["q"]
     n_state = n_seg + 3
     seg_state = rng.permutation(n_state)[:n_seg].astype(np.int32)
     S0 = (rng.standard_normal((n_state, H, dk, dv)) * 0.1).astype(np.float32)
     gr = synth.make_chain_grads(N, H, dk, dv, n_state, seed=seed + 4)
-    dims = mom.dims_of(synth.LayerConfig(1, 1, 64, H, dk, dv, 1, 1, "bf16"))
+    dims = mom.dims_of(synth.LayerConfig(1, 1, 64, H, dk, dv, 1, 1, "f32" if store == "f32" else "bf16"))
     out = dict(dq=nan(N, H, dk), dk=nan(N, H, dk), dv=nan(N, H, dv), da=nan(N, H), dc=nan(N, H),
                ds0=nan(n_state, H, dk, dv))
     ws = torch.empty(mom.gdn_chunk_bwd_workspace_bytes(dims, n_seg, N), dtype=torch.uint8, device="cuda")
-    f16 = torch.float16
+    f16 = torch.float32 if store == "f32" else torch.float16
     fn = mom.gla_chunk_bwd if rule == "gla" else mom.gdn_chunk_bwd
     args = (dims, n_seg, N, n_tok, n_state, to_gpu(seg_off), to_gpu(seg_state), to_gpu(row_token), to_gpu(qtok, f16),
             to_gpu(ch["k"], f16), to_gpu(ch["v"], f16), to_gpu(ch["alpha"]), to_gpu(ch["beta"]),
@@ -84,6 +93,34 @@ def test_chunk_bwd_segments(rule, dk, dv, with_state, with_dstate, shared_tokens
         assert np.array_equal(got["ds0"][ss[s]], r["dstate"][ss[s]])
     unused = sorted(set(range(r["n_state"])) - set(ss.tolist()))
     assert np.all(np.isnan(got["ds0"][unused]))
+
+
+@pytest.mark.parametrize("rule,dk,dv,with_state,with_dstate,shared_tokens,gates", [
+    ("gdn", 64, 64, True, True, True, None), ("gdn", 128, 256, True, True, False, None),
+    ("gdn", 64, 128, False, False, True, None), ("gla", 64, 64, True, True, False, None),
+    ("gla", 128, 128, False, True, True, None), ("gdn", 64, 64, True, True, False, "gate0"),
+    ("gdn", 64, 64, True, True, False, "deltanet")])
+def test_chunk_bwd_segments_f32(rule, dk, dv, with_state, with_dstate, shared_tokens, gates):
+    """Float32 storage: the row-by-row reverse sweep on the same ragged segments
+    (one and several 64-column blocks, whose partial sums are added after),
+    with forget gates of exactly 0 inside chunks and fixed at 1 (DeltaNet)."""
+    log("chunk_bwd f32", rule, dk, dv, "state" if with_state else "-", "dstate" if with_dstate else "-",
+        "shared" if shared_tokens else "", gates or "")
+    r = run_bwd_segments(rule, dk, dv, with_state, with_dstate, shared_tokens, store="f32", gates=gates)
+    got, ref, ss = r["out"], r["ref"], r["seg_state"]
+    for name, rn in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("d_alpha", "da"), ("d_beta", "dc")):
+        assert_grad(name, got[rn], ref[rn], GRAD_REL_F32)
+    assert_grad("dstate_in", got["ds0"][ss], ref["dstate0"][ss], GRAD_REL_F32)
+    for s in np.nonzero(r["lens"] == 0)[0]:
+        assert np.array_equal(got["ds0"][ss[s]], r["dstate"][ss[s]])
+    unused = sorted(set(range(r["n_state"])) - set(ss.tolist()))
+    assert np.all(np.isnan(got["ds0"][unused]))
+    # the same call again gives the same bits (fixed summation order)
+    out = {kk: nan(*vv.shape) for kk, vv in r["out"].items()}
+    r["fn"](*r["args"], out["dq"], out["dk"], out["dv"], out["da"], out["dc"], out["ds0"], r["ws"])
+    torch.cuda.synchronize()
+    for kk, vv in out.items():
+        assert np.array_equal(vv.cpu().numpy(), r["out"][kk], equal_nan=True), kk
 
 
 def test_chunk_bwd_deterministic():

@@ -49,6 +49,38 @@ def test_layer_bwd_reduced(name, B, T, rule):
         assert_grad(name_g, f(g[name_g]), ref[rn])
 
 
+@pytest.mark.parametrize("rule,train", [("gdn", False), ("gla", False), ("gdn", True)])
+def test_layer_bwd_tiny_f32(rule, train):
+    """The float32 layer's gradients (the row-by-row reverse sweep for the
+    recurrence), from non-zero entering states with final-state gradients,
+    after a plain forward and after a training forward, to the float32
+    tolerance (1e-5, relative to each tensor's largest value for max-abs)."""
+    from test_gpu_bwd import GRAD_REL_F32
+    cfg = synth.CONFIGS["tiny_f32"]
+    B, T = cfg.B, cfg.T
+    inp = synth.make_layer_inputs(cfg, seed=25)
+    NT = B * T
+    rng = np.random.default_rng(26)
+    dout = rng.standard_normal((NT, cfg.H, cfg.dv)).astype(np.float32)
+    S0 = (0.1 * rng.standard_normal((B, cfg.M + 1, cfg.H, cfg.dk, cfg.dv))).astype(np.float32)
+    dS = rng.standard_normal(S0.shape).astype(np.float32)
+    layer = mom.MomLayer(cfg, inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"], rule=rule)
+    x = to_gpu(inp["x"])
+    log("layer_bwd f32", rule, "train" if train else "")
+    _, _, b = layer.forward(x, to_gpu(inp["alpha"]), to_gpu(inp["beta"]), state_in=to_gpu(S0), train=train)
+    g = layer.backward(x, to_gpu(dout), b, dstate_out=to_gpu(dS), state_in=to_gpu(S0))
+    torch.cuda.synchronize()
+    dims = (B, T, cfg.D, cfg.H, cfg.dk, cfg.dv, cfg.M, cfg.K)
+    ref = oracle.layer_bwd(dims, inp["x"], inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"], inp["alpha"],
+                           inp["beta"], dout, state0=S0, dstate=dS, rule=rule)
+    assert np.array_equal(b["idx"].cpu().numpy(), ref["idx"])
+    f = lambda t: t.float().cpu().numpy()
+    for name_g, rn in (("d_alpha", "d_alpha"), ("d_beta", "d_beta"), ("dq", "dq"), ("dk", "dk_rows"),
+                       ("dv", "dv_rows"), ("dx_router", "dx_router"), ("dw_r", "dw_r"), ("dbias", "dbias"),
+                       ("dstate_in", "dstate0")):
+        assert_grad(name_g, f(g[name_g]), ref[rn], GRAD_REL_F32)
+
+
 def test_combine_route_dispatch_bwd_full_size():
     """At the 380M shape (8 x 2048 tokens), the three gather / router gradient
     entry points on the GPU's own forward results, against the checker's
