@@ -67,6 +67,10 @@ __device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmc
 __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void vm_wait_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void vm_wait_n() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef float f16x16 __attribute__((ext_vector_type(16)));

@@ -69,6 +69,13 @@ namespace mom {
 // 16-row block of its column) and skips the read-out (no Q, P or O; state_out
 // may then be null); MODE 2 does both, the forward pass of a training step,
 // whose o and states equal MODE 0's bit for bit.
+// Rows of the entering state staged per round in the training modes: as many
+// as NW waves' 16 columns fit in one buffer's Q area (GC x DK), at most DK.
+template <int DK, int NW>
+constexpr int chain16_state_rows() {
+  return GC * DK / (NW * 16) < DK ? GC * DK / (NW * 16) : DK;
+}
+
 template <int DK, int NW, bool DELTA, bool MAP, int MODE = 0>
 __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
     int H, int dv, int width, int col_base, int sw, int ident, int n_seg, const int32_t* __restrict__ seg_off,
@@ -214,9 +221,12 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
   int buf = 0;
   for (int64_t r0 = rbeg; r0 < rend; r0 += GC, buf ^= 1) {
     const int L = (int)min((int64_t)GC, rend - r0);
-    // this wave's copies have landed (only the previous chunk's 4 output
-    // stores were issued after them); then every wave's
-    if (r0 == rbeg || !READ) vm_wait_all();
+    // this wave's copies have landed (only the previous chunk's stores were
+    // issued after them: 4 output pieces, and in the training modes DK / 32
+    // of the entering state); then every wave's
+    if (r0 == rbeg || MAP) vm_wait_all();
+    else if (MODE == 1) vm_wait_n<DK / 32>();
+    else if (MODE == 2) vm_wait_n<DK / 32 + 4>();
     else vm_wait_4();
     lds_barrier();
     pf_setup(r0 + GC < rend ? r0 + GC : r0, buf ^ 1, reinterpret_cast<const int32_t*>(smem + buf * BUF + OFF_TOK));
@@ -228,14 +238,6 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
     const f16_t* Ts = Bc + OFF_T;
     const f16_t* Ps = Bc + OFF_P;
     const float* Eg = reinterpret_cast<const float*>(Bc + OFF_E);  // gamma_i, then gamma_L / gamma_i
-    if constexpr (MODE != 0) {  // the entering state, transposed, as half
-      f16_t* hc = hws + ((int64_t)(cbase + (r0 - rbeg) / GC) * H + h) * sw * DK + (int64_t)(ncol0 + c16) * DK + 4 * G;
-#pragma unroll
-      for (int a = 0; a < ND; ++a) {
-        const half4 hv = {(f16_t)S[a][0], (f16_t)S[a][1], (f16_t)S[a][2], (f16_t)S[a][3]};
-        *reinterpret_cast<half4*>(hc + 16 * a) = hv;
-      }
-    }
 
     // ---- Y = K S and O^T = S^T Q^T; the state's 32-row blocks as operands
     f4v Y[4], O[4];
@@ -270,6 +272,38 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
       for (int t = 0; t < 4; ++t) {
         Y[t] = mfma16(kf[kb & 1][t], sop, Y[t]);
         if (READ) O[t] = mfma16(sop, qf[kb & 1][t], O[t]);
+      }
+    }
+    // The entering state (S is updated only at the end of the chunk),
+    // transposed, as half, issued after the next chunk's copies so that
+    // waiting for those does not wait for these stores.  The wave's columns
+    // pass through LDS, RR rows at a time (8-byte pieces in, 16-byte pieces
+    // out, the 16-byte chunks of each column XOR-swizzled by column), so that
+    // every store writes runs of RR / 8 whole 16-byte pieces of a column: in
+    // mode 1 through the Q area of the current buffer (no read-out, so never
+    // loaded), in mode 2 through an area of its own after the two buffers.
+    if constexpr (MODE != 0) {
+      f16_t* hw = hws + ((int64_t)(cbase + (r0 - rbeg) / GC) * H + h) * sw * DK + (int64_t)ncol0 * DK;
+      constexpr int RR = chain16_state_rows<DK, NW>();  // rows per round
+      constexpr int CPC = RR / 8;                       // 16-byte chunks per column
+      f16_t* st = (MODE == 1 ? smem + buf * BUF + OFF_Q : smem + 2 * BUF) + w * 16 * RR;
+#pragma unroll
+      for (int r = 0; r < DK / RR; ++r) {
+#pragma unroll
+        for (int a = 0; a < RR / 16; ++a) {
+          const int ch = 2 * a + G / 2;  // chunk of rows 16 a + 4 G ..
+          const int aa = r * (RR / 16) + a;
+          const half4 hv = {(f16_t)S[aa][0], (f16_t)S[aa][1], (f16_t)S[aa][2], (f16_t)S[aa][3]};
+          *reinterpret_cast<half4*>(st + c16 * RR + 8 * (ch ^ (c16 & (CPC - 1))) + 4 * (G & 1)) = hv;
+        }
+        wave_lds_fence();
+#pragma unroll
+        for (int p0 = 0; p0 < 16 * CPC; p0 += 64) {
+          const int p = p0 + lane, col = p / CPC, ch = p % CPC;
+          const h8v x = *reinterpret_cast<const h8v*>(st + col * RR + 8 * (ch ^ (col & (CPC - 1))));
+          *reinterpret_cast<h8v*>(hw + (int64_t)col * DK + r * RR + 8 * ch) = x;
+        }
+        wave_lds_fence();
       }
     }
     CHAIN_PHASE();
@@ -349,8 +383,10 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
 }
 
 template <int DK, int NW>
-constexpr size_t chain16_lds_bytes() {
-  return (size_t)2 * (2 * GC * DK + GC * 16 * NW + 2 * GC * GC + 4 * GC + 2 * GC) * sizeof(f16_t);
+constexpr size_t chain16_lds_bytes(int mode = 0) {
+  // two buffers, and in mode 2 the entering state's staging area (NW x 16 columns x RR rows)
+  return (size_t)2 * (2 * GC * DK + GC * 16 * NW + 2 * GC * GC + 4 * GC + 2 * GC) * sizeof(f16_t) +
+         (mode == 2 ? (size_t)NW * 16 * chain16_state_rows<DK, NW>() * sizeof(f16_t) : 0);
 }
 
 // ------------------------------------------------------------------ prep
@@ -771,7 +807,7 @@ static mom_status launch_chain16(const mom_dims& d, int n_seg, const int32_t* se
                                  const void* v, const float* state_in, float* state_out, float* o, hipStream_t st,
                                  int width, int col_base, int sw, int ident, const int32_t* grp_seg,
                                  f16_t* hws = nullptr) {
-  constexpr size_t lds = chain16_lds_bytes<DK, NW>();
+  constexpr size_t lds = chain16_lds_bytes<DK, NW>(MODE);
   static bool attr = false;  // the dynamic LDS limit is raised once per kernel
   if (!attr) {
     if (hipFuncSetAttribute((const void*)k_gdn_chain16<DK, NW, DELTA, MAP, MODE>,
