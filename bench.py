@@ -25,6 +25,31 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0      # dense bf16 / fp16 matrix cores
 FP32_VALU_PEAK_TFLOPS = 157.3  # vector fp32 (packed); 78.6 without packed ops
 
+# Seconds of untimed steps each line runs before its W warm-up steps.  The GPU
+# raises its clocks only after about a tenth of a second of load; a handful of
+# warm-up steps (a few milliseconds) leaves the timed steps on the way up
+# (measured: the 380M-shape step took 0.454-0.456 ms after 5 warm-up steps and
+# 0.403-0.413 ms after 200).
+CLOCK_WARMUP_S = 0.3
+
+
+def ramp(fn, seconds=None):
+    """Run fn (one untimed step of the line about to be timed) repeatedly for
+    `seconds` of wall time; returns the number of steps run."""
+    import torch
+    seconds = CLOCK_WARMUP_S if seconds is None else seconds
+    n = 0
+    if seconds <= 0:
+        return n
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(4):
+            fn()
+        n += 4
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -42,6 +67,8 @@ def parse():
                    help="other prefill workloads timed after the headline one (comma list; '' for none)")
     p.add_argument("--serial", action="store_true",
                    help="time the steps in order on one stream (default: the layer's two-stream schedule)")
+    p.add_argument("--clock-warmup", type=float, default=CLOCK_WARMUP_S,
+                   help="seconds of untimed steps before each line's warm-up steps (0 for none)")
     p.add_argument("--traffic", default=None,
                    help="summary of measured HBM bytes per call (default: profiles/traffic_<workload>.json)")
     return p.parse_args()
@@ -152,6 +179,7 @@ def time_gla_layer(cfg, inp, x, alpha, beta, steps, warmup):
     from mixture_memories_recurrence_amd import mom
     layer = mom.MomLayer(cfg, inp["w_r"], inp["bias"], inp["w_q"], inp["w_k"], inp["w_v"], rule="gla")
     state = torch.empty(cfg.B, cfg.M + 1, cfg.H, cfg.dk, cfg.dv, dtype=torch.float32, device="cuda")
+    ramp(lambda: layer.forward(x, alpha, beta, state_out=state))
     for _ in range(warmup):
         layer.forward(x, alpha, beta, state_out=state)
     torch.cuda.synchronize()
@@ -185,6 +213,7 @@ def time_chunk_bwd(cfg, inp, x, alpha, beta, steps, warmup):
     stream = torch.cuda.current_stream()
 
     def timed(fn):
+        ramp(fn)
         for _ in range(warmup):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -245,6 +274,7 @@ def time_single_memory(steps, warmup):
     def step():
         mom.gdn_chunk_fwd(dims, B, N, N, B, seg_off, None, None, q, k, v, alpha, beta, None, state, o, ws)
 
+    ramp(step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -317,6 +347,7 @@ class Workload:
         kernels; returns (wall ms per step, GPU-event ms per step)."""
         import torch
         fn = self.step_serial if serial else self.step_overlapped
+        ramp(fn)
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -391,6 +422,8 @@ def main():
     import torch
     from mixture_memories_recurrence_amd import mom, synth
 
+    global CLOCK_WARMUP_S
+    CLOCK_WARMUP_S = args.clock_warmup
     w = Workload(args.workload)
     cfg, inp, x, alpha, beta = w.cfg, w.inp, w.x, w.alpha, w.beta
     NT = cfg.B * cfg.T
@@ -420,6 +453,7 @@ def main():
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "gpu_ms_per_step": round(gpu_ms, 4),
+        "clock_warmup_s": CLOCK_WARMUP_S,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": describe(cfg), "tokens_per_step": NT, "chunk": cfg.chunk},
@@ -441,6 +475,7 @@ def main():
             steps_in.append((torch.from_numpy(d["x"]).to(torch.bfloat16).cuda(), torch.from_numpy(d["alpha"]).cuda(),
                              torch.from_numpy(d["beta"]).cuda()))
         db = dlayer.buffers(n_seq, 1)
+        ramp(lambda: dlayer.decode_step(*steps_in[0], states))
         for i in range(3):
             dlayer.decode_step(*steps_in[i % 4], states)
         torch.cuda.synchronize()
