@@ -59,3 +59,20 @@ def test_layer_bound(name, mtok):
         assert us["dispatch"] == pytest.approx(6296 * NT / 8e12 * 1e6, rel=1e-9)
         assert us["combine"] == pytest.approx(16400 * NT / 8e12 * 1e6, rel=1e-9)
         assert us["chunk"] == pytest.approx(24672 * NT / 8e12 * 1e6, rel=1e-9)
+
+
+def test_clock_warmup_runs_whole_groups_for_the_time_asked(monkeypatch):
+    """bench.ramp runs the line's own step untimed, in groups of four with a
+    device synchronisation after each group, until the time asked has passed;
+    with no time asked it runs nothing."""
+    import time
+    import torch
+    import bench
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda *a, **k: None)
+    calls = []
+    assert bench.ramp(lambda: calls.append(1), 0) == 0
+    assert calls == []
+    t0 = time.perf_counter()
+    n = bench.ramp(lambda: calls.append(1), 0.05)
+    assert time.perf_counter() - t0 >= 0.05
+    assert n == len(calls) and n >= 4 and n % 4 == 0
