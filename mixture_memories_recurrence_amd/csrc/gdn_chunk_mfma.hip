@@ -348,6 +348,18 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
       ub[kb] = acc16_to_op(U[2 * kb], U[2 * kb + 1], ones, ones);
       u2b[kb] = acc16_to_op(U[2 * kb], U[2 * kb + 1], s0, s1);
     }
+    // ---- S <- gamma_L S + K^T U' (issued before the read-out, which the next
+    // chunk does not need, so that the read-out runs while these products do)
+    const float eL = Eg[GC - 1];
+#pragma unroll
+    for (int a = 0; a < ND; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[a][e] *= eL;
+#pragma unroll
+    for (int kb = 0; kb < GC / 32; ++kb)
+#pragma unroll
+      for (int a = 0; a < ND; ++a) S[a] = mfma16(col_frag16<DK>(Ks, kb, 16 * a, lane), u2b[kb], S[a]);
+    CHAIN_PHASE();
     // ---- O^T = O^T diag(gamma) + U^T P^T, stored as 16-byte row pieces
 #pragma unroll
     for (int t = 0; t < (READ ? 4 : 0); ++t) {
@@ -362,17 +374,6 @@ __global__ __launch_bounds__(64 * NW) void k_gdn_chain16(
       if (16 * t + c16 < L)
         *reinterpret_cast<float4*>(o + ((r0 + 16 * t + c16) * H + h) * dv + ncol0 + 4 * G) =
             make_float4(O[t][0], O[t][1], O[t][2], O[t][3]);
-    CHAIN_PHASE();
-    // ---- S <- gamma_L S + K^T U'
-    const float eL = Eg[GC - 1];
-#pragma unroll
-    for (int a = 0; a < ND; ++a)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) S[a][e] *= eL;
-#pragma unroll
-    for (int kb = 0; kb < GC / 32; ++kb)
-#pragma unroll
-      for (int a = 0; a < ND; ++a) S[a] = mfma16(col_frag16<DK>(Ks, kb, 16 * a, lane), u2b[kb], S[a]);
   }
   vm_wait_all();  // the last (repeated) prefetch has landed before the block ends
   if (MODE == 1 && !state_out) return;
